@@ -1,0 +1,248 @@
+"""Benchmark of the top-1 MoE gate hot path on one MI355X.
+
+One step = moe_top1_fwd + moe_top1_bwd + moe_aux_loss over one batch of synthetic tokens
+already resident in HBM.  Prints one JSON line (last line of stdout):
+
+  value          routed tokens/s of the whole step (T / step time)
+  roofline       the dominant kernel's algorithmic flops (or bytes) per launch divided
+                 by its average launch time, timed with HIP events around each of its
+                 launches inside the timed region, against the MI355X peak
+  cpu_baseline   the fp64 CPU oracle timed on this host on a bounded sample
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2|1|3|4|5] [--graph]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}
+METRIC = "routed tokens/s fwd+bwd+aux (H=128, N_E=4, fp32); % of HBM/MFMA roofline"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic(kernel, wl):
+    """(amount, unit, bound) per launch: flops for the MFMA GEMMs, HBM bytes otherwise."""
+    T, H, NE = wl.T, wl.H, wl.NE
+    s = 2 if wl.act == "bf16" else 4
+    if kernel in ("fwd_gemm", "dx_gemm", "dw_gemm"):
+        return 2.0 * T * H * H, "flop", "mfma"
+    if kernel == "route":
+        return T * NE * 4 + T * 4, "byte", "hbm"
+    if kernel == "scatter":
+        return T * 4 * 2, "byte", "hbm"
+    if kernel == "aux_rows":
+        return 8.0 * T * NE, "byte", "hbm"
+    if kernel == "reduce":
+        return NE * H * H * 4 + NE * H * 4, "byte", "hbm"
+    return 0.0, "byte", "hbm"
+
+
+def pass_roofline_us(wl):
+    """Roofline time (us) of fwd, bwd and aux at the MI355X peaks (algorithmic bytes/flops)."""
+    T, H, NE = wl.T, wl.H, wl.NE
+    s = 2 if wl.act == "bf16" else 4
+    pk = PEAK_TFLOPS[wl.act] * 1e12
+    bw = PEAK_HBM_GBS * 1e9
+    fb = T * H * s * 2 + T * NE * 4 + NE * H * H * s + NE * H * 4 + T * 4
+    ff = 2.0 * T * H * H + T * H
+    bb = 3 * T * H * s + T * 4 + NE * H * H * s + NE * H * H * 4 + NE * H * 4
+    bf = 4.0 * T * H * H + T * H
+    ab = 8.0 * T * NE + NE * 4
+    return {"fwd": max(fb / bw, ff / pk) * 1e6, "bwd": max(bb / bw, bf / pk) * 1e6, "aux": ab / bw * 1e6}
+
+
+def cpu_baseline(inp, budget_s=12.0):
+    """The oracle as it stands, on this host's cores, over a bounded sample of the workload."""
+    import numpy as np
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    wl = inp.wl
+    T = wl.T
+    # sample: the first n tokens of the workload (whole batch if it fits the budget)
+    n = T
+    x, g, dy = inp.fused_ctx.reshape(T, -1), inp.gate_logits.reshape(T, -1), inp.d_out.reshape(T, -1)
+    t0 = time.perf_counter()
+    O.run_all(inp)
+    one = time.perf_counter() - t0
+    if one > budget_s:
+        n = max(1024, int(T * budget_s / one / 2))
+    reps, tok, el = 0, 0, 0.0
+    while el < budget_s and reps < 1000:
+        t0 = time.perf_counter()
+        f = O.forward(x[:n], g[:n], inp.W, inp.b)
+        O.backward(dy[:n], x[:n], inp.W, f.expert_idx)
+        O.aux(g[:n], f.counts, wl.lam)
+        el += time.perf_counter() - t0
+        reps += 1
+        tok += n
+    return {"value": tok / el, "unit": "routed tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{reps} x fwd+bwd+aux over the first {n} of {T} tokens ({el:.1f} s, fp64 NumPy)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--graph", action="store_true", help="replay the step as one captured HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mixture_experts_top_amd as moe
+    import workloads
+    from tests import gpu_run
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        sys.exit(1)
+    moe.load_library()
+    wl = workloads.workload(args.workload)
+    log(f"[bench] workload {args.workload}: {wl}")
+    inp = workloads.make_inputs(wl)
+    d = gpu_run.upload(inp)
+    o = gpu_run.Buffers(d, poison=False)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        gpu_run.step(d, o)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # per-kernel averages (outside the timed region) to find the dominant kernel
+    nk = 10
+    kern_us = {}
+    for k in moe.KERNELS:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nk)]
+        for a, b in evs:
+            a.record(); b.record()
+        torch.cuda.synchronize()
+        for a, b in evs:
+            moe.moe_set_launch_timer(k, a, b)
+            step()
+        moe.moe_set_launch_timer(None)
+        torch.cuda.synchronize()
+        kern_us[k] = float(np.mean([a.elapsed_time(b) for a, b in evs]) * 1e3)
+    dom = max((k for k in kern_us if k in ("fwd_gemm", "dx_gemm", "dw_gemm", "aux_rows", "reduce")),
+              key=lambda k: kern_us[k])
+    log("[bench] kernel avg us: " + ", ".join(f"{k}={v:.2f}" for k, v in kern_us.items()) + f"; dominant={dom}")
+
+    graph = None
+    if args.graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(stream)
+        with torch.cuda.stream(s):
+            step()
+        stream.wait_stream(s)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+
+    # timed region: K steps, the dominant kernel bracketed by events in every step
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for a, b in evs:
+        a.record(); b.record()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        if graph is not None:
+            graph.replay()
+        else:
+            moe.moe_set_launch_timer(dom, *evs[i])
+            step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    moe.moe_set_launch_timer(None)
+    ms = (t1 - t0) / K * 1e3
+    if graph is None:
+        dom_us = float(np.mean([a.elapsed_time(b) for a, b in evs]) * 1e3)
+    else:
+        dom_us = kern_us[dom]
+    amount, unit, bound = algorithmic(dom, wl)
+    if bound == "mfma":
+        achieved = amount / (dom_us * 1e-6) / 1e12
+        peak = PEAK_TFLOPS[wl.act]
+        runit = "TFLOP/s"
+    else:
+        achieved = amount / (dom_us * 1e-6) / 1e9
+        peak = PEAK_HBM_GBS
+        runit = "GB/s"
+
+    # per-pass times (eager, after the timed region)
+    def time_pass(fn, n=20):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n * 1e3
+
+    pass_us = {"fwd": time_pass(lambda: gpu_run.fwd(d, o)), "bwd": time_pass(lambda: gpu_run.bwd(d, o)),
+               "aux": time_pass(lambda: gpu_run.aux(d, o))}
+    roof = pass_roofline_us(wl)
+    step_roof_frac = sum(roof.values()) / (ms * 1e3)
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(inp, args.cpu_budget)
+    T = wl.T
+    out = {
+        "metric": METRIC,
+        "value": T / (ms * 1e-3),
+        "unit": "routed tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.act,
+        "data": "synthetic (seeded; see workloads.py)",
+        "config": {"workload": wl.name, "B": wl.B, "N_H": wl.NH, "H": wl.H, "N_E": wl.NE, "T": T,
+                   "lambda": wl.lam, "act": wl.act, "launch": "hip-graph" if graph is not None else "eager",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": bound, "kernel": dom, "achieved": achieved, "peak": peak, "unit": runit,
+                     "frac": achieved / peak, "traffic": None, "avg_launch_us": dom_us,
+                     "per_launch": f"{amount:.4g} {unit}"},
+        "step_roofline_frac": step_roof_frac,
+        "pass_us": pass_us,
+        "pass_roofline_us": roof,
+        "kernel_avg_us": kern_us,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,185 @@
+/*
+ * moe_top1.h -- C ABI of the top-1 Mixture-of-Experts gate for AMD Instinct MI355X (gfx950).
+ *
+ * The operations are those of the commit page "11b96dac6a  Top-1 Mixture-of-Experts
+ * gate per Switch Transformer":
+ *   - forward   (summary block, PERFORMANCE block): pick the top-1 expert of each
+ *               (b, h) token's gate logits and apply that expert's [H, H] linear plus
+ *               bias to fused_ctx, giving routed_ctx [B, N_H, H];
+ *   - backward  (summary block, ARCHITECTURE block): gradients through the selected
+ *               expert's W and bias only, giving d_W, d_b and d_fused_ctx; inactive
+ *               experts get exactly zero and the gate gets nothing from this path;
+ *               the per-token d_W / d_b contributions are collapsed over the token axis
+ *               by a deterministic reduction with no atomics (the reduce_axis0 design of
+ *               the perf-pass page "b23f8f2efa");
+ *   - aux loss  (summary block): softmax of gate_logits and the load-balancing loss
+ *               lambda * N_E * sum_e frac_e * mean_prob_e, with its gradient w.r.t. the
+ *               gate logits (frac, a count, is held constant).
+ *
+ * Notation: T = B * N_H tokens, token t = b * N_H + h.  All tensors are dense,
+ * row-major and contiguous:
+ *   fused_ctx, routed_ctx, d_routed_ctx, d_fused_ctx   [B, N_H, H]       act dtype
+ *   gate_logits, d_gate_logits, probs                  [B, N_H, N_E]     fp32
+ *   W                                                  [N_E, H_out, H_in] act dtype (y = W x)
+ *   b                                                  [N_E, H]          fp32
+ *   d_W                                                [N_E, H, H]       fp32
+ *   d_b, expert_counts, frac, mean_prob                [N_E]             fp32 / int32
+ *   expert_idx, perm                                   [T]               int32
+ *   expert_offsets                                     [N_E + 1]         int32
+ * "act dtype" is fp32 (MOE_DTYPE_F32) or bf16 (MOE_DTYPE_BF16, stored as raw 16-bit
+ * patterns; products are accumulated in fp32 and rounded to bf16, nearest even, on store).
+ *
+ * Ownership and execution.  Every pointer argument is a device pointer owned by the
+ * caller (except size outputs, which are host pointers).  Calls only enqueue work on the
+ * given HIP stream (NULL = the default stream) and return; they never allocate, free or
+ * synchronise, keep no state between calls and read nothing back to the host, so they
+ * may be captured into a HIP graph.  Buffers must stay valid until the stream has run
+ * the call.  Two calls may run concurrently only with distinct workspaces and outputs.
+ * Results are bitwise reproducible: every floating-point reduction has a fixed order and
+ * no atomics are used.
+ *
+ * Errors.  Every argument is validated before anything is launched; on error nothing is
+ * enqueued and the return value says why (moe_status_string, moe_last_error):
+ *   MOE_ERR_INVALID_ARG  a required pointer is NULL or not 16-byte aligned, a size is
+ *                        <= 0, T * max(H, N_E) >= 2^31, or lambda is not finite;
+ *   MOE_ERR_UNSUPPORTED  H not in {64, 128, 256, 512}, N_E not in [1, 64], or an
+ *                        unknown dtype;
+ *   MOE_ERR_WORKSPACE    workspace is NULL or smaller than moe_workspace_bytes();
+ *   MOE_ERR_HIP          a kernel launch failed (the HIP error text is in moe_last_error).
+ * Launch extents are always derived by the library from (B, N_H, H, N_E), never taken
+ * from the caller.
+ */
+#ifndef MOE_TOP1_H
+#define MOE_TOP1_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,
+    MOE_ERR_UNSUPPORTED = 2,
+    MOE_ERR_WORKSPACE = 3,
+    MOE_ERR_HIP = 4
+} moe_status_t;
+
+typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype_t;
+
+/* MOE_ABI_VERSION of the built library. */
+int moe_abi_version(void);
+
+/* Static text for a status code. */
+const char* moe_status_string(int status);
+
+/* Detail of the last error returned on the calling thread (static storage, thread-local). */
+const char* moe_last_error(void);
+
+/*
+ * Workspace size in bytes (host-only; no device is touched).  One workspace of this size
+ * serves moe_top1_route, moe_top1_fwd, moe_top1_bwd and moe_aux_loss for the same
+ * (B, N_H, H, N_E, act).  The workspace holds routing histograms and the fixed-size
+ * per-chunk partial sums of d_W / d_b; its contents need no initialisation and are
+ * meaningless between calls.
+ */
+moe_status_t moe_workspace_bytes(int64_t B, int64_t NH, int64_t H, int64_t NE, int act,
+                                 size_t* bytes_out);
+
+/*
+ * Routing half of the forward pass (summary and PERFORMANCE blocks of the MoE-gate page:
+ * the top-1 expert of each token's gate logits).
+ *   expert_idx[t]     argmax_e gate_logits[t, e]; on equal logits the lowest e wins.
+ *   expert_counts[e]  number of tokens routed to e.
+ *   expert_offsets    exclusive prefix sum of expert_counts, [0, c_0, c_0+c_1, ..., T].
+ *   perm              the tokens of expert 0, then of expert 1, ..., each group in
+ *                     ascending token order (a stable counting sort by expert).
+ * All four outputs are overwritten; integers are exact.
+ */
+moe_status_t moe_top1_route(const float* gate_logits, int32_t* expert_idx, int32_t* expert_counts,
+                            int32_t* expert_offsets, int32_t* perm,
+                            int64_t B, int64_t NH, int64_t NE,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Forward pass (summary block of the MoE-gate page): moe_top1_route, then
+ *   routed_ctx[t, :] = W[e*(t)] @ fused_ctx[t, :] + b[e*(t)]
+ * for every token (no capacity limit, no scaling by the gate probability).
+ * routed_ctx is overwritten; the routing outputs are as for moe_top1_route and are the
+ * inputs of moe_top1_bwd and moe_aux_loss.
+ */
+moe_status_t moe_top1_fwd(const void* fused_ctx, const float* gate_logits, const void* W,
+                          const float* b, void* routed_ctx,
+                          int32_t* expert_idx, int32_t* expert_counts, int32_t* expert_offsets,
+                          int32_t* perm,
+                          int64_t B, int64_t NH, int64_t H, int64_t NE, int act,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward pass (summary and ARCHITECTURE blocks of the MoE-gate page), given the
+ * expert_offsets and perm written by moe_top1_fwd for the same tokens:
+ *   d_fused_ctx[t, :] = W[e*(t)]^T @ d_routed_ctx[t, :]      (overwritten, or added to
+ *                                                              the existing contents when
+ *                                                              accumulate_dx != 0)
+ *   d_W[e] = sum_{t : e*(t) = e} d_routed_ctx[t, :]^T (outer) fused_ctx[t, :]  (overwritten)
+ *   d_b[e] = sum_{t : e*(t) = e} d_routed_ctx[t, :]                            (overwritten)
+ * Experts with no tokens get d_W[e] = d_b[e] = +0.0 exactly.  The token sums are taken
+ * per fixed-size chunk of each expert's tokens and the chunk partials are then summed
+ * in chunk order (no atomics), so the result depends only on the inputs and the shape.
+ * The gate logits get no gradient here.
+ */
+moe_status_t moe_top1_bwd(const void* d_routed_ctx, const void* fused_ctx, const void* W,
+                          const int32_t* expert_offsets, const int32_t* perm,
+                          void* d_fused_ctx, float* d_W, float* d_b, int accumulate_dx,
+                          int64_t B, int64_t NH, int64_t H, int64_t NE, int act,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Load-balancing aux loss (summary block of the MoE-gate page; softmax in the max-shifted
+ * form of the softmax/cross-entropy page "6cfd7e6691"):
+ *   p[t, :]       = softmax(gate_logits[t, :])
+ *   frac[e]       = expert_counts[e] / T
+ *   mean_prob[e]  = (1/T) sum_t p[t, e]
+ *   loss          = lambda * N_E * sum_e frac[e] * mean_prob[e]
+ *   d_gate_logits[t, j] = (lambda * N_E / T) * p[t, j] * (frac[j] - sum_e frac[e] p[t, e])
+ * expert_counts comes from moe_top1_fwd; pass NULL to have it recomputed from the logits.
+ * loss [1] and d_gate_logits are written on the device; frac, mean_prob and probs are
+ * optional outputs (NULL = not written).
+ */
+moe_status_t moe_aux_loss(const float* gate_logits, const int32_t* expert_counts, float lambda,
+                          float* loss, float* d_gate_logits,
+                          float* frac, float* mean_prob, float* probs,
+                          int64_t B, int64_t NH, int64_t NE,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Instrumentation.  While set, every launch of kernel `kernel_id` (MOE_KERNEL_*) made by
+ * the calls above is bracketed by hipEventRecord(ev_start) and hipEventRecord(ev_stop) on
+ * the call's stream.  The events are hipEvent_t handles created by the caller.  Pass
+ * kernel_id < 0 to clear.  Process-wide setting; not thread-safe against concurrent calls.
+ */
+enum {
+    MOE_KERNEL_ROUTE = 0,
+    MOE_KERNEL_SCAN = 1,
+    MOE_KERNEL_SCATTER = 2,
+    MOE_KERNEL_FWD_GEMM = 3,
+    MOE_KERNEL_DX_GEMM = 4,
+    MOE_KERNEL_DW_GEMM = 5,
+    MOE_KERNEL_REDUCE = 6,
+    MOE_KERNEL_AUX_ROWS = 7,
+    MOE_KERNEL_AUX_FINAL = 8,
+    MOE_KERNEL_COUNT = 9
+};
+moe_status_t moe_set_launch_timer(int kernel_id, void* ev_start, void* ev_stop);
+
+/* Name of a MOE_KERNEL_* id (static text), NULL if out of range. */
+const char* moe_kernel_name(int kernel_id);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_TOP1_H */

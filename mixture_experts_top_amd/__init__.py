@@ -1,0 +1,226 @@
+"""Top-1 Mixture-of-Experts gate on MI355X (gfx950): Python binding of libmoe_top1.so.
+
+The functions here carry the names of the C entry points in include/moe_top1.h and do
+argument marshalling only: shapes are read from the tensors, device pointers and the
+current HIP stream are passed through, and every step of the computation runs in the
+library's HIP kernels.  There is no fallback: if the library or a GPU is missing, the
+calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+__all__ = [
+    "load_library", "library_path", "moe_abi_version", "moe_workspace_bytes", "moe_top1_route",
+    "moe_top1_fwd", "moe_top1_bwd", "moe_aux_loss", "moe_set_launch_timer", "moe_kernel_name",
+    "MoeError", "KERNELS", "DTYPE_F32", "DTYPE_BF16",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+DTYPE_F32, DTYPE_BF16 = 0, 1
+KERNELS = ["route", "scan", "scatter", "fwd_gemm", "dx_gemm", "dw_gemm", "reduce", "aux_rows", "aux_final"]
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"[status {status}] {msg}")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(_PKG, "libmoe_top1.so")
+
+
+def load_library() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m mixture_experts_top_amd.build` "
+                          "or __graft_entry__.build()")
+    # torch first: its HIP runtime (same soname) is then the one the library binds to,
+    # so the process holds a single runtime and torch's device pointers are valid here.
+    import torch  # noqa: F401
+    lib = ctypes.CDLL(path)
+    P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    sig = {
+        "moe_abi_version": ([], I32),
+        "moe_status_string": ([I32], ctypes.c_char_p),
+        "moe_last_error": ([], ctypes.c_char_p),
+        "moe_kernel_name": ([I32], ctypes.c_char_p),
+        "moe_workspace_bytes": ([I64, I64, I64, I64, I32, ctypes.POINTER(SZ)], I32),
+        "moe_top1_route": ([P, P, P, P, P, I64, I64, I64, P, SZ, P], I32),
+        "moe_top1_fwd": ([P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I32, P, SZ, P], I32),
+        "moe_top1_bwd": ([P, P, P, P, P, P, P, P, I32, I64, I64, I64, I64, I32, P, SZ, P], I32),
+        "moe_aux_loss": ([P, P, ctypes.c_float, P, P, P, P, P, I64, I64, I64, P, SZ, P], I32),
+        "moe_set_launch_timer": ([I32, P, P], I32),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    _lib = lib
+    return lib
+
+
+def _check(st: int):
+    if st != 0:
+        lib = load_library()
+        raise MoeError(st, f"{lib.moe_status_string(st).decode()}: {lib.moe_last_error().decode()}")
+
+
+def moe_abi_version() -> int:
+    return load_library().moe_abi_version()
+
+
+def moe_kernel_name(k: int) -> Optional[str]:
+    r = load_library().moe_kernel_name(k)
+    return r.decode() if r else None
+
+
+def moe_workspace_bytes(B: int, NH: int, H: int, NE: int, act: int = DTYPE_F32) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load_library().moe_workspace_bytes(B, NH, H, NE, act, ctypes.byref(out)))
+    return out.value
+
+
+# ------------------------------------------------------------------ tensor helpers
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("all tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("all tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _act(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    raise ValueError(f"activation dtype must be float32 or bfloat16, got {t.dtype}")
+
+
+def _workspace(ws, B, NH, H, NE, act, device):
+    import torch
+    need = moe_workspace_bytes(B, NH, H, NE, act)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return ws, ws.numel() * ws.element_size()
+
+
+def _shape3(t, name):
+    if t.dim() != 3:
+        raise ValueError(f"{name} must be [B, N_H, *], got {tuple(t.shape)}")
+    return tuple(int(x) for x in t.shape)
+
+
+def _expect(t, name, shape, dtype):
+    """Host-side check that a buffer has exactly the shape and dtype the kernels assume."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+# ------------------------------------------------------------------ entry points
+
+def moe_top1_route(gate_logits, expert_idx, expert_counts, expert_offsets, perm, workspace=None, stream=None):
+    import torch
+    B, NH, NE = _shape3(gate_logits, "gate_logits")
+    T = B * NH
+    _expect(gate_logits, "gate_logits", (B, NH, NE), torch.float32)
+    _expect(expert_idx, "expert_idx", (T,), torch.int32)
+    _expect(expert_counts, "expert_counts", (NE,), torch.int32)
+    _expect(expert_offsets, "expert_offsets", (NE + 1,), torch.int32)
+    _expect(perm, "perm", (T,), torch.int32)
+    ws, wsb = _workspace(workspace, B, NH, 64, NE, DTYPE_F32, gate_logits.device)
+    _check(load_library().moe_top1_route(_ptr(gate_logits), _ptr(expert_idx), _ptr(expert_counts),
+                                         _ptr(expert_offsets), _ptr(perm), B, NH, NE, _ptr(ws), wsb,
+                                         _stream(stream)))
+
+
+def moe_top1_fwd(fused_ctx, gate_logits, W, b, routed_ctx, expert_idx, expert_counts, expert_offsets, perm,
+                 workspace=None, stream=None):
+    import torch
+    B, NH, H = _shape3(fused_ctx, "fused_ctx")
+    NE = int(gate_logits.shape[-1])
+    T = B * NH
+    act = _act(fused_ctx)
+    _expect(gate_logits, "gate_logits", (B, NH, NE), torch.float32)
+    _expect(W, "W", (NE, H, H), fused_ctx.dtype)
+    _expect(b, "b", (NE, H), torch.float32)
+    _expect(routed_ctx, "routed_ctx", (B, NH, H), fused_ctx.dtype)
+    _expect(expert_idx, "expert_idx", (T,), torch.int32)
+    _expect(expert_counts, "expert_counts", (NE,), torch.int32)
+    _expect(expert_offsets, "expert_offsets", (NE + 1,), torch.int32)
+    _expect(perm, "perm", (T,), torch.int32)
+    ws, wsb = _workspace(workspace, B, NH, H, NE, act, fused_ctx.device)
+    _check(load_library().moe_top1_fwd(_ptr(fused_ctx), _ptr(gate_logits), _ptr(W), _ptr(b), _ptr(routed_ctx),
+                                       _ptr(expert_idx), _ptr(expert_counts), _ptr(expert_offsets), _ptr(perm),
+                                       B, NH, H, NE, act, _ptr(ws), wsb, _stream(stream)))
+
+
+def moe_top1_bwd(d_routed_ctx, fused_ctx, W, expert_offsets, perm, d_fused_ctx, d_W, d_b, accumulate_dx=False,
+                 workspace=None, stream=None):
+    import torch
+    B, NH, H = _shape3(fused_ctx, "fused_ctx")
+    NE = int(W.shape[0])
+    T = B * NH
+    act = _act(fused_ctx)
+    _expect(d_routed_ctx, "d_routed_ctx", (B, NH, H), fused_ctx.dtype)
+    _expect(W, "W", (NE, H, H), fused_ctx.dtype)
+    _expect(expert_offsets, "expert_offsets", (NE + 1,), torch.int32)
+    _expect(perm, "perm", (T,), torch.int32)
+    _expect(d_fused_ctx, "d_fused_ctx", (B, NH, H), fused_ctx.dtype)
+    _expect(d_W, "d_W", (NE, H, H), torch.float32)
+    _expect(d_b, "d_b", (NE, H), torch.float32)
+    ws, wsb = _workspace(workspace, B, NH, H, NE, act, fused_ctx.device)
+    _check(load_library().moe_top1_bwd(_ptr(d_routed_ctx), _ptr(fused_ctx), _ptr(W), _ptr(expert_offsets),
+                                       _ptr(perm), _ptr(d_fused_ctx), _ptr(d_W), _ptr(d_b), int(bool(accumulate_dx)),
+                                       B, NH, H, NE, act, _ptr(ws), wsb, _stream(stream)))
+
+
+def moe_aux_loss(gate_logits, expert_counts, lam, loss, d_gate_logits, frac=None, mean_prob=None, probs=None,
+                 workspace=None, stream=None):
+    import torch
+    B, NH, NE = _shape3(gate_logits, "gate_logits")
+    _expect(gate_logits, "gate_logits", (B, NH, NE), torch.float32)
+    _expect(expert_counts, "expert_counts", (NE,), torch.int32)
+    _expect(loss, "loss", (1,), torch.float32)
+    _expect(d_gate_logits, "d_gate_logits", (B, NH, NE), torch.float32)
+    _expect(frac, "frac", (NE,), torch.float32)
+    _expect(mean_prob, "mean_prob", (NE,), torch.float32)
+    _expect(probs, "probs", (B, NH, NE), torch.float32)
+    ws, wsb = _workspace(workspace, B, NH, 64, NE, DTYPE_F32, gate_logits.device)
+    _check(load_library().moe_aux_loss(_ptr(gate_logits), _ptr(expert_counts), float(lam), _ptr(loss),
+                                       _ptr(d_gate_logits), _ptr(frac), _ptr(mean_prob), _ptr(probs),
+                                       B, NH, NE, _ptr(ws), wsb, _stream(stream)))
+
+
+def moe_set_launch_timer(kernel, ev_start=None, ev_stop=None):
+    """Bracket every launch of one kernel (name or MOE_KERNEL_* id) with two torch.cuda.Events;
+    kernel=None clears."""
+    lib = load_library()
+    if kernel is None:
+        _check(lib.moe_set_launch_timer(-1, None, None))
+        return
+    kid = KERNELS.index(kernel) if isinstance(kernel, str) else int(kernel)
+    _check(lib.moe_set_launch_timer(kid, ev_start.cuda_event, ev_stop.cuda_event))

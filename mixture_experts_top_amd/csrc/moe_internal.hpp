@@ -1,0 +1,91 @@
+// Internal declarations of the top-1 MoE gate library (gfx950 / CDNA4).
+//
+// The C ABI lives in include/moe_top1.h; this header holds the workspace plan, the
+// constants shared by kernels and host code, and the host-side launchers that each
+// kernel file provides.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Routing: one workgroup of 256 threads (4 waves) ranks 1024 tokens as 16 groups of 64.
+constexpr int kRouteThreads = 256;
+constexpr int kRouteTokens = 1024;
+constexpr int kRouteGroups = kRouteTokens / 64;
+constexpr int kMaxExperts = 64;
+constexpr int kScanThreads = 1024;
+
+// Aux loss: one workgroup of 256 threads covers 1024 tokens.
+constexpr int kAuxThreads = 256;
+constexpr int kAuxTokens = 1024;
+
+enum KernelId {
+    K_ROUTE = 0, K_SCAN, K_SCATTER, K_FWD_GEMM, K_DX_GEMM, K_DW_GEMM, K_REDUCE,
+    K_AUX_ROWS, K_AUX_FINAL, K_COUNT
+};
+
+// Workspace layout for one (T, H, N_E, act).  Every section starts on a 256-byte boundary.
+struct Plan {
+    int64_t T = 0;
+    int H = 0, NE = 0, act = 0;
+    int n_rblk = 0;       // routing blocks
+    int chunk = 0;        // tokens per d_W chunk
+    int n_chunk_max = 0;  // upper bound of sum_e ceil(c_e / chunk)
+    int n_ablk = 0;       // aux blocks
+    size_t off_hist = 0, off_blkbase = 0, off_idx = 0, off_counts = 0, off_offsets = 0;
+    size_t off_pdw = 0, off_pdb = 0, off_paux = 0;
+    size_t total = 0;
+};
+
+Plan make_plan(int64_t T, int H, int NE, int act);
+
+// Launch timer hook (moe_set_launch_timer): brackets launches of one kernel with events.
+struct TimerScope {
+    hipStream_t s;
+    bool on;
+    TimerScope(KernelId k, hipStream_t s);
+    ~TimerScope();
+};
+
+// ---- launchers (each returns the hipError_t of its launch) ----
+hipError_t launch_route(const float* G, int64_t T, int NE, int32_t* idx, int32_t* hist,
+                        int n_rblk, hipStream_t s);
+hipError_t launch_scan(const int32_t* hist, int n_rblk, int NE, int32_t* blkbase,
+                       int32_t* counts, int32_t* offsets, hipStream_t s);
+hipError_t launch_scatter(const int32_t* idx, int64_t T, int NE, const int32_t* blkbase,
+                          int32_t* perm, int n_rblk, hipStream_t s);
+
+hipError_t launch_fwd_gemm_f32(const float* X, const float* W, const float* bias, float* Y,
+                               const int32_t* offsets, const int32_t* perm, int64_t T, int H, int NE,
+                               hipStream_t s);
+hipError_t launch_dx_gemm_f32(const float* dY, const float* W, float* dX, int accumulate,
+                              const int32_t* offsets, const int32_t* perm, int64_t T, int H, int NE,
+                              hipStream_t s);
+hipError_t launch_dw_gemm_f32(const float* dY, const float* X, float* part_dw, float* part_db,
+                              const int32_t* offsets, const int32_t* perm, int H, int NE, int chunk,
+                              int n_chunk_max, hipStream_t s);
+// bf16 storage (raw uint16 patterns), fp32 accumulation
+hipError_t launch_fwd_gemm_bf16(const uint16_t* X, const uint16_t* W, const float* bias, uint16_t* Y,
+                                const int32_t* offsets, const int32_t* perm, int64_t T, int H, int NE,
+                                hipStream_t s);
+hipError_t launch_dx_gemm_bf16(const uint16_t* dY, const uint16_t* W, uint16_t* dX, int accumulate,
+                               const int32_t* offsets, const int32_t* perm, int64_t T, int H, int NE,
+                               hipStream_t s);
+hipError_t launch_dw_gemm_bf16(const uint16_t* dY, const uint16_t* X, float* part_dw, float* part_db,
+                               const int32_t* offsets, const int32_t* perm, int H, int NE, int chunk,
+                               int n_chunk_max, hipStream_t s);
+hipError_t launch_reduce_dw(const float* part_dw, const float* part_db, const int32_t* offsets,
+                            int H, int NE, int chunk, float* dW, float* db, hipStream_t s);
+
+hipError_t launch_aux_rows(const float* G, const int32_t* counts, int64_t T, int NE, float lam,
+                           float* dG, float* probs, float* part, int n_ablk, hipStream_t s);
+hipError_t launch_aux_final(const float* part, const int32_t* counts, int n_ablk, int64_t T, int NE,
+                            float lam, float* loss, float* frac, float* mean_prob, hipStream_t s);
+
+}  // namespace moe

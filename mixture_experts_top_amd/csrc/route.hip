@@ -1,0 +1,210 @@
+// Routing and the stable counting sort by expert.
+//
+// Top-1 routing follows the MoE-gate commit page ("11b96dac6a"), summary and
+// PERFORMANCE blocks: each (b, h) token goes to the expert with the largest gate logit.
+// The page lets one thread scan the logits serially; a strict ">" scan upward from
+// expert 0 gives the lowest index among equal maxima, and every thread here does the
+// same scan for its own token.
+//
+// The counting sort (histogram -> scan -> scatter) has no counterpart on the pages; it
+// groups the tokens of each expert so that the expert linears become dense GEMMs.
+// Ranks inside a block come from wavefront ballots (lane order = token order), so the
+// permutation is stable and no atomics are used anywhere.
+#include "moe_internal.hpp"
+
+namespace moe {
+
+__device__ __forceinline__ int argmax_row(const float* __restrict__ g, int NE) {
+    float best = g[0];
+    int e_best = 0;
+    for (int e = 1; e < NE; ++e) {
+        float v = g[e];
+        if (v > best) { best = v; e_best = e; }
+    }
+    return e_best;
+}
+
+__device__ __forceinline__ int argmax_row4(const float* __restrict__ g, int NE) {
+    // NE % 4 == 0 and the row is 16-byte aligned.
+    const f32x4* g4 = reinterpret_cast<const f32x4*>(g);
+    f32x4 v = g4[0];
+    float best = v.x;
+    int e_best = 0;
+    if (v.y > best) { best = v.y; e_best = 1; }
+    if (v.z > best) { best = v.z; e_best = 2; }
+    if (v.w > best) { best = v.w; e_best = 3; }
+    for (int q = 1; q < NE / 4; ++q) {
+        v = g4[q];
+        if (v.x > best) { best = v.x; e_best = 4 * q; }
+        if (v.y > best) { best = v.y; e_best = 4 * q + 1; }
+        if (v.z > best) { best = v.z; e_best = 4 * q + 2; }
+        if (v.w > best) { best = v.w; e_best = 4 * q + 3; }
+    }
+    return e_best;
+}
+
+// Ranks each lane's expert among the lanes of its wave with the same expert.
+// Returns the rank (number of lower lanes with the same expert); for every expert that
+// occurs, the lowest such lane stores the wave's count into cnt[e].
+// e < 0 marks an inactive lane.
+__device__ __forceinline__ int wave_rank(int e, int* cnt) {
+    const int lane = __lane_id();
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    uint64_t active = __ballot(e >= 0);
+    int rank = 0;
+    while (active) {
+        const int leader = __ffsll((unsigned long long)active) - 1;
+        const int el = __builtin_amdgcn_readlane(e, leader);
+        const uint64_t m = __ballot(e == el);
+        if (e == el) rank = __popcll(m & lt);
+        if (lane == leader) cnt[el] = __popcll(m);
+        active &= ~m;
+    }
+    return rank;
+}
+
+// One block: tokens [blk*1024, blk*1024+1024).  Writes expert_idx (if non-null) and the
+// block's histogram hist[blk, :].
+__global__ __launch_bounds__(kRouteThreads) void k_route(const float* __restrict__ G, int T, int NE,
+                                                         int* __restrict__ idx_out,
+                                                         int* __restrict__ hist) {
+    __shared__ int cnt[kRouteGroups][kMaxExperts];
+    const int tid = threadIdx.x;
+    for (int i = tid; i < kRouteGroups * kMaxExperts; i += kRouteThreads) (&cnt[0][0])[i] = 0;
+    __syncthreads();
+    const int wave = tid / 64, lane = tid % 64;
+    const int64_t base = (int64_t)blockIdx.x * kRouteTokens;
+    const bool vec = (NE % 4) == 0;
+    for (int g = wave; g < kRouteGroups; g += kRouteThreads / 64) {
+        const int64_t t = base + g * 64 + lane;
+        int e = -1;
+        if (t < T) {
+            const float* row = G + t * NE;
+            e = vec ? argmax_row4(row, NE) : argmax_row(row, NE);
+            if (idx_out) idx_out[t] = e;
+        }
+        wave_rank(e, cnt[g]);
+    }
+    __syncthreads();
+    if (tid < NE) {
+        int s = 0;
+        for (int g = 0; g < kRouteGroups; ++g) s += cnt[g][tid];
+        hist[(int64_t)blockIdx.x * NE + tid] = s;
+    }
+}
+
+// One workgroup of 1024 threads.  Thread (s, e) owns a contiguous segment of blocks for
+// expert e; segment totals are scanned in LDS, then every block gets its global base
+// position blkbase[blk, e] = offsets[e] + (tokens of expert e in earlier blocks).
+__global__ __launch_bounds__(kScanThreads) void k_scan(const int* __restrict__ hist, int nblk, int NE,
+                                                       int* __restrict__ blkbase,
+                                                       int* __restrict__ counts,
+                                                       int* __restrict__ offsets) {
+    __shared__ int tot[kScanThreads];
+    __shared__ int ex_off[kMaxExperts + 1];
+    int nep = 1;
+    while (nep < NE) nep <<= 1;
+    const int S = kScanThreads / nep;  // segments per expert
+    const int tid = threadIdx.x;
+    const int e = tid % nep, s = tid / nep;
+    const int L = (nblk + S - 1) / S;
+    const int b0 = min(nblk, s * L), b1 = min(nblk, b0 + L);
+    int sum = 0;
+    if (e < NE)
+        for (int b = b0; b < b1; ++b) sum += hist[(int64_t)b * NE + e];
+    tot[s * nep + e] = sum;
+    __syncthreads();
+    // inclusive scan over s for each e (Hillis-Steele)
+    for (int d = 1; d < S; d <<= 1) {
+        int v = (s >= d) ? tot[(s - d) * nep + e] : 0;
+        __syncthreads();
+        tot[s * nep + e] += v;
+        __syncthreads();
+    }
+    if (tid == 0) {
+        int acc = 0;
+        ex_off[0] = 0;
+        for (int x = 0; x < NE; ++x) {
+            int c = tot[(S - 1) * nep + x];
+            counts[x] = c;
+            acc += c;
+            ex_off[x + 1] = acc;
+        }
+        for (int x = 0; x <= NE; ++x) offsets[x] = ex_off[x];
+    }
+    __syncthreads();
+    if (e < NE) {
+        int run = ex_off[e] + ((s > 0) ? tot[(s - 1) * nep + e] : 0);
+        for (int b = b0; b < b1; ++b) {
+            blkbase[(int64_t)b * NE + e] = run;
+            run += hist[(int64_t)b * NE + e];
+        }
+    }
+}
+
+// Same block decomposition as k_route.  Recomputes the in-block ranks from expert_idx
+// and writes perm[blkbase[blk, e] + rank] = t.
+__global__ __launch_bounds__(kRouteThreads) void k_scatter(const int* __restrict__ idx, int T, int NE,
+                                                           const int* __restrict__ blkbase,
+                                                           int* __restrict__ perm) {
+    __shared__ int cnt[kRouteGroups][kMaxExperts];
+    __shared__ int bb[kMaxExperts];
+    const int tid = threadIdx.x;
+    for (int i = tid; i < kRouteGroups * kMaxExperts; i += kRouteThreads) (&cnt[0][0])[i] = 0;
+    if (tid < NE) bb[tid] = blkbase[(int64_t)blockIdx.x * NE + tid];
+    __syncthreads();
+    const int wave = tid / 64, lane = tid % 64;
+    const int64_t base = (int64_t)blockIdx.x * kRouteTokens;
+    constexpr int GPW = kRouteGroups / (kRouteThreads / 64);  // groups per wave
+    int my_e[GPW], my_rank[GPW];
+#pragma unroll
+    for (int j = 0; j < GPW; ++j) {
+        const int g = wave + j * (kRouteThreads / 64);
+        const int64_t t = base + g * 64 + lane;
+        const int e = (t < T) ? idx[t] : -1;
+        my_e[j] = e;
+        my_rank[j] = wave_rank(e, cnt[g]);
+    }
+    __syncthreads();
+    // exclusive prefix over groups, per expert
+    if (tid < NE) {
+        int run = 0;
+        for (int g = 0; g < kRouteGroups; ++g) {
+            int c = cnt[g][tid];
+            cnt[g][tid] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < GPW; ++j) {
+        const int g = wave + j * (kRouteThreads / 64);
+        const int e = my_e[j];
+        if (e >= 0) {
+            const int64_t t = base + g * 64 + lane;
+            perm[bb[e] + cnt[g][e] + my_rank[j]] = (int)t;
+        }
+    }
+}
+
+hipError_t launch_route(const float* G, int64_t T, int NE, int32_t* idx, int32_t* hist, int n_rblk,
+                        hipStream_t s) {
+    hipLaunchKernelGGL(k_route, dim3(n_rblk), dim3(kRouteThreads), 0, s, G, (int)T, NE, idx, hist);
+    return hipGetLastError();
+}
+
+hipError_t launch_scan(const int32_t* hist, int n_rblk, int NE, int32_t* blkbase, int32_t* counts,
+                       int32_t* offsets, hipStream_t s) {
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(kScanThreads), 0, s, hist, n_rblk, NE, blkbase, counts,
+                       offsets);
+    return hipGetLastError();
+}
+
+hipError_t launch_scatter(const int32_t* idx, int64_t T, int NE, const int32_t* blkbase, int32_t* perm,
+                          int n_rblk, hipStream_t s) {
+    hipLaunchKernelGGL(k_scatter, dim3(n_rblk), dim3(kRouteThreads), 0, s, idx, (int)T, NE, blkbase,
+                       perm);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,109 @@
+"""Runs the HIP path (through the C ABI binding) on workloads.Inputs and returns host arrays.
+
+Imports no oracle code: the parity tests compare what this returns with the oracle.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+import mixture_experts_top_amd as moe
+
+
+def dev_act(arr_f32: np.ndarray, bits: Optional[np.ndarray], device="cuda") -> torch.Tensor:
+    if bits is not None:
+        return torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(arr_f32)).to(device)
+
+
+def to_host(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return (t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+    return t.cpu().numpy()
+
+
+@dataclass
+class DevInputs:
+    x: torch.Tensor
+    g: torch.Tensor
+    W: torch.Tensor
+    b: torch.Tensor
+    dy: torch.Tensor
+    lam: float
+
+
+def upload(inp, device="cuda") -> DevInputs:
+    return DevInputs(
+        x=dev_act(inp.fused_ctx, inp.fused_ctx_bits, device),
+        g=torch.from_numpy(inp.gate_logits).to(device),
+        W=dev_act(inp.W, inp.W_bits, device),
+        b=torch.from_numpy(inp.b).to(device),
+        dy=dev_act(inp.d_out, inp.d_out_bits, device),
+        lam=inp.wl.lam,
+    )
+
+
+class Buffers:
+    """Output buffers + workspace for one shape, reusable across calls."""
+
+    def __init__(self, d: DevInputs, poison: bool = True):
+        B, NH, H = d.x.shape
+        NE = d.W.shape[0]
+        T = B * NH
+        dev = d.x.device
+        act = moe.DTYPE_BF16 if d.x.dtype == torch.bfloat16 else moe.DTYPE_F32
+        self.y = torch.empty_like(d.x)
+        self.idx = torch.empty(T, dtype=torch.int32, device=dev)
+        self.counts = torch.empty(NE, dtype=torch.int32, device=dev)
+        self.offsets = torch.empty(NE + 1, dtype=torch.int32, device=dev)
+        self.perm = torch.empty(T, dtype=torch.int32, device=dev)
+        self.dx = torch.empty_like(d.x)
+        self.dW = torch.empty(NE, H, H, dtype=torch.float32, device=dev)
+        self.db = torch.empty(NE, H, dtype=torch.float32, device=dev)
+        self.loss = torch.empty(1, dtype=torch.float32, device=dev)
+        self.dg = torch.empty_like(d.g)
+        self.frac = torch.empty(NE, dtype=torch.float32, device=dev)
+        self.mean_prob = torch.empty(NE, dtype=torch.float32, device=dev)
+        self.probs = torch.empty_like(d.g)
+        self.ws = torch.empty(moe.moe_workspace_bytes(B, NH, H, NE, act), dtype=torch.uint8, device=dev)
+        if poison:  # every output must be written by the library: start from NaN / -1
+            for t in (self.y, self.dx, self.dW, self.db, self.loss, self.dg, self.frac, self.mean_prob, self.probs):
+                t.fill_(float("nan"))
+            for t in (self.idx, self.counts, self.offsets, self.perm):
+                t.fill_(-1)
+            self.ws.fill_(0xFF)
+
+
+def fwd(d: DevInputs, o: Buffers):
+    moe.moe_top1_fwd(d.x, d.g, d.W, d.b, o.y, o.idx, o.counts, o.offsets, o.perm, workspace=o.ws)
+
+
+def bwd(d: DevInputs, o: Buffers, accumulate=False):
+    moe.moe_top1_bwd(d.dy, d.x, d.W, o.offsets, o.perm, o.dx, o.dW, o.db, accumulate_dx=accumulate, workspace=o.ws)
+
+
+def aux(d: DevInputs, o: Buffers, counts=True, lam=None):
+    moe.moe_aux_loss(d.g, o.counts if counts else None, d.lam if lam is None else lam, o.loss, o.dg,
+                     frac=o.frac, mean_prob=o.mean_prob, probs=o.probs, workspace=o.ws)
+
+
+def step(d: DevInputs, o: Buffers):
+    fwd(d, o)
+    bwd(d, o)
+    aux(d, o)
+
+
+def snapshot(o: Buffers) -> dict:
+    torch.cuda.synchronize()
+    return {k: to_host(getattr(o, k)) for k in
+            ("y", "idx", "counts", "offsets", "perm", "dx", "dW", "db", "loss", "dg", "frac", "mean_prob", "probs")}
+
+
+def run(inp, device="cuda") -> dict:
+    d = upload(inp, device)
+    o = Buffers(d)
+    step(d, o)
+    return snapshot(o)

@@ -1,0 +1,29 @@
+"""Bitwise reproducibility: no atomics, fixed reduction orders."""
+import numpy as np
+import pytest
+
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("wl", [workloads.workload(2), workloads.custom(173, 7, 256, 5),
+                                workloads.custom(1000, 5, 128, 8, gate_bias={4: 2.5}, lam=0.05)],
+                         ids=["pages_shape", "ragged_H256_NE5", "skewed"])
+def test_repeats_are_bitwise_identical(gpu_lib, wl):
+    from tests import gpu_run
+    inp = workloads.make_inputs(wl)
+    other = workloads.make_inputs(workloads.custom(37, 3, 64, 3))
+    d = gpu_run.upload(inp)
+    d2 = gpu_run.upload(other)
+    o = gpu_run.Buffers(d)
+    o2 = gpu_run.Buffers(d2)
+    gpu_run.step(d, o)
+    ref = gpu_run.snapshot(o)
+    for rep in range(10):
+        gpu_run.step(d2, o2)  # interleave another shape
+        o_new = gpu_run.Buffers(d)
+        gpu_run.step(d, o_new)
+        got = gpu_run.snapshot(o_new)
+        for k, v in ref.items():
+            assert np.array_equal(v.view(np.uint8), got[k].view(np.uint8)), f"repeat {rep}: {k} differs"

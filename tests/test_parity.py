@@ -1,0 +1,192 @@
+"""Parity of the HIP path (called through the C ABI) with the fp64 CPU oracle.
+
+Small shapes are compared element by element on every output; they span several
+128-row tiles, several d_W chunks per expert and ragged tails.  The full-size workloads
+are compared in the launch configuration the benchmark times: completely where the
+oracle is quick, and on sampled rows otherwise.
+"""
+import numpy as np
+import pytest
+
+import workloads
+from oracle import moe_oracle as O
+from tests import compare as C
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle(inp, lam=None):
+    return O.run_all(inp, lam)
+
+
+def check_routing(got, f):
+    C.exact("expert_idx", got["idx"], f.expert_idx)
+    C.exact("counts", got["counts"], f.counts)
+    C.exact("offsets", got["offsets"], f.offsets)
+    C.exact("perm", got["perm"], f.perm)
+
+
+def check_all(inp, got, lam=None):
+    f, bw, a = _oracle(inp, lam)
+    check_routing(got, f)
+    T, H = f.routed_ctx.shape
+    if inp.wl.act == "bf16":
+        C.bf16_scaled("routed_ctx", got["y"].reshape(T, H), f.routed_ctx)
+        C.bf16_scaled("d_fused_ctx", got["dx"].reshape(T, H), bw.d_fused_ctx)
+        C.bf16_scaled("d_W", got["dW"], bw.d_W, per_expert=True)
+        C.bf16_scaled("d_b", got["db"], bw.d_b, per_expert=True)
+    else:
+        C.elementwise("routed_ctx", got["y"].reshape(T, H), f.routed_ctx)
+        C.elementwise("d_fused_ctx", got["dx"].reshape(T, H), bw.d_fused_ctx)
+        C.per_expert_scaled("d_W", got["dW"], bw.d_W)
+        C.per_expert_scaled("d_b", got["db"], bw.d_b)
+    empty = f.counts == 0
+    assert np.all(got["dW"][empty] == 0) and not np.signbit(got["dW"][empty]).any(), "inactive expert d_W not +0.0"
+    assert np.all(got["db"][empty] == 0) and not np.signbit(got["db"][empty]).any(), "inactive expert d_b not +0.0"
+    check_aux(inp, got, a, f.counts)
+
+
+def check_aux(inp, got, a, counts):
+    NE = counts.shape[0]
+    T = int(counts.sum())
+    C.elementwise("loss", got["loss"][0], a.loss)
+    C.elementwise("mean_prob", got["mean_prob"], a.mean_prob)
+    C.elementwise("probs", got["probs"].reshape(T, NE), a.probs)
+    C.frac_ulp("frac", got["frac"], counts, T)
+    scale = T / (inp.wl.lam * NE)
+    C.elementwise("d_gate_logits * T/(lambda N_E)", got["dg"].reshape(T, NE) * scale, a.d_gate_logits * scale)
+
+
+SMALL = {
+    "tiny_ref_ties": workloads.workload(1),
+    "ragged_H128_NE3": workloads.custom(173, 7, 128, 3),
+    "ragged_H64_NE5": workloads.custom(97, 5, 64, 5),
+    "H256_NE8": workloads.custom(61, 9, 256, 8),
+    "H512_NE4": workloads.custom(40, 6, 512, 4),
+    "dense_NE1": workloads.custom(300, 5, 128, 1),
+    "single_token": workloads.custom(1, 1, 128, 4),
+    "NE64_many_empty": workloads.custom(50, 4, 64, 64),
+    "NE7_H256_int_ties": workloads.custom(80, 5, 256, 7, gate="int"),
+    "empty_expert": workloads.custom(64, 5, 128, 4, gate_bias={2: -1.0e4}),
+    "skewed_lam005": workloads.custom(1000, 5, 128, 8, gate_bias={4: 2.5}, lam=0.05),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_small_full_parity(gpu_lib, name):
+    from tests import gpu_run
+    inp = workloads.make_inputs(SMALL[name])
+    print(f"[parity] {name} {SMALL[name]}", flush=True)
+    check_all(inp, gpu_run.run(inp))
+
+
+def test_all_logits_equal_route_to_expert_zero(gpu_lib):
+    from tests import gpu_run
+    inp = workloads.make_inputs(workloads.custom(33, 5, 128, 6))
+    inp.gate_logits[...] = 0.5
+    got = gpu_run.run(inp)
+    assert (got["idx"] == 0).all()
+    assert list(got["counts"]) == [165, 0, 0, 0, 0, 0]
+    check_all(inp, got)
+
+
+def test_route_entry_point_matches_fwd_routing(gpu_lib):
+    import torch
+    import mixture_experts_top_amd as moe
+    from tests import gpu_run
+    inp = workloads.make_inputs(workloads.workload(3, B=4096))
+    d = gpu_run.upload(inp)
+    T, NE = inp.wl.T, inp.wl.NE
+    idx = torch.full((T,), -1, dtype=torch.int32, device="cuda")
+    cnt = torch.full((NE,), -1, dtype=torch.int32, device="cuda")
+    off = torch.full((NE + 1,), -1, dtype=torch.int32, device="cuda")
+    perm = torch.full((T,), -1, dtype=torch.int32, device="cuda")
+    moe.moe_top1_route(d.g, idx, cnt, off, perm)
+    e = O.route(inp.gate_logits, NE)
+    counts, offsets, p = O.group(e, NE)
+    C.exact("idx", idx.cpu().numpy(), e)
+    C.exact("counts", cnt.cpu().numpy(), counts)
+    C.exact("offsets", off.cpu().numpy(), offsets)
+    C.exact("perm", perm.cpu().numpy(), p)
+
+
+def test_accumulate_dx(gpu_lib):
+    import torch
+    from tests import gpu_run
+    inp = workloads.make_inputs(workloads.custom(70, 5, 128, 4))
+    d = gpu_run.upload(inp)
+    o = gpu_run.Buffers(d)
+    gpu_run.fwd(d, o)
+    prev = np.random.default_rng(5).standard_normal(inp.fused_ctx.shape).astype(np.float32)
+    o.dx.copy_(torch.from_numpy(prev))
+    gpu_run.bwd(d, o, accumulate=True)
+    got = gpu_run.snapshot(o)
+    f = O.forward(inp.fused_ctx, inp.gate_logits, inp.W, inp.b)
+    bw = O.backward(inp.d_out, inp.fused_ctx, inp.W, f.expert_idx, prev)
+    C.elementwise("d_fused_ctx (accumulate)", got["dx"].reshape(bw.d_fused_ctx.shape), bw.d_fused_ctx)
+
+
+def test_aux_without_counts_recomputes_them(gpu_lib):
+    from tests import gpu_run
+    inp = workloads.make_inputs(workloads.custom(500, 5, 64, 6, lam=0.02))
+    d = gpu_run.upload(inp)
+    o = gpu_run.Buffers(d)
+    gpu_run.aux(d, o, counts=False)
+    got = gpu_run.snapshot(o)
+    e = O.route(inp.gate_logits, 6)
+    counts, _, _ = O.group(e, 6)
+    a = O.aux(inp.gate_logits, counts, 0.02)
+    check_aux(inp, got, a, counts)
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+@pytest.mark.slow
+@pytest.mark.parametrize("k", [2, 3])
+def test_workload_full_parity(gpu_lib, k):
+    from tests import gpu_run
+    wl = workloads.workload(k)
+    print(f"[parity] workload {k} {wl}", flush=True)
+    inp = workloads.make_inputs(wl)
+    check_all(inp, gpu_run.run(inp))
+
+
+@pytest.mark.slow
+def test_large_stress_sampled_parity(gpu_lib):
+    """1,048,576 tokens, H=256, N_E=16: routing and the aux pass in full; routed_ctx and
+    d_fused_ctx on sampled tokens; d_b in full; d_W on sampled output rows of every expert."""
+    from tests import gpu_run
+    wl = workloads.workload(5)
+    print(f"[parity] workload 5 {wl}", flush=True)
+    inp = workloads.make_inputs(wl)
+    got = gpu_run.run(inp)
+    T, H, NE = wl.T, wl.H, wl.NE
+    e = O.route(inp.gate_logits, NE)
+    counts, offsets, perm = O.group(e, NE)
+    C.exact("expert_idx", got["idx"], e)
+    C.exact("counts", got["counts"], counts)
+    C.exact("offsets", got["offsets"], offsets)
+    C.exact("perm", got["perm"], perm)
+    rng = np.random.default_rng(123)
+    rows = np.sort(rng.choice(T, 4096, replace=False))
+    rows = np.concatenate([rows, [0, T - 1], perm[offsets[1:-1] - 1], perm[offsets[1:-1]]])
+    X = inp.fused_ctx.reshape(T, H)
+    dY = inp.d_out.reshape(T, H)
+    fs = O.forward(X[rows], inp.gate_logits.reshape(T, NE)[rows], inp.W, inp.b)
+    C.elementwise("routed_ctx[sample]", got["y"].reshape(T, H)[rows], fs.routed_ctx)
+    bs = O.backward(dY[rows], X[rows], inp.W, e[rows])
+    C.elementwise("d_fused_ctx[sample]", got["dx"].reshape(T, H)[rows], bs.d_fused_ctx)
+    # d_b in full and d_W on 8 sampled output rows per expert, tolerance scaled by the
+    # RMS of the sampled slice
+    gdW, gdb = got["dW"], got["db"]
+    db = np.zeros((NE, H))
+    for x in range(NE):
+        S = perm[offsets[x]:offsets[x + 1]]
+        dYe = dY[S].astype(np.float64)
+        db[x] = dYe.sum(axis=0)
+        orows = rng.choice(H, 8, replace=False)
+        ref = dYe[:, orows].T @ X[S].astype(np.float64)
+        C.per_expert_scaled(f"d_W[{x}][sampled rows]", gdW[x][orows][None], ref[None])
+    C.per_expert_scaled("d_b", gdb, db)
+    a = O.aux(inp.gate_logits, counts, wl.lam)
+    check_aux(inp, got, a, counts)
