@@ -63,6 +63,35 @@ def pass_roofline_us(wl):
     return {"fwd": max(fb / bw, ff / pk) * 1e6, "bwd": max(bb / bw, bf / pk) * 1e6, "aux": ab / bw * 1e6}
 
 
+KERNEL_SOURCES = {"fwd_gemm": "gemm", "dx_gemm": "gemm", "dw_gemm": "gemm", "route": "route.hip",
+                  "scan": "route.hip", "scatter": "route.hip", "reduce": "reduce.hip", "aux_rows": "aux.hip",
+                  "aux_final": "aux.hip", "w_transpose": "gemm_bf16.hip"}
+
+
+def kernel_source_digest(kernel, act):
+    """sha256 of the HIP source that holds a kernel (for matching stored counter readings)."""
+    import hashlib
+    src = KERNEL_SOURCES[kernel]
+    if src == "gemm":
+        src = "gemm_bf16.hip" if act == "bf16" else "gemm_f32.hip"
+    path = os.path.join(ROOT, "mixture_experts_top_amd", "csrc", src)
+    with open(path, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()
+
+
+def measured_traffic(kernel, wl):
+    """HBM bytes per launch from the stored rocprofv3 FETCH_SIZE / WRITE_SIZE readings, scaled
+    by a plain copy's readings; None if there is none or the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{wl.name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_sha256") != kernel_source_digest(kernel, wl.act):
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
 def cpu_baseline(inp, budget_s=12.0):
     """The oracle as it stands, on this host's cores, over a bounded sample of the workload."""
     import numpy as np
@@ -104,6 +133,11 @@ def main():
     ap.add_argument("--graph", action="store_true", help="replay the step as one captured HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run a plain device copy of this size first (counter calibration under rocprofv3 --pmc)")
+    ap.add_argument("--skip-kernel-survey", action="store_true",
+                    help="do not time every kernel first; time --kernel in the timed region")
+    ap.add_argument("--kernel", default=None, help="kernel timed live in the timed region (default: the slowest)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -131,6 +165,16 @@ def main():
     def step():
         gpu_run.step(d, o)
 
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy: {args.calib_copy_mib} MiB read + {args.calib_copy_mib} MiB written, 3 launches")
+        del src, dst
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -138,7 +182,7 @@ def main():
     # per-kernel averages (outside the timed region) to find the dominant kernel
     nk = 10
     kern_us = {}
-    for k in moe.KERNELS:
+    for k in ([] if args.skip_kernel_survey else moe.KERNELS):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nk)]
         for a, b in evs:
             a.record(); b.record()
@@ -149,8 +193,13 @@ def main():
         moe.moe_set_launch_timer(None)
         torch.cuda.synchronize()
         kern_us[k] = float(np.mean([a.elapsed_time(b) for a, b in evs]) * 1e3)
-    dom = max((k for k in kern_us if k in ("fwd_gemm", "dx_gemm", "dw_gemm", "aux_rows", "reduce")),
-              key=lambda k: kern_us[k])
+    if args.kernel:
+        dom = args.kernel
+    elif kern_us:
+        dom = max((k for k in kern_us if k in ("fwd_gemm", "dx_gemm", "dw_gemm", "aux_rows", "reduce")),
+                  key=lambda k: kern_us[k])
+    else:
+        dom = "fwd_gemm"
     log("[bench] kernel avg us: " + ", ".join(f"{k}={v:.2f}" for k, v in kern_us.items()) + f"; dominant={dom}")
 
     graph = None
@@ -188,7 +237,7 @@ def main():
     if graph is None:
         dom_us = float(np.mean([a.elapsed_time(b) for a, b in evs]) * 1e3)
     else:
-        dom_us = kern_us[dom]
+        dom_us = kern_us.get(dom, float("nan"))
     amount, unit, bound = algorithmic(dom, wl)
     if bound == "mfma":
         achieved = amount / (dom_us * 1e-6) / 1e12
@@ -233,7 +282,7 @@ def main():
                    "lambda": wl.lam, "act": wl.act, "launch": "hip-graph" if graph is not None else "eager",
                    "parallelism": "single GPU"},
         "roofline": {"bound": bound, "kernel": dom, "achieved": achieved, "peak": peak, "unit": runit,
-                     "frac": achieved / peak, "traffic": None, "avg_launch_us": dom_us,
+                     "frac": achieved / peak, "traffic": measured_traffic(dom, wl), "avg_launch_us": dom_us,
                      "per_launch": f"{amount:.4g} {unit}"},
         "step_roofline_frac": step_roof_frac,
         "pass_us": pass_us,

@@ -172,7 +172,8 @@ enum {
     MOE_KERNEL_REDUCE = 6,
     MOE_KERNEL_AUX_ROWS = 7,
     MOE_KERNEL_AUX_FINAL = 8,
-    MOE_KERNEL_COUNT = 9
+    MOE_KERNEL_W_TRANSPOSE = 9,   /* bf16 backward only: W^T staged for the dX GEMM */
+    MOE_KERNEL_COUNT = 10
 };
 moe_status_t moe_set_launch_timer(int kernel_id, void* ev_start, void* ev_stop);
 

@@ -20,7 +20,8 @@ __all__ = [
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 DTYPE_F32, DTYPE_BF16 = 0, 1
-KERNELS = ["route", "scan", "scatter", "fwd_gemm", "dx_gemm", "dw_gemm", "reduce", "aux_rows", "aux_final"]
+KERNELS = ["route", "scan", "scatter", "fwd_gemm", "dx_gemm", "dw_gemm", "reduce", "aux_rows", "aux_final",
+           "w_transpose"]
 
 _lib: Optional[ctypes.CDLL] = None
 

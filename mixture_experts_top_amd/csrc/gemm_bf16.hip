@@ -1,19 +1,350 @@
-// bf16 grouped expert GEMMs (placeholder until the MFMA bf16 kernels land).
+// Grouped expert GEMMs with bf16 storage and fp32 accumulation (v_mfma_f32_32x32x16_bf16).
+//
+// Same operations as the fp32 kernels (MoE-gate commit page "11b96dac6a": the selected
+// expert's [H, H] linear plus bias forward; gradients through that expert only), for
+// activations and weights stored as bf16.  Accumulation is fp32; routed_ctx and
+// d_fused_ctx are rounded to bf16 (nearest even) when stored; d_W / d_b partials stay fp32.
+//
+// v_mfma_f32_32x32x16_bf16: lane l (half h = l / 32) supplies 8 consecutive k of row
+// m = l % 32 of A and of column n = l % 32 of B (k = 8h .. 8h+7); the fp32 result has the
+// same lane layout as the fp32 32x32 instruction.  Every operand is therefore one 16-byte
+// LDS read from a tile whose K dimension is contiguous:
+//   forward  A = X rows, B = W[e] rows (W is [out][in]: K = in is contiguous)
+//   dX       A = dY rows, B = W[e]^T rows, from a transposed copy of W made per call
+//   dW       A = dY^T, B = X^T: token rows are transposed in registers while staging
+//            (4 tokens x 8 features per thread) so K = tokens is contiguous in LDS.
 #include "moe_internal.hpp"
 
 namespace moe {
 
-hipError_t launch_fwd_gemm_bf16(const uint16_t*, const uint16_t*, const float*, uint16_t*, const int32_t*,
-                                const int32_t*, int64_t, int, int, hipStream_t) {
-    return hipErrorNotSupported;
+namespace {
+
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ f32x16 mfma_bf16(u16x8 a, u16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
 }
-hipError_t launch_dx_gemm_bf16(const uint16_t*, const uint16_t*, uint16_t*, int, const int32_t*, const int32_t*,
-                               int64_t, int, int, hipStream_t) {
-    return hipErrorNotSupported;
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;  // NaN stays NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
 }
-hipError_t launch_dw_gemm_bf16(const uint16_t*, const uint16_t*, float*, float*, const int32_t*, const int32_t*,
-                               int, int, int, int, hipStream_t) {
-    return hipErrorNotSupported;
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+__device__ __forceinline__ u16x8 ld8(const uint16_t* p) { return *reinterpret_cast<const u16x8*>(p); }
+__device__ __forceinline__ void st8(uint16_t* p, u16x8 v) { *reinterpret_cast<u16x8*>(p) = v; }
+
+__device__ __forceinline__ bool find_tile(const int* __restrict__ offsets, int NE, int mt, int bm, int& e, int& r0,
+                                          int& r1) {
+    int acc = 0;
+    for (int i = 0; i < NE; ++i) {
+        const int c0 = offsets[i], c1 = offsets[i + 1];
+        const int n = (c1 - c0 + bm - 1) / bm;
+        if (mt < acc + n) {
+            e = i;
+            r0 = c0 + (mt - acc) * bm;
+            r1 = min(c1, r0 + bm);
+            return true;
+        }
+        acc += n;
+    }
+    return false;
+}
+
+__device__ __forceinline__ void xcd_split(int bid, int per, int& major, int& minor) {
+    const int grp = bid / (8 * per), loc = bid % (8 * per);
+    major = grp * 8 + loc % 8;
+    minor = loc / 8;
+}
+
+}  // namespace
+
+// Wt[e][i][o] = W[e][o][i], 64 x 64 tiles through LDS.
+__global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restrict__ W, uint16_t* __restrict__ Wt,
+                                                        int H) {
+    __shared__ uint16_t tile[64][66];
+    const size_t base = (size_t)blockIdx.z * H * H;
+    const int bx = blockIdx.x * 64, by = blockIdx.y * 64;
+    const int tx = threadIdx.x % 64, ty = threadIdx.x / 64;
+    for (int r = ty; r < 64; r += 4) tile[r][tx] = W[base + (size_t)(by + r) * H + bx + tx];
+    __syncthreads();
+    for (int r = ty; r < 64; r += 4) Wt[base + (size_t)(bx + r) * H + by + tx] = tile[tx][r];
+}
+
+// Out[t, n0:n0+BN] = A[t, :] . Bw[e][n0:n0+BN, :]^T (+ bias[e] | + Out[t] when accumulating).
+template <int H, int BN, bool DX>
+__global__ __launch_bounds__(kThreads) void k_rows_bf16(const uint16_t* __restrict__ A,
+                                                         const uint16_t* __restrict__ Bw,
+                                                         const float* __restrict__ bias,
+                                                         uint16_t* __restrict__ Out,
+                                                         const int* __restrict__ offsets,
+                                                         const int* __restrict__ perm, int NE, int accumulate) {
+    constexpr int BM = 128, KC = 64, KP = KC + 8;
+    constexpr int NT = H / BN;
+    constexpr int WTM = BM / 2, WTN = BN / 2;
+    constexpr int SM = WTM / 32, SN = WTN / 32;
+    __shared__ uint16_t As[BM][KP];
+    __shared__ uint16_t Bs[BN][KP];
+    __shared__ int tok[BM];
+
+    int mt, nt;
+    xcd_split(blockIdx.x, NT, mt, nt);
+    int e, r0, r1;
+    if (!find_tile(offsets, NE, mt, BM, e, r0, r1)) return;
+    const int rows = r1 - r0;
+    const int tid = threadIdx.x;
+    if (tid < BM) tok[tid] = (tid < rows) ? perm[r0 + tid] : -1;
+    __syncthreads();
+
+    const int n0 = nt * BN;
+    const uint16_t* __restrict__ Be = Bw + (size_t)e * H * H;
+    const int wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
+    const int wm = wave / 2, wn = wave % 2;
+
+    f32x16 acc[SM][SN];
+#pragma unroll
+    for (int i = 0; i < SM; ++i)
+#pragma unroll
+        for (int j = 0; j < SN; ++j) acc[i][j] = f32x16{};
+
+    for (int k0 = 0; k0 < H; k0 += KC) {
+#pragma unroll
+        for (int i = 0; i < BM / 32; ++i) {
+            const int r = tid / 8 + 32 * i, c = 8 * (tid % 8);
+            const int t = tok[r];
+            u16x8 v = u16x8{};
+            if (t >= 0) v = ld8(A + (size_t)t * H + k0 + c);
+            st8(&As[r][c], v);
+        }
+#pragma unroll
+        for (int i = 0; i < BN / 32; ++i) {
+            const int r = tid / 8 + 32 * i, c = 8 * (tid % 8);
+            st8(&Bs[r][c], ld8(Be + (size_t)(n0 + r) * H + k0 + c));
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < KC; kk += 16) {
+            u16x8 a[SM], b[SN];
+#pragma unroll
+            for (int i = 0; i < SM; ++i) a[i] = ld8(&As[wm * WTM + i * 32 + l32][kk + 8 * h]);
+#pragma unroll
+            for (int j = 0; j < SN; ++j) b[j] = ld8(&Bs[wn * WTN + j * 32 + l32][kk + 8 * h]);
+#pragma unroll
+            for (int i = 0; i < SM; ++i)
+#pragma unroll
+                for (int j = 0; j < SN; ++j) acc[i][j] = mfma_bf16(a[i], b[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int j = 0; j < SN; ++j) {
+        const int col = n0 + wn * WTN + j * 32 + l32;
+        const float bv = DX ? 0.0f : bias[(size_t)e * H + col];
+#pragma unroll
+        for (int i = 0; i < SM; ++i) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = wm * WTM + i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
+                const int t = tok[row];
+                if (t >= 0) {
+                    uint16_t* o = Out + (size_t)t * H + col;
+                    float v = acc[i][j][r] + bv;
+                    if (DX && accumulate) v = bf16_to_f32(*o) + v;
+                    *o = f32_to_bf16(v);
+                }
+            }
+        }
+    }
+}
+
+// d_W / d_b partials for one chunk of one expert's tokens, output tile [o0:o0+BT, i0:i0+BT].
+template <int H>
+__global__ __launch_bounds__(kThreads) void k_dw_bf16(const uint16_t* __restrict__ dY,
+                                                       const uint16_t* __restrict__ X,
+                                                       float* __restrict__ part_dw, float* __restrict__ part_db,
+                                                       const int* __restrict__ offsets,
+                                                       const int* __restrict__ perm, int NE, int chunk) {
+    constexpr int BT = (H >= 128) ? 128 : 64;
+    constexpr int NTI = H / BT, TPC = NTI * NTI;
+    constexpr int KC = 64, KP = KC + 8;
+    constexpr int WT = BT / 2, SUB = WT / 32;
+    constexpr int ITEMS = (KC / 4) * (BT / 8);  // (4 tokens x 8 features) blocks per stage
+    __shared__ uint16_t As[BT][KP];  // dY^T: [o][t]
+    __shared__ uint16_t Bs[BT][KP];  // X^T:  [i][t]
+
+    int c, tile;
+    xcd_split(blockIdx.x, TPC, c, tile);
+    int e = -1, t0 = 0, t1 = 0;
+    {
+        int acc = 0;
+        for (int i = 0; i < NE; ++i) {
+            const int c0 = offsets[i], c1 = offsets[i + 1];
+            const int n = (c1 - c0 + chunk - 1) / chunk;
+            if (c < acc + n) {
+                e = i;
+                t0 = c0 + (c - acc) * chunk;
+                t1 = min(c1, t0 + chunk);
+                break;
+            }
+            acc += n;
+        }
+    }
+    if (e < 0) return;
+    const int o0 = (tile / NTI) * BT, i0 = (tile % NTI) * BT;
+    const bool do_db = (tile % NTI) == 0;
+    const int tid = threadIdx.x;
+    const int wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
+    const int wm = wave / 2, wn = wave % 2;
+
+    f32x16 acc[SUB][SUB];
+#pragma unroll
+    for (int i = 0; i < SUB; ++i)
+#pragma unroll
+        for (int j = 0; j < SUB; ++j) acc[i][j] = f32x16{};
+    float dbacc = 0.0f;
+
+    for (int k0 = t0; k0 < t1; k0 += KC) {
+        for (int q = tid; q < ITEMS; q += kThreads) {
+            const int tq = q / (BT / 8), fq = q % (BT / 8);
+            u16x8 va[4], vb[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int k = k0 + 4 * tq + j;
+                va[j] = u16x8{};
+                vb[j] = u16x8{};
+                if (k < t1) {
+                    const size_t t = (size_t)perm[k];
+                    va[j] = ld8(dY + t * H + o0 + 8 * fq);
+                    vb[j] = ld8(X + t * H + i0 + 8 * fq);
+                }
+            }
+#pragma unroll
+            for (int f = 0; f < 8; ++f) {
+                uint2 wa, wb;
+                wa.x = (uint32_t)va[0][f] | ((uint32_t)va[1][f] << 16);
+                wa.y = (uint32_t)va[2][f] | ((uint32_t)va[3][f] << 16);
+                wb.x = (uint32_t)vb[0][f] | ((uint32_t)vb[1][f] << 16);
+                wb.y = (uint32_t)vb[2][f] | ((uint32_t)vb[3][f] << 16);
+                *reinterpret_cast<uint2*>(&As[8 * fq + f][4 * tq]) = wa;
+                *reinterpret_cast<uint2*>(&Bs[8 * fq + f][4 * tq]) = wb;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < KC; kk += 16) {
+            u16x8 a[SUB], b[SUB];
+#pragma unroll
+            for (int i = 0; i < SUB; ++i) a[i] = ld8(&As[wm * WT + i * 32 + l32][kk + 8 * h]);
+#pragma unroll
+            for (int j = 0; j < SUB; ++j) b[j] = ld8(&Bs[wn * WT + j * 32 + l32][kk + 8 * h]);
+#pragma unroll
+            for (int i = 0; i < SUB; ++i)
+#pragma unroll
+                for (int j = 0; j < SUB; ++j) acc[i][j] = mfma_bf16(a[i], b[j], acc[i][j]);
+        }
+        if (do_db && tid < BT) {
+#pragma unroll
+            for (int q = 0; q < KC / 8; ++q) {
+                const u16x8 v = ld8(&As[tid][8 * q]);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) dbacc += bf16_to_f32(v[j]);
+            }
+        }
+        __syncthreads();
+    }
+
+    float* __restrict__ P = part_dw + (size_t)c * H * H;
+#pragma unroll
+    for (int i = 0; i < SUB; ++i)
+#pragma unroll
+        for (int j = 0; j < SUB; ++j) {
+            const int col = i0 + wn * WT + j * 32 + l32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = o0 + wm * WT + i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
+                P[(size_t)row * H + col] = acc[i][j][r];
+            }
+        }
+    if (do_db && tid < BT) part_db[(size_t)c * H + o0 + tid] = dbacc;
+}
+
+// ---------------------------------------------------------------- launchers
+static inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+template <int H>
+static hipError_t rows_bf16(bool dx, const uint16_t* A, const uint16_t* Bw, const float* bias, uint16_t* Out,
+                            int accumulate, const int32_t* offsets, const int32_t* perm, int64_t T, int NE,
+                            hipStream_t s) {
+    constexpr int BN = (H >= 128) ? 128 : H;
+    constexpr int NT = H / BN;
+    const int mtiles = (int)((T + 127) / 128) + NE;
+    const int grid = round_up(mtiles, 8) * NT;
+    if (dx)
+        hipLaunchKernelGGL((k_rows_bf16<H, BN, true>), dim3(grid), dim3(kThreads), 0, s, A, Bw, bias, Out, offsets,
+                           perm, NE, accumulate);
+    else
+        hipLaunchKernelGGL((k_rows_bf16<H, BN, false>), dim3(grid), dim3(kThreads), 0, s, A, Bw, bias, Out, offsets,
+                           perm, NE, accumulate);
+    return hipGetLastError();
+}
+
+static hipError_t rows_bf16_dispatch(bool dx, const uint16_t* A, const uint16_t* Bw, const float* bias,
+                                     uint16_t* Out, int accumulate, const int32_t* offsets, const int32_t* perm,
+                                     int64_t T, int H, int NE, hipStream_t s) {
+    switch (H) {
+        case 64: return rows_bf16<64>(dx, A, Bw, bias, Out, accumulate, offsets, perm, T, NE, s);
+        case 128: return rows_bf16<128>(dx, A, Bw, bias, Out, accumulate, offsets, perm, T, NE, s);
+        case 256: return rows_bf16<256>(dx, A, Bw, bias, Out, accumulate, offsets, perm, T, NE, s);
+        case 512: return rows_bf16<512>(dx, A, Bw, bias, Out, accumulate, offsets, perm, T, NE, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_gemm_bf16(const uint16_t* X, const uint16_t* W, const float* bias, uint16_t* Y,
+                                const int32_t* offsets, const int32_t* perm, int64_t T, int H, int NE,
+                                hipStream_t s) {
+    return rows_bf16_dispatch(false, X, W, bias, Y, 0, offsets, perm, T, H, NE, s);
+}
+
+hipError_t launch_transpose_w_bf16(const uint16_t* W, uint16_t* Wt, int H, int NE, hipStream_t s) {
+    hipLaunchKernelGGL(k_transpose_bf16, dim3(H / 64, H / 64, NE), dim3(256), 0, s, W, Wt, H);
+    return hipGetLastError();
+}
+
+hipError_t launch_dx_gemm_bf16(const uint16_t* dY, const uint16_t* Wt, uint16_t* dX, int accumulate,
+                               const int32_t* offsets, const int32_t* perm, int64_t T, int H, int NE,
+                               hipStream_t s) {
+    return rows_bf16_dispatch(true, dY, Wt, nullptr, dX, accumulate, offsets, perm, T, H, NE, s);
+}
+
+template <int H>
+static hipError_t dw_bf16(const uint16_t* dY, const uint16_t* X, float* pdw, float* pdb, const int32_t* offsets,
+                          const int32_t* perm, int NE, int chunk, int n_chunk_max, hipStream_t s) {
+    constexpr int BT = (H >= 128) ? 128 : 64;
+    constexpr int TPC = (H / BT) * (H / BT);
+    const int grid = round_up(n_chunk_max, 8) * TPC;
+    hipLaunchKernelGGL((k_dw_bf16<H>), dim3(grid), dim3(kThreads), 0, s, dY, X, pdw, pdb, offsets, perm, NE,
+                       chunk);
+    return hipGetLastError();
+}
+
+hipError_t launch_dw_gemm_bf16(const uint16_t* dY, const uint16_t* X, float* pdw, float* pdb,
+                               const int32_t* offsets, const int32_t* perm, int H, int NE, int chunk,
+                               int n_chunk_max, hipStream_t s) {
+    switch (H) {
+        case 64: return dw_bf16<64>(dY, X, pdw, pdb, offsets, perm, NE, chunk, n_chunk_max, s);
+        case 128: return dw_bf16<128>(dY, X, pdw, pdb, offsets, perm, NE, chunk, n_chunk_max, s);
+        case 256: return dw_bf16<256>(dY, X, pdw, pdb, offsets, perm, NE, chunk, n_chunk_max, s);
+        case 512: return dw_bf16<512>(dY, X, pdw, pdb, offsets, perm, NE, chunk, n_chunk_max, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace moe

@@ -59,6 +59,7 @@ Plan make_plan(int64_t T, int H, int NE, int act) {
     p.off_paux = o;    o += align256((size_t)p.n_ablk * NE * 4);
     p.off_pdw = o;     o += align256((size_t)p.n_chunk_max * H * H * 4);
     p.off_pdb = o;     o += align256((size_t)p.n_chunk_max * H * 4);
+    p.off_wt = o;      o += (act == MOE_DTYPE_BF16) ? align256((size_t)NE * H * H * 2) : 0;
     p.total = o;
     return p;
 }
@@ -165,7 +166,7 @@ const char* moe_last_error(void) { return g_err; }
 
 const char* moe_kernel_name(int k) {
     static const char* names[K_COUNT] = {"route", "scan", "scatter", "fwd_gemm", "dx_gemm",
-                                         "dw_gemm", "reduce", "aux_rows", "aux_final"};
+                                         "dw_gemm", "reduce", "aux_rows", "aux_final", "w_transpose"};
     return (k >= 0 && k < K_COUNT) ? names[k] : nullptr;
 }
 
@@ -261,8 +262,10 @@ moe_status_t moe_top1_bwd(const void* d_routed_ctx, const void* fused_ctx, const
                                   perm, p.H, p.NE, p.chunk, p.n_chunk_max, s),
                "dw gemm");
     } else {
+        uint16_t* wt = at<uint16_t>(workspace, p.off_wt);
+        LAUNCH(K_W_TRANSPOSE, launch_transpose_w_bf16((const uint16_t*)W, wt, p.H, p.NE, s), "w transpose");
         LAUNCH(K_DX_GEMM,
-               launch_dx_gemm_bf16((const uint16_t*)d_routed_ctx, (const uint16_t*)W, (uint16_t*)d_fused_ctx,
+               launch_dx_gemm_bf16((const uint16_t*)d_routed_ctx, wt, (uint16_t*)d_fused_ctx,
                                    accumulate_dx, expert_offsets, perm, p.T, p.H, p.NE, s),
                "dx gemm");
         LAUNCH(K_DW_GEMM,

@@ -27,7 +27,7 @@ constexpr int kAuxTokens = 1024;
 
 enum KernelId {
     K_ROUTE = 0, K_SCAN, K_SCATTER, K_FWD_GEMM, K_DX_GEMM, K_DW_GEMM, K_REDUCE,
-    K_AUX_ROWS, K_AUX_FINAL, K_COUNT
+    K_AUX_ROWS, K_AUX_FINAL, K_W_TRANSPOSE, K_COUNT
 };
 
 // Workspace layout for one (T, H, N_E, act).  Every section starts on a 256-byte boundary.
@@ -39,7 +39,7 @@ struct Plan {
     int n_chunk_max = 0;  // upper bound of sum_e ceil(c_e / chunk)
     int n_ablk = 0;       // aux blocks
     size_t off_hist = 0, off_blkbase = 0, off_idx = 0, off_counts = 0, off_offsets = 0;
-    size_t off_pdw = 0, off_pdb = 0, off_paux = 0;
+    size_t off_pdw = 0, off_pdb = 0, off_paux = 0, off_wt = 0;
     size_t total = 0;
 };
 
@@ -74,6 +74,7 @@ hipError_t launch_dw_gemm_f32(const float* dY, const float* X, float* part_dw, f
 hipError_t launch_fwd_gemm_bf16(const uint16_t* X, const uint16_t* W, const float* bias, uint16_t* Y,
                                 const int32_t* offsets, const int32_t* perm, int64_t T, int H, int NE,
                                 hipStream_t s);
+hipError_t launch_transpose_w_bf16(const uint16_t* W, uint16_t* Wt, int H, int NE, hipStream_t s);
 hipError_t launch_dx_gemm_bf16(const uint16_t* dY, const uint16_t* W, uint16_t* dX, int accumulate,
                                const int32_t* offsets, const int32_t* perm, int64_t T, int H, int NE,
                                hipStream_t s);

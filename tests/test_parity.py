@@ -69,6 +69,10 @@ SMALL = {
     "NE7_H256_int_ties": workloads.custom(80, 5, 256, 7, gate="int"),
     "empty_expert": workloads.custom(64, 5, 128, 4, gate_bias={2: -1.0e4}),
     "skewed_lam005": workloads.custom(1000, 5, 128, 8, gate_bias={4: 2.5}, lam=0.05),
+    "bf16_H128_NE4": workloads.custom(200, 5, 128, 4, act="bf16"),
+    "bf16_H512_NE8": workloads.custom(64, 5, 512, 8, act="bf16"),
+    "bf16_H64_NE3_ties": workloads.custom(97, 5, 64, 3, act="bf16", gate="int"),
+    "bf16_H256_NE5": workloads.custom(150, 5, 256, 5, act="bf16"),
 }
 
 
@@ -126,6 +130,24 @@ def test_accumulate_dx(gpu_lib):
     C.elementwise("d_fused_ctx (accumulate)", got["dx"].reshape(bw.d_fused_ctx.shape), bw.d_fused_ctx)
 
 
+def test_accumulate_dx_bf16(gpu_lib):
+    import torch
+    from tests import gpu_run
+    inp = workloads.make_inputs(workloads.custom(70, 5, 256, 4, act="bf16"))
+    d = gpu_run.upload(inp)
+    o = gpu_run.Buffers(d)
+    gpu_run.fwd(d, o)
+    prev_bits = workloads.f32_to_bf16_bits(
+        np.random.default_rng(6).standard_normal(inp.fused_ctx.shape).astype(np.float32))
+    prev = workloads.bf16_bits_to_f32(prev_bits)
+    o.dx.copy_(gpu_run.dev_act(prev, prev_bits))
+    gpu_run.bwd(d, o, accumulate=True)
+    got = gpu_run.snapshot(o)
+    f = O.forward(inp.fused_ctx, inp.gate_logits, inp.W, inp.b)
+    bw = O.backward(inp.d_out, inp.fused_ctx, inp.W, f.expert_idx, prev)
+    C.bf16_scaled("d_fused_ctx (accumulate)", got["dx"].reshape(bw.d_fused_ctx.shape), bw.d_fused_ctx)
+
+
 def test_aux_without_counts_recomputes_them(gpu_lib):
     from tests import gpu_run
     inp = workloads.make_inputs(workloads.custom(500, 5, 64, 6, lam=0.02))
@@ -142,7 +164,7 @@ def test_aux_without_counts_recomputes_them(gpu_lib):
 # ------------------------------------------------------------------ full-size workloads
 
 @pytest.mark.slow
-@pytest.mark.parametrize("k", [2, 3])
+@pytest.mark.parametrize("k", [2, 3, 4])
 def test_workload_full_parity(gpu_lib, k):
     from tests import gpu_run
     wl = workloads.workload(k)
