@@ -85,15 +85,15 @@ def bwd(d: DevInputs, o: Buffers, accumulate=False):
     moe.moe_top1_bwd(d.dy, d.x, d.W, o.offsets, o.perm, o.dx, o.dW, o.db, accumulate_dx=accumulate, workspace=o.ws)
 
 
-def aux(d: DevInputs, o: Buffers, counts=True, lam=None):
+def aux(d: DevInputs, o: Buffers, counts=True, lam=None, probs=True):
     moe.moe_aux_loss(d.g, o.counts if counts else None, d.lam if lam is None else lam, o.loss, o.dg,
-                     frac=o.frac, mean_prob=o.mean_prob, probs=o.probs, workspace=o.ws)
+                     frac=o.frac, mean_prob=o.mean_prob, probs=o.probs if probs else None, workspace=o.ws)
 
 
-def step(d: DevInputs, o: Buffers):
+def step(d: DevInputs, o: Buffers, probs=True):
     fwd(d, o)
     bwd(d, o)
-    aux(d, o)
+    aux(d, o, probs=probs)
 
 
 def snapshot(o: Buffers) -> dict:
