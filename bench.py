@@ -36,13 +36,15 @@ def algorithmic(kernel, wl):
     """(amount, unit, bound) per launch: flops for the MFMA GEMMs, HBM bytes otherwise."""
     T, H, NE = wl.T, wl.H, wl.NE
     s = 2 if wl.act == "bf16" else 4
-    if kernel in ("fwd_gemm", "dx_gemm", "dw_gemm"):
+    if kernel == "fwd_gemm":
         return 2.0 * T * H * H, "flop", "mfma"
+    if kernel == "bwd_gemm":  # dX and dW in one launch
+        return 4.0 * T * H * H, "flop", "mfma"
     if kernel == "route":
         return T * NE * 4 + T * 4, "byte", "hbm"
     if kernel == "scatter":
         return T * 4 * 2, "byte", "hbm"
-    if kernel == "aux_rows":
+    if kernel == "aux":
         return 8.0 * T * NE, "byte", "hbm"
     if kernel == "reduce":
         return NE * H * H * 4 + NE * H * 4, "byte", "hbm"
@@ -63,9 +65,9 @@ def pass_roofline_us(wl):
     return {"fwd": max(fb / bw, ff / pk) * 1e6, "bwd": max(bb / bw, bf / pk) * 1e6, "aux": ab / bw * 1e6}
 
 
-KERNEL_SOURCES = {"fwd_gemm": "gemm", "dx_gemm": "gemm", "dw_gemm": "gemm", "route": "route.hip",
-                  "scan": "route.hip", "scatter": "route.hip", "reduce": "reduce.hip", "aux_rows": "aux.hip",
-                  "aux_final": "aux.hip", "w_transpose": "gemm_bf16.hip"}
+KERNEL_SOURCES = {"fwd_gemm": "gemm", "bwd_gemm": "gemm", "route": "route.hip", "scan": "route.hip",
+                  "scatter": "route.hip", "reduce": "reduce.hip", "aux": "aux.hip", "aux_final": "aux.hip",
+                  "w_transpose": "gemm_bf16.hip"}
 
 
 def kernel_source_digest(kernel, act):
@@ -196,7 +198,7 @@ def main():
     if args.kernel:
         dom = args.kernel
     elif kern_us:
-        dom = max((k for k in kern_us if k in ("fwd_gemm", "dx_gemm", "dw_gemm", "aux_rows", "reduce")),
+        dom = max((k for k in kern_us if k in ("fwd_gemm", "bwd_gemm", "aux", "reduce")),
                   key=lambda k: kern_us[k])
     else:
         dom = "fwd_gemm"

@@ -163,17 +163,16 @@ moe_status_t moe_aux_loss(const float* gate_logits, const int32_t* expert_counts
  * kernel_id < 0 to clear.  Process-wide setting; not thread-safe against concurrent calls.
  */
 enum {
-    MOE_KERNEL_ROUTE = 0,
-    MOE_KERNEL_SCAN = 1,
-    MOE_KERNEL_SCATTER = 2,
-    MOE_KERNEL_FWD_GEMM = 3,
-    MOE_KERNEL_DX_GEMM = 4,
-    MOE_KERNEL_DW_GEMM = 5,
-    MOE_KERNEL_REDUCE = 6,
-    MOE_KERNEL_AUX_ROWS = 7,
-    MOE_KERNEL_AUX_FINAL = 8,
-    MOE_KERNEL_W_TRANSPOSE = 9,   /* bf16 backward only: W^T staged for the dX GEMM */
-    MOE_KERNEL_COUNT = 10
+    MOE_KERNEL_ROUTE = 0,        /* argmax + per-block histogram */
+    MOE_KERNEL_SCAN = 1,         /* counts, offsets, per-block bases (large inputs) */
+    MOE_KERNEL_SCATTER = 2,      /* stable perm (small inputs: with the scan folded in) */
+    MOE_KERNEL_FWD_GEMM = 3,     /* grouped forward GEMM + bias */
+    MOE_KERNEL_BWD_GEMM = 4,     /* grouped dX GEMM and d_W / d_b chunk partials, one launch */
+    MOE_KERNEL_REDUCE = 5,       /* deterministic chunk reduction -> d_W, d_b */
+    MOE_KERNEL_AUX = 6,          /* softmax, dG, per-block column sums of p */
+    MOE_KERNEL_AUX_FINAL = 7,    /* mean_prob, frac, loss */
+    MOE_KERNEL_W_TRANSPOSE = 8,  /* bf16 backward only: W^T staged for the dX GEMM */
+    MOE_KERNEL_COUNT = 9
 };
 moe_status_t moe_set_launch_timer(int kernel_id, void* ev_start, void* ev_stop);
 

@@ -20,8 +20,7 @@ __all__ = [
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 DTYPE_F32, DTYPE_BF16 = 0, 1
-KERNELS = ["route", "scan", "scatter", "fwd_gemm", "dx_gemm", "dw_gemm", "reduce", "aux_rows", "aux_final",
-           "w_transpose"]
+KERNELS = ["route", "scan", "scatter", "fwd_gemm", "bwd_gemm", "reduce", "aux", "aux_final", "w_transpose"]
 
 _lib: Optional[ctypes.CDLL] = None
 

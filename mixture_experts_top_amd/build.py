@@ -41,29 +41,33 @@ COMMON = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON, "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-c", src, "-o", obj]
+def _compile(src: str, build_dir: str = BUILD, defines=()) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [hipcc(), *COMMON, *[f"-D{d}" for d in defines], "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(jobs: int = 8, verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int = 8, verbose: bool = False, defines=(), out: str = LIB, build_dir: str = BUILD) -> str:
+    """Compile and link.  `defines` override the kernels' compile-time tuning constants
+    (for building variants elsewhere); the default build uses the values in the sources."""
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sources()
     with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda f: _compile(f, build_dir, defines), srcs))
+    LIB_OUT = out
+    tmp = LIB_OUT + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, LIB_OUT)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {LIB_OUT}")
+    return LIB_OUT
 
 
 if __name__ == "__main__":

@@ -121,6 +121,7 @@ __global__ __launch_bounds__(256) void k_aux_final(const float* __restrict__ par
     const int tid = threadIdx.x, e = tid % nep, s = tid / nep;
     float v = 0.0f;
     if (e < NE)
+#pragma unroll 8
         for (int b = s; b < nblk; b += S) v += part[(int64_t)b * NE + e];
     acc[tid] = v;
     __syncthreads();

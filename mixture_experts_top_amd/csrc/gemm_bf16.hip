@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restri
 
 // Out[t, n0:n0+BN] = A[t, :] . Bw[e][n0:n0+BN, :]^T (+ bias[e] | + Out[t] when accumulating).
 template <int H, int BN, bool DX>
-__global__ __launch_bounds__(kThreads) void k_rows_bf16(const uint16_t* __restrict__ A,
+__device__ __forceinline__ void rows_bf16_body(int bid, const uint16_t* __restrict__ A,
                                                          const uint16_t* __restrict__ Bw,
                                                          const float* __restrict__ bias,
                                                          uint16_t* __restrict__ Out,
@@ -94,7 +94,7 @@ __global__ __launch_bounds__(kThreads) void k_rows_bf16(const uint16_t* __restri
     __shared__ int tok[BM];
 
     int mt, nt;
-    xcd_split(blockIdx.x, NT, mt, nt);
+    xcd_split(bid, NT, mt, nt);
     int e, r0, r1;
     if (!find_tile(offsets, NE, mt, BM, e, r0, r1)) return;
     const int rows = r1 - r0;
@@ -166,11 +166,11 @@ __global__ __launch_bounds__(kThreads) void k_rows_bf16(const uint16_t* __restri
 
 // d_W / d_b partials for one chunk of one expert's tokens, output tile [o0:o0+BT, i0:i0+BT].
 template <int H>
-__global__ __launch_bounds__(kThreads) void k_dw_bf16(const uint16_t* __restrict__ dY,
+__device__ __forceinline__ void dw_bf16_body(int bid, const uint16_t* __restrict__ dY,
                                                        const uint16_t* __restrict__ X,
                                                        float* __restrict__ part_dw, float* __restrict__ part_db,
                                                        const int* __restrict__ offsets,
-                                                       const int* __restrict__ perm, int NE, int chunk) {
+                                                       const int* __restrict__ perm, int NE, int P, int T) {
     constexpr int BT = (H >= 128) ? 128 : 64;
     constexpr int NTI = H / BT, TPC = NTI * NTI;
     constexpr int KC = 64, KP = KC + 8;
@@ -180,23 +180,9 @@ __global__ __launch_bounds__(kThreads) void k_dw_bf16(const uint16_t* __restrict
     __shared__ uint16_t Bs[BT][KP];  // X^T:  [i][t]
 
     int c, tile;
-    xcd_split(blockIdx.x, TPC, c, tile);
+    xcd_split(bid, TPC, c, tile);
     int e = -1, t0 = 0, t1 = 0;
-    {
-        int acc = 0;
-        for (int i = 0; i < NE; ++i) {
-            const int c0 = offsets[i], c1 = offsets[i + 1];
-            const int n = (c1 - c0 + chunk - 1) / chunk;
-            if (c < acc + n) {
-                e = i;
-                t0 = c0 + (c - acc) * chunk;
-                t1 = min(c1, t0 + chunk);
-                break;
-            }
-            acc += n;
-        }
-    }
-    if (e < 0) return;
+    if (!find_chunk(offsets, NE, P, T, c, e, t0, t1)) return;
     const int o0 = (tile / NTI) * BT, i0 = (tile % NTI) * BT;
     const bool do_db = (tile % NTI) == 0;
     const int tid = threadIdx.x;
@@ -260,7 +246,7 @@ __global__ __launch_bounds__(kThreads) void k_dw_bf16(const uint16_t* __restrict
         __syncthreads();
     }
 
-    float* __restrict__ P = part_dw + (size_t)c * H * H;
+    float* __restrict__ Pd = part_dw + (size_t)c * H * H;
 #pragma unroll
     for (int i = 0; i < SUB; ++i)
 #pragma unroll
@@ -269,48 +255,73 @@ __global__ __launch_bounds__(kThreads) void k_dw_bf16(const uint16_t* __restrict
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = o0 + wm * WT + i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
-                P[(size_t)row * H + col] = acc[i][j][r];
+                Pd[(size_t)row * H + col] = acc[i][j][r];
             }
         }
     if (do_db && tid < BT) part_db[(size_t)c * H + o0 + tid] = dbacc;
+}
+
+// Kernels.  The backward is one launch: dX tiles first, then dW / db chunk tiles.
+template <int H, int BN>
+__global__ __launch_bounds__(kThreads) void k_fwd_bf16(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
+                                                        const float* __restrict__ bias, uint16_t* __restrict__ Y,
+                                                        const int* __restrict__ offsets,
+                                                        const int* __restrict__ perm, int NE) {
+    rows_bf16_body<H, BN, false>(blockIdx.x, X, W, bias, Y, offsets, perm, NE, 0);
+}
+
+template <int H, int BN>
+__global__ __launch_bounds__(kThreads) void k_bwd_bf16(const uint16_t* __restrict__ dY,
+                                                        const uint16_t* __restrict__ X,
+                                                        const uint16_t* __restrict__ Wt, uint16_t* __restrict__ dX,
+                                                        int accumulate, float* __restrict__ part_dw,
+                                                        float* __restrict__ part_db,
+                                                        const int* __restrict__ offsets,
+                                                        const int* __restrict__ perm, int NE, int P, int T, int n_dx) {
+    if ((int)blockIdx.x < n_dx)
+        rows_bf16_body<H, BN, true>(blockIdx.x, dY, Wt, nullptr, dX, offsets, perm, NE, accumulate);
+    else
+        dw_bf16_body<H>(blockIdx.x - n_dx, dY, X, part_dw, part_db, offsets, perm, NE, P, T);
 }
 
 // ---------------------------------------------------------------- launchers
 static inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
 template <int H>
-static hipError_t rows_bf16(bool dx, const uint16_t* A, const uint16_t* Bw, const float* bias, uint16_t* Out,
-                            int accumulate, const int32_t* offsets, const int32_t* perm, int64_t T, int NE,
-                            hipStream_t s) {
+static hipError_t fwd_bf16(const uint16_t* X, const uint16_t* W, const float* bias, uint16_t* Y,
+                           const int32_t* offsets, const int32_t* perm, int64_t T, int NE, hipStream_t s) {
     constexpr int BN = (H >= 128) ? 128 : H;
     constexpr int NT = H / BN;
-    const int mtiles = (int)((T + 127) / 128) + NE;
-    const int grid = round_up(mtiles, 8) * NT;
-    if (dx)
-        hipLaunchKernelGGL((k_rows_bf16<H, BN, true>), dim3(grid), dim3(kThreads), 0, s, A, Bw, bias, Out, offsets,
-                           perm, NE, accumulate);
-    else
-        hipLaunchKernelGGL((k_rows_bf16<H, BN, false>), dim3(grid), dim3(kThreads), 0, s, A, Bw, bias, Out, offsets,
-                           perm, NE, accumulate);
+    const int grid = round_up((int)((T + 127) / 128) + NE, 8) * NT;
+    hipLaunchKernelGGL((k_fwd_bf16<H, BN>), dim3(grid), dim3(kThreads), 0, s, X, W, bias, Y, offsets, perm, NE);
     return hipGetLastError();
 }
 
-static hipError_t rows_bf16_dispatch(bool dx, const uint16_t* A, const uint16_t* Bw, const float* bias,
-                                     uint16_t* Out, int accumulate, const int32_t* offsets, const int32_t* perm,
-                                     int64_t T, int H, int NE, hipStream_t s) {
-    switch (H) {
-        case 64: return rows_bf16<64>(dx, A, Bw, bias, Out, accumulate, offsets, perm, T, NE, s);
-        case 128: return rows_bf16<128>(dx, A, Bw, bias, Out, accumulate, offsets, perm, T, NE, s);
-        case 256: return rows_bf16<256>(dx, A, Bw, bias, Out, accumulate, offsets, perm, T, NE, s);
-        case 512: return rows_bf16<512>(dx, A, Bw, bias, Out, accumulate, offsets, perm, T, NE, s);
-    }
-    return hipErrorInvalidValue;
+template <int H>
+static hipError_t bwd_bf16(const uint16_t* dY, const uint16_t* X, const uint16_t* Wt, uint16_t* dX, int accumulate,
+                           float* pdw, float* pdb, const int32_t* offsets, const int32_t* perm, int64_t T, int NE,
+                           int P, int n_chunk_max, hipStream_t s) {
+    constexpr int BN = (H >= 128) ? 128 : H;
+    constexpr int NT = H / BN;
+    constexpr int BT = (H >= 128) ? 128 : 64;
+    constexpr int TPC = (H / BT) * (H / BT);
+    const int n_dx = round_up((int)((T + 127) / 128) + NE, 8) * NT;
+    const int grid = n_dx + round_up(n_chunk_max, 8) * TPC;
+    hipLaunchKernelGGL((k_bwd_bf16<H, BN>), dim3(grid), dim3(kThreads), 0, s, dY, X, Wt, dX, accumulate, pdw, pdb,
+                       offsets, perm, NE, P, (int)T, n_dx);
+    return hipGetLastError();
 }
 
 hipError_t launch_fwd_gemm_bf16(const uint16_t* X, const uint16_t* W, const float* bias, uint16_t* Y,
                                 const int32_t* offsets, const int32_t* perm, int64_t T, int H, int NE,
                                 hipStream_t s) {
-    return rows_bf16_dispatch(false, X, W, bias, Y, 0, offsets, perm, T, H, NE, s);
+    switch (H) {
+        case 64: return fwd_bf16<64>(X, W, bias, Y, offsets, perm, T, NE, s);
+        case 128: return fwd_bf16<128>(X, W, bias, Y, offsets, perm, T, NE, s);
+        case 256: return fwd_bf16<256>(X, W, bias, Y, offsets, perm, T, NE, s);
+        case 512: return fwd_bf16<512>(X, W, bias, Y, offsets, perm, T, NE, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_transpose_w_bf16(const uint16_t* W, uint16_t* Wt, int H, int NE, hipStream_t s) {
@@ -318,31 +329,14 @@ hipError_t launch_transpose_w_bf16(const uint16_t* W, uint16_t* Wt, int H, int N
     return hipGetLastError();
 }
 
-hipError_t launch_dx_gemm_bf16(const uint16_t* dY, const uint16_t* Wt, uint16_t* dX, int accumulate,
-                               const int32_t* offsets, const int32_t* perm, int64_t T, int H, int NE,
-                               hipStream_t s) {
-    return rows_bf16_dispatch(true, dY, Wt, nullptr, dX, accumulate, offsets, perm, T, H, NE, s);
-}
-
-template <int H>
-static hipError_t dw_bf16(const uint16_t* dY, const uint16_t* X, float* pdw, float* pdb, const int32_t* offsets,
-                          const int32_t* perm, int NE, int chunk, int n_chunk_max, hipStream_t s) {
-    constexpr int BT = (H >= 128) ? 128 : 64;
-    constexpr int TPC = (H / BT) * (H / BT);
-    const int grid = round_up(n_chunk_max, 8) * TPC;
-    hipLaunchKernelGGL((k_dw_bf16<H>), dim3(grid), dim3(kThreads), 0, s, dY, X, pdw, pdb, offsets, perm, NE,
-                       chunk);
-    return hipGetLastError();
-}
-
-hipError_t launch_dw_gemm_bf16(const uint16_t* dY, const uint16_t* X, float* pdw, float* pdb,
-                               const int32_t* offsets, const int32_t* perm, int H, int NE, int chunk,
-                               int n_chunk_max, hipStream_t s) {
+hipError_t launch_bwd_gemm_bf16(const uint16_t* dY, const uint16_t* X, const uint16_t* Wt, uint16_t* dX,
+                                int accumulate, float* pdw, float* pdb, const int32_t* offsets, const int32_t* perm,
+                                int64_t T, int H, int NE, int P, int n_chunk_max, hipStream_t s) {
     switch (H) {
-        case 64: return dw_bf16<64>(dY, X, pdw, pdb, offsets, perm, NE, chunk, n_chunk_max, s);
-        case 128: return dw_bf16<128>(dY, X, pdw, pdb, offsets, perm, NE, chunk, n_chunk_max, s);
-        case 256: return dw_bf16<256>(dY, X, pdw, pdb, offsets, perm, NE, chunk, n_chunk_max, s);
-        case 512: return dw_bf16<512>(dY, X, pdw, pdb, offsets, perm, NE, chunk, n_chunk_max, s);
+        case 64: return bwd_bf16<64>(dY, X, Wt, dX, accumulate, pdw, pdb, offsets, perm, T, NE, P, n_chunk_max, s);
+        case 128: return bwd_bf16<128>(dY, X, Wt, dX, accumulate, pdw, pdb, offsets, perm, T, NE, P, n_chunk_max, s);
+        case 256: return bwd_bf16<256>(dY, X, Wt, dX, accumulate, pdw, pdb, offsets, perm, T, NE, P, n_chunk_max, s);
+        case 512: return bwd_bf16<512>(dY, X, Wt, dX, accumulate, pdw, pdb, offsets, perm, T, NE, P, n_chunk_max, s);
     }
     return hipErrorInvalidValue;
 }

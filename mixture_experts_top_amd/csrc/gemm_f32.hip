@@ -24,6 +24,19 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;   // 4 waves, arranged 2 x 2 over the output tile
+// K slice staged per LDS buffer (a multiple of 8), per kernel; chosen by measurement.
+#ifndef MOE_F32_KC_FWD
+#define MOE_F32_KC_FWD 32
+#endif
+#ifndef MOE_F32_KC_DX
+#define MOE_F32_KC_DX 16
+#endif
+#ifndef MOE_F32_KC_DW
+#define MOE_F32_KC_DW 16
+#endif
+#ifndef MOE_ROWS_BIG_TILES_PER_CU
+#define MOE_ROWS_BIG_TILES_PER_CU 2
+#endif
 constexpr int kPad = 4;         // LDS row padding (floats): keeps 16-byte alignment, spreads banks
 
 __device__ __forceinline__ f32x16 mfma32(float a, float b, f32x16 c) {
@@ -65,27 +78,35 @@ __device__ __forceinline__ void xcd_split(int bid, int per, int& major, int& min
 // ----------------------------------------------------------------------------------
 // Row GEMM: Out[t, n0:n0+BN] = A[t, :] . B[:, n0:n0+BN] (+ bias) for the BM rows of one
 // expert tile.  DX = false: B[k][n] = W[e][n][k] (forward).  DX = true: B[k][n] = W[e][k][n].
+// K is walked in 32-wide slices with two LDS buffers: the global loads of slice c+1 are
+// issued into registers before the MFMAs of slice c, and stored to the other buffer after
+// them, so one barrier per slice suffices and load latency hides behind the MFMAs.
 // ----------------------------------------------------------------------------------
-template <int H, int BN, bool DX>
-__global__ __launch_bounds__(kThreads) void k_rows_f32(const float* __restrict__ A,
+template <int H, int BM, int BN, int KC, bool DX>
+__device__ __forceinline__ void rows_f32_body(int bid, const float* __restrict__ A,
                                                         const float* __restrict__ W,
                                                         const float* __restrict__ bias,
                                                         float* __restrict__ Out,
                                                         const int* __restrict__ offsets,
                                                         const int* __restrict__ perm, int NE,
                                                         int accumulate) {
-    constexpr int BM = 128, KC = 32;
+    constexpr int NKC = H / KC;
     constexpr int NT = H / BN;
-    constexpr int WTM = BM / 2, WTN = BN / 2;
+    constexpr int WM = (BM >= 64) ? 2 : 1, WN = 4 / WM;  // wavefront grid over the tile
+    constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int SM = WTM / 32, SN = WTN / 32;
+    static_assert(SM >= 1 && SN >= 1, "wavefront tile must hold a 32x32 block");
+    constexpr int TPR = KC / 4, RPP = kThreads / TPR;   // threads per row slice, rows per pass
+    constexpr int AL = BM / RPP, BL = BN * KC / (4 * kThreads);  // float4 loads per thread per slice
+    static_assert(KC % 8 == 0 && BM % RPP == 0 && (BN * KC) % (4 * kThreads) == 0, "tile shape");
     constexpr int BS_ROWS = DX ? KC : BN;
     constexpr int BS_COLS = DX ? BN + kPad : KC + kPad;
-    __shared__ float As[BM][KC + kPad];
-    __shared__ float Bs[BS_ROWS][BS_COLS];
+    __shared__ float As[2][BM][KC + kPad];
+    __shared__ float Bs[2][BS_ROWS][BS_COLS];
     __shared__ int tok[BM];
 
     int mt, nt;
-    xcd_split(blockIdx.x, NT, mt, nt);
+    xcd_split(bid, NT, mt, nt);
     int e, r0, r1;
     if (!find_tile(offsets, NE, mt, BM, e, r0, r1)) return;
     const int rows = r1 - r0;
@@ -96,7 +117,43 @@ __global__ __launch_bounds__(kThreads) void k_rows_f32(const float* __restrict__
     const int n0 = nt * BN;
     const float* __restrict__ We = W + (size_t)e * H * H;
     const int wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
-    const int wm = wave / 2, wn = wave % 2;
+    const int wm = wave / WN, wn = wave % WN;
+
+    // per-thread load coordinates (fixed across slices)
+    const float* a_src[AL];
+#pragma unroll
+    for (int i = 0; i < AL; ++i) {
+        const int t = tok[tid / TPR + RPP * i];
+        a_src[i] = (t >= 0) ? A + (size_t)t * H + 4 * (tid % TPR) : nullptr;
+    }
+    f32x4 ra[AL], rb[BL];
+    auto load_slice = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < AL; ++i) ra[i] = a_src[i] ? ld4(a_src[i] + k0) : f32x4{};
+#pragma unroll
+        for (int i = 0; i < BL; ++i) {
+            if (!DX) {
+                const int r = tid / TPR + RPP * i, c = 4 * (tid % TPR);
+                rb[i] = ld4(We + (size_t)(n0 + r) * H + k0 + c);
+            } else {
+                const int q = tid + kThreads * i, r = q / (BN / 4), c = 4 * (q % (BN / 4));
+                rb[i] = ld4(We + (size_t)(k0 + r) * H + n0 + c);
+            }
+        }
+    };
+    auto store_slice = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < AL; ++i) st4(&As[buf][tid / TPR + RPP * i][4 * (tid % TPR)], ra[i]);
+#pragma unroll
+        for (int i = 0; i < BL; ++i) {
+            if (!DX) {
+                st4(&Bs[buf][tid / TPR + RPP * i][4 * (tid % TPR)], rb[i]);
+            } else {
+                const int q = tid + kThreads * i;
+                st4(&Bs[buf][q / (BN / 4)][4 * (q % (BN / 4))], rb[i]);
+            }
+        }
+    };
 
     f32x16 acc[SM][SN];
 #pragma unroll
@@ -104,45 +161,26 @@ __global__ __launch_bounds__(kThreads) void k_rows_f32(const float* __restrict__
 #pragma unroll
         for (int j = 0; j < SN; ++j) acc[i][j] = f32x16{};
 
-    for (int k0 = 0; k0 < H; k0 += KC) {
-        // A: BM rows x KC, 8 threads per row (128 B each).
-#pragma unroll
-        for (int i = 0; i < BM / 32; ++i) {
-            const int r = tid / 8 + 32 * i, c = 4 * (tid % 8);
-            const int t = tok[r];
-            f32x4 v = f32x4{};
-            if (t >= 0) v = ld4(A + (size_t)t * H + k0 + c);
-            st4(&As[r][c], v);
-        }
-        if (!DX) {
-#pragma unroll
-            for (int i = 0; i < BN / 32; ++i) {
-                const int r = tid / 8 + 32 * i, c = 4 * (tid % 8);
-                st4(&Bs[r][c], ld4(We + (size_t)(n0 + r) * H + k0 + c));
-            }
-        } else {
-            constexpr int Q = BN / 4;  // float4 per W row segment
-#pragma unroll
-            for (int i = 0; i < KC * Q / kThreads; ++i) {
-                const int q = tid + kThreads * i;
-                const int r = q / Q, c = 4 * (q % Q);
-                st4(&Bs[r][c], ld4(We + (size_t)(k0 + r) * H + n0 + c));
-            }
-        }
-        __syncthreads();
+    load_slice(0);
+    store_slice(0);
+    __syncthreads();
+#pragma unroll 1
+    for (int c = 0; c < NKC; ++c) {
+        const int buf = c & 1;
+        if (c + 1 < NKC) load_slice((c + 1) * KC);
 #pragma unroll
         for (int kk = 0; kk < KC; kk += 8) {
             f32x4 a[SM], b[SN];
 #pragma unroll
-            for (int i = 0; i < SM; ++i) a[i] = ld4(&As[wm * WTM + i * 32 + l32][kk + 4 * h]);
+            for (int i = 0; i < SM; ++i) a[i] = ld4(&As[buf][wm * WTM + i * 32 + l32][kk + 4 * h]);
 #pragma unroll
             for (int j = 0; j < SN; ++j) {
                 if (!DX) {
-                    b[j] = ld4(&Bs[wn * WTN + j * 32 + l32][kk + 4 * h]);
+                    b[j] = ld4(&Bs[buf][wn * WTN + j * 32 + l32][kk + 4 * h]);
                 } else {
-                    const int c = wn * WTN + j * 32 + l32;
-                    b[j] = f32x4{Bs[kk + 4 * h + 0][c], Bs[kk + 4 * h + 1][c], Bs[kk + 4 * h + 2][c],
-                                 Bs[kk + 4 * h + 3][c]};
+                    const int cc = wn * WTN + j * 32 + l32;
+                    b[j] = f32x4{Bs[buf][kk + 4 * h + 0][cc], Bs[buf][kk + 4 * h + 1][cc],
+                                 Bs[buf][kk + 4 * h + 2][cc], Bs[buf][kk + 4 * h + 3][cc]};
                 }
             }
 #pragma unroll
@@ -152,6 +190,7 @@ __global__ __launch_bounds__(kThreads) void k_rows_f32(const float* __restrict__
 #pragma unroll
                     for (int j = 0; j < SN; ++j) acc[i][j] = mfma32(a[i][s], b[j][s], acc[i][j]);
         }
+        if (c + 1 < NKC) store_slice(buf ^ 1);
         __syncthreads();
     }
 
@@ -182,46 +221,35 @@ __global__ __launch_bounds__(kThreads) void k_rows_f32(const float* __restrict__
 //   part_dw[c][o][i] = sum_{t in chunk} dY[t][o] X[t][i]
 //   part_db[c][o]    = sum_{t in chunk} dY[t][o]          (tiles with it == 0)
 // Token order inside a chunk is fixed (perm order), as is the MFMA accumulation order.
+// Same two-buffer pipeline as the row GEMM; token ids of slice c+2 are fetched while slice
+// c+1's rows are being loaded, so the gather never waits on an index load.
 // ----------------------------------------------------------------------------------
-template <int H>
-__global__ __launch_bounds__(kThreads) void k_dw_f32(const float* __restrict__ dY,
+template <int H, int KC>
+__device__ __forceinline__ void dw_f32_body(int bid, const float* __restrict__ dY,
                                                       const float* __restrict__ X,
                                                       float* __restrict__ part_dw,
                                                       float* __restrict__ part_db,
                                                       const int* __restrict__ offsets,
                                                       const int* __restrict__ perm, int NE,
-                                                      int chunk) {
+                                                      int P, int T) {
     constexpr int BT = (H >= 128) ? 128 : 64;
     constexpr int NTI = H / BT, TPC = NTI * NTI;
-    constexpr int KC = 32;
     constexpr int WT = BT / 2, SUB = WT / 32;
-    __shared__ float As[KC][BT + kPad];  // dY rows, columns o0..o0+BT
-    __shared__ float Bs[KC][BT + kPad];  // X rows, columns i0..i0+BT
+    constexpr int Q = BT / 4;                  // float4 per row segment
+    constexpr int LD = KC * Q / kThreads;      // float4 loads per thread per tensor per slice
+    __shared__ float As[2][KC][BT + kPad];     // dY rows, columns o0..o0+BT
+    __shared__ float Bs[2][KC][BT + kPad];     // X rows, columns i0..i0+BT
 
     int c, tile;
-    xcd_split(blockIdx.x, TPC, c, tile);
-    // expert and token range of chunk c
+    xcd_split(bid, TPC, c, tile);
     int e = -1, t0 = 0, t1 = 0;
-    {
-        int acc = 0;
-        for (int i = 0; i < NE; ++i) {
-            const int c0 = offsets[i], c1 = offsets[i + 1];
-            const int n = (c1 - c0 + chunk - 1) / chunk;
-            if (c < acc + n) {
-                e = i;
-                t0 = c0 + (c - acc) * chunk;
-                t1 = min(c1, t0 + chunk);
-                break;
-            }
-            acc += n;
-        }
-    }
-    if (e < 0) return;
+    if (!find_chunk(offsets, NE, P, T, c, e, t0, t1)) return;
     const int o0 = (tile / NTI) * BT, i0 = (tile % NTI) * BT;
     const bool do_db = (tile % NTI) == 0;
     const int tid = threadIdx.x;
     const int wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
     const int wm = wave / 2, wn = wave % 2;
+    const int nslices = (t1 - t0 + KC - 1) / KC;
 
     f32x16 acc[SUB][SUB];
 #pragma unroll
@@ -230,32 +258,59 @@ __global__ __launch_bounds__(kThreads) void k_dw_f32(const float* __restrict__ d
         for (int j = 0; j < SUB; ++j) acc[i][j] = f32x16{};
     float dbacc = 0.0f;
 
-    constexpr int Q = BT / 4;  // float4 per row segment
-    for (int k0 = t0; k0 < t1; k0 += KC) {
+    int tk[LD];
+    f32x4 ra[LD], rb[LD];
+    auto load_ids = [&](int s) {
 #pragma unroll
-        for (int i = 0; i < KC * Q / kThreads; ++i) {
-            const int q = tid + kThreads * i;
-            const int r = q / Q, cc = 4 * (q % Q);
-            f32x4 va = f32x4{}, vb = f32x4{};
-            if (k0 + r < t1) {
-                const size_t t = (size_t)perm[k0 + r];
-                va = ld4(dY + t * H + o0 + cc);
-                vb = ld4(X + t * H + i0 + cc);
-            }
-            st4(&As[r][cc], va);
-            st4(&Bs[r][cc], vb);
+        for (int i = 0; i < LD; ++i) {
+            const int k = t0 + s * KC + (tid + kThreads * i) / Q;
+            tk[i] = (s < nslices && k < t1) ? perm[k] : -1;
         }
-        __syncthreads();
+    };
+    auto load_rows = [&]() {
+#pragma unroll
+        for (int i = 0; i < LD; ++i) {
+            const int cc = 4 * ((tid + kThreads * i) % Q);
+            ra[i] = f32x4{};
+            rb[i] = f32x4{};
+            if (tk[i] >= 0) {
+                const size_t t = (size_t)tk[i];
+                ra[i] = ld4(dY + t * H + o0 + cc);
+                rb[i] = ld4(X + t * H + i0 + cc);
+            }
+        }
+    };
+    auto store_rows = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < LD; ++i) {
+            const int q = tid + kThreads * i;
+            st4(&As[buf][q / Q][4 * (q % Q)], ra[i]);
+            st4(&Bs[buf][q / Q][4 * (q % Q)], rb[i]);
+        }
+    };
+
+    load_ids(0);
+    load_rows();
+    load_ids(1);
+    store_rows(0);
+    __syncthreads();
+#pragma unroll 1
+    for (int s = 0; s < nslices; ++s) {
+        const int buf = s & 1;
+        if (s + 1 < nslices) {
+            load_rows();       // rows of slice s+1 (ids fetched one slice earlier)
+            load_ids(s + 2);
+        }
 #pragma unroll
         for (int kk = 0; kk < KC; kk += 8) {
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int k = kk + 4 * h + s;
+            for (int q = 0; q < 4; ++q) {
+                const int k = kk + 4 * h + q;
                 float a[SUB], b[SUB];
 #pragma unroll
-                for (int i = 0; i < SUB; ++i) a[i] = As[k][wm * WT + i * 32 + l32];
+                for (int i = 0; i < SUB; ++i) a[i] = As[buf][k][wm * WT + i * 32 + l32];
 #pragma unroll
-                for (int j = 0; j < SUB; ++j) b[j] = Bs[k][wn * WT + j * 32 + l32];
+                for (int j = 0; j < SUB; ++j) b[j] = Bs[buf][k][wn * WT + j * 32 + l32];
 #pragma unroll
                 for (int i = 0; i < SUB; ++i)
 #pragma unroll
@@ -264,12 +319,13 @@ __global__ __launch_bounds__(kThreads) void k_dw_f32(const float* __restrict__ d
         }
         if (do_db && tid < BT) {
 #pragma unroll 8
-            for (int k = 0; k < KC; ++k) dbacc += As[k][tid];
+            for (int k = 0; k < KC; ++k) dbacc += As[buf][k][tid];
         }
+        if (s + 1 < nslices) store_rows(buf ^ 1);
         __syncthreads();
     }
 
-    float* __restrict__ P = part_dw + (size_t)c * H * H;
+    float* __restrict__ Pd = part_dw + (size_t)c * H * H;
 #pragma unroll
     for (int i = 0; i < SUB; ++i)
 #pragma unroll
@@ -278,10 +334,36 @@ __global__ __launch_bounds__(kThreads) void k_dw_f32(const float* __restrict__ d
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = o0 + wm * WT + i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
-                P[(size_t)row * H + col] = acc[i][j][r];
+                Pd[(size_t)row * H + col] = acc[i][j][r];
             }
         }
     if (do_db && tid < BT) part_db[(size_t)c * H + o0 + tid] = dbacc;
+}
+
+// ----------------------------------------------------------------------------------
+// Kernels.  The backward is one launch: its first n_dx workgroups are dX tiles and the rest
+// are dW / db chunk tiles, so both halves fill the GPU together.
+// ----------------------------------------------------------------------------------
+template <int H, int BM, int BN, int KC>
+__global__ __launch_bounds__(kThreads) void k_fwd_f32(const float* __restrict__ X, const float* __restrict__ W,
+                                                       const float* __restrict__ bias, float* __restrict__ Y,
+                                                       const int* __restrict__ offsets,
+                                                       const int* __restrict__ perm, int NE) {
+    rows_f32_body<H, BM, BN, KC, false>(blockIdx.x, X, W, bias, Y, offsets, perm, NE, 0);
+}
+
+template <int H, int BM, int BN, int KCX, int KCW>
+__global__ __launch_bounds__(kThreads) void k_bwd_f32(const float* __restrict__ dY, const float* __restrict__ X,
+                                                       const float* __restrict__ W, float* __restrict__ dX,
+                                                       int accumulate, float* __restrict__ part_dw,
+                                                       float* __restrict__ part_db,
+                                                       const int* __restrict__ offsets,
+                                                       const int* __restrict__ perm, int NE, int P, int T,
+                                                       int n_dx) {
+    if ((int)blockIdx.x < n_dx)
+        rows_f32_body<H, BM, BN, KCX, true>(blockIdx.x, dY, W, nullptr, dX, offsets, perm, NE, accumulate);
+    else
+        dw_f32_body<H, KCW>(blockIdx.x - n_dx, dY, X, part_dw, part_db, offsets, perm, NE, P, T);
 }
 
 // ----------------------------------------------------------------------------------
@@ -289,66 +371,81 @@ __global__ __launch_bounds__(kThreads) void k_dw_f32(const float* __restrict__ d
 // ----------------------------------------------------------------------------------
 static inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
+// 128-row tiles once they give enough workgroups per compute unit, else 64-row tiles.
+#ifndef MOE_ROWS_SMALL_BM
+#define MOE_ROWS_SMALL_BM 64
+#endif
 template <int H>
-static hipError_t rows_f32(bool dx, const float* A, const float* W, const float* bias, float* Out,
-                           int accumulate, const int32_t* offsets, const int32_t* perm, int64_t T,
-                           int NE, hipStream_t s) {
+static int rows_bm(int64_t T) {
+    constexpr int NT = H / ((H >= 128) ? 128 : H);
+    return ((T / 128) * NT >= MOE_ROWS_BIG_TILES_PER_CU * 256) ? 128 : MOE_ROWS_SMALL_BM;
+}
+
+template <int H>
+static int rows_grid(int64_t T, int NE, int bm) {
+    constexpr int NT = H / ((H >= 128) ? 128 : H);
+    return round_up((int)((T + bm - 1) / bm) + NE, 8) * NT;
+}
+
+template <int H>
+static int dw_grid(int n_chunk_max) {
+    constexpr int BT = (H >= 128) ? 128 : 64;
+    constexpr int TPC = (H / BT) * (H / BT);
+    return round_up(n_chunk_max, 8) * TPC;
+}
+
+template <int H>
+static hipError_t fwd_f32(const float* X, const float* W, const float* bias, float* Y, const int32_t* offsets,
+                          const int32_t* perm, int64_t T, int NE, hipStream_t s) {
     constexpr int BN = (H >= 128) ? 128 : H;
-    constexpr int NT = H / BN;
-    const int mtiles = (int)((T + 127) / 128) + NE;
-    const int grid = round_up(mtiles, 8) * NT;
-    if (dx)
-        hipLaunchKernelGGL((k_rows_f32<H, BN, true>), dim3(grid), dim3(kThreads), 0, s, A, W, bias, Out,
-                           offsets, perm, NE, accumulate);
+    const int bm = rows_bm<H>(T);
+    const int grid = rows_grid<H>(T, NE, bm);
+    if (bm == 128)
+        hipLaunchKernelGGL((k_fwd_f32<H, 128, BN, MOE_F32_KC_FWD>), dim3(grid), dim3(kThreads), 0, s, X, W, bias, Y,
+                           offsets, perm, NE);
     else
-        hipLaunchKernelGGL((k_rows_f32<H, BN, false>), dim3(grid), dim3(kThreads), 0, s, A, W, bias, Out,
-                           offsets, perm, NE, accumulate);
+        hipLaunchKernelGGL((k_fwd_f32<H, MOE_ROWS_SMALL_BM, BN, MOE_F32_KC_FWD>), dim3(grid), dim3(kThreads), 0, s, X,
+                           W, bias, Y, offsets, perm, NE);
     return hipGetLastError();
 }
 
-static hipError_t rows_f32_dispatch(bool dx, const float* A, const float* W, const float* bias,
-                                    float* Out, int accumulate, const int32_t* offsets,
-                                    const int32_t* perm, int64_t T, int H, int NE, hipStream_t s) {
+template <int H>
+static hipError_t bwd_f32(const float* dY, const float* X, const float* W, float* dX, int accumulate, float* pdw,
+                          float* pdb, const int32_t* offsets, const int32_t* perm, int64_t T, int NE, int P,
+                          int n_chunk_max, hipStream_t s) {
+    constexpr int BN = (H >= 128) ? 128 : H;
+    const int bm = rows_bm<H>(T);
+    const int n_dx = rows_grid<H>(T, NE, bm);
+    const int grid = n_dx + dw_grid<H>(n_chunk_max);
+    if (bm == 128)
+        hipLaunchKernelGGL((k_bwd_f32<H, 128, BN, MOE_F32_KC_DX, MOE_F32_KC_DW>), dim3(grid), dim3(kThreads), 0, s,
+                           dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, NE, P, (int)T, n_dx);
+    else
+        hipLaunchKernelGGL((k_bwd_f32<H, MOE_ROWS_SMALL_BM, BN, MOE_F32_KC_DX, MOE_F32_KC_DW>), dim3(grid),
+                           dim3(kThreads), 0, s, dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, NE, P, (int)T,
+                           n_dx);
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd_gemm_f32(const float* X, const float* W, const float* bias, float* Y, const int32_t* offsets,
+                               const int32_t* perm, int64_t T, int H, int NE, hipStream_t s) {
     switch (H) {
-        case 64: return rows_f32<64>(dx, A, W, bias, Out, accumulate, offsets, perm, T, NE, s);
-        case 128: return rows_f32<128>(dx, A, W, bias, Out, accumulate, offsets, perm, T, NE, s);
-        case 256: return rows_f32<256>(dx, A, W, bias, Out, accumulate, offsets, perm, T, NE, s);
-        case 512: return rows_f32<512>(dx, A, W, bias, Out, accumulate, offsets, perm, T, NE, s);
+        case 64: return fwd_f32<64>(X, W, bias, Y, offsets, perm, T, NE, s);
+        case 128: return fwd_f32<128>(X, W, bias, Y, offsets, perm, T, NE, s);
+        case 256: return fwd_f32<256>(X, W, bias, Y, offsets, perm, T, NE, s);
+        case 512: return fwd_f32<512>(X, W, bias, Y, offsets, perm, T, NE, s);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_fwd_gemm_f32(const float* X, const float* W, const float* bias, float* Y,
-                               const int32_t* offsets, const int32_t* perm, int64_t T, int H, int NE,
-                               hipStream_t s) {
-    return rows_f32_dispatch(false, X, W, bias, Y, 0, offsets, perm, T, H, NE, s);
-}
-
-hipError_t launch_dx_gemm_f32(const float* dY, const float* W, float* dX, int accumulate,
-                              const int32_t* offsets, const int32_t* perm, int64_t T, int H, int NE,
-                              hipStream_t s) {
-    return rows_f32_dispatch(true, dY, W, nullptr, dX, accumulate, offsets, perm, T, H, NE, s);
-}
-
-template <int H>
-static hipError_t dw_f32(const float* dY, const float* X, float* pdw, float* pdb, const int32_t* offsets,
-                         const int32_t* perm, int NE, int chunk, int n_chunk_max, hipStream_t s) {
-    constexpr int BT = (H >= 128) ? 128 : 64;
-    constexpr int TPC = (H / BT) * (H / BT);
-    const int grid = round_up(n_chunk_max, 8) * TPC;
-    hipLaunchKernelGGL((k_dw_f32<H>), dim3(grid), dim3(kThreads), 0, s, dY, X, pdw, pdb, offsets, perm, NE,
-                       chunk);
-    return hipGetLastError();
-}
-
-hipError_t launch_dw_gemm_f32(const float* dY, const float* X, float* pdw, float* pdb,
-                              const int32_t* offsets, const int32_t* perm, int H, int NE, int chunk,
-                              int n_chunk_max, hipStream_t s) {
+hipError_t launch_bwd_gemm_f32(const float* dY, const float* X, const float* W, float* dX, int accumulate,
+                               float* pdw, float* pdb, const int32_t* offsets, const int32_t* perm, int64_t T, int H,
+                               int NE, int P, int n_chunk_max, hipStream_t s) {
     switch (H) {
-        case 64: return dw_f32<64>(dY, X, pdw, pdb, offsets, perm, NE, chunk, n_chunk_max, s);
-        case 128: return dw_f32<128>(dY, X, pdw, pdb, offsets, perm, NE, chunk, n_chunk_max, s);
-        case 256: return dw_f32<256>(dY, X, pdw, pdb, offsets, perm, NE, chunk, n_chunk_max, s);
-        case 512: return dw_f32<512>(dY, X, pdw, pdb, offsets, perm, NE, chunk, n_chunk_max, s);
+        case 64: return bwd_f32<64>(dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, T, NE, P, n_chunk_max, s);
+        case 128: return bwd_f32<128>(dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, T, NE, P, n_chunk_max, s);
+        case 256: return bwd_f32<256>(dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, T, NE, P, n_chunk_max, s);
+        case 512: return bwd_f32<512>(dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, T, NE, P, n_chunk_max, s);
     }
     return hipErrorInvalidValue;
 }

@@ -26,16 +26,25 @@ static moe_status_t hip_fail(hipError_t e, const char* what) {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Tokens per d_W chunk.  Depends only on (T, H), so results are reproducible for a shape.
-// Aims at about eight workgroups per compute unit for large T while keeping the partial
-// buffers small relative to the activations.
-static int chunk_tokens(int64_t T, int H) {
+// Number of d_W chunks P for T tokens (see expert_nchunks): about eight workgroups per compute
+// unit once the output tiles of a chunk are counted (several rounds, so the last partial
+// round is short), and chunks of at least 128 tokens.  The
+// chunk partials then stay within P x (H^2 + H) floats whatever the routing skew.  Depends
+// only on (T, H), so results are reproducible for a shape.
+#ifndef MOE_DW_WORKGROUPS
+#define MOE_DW_WORKGROUPS 2048
+#endif
+#ifndef MOE_DW_MIN_CHUNK
+#define MOE_DW_MIN_CHUNK 128
+#endif
+static int plan_chunks(int64_t T, int H) {
     const int bt = (H >= 128) ? 128 : 64;
-    const int64_t tiles_per_chunk = (int64_t)(H / bt) * (H / bt);
-    int64_t target = T * tiles_per_chunk / 2048;
-    int c = 64;
-    while (c < 4096 && c < target) c <<= 1;
-    return c;
+    const int tiles_per_chunk = (H / bt) * (H / bt);
+    const int64_t pmax = (MOE_DW_WORKGROUPS + tiles_per_chunk - 1) / tiles_per_chunk;
+    int64_t p = T / MOE_DW_MIN_CHUNK;
+    if (p > pmax) p = pmax;
+    if (p < 1) p = 1;
+    return (int)p;
 }
 
 Plan make_plan(int64_t T, int H, int NE, int act) {
@@ -47,8 +56,8 @@ Plan make_plan(int64_t T, int H, int NE, int act) {
     p.n_rblk = (int)((T + kRouteTokens - 1) / kRouteTokens);
     p.n_ablk = (int)((T + kAuxTokens - 1) / kAuxTokens);
     if (H > 0) {
-        p.chunk = chunk_tokens(T, H);
-        p.n_chunk_max = (int)((T + p.chunk - 1) / p.chunk) + NE;
+        p.chunks = plan_chunks(T, H);
+        p.n_chunk_max = p.chunks + NE;
     }
     size_t o = 0;
     p.off_hist = o;    o += align256((size_t)p.n_rblk * NE * 4);
@@ -138,6 +147,11 @@ static moe_status_t do_route(const float* G, int32_t* idx, int32_t* counts, int3
     int32_t* hist = at<int32_t>(ws, p.off_hist);
     int32_t* blkbase = at<int32_t>(ws, p.off_blkbase);
     LAUNCH(K_ROUTE, launch_route(G, p.T, p.NE, idx, hist, p.n_rblk, s), "route");
+    if (perm && scatter_scan_fits(p.n_rblk, p.NE)) {
+        LAUNCH(K_SCATTER, launch_scatter_scan(idx, p.T, p.NE, hist, p.n_rblk, counts, offsets, perm, s),
+               "scatter+scan");
+        return MOE_OK;
+    }
     LAUNCH(K_SCAN, launch_scan(hist, p.n_rblk, p.NE, blkbase, counts, offsets, s), "scan");
     if (perm) LAUNCH(K_SCATTER, launch_scatter(idx, p.T, p.NE, blkbase, perm, p.n_rblk, s), "scatter");
     return MOE_OK;
@@ -165,8 +179,8 @@ const char* moe_status_string(int st) {
 const char* moe_last_error(void) { return g_err; }
 
 const char* moe_kernel_name(int k) {
-    static const char* names[K_COUNT] = {"route", "scan", "scatter", "fwd_gemm", "dx_gemm",
-                                         "dw_gemm", "reduce", "aux_rows", "aux_final", "w_transpose"};
+    static const char* names[K_COUNT] = {"route", "scan", "scatter", "fwd_gemm", "bwd_gemm",
+                                         "reduce", "aux", "aux_final", "w_transpose"};
     return (k >= 0 && k < K_COUNT) ? names[k] : nullptr;
 }
 
@@ -253,27 +267,21 @@ moe_status_t moe_top1_bwd(const void* d_routed_ctx, const void* fused_ctx, const
     float* pdw = at<float>(workspace, p.off_pdw);
     float* pdb = at<float>(workspace, p.off_pdb);
     if (act == MOE_DTYPE_F32) {
-        LAUNCH(K_DX_GEMM,
-               launch_dx_gemm_f32((const float*)d_routed_ctx, (const float*)W, (float*)d_fused_ctx, accumulate_dx,
-                                  expert_offsets, perm, p.T, p.H, p.NE, s),
-               "dx gemm");
-        LAUNCH(K_DW_GEMM,
-               launch_dw_gemm_f32((const float*)d_routed_ctx, (const float*)fused_ctx, pdw, pdb, expert_offsets,
-                                  perm, p.H, p.NE, p.chunk, p.n_chunk_max, s),
-               "dw gemm");
+        LAUNCH(K_BWD_GEMM,
+               launch_bwd_gemm_f32((const float*)d_routed_ctx, (const float*)fused_ctx, (const float*)W,
+                                   (float*)d_fused_ctx, accumulate_dx, pdw, pdb, expert_offsets, perm, p.T, p.H,
+                                   p.NE, p.chunks, p.n_chunk_max, s),
+               "bwd gemm");
     } else {
         uint16_t* wt = at<uint16_t>(workspace, p.off_wt);
         LAUNCH(K_W_TRANSPOSE, launch_transpose_w_bf16((const uint16_t*)W, wt, p.H, p.NE, s), "w transpose");
-        LAUNCH(K_DX_GEMM,
-               launch_dx_gemm_bf16((const uint16_t*)d_routed_ctx, wt, (uint16_t*)d_fused_ctx,
-                                   accumulate_dx, expert_offsets, perm, p.T, p.H, p.NE, s),
-               "dx gemm");
-        LAUNCH(K_DW_GEMM,
-               launch_dw_gemm_bf16((const uint16_t*)d_routed_ctx, (const uint16_t*)fused_ctx, pdw, pdb,
-                                   expert_offsets, perm, p.H, p.NE, p.chunk, p.n_chunk_max, s),
-               "dw gemm");
+        LAUNCH(K_BWD_GEMM,
+               launch_bwd_gemm_bf16((const uint16_t*)d_routed_ctx, (const uint16_t*)fused_ctx, wt,
+                                    (uint16_t*)d_fused_ctx, accumulate_dx, pdw, pdb, expert_offsets, perm, p.T, p.H,
+                                    p.NE, p.chunks, p.n_chunk_max, s),
+               "bwd gemm");
     }
-    LAUNCH(K_REDUCE, launch_reduce_dw(pdw, pdb, expert_offsets, p.H, p.NE, p.chunk, d_W, d_b, s), "reduce");
+    LAUNCH(K_REDUCE, launch_reduce_dw(pdw, pdb, expert_offsets, p.T, p.H, p.NE, p.chunks, d_W, d_b, s), "reduce");
     return MOE_OK;
 }
 
@@ -302,7 +310,7 @@ moe_status_t moe_aux_loss(const float* gate_logits, const int32_t* expert_counts
         counts = c;
     }
     float* part = at<float>(workspace, p.off_paux);
-    LAUNCH(K_AUX_ROWS, launch_aux_rows(gate_logits, counts, p.T, p.NE, lambda, d_gate_logits, probs, part, p.n_ablk, s),
+    LAUNCH(K_AUX, launch_aux_rows(gate_logits, counts, p.T, p.NE, lambda, d_gate_logits, probs, part, p.n_ablk, s),
            "aux rows");
     LAUNCH(K_AUX_FINAL, launch_aux_final(part, counts, p.n_ablk, p.T, p.NE, lambda, loss, frac, mean_prob, s),
            "aux final");

@@ -14,29 +14,55 @@ namespace moe {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// Routing: one workgroup of 256 threads (4 waves) ranks 1024 tokens as 16 groups of 64.
+// Routing: one workgroup of 256 threads (4 waves) ranks 256 tokens as 4 groups of 64.
 constexpr int kRouteThreads = 256;
-constexpr int kRouteTokens = 1024;
+constexpr int kRouteTokens = 256;
 constexpr int kRouteGroups = kRouteTokens / 64;
 constexpr int kMaxExperts = 64;
 constexpr int kScanThreads = 1024;
 
-// Aux loss: one workgroup of 256 threads covers 1024 tokens.
+// Aux loss: one workgroup of 256 threads covers 256 tokens (one per thread).
 constexpr int kAuxThreads = 256;
-constexpr int kAuxTokens = 1024;
+constexpr int kAuxTokens = 256;
 
 enum KernelId {
-    K_ROUTE = 0, K_SCAN, K_SCATTER, K_FWD_GEMM, K_DX_GEMM, K_DW_GEMM, K_REDUCE,
-    K_AUX_ROWS, K_AUX_FINAL, K_W_TRANSPOSE, K_COUNT
+    K_ROUTE = 0, K_SCAN, K_SCATTER, K_FWD_GEMM, K_BWD_GEMM, K_REDUCE, K_AUX, K_AUX_FINAL, K_W_TRANSPOSE, K_COUNT
 };
+
+// Chunking of each expert's tokens for the d_W split-K.  With P chunks planned for T
+// tokens, expert e (c_e tokens) gets n_e = ceil(c_e P / T) chunks (none if c_e = 0), and
+// chunk j covers its tokens [floor(j c_e / n_e), floor((j+1) c_e / n_e)).  So chunks are
+// about T / P tokens everywhere, the count follows each expert's share of the tokens, and
+// sum_e n_e <= P + N_E.  Chunk ids run expert by expert.  Depends only on (offsets, P, T).
+__device__ __forceinline__ int expert_nchunks(int c, int P, int T) {
+    return c == 0 ? 0 : (int)(((int64_t)c * P + T - 1) / T);
+}
+
+__device__ __forceinline__ bool find_chunk(const int* __restrict__ offsets, int NE, int P, int T, int c, int& e,
+                                           int& t0, int& t1) {
+    int acc = 0;
+    for (int i = 0; i < NE; ++i) {
+        const int c0 = offsets[i], ce = offsets[i + 1] - c0;
+        const int n = expert_nchunks(ce, P, T);
+        if (c < acc + n) {
+            const int j = c - acc;
+            e = i;
+            t0 = c0 + (int)((int64_t)j * ce / n);
+            t1 = c0 + (int)((int64_t)(j + 1) * ce / n);
+            return true;
+        }
+        acc += n;
+    }
+    return false;
+}
 
 // Workspace layout for one (T, H, N_E, act).  Every section starts on a 256-byte boundary.
 struct Plan {
     int64_t T = 0;
     int H = 0, NE = 0, act = 0;
     int n_rblk = 0;       // routing blocks
-    int chunk = 0;        // tokens per d_W chunk
-    int n_chunk_max = 0;  // upper bound of sum_e ceil(c_e / chunk)
+    int chunks = 0;       // P: planned d_W chunks (see expert_nchunks)
+    int n_chunk_max = 0;  // P + N_E, upper bound of the chunk count
     int n_ablk = 0;       // aux blocks
     size_t off_hist = 0, off_blkbase = 0, off_idx = 0, off_counts = 0, off_offsets = 0;
     size_t off_pdw = 0, off_pdb = 0, off_paux = 0, off_wt = 0;
@@ -56,6 +82,9 @@ struct TimerScope {
 // ---- launchers (each returns the hipError_t of its launch) ----
 hipError_t launch_route(const float* G, int64_t T, int NE, int32_t* idx, int32_t* hist,
                         int n_rblk, hipStream_t s);
+bool scatter_scan_fits(int n_rblk, int NE);
+hipError_t launch_scatter_scan(const int32_t* idx, int64_t T, int NE, const int32_t* hist, int n_rblk,
+                               int32_t* counts, int32_t* offsets, int32_t* perm, hipStream_t s);
 hipError_t launch_scan(const int32_t* hist, int n_rblk, int NE, int32_t* blkbase,
                        int32_t* counts, int32_t* offsets, hipStream_t s);
 hipError_t launch_scatter(const int32_t* idx, int64_t T, int NE, const int32_t* blkbase,
@@ -64,25 +93,21 @@ hipError_t launch_scatter(const int32_t* idx, int64_t T, int NE, const int32_t* 
 hipError_t launch_fwd_gemm_f32(const float* X, const float* W, const float* bias, float* Y,
                                const int32_t* offsets, const int32_t* perm, int64_t T, int H, int NE,
                                hipStream_t s);
-hipError_t launch_dx_gemm_f32(const float* dY, const float* W, float* dX, int accumulate,
-                              const int32_t* offsets, const int32_t* perm, int64_t T, int H, int NE,
-                              hipStream_t s);
-hipError_t launch_dw_gemm_f32(const float* dY, const float* X, float* part_dw, float* part_db,
-                              const int32_t* offsets, const int32_t* perm, int H, int NE, int chunk,
-                              int n_chunk_max, hipStream_t s);
+// dX (overwrite or accumulate) and the d_W / d_b chunk partials, one launch
+hipError_t launch_bwd_gemm_f32(const float* dY, const float* X, const float* W, float* dX, int accumulate,
+                               float* part_dw, float* part_db, const int32_t* offsets, const int32_t* perm,
+                               int64_t T, int H, int NE, int P, int n_chunk_max, hipStream_t s);
 // bf16 storage (raw uint16 patterns), fp32 accumulation
 hipError_t launch_fwd_gemm_bf16(const uint16_t* X, const uint16_t* W, const float* bias, uint16_t* Y,
                                 const int32_t* offsets, const int32_t* perm, int64_t T, int H, int NE,
                                 hipStream_t s);
 hipError_t launch_transpose_w_bf16(const uint16_t* W, uint16_t* Wt, int H, int NE, hipStream_t s);
-hipError_t launch_dx_gemm_bf16(const uint16_t* dY, const uint16_t* W, uint16_t* dX, int accumulate,
-                               const int32_t* offsets, const int32_t* perm, int64_t T, int H, int NE,
-                               hipStream_t s);
-hipError_t launch_dw_gemm_bf16(const uint16_t* dY, const uint16_t* X, float* part_dw, float* part_db,
-                               const int32_t* offsets, const int32_t* perm, int H, int NE, int chunk,
-                               int n_chunk_max, hipStream_t s);
+hipError_t launch_bwd_gemm_bf16(const uint16_t* dY, const uint16_t* X, const uint16_t* Wt, uint16_t* dX,
+                                int accumulate, float* part_dw, float* part_db, const int32_t* offsets,
+                                const int32_t* perm, int64_t T, int H, int NE, int P, int n_chunk_max,
+                                hipStream_t s);
 hipError_t launch_reduce_dw(const float* part_dw, const float* part_db, const int32_t* offsets,
-                            int H, int NE, int chunk, float* dW, float* db, hipStream_t s);
+                            int64_t T, int H, int NE, int P, float* dW, float* db, hipStream_t s);
 
 hipError_t launch_aux_rows(const float* G, const int32_t* counts, int64_t T, int NE, float lam,
                            float* dG, float* probs, float* part, int n_ablk, hipStream_t s);

@@ -7,8 +7,8 @@
 // writer per output and no atomics.  Here the rows are the fixed-size token chunks of
 // one expert (chunk partials, not per-token scratch), so the reduced axis is short.
 //
-// Block (64 x 4): tx owns one float4 column, ty sums chunks ty, ty+4, ... in ascending
-// order, and the four partial sums are added in a fixed order.  An expert with no
+// Block (RX x RY, RX RY = 256): tx owns one float4 column, ty sums chunks ty, ty+RY, ... in
+// ascending order, and the RY partial sums are added in a fixed order.  An expert with no
 // tokens has no chunks and gets +0.0.
 #include "moe_internal.hpp"
 
@@ -19,46 +19,67 @@ __device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<
 __device__ __forceinline__ void st4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
 }  // namespace
 
+// Sums rows [cs, cs + n) of a [rows][len] fp32 array into out[col0 : col0 + 4 RX] (float4
+// lanes); +0.0 when n == 0.  Thread row ty takes rows ty, ty + RY, ... in order, then the RY
+// row sums are added in order.
+template <int RY>
+__device__ __forceinline__ void column_sum(const float* __restrict__ in, size_t len, int cs, int n, size_t col0,
+                                           float* __restrict__ out, f32x4* red) {
+    constexpr int RX = 256 / RY;
+    const int tx = threadIdx.x % RX, ty = threadIdx.x / RX;
+    const size_t col = col0 + 4 * (size_t)tx;
+    const bool ok = col < len;
+    f32x4 s = f32x4{};
+    if (ok) {
+#pragma unroll 8
+        for (int c = ty; c < n; c += RY) s += ld4(in + (size_t)(cs + c) * len + col);
+    }
+    red[ty * RX + tx] = s;
+    __syncthreads();
+    if (ty == 0 && ok) {
+        f32x4 r = red[tx];
+#pragma unroll
+        for (int q = 1; q < RY; ++q) r += red[q * RX + tx];
+        st4(out + col, r);
+    }
+    __syncthreads();
+}
+
+// grid (H*H/(4 RX) + 1, N_E): x < H*H/(4 RX) -> a column tile of dW[e]; the last x -> db[e].
+// RY rows of threads share an expert's chunk rows: 4 when experts have few chunks (wide
+// column tiles, few workgroups), 16 when they can have many (more loads in flight).
+template <int RY>
 __global__ __launch_bounds__(256) void k_reduce_dw(const float* __restrict__ pdw,
                                                    const float* __restrict__ pdb,
                                                    const int* __restrict__ offsets, int H, int NE,
-                                                   int chunk, float* __restrict__ dW,
+                                                   int P, int T, float* __restrict__ dW,
                                                    float* __restrict__ db) {
-    __shared__ f32x4 red[4][64];
+    constexpr int RX = 256 / RY;
+    __shared__ f32x4 red[256];
     const int e = blockIdx.y;
     int cs = 0;
-    for (int i = 0; i < e; ++i) cs += (offsets[i + 1] - offsets[i] + chunk - 1) / chunk;
-    const int n = (offsets[e + 1] - offsets[e] + chunk - 1) / chunk;
-    const int tx = threadIdx.x % 64, ty = threadIdx.x / 64;
+    for (int i = 0; i < e; ++i) cs += expert_nchunks(offsets[i + 1] - offsets[i], P, T);
+    const int n = expert_nchunks(offsets[e + 1] - offsets[e], P, T);
     const size_t HH = (size_t)H * H;
-    const int nbx = (int)(HH / 256);
+    const int nbx = (int)(HH / (4 * RX));
     if ((int)blockIdx.x < nbx) {
-        const size_t col = ((size_t)blockIdx.x * 64 + tx) * 4;
-        f32x4 s = f32x4{};
-        for (int c = ty; c < n; c += 4) s += ld4(pdw + (size_t)(cs + c) * HH + col);
-        red[ty][tx] = s;
-        __syncthreads();
-        if (ty == 0) st4(dW + (size_t)e * HH + col, ((red[0][tx] + red[1][tx]) + red[2][tx]) + red[3][tx]);
+        column_sum<RY>(pdw, HH, cs, n, (size_t)blockIdx.x * 4 * RX, dW + (size_t)e * HH, red);
     } else {
-        for (int c4 = 0; c4 < H / 4; c4 += 64) {
-            const int col = (c4 + tx) * 4;
-            f32x4 s = f32x4{};
-            if (col < H)
-                for (int c = ty; c < n; c += 4) s += ld4(pdb + (size_t)(cs + c) * H + col);
-            red[ty][tx] = s;
-            __syncthreads();
-            if (ty == 0 && col < H)
-                st4(db + (size_t)e * H + col, ((red[0][tx] + red[1][tx]) + red[2][tx]) + red[3][tx]);
-            __syncthreads();
-        }
+        for (int c0 = 0; c0 < H; c0 += 4 * RX) column_sum<RY>(pdb, H, cs, n, c0, db + (size_t)e * H, red);
     }
 }
 
-hipError_t launch_reduce_dw(const float* part_dw, const float* part_db, const int32_t* offsets, int H,
-                            int NE, int chunk, float* dW, float* db, hipStream_t s) {
-    const int nbx = H * H / 256;
-    hipLaunchKernelGGL(k_reduce_dw, dim3(nbx + 1, NE), dim3(256), 0, s, part_dw, part_db, offsets, H, NE,
-                       chunk, dW, db);
+hipError_t launch_reduce_dw(const float* part_dw, const float* part_db, const int32_t* offsets, int64_t T, int H,
+                            int NE, int P, float* dW, float* db, hipStream_t s) {
+    if (P >= 1024) {
+        const int nbx = H * H / (4 * 16);
+        hipLaunchKernelGGL(k_reduce_dw<16>, dim3(nbx + 1, NE), dim3(256), 0, s, part_dw, part_db, offsets, H, NE, P,
+                           (int)T, dW, db);
+    } else {
+        const int nbx = H * H / (4 * 64);
+        hipLaunchKernelGGL(k_reduce_dw<4>, dim3(nbx + 1, NE), dim3(256), 0, s, part_dw, part_db, offsets, H, NE, P,
+                           (int)T, dW, db);
+    }
     return hipGetLastError();
 }
 

@@ -47,7 +47,7 @@ __device__ __forceinline__ int argmax_row4(const float* __restrict__ g, int NE) 
 // Returns the rank (number of lower lanes with the same expert); for every expert that
 // occurs, the lowest such lane stores the wave's count into cnt[e].
 // e < 0 marks an inactive lane.
-__device__ __forceinline__ int wave_rank(int e, int* cnt) {
+__device__ __forceinline__ int wave_rank(int e, int* cnt /* nullable */) {
     const int lane = __lane_id();
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     uint64_t active = __ballot(e >= 0);
@@ -57,7 +57,7 @@ __device__ __forceinline__ int wave_rank(int e, int* cnt) {
         const int el = __builtin_amdgcn_readlane(e, leader);
         const uint64_t m = __ballot(e == el);
         if (e == el) rank = __popcll(m & lt);
-        if (lane == leader) cnt[el] = __popcll(m);
+        if (cnt && lane == leader) cnt[el] = __popcll(m);
         active &= ~m;
     }
     return rank;
@@ -111,6 +111,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(const int* __restrict__ h
     const int b0 = min(nblk, s * L), b1 = min(nblk, b0 + L);
     int sum = 0;
     if (e < NE)
+#pragma unroll 8
         for (int b = b0; b < b1; ++b) sum += hist[(int64_t)b * NE + e];
     tot[s * nep + e] = sum;
     __syncthreads();
@@ -135,6 +136,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(const int* __restrict__ h
     __syncthreads();
     if (e < NE) {
         int run = ex_off[e] + ((s > 0) ? tot[(s - 1) * nep + e] : 0);
+#pragma unroll 8
         for (int b = b0; b < b1; ++b) {
             blkbase[(int64_t)b * NE + e] = run;
             run += hist[(int64_t)b * NE + e];
@@ -185,6 +187,81 @@ __global__ __launch_bounds__(kRouteThreads) void k_scatter(const int* __restrict
             perm[bb[e] + cnt[g][e] + my_rank[j]] = (int)t;
         }
     }
+}
+
+// Scatter with the scan folded in, for small histograms (n_blk x N_E entries): every block
+// sums the histogram columns itself (all blocks -> counts and offsets, earlier blocks -> its
+// own base), so routing is two launches.  Block 0 writes counts and offsets.
+static_assert(kRouteGroups == kRouteThreads / 64, "one 64-token group per wavefront");
+
+__global__ __launch_bounds__(kRouteThreads) void k_scatter_scan(const int* __restrict__ idx, int T, int NE,
+                                                                const int* __restrict__ hist, int nblk,
+                                                                int* __restrict__ counts, int* __restrict__ offsets,
+                                                                int* __restrict__ perm) {
+    __shared__ int cnt[kRouteGroups][kMaxExperts];
+    __shared__ int part[2][kRouteThreads];
+    __shared__ int bb[kMaxExperts];
+    const int tid = threadIdx.x;
+    const int b = blockIdx.x;
+    int nep = 1;
+    while (nep < NE) nep <<= 1;
+    const int S = kRouteThreads / nep;
+    {
+        const int e = tid % nep, sg = tid / nep;
+        int all = 0, before = 0;
+        if (e < NE)
+            for (int x = sg; x < nblk; x += S) {
+                const int v = hist[(int64_t)x * NE + e];
+                all += v;
+                before += (x < b) ? v : 0;
+            }
+        part[0][tid] = all;
+        part[1][tid] = before;
+    }
+    for (int i = tid; i < kRouteGroups * kMaxExperts; i += kRouteThreads) (&cnt[0][0])[i] = 0;
+    __syncthreads();
+    if (tid == 0) {
+        int acc = 0;
+        for (int e = 0; e < NE; ++e) {
+            int tot = 0, bef = 0;
+            for (int sg = 0; sg < S; ++sg) {
+                tot += part[0][sg * nep + e];
+                bef += part[1][sg * nep + e];
+            }
+            bb[e] = acc + bef;
+            if (b == 0) {
+                counts[e] = tot;
+                offsets[e] = acc;
+            }
+            acc += tot;
+        }
+        if (b == 0) offsets[NE] = acc;
+    }
+    __syncthreads();
+    const int wave = tid / 64, lane = tid % 64;
+    const int64_t t = (int64_t)b * kRouteTokens + wave * 64 + lane;
+    const int e = (t < T) ? idx[t] : -1;
+    const int r = wave_rank(e, cnt[wave]);
+    __syncthreads();
+    if (tid < NE) {
+        int run = 0;
+        for (int g = 0; g < kRouteGroups; ++g) {
+            const int c = cnt[g][tid];
+            cnt[g][tid] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    if (e >= 0) perm[bb[e] + cnt[wave][e] + r] = (int)t;
+}
+
+bool scatter_scan_fits(int n_rblk, int NE) { return (int64_t)n_rblk * NE <= 4096; }
+
+hipError_t launch_scatter_scan(const int32_t* idx, int64_t T, int NE, const int32_t* hist, int n_rblk,
+                               int32_t* counts, int32_t* offsets, int32_t* perm, hipStream_t s) {
+    hipLaunchKernelGGL(k_scatter_scan, dim3(n_rblk), dim3(kRouteThreads), 0, s, idx, (int)T, NE, hist, n_rblk, counts,
+                       offsets, perm);
+    return hipGetLastError();
 }
 
 hipError_t launch_route(const float* G, int64_t T, int NE, int32_t* idx, int32_t* hist, int n_rblk,

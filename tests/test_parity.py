@@ -69,6 +69,8 @@ SMALL = {
     "NE7_H256_int_ties": workloads.custom(80, 5, 256, 7, gate="int"),
     "empty_expert": workloads.custom(64, 5, 128, 4, gate_bias={2: -1.0e4}),
     "skewed_lam005": workloads.custom(1000, 5, 128, 8, gate_bias={4: 2.5}, lam=0.05),
+    "multiblock_route_aux_ragged": workloads.custom(8191, 5, 64, 8),
+    "multiblock_NE5_H128": workloads.custom(3001, 13, 128, 5),
     "bf16_H128_NE4": workloads.custom(200, 5, 128, 4, act="bf16"),
     "bf16_H512_NE8": workloads.custom(64, 5, 512, 8, act="bf16"),
     "bf16_H64_NE3_ties": workloads.custom(97, 5, 64, 3, act="bf16", gate="int"),
@@ -148,9 +150,10 @@ def test_accumulate_dx_bf16(gpu_lib):
     C.bf16_scaled("d_fused_ctx (accumulate)", got["dx"].reshape(bw.d_fused_ctx.shape), bw.d_fused_ctx)
 
 
-def test_aux_without_counts_recomputes_them(gpu_lib):
+@pytest.mark.parametrize("B", [500, 9000], ids=["one_workgroup", "multiblock"])
+def test_aux_without_counts_recomputes_them(gpu_lib, B):
     from tests import gpu_run
-    inp = workloads.make_inputs(workloads.custom(500, 5, 64, 6, lam=0.02))
+    inp = workloads.make_inputs(workloads.custom(B, 5, 64, 6, lam=0.02))
     d = gpu_run.upload(inp)
     o = gpu_run.Buffers(d)
     gpu_run.aux(d, o, counts=False)
