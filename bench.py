@@ -126,6 +126,102 @@ def cpu_baseline(inp, budget_s=12.0):
             "sample": f"{reps} x fwd+bwd+aux over the first {n} of {T} tokens ({el:.1f} s, fp64 NumPy)"}
 
 
+def bench_row(args):
+    """One JSON line for a row next to the gate: reduce_axis0, collapse, bwd_from_mean, softmax_ce, lambda."""
+    import numpy as np
+    import torch
+
+    import mixture_experts_top_amd as moe
+    from oracle import next_rows as N
+    moe.load_library()
+    dev = "cuda"
+    g = torch.Generator(device=dev).manual_seed(1234)
+    K = args.steps
+
+    def timed(fn, reps=K, warm=args.warmup):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        return a.elapsed_time(b) / reps * 1e3, (t1 - t0) / reps * 1e3
+
+    def cpu_time(fn, budget=args.cpu_budget / 2):
+        reps, el = 0, 0.0
+        while el < budget and reps < 200:
+            t0 = time.perf_counter()
+            fn()
+            el += time.perf_counter() - t0
+            reps += 1
+        return el / reps, reps
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    row = args.row
+    if row == "reduce_axis0":
+        nb, nt = 20480, 65536  # n_batch = B*N_H (4096 x 5), n_tail = N_E*H*H (4 x 128 x 128)
+        x = torch.randn(nb, nt, device=dev, generator=g)
+        out = torch.empty(nt, device=dev)
+        ws = torch.empty(max(moe.moe_reduce_axis0_workspace_bytes(nb, nt), 16), dtype=torch.uint8, device=dev)
+        us, wall_ms = timed(lambda: moe.moe_reduce_axis0(x, out, workspace=ws))
+        nbytes = nb * nt * 4 + nt * 4
+        xs = x[:2048].cpu().numpy()
+        ct, reps = cpu_time(lambda: N.reduce_axis0(xs))
+        cpu = {"value": xs.nbytes / ct / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+               "sample": f"{reps} x fp64 column sum of the first 2048 of {nb} rows"}
+        cfg = {"workload": "pages_moe_dw_scratch", "n_batch": nb, "n_tail": nt}
+    elif row in ("collapse_fwd", "collapse_bwd"):
+        B, NH, H = 131072, 8, 256
+        x = torch.randn(B, NH, H, device=dev, generator=g)
+        m = torch.randn(B, H, device=dev, generator=g)
+        if row == "collapse_fwd":
+            us, wall_ms = timed(lambda: moe.moe_horizon_mean_collapse_fwd(x, m))
+            xs = x[:8192].cpu().numpy()
+            ct, reps = cpu_time(lambda: N.horizon_mean_fwd(xs))
+        else:
+            us, wall_ms = timed(lambda: moe.moe_horizon_mean_collapse_bwd(m, x))
+            ms_ = m[:8192].cpu().numpy()
+            ct, reps = cpu_time(lambda: N.horizon_mean_bwd(ms_, NH))
+        nbytes = B * NH * H * 4 + B * H * 4
+        cpu = {"value": (8192 * (NH + 1) * H * 8) / ct / 1e9, "unit": "GB/s (fp64)", "cores": int(cores),
+               "kind": "oracle", "sample": f"{reps} x the first 8192 of {B} batch rows"}
+        cfg = {"workload": "large_stress_shape", "B": B, "N_H": NH, "H": H, "act": "f32"}
+    elif row == "softmax_ce":
+        B, NH, A = 131072, 8, 21
+        z = torch.randn(B, NH, A, device=dev, generator=g) * 3
+        lab = torch.randint(0, A, (B, NH), device=dev, generator=g, dtype=torch.int32)
+        lab[:, -1] = -1
+        grad = torch.empty_like(z)
+        ce = torch.empty(B, NH, device=dev)
+        us, wall_ms = timed(lambda: moe.moe_softmax_ce_grad(z, lab, grad, ce))
+        nbytes = B * NH * (A * 8 + 8)
+        zs, ls = z[:4096].cpu().numpy(), lab[:4096].cpu().numpy()
+        ct, reps = cpu_time(lambda: N.softmax_ce(zs, ls))
+        cpu = {"value": 4096 * NH / ct, "unit": "rows/s", "cores": int(cores), "kind": "oracle",
+               "sample": f"{reps} x the first 4096 of {B} batch rows (x{NH} horizons)"}
+        cfg = {"workload": "softmax_ce_21_atoms", "B": B, "N_H": NH, "A": A}
+    else:
+        raise SystemExit(f"unknown --row {row}")
+    achieved = nbytes / (us * 1e-6) / 1e9
+    out = {"metric": f"{row} HBM throughput", "value": achieved, "unit": "GB/s", "n_gpus": 1, "steps": K,
+           "warmup": args.warmup, "ms_per_step": us / 1e3, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded torch generator)", "config": cfg,
+           "roofline": {"bound": "hbm", "kernel": row, "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": achieved / PEAK_HBM_GBS, "traffic": None, "avg_launch_us": us,
+                        "per_launch": f"{nbytes:.4g} byte"},
+           "wall_ms_per_call": wall_ms, "cpu_baseline": cpu}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -140,6 +236,8 @@ def main():
     ap.add_argument("--skip-kernel-survey", action="store_true",
                     help="do not time every kernel first; time --kernel in the timed region")
     ap.add_argument("--kernel", default=None, help="kernel timed live in the timed region (default: the slowest)")
+    ap.add_argument("--row", default="gate",
+                    help="gate (default) | reduce_axis0 | collapse_fwd | collapse_bwd | softmax_ce")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -156,6 +254,9 @@ def main():
     if not torch.cuda.is_available():
         log("no GPU visible")
         sys.exit(1)
+    if args.row != "gate":
+        bench_row(args)
+        return
     moe.load_library()
     wl = workloads.workload(args.workload)
     log(f"[bench] workload {args.workload}: {wl}")

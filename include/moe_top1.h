@@ -157,6 +157,82 @@ moe_status_t moe_aux_loss(const float* gate_logits, const int32_t* expert_counts
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Adaptive load-balancing weight, on the device (adaptive-lambda page "2d0e6b6bdc", formula
+ * and wiring blocks): a single-thread launch computing
+ *   lambda_eff[0] = lambda_floor + lambda_max_extra * max(0, target - ent_ema[0]) / target,
+ *   target = entropy_target_frac * ln(N_E),
+ * so that moe_aux_loss_lambda_dev can read the weight from device memory with no
+ * device-to-host read.  The page's knobs are floor 0.01, max extra 0.09, target fraction 0.7.
+ * ent_ema [1] and lambda_eff [1] are fp32 device pointers (4-byte aligned); N_E in [2, 64];
+ * the knobs must be finite and the target fraction positive, else MOE_ERR_INVALID_ARG.
+ * How ent_ema is produced is up to the caller (the pages do not specify it).
+ */
+moe_status_t moe_lambda_eff_update(const float* ent_ema, float lambda_floor, float lambda_max_extra,
+                                   float entropy_target_frac, int64_t NE, float* lambda_eff, void* stream);
+
+/*
+ * moe_aux_loss with lambda read from device memory (lambda_dev [1], fp32, e.g. the output of
+ * moe_lambda_eff_update) when the kernels run.  Same outputs, errors and workspace as
+ * moe_aux_loss; bitwise equal to it for the same lambda value.
+ */
+moe_status_t moe_aux_loss_lambda_dev(const float* gate_logits, const int32_t* expert_counts,
+                                     const float* lambda_dev, float* loss, float* d_gate_logits,
+                                     float* frac, float* mean_prob, float* probs,
+                                     int64_t B, int64_t NH, int64_t NE,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * reduce_axis0 (perf-pass page "b23f8f2efa", reduce_axis0 entry; MHA page "9170d24fe3",
+ * trainer and BUG blocks): out[j] = sum_{r < n_batch} in[r * n_tail + j] for j < n_tail, fp32,
+ * with a fixed summation order and no atomics (bitwise reproducible for a shape).  The rows
+ * are split into a number of fixed chunks that depends only on (n_batch, n_tail); their
+ * partial sums live in the workspace (moe_reduce_axis0_workspace_bytes; may be 0 bytes, and
+ * then workspace may be NULL).  When n_tail % 4 == 0, in and out must be 16-byte aligned,
+ * else 4-byte aligned.  out is overwritten; in is not modified.
+ */
+moe_status_t moe_reduce_axis0_workspace_bytes(int64_t n_batch, int64_t n_tail, size_t* bytes_out);
+moe_status_t moe_reduce_axis0(const float* in, int64_t n_batch, int64_t n_tail, float* out,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Horizon mean collapse (MHA page "9170d24fe3", new-kernel block) and its backward:
+ *   fwd: ctx_mean[b, :] = (sum_h x[b, h, :]) * (1/N_H)        x [B, N_H, H] -> [B, H]
+ *   bwd: d_x[b, h, :]   = d_ctx_mean[b, :] * (1/N_H)          [B, H] -> [B, N_H, H]
+ * (1/N_H is the fp32 reciprocal; horizons are summed in order h = 0..N_H-1.)  act as for the
+ * gate; H must be a multiple of 4 (fp32) or 8 (bf16); 16-byte aligned pointers.
+ */
+moe_status_t moe_horizon_mean_collapse_fwd(const void* x, void* ctx_mean, int64_t B, int64_t NH,
+                                           int64_t H, int act, void* stream);
+moe_status_t moe_horizon_mean_collapse_bwd(const void* d_ctx_mean, void* d_x, int64_t B, int64_t NH,
+                                           int64_t H, int act, void* stream);
+
+/*
+ * moe_top1_bwd with the horizon mean collapse folded into its input: instead of
+ * d_routed_ctx [B, N_H, H] it takes d_ctx_mean [B, H] and uses
+ *   d_routed_ctx[b, h, :] = d_ctx_mean[b, :] * (1/N_H)
+ * while staging the GEMM operands, so d_routed_ctx is never written or read.  Outputs,
+ * workspace and errors as moe_top1_bwd; bitwise equal to moe_horizon_mean_collapse_bwd
+ * followed by moe_top1_bwd.  fp32 activations only (bf16 -> MOE_ERR_UNSUPPORTED).
+ */
+moe_status_t moe_top1_bwd_from_mean(const float* d_ctx_mean, const void* fused_ctx, const void* W,
+                                    const int32_t* expert_offsets, const int32_t* perm,
+                                    void* d_fused_ctx, float* d_W, float* d_b, int accumulate_dx,
+                                    int64_t B, int64_t NH, int64_t H, int64_t NE, int act,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Softmax + cross-entropy gradient head (softmax/cross-entropy page "6cfd7e6691", kernel
+ * block), per (b, h) row of A atom logits (A in [1, 64]; the page uses 21):
+ *   p = softmax(logits[b, h, :]) (max-shifted), ce[b, h] = -log(max(p[label], 1e-30)),
+ *   grad[b, h, :] = (p - onehot(label)) * (1/B)
+ * label = labels[b, h]; a label of -1 (sentinel), or any label outside [0, A), gives
+ * ce = 0 and a zero gradient row.  logits, grad [B, N_H, A] fp32; labels [B, N_H] int32;
+ * ce [B, N_H] fp32; 4-byte aligned.  Scaling / summing the loss is left to the caller.
+ */
+moe_status_t moe_softmax_ce_grad(const float* logits, const int32_t* labels, float* grad, float* ce,
+                                 int64_t B, int64_t NH, int64_t A, void* stream);
+
+/*
  * Instrumentation.  While set, every launch of kernel `kernel_id` (MOE_KERNEL_*) made by
  * the calls above is bracketed by hipEventRecord(ev_start) and hipEventRecord(ev_stop) on
  * the call's stream.  The events are hipEvent_t handles created by the caller.  Pass
@@ -172,7 +248,11 @@ enum {
     MOE_KERNEL_AUX = 6,          /* softmax, dG, per-block column sums of p */
     MOE_KERNEL_AUX_FINAL = 7,    /* mean_prob, frac, loss */
     MOE_KERNEL_W_TRANSPOSE = 8,  /* bf16 backward only: W^T staged for the dX GEMM */
-    MOE_KERNEL_COUNT = 9
+    MOE_KERNEL_LAMBDA = 9,       /* adaptive lambda update */
+    MOE_KERNEL_REDUCE_AXIS0 = 10,/* standalone reduce_axis0 */
+    MOE_KERNEL_COLLAPSE = 11,    /* horizon mean collapse, forward or backward */
+    MOE_KERNEL_SOFTMAX_CE = 12,  /* softmax + cross-entropy gradient head */
+    MOE_KERNEL_COUNT = 13
 };
 moe_status_t moe_set_launch_timer(int kernel_id, void* ev_start, void* ev_stop);
 

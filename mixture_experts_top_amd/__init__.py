@@ -15,12 +15,15 @@ from typing import Optional
 __all__ = [
     "load_library", "library_path", "moe_abi_version", "moe_workspace_bytes", "moe_top1_route",
     "moe_top1_fwd", "moe_top1_bwd", "moe_aux_loss", "moe_set_launch_timer", "moe_kernel_name",
-    "MoeError", "KERNELS", "DTYPE_F32", "DTYPE_BF16",
+    "moe_lambda_eff_update", "moe_aux_loss_lambda_dev", "moe_reduce_axis0", "moe_reduce_axis0_workspace_bytes",
+    "moe_horizon_mean_collapse_fwd", "moe_horizon_mean_collapse_bwd", "moe_top1_bwd_from_mean",
+    "moe_softmax_ce_grad", "MoeError", "KERNELS", "DTYPE_F32", "DTYPE_BF16",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 DTYPE_F32, DTYPE_BF16 = 0, 1
-KERNELS = ["route", "scan", "scatter", "fwd_gemm", "bwd_gemm", "reduce", "aux", "aux_final", "w_transpose"]
+KERNELS = ["route", "scan", "scatter", "fwd_gemm", "bwd_gemm", "reduce", "aux", "aux_final", "w_transpose",
+           "lambda_update", "reduce_axis0", "collapse", "softmax_ce"]
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -59,6 +62,14 @@ def load_library() -> ctypes.CDLL:
         "moe_top1_bwd": ([P, P, P, P, P, P, P, P, I32, I64, I64, I64, I64, I32, P, SZ, P], I32),
         "moe_aux_loss": ([P, P, ctypes.c_float, P, P, P, P, P, I64, I64, I64, P, SZ, P], I32),
         "moe_set_launch_timer": ([I32, P, P], I32),
+        "moe_lambda_eff_update": ([P, ctypes.c_float, ctypes.c_float, ctypes.c_float, I64, P, P], I32),
+        "moe_aux_loss_lambda_dev": ([P, P, P, P, P, P, P, P, I64, I64, I64, P, SZ, P], I32),
+        "moe_reduce_axis0_workspace_bytes": ([I64, I64, ctypes.POINTER(SZ)], I32),
+        "moe_reduce_axis0": ([P, I64, I64, P, P, SZ, P], I32),
+        "moe_horizon_mean_collapse_fwd": ([P, P, I64, I64, I64, I32, P], I32),
+        "moe_horizon_mean_collapse_bwd": ([P, P, I64, I64, I64, I32, P], I32),
+        "moe_top1_bwd_from_mean": ([P, P, P, P, P, P, P, P, I32, I64, I64, I64, I64, I32, P, SZ, P], I32),
+        "moe_softmax_ce_grad": ([P, P, P, P, I64, I64, I64, P], I32),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -213,6 +224,101 @@ def moe_aux_loss(gate_logits, expert_counts, lam, loss, d_gate_logits, frac=None
     _check(load_library().moe_aux_loss(_ptr(gate_logits), _ptr(expert_counts), float(lam), _ptr(loss),
                                        _ptr(d_gate_logits), _ptr(frac), _ptr(mean_prob), _ptr(probs),
                                        B, NH, NE, _ptr(ws), wsb, _stream(stream)))
+
+
+def moe_lambda_eff_update(ent_ema, lambda_eff, NE, lambda_floor=0.01, lambda_max_extra=0.09,
+                          entropy_target_frac=0.7, stream=None):
+    import torch
+    _expect(ent_ema, "ent_ema", (1,), torch.float32)
+    _expect(lambda_eff, "lambda_eff", (1,), torch.float32)
+    _check(load_library().moe_lambda_eff_update(_ptr(ent_ema), float(lambda_floor), float(lambda_max_extra),
+                                                float(entropy_target_frac), int(NE), _ptr(lambda_eff),
+                                                _stream(stream)))
+
+
+def moe_aux_loss_lambda_dev(gate_logits, expert_counts, lambda_dev, loss, d_gate_logits, frac=None, mean_prob=None,
+                            probs=None, workspace=None, stream=None):
+    import torch
+    B, NH, NE = _shape3(gate_logits, "gate_logits")
+    _expect(gate_logits, "gate_logits", (B, NH, NE), torch.float32)
+    _expect(expert_counts, "expert_counts", (NE,), torch.int32)
+    _expect(lambda_dev, "lambda_dev", (1,), torch.float32)
+    _expect(loss, "loss", (1,), torch.float32)
+    _expect(d_gate_logits, "d_gate_logits", (B, NH, NE), torch.float32)
+    _expect(frac, "frac", (NE,), torch.float32)
+    _expect(mean_prob, "mean_prob", (NE,), torch.float32)
+    _expect(probs, "probs", (B, NH, NE), torch.float32)
+    ws, wsb = _workspace(workspace, B, NH, 64, NE, DTYPE_F32, gate_logits.device)
+    _check(load_library().moe_aux_loss_lambda_dev(_ptr(gate_logits), _ptr(expert_counts), _ptr(lambda_dev),
+                                                  _ptr(loss), _ptr(d_gate_logits), _ptr(frac), _ptr(mean_prob),
+                                                  _ptr(probs), B, NH, NE, _ptr(ws), wsb, _stream(stream)))
+
+
+def moe_reduce_axis0_workspace_bytes(n_batch: int, n_tail: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load_library().moe_reduce_axis0_workspace_bytes(n_batch, n_tail, ctypes.byref(out)))
+    return out.value
+
+
+def moe_reduce_axis0(inp, out, workspace=None, stream=None):
+    """inp [n_batch, n_tail] fp32 -> out [n_tail]."""
+    import torch
+    if inp.dim() != 2:
+        raise ValueError("inp must be [n_batch, n_tail]")
+    n_batch, n_tail = (int(x) for x in inp.shape)
+    _expect(inp, "inp", (n_batch, n_tail), torch.float32)
+    _expect(out, "out", (n_tail,), torch.float32)
+    need = moe_reduce_axis0_workspace_bytes(n_batch, n_tail)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=inp.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().moe_reduce_axis0(_ptr(inp), n_batch, n_tail, _ptr(out), _ptr(workspace), wsb,
+                                           _stream(stream)))
+
+
+def moe_horizon_mean_collapse_fwd(x, ctx_mean, stream=None):
+    B, NH, H = _shape3(x, "x")
+    _expect(ctx_mean, "ctx_mean", (B, H), x.dtype)
+    _check(load_library().moe_horizon_mean_collapse_fwd(_ptr(x), _ptr(ctx_mean), B, NH, H, _act(x), _stream(stream)))
+
+
+def moe_horizon_mean_collapse_bwd(d_ctx_mean, d_x, stream=None):
+    B, NH, H = _shape3(d_x, "d_x")
+    _expect(d_ctx_mean, "d_ctx_mean", (B, H), d_x.dtype)
+    _check(load_library().moe_horizon_mean_collapse_bwd(_ptr(d_ctx_mean), _ptr(d_x), B, NH, H, _act(d_x),
+                                                        _stream(stream)))
+
+
+def moe_top1_bwd_from_mean(d_ctx_mean, fused_ctx, W, expert_offsets, perm, d_fused_ctx, d_W, d_b,
+                           accumulate_dx=False, workspace=None, stream=None):
+    import torch
+    B, NH, H = _shape3(fused_ctx, "fused_ctx")
+    NE = int(W.shape[0])
+    T = B * NH
+    act = _act(fused_ctx)
+    _expect(d_ctx_mean, "d_ctx_mean", (B, H), torch.float32)
+    _expect(W, "W", (NE, H, H), fused_ctx.dtype)
+    _expect(expert_offsets, "expert_offsets", (NE + 1,), torch.int32)
+    _expect(perm, "perm", (T,), torch.int32)
+    _expect(d_fused_ctx, "d_fused_ctx", (B, NH, H), fused_ctx.dtype)
+    _expect(d_W, "d_W", (NE, H, H), torch.float32)
+    _expect(d_b, "d_b", (NE, H), torch.float32)
+    ws, wsb = _workspace(workspace, B, NH, H, NE, act, fused_ctx.device)
+    _check(load_library().moe_top1_bwd_from_mean(_ptr(d_ctx_mean), _ptr(fused_ctx), _ptr(W), _ptr(expert_offsets),
+                                                 _ptr(perm), _ptr(d_fused_ctx), _ptr(d_W), _ptr(d_b),
+                                                 int(bool(accumulate_dx)), B, NH, H, NE, act, _ptr(ws), wsb,
+                                                 _stream(stream)))
+
+
+def moe_softmax_ce_grad(logits, labels, grad, ce, stream=None):
+    import torch
+    B, NH, A = _shape3(logits, "logits")
+    _expect(logits, "logits", (B, NH, A), torch.float32)
+    _expect(labels, "labels", (B, NH), torch.int32)
+    _expect(grad, "grad", (B, NH, A), torch.float32)
+    _expect(ce, "ce", (B, NH), torch.float32)
+    _check(load_library().moe_softmax_ce_grad(_ptr(logits), _ptr(labels), _ptr(grad), _ptr(ce), B, NH, A,
+                                              _stream(stream)))
 
 
 def moe_set_launch_timer(kernel, ev_start=None, ev_stop=None):

@@ -18,11 +18,14 @@ namespace moe {
 template <int NEB>
 __global__ __launch_bounds__(kAuxThreads) void k_aux_rows(const float* __restrict__ G,
                                                           const int* __restrict__ counts, int T,
-                                                          int NE, float lam, float* __restrict__ dG,
+                                                          int NE, float lam_value,
+                                                          const float* __restrict__ lam_dev,
+                                                          float* __restrict__ dG,
                                                           float* __restrict__ probs,
                                                           float* __restrict__ part) {
     __shared__ float red[kAuxThreads / 64][NEB];
     const int tid = threadIdx.x;
+    const float lam = lam_dev ? lam_dev[0] : lam_value;
     float frac[NEB], psum[NEB];
 #pragma unroll
     for (int e = 0; e < NEB; ++e) {
@@ -110,7 +113,8 @@ __global__ __launch_bounds__(kAuxThreads) void k_aux_rows(const float* __restric
 // are then added in order; mean_prob, frac and the loss follow.
 __global__ __launch_bounds__(256) void k_aux_final(const float* __restrict__ part,
                                                    const int* __restrict__ counts, int nblk, int T,
-                                                   int NE, float lam, float* __restrict__ loss,
+                                                   int NE, float lam_value, const float* __restrict__ lam_dev,
+                                                   float* __restrict__ loss,
                                                    float* __restrict__ frac_out,
                                                    float* __restrict__ mean_prob_out) {
     __shared__ float acc[256];
@@ -137,31 +141,49 @@ __global__ __launch_bounds__(256) void k_aux_final(const float* __restrict__ par
     }
     __syncthreads();
     if (tid == 0) {
+        const float lam = lam_dev ? lam_dev[0] : lam_value;
         double d = 0.0;
         for (int x = 0; x < NE; ++x) d += (double)fr[x] * (double)mp[x];
         loss[0] = (float)((double)lam * (double)NE * d);
     }
 }
 
-hipError_t launch_aux_rows(const float* G, const int32_t* counts, int64_t T, int NE, float lam, float* dG,
-                           float* probs, float* part, int n_ablk, hipStream_t s) {
+// Adaptive load-balancing weight (adaptive-lambda page, formula block), one thread:
+//   lambda_eff = floor + max_extra * max(0, target - ent_ema) / target,  target = frac_t * ln(K)
+__global__ void k_lambda_eff(const float* __restrict__ ent_ema, float floor_, float max_extra, float target_frac,
+                             int K, float* __restrict__ lambda_eff) {
+    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    const double target = (double)target_frac * log((double)K);
+    const double deficit = fmax(0.0, target - (double)ent_ema[0]);
+    lambda_eff[0] = (float)((double)floor_ + (double)max_extra * deficit / target);
+}
+
+hipError_t launch_lambda_eff(const float* ent_ema, float floor_, float max_extra, float target_frac, int K,
+                             float* lambda_eff, hipStream_t s) {
+    hipLaunchKernelGGL(k_lambda_eff, dim3(1), dim3(64), 0, s, ent_ema, floor_, max_extra, target_frac, K, lambda_eff);
+    return hipGetLastError();
+}
+
+hipError_t launch_aux_rows(const float* G, const int32_t* counts, int64_t T, int NE, float lam, const float* lam_dev,
+                           float* dG, float* probs, float* part, int n_ablk, hipStream_t s) {
     dim3 grid(n_ablk), block(kAuxThreads);
     if (NE <= 4)
-        hipLaunchKernelGGL(k_aux_rows<4>, grid, block, 0, s, G, counts, (int)T, NE, lam, dG, probs, part);
+        hipLaunchKernelGGL(k_aux_rows<4>, grid, block, 0, s, G, counts, (int)T, NE, lam, lam_dev, dG, probs, part);
     else if (NE <= 8)
-        hipLaunchKernelGGL(k_aux_rows<8>, grid, block, 0, s, G, counts, (int)T, NE, lam, dG, probs, part);
+        hipLaunchKernelGGL(k_aux_rows<8>, grid, block, 0, s, G, counts, (int)T, NE, lam, lam_dev, dG, probs, part);
     else if (NE <= 16)
-        hipLaunchKernelGGL(k_aux_rows<16>, grid, block, 0, s, G, counts, (int)T, NE, lam, dG, probs, part);
+        hipLaunchKernelGGL(k_aux_rows<16>, grid, block, 0, s, G, counts, (int)T, NE, lam, lam_dev, dG, probs, part);
     else if (NE <= 32)
-        hipLaunchKernelGGL(k_aux_rows<32>, grid, block, 0, s, G, counts, (int)T, NE, lam, dG, probs, part);
+        hipLaunchKernelGGL(k_aux_rows<32>, grid, block, 0, s, G, counts, (int)T, NE, lam, lam_dev, dG, probs, part);
     else
-        hipLaunchKernelGGL(k_aux_rows<64>, grid, block, 0, s, G, counts, (int)T, NE, lam, dG, probs, part);
+        hipLaunchKernelGGL(k_aux_rows<64>, grid, block, 0, s, G, counts, (int)T, NE, lam, lam_dev, dG, probs, part);
     return hipGetLastError();
 }
 
 hipError_t launch_aux_final(const float* part, const int32_t* counts, int n_ablk, int64_t T, int NE,
-                            float lam, float* loss, float* frac, float* mean_prob, hipStream_t s) {
-    hipLaunchKernelGGL(k_aux_final, dim3(1), dim3(256), 0, s, part, counts, n_ablk, (int)T, NE, lam, loss,
+                            float lam, const float* lam_dev, float* loss, float* frac, float* mean_prob,
+                            hipStream_t s) {
+    hipLaunchKernelGGL(k_aux_final, dim3(1), dim3(256), 0, s, part, counts, n_ablk, (int)T, NE, lam, lam_dev, loss,
                        frac, mean_prob);
     return hipGetLastError();
 }

@@ -1,0 +1,99 @@
+// Horizon mean collapse (MHA page "9170d24fe3", new-kernel block): [B, N_H, H] -> [B, H] by
+// averaging over the horizon axis, single pass, no cross-thread reduction; its backward
+// gives every horizon d_out[b] / N_H.  Both scale by the fp32 reciprocal of N_H.
+//
+// One thread per (b, 16-byte column group): the forward sums the N_H rows of its column in
+// horizon order, so accesses are coalesced along H and the result is deterministic.
+#include "moe_internal.hpp"
+
+namespace moe {
+
+namespace {
+__device__ __forceinline__ float bf(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+__device__ __forceinline__ uint16_t to_bf(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+}  // namespace
+
+__global__ __launch_bounds__(256) void k_collapse_fwd_f32(const float* __restrict__ x, float* __restrict__ out,
+                                                          int64_t B, int NH, int H) {
+    const int q = H / 4;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= B * q) return;
+    const int64_t b = i / q, c = (i % q) * 4;
+    const float inv = 1.0f / (float)NH;
+    f32x4 s = f32x4{};
+    for (int h = 0; h < NH; ++h) s += *reinterpret_cast<const f32x4*>(x + (b * NH + h) * H + c);
+    *reinterpret_cast<f32x4*>(out + b * H + c) = s * inv;
+}
+
+__global__ __launch_bounds__(256) void k_collapse_bwd_f32(const float* __restrict__ dout, float* __restrict__ dx,
+                                                          int64_t B, int NH, int H) {
+    const int q = H / 4;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over B * NH * q
+    if (i >= B * NH * q) return;
+    const int64_t row = i / q, c = (i % q) * 4;
+    const int64_t b = row / NH;
+    const float inv = 1.0f / (float)NH;
+    *reinterpret_cast<f32x4*>(dx + row * H + c) = *reinterpret_cast<const f32x4*>(dout + b * H + c) * inv;
+}
+
+__global__ __launch_bounds__(256) void k_collapse_fwd_bf16(const uint16_t* __restrict__ x, uint16_t* __restrict__ out,
+                                                           int64_t B, int NH, int H) {
+    const int q = H / 8;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= B * q) return;
+    const int64_t b = i / q, c = (i % q) * 8;
+    const float inv = 1.0f / (float)NH;
+    float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int h = 0; h < NH; ++h) {
+        const u16x8 v = *reinterpret_cast<const u16x8*>(x + (b * NH + h) * H + c);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s[j] += bf(v[j]);
+    }
+    u16x8 o;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = to_bf(s[j] * inv);
+    *reinterpret_cast<u16x8*>(out + b * H + c) = o;
+}
+
+__global__ __launch_bounds__(256) void k_collapse_bwd_bf16(const uint16_t* __restrict__ dout, uint16_t* __restrict__ dx,
+                                                           int64_t B, int NH, int H) {
+    const int q = H / 8;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= B * NH * q) return;
+    const int64_t row = i / q, c = (i % q) * 8;
+    const int64_t b = row / NH;
+    const float inv = 1.0f / (float)NH;
+    const u16x8 v = *reinterpret_cast<const u16x8*>(dout + b * H + c);
+    u16x8 o;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = to_bf(bf(v[j]) * inv);
+    *reinterpret_cast<u16x8*>(dx + row * H + c) = o;
+}
+
+hipError_t launch_collapse(bool bwd, int act, const void* in, void* out, int64_t B, int NH, int H, hipStream_t s) {
+    const int per = (act == 0) ? 4 : 8;
+    const int64_t n = (bwd ? B * NH : B) * (H / per);
+    const dim3 grid((unsigned)((n + 255) / 256));
+    if (act == 0) {
+        if (bwd)
+            hipLaunchKernelGGL(k_collapse_bwd_f32, grid, dim3(256), 0, s, (const float*)in, (float*)out, B, NH, H);
+        else
+            hipLaunchKernelGGL(k_collapse_fwd_f32, grid, dim3(256), 0, s, (const float*)in, (float*)out, B, NH, H);
+    } else {
+        if (bwd)
+            hipLaunchKernelGGL(k_collapse_bwd_bf16, grid, dim3(256), 0, s, (const uint16_t*)in, (uint16_t*)out, B, NH,
+                               H);
+        else
+            hipLaunchKernelGGL(k_collapse_fwd_bf16, grid, dim3(256), 0, s, (const uint16_t*)in, (uint16_t*)out, B, NH,
+                               H);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -82,14 +82,15 @@ __device__ __forceinline__ void xcd_split(int bid, int per, int& major, int& min
 // issued into registers before the MFMAs of slice c, and stored to the other buffer after
 // them, so one barrier per slice suffices and load latency hides behind the MFMAs.
 // ----------------------------------------------------------------------------------
-template <int H, int BM, int BN, int KC, bool DX>
+template <int H, int BM, int BN, int KC, bool DX, bool MEAN = false>
 __device__ __forceinline__ void rows_f32_body(int bid, const float* __restrict__ A,
                                                         const float* __restrict__ W,
                                                         const float* __restrict__ bias,
                                                         float* __restrict__ Out,
                                                         const int* __restrict__ offsets,
                                                         const int* __restrict__ perm, int NE,
-                                                        int accumulate) {
+                                                        int accumulate, int nh = 1, float inv_nh = 1.0f) {
+    // MEAN: row t of A is A[t / nh] * inv_nh (the backward of a mean over nh horizons)
     constexpr int NKC = H / KC;
     constexpr int NT = H / BN;
     constexpr int WM = (BM >= 64) ? 2 : 1, WN = 4 / WM;  // wavefront grid over the tile
@@ -124,12 +125,16 @@ __device__ __forceinline__ void rows_f32_body(int bid, const float* __restrict__
 #pragma unroll
     for (int i = 0; i < AL; ++i) {
         const int t = tok[tid / TPR + RPP * i];
-        a_src[i] = (t >= 0) ? A + (size_t)t * H + 4 * (tid % TPR) : nullptr;
+        const int row = MEAN ? t / nh : t;
+        a_src[i] = (t >= 0) ? A + (size_t)row * H + 4 * (tid % TPR) : nullptr;
     }
     f32x4 ra[AL], rb[BL];
     auto load_slice = [&](int k0) {
 #pragma unroll
-        for (int i = 0; i < AL; ++i) ra[i] = a_src[i] ? ld4(a_src[i] + k0) : f32x4{};
+        for (int i = 0; i < AL; ++i) {
+            ra[i] = a_src[i] ? ld4(a_src[i] + k0) : f32x4{};
+            if (MEAN) ra[i] *= inv_nh;
+        }
 #pragma unroll
         for (int i = 0; i < BL; ++i) {
             if (!DX) {
@@ -224,14 +229,14 @@ __device__ __forceinline__ void rows_f32_body(int bid, const float* __restrict__
 // Same two-buffer pipeline as the row GEMM; token ids of slice c+2 are fetched while slice
 // c+1's rows are being loaded, so the gather never waits on an index load.
 // ----------------------------------------------------------------------------------
-template <int H, int KC>
+template <int H, int KC, bool MEAN = false>
 __device__ __forceinline__ void dw_f32_body(int bid, const float* __restrict__ dY,
                                                       const float* __restrict__ X,
                                                       float* __restrict__ part_dw,
                                                       float* __restrict__ part_db,
                                                       const int* __restrict__ offsets,
                                                       const int* __restrict__ perm, int NE,
-                                                      int P, int T) {
+                                                      int P, int T, int nh = 1, float inv_nh = 1.0f) {
     constexpr int BT = (H >= 128) ? 128 : 64;
     constexpr int NTI = H / BT, TPC = NTI * NTI;
     constexpr int WT = BT / 2, SUB = WT / 32;
@@ -275,7 +280,11 @@ __device__ __forceinline__ void dw_f32_body(int bid, const float* __restrict__ d
             rb[i] = f32x4{};
             if (tk[i] >= 0) {
                 const size_t t = (size_t)tk[i];
-                ra[i] = ld4(dY + t * H + o0 + cc);
+                if (MEAN) {
+                    ra[i] = ld4(dY + (t / nh) * H + o0 + cc) * inv_nh;
+                } else {
+                    ra[i] = ld4(dY + t * H + o0 + cc);
+                }
                 rb[i] = ld4(X + t * H + i0 + cc);
             }
         }
@@ -352,18 +361,19 @@ __global__ __launch_bounds__(kThreads) void k_fwd_f32(const float* __restrict__ 
     rows_f32_body<H, BM, BN, KC, false>(blockIdx.x, X, W, bias, Y, offsets, perm, NE, 0);
 }
 
-template <int H, int BM, int BN, int KCX, int KCW>
+template <int H, int BM, int BN, int KCX, int KCW, bool MEAN>
 __global__ __launch_bounds__(kThreads) void k_bwd_f32(const float* __restrict__ dY, const float* __restrict__ X,
                                                        const float* __restrict__ W, float* __restrict__ dX,
                                                        int accumulate, float* __restrict__ part_dw,
                                                        float* __restrict__ part_db,
                                                        const int* __restrict__ offsets,
                                                        const int* __restrict__ perm, int NE, int P, int T,
-                                                       int n_dx) {
+                                                       int n_dx, int nh, float inv_nh) {
     if ((int)blockIdx.x < n_dx)
-        rows_f32_body<H, BM, BN, KCX, true>(blockIdx.x, dY, W, nullptr, dX, offsets, perm, NE, accumulate);
+        rows_f32_body<H, BM, BN, KCX, true, MEAN>(blockIdx.x, dY, W, nullptr, dX, offsets, perm, NE, accumulate, nh,
+                                                  inv_nh);
     else
-        dw_f32_body<H, KCW>(blockIdx.x - n_dx, dY, X, part_dw, part_db, offsets, perm, NE, P, T);
+        dw_f32_body<H, KCW, MEAN>(blockIdx.x - n_dx, dY, X, part_dw, part_db, offsets, perm, NE, P, T, nh, inv_nh);
 }
 
 // ----------------------------------------------------------------------------------
@@ -409,21 +419,22 @@ static hipError_t fwd_f32(const float* X, const float* W, const float* bias, flo
     return hipGetLastError();
 }
 
-template <int H>
+template <int H, bool MEAN>
 static hipError_t bwd_f32(const float* dY, const float* X, const float* W, float* dX, int accumulate, float* pdw,
                           float* pdb, const int32_t* offsets, const int32_t* perm, int64_t T, int NE, int P,
-                          int n_chunk_max, hipStream_t s) {
+                          int n_chunk_max, int nh, hipStream_t s) {
     constexpr int BN = (H >= 128) ? 128 : H;
     const int bm = rows_bm<H>(T);
     const int n_dx = rows_grid<H>(T, NE, bm);
     const int grid = n_dx + dw_grid<H>(n_chunk_max);
+    const float inv_nh = 1.0f / (float)nh;
     if (bm == 128)
-        hipLaunchKernelGGL((k_bwd_f32<H, 128, BN, MOE_F32_KC_DX, MOE_F32_KC_DW>), dim3(grid), dim3(kThreads), 0, s,
-                           dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, NE, P, (int)T, n_dx);
+        hipLaunchKernelGGL((k_bwd_f32<H, 128, BN, MOE_F32_KC_DX, MOE_F32_KC_DW, MEAN>), dim3(grid), dim3(kThreads), 0,
+                           s, dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, NE, P, (int)T, n_dx, nh, inv_nh);
     else
-        hipLaunchKernelGGL((k_bwd_f32<H, MOE_ROWS_SMALL_BM, BN, MOE_F32_KC_DX, MOE_F32_KC_DW>), dim3(grid),
+        hipLaunchKernelGGL((k_bwd_f32<H, MOE_ROWS_SMALL_BM, BN, MOE_F32_KC_DX, MOE_F32_KC_DW, MEAN>), dim3(grid),
                            dim3(kThreads), 0, s, dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, NE, P, (int)T,
-                           n_dx);
+                           n_dx, nh, inv_nh);
     return hipGetLastError();
 }
 
@@ -438,16 +449,34 @@ hipError_t launch_fwd_gemm_f32(const float* X, const float* W, const float* bias
     return hipErrorInvalidValue;
 }
 
+template <bool MEAN>
+static hipError_t bwd_f32_h(const float* dY, const float* X, const float* W, float* dX, int accumulate, float* pdw,
+                            float* pdb, const int32_t* offsets, const int32_t* perm, int64_t T, int H, int NE, int P,
+                            int n_chunk_max, int nh, hipStream_t s) {
+    switch (H) {
+        case 64:
+            return bwd_f32<64, MEAN>(dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, T, NE, P, n_chunk_max, nh, s);
+        case 128:
+            return bwd_f32<128, MEAN>(dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, T, NE, P, n_chunk_max, nh, s);
+        case 256:
+            return bwd_f32<256, MEAN>(dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, T, NE, P, n_chunk_max, nh, s);
+        case 512:
+            return bwd_f32<512, MEAN>(dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, T, NE, P, n_chunk_max, nh, s);
+    }
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_bwd_gemm_f32(const float* dY, const float* X, const float* W, float* dX, int accumulate,
                                float* pdw, float* pdb, const int32_t* offsets, const int32_t* perm, int64_t T, int H,
                                int NE, int P, int n_chunk_max, hipStream_t s) {
-    switch (H) {
-        case 64: return bwd_f32<64>(dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, T, NE, P, n_chunk_max, s);
-        case 128: return bwd_f32<128>(dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, T, NE, P, n_chunk_max, s);
-        case 256: return bwd_f32<256>(dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, T, NE, P, n_chunk_max, s);
-        case 512: return bwd_f32<512>(dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, T, NE, P, n_chunk_max, s);
-    }
-    return hipErrorInvalidValue;
+    return bwd_f32_h<false>(dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, T, H, NE, P, n_chunk_max, 1, s);
+}
+
+hipError_t launch_bwd_gemm_f32_from_mean(const float* d_mean, const float* X, const float* W, float* dX,
+                                         int accumulate, float* pdw, float* pdb, const int32_t* offsets,
+                                         const int32_t* perm, int64_t T, int H, int NE, int NH, int P,
+                                         int n_chunk_max, hipStream_t s) {
+    return bwd_f32_h<true>(d_mean, X, W, dX, accumulate, pdw, pdb, offsets, perm, T, H, NE, P, n_chunk_max, NH, s);
 }
 
 }  // namespace moe

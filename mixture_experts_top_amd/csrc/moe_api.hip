@@ -180,7 +180,8 @@ const char* moe_last_error(void) { return g_err; }
 
 const char* moe_kernel_name(int k) {
     static const char* names[K_COUNT] = {"route", "scan", "scatter", "fwd_gemm", "bwd_gemm",
-                                         "reduce", "aux", "aux_final", "w_transpose"};
+                                         "reduce", "aux", "aux_final", "w_transpose", "lambda_update",
+                                         "reduce_axis0", "collapse", "softmax_ce"};
     return (k >= 0 && k < K_COUNT) ? names[k] : nullptr;
 }
 
@@ -252,48 +253,71 @@ moe_status_t moe_top1_fwd(const void* fused_ctx, const float* gate_logits, const
     return MOE_OK;
 }
 
-moe_status_t moe_top1_bwd(const void* d_routed_ctx, const void* fused_ctx, const void* W,
-                          const int32_t* expert_offsets, const int32_t* perm, void* d_fused_ctx, float* d_W,
-                          float* d_b, int accumulate_dx, int64_t B, int64_t NH, int64_t H, int64_t NE, int act,
-                          void* workspace, size_t workspace_bytes, void* stream) {
-    const char* fn = "moe_top1_bwd";
+static moe_status_t bwd_impl(const char* fn, const void* dy, int from_mean, const void* fused_ctx, const void* W,
+                             const int32_t* expert_offsets, const int32_t* perm, void* d_fused_ctx, float* d_W,
+                             float* d_b, int accumulate_dx, int64_t B, int64_t NH, int64_t H, int64_t NE, int act,
+                             void* workspace, size_t workspace_bytes, void* stream) {
     moe_status_t st = check_shape(fn, B, NH, H, NE, act, true);
     if (st != MOE_OK) return st;
-    REQ(d_routed_ctx); REQ(fused_ctx); REQ(W); REQ(expert_offsets); REQ(perm);
+    if (from_mean && act != MOE_DTYPE_F32)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: only fp32 activations are supported", fn);
+    REQ(dy); REQ(fused_ctx); REQ(W); REQ(expert_offsets); REQ(perm);
     REQ(d_fused_ctx); REQ(d_W); REQ(d_b);
     const Plan p = make_plan(B * NH, (int)H, (int)NE, act);
     if ((st = check_ws(fn, p, workspace, workspace_bytes)) != MOE_OK) return st;
     hipStream_t s = (hipStream_t)stream;
     float* pdw = at<float>(workspace, p.off_pdw);
     float* pdb = at<float>(workspace, p.off_pdb);
-    if (act == MOE_DTYPE_F32) {
+    if (from_mean) {
         LAUNCH(K_BWD_GEMM,
-               launch_bwd_gemm_f32((const float*)d_routed_ctx, (const float*)fused_ctx, (const float*)W,
-                                   (float*)d_fused_ctx, accumulate_dx, pdw, pdb, expert_offsets, perm, p.T, p.H,
-                                   p.NE, p.chunks, p.n_chunk_max, s),
+               launch_bwd_gemm_f32_from_mean((const float*)dy, (const float*)fused_ctx, (const float*)W,
+                                             (float*)d_fused_ctx, accumulate_dx, pdw, pdb, expert_offsets, perm, p.T,
+                                             p.H, p.NE, (int)NH, p.chunks, p.n_chunk_max, s),
+               "bwd gemm (from mean)");
+    } else if (act == MOE_DTYPE_F32) {
+        LAUNCH(K_BWD_GEMM,
+               launch_bwd_gemm_f32((const float*)dy, (const float*)fused_ctx, (const float*)W, (float*)d_fused_ctx,
+                                   accumulate_dx, pdw, pdb, expert_offsets, perm, p.T, p.H, p.NE, p.chunks,
+                                   p.n_chunk_max, s),
                "bwd gemm");
     } else {
         uint16_t* wt = at<uint16_t>(workspace, p.off_wt);
         LAUNCH(K_W_TRANSPOSE, launch_transpose_w_bf16((const uint16_t*)W, wt, p.H, p.NE, s), "w transpose");
         LAUNCH(K_BWD_GEMM,
-               launch_bwd_gemm_bf16((const uint16_t*)d_routed_ctx, (const uint16_t*)fused_ctx, wt,
-                                    (uint16_t*)d_fused_ctx, accumulate_dx, pdw, pdb, expert_offsets, perm, p.T, p.H,
-                                    p.NE, p.chunks, p.n_chunk_max, s),
+               launch_bwd_gemm_bf16((const uint16_t*)dy, (const uint16_t*)fused_ctx, wt, (uint16_t*)d_fused_ctx,
+                                    accumulate_dx, pdw, pdb, expert_offsets, perm, p.T, p.H, p.NE, p.chunks,
+                                    p.n_chunk_max, s),
                "bwd gemm");
     }
     LAUNCH(K_REDUCE, launch_reduce_dw(pdw, pdb, expert_offsets, p.T, p.H, p.NE, p.chunks, d_W, d_b, s), "reduce");
     return MOE_OK;
 }
 
-moe_status_t moe_aux_loss(const float* gate_logits, const int32_t* expert_counts, float lambda, float* loss,
-                          float* d_gate_logits, float* frac, float* mean_prob, float* probs, int64_t B,
-                          int64_t NH, int64_t NE, void* workspace, size_t workspace_bytes, void* stream) {
-    const char* fn = "moe_aux_loss";
+moe_status_t moe_top1_bwd(const void* d_routed_ctx, const void* fused_ctx, const void* W,
+                          const int32_t* expert_offsets, const int32_t* perm, void* d_fused_ctx, float* d_W,
+                          float* d_b, int accumulate_dx, int64_t B, int64_t NH, int64_t H, int64_t NE, int act,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    return bwd_impl("moe_top1_bwd", d_routed_ctx, 0, fused_ctx, W, expert_offsets, perm, d_fused_ctx, d_W, d_b,
+                    accumulate_dx, B, NH, H, NE, act, workspace, workspace_bytes, stream);
+}
+
+moe_status_t moe_top1_bwd_from_mean(const float* d_ctx_mean, const void* fused_ctx, const void* W,
+                                    const int32_t* expert_offsets, const int32_t* perm, void* d_fused_ctx, float* d_W,
+                                    float* d_b, int accumulate_dx, int64_t B, int64_t NH, int64_t H, int64_t NE,
+                                    int act, void* workspace, size_t workspace_bytes, void* stream) {
+    return bwd_impl("moe_top1_bwd_from_mean", d_ctx_mean, 1, fused_ctx, W, expert_offsets, perm, d_fused_ctx, d_W,
+                    d_b, accumulate_dx, B, NH, H, NE, act, workspace, workspace_bytes, stream);
+}
+
+static moe_status_t aux_impl(const char* fn, const float* gate_logits, const int32_t* expert_counts, float lambda,
+                             const float* lambda_dev, float* loss, float* d_gate_logits, float* frac, float* mean_prob,
+                             float* probs, int64_t B, int64_t NH, int64_t NE, void* workspace, size_t workspace_bytes,
+                             void* stream) {
     moe_status_t st = check_shape(fn, B, NH, 0, NE, MOE_DTYPE_F32, false);
     if (st != MOE_OK) return st;
     REQ(gate_logits); OPT(expert_counts); REQ(loss); REQ(d_gate_logits);
     OPT(frac); OPT(mean_prob); OPT(probs);
-    if (!isfinite(lambda)) return fail(MOE_ERR_INVALID_ARG, "%s: lambda is not finite", fn);
+    if (!lambda_dev && !isfinite(lambda)) return fail(MOE_ERR_INVALID_ARG, "%s: lambda is not finite", fn);
     Plan p = make_plan(B * NH, 64, (int)NE, MOE_DTYPE_F32);
     const size_t need = p.off_pdw;
     if (!workspace) return fail(MOE_ERR_WORKSPACE, "%s: workspace is NULL", fn);
@@ -310,10 +334,133 @@ moe_status_t moe_aux_loss(const float* gate_logits, const int32_t* expert_counts
         counts = c;
     }
     float* part = at<float>(workspace, p.off_paux);
-    LAUNCH(K_AUX, launch_aux_rows(gate_logits, counts, p.T, p.NE, lambda, d_gate_logits, probs, part, p.n_ablk, s),
+    LAUNCH(K_AUX,
+           launch_aux_rows(gate_logits, counts, p.T, p.NE, lambda, lambda_dev, d_gate_logits, probs, part, p.n_ablk, s),
            "aux rows");
-    LAUNCH(K_AUX_FINAL, launch_aux_final(part, counts, p.n_ablk, p.T, p.NE, lambda, loss, frac, mean_prob, s),
+    LAUNCH(K_AUX_FINAL,
+           launch_aux_final(part, counts, p.n_ablk, p.T, p.NE, lambda, lambda_dev, loss, frac, mean_prob, s),
            "aux final");
+    return MOE_OK;
+}
+
+moe_status_t moe_aux_loss(const float* gate_logits, const int32_t* expert_counts, float lambda, float* loss,
+                          float* d_gate_logits, float* frac, float* mean_prob, float* probs, int64_t B,
+                          int64_t NH, int64_t NE, void* workspace, size_t workspace_bytes, void* stream) {
+    return aux_impl("moe_aux_loss", gate_logits, expert_counts, lambda, nullptr, loss, d_gate_logits, frac, mean_prob,
+                    probs, B, NH, NE, workspace, workspace_bytes, stream);
+}
+
+moe_status_t moe_aux_loss_lambda_dev(const float* gate_logits, const int32_t* expert_counts, const float* lambda_dev,
+                                     float* loss, float* d_gate_logits, float* frac, float* mean_prob, float* probs,
+                                     int64_t B, int64_t NH, int64_t NE, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+    const char* fn = "moe_aux_loss_lambda_dev";
+    if (!lambda_dev) return fail(MOE_ERR_INVALID_ARG, "%s: required pointer 'lambda_dev' is NULL", fn);
+    return aux_impl(fn, gate_logits, expert_counts, 0.0f, lambda_dev, loss, d_gate_logits, frac, mean_prob, probs,
+                    B, NH, NE, workspace, workspace_bytes, stream);
+}
+
+moe_status_t moe_lambda_eff_update(const float* ent_ema, float lambda_floor, float lambda_max_extra,
+                                   float entropy_target_frac, int64_t NE, float* lambda_eff, void* stream) {
+    const char* fn = "moe_lambda_eff_update";
+    if (!ent_ema) return fail(MOE_ERR_INVALID_ARG, "%s: required pointer 'ent_ema' is NULL", fn);
+    if (!lambda_eff) return fail(MOE_ERR_INVALID_ARG, "%s: required pointer 'lambda_eff' is NULL", fn);
+    if (((uintptr_t)ent_ema & 3u) || ((uintptr_t)lambda_eff & 3u))
+        return fail(MOE_ERR_INVALID_ARG, "%s: pointers must be 4-byte aligned", fn);
+    if (NE < 2 || NE > kMaxExperts)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: N_E=%lld outside [2, 64] (ln N_E must be positive)", fn, (long long)NE);
+    if (!isfinite(lambda_floor) || !isfinite(lambda_max_extra) || !(entropy_target_frac > 0.0f) ||
+        !isfinite(entropy_target_frac))
+        return fail(MOE_ERR_INVALID_ARG, "%s: knobs must be finite and the target fraction positive", fn);
+    hipStream_t s = (hipStream_t)stream;
+    LAUNCH(K_LAMBDA,
+           launch_lambda_eff(ent_ema, lambda_floor, lambda_max_extra, entropy_target_frac, (int)NE, lambda_eff, s),
+           "lambda update");
+    return MOE_OK;
+}
+
+// ---------------------------------------------------------------- reduce_axis0
+static moe_status_t check_axis0(const char* fn, int64_t n_batch, int64_t n_tail) {
+    if (n_batch <= 0 || n_tail <= 0)
+        return fail(MOE_ERR_INVALID_ARG, "%s: n_batch and n_tail must be positive", fn);
+    if (n_tail >= ((int64_t)1 << 31) || n_batch > ((int64_t)1 << 40) / n_tail)
+        return fail(MOE_ERR_INVALID_ARG, "%s: n_batch * n_tail too large", fn);
+    return MOE_OK;
+}
+
+static size_t axis0_ws(int64_t n_batch, int64_t n_tail) {
+    const int64_t R = reduce_axis0_chunks(n_batch, n_tail, n_tail % 4 == 0);
+    return R > 1 ? align256((size_t)R * n_tail * 4) : 0;
+}
+
+moe_status_t moe_reduce_axis0_workspace_bytes(int64_t n_batch, int64_t n_tail, size_t* bytes_out) {
+    const char* fn = "moe_reduce_axis0_workspace_bytes";
+    if (!bytes_out) return fail(MOE_ERR_INVALID_ARG, "%s: bytes_out is NULL", fn);
+    moe_status_t st = check_axis0(fn, n_batch, n_tail);
+    if (st != MOE_OK) return st;
+    *bytes_out = axis0_ws(n_batch, n_tail);
+    return MOE_OK;
+}
+
+moe_status_t moe_reduce_axis0(const float* in, int64_t n_batch, int64_t n_tail, float* out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    const char* fn = "moe_reduce_axis0";
+    moe_status_t st = check_axis0(fn, n_batch, n_tail);
+    if (st != MOE_OK) return st;
+    const bool vec = n_tail % 4 == 0;
+    if (!in || !out) return fail(MOE_ERR_INVALID_ARG, "%s: in and out must be non-NULL", fn);
+    if (vec ? (!aligned16(in) || !aligned16(out)) : (((uintptr_t)in | (uintptr_t)out) & 3u))
+        return fail(MOE_ERR_INVALID_ARG, "%s: in/out must be %d-byte aligned", fn, vec ? 16 : 4);
+    const size_t need = axis0_ws(n_batch, n_tail);
+    if (need > 0) {
+        if (!workspace) return fail(MOE_ERR_WORKSPACE, "%s: workspace is NULL (%zu bytes needed)", fn, need);
+        if (!aligned16(workspace)) return fail(MOE_ERR_INVALID_ARG, "%s: workspace is not 16-byte aligned", fn);
+        if (workspace_bytes < need)
+            return fail(MOE_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, workspace_bytes, need);
+    }
+    hipStream_t s = (hipStream_t)stream;
+    LAUNCH(K_REDUCE_AXIS0, launch_reduce_axis0(in, n_batch, n_tail, out, (float*)workspace, vec, s), "reduce_axis0");
+    return MOE_OK;
+}
+
+// ---------------------------------------------------------------- horizon mean collapse
+static moe_status_t collapse_impl(const char* fn, bool bwd, const void* in, void* out, int64_t B, int64_t NH,
+                                  int64_t H, int act, void* stream) {
+    if (B <= 0 || NH <= 0 || H <= 0) return fail(MOE_ERR_INVALID_ARG, "%s: sizes must be positive", fn);
+    if (act != MOE_DTYPE_F32 && act != MOE_DTYPE_BF16) return fail(MOE_ERR_UNSUPPORTED, "%s: unknown dtype", fn);
+    const int per = act == MOE_DTYPE_F32 ? 4 : 8;
+    if (H % per != 0) return fail(MOE_ERR_UNSUPPORTED, "%s: H must be a multiple of %d", fn, per);
+    if (NH > ((int64_t)1 << 20) || B * NH > ((int64_t)1 << 40) / H)
+        return fail(MOE_ERR_INVALID_ARG, "%s: shape too large", fn);
+    if (!in || !out) return fail(MOE_ERR_INVALID_ARG, "%s: in and out must be non-NULL", fn);
+    if (!aligned16(in) || !aligned16(out)) return fail(MOE_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", fn);
+    hipStream_t s = (hipStream_t)stream;
+    LAUNCH(K_COLLAPSE, launch_collapse(bwd, act, in, out, B, (int)NH, (int)H, s), "collapse");
+    return MOE_OK;
+}
+
+moe_status_t moe_horizon_mean_collapse_fwd(const void* x, void* ctx_mean, int64_t B, int64_t NH, int64_t H, int act,
+                                           void* stream) {
+    return collapse_impl("moe_horizon_mean_collapse_fwd", false, x, ctx_mean, B, NH, H, act, stream);
+}
+
+moe_status_t moe_horizon_mean_collapse_bwd(const void* d_ctx_mean, void* d_x, int64_t B, int64_t NH, int64_t H,
+                                           int act, void* stream) {
+    return collapse_impl("moe_horizon_mean_collapse_bwd", true, d_ctx_mean, d_x, B, NH, H, act, stream);
+}
+
+// ---------------------------------------------------------------- softmax-CE head
+moe_status_t moe_softmax_ce_grad(const float* logits, const int32_t* labels, float* grad, float* ce, int64_t B,
+                                 int64_t NH, int64_t A, void* stream) {
+    const char* fn = "moe_softmax_ce_grad";
+    if (B <= 0 || NH <= 0) return fail(MOE_ERR_INVALID_ARG, "%s: sizes must be positive", fn);
+    if (A < 1 || A > 64) return fail(MOE_ERR_UNSUPPORTED, "%s: A=%lld outside [1, 64]", fn, (long long)A);
+    if (B > ((int64_t)1 << 40) / NH) return fail(MOE_ERR_INVALID_ARG, "%s: shape too large", fn);
+    if (!logits || !labels || !grad || !ce) return fail(MOE_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (((uintptr_t)logits | (uintptr_t)labels | (uintptr_t)grad | (uintptr_t)ce) & 3u)
+        return fail(MOE_ERR_INVALID_ARG, "%s: pointers must be 4-byte aligned", fn);
+    hipStream_t s = (hipStream_t)stream;
+    LAUNCH(K_SOFTMAX_CE, launch_softmax_ce(logits, labels, B * NH, (int)A, B, grad, ce, s), "softmax-CE");
     return MOE_OK;
 }
 

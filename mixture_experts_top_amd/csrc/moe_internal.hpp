@@ -26,7 +26,8 @@ constexpr int kAuxThreads = 256;
 constexpr int kAuxTokens = 256;
 
 enum KernelId {
-    K_ROUTE = 0, K_SCAN, K_SCATTER, K_FWD_GEMM, K_BWD_GEMM, K_REDUCE, K_AUX, K_AUX_FINAL, K_W_TRANSPOSE, K_COUNT
+    K_ROUTE = 0, K_SCAN, K_SCATTER, K_FWD_GEMM, K_BWD_GEMM, K_REDUCE, K_AUX, K_AUX_FINAL, K_W_TRANSPOSE,
+    K_LAMBDA, K_REDUCE_AXIS0, K_COLLAPSE, K_SOFTMAX_CE, K_COUNT
 };
 
 // Chunking of each expert's tokens for the d_W split-K.  With P chunks planned for T
@@ -97,6 +98,11 @@ hipError_t launch_fwd_gemm_f32(const float* X, const float* W, const float* bias
 hipError_t launch_bwd_gemm_f32(const float* dY, const float* X, const float* W, float* dX, int accumulate,
                                float* part_dw, float* part_db, const int32_t* offsets, const int32_t* perm,
                                int64_t T, int H, int NE, int P, int n_chunk_max, hipStream_t s);
+// same, with row t of dY = d_mean[t / NH] * (1/NH) (backward through a mean over NH horizons)
+hipError_t launch_bwd_gemm_f32_from_mean(const float* d_mean, const float* X, const float* W, float* dX,
+                                         int accumulate, float* part_dw, float* part_db, const int32_t* offsets,
+                                         const int32_t* perm, int64_t T, int H, int NE, int NH, int P,
+                                         int n_chunk_max, hipStream_t s);
 // bf16 storage (raw uint16 patterns), fp32 accumulation
 hipError_t launch_fwd_gemm_bf16(const uint16_t* X, const uint16_t* W, const float* bias, uint16_t* Y,
                                 const int32_t* offsets, const int32_t* perm, int64_t T, int H, int NE,
@@ -109,9 +115,18 @@ hipError_t launch_bwd_gemm_bf16(const uint16_t* dY, const uint16_t* X, const uin
 hipError_t launch_reduce_dw(const float* part_dw, const float* part_db, const int32_t* offsets,
                             int64_t T, int H, int NE, int P, float* dW, float* db, hipStream_t s);
 
-hipError_t launch_aux_rows(const float* G, const int32_t* counts, int64_t T, int NE, float lam,
+hipError_t launch_aux_rows(const float* G, const int32_t* counts, int64_t T, int NE, float lam, const float* lam_dev,
                            float* dG, float* probs, float* part, int n_ablk, hipStream_t s);
 hipError_t launch_aux_final(const float* part, const int32_t* counts, int n_ablk, int64_t T, int NE,
-                            float lam, float* loss, float* frac, float* mean_prob, hipStream_t s);
+                            float lam, const float* lam_dev, float* loss, float* frac, float* mean_prob,
+                            hipStream_t s);
+int64_t reduce_axis0_chunks(int64_t n_batch, int64_t n_tail, bool vec);
+hipError_t launch_reduce_axis0(const float* in, int64_t n_batch, int64_t n_tail, float* out, float* part, bool vec,
+                               hipStream_t s);
+hipError_t launch_collapse(bool bwd, int act, const void* in, void* out, int64_t B, int NH, int H, hipStream_t s);
+hipError_t launch_softmax_ce(const float* logits, const int32_t* labels, int64_t rows, int A, int64_t B, float* grad,
+                             float* ce, hipStream_t s);
+hipError_t launch_lambda_eff(const float* ent_ema, float floor_, float max_extra, float target_frac, int K,
+                             float* lambda_eff, hipStream_t s);
 
 }  // namespace moe

@@ -1,0 +1,61 @@
+// Softmax + cross-entropy gradient head (softmax/cross-entropy page "6cfd7e6691", kernel
+// block): for each (b, h) row of A atom logits,
+//   p = softmax(z) (shift by the row max, exponentiate, normalise by the row sum)
+//   ce[b, h] = -log(max(p[label], 1e-30))
+//   grad[b, h, :] = (p - onehot(label)) / B          (mean over the batch)
+// and a label of -1 (the sentinel) gives ce = 0 and a zero gradient row; labels outside
+// [0, A) are treated the same way.  The page uses one block per row and one thread per atom;
+// here one thread owns a row and a workgroup of 256 rows stages its logits and gradients
+// through LDS, so every HBM access is a contiguous sweep.  One writer per output, no atomics.
+#include "moe_internal.hpp"
+
+namespace moe {
+
+template <int AB>  // A <= AB
+__global__ __launch_bounds__(256) void k_softmax_ce(const float* __restrict__ logits, const int* __restrict__ labels,
+                                                    int64_t rows, int A, float invB, float* __restrict__ grad,
+                                                    float* __restrict__ ce) {
+    __shared__ float tile[256 * AB];
+    const int tid = threadIdx.x;
+    const int64_t r0 = (int64_t)blockIdx.x * 256;
+    const int nrows = (int)min((int64_t)256, rows - r0);
+    const int64_t base = r0 * A;
+    const int n = nrows * A;
+    for (int i = tid; i < n; i += 256) tile[i] = logits[base + i];
+    __syncthreads();
+    if (tid < nrows) {
+        float* z = tile + tid * A;
+        const int lab = labels[r0 + tid];
+        const bool valid = lab >= 0 && lab < A;
+        float m = z[0];
+        for (int a = 1; a < A; ++a) m = fmaxf(m, z[a]);
+        float S = 0.0f;
+        for (int a = 0; a < A; ++a) {
+            const float e = expf(z[a] - m);
+            z[a] = e;
+            S += e;
+        }
+        float p_lab = 0.0f;
+        for (int a = 0; a < A; ++a) {
+            const float p = z[a] / S;
+            if (a == lab) p_lab = p;
+            z[a] = valid ? (p - (a == lab ? 1.0f : 0.0f)) * invB : 0.0f;
+        }
+        ce[r0 + tid] = valid ? -logf(fmaxf(p_lab, 1e-30f)) : 0.0f;
+    }
+    __syncthreads();
+    for (int i = tid; i < n; i += 256) grad[base + i] = tile[i];
+}
+
+hipError_t launch_softmax_ce(const float* logits, const int32_t* labels, int64_t rows, int A, int64_t B, float* grad,
+                             float* ce, hipStream_t s) {
+    const dim3 grid((unsigned)((rows + 255) / 256));
+    const float invB = 1.0f / (float)B;
+    if (A <= 32)
+        hipLaunchKernelGGL(k_softmax_ce<32>, grid, dim3(256), 0, s, logits, labels, rows, A, invB, grad, ce);
+    else
+        hipLaunchKernelGGL(k_softmax_ce<64>, grid, dim3(256), 0, s, logits, labels, rows, A, invB, grad, ce);
+    return hipGetLastError();
+}
+
+}  // namespace moe

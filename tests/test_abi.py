@@ -138,3 +138,34 @@ def test_binding_refuses_cpu_tensors():
                        torch.zeros(10, dtype=torch.int32), torch.zeros(4, dtype=torch.int32),
                        torch.zeros(5, dtype=torch.int32), torch.zeros(10, dtype=torch.int32),
                        workspace=torch.zeros(1 << 20, dtype=torch.uint8))
+
+
+def test_lambda_entry_points_validation(lib):
+    assert lib.moe_lambda_eff_update(None, 0.01, 0.09, 0.7, 8, FAKE, None) == INVALID
+    assert lib.moe_lambda_eff_update(FAKE, 0.01, 0.09, 0.7, 8, None, None) == INVALID
+    assert lib.moe_lambda_eff_update(FAKE + 2, 0.01, 0.09, 0.7, 8, FAKE, None) == INVALID
+    assert lib.moe_lambda_eff_update(FAKE, 0.01, 0.09, 0.7, 1, FAKE, None) == UNSUPPORTED
+    assert lib.moe_lambda_eff_update(FAKE, 0.01, 0.09, 0.0, 8, FAKE, None) == INVALID
+    assert lib.moe_lambda_eff_update(FAKE, float("nan"), 0.09, 0.7, 8, FAKE, None) == INVALID
+    assert lib.moe_aux_loss_lambda_dev(FAKE, FAKE, None, FAKE, FAKE, None, None, None, 8, 5, 4, FAKE, 1 << 40,
+                                       None) == INVALID
+    assert lib.moe_aux_loss_lambda_dev(None, FAKE, FAKE, FAKE, FAKE, None, None, None, 8, 5, 4, FAKE, 1 << 40,
+                                       None) == INVALID
+
+
+def test_next_rows_validation(lib):
+    out = ctypes.c_size_t(0)
+    assert lib.moe_reduce_axis0_workspace_bytes(0, 5, ctypes.byref(out)) == INVALID
+    assert lib.moe_reduce_axis0_workspace_bytes(20480, 65536, ctypes.byref(out)) == 0 and out.value > 0
+    assert lib.moe_reduce_axis0_workspace_bytes(10, 64, ctypes.byref(out)) == 0 and out.value == 0
+    assert lib.moe_reduce_axis0(None, 4, 4, FAKE, None, 0, None) == INVALID
+    assert lib.moe_reduce_axis0(FAKE + 4, 4, 4, FAKE, None, 0, None) == INVALID       # float4 path needs 16 B
+    assert lib.moe_reduce_axis0(FAKE, 20480, 65536, FAKE, None, 0, None) == WORKSPACE
+    assert lib.moe_horizon_mean_collapse_fwd(FAKE, FAKE, 4, 5, 6, 0, None) == UNSUPPORTED   # H % 4
+    assert lib.moe_horizon_mean_collapse_bwd(FAKE, FAKE, 4, 5, 12, 1, None) == UNSUPPORTED  # H % 8 for bf16
+    assert lib.moe_horizon_mean_collapse_fwd(None, FAKE, 4, 5, 64, 0, None) == INVALID
+    assert lib.moe_top1_bwd_from_mean(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 5, 128, 4, 1, FAKE,
+                                      1 << 40, None) == UNSUPPORTED                      # bf16
+    assert lib.moe_softmax_ce_grad(FAKE, FAKE, FAKE, FAKE, 4, 5, 65, None) == UNSUPPORTED
+    assert lib.moe_softmax_ce_grad(FAKE, None, FAKE, FAKE, 4, 5, 21, None) == INVALID
+    assert lib.moe_softmax_ce_grad(FAKE, FAKE, FAKE, FAKE, 0, 5, 21, None) == INVALID
