@@ -40,23 +40,6 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_floa
 __device__ __forceinline__ u16x8 ld8(const uint16_t* p) { return *reinterpret_cast<const u16x8*>(p); }
 __device__ __forceinline__ void st8(uint16_t* p, u16x8 v) { *reinterpret_cast<u16x8*>(p) = v; }
 
-__device__ __forceinline__ bool find_tile(const int* __restrict__ offsets, int NE, int mt, int bm, int& e, int& r0,
-                                          int& r1) {
-    int acc = 0;
-    for (int i = 0; i < NE; ++i) {
-        const int c0 = offsets[i], c1 = offsets[i + 1];
-        const int n = (c1 - c0 + bm - 1) / bm;
-        if (mt < acc + n) {
-            e = i;
-            r0 = c0 + (mt - acc) * bm;
-            r1 = min(c1, r0 + bm);
-            return true;
-        }
-        acc += n;
-    }
-    return false;
-}
-
 __device__ __forceinline__ void xcd_split(int bid, int per, int& major, int& minor) {
     const int grp = bid / (8 * per), loc = bid % (8 * per);
     major = grp * 8 + loc % 8;

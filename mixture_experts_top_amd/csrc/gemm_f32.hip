@@ -37,7 +37,13 @@ constexpr int kThreads = 256;   // 4 waves, arranged 2 x 2 over the output tile
 #ifndef MOE_ROWS_BIG_TILES_PER_CU
 #define MOE_ROWS_BIG_TILES_PER_CU 2
 #endif
-constexpr int kPad = 4;         // LDS row padding (floats): keeps 16-byte alignment, spreads banks
+constexpr int kPad = 4;         // LDS row padding (floats) for K-contiguous tiles: 16-byte aligned rows
+#ifndef MOE_F32_PAD_KN
+#define MOE_F32_PAD_KN 8
+#endif
+// Padding of tiles stored [k][n] and read one float per lane, lanes 32..63 four rows below
+// lanes 0..31: a row stride of 8 (mod 64) floats puts the two halves on disjoint LDS banks.
+constexpr int kPadKN = MOE_F32_PAD_KN;
 
 __device__ __forceinline__ f32x16 mfma32(float a, float b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
@@ -45,25 +51,6 @@ __device__ __forceinline__ f32x16 mfma32(float a, float b, f32x16 c) {
 
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 __device__ __forceinline__ void st4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
-
-// Finds the expert and row range of M-tile `mt` when every expert's rows are cut into
-// tiles of `bm`.  Returns false if mt is past the last tile.
-__device__ __forceinline__ bool find_tile(const int* __restrict__ offsets, int NE, int mt, int bm,
-                                          int& e, int& r0, int& r1) {
-    int acc = 0;
-    for (int i = 0; i < NE; ++i) {
-        const int c0 = offsets[i], c1 = offsets[i + 1];
-        const int n = (c1 - c0 + bm - 1) / bm;
-        if (mt < acc + n) {
-            e = i;
-            r0 = c0 + (mt - acc) * bm;
-            r1 = min(c1, r0 + bm);
-            return true;
-        }
-        acc += n;
-    }
-    return false;
-}
 
 // Workgroup ids are dealt to the 8 XCDs round-robin.  The `per` tiles that share one
 // operand block get ids id, id+8, id+16, ... so they land on the same XCD (same L2).
@@ -101,7 +88,7 @@ __device__ __forceinline__ void rows_f32_body(int bid, const float* __restrict__
     constexpr int AL = BM / RPP, BL = BN * KC / (4 * kThreads);  // float4 loads per thread per slice
     static_assert(KC % 8 == 0 && BM % RPP == 0 && (BN * KC) % (4 * kThreads) == 0, "tile shape");
     constexpr int BS_ROWS = DX ? KC : BN;
-    constexpr int BS_COLS = DX ? BN + kPad : KC + kPad;
+    constexpr int BS_COLS = DX ? BN + kPadKN : KC + kPad;
     __shared__ float As[2][BM][KC + kPad];
     __shared__ float Bs[2][BS_ROWS][BS_COLS];
     __shared__ int tok[BM];
@@ -169,32 +156,42 @@ __device__ __forceinline__ void rows_f32_body(int bid, const float* __restrict__
     load_slice(0);
     store_slice(0);
     __syncthreads();
-#pragma unroll 1
-    for (int c = 0; c < NKC; ++c) {
-        const int buf = c & 1;
-        if (c + 1 < NKC) load_slice((c + 1) * KC);
+    // LDS fragments of one 8-k group, double-buffered in registers: the reads of group g+1
+    // are issued before the MFMAs of group g.
+    constexpr int NG = KC / 8;
+    f32x4 fa[2][SM], fb[2][SN];
+    auto load_frag = [&](int buf, int g, int slot) {
+        const int kk = 8 * g + 4 * h;
 #pragma unroll
-        for (int kk = 0; kk < KC; kk += 8) {
-            f32x4 a[SM], b[SN];
+        for (int i = 0; i < SM; ++i) fa[slot][i] = ld4(&As[buf][wm * WTM + i * 32 + l32][kk]);
 #pragma unroll
-            for (int i = 0; i < SM; ++i) a[i] = ld4(&As[buf][wm * WTM + i * 32 + l32][kk + 4 * h]);
-#pragma unroll
-            for (int j = 0; j < SN; ++j) {
-                if (!DX) {
-                    b[j] = ld4(&Bs[buf][wn * WTN + j * 32 + l32][kk + 4 * h]);
-                } else {
-                    const int cc = wn * WTN + j * 32 + l32;
-                    b[j] = f32x4{Bs[buf][kk + 4 * h + 0][cc], Bs[buf][kk + 4 * h + 1][cc],
-                                 Bs[buf][kk + 4 * h + 2][cc], Bs[buf][kk + 4 * h + 3][cc]};
-                }
+        for (int j = 0; j < SN; ++j) {
+            if (!DX) {
+                fb[slot][j] = ld4(&Bs[buf][wn * WTN + j * 32 + l32][kk]);
+            } else {
+                const int cc = wn * WTN + j * 32 + l32;
+                fb[slot][j] = f32x4{Bs[buf][kk + 0][cc], Bs[buf][kk + 1][cc], Bs[buf][kk + 2][cc], Bs[buf][kk + 3][cc]};
             }
+        }
+    };
+    auto compute = [&](int buf) {
+        load_frag(buf, 0, 0);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            if (g + 1 < NG) load_frag(buf, g + 1, (g + 1) & 1);
 #pragma unroll
             for (int s = 0; s < 4; ++s)
 #pragma unroll
                 for (int i = 0; i < SM; ++i)
 #pragma unroll
-                    for (int j = 0; j < SN; ++j) acc[i][j] = mfma32(a[i][s], b[j][s], acc[i][j]);
+                    for (int j = 0; j < SN; ++j) acc[i][j] = mfma32(fa[g & 1][i][s], fb[g & 1][j][s], acc[i][j]);
         }
+    };
+#pragma unroll 1
+    for (int c = 0; c < NKC; ++c) {
+        const int buf = c & 1;
+        if (c + 1 < NKC) load_slice((c + 1) * KC);
+        compute(buf);
         if (c + 1 < NKC) store_slice(buf ^ 1);
         __syncthreads();
     }
@@ -242,8 +239,8 @@ __device__ __forceinline__ void dw_f32_body(int bid, const float* __restrict__ d
     constexpr int WT = BT / 2, SUB = WT / 32;
     constexpr int Q = BT / 4;                  // float4 per row segment
     constexpr int LD = KC * Q / kThreads;      // float4 loads per thread per tensor per slice
-    __shared__ float As[2][KC][BT + kPad];     // dY rows, columns o0..o0+BT
-    __shared__ float Bs[2][KC][BT + kPad];     // X rows, columns i0..i0+BT
+    __shared__ float As[2][KC][BT + kPadKN];   // dY rows, columns o0..o0+BT
+    __shared__ float Bs[2][KC][BT + kPadKN];   // X rows, columns i0..i0+BT
 
     int c, tile;
     xcd_split(bid, TPC, c, tile);
@@ -353,8 +350,13 @@ __device__ __forceinline__ void dw_f32_body(int bid, const float* __restrict__ d
 // Kernels.  The backward is one launch: its first n_dx workgroups are dX tiles and the rest
 // are dW / db chunk tiles, so both halves fill the GPU together.
 // ----------------------------------------------------------------------------------
+#ifdef MOE_FWD_WAVES_PER_EU
+#define MOE_FWD_ATTR __attribute__((amdgpu_waves_per_eu(MOE_FWD_WAVES_PER_EU)))
+#else
+#define MOE_FWD_ATTR
+#endif
 template <int H, int BM, int BN, int KC>
-__global__ __launch_bounds__(kThreads) void k_fwd_f32(const float* __restrict__ X, const float* __restrict__ W,
+__global__ __launch_bounds__(kThreads) MOE_FWD_ATTR void k_fwd_f32(const float* __restrict__ X, const float* __restrict__ W,
                                                        const float* __restrict__ bias, float* __restrict__ Y,
                                                        const int* __restrict__ offsets,
                                                        const int* __restrict__ perm, int NE) {

@@ -39,22 +39,61 @@ __device__ __forceinline__ int expert_nchunks(int c, int P, int T) {
     return c == 0 ? 0 : (int)(((int64_t)c * P + T - 1) / T);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wavefront (every lane holds one term).
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+    const int lane = __lane_id();
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int u = __shfl_up(v, d);
+        if (lane >= d) v += u;
+    }
+    return v;
+}
+
+// Wavefront-wide lookup of the unit `u` in a list cut expert by expert: lane l < NE holds
+// expert l's offsets and its number of units n_l; a prefix sum over lanes finds the expert
+// whose units cover u.  One load per lane and no serial chain; all lanes get the same
+// (uniform) result.  Returns false if u is past the last unit.
+__device__ __forceinline__ bool wave_find(const int* __restrict__ offsets, int NE, int u, int bm, int P, int T,
+                                          bool chunks, int& e, int& j, int& lo, int& cnt, int& n_e) {
+    const int lane = __lane_id();
+    int l0 = 0, c = 0, n = 0;
+    if (lane < NE) {
+        l0 = offsets[lane];
+        c = offsets[lane + 1] - l0;
+        n = chunks ? expert_nchunks(c, P, T) : (c + bm - 1) / bm;
+    }
+    const int incl = wave_inclusive_sum(n);
+    const int excl = incl - n;
+    const uint64_t hit = __ballot(lane < NE && u >= excl && u < incl);
+    if (hit == 0) return false;
+    const int le = __ffsll((unsigned long long)hit) - 1;
+    e = le;
+    j = u - __builtin_amdgcn_readlane(excl, le);
+    lo = __builtin_amdgcn_readlane(l0, le);
+    cnt = __builtin_amdgcn_readlane(c, le);
+    n_e = __builtin_amdgcn_readlane(n, le);
+    return true;
+}
+
+// M-tile `mt` of rows cut into tiles of bm per expert -> expert e, rows [r0, r1) of perm.
+__device__ __forceinline__ bool find_tile(const int* __restrict__ offsets, int NE, int mt, int bm, int& e, int& r0,
+                                          int& r1) {
+    int j, lo, cnt, n;
+    if (!wave_find(offsets, NE, mt, bm, 0, 1, false, e, j, lo, cnt, n)) return false;
+    r0 = lo + j * bm;
+    r1 = min(lo + cnt, r0 + bm);
+    return true;
+}
+
+// d_W chunk c -> expert e, token positions [t0, t1) of perm (see expert_nchunks).
 __device__ __forceinline__ bool find_chunk(const int* __restrict__ offsets, int NE, int P, int T, int c, int& e,
                                            int& t0, int& t1) {
-    int acc = 0;
-    for (int i = 0; i < NE; ++i) {
-        const int c0 = offsets[i], ce = offsets[i + 1] - c0;
-        const int n = expert_nchunks(ce, P, T);
-        if (c < acc + n) {
-            const int j = c - acc;
-            e = i;
-            t0 = c0 + (int)((int64_t)j * ce / n);
-            t1 = c0 + (int)((int64_t)(j + 1) * ce / n);
-            return true;
-        }
-        acc += n;
-    }
-    return false;
+    int j, lo, cnt, n;
+    if (!wave_find(offsets, NE, c, 1, P, T, true, e, j, lo, cnt, n)) return false;
+    t0 = lo + (int)((int64_t)j * cnt / n);
+    t1 = lo + (int)((int64_t)(j + 1) * cnt / n);
+    return true;
 }
 
 // Workspace layout for one (T, H, N_E, act).  Every section starts on a 256-byte boundary.
