@@ -61,20 +61,32 @@ __global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restri
 }
 
 // Out[t, n0:n0+BN] = A[t, :] . Bw[e][n0:n0+BN, :]^T (+ bias[e] | + Out[t] when accumulating).
+template <int H, int BN>
+struct RowsBf16Smem {
+    static constexpr int BM = 128, KC = 64, KP = KC + 8;
+    static constexpr size_t a = sizeof(uint16_t) * 2 * BM * KP, b = sizeof(uint16_t) * 2 * BN * KP, tok = 4 * BM;
+    static constexpr size_t bytes = a + b + tok;
+};
+
 template <int H, int BN, bool DX>
-__device__ __forceinline__ void rows_bf16_body(int bid, const uint16_t* __restrict__ A,
-                                                         const uint16_t* __restrict__ Bw,
-                                                         const float* __restrict__ bias,
-                                                         uint16_t* __restrict__ Out,
-                                                         const int* __restrict__ offsets,
-                                                         const int* __restrict__ perm, int NE, int accumulate) {
-    constexpr int BM = 128, KC = 64, KP = KC + 8;
+__device__ __forceinline__ void rows_bf16_body(char* smem, int bid, const uint16_t* __restrict__ A,
+                                               const uint16_t* __restrict__ Bw,
+                                               const float* __restrict__ bias,
+                                               uint16_t* __restrict__ Out,
+                                               const int* __restrict__ offsets,
+                                               const int* __restrict__ perm, int NE, int accumulate) {
+    constexpr int BM = 128, KC = 64, KP = KC + 8, NKC = H / KC;
     constexpr int NT = H / BN;
     constexpr int WTM = BM / 2, WTN = BN / 2;
     constexpr int SM = WTM / 32, SN = WTN / 32;
-    __shared__ uint16_t As[BM][KP];
-    __shared__ uint16_t Bs[BN][KP];
-    __shared__ int tok[BM];
+    constexpr int TPR = KC / 8, RPP = kThreads / TPR;   // threads per 128-byte row slice, rows per pass
+    constexpr int AL = BM / RPP, BL = BN / RPP;
+    static_assert(H % KC == 0 && BM % RPP == 0 && BN % RPP == 0, "tile shape");
+    // two LDS buffers: the global loads of K-slice c+1 are issued before the MFMAs of slice c
+    using SM_ = RowsBf16Smem<H, BN>;
+    uint16_t(&As)[2][BM][KP] = *reinterpret_cast<uint16_t(*)[2][BM][KP]>(smem);
+    uint16_t(&Bs)[2][BN][KP] = *reinterpret_cast<uint16_t(*)[2][BN][KP]>(smem + SM_::a);
+    int* tok = reinterpret_cast<int*>(smem + SM_::a + SM_::b);
 
     int mt, nt;
     xcd_split(bid, NT, mt, nt);
@@ -90,39 +102,53 @@ __device__ __forceinline__ void rows_bf16_body(int bid, const uint16_t* __restri
     const int wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
     const int wm = wave / 2, wn = wave % 2;
 
+    const uint16_t* a_src[AL];
+#pragma unroll
+    for (int i = 0; i < AL; ++i) {
+        const int t = tok[tid / TPR + RPP * i];
+        a_src[i] = (t >= 0) ? A + (size_t)t * H + 8 * (tid % TPR) : nullptr;
+    }
+    u16x8 ra[AL], rb[BL];
+    auto load_slice = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < AL; ++i) ra[i] = a_src[i] ? ld8(a_src[i] + k0) : u16x8{};
+#pragma unroll
+        for (int i = 0; i < BL; ++i)
+            rb[i] = ld8(Be + (size_t)(n0 + tid / TPR + RPP * i) * H + k0 + 8 * (tid % TPR));
+    };
+    auto store_slice = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < AL; ++i) st8(&As[buf][tid / TPR + RPP * i][8 * (tid % TPR)], ra[i]);
+#pragma unroll
+        for (int i = 0; i < BL; ++i) st8(&Bs[buf][tid / TPR + RPP * i][8 * (tid % TPR)], rb[i]);
+    };
+
     f32x16 acc[SM][SN];
 #pragma unroll
     for (int i = 0; i < SM; ++i)
 #pragma unroll
         for (int j = 0; j < SN; ++j) acc[i][j] = f32x16{};
 
-    for (int k0 = 0; k0 < H; k0 += KC) {
-#pragma unroll
-        for (int i = 0; i < BM / 32; ++i) {
-            const int r = tid / 8 + 32 * i, c = 8 * (tid % 8);
-            const int t = tok[r];
-            u16x8 v = u16x8{};
-            if (t >= 0) v = ld8(A + (size_t)t * H + k0 + c);
-            st8(&As[r][c], v);
-        }
-#pragma unroll
-        for (int i = 0; i < BN / 32; ++i) {
-            const int r = tid / 8 + 32 * i, c = 8 * (tid % 8);
-            st8(&Bs[r][c], ld8(Be + (size_t)(n0 + r) * H + k0 + c));
-        }
-        __syncthreads();
+    load_slice(0);
+    store_slice(0);
+    __syncthreads();
+#pragma unroll 1
+    for (int c = 0; c < NKC; ++c) {
+        const int buf = c & 1;
+        if (c + 1 < NKC) load_slice((c + 1) * KC);
 #pragma unroll
         for (int kk = 0; kk < KC; kk += 16) {
             u16x8 a[SM], b[SN];
 #pragma unroll
-            for (int i = 0; i < SM; ++i) a[i] = ld8(&As[wm * WTM + i * 32 + l32][kk + 8 * h]);
+            for (int i = 0; i < SM; ++i) a[i] = ld8(&As[buf][wm * WTM + i * 32 + l32][kk + 8 * h]);
 #pragma unroll
-            for (int j = 0; j < SN; ++j) b[j] = ld8(&Bs[wn * WTN + j * 32 + l32][kk + 8 * h]);
+            for (int j = 0; j < SN; ++j) b[j] = ld8(&Bs[buf][wn * WTN + j * 32 + l32][kk + 8 * h]);
 #pragma unroll
             for (int i = 0; i < SM; ++i)
 #pragma unroll
                 for (int j = 0; j < SN; ++j) acc[i][j] = mfma_bf16(a[i], b[j], acc[i][j]);
         }
+        if (c + 1 < NKC) store_slice(buf ^ 1);
         __syncthreads();
     }
 
@@ -149,7 +175,14 @@ __device__ __forceinline__ void rows_bf16_body(int bid, const uint16_t* __restri
 
 // d_W / d_b partials for one chunk of one expert's tokens, output tile [o0:o0+BT, i0:i0+BT].
 template <int H>
-__device__ __forceinline__ void dw_bf16_body(int bid, const uint16_t* __restrict__ dY,
+struct DwBf16Smem {
+    static constexpr int BT = (H >= 128) ? 128 : 64, KC = 64, KP = KC + 8;
+    static constexpr size_t a = sizeof(uint16_t) * 2 * BT * KP;
+    static constexpr size_t bytes = 2 * a;
+};
+
+template <int H>
+__device__ __forceinline__ void dw_bf16_body(char* smem, int bid, const uint16_t* __restrict__ dY,
                                                        const uint16_t* __restrict__ X,
                                                        float* __restrict__ part_dw, float* __restrict__ part_db,
                                                        const int* __restrict__ offsets,
@@ -159,8 +192,8 @@ __device__ __forceinline__ void dw_bf16_body(int bid, const uint16_t* __restrict
     constexpr int KC = 64, KP = KC + 8;
     constexpr int WT = BT / 2, SUB = WT / 32;
     constexpr int ITEMS = (KC / 4) * (BT / 8);  // (4 tokens x 8 features) blocks per stage
-    __shared__ uint16_t As[BT][KP];  // dY^T: [o][t]
-    __shared__ uint16_t Bs[BT][KP];  // X^T:  [i][t]
+    uint16_t(&As)[2][BT][KP] = *reinterpret_cast<uint16_t(*)[2][BT][KP]>(smem);                     // dY^T [o][t]
+    uint16_t(&Bs)[2][BT][KP] = *reinterpret_cast<uint16_t(*)[2][BT][KP]>(smem + DwBf16Smem<H>::a);  // X^T  [i][t]
 
     int c, tile;
     xcd_split(bid, TPC, c, tile);
@@ -179,40 +212,80 @@ __device__ __forceinline__ void dw_bf16_body(int bid, const uint16_t* __restrict
         for (int j = 0; j < SUB; ++j) acc[i][j] = f32x16{};
     float dbacc = 0.0f;
 
-    for (int k0 = t0; k0 < t1; k0 += KC) {
-        for (int q = tid; q < ITEMS; q += kThreads) {
-            const int tq = q / (BT / 8), fq = q % (BT / 8);
-            u16x8 va[4], vb[4];
+    // Two LDS buffers; per thread IPT items of (4 tokens x 8 features) per tensor, loaded one
+    // slice ahead of the MFMAs, transposed in registers when stored.  Token ids are fetched
+    // one slice further ahead.
+    constexpr int IPT = (ITEMS + kThreads - 1) / kThreads;
+    const int nslices = (t1 - t0 + KC - 1) / KC;
+    int tk[IPT][4];
+    u16x8 va[IPT][4], vb[IPT][4];
+    auto load_ids = [&](int sl) {
+#pragma unroll
+        for (int it = 0; it < IPT; ++it) {
+            const int q = tid + kThreads * it;
+            const int tq = q / (BT / 8);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int k = k0 + 4 * tq + j;
-                va[j] = u16x8{};
-                vb[j] = u16x8{};
-                if (k < t1) {
-                    const size_t t = (size_t)perm[k];
-                    va[j] = ld8(dY + t * H + o0 + 8 * fq);
-                    vb[j] = ld8(X + t * H + i0 + 8 * fq);
-                }
-            }
-#pragma unroll
-            for (int f = 0; f < 8; ++f) {
-                uint2 wa, wb;
-                wa.x = (uint32_t)va[0][f] | ((uint32_t)va[1][f] << 16);
-                wa.y = (uint32_t)va[2][f] | ((uint32_t)va[3][f] << 16);
-                wb.x = (uint32_t)vb[0][f] | ((uint32_t)vb[1][f] << 16);
-                wb.y = (uint32_t)vb[2][f] | ((uint32_t)vb[3][f] << 16);
-                *reinterpret_cast<uint2*>(&As[8 * fq + f][4 * tq]) = wa;
-                *reinterpret_cast<uint2*>(&Bs[8 * fq + f][4 * tq]) = wb;
+                const int k = t0 + sl * KC + 4 * tq + j;
+                tk[it][j] = (q < ITEMS && sl < nslices && k < t1) ? perm[k] : -1;
             }
         }
-        __syncthreads();
+    };
+    auto load_rows = [&]() {
+#pragma unroll
+        for (int it = 0; it < IPT; ++it) {
+            const int fq = (tid + kThreads * it) % (BT / 8);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                va[it][j] = u16x8{};
+                vb[it][j] = u16x8{};
+                if (tk[it][j] >= 0) {
+                    const size_t t = (size_t)tk[it][j];
+                    va[it][j] = ld8(dY + t * H + o0 + 8 * fq);
+                    vb[it][j] = ld8(X + t * H + i0 + 8 * fq);
+                }
+            }
+        }
+    };
+    auto store_rows = [&](int buf) {
+#pragma unroll
+        for (int it = 0; it < IPT; ++it) {
+            const int q = tid + kThreads * it;
+            if (q < ITEMS) {
+                const int tq = q / (BT / 8), fq = q % (BT / 8);
+#pragma unroll
+                for (int f = 0; f < 8; ++f) {
+                    uint2 wa, wb;
+                    wa.x = (uint32_t)va[it][0][f] | ((uint32_t)va[it][1][f] << 16);
+                    wa.y = (uint32_t)va[it][2][f] | ((uint32_t)va[it][3][f] << 16);
+                    wb.x = (uint32_t)vb[it][0][f] | ((uint32_t)vb[it][1][f] << 16);
+                    wb.y = (uint32_t)vb[it][2][f] | ((uint32_t)vb[it][3][f] << 16);
+                    *reinterpret_cast<uint2*>(&As[buf][8 * fq + f][4 * tq]) = wa;
+                    *reinterpret_cast<uint2*>(&Bs[buf][8 * fq + f][4 * tq]) = wb;
+                }
+            }
+        }
+    };
+
+    load_ids(0);
+    load_rows();
+    load_ids(1);
+    store_rows(0);
+    __syncthreads();
+#pragma unroll 1
+    for (int sl = 0; sl < nslices; ++sl) {
+        const int buf = sl & 1;
+        if (sl + 1 < nslices) {
+            load_rows();
+            load_ids(sl + 2);
+        }
 #pragma unroll
         for (int kk = 0; kk < KC; kk += 16) {
             u16x8 a[SUB], b[SUB];
 #pragma unroll
-            for (int i = 0; i < SUB; ++i) a[i] = ld8(&As[wm * WT + i * 32 + l32][kk + 8 * h]);
+            for (int i = 0; i < SUB; ++i) a[i] = ld8(&As[buf][wm * WT + i * 32 + l32][kk + 8 * h]);
 #pragma unroll
-            for (int j = 0; j < SUB; ++j) b[j] = ld8(&Bs[wn * WT + j * 32 + l32][kk + 8 * h]);
+            for (int j = 0; j < SUB; ++j) b[j] = ld8(&Bs[buf][wn * WT + j * 32 + l32][kk + 8 * h]);
 #pragma unroll
             for (int i = 0; i < SUB; ++i)
 #pragma unroll
@@ -221,11 +294,12 @@ __device__ __forceinline__ void dw_bf16_body(int bid, const uint16_t* __restrict
         if (do_db && tid < BT) {
 #pragma unroll
             for (int q = 0; q < KC / 8; ++q) {
-                const u16x8 v = ld8(&As[tid][8 * q]);
+                const u16x8 v = ld8(&As[buf][tid][8 * q]);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) dbacc += bf16_to_f32(v[j]);
             }
         }
+        if (sl + 1 < nslices) store_rows(buf ^ 1);
         __syncthreads();
     }
 
@@ -250,7 +324,8 @@ __global__ __launch_bounds__(kThreads) void k_fwd_bf16(const uint16_t* __restric
                                                         const float* __restrict__ bias, uint16_t* __restrict__ Y,
                                                         const int* __restrict__ offsets,
                                                         const int* __restrict__ perm, int NE) {
-    rows_bf16_body<H, BN, false>(blockIdx.x, X, W, bias, Y, offsets, perm, NE, 0);
+    __shared__ __attribute__((aligned(16))) char smem[RowsBf16Smem<H, BN>::bytes];
+    rows_bf16_body<H, BN, false>(smem, blockIdx.x, X, W, bias, Y, offsets, perm, NE, 0);
 }
 
 template <int H, int BN>
@@ -261,10 +336,12 @@ __global__ __launch_bounds__(kThreads) void k_bwd_bf16(const uint16_t* __restric
                                                         float* __restrict__ part_db,
                                                         const int* __restrict__ offsets,
                                                         const int* __restrict__ perm, int NE, int P, int T, int n_dx) {
+    constexpr size_t r = RowsBf16Smem<H, BN>::bytes, d = DwBf16Smem<H>::bytes;
+    __shared__ __attribute__((aligned(16))) char smem[r > d ? r : d];  // one LDS region, either role
     if ((int)blockIdx.x < n_dx)
-        rows_bf16_body<H, BN, true>(blockIdx.x, dY, Wt, nullptr, dX, offsets, perm, NE, accumulate);
+        rows_bf16_body<H, BN, true>(smem, blockIdx.x, dY, Wt, nullptr, dX, offsets, perm, NE, accumulate);
     else
-        dw_bf16_body<H>(blockIdx.x - n_dx, dY, X, part_dw, part_db, offsets, perm, NE, P, T);
+        dw_bf16_body<H>(smem, blockIdx.x - n_dx, dY, X, part_dw, part_db, offsets, perm, NE, P, T);
 }
 
 // ---------------------------------------------------------------- launchers

@@ -69,8 +69,15 @@ __device__ __forceinline__ void xcd_split(int bid, int per, int& major, int& min
 // issued into registers before the MFMAs of slice c, and stored to the other buffer after
 // them, so one barrier per slice suffices and load latency hides behind the MFMAs.
 // ----------------------------------------------------------------------------------
+template <int BM, int BN, int KC, bool DX>
+struct RowsF32Smem {
+    static constexpr int BS_ROWS = DX ? KC : BN, BS_COLS = DX ? BN + kPadKN : KC + kPad;
+    static constexpr size_t a = sizeof(float) * 2 * BM * (KC + kPad), b = sizeof(float) * 2 * BS_ROWS * BS_COLS;
+    static constexpr size_t bytes = a + b + 4 * BM;
+};
+
 template <int H, int BM, int BN, int KC, bool DX, bool MEAN = false>
-__device__ __forceinline__ void rows_f32_body(int bid, const float* __restrict__ A,
+__device__ __forceinline__ void rows_f32_body(char* smem, int bid, const float* __restrict__ A,
                                                         const float* __restrict__ W,
                                                         const float* __restrict__ bias,
                                                         float* __restrict__ Out,
@@ -89,9 +96,10 @@ __device__ __forceinline__ void rows_f32_body(int bid, const float* __restrict__
     static_assert(KC % 8 == 0 && BM % RPP == 0 && (BN * KC) % (4 * kThreads) == 0, "tile shape");
     constexpr int BS_ROWS = DX ? KC : BN;
     constexpr int BS_COLS = DX ? BN + kPadKN : KC + kPad;
-    __shared__ float As[2][BM][KC + kPad];
-    __shared__ float Bs[2][BS_ROWS][BS_COLS];
-    __shared__ int tok[BM];
+    using SM_ = RowsF32Smem<BM, BN, KC, DX>;
+    float(&As)[2][BM][KC + kPad] = *reinterpret_cast<float(*)[2][BM][KC + kPad]>(smem);
+    float(&Bs)[2][BS_ROWS][BS_COLS] = *reinterpret_cast<float(*)[2][BS_ROWS][BS_COLS]>(smem + SM_::a);
+    int* tok = reinterpret_cast<int*>(smem + SM_::a + SM_::b);
 
     int mt, nt;
     xcd_split(bid, NT, mt, nt);
@@ -226,8 +234,15 @@ __device__ __forceinline__ void rows_f32_body(int bid, const float* __restrict__
 // Same two-buffer pipeline as the row GEMM; token ids of slice c+2 are fetched while slice
 // c+1's rows are being loaded, so the gather never waits on an index load.
 // ----------------------------------------------------------------------------------
+template <int H, int KC>
+struct DwF32Smem {
+    static constexpr int BT = (H >= 128) ? 128 : 64;
+    static constexpr size_t a = sizeof(float) * 2 * KC * (BT + kPadKN);
+    static constexpr size_t bytes = 2 * a;
+};
+
 template <int H, int KC, bool MEAN = false>
-__device__ __forceinline__ void dw_f32_body(int bid, const float* __restrict__ dY,
+__device__ __forceinline__ void dw_f32_body(char* smem, int bid, const float* __restrict__ dY,
                                                       const float* __restrict__ X,
                                                       float* __restrict__ part_dw,
                                                       float* __restrict__ part_db,
@@ -239,8 +254,9 @@ __device__ __forceinline__ void dw_f32_body(int bid, const float* __restrict__ d
     constexpr int WT = BT / 2, SUB = WT / 32;
     constexpr int Q = BT / 4;                  // float4 per row segment
     constexpr int LD = KC * Q / kThreads;      // float4 loads per thread per tensor per slice
-    __shared__ float As[2][KC][BT + kPadKN];   // dY rows, columns o0..o0+BT
-    __shared__ float Bs[2][KC][BT + kPadKN];   // X rows, columns i0..i0+BT
+    float(&As)[2][KC][BT + kPadKN] = *reinterpret_cast<float(*)[2][KC][BT + kPadKN]>(smem);  // dY rows, o0..o0+BT
+    float(&Bs)[2][KC][BT + kPadKN] =
+        *reinterpret_cast<float(*)[2][KC][BT + kPadKN]>(smem + DwF32Smem<H, KC>::a);      // X rows, i0..i0+BT
 
     int c, tile;
     xcd_split(bid, TPC, c, tile);
@@ -360,7 +376,8 @@ __global__ __launch_bounds__(kThreads) MOE_FWD_ATTR void k_fwd_f32(const float* 
                                                        const float* __restrict__ bias, float* __restrict__ Y,
                                                        const int* __restrict__ offsets,
                                                        const int* __restrict__ perm, int NE) {
-    rows_f32_body<H, BM, BN, KC, false>(blockIdx.x, X, W, bias, Y, offsets, perm, NE, 0);
+    __shared__ __attribute__((aligned(16))) char smem[RowsF32Smem<BM, BN, KC, false>::bytes];
+    rows_f32_body<H, BM, BN, KC, false>(smem, blockIdx.x, X, W, bias, Y, offsets, perm, NE, 0);
 }
 
 template <int H, int BM, int BN, int KCX, int KCW, bool MEAN>
@@ -371,11 +388,14 @@ __global__ __launch_bounds__(kThreads) void k_bwd_f32(const float* __restrict__ 
                                                        const int* __restrict__ offsets,
                                                        const int* __restrict__ perm, int NE, int P, int T,
                                                        int n_dx, int nh, float inv_nh) {
+    constexpr size_t r = RowsF32Smem<BM, BN, KCX, true>::bytes, d = DwF32Smem<H, KCW>::bytes;
+    __shared__ __attribute__((aligned(16))) char smem[r > d ? r : d];  // one LDS region, either role
     if ((int)blockIdx.x < n_dx)
-        rows_f32_body<H, BM, BN, KCX, true, MEAN>(blockIdx.x, dY, W, nullptr, dX, offsets, perm, NE, accumulate, nh,
-                                                  inv_nh);
+        rows_f32_body<H, BM, BN, KCX, true, MEAN>(smem, blockIdx.x, dY, W, nullptr, dX, offsets, perm, NE,
+                                                  accumulate, nh, inv_nh);
     else
-        dw_f32_body<H, KCW, MEAN>(blockIdx.x - n_dx, dY, X, part_dw, part_db, offsets, perm, NE, P, T, nh, inv_nh);
+        dw_f32_body<H, KCW, MEAN>(smem, blockIdx.x - n_dx, dY, X, part_dw, part_db, offsets, perm, NE, P, T, nh,
+                                  inv_nh);
 }
 
 // ----------------------------------------------------------------------------------
