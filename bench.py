@@ -5,8 +5,9 @@ already resident in HBM.  Prints one JSON line (last line of stdout):
 
   value          routed tokens/s of the whole step (T / step time)
   roofline       the dominant kernel's algorithmic flops (or bytes) per launch divided
-                 by its average launch time, timed with HIP events around each of its
-                 launches inside the timed region, against the MI355X peak
+                 by its average duration, from HIP events that the library records at the
+                 start and end of each of its launches inside the timed region, against the
+                 MI355X peak
   cpu_baseline   the fp64 CPU oracle timed on this host on a bounded sample
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2|1|3|4|5] [--graph]
@@ -285,17 +286,25 @@ def main():
     # per-kernel averages (outside the timed region) to find the dominant kernel
     nk = 10
     kern_us = {}
-    for k in ([] if args.skip_kernel_survey else moe.KERNELS):
+    gate_kernels = ["route", "scan", "scatter", "fwd_gemm", "bwd_gemm", "reduce", "aux", "aux_final"]
+    if wl.act == "bf16":
+        gate_kernels.append("w_transpose")
+    for k in ([] if args.skip_kernel_survey else gate_kernels):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nk)]
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(nk)]
         for a, b in evs:
             a.record(); b.record()
         torch.cuda.synchronize()
-        for a, b in evs:
+        for (a, b), m in zip(evs, marks):
+            m.record()
             moe.moe_set_launch_timer(k, a, b)
             step()
         moe.moe_set_launch_timer(None)
         torch.cuda.synchronize()
-        kern_us[k] = float(np.mean([a.elapsed_time(b) for a, b in evs]) * 1e3)
+        # a kernel this shape does not launch leaves its events at their earlier timestamps
+        vals = [a.elapsed_time(b) for (a, b), m in zip(evs, marks) if m.elapsed_time(a) >= 0]
+        if vals:
+            kern_us[k] = float(np.mean(vals) * 1e3)
     if args.kernel:
         dom = args.kernel
     elif kern_us:
