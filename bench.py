@@ -230,6 +230,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--graph", action="store_true", help="replay the step as one captured HIP graph")
+    ap.add_argument("--aux-stream", action="store_true",
+                    help="run the auxiliary loss on a second stream, overlapping the backward (default: "
+                         "after it, on one stream; the cross-stream join costs more than it hides at the "
+                         "pages' shape)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -265,9 +269,10 @@ def main():
     d = gpu_run.upload(inp)
     o = gpu_run.Buffers(d, poison=False)
     stream = torch.cuda.current_stream()
+    aux_stream = torch.cuda.Stream() if args.aux_stream else None  # default priority
 
     def step():  # the optional probs output is not requested: the aux pass writes dG only
-        gpu_run.step(d, o, probs=False)
+        gpu_run.step(d, o, probs=False, aux_stream=aux_stream)
 
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 20
@@ -392,6 +397,7 @@ def main():
         "data": "synthetic (seeded; see workloads.py)",
         "config": {"workload": wl.name, "B": wl.B, "N_H": wl.NH, "H": wl.H, "N_E": wl.NE, "T": T,
                    "lambda": wl.lam, "act": wl.act, "launch": "hip-graph" if graph is not None else "eager",
+                   "streams": 1 if aux_stream is None else 2,
                    "parallelism": "single GPU"},
         "roofline": {"bound": bound, "kernel": dom, "achieved": achieved, "peak": peak, "unit": runit,
                      "frac": achieved / peak, "traffic": measured_traffic(dom, wl), "avg_launch_us": dom_us,

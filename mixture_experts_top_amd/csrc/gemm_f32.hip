@@ -73,17 +73,19 @@ template <int BM, int BN, int KC, bool DX>
 struct RowsF32Smem {
     static constexpr int BS_ROWS = DX ? KC : BN, BS_COLS = DX ? BN + kPadKN : KC + kPad;
     static constexpr size_t a = sizeof(float) * 2 * BM * (KC + kPad), b = sizeof(float) * 2 * BS_ROWS * BS_COLS;
-    static constexpr size_t bytes = a + b + 4 * BM;
+    static constexpr size_t bytes = a + b + 2 * 4 * BM;  // + token ids of the current and the next tile
 };
 
+// Persistent: workgroup `wg` of `nwg` computes tiles wg, wg + nwg, ... of the `ntile_ids` tile
+// ids (ids past the real tile count are skipped).  The experts' offsets are read once per
+// wavefront; during the last K-slice of a tile the next tile's token ids and first K-slice are
+// loaded, so that latency overlaps the MFMAs and the epilogue stores.
 template <int H, int BM, int BN, int KC, bool DX, bool MEAN = false>
-__device__ __forceinline__ void rows_f32_body(char* smem, int bid, const float* __restrict__ A,
-                                                        const float* __restrict__ W,
-                                                        const float* __restrict__ bias,
-                                                        float* __restrict__ Out,
-                                                        const int* __restrict__ offsets,
-                                                        const int* __restrict__ perm, int NE,
-                                                        int accumulate, int nh = 1, float inv_nh = 1.0f) {
+__device__ __forceinline__ void rows_f32_body(char* smem, int wg, int nwg, int ntile_ids,
+                                              const float* __restrict__ A, const float* __restrict__ W,
+                                              const float* __restrict__ bias, float* __restrict__ Out,
+                                              const int* __restrict__ offsets, const int* __restrict__ perm,
+                                              int NE, int accumulate, int nh = 1, float inv_nh = 1.0f) {
     // MEAN: row t of A is A[t / nh] * inv_nh (the backward of a mean over nh horizons)
     constexpr int NKC = H / KC;
     constexpr int NT = H / BN;
@@ -99,29 +101,62 @@ __device__ __forceinline__ void rows_f32_body(char* smem, int bid, const float* 
     using SM_ = RowsF32Smem<BM, BN, KC, DX>;
     float(&As)[2][BM][KC + kPad] = *reinterpret_cast<float(*)[2][BM][KC + kPad]>(smem);
     float(&Bs)[2][BS_ROWS][BS_COLS] = *reinterpret_cast<float(*)[2][BS_ROWS][BS_COLS]>(smem + SM_::a);
-    int* tok = reinterpret_cast<int*>(smem + SM_::a + SM_::b);
+    int(&tok)[2][BM] = *reinterpret_cast<int(*)[2][BM]>(smem + SM_::a + SM_::b);
 
-    int mt, nt;
-    xcd_split(bid, NT, mt, nt);
-    int e, r0, r1;
-    if (!find_tile(offsets, NE, mt, BM, e, r0, r1)) return;
-    const int rows = r1 - r0;
     const int tid = threadIdx.x;
-    if (tid < BM) tok[tid] = (tid < rows) ? perm[r0 + tid] : -1;
-    __syncthreads();
-
-    const int n0 = nt * BN;
-    const float* __restrict__ We = W + (size_t)e * H * H;
     const int wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
     const int wm = wave / WN, wn = wave % WN;
 
-    // per-thread load coordinates (fixed across slices)
+    // expert table: lane l < NE holds expert l's first row, row count and tile count
+    int x_lo = 0, x_cnt = 0, x_n = 0;
+    if (lane < NE) {
+        x_lo = offsets[lane];
+        x_cnt = offsets[lane + 1] - x_lo;
+        x_n = (x_cnt + BM - 1) / BM;
+    }
+    const int x_incl = wave_inclusive_sum(x_n), x_excl = x_incl - x_n;
+    auto lookup = [&](int id, int& e, int& r0, int& rows, int& n0) -> bool {
+        int mt, nt;
+        xcd_split(id, NT, mt, nt);
+        const uint64_t hit = __ballot(lane < NE && mt >= x_excl && mt < x_incl);
+        if (hit == 0) return false;
+        const int le = __ffsll((unsigned long long)hit) - 1;
+        const int j = mt - __builtin_amdgcn_readlane(x_excl, le);
+        e = le;
+        r0 = __builtin_amdgcn_readlane(x_lo, le) + j * BM;
+        rows = min(BM, __builtin_amdgcn_readlane(x_cnt, le) - j * BM);
+        n0 = nt * BN;
+        return true;
+    };
+    auto next_valid = [&](int id, int& e, int& r0, int& rows, int& n0) -> int {
+        for (; id < ntile_ids; id += nwg)
+            if (lookup(id, e, r0, rows, n0)) return id;
+        return -1;
+    };
+
+    int e, r0, rows, n0;
+    int id = next_valid(wg, e, r0, rows, n0);
+    if (id < 0) return;
+    int cur = 0;
+    if (tid < BM) tok[cur][tid] = (tid < rows) ? perm[r0 + tid] : -1;
+    __syncthreads();
+
+    const float* __restrict__ We = W + (size_t)e * H * H;
+    int wn0 = n0;  // column offset the W loads use (switches to the next tile during its prefetch)
     const float* a_src[AL];
+    auto set_a_src = [&](const int* t_of_row) {
 #pragma unroll
-    for (int i = 0; i < AL; ++i) {
-        const int t = tok[tid / TPR + RPP * i];
-        const int row = MEAN ? t / nh : t;
-        a_src[i] = (t >= 0) ? A + (size_t)row * H + 4 * (tid % TPR) : nullptr;
+        for (int i = 0; i < AL; ++i) {
+            const int t = t_of_row[i];
+            const int row = MEAN ? t / nh : t;
+            a_src[i] = (t >= 0) ? A + (size_t)row * H + 4 * (tid % TPR) : nullptr;
+        }
+    };
+    {
+        int t0[AL];
+#pragma unroll
+        for (int i = 0; i < AL; ++i) t0[i] = tok[cur][tid / TPR + RPP * i];
+        set_a_src(t0);
     }
     f32x4 ra[AL], rb[BL];
     auto load_slice = [&](int k0) {
@@ -134,10 +169,10 @@ __device__ __forceinline__ void rows_f32_body(char* smem, int bid, const float* 
         for (int i = 0; i < BL; ++i) {
             if (!DX) {
                 const int r = tid / TPR + RPP * i, c = 4 * (tid % TPR);
-                rb[i] = ld4(We + (size_t)(n0 + r) * H + k0 + c);
+                rb[i] = ld4(We + (size_t)(wn0 + r) * H + k0 + c);
             } else {
                 const int q = tid + kThreads * i, r = q / (BN / 4), c = 4 * (q % (BN / 4));
-                rb[i] = ld4(We + (size_t)(k0 + r) * H + n0 + c);
+                rb[i] = ld4(We + (size_t)(k0 + r) * H + wn0 + c);
             }
         }
     };
@@ -161,9 +196,6 @@ __device__ __forceinline__ void rows_f32_body(char* smem, int bid, const float* 
 #pragma unroll
         for (int j = 0; j < SN; ++j) acc[i][j] = f32x16{};
 
-    load_slice(0);
-    store_slice(0);
-    __syncthreads();
     // LDS fragments of one 8-k group, double-buffered in registers: the reads of group g+1
     // are issued before the MFMAs of group g.
     constexpr int NG = KC / 8;
@@ -195,33 +227,73 @@ __device__ __forceinline__ void rows_f32_body(char* smem, int bid, const float* 
                     for (int j = 0; j < SN; ++j) acc[i][j] = mfma32(fa[g & 1][i][s], fb[g & 1][j][s], acc[i][j]);
         }
     };
-#pragma unroll 1
-    for (int c = 0; c < NKC; ++c) {
-        const int buf = c & 1;
-        if (c + 1 < NKC) load_slice((c + 1) * KC);
-        compute(buf);
-        if (c + 1 < NKC) store_slice(buf ^ 1);
-        __syncthreads();
-    }
 
+    load_slice(0);
+    store_slice(0);
+    __syncthreads();
+    int gs = 0;  // slices done by this workgroup (LDS buffer parity)
+#pragma unroll 1
+    for (;;) {
+        int e2 = 0, r02 = 0, rows2 = 0, n02 = 0;
+        const int nid = next_valid(id + nwg, e2, r02, rows2, n02);
+        const bool has_next = nid >= 0;
+        // token ids of the next tile: for its epilogue (LDS) and its gathered rows
+        int tok_next = -1, tn[AL];
 #pragma unroll
-    for (int j = 0; j < SN; ++j) {
-        const int col = n0 + wn * WTN + j * 32 + l32;
-        const float bv = DX ? 0.0f : bias[(size_t)e * H + col];
+        for (int i = 0; i < AL; ++i) tn[i] = -1;
+        if (has_next) {
+            if (tid < BM && tid < rows2) tok_next = perm[r02 + tid];
 #pragma unroll
-        for (int i = 0; i < SM; ++i) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = wm * WTM + i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
-                const int t = tok[row];
-                if (t >= 0) {
-                    float* o = Out + (size_t)t * H + col;
-                    float v = acc[i][j][r] + bv;
-                    if (DX && accumulate) v = *o + v;
-                    *o = v;
-                }
+            for (int i = 0; i < AL; ++i) {
+                const int row = tid / TPR + RPP * i;
+                if (row < rows2) tn[i] = perm[r02 + row];
             }
         }
+#pragma unroll 1
+        for (int c = 0; c < NKC; ++c, ++gs) {
+            const int buf = gs & 1;
+            if (c + 1 < NKC) {
+                load_slice((c + 1) * KC);
+            } else if (has_next) {
+                set_a_src(tn);
+                We = W + (size_t)e2 * H * H;
+                wn0 = n02;
+                load_slice(0);
+            }
+            compute(buf);
+            if (c + 1 < NKC || has_next) store_slice(buf ^ 1);
+            __syncthreads();
+        }
+
+        // epilogue of this tile (its e, n0 and token ids)
+#pragma unroll
+        for (int j = 0; j < SN; ++j) {
+            const int col = n0 + wn * WTN + j * 32 + l32;
+            const float bv = DX ? 0.0f : bias[(size_t)e * H + col];
+#pragma unroll
+            for (int i = 0; i < SM; ++i) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = wm * WTM + i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
+                    const int t = tok[cur][row];
+                    if (t >= 0) {
+                        float* o = Out + (size_t)t * H + col;
+                        float v = acc[i][j][r] + bv;
+                        if (DX && accumulate) v = *o + v;
+                        *o = v;
+                    }
+                }
+                acc[i][j] = f32x16{};
+            }
+        }
+        if (!has_next) break;
+        if (tid < BM) tok[cur ^ 1][tid] = tok_next;  // read in the next epilogue, after its barriers
+        cur ^= 1;
+        id = nid;
+        e = e2;
+        r0 = r02;
+        rows = rows2;
+        n0 = n02;
     }
 }
 
@@ -375,9 +447,10 @@ template <int H, int BM, int BN, int KC>
 __global__ __launch_bounds__(kThreads) MOE_FWD_ATTR void k_fwd_f32(const float* __restrict__ X, const float* __restrict__ W,
                                                        const float* __restrict__ bias, float* __restrict__ Y,
                                                        const int* __restrict__ offsets,
-                                                       const int* __restrict__ perm, int NE) {
+                                                       const int* __restrict__ perm, int NE, int ntile_ids) {
     __shared__ __attribute__((aligned(16))) char smem[RowsF32Smem<BM, BN, KC, false>::bytes];
-    rows_f32_body<H, BM, BN, KC, false>(smem, blockIdx.x, X, W, bias, Y, offsets, perm, NE, 0);
+    rows_f32_body<H, BM, BN, KC, false>(smem, blockIdx.x, gridDim.x, ntile_ids, X, W, bias, Y, offsets, perm, NE,
+                                        0);
 }
 
 template <int H, int BM, int BN, int KCX, int KCW, bool MEAN>
@@ -387,12 +460,12 @@ __global__ __launch_bounds__(kThreads) void k_bwd_f32(const float* __restrict__ 
                                                        float* __restrict__ part_db,
                                                        const int* __restrict__ offsets,
                                                        const int* __restrict__ perm, int NE, int P, int T,
-                                                       int n_dx, int nh, float inv_nh) {
+                                                       int n_dx, int dx_tile_ids, int nh, float inv_nh) {
     constexpr size_t r = RowsF32Smem<BM, BN, KCX, true>::bytes, d = DwF32Smem<H, KCW>::bytes;
     __shared__ __attribute__((aligned(16))) char smem[r > d ? r : d];  // one LDS region, either role
     if ((int)blockIdx.x < n_dx)
-        rows_f32_body<H, BM, BN, KCX, true, MEAN>(smem, blockIdx.x, dY, W, nullptr, dX, offsets, perm, NE,
-                                                  accumulate, nh, inv_nh);
+        rows_f32_body<H, BM, BN, KCX, true, MEAN>(smem, blockIdx.x, n_dx, dx_tile_ids, dY, W, nullptr, dX, offsets,
+                                                  perm, NE, accumulate, nh, inv_nh);
     else
         dw_f32_body<H, KCW, MEAN>(smem, blockIdx.x - n_dx, dY, X, part_dw, part_db, offsets, perm, NE, P, T, nh,
                                   inv_nh);
@@ -426,18 +499,31 @@ static int dw_grid(int n_chunk_max) {
     return round_up(n_chunk_max, 8) * TPC;
 }
 
+// Row-GEMM workgroups once the tile ids reach `from` (0: one workgroup per tile).  Both
+// counts are multiples of 8, so every tile id a workgroup takes maps to the XCD of its
+// first one.  Forward: two per CU, its occupancy.  dX (fused backward): one per CU, the
+// dW workgroups fill the rest; below two tiles per workgroup it keeps one per tile.
+#ifndef MOE_FWD_PERSIST_WGS
+#define MOE_FWD_PERSIST_WGS 512
+#endif
+#ifndef MOE_DX_PERSIST_WGS
+#define MOE_DX_PERSIST_WGS 256
+#endif
+static int persist_wgs(int ids, int wgs, int from) { return (wgs <= 0 || ids < from) ? ids : wgs; }
+
 template <int H>
 static hipError_t fwd_f32(const float* X, const float* W, const float* bias, float* Y, const int32_t* offsets,
                           const int32_t* perm, int64_t T, int NE, hipStream_t s) {
     constexpr int BN = (H >= 128) ? 128 : H;
     const int bm = rows_bm<H>(T);
-    const int grid = rows_grid<H>(T, NE, bm);
+    const int ids = rows_grid<H>(T, NE, bm);
+    const int grid = persist_wgs(ids, MOE_FWD_PERSIST_WGS, MOE_FWD_PERSIST_WGS);
     if (bm == 128)
         hipLaunchKernelGGL((k_fwd_f32<H, 128, BN, MOE_F32_KC_FWD>), dim3(grid), dim3(kThreads), 0, s, X, W, bias, Y,
-                           offsets, perm, NE);
+                           offsets, perm, NE, ids);
     else
         hipLaunchKernelGGL((k_fwd_f32<H, MOE_ROWS_SMALL_BM, BN, MOE_F32_KC_FWD>), dim3(grid), dim3(kThreads), 0, s, X,
-                           W, bias, Y, offsets, perm, NE);
+                           W, bias, Y, offsets, perm, NE, ids);
     return hipGetLastError();
 }
 
@@ -447,16 +533,18 @@ static hipError_t bwd_f32(const float* dY, const float* X, const float* W, float
                           int n_chunk_max, int nh, hipStream_t s) {
     constexpr int BN = (H >= 128) ? 128 : H;
     const int bm = rows_bm<H>(T);
-    const int n_dx = rows_grid<H>(T, NE, bm);
+    const int dx_ids = rows_grid<H>(T, NE, bm);
+    const int n_dx = persist_wgs(dx_ids, MOE_DX_PERSIST_WGS, 2 * MOE_DX_PERSIST_WGS);  // a multiple of 8
     const int grid = n_dx + dw_grid<H>(n_chunk_max);
     const float inv_nh = 1.0f / (float)nh;
     if (bm == 128)
         hipLaunchKernelGGL((k_bwd_f32<H, 128, BN, MOE_F32_KC_DX, MOE_F32_KC_DW, MEAN>), dim3(grid), dim3(kThreads), 0,
-                           s, dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, NE, P, (int)T, n_dx, nh, inv_nh);
+                           s, dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, NE, P, (int)T, n_dx, dx_ids, nh,
+                           inv_nh);
     else
         hipLaunchKernelGGL((k_bwd_f32<H, MOE_ROWS_SMALL_BM, BN, MOE_F32_KC_DX, MOE_F32_KC_DW, MEAN>), dim3(grid),
                            dim3(kThreads), 0, s, dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, NE, P, (int)T,
-                           n_dx, nh, inv_nh);
+                           n_dx, dx_ids, nh, inv_nh);
     return hipGetLastError();
 }
 

@@ -220,15 +220,19 @@ __global__ __launch_bounds__(kRouteThreads) void k_scatter_scan(const int* __res
     }
     for (int i = tid; i < kRouteGroups * kMaxExperts; i += kRouteThreads) (&cnt[0][0])[i] = 0;
     __syncthreads();
+    // tree over the S segments of each expert (integer sums: exact in any order)
+    for (int half = S / 2; half >= 1; half >>= 1) {
+        if (tid / nep < half) {
+            part[0][tid] += part[0][tid + half * nep];
+            part[1][tid] += part[1][tid + half * nep];
+        }
+        __syncthreads();
+    }
     if (tid == 0) {
         int acc = 0;
         for (int e = 0; e < NE; ++e) {
-            int tot = 0, bef = 0;
-            for (int sg = 0; sg < S; ++sg) {
-                tot += part[0][sg * nep + e];
-                bef += part[1][sg * nep + e];
-            }
-            bb[e] = acc + bef;
+            const int tot = part[0][e];
+            bb[e] = acc + part[1][e];
             if (b == 0) {
                 counts[e] = tot;
                 offsets[e] = acc;

@@ -85,15 +85,27 @@ def bwd(d: DevInputs, o: Buffers, accumulate=False):
     moe.moe_top1_bwd(d.dy, d.x, d.W, o.offsets, o.perm, o.dx, o.dW, o.db, accumulate_dx=accumulate, workspace=o.ws)
 
 
-def aux(d: DevInputs, o: Buffers, counts=True, lam=None, probs=True):
+def aux(d: DevInputs, o: Buffers, counts=True, lam=None, probs=True, stream=None):
     moe.moe_aux_loss(d.g, o.counts if counts else None, d.lam if lam is None else lam, o.loss, o.dg,
-                     frac=o.frac, mean_prob=o.mean_prob, probs=o.probs if probs else None, workspace=o.ws)
+                     frac=o.frac, mean_prob=o.mean_prob, probs=o.probs if probs else None, workspace=o.ws,
+                     stream=stream)
 
 
-def step(d: DevInputs, o: Buffers, probs=True):
+def step(d: DevInputs, o: Buffers, probs=True, aux_stream=None):
+    """One pass of the hot path.  With `aux_stream`, the auxiliary loss (which needs only the
+    logits and the counts) runs on that stream, overlapping the backward; the calling stream
+    waits for it at the end.  The two use disjoint parts of the one workspace."""
     fwd(d, o)
+    if aux_stream is None:
+        bwd(d, o)
+        aux(d, o, probs=probs)
+        return
+    main = torch.cuda.current_stream()
+    aux_stream.wait_stream(main)
+    with torch.cuda.stream(aux_stream):
+        aux(d, o, probs=probs, stream=aux_stream)
     bwd(d, o)
-    aux(d, o, probs=probs)
+    main.wait_stream(aux_stream)
 
 
 def snapshot(o: Buffers) -> dict:

@@ -28,3 +28,25 @@ def test_repeats_are_bitwise_identical(gpu_lib, wl):
         got = gpu_run.snapshot(o_new)
         for k, v in ref.items():
             assert np.array_equal(v.view(np.uint8), got[k].view(np.uint8)), f"repeat {rep}: {k} differs"
+
+
+@pytest.mark.parametrize("wl", [workloads.workload(2), workloads.custom(20000, 5, 256, 8, gate_bias={4: 1.5}),
+                                workloads.custom(300, 5, 512, 8, act="bf16")],
+                         ids=["pages_shape", "persistent_H256", "bf16_H512"])
+def test_aux_on_second_stream_matches_serial(gpu_lib, wl):
+    """The auxiliary loss on its own stream, overlapping the backward, gives the serial
+    step's bits: the two passes share the workspace but not its regions."""
+    import torch
+    from tests import gpu_run
+    inp = workloads.make_inputs(wl)
+    d = gpu_run.upload(inp)
+    o = gpu_run.Buffers(d)
+    gpu_run.step(d, o)
+    ref = gpu_run.snapshot(o)
+    side = torch.cuda.Stream()
+    o2 = gpu_run.Buffers(d)
+    for rep in range(3):
+        gpu_run.step(d, o2, aux_stream=side)
+        got = gpu_run.snapshot(o2)
+        for k, v in ref.items():
+            assert np.array_equal(v.view(np.uint8), got[k].view(np.uint8)), f"repeat {rep}: {k} differs"

@@ -177,6 +177,17 @@ def test_workload_full_parity(gpu_lib, k):
 
 
 @pytest.mark.slow
+def test_persistent_tiles_full_parity(gpu_lib):
+    """100,000 tokens, H=256, skewed: the forward's and dX's tiles outnumber their
+    persistent workgroups three to one and more, with a ragged tile at every expert's end."""
+    from tests import gpu_run
+    wl = workloads.custom(20000, 5, 256, 8, gate_bias={4: 1.5}, lam=0.05)
+    print(f"[parity] persistent tiles {wl}", flush=True)
+    inp = workloads.make_inputs(wl)
+    check_all(inp, gpu_run.run(inp))
+
+
+@pytest.mark.slow
 def test_large_stress_sampled_parity(gpu_lib):
     """1,048,576 tokens, H=256, N_E=16: routing and the aux pass in full; routed_ctx and
     d_fused_ctx on sampled tokens; d_b in full; d_W on sampled output rows of every expert."""
