@@ -60,6 +60,38 @@ __device__ __forceinline__ void xcd_split(int bid, int per, int& major, int& min
     minor = loc / 8;
 }
 
+// Stores one 32x32 accumulator block: its row 8 (r / 4) + 4 h + (r % 4) goes to token
+// tok_of(r) (negative: a padded row, not stored), column `col`.  No load may be pending
+// when the conditional stores run: a wait inside them would also wait for every store
+// issued before it.  With `prior` the output's current value is added (gradient
+// accumulation): four rows' loads go out before their stores (a padded row reads row 0
+// and drops it), so the block waits for memory four times, not sixteen.
+template <class TokOf>
+__device__ __forceinline__ void store_block(float* __restrict__ Out, int H, int col, const f32x16& a, float bv,
+                                            bool prior, TokOf tok_of) {
+    if (prior) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            int tk[4];
+            float old[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                tk[u] = tok_of(4 * q + u);
+                old[u] = Out[(size_t)(tk[u] < 0 ? 0 : tk[u]) * H + col];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (tk[u] >= 0) Out[(size_t)tk[u] * H + col] = old[u] + (a[4 * q + u] + bv);
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int t = tok_of(r);
+            if (t >= 0) Out[(size_t)t * H + col] = a[r] + bv;
+        }
+    }
+}
+
 }  // namespace
 
 // ----------------------------------------------------------------------------------
@@ -228,6 +260,12 @@ __device__ __forceinline__ void rows_f32_body(char* smem, int wg, int nwg, int n
         }
     };
 
+    float bv_cur[SN], bv_next[SN];
+#pragma unroll
+    for (int j = 0; j < SN; ++j) {
+        bv_cur[j] = DX ? 0.0f : bias[(size_t)e * H + n0 + wn * WTN + j * 32 + l32];
+        bv_next[j] = 0.0f;
+    }
     load_slice(0);
     store_slice(0);
     __syncthreads();
@@ -242,6 +280,10 @@ __device__ __forceinline__ void rows_f32_body(char* smem, int wg, int nwg, int n
 #pragma unroll
         for (int i = 0; i < AL; ++i) tn[i] = -1;
         if (has_next) {
+            if (!DX) {
+#pragma unroll
+                for (int j = 0; j < SN; ++j) bv_next[j] = bias[(size_t)e2 * H + n02 + wn * WTN + j * 32 + l32];
+            }
             if (tid < BM && tid < rows2) tok_next = perm[r02 + tid];
 #pragma unroll
             for (int i = 0; i < AL; ++i) {
@@ -265,29 +307,22 @@ __device__ __forceinline__ void rows_f32_body(char* smem, int wg, int nwg, int n
             __syncthreads();
         }
 
-        // epilogue of this tile (its e, n0 and token ids)
+        // epilogue of this tile (its n0, bias and token ids; the bias was loaded a tile ahead,
+        // so no load is pending in the stores)
 #pragma unroll
-        for (int j = 0; j < SN; ++j) {
-            const int col = n0 + wn * WTN + j * 32 + l32;
-            const float bv = DX ? 0.0f : bias[(size_t)e * H + col];
+        for (int i = 0; i < SM; ++i) {
+            const int* tr = &tok[cur][wm * WTM + i * 32 + 4 * h];
 #pragma unroll
-            for (int i = 0; i < SM; ++i) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = wm * WTM + i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
-                    const int t = tok[cur][row];
-                    if (t >= 0) {
-                        float* o = Out + (size_t)t * H + col;
-                        float v = acc[i][j][r] + bv;
-                        if (DX && accumulate) v = *o + v;
-                        *o = v;
-                    }
-                }
+            for (int j = 0; j < SN; ++j) {
+                store_block(Out, H, n0 + wn * WTN + j * 32 + l32, acc[i][j], bv_cur[j], DX && accumulate,
+                            [&](int r) { return tr[8 * (r / 4) + (r % 4)]; });
                 acc[i][j] = f32x16{};
             }
         }
         if (!has_next) break;
         if (tid < BM) tok[cur ^ 1][tid] = tok_next;  // read in the next epilogue, after its barriers
+#pragma unroll
+        for (int j = 0; j < SN; ++j) bv_cur[j] = bv_next[j];
         cur ^= 1;
         id = nid;
         e = e2;
@@ -297,14 +332,185 @@ __device__ __forceinline__ void rows_f32_body(char* smem, int wg, int nwg, int n
     }
 }
 
+// One tile per workgroup, with a ring of PF K-slices in registers: while slice c computes,
+// the global loads of the next PF slices are outstanding (all of K when it fits), so a
+// tile waits on about three memory round trips (offsets, perm, first operands) rather than
+// one per slice.  Used when the grid has no more tiles than resident workgroups, where a
+// tile's latency is the kernel's time.
+template <int H, int BM, int BN, int KC, bool DX, bool MEAN = false>
+__device__ __forceinline__ void rows_f32_onepass_body(char* smem, int bid, const float* __restrict__ A,
+                                                      const float* __restrict__ W, const float* __restrict__ bias,
+                                                      float* __restrict__ Out, const int* __restrict__ offsets,
+                                                      const int* __restrict__ perm, int NE, int accumulate,
+                                                      int nh = 1, float inv_nh = 1.0f) {
+    constexpr int NKC = H / KC;
+    constexpr int NT = H / BN;
+    constexpr int WM = (BM >= 64) ? 2 : 1, WN = 4 / WM;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int SM = WTM / 32, SN = WTN / 32;
+    static_assert(SM >= 1 && SN >= 1, "wavefront tile must hold a 32x32 block");
+    constexpr int TPR = KC / 4, RPP = kThreads / TPR;
+    constexpr int AL = BM / RPP, BL = BN * KC / (4 * kThreads);
+    static_assert(KC % 8 == 0 && BM % RPP == 0 && (BN * KC) % (4 * kThreads) == 0, "tile shape");
+    constexpr int PF0 = 24 / (AL + BL);  // about 96 registers of slices in flight
+    constexpr int PF = PF0 < 1 ? 1 : (PF0 > NKC ? NKC : PF0);
+    constexpr int BS_ROWS = DX ? KC : BN;
+    constexpr int BS_COLS = DX ? BN + kPadKN : KC + kPad;
+    using SM_ = RowsF32Smem<BM, BN, KC, DX>;
+    float(&As)[2][BM][KC + kPad] = *reinterpret_cast<float(*)[2][BM][KC + kPad]>(smem);
+    float(&Bs)[2][BS_ROWS][BS_COLS] = *reinterpret_cast<float(*)[2][BS_ROWS][BS_COLS]>(smem + SM_::a);
+    int(&tok)[2][BM] = *reinterpret_cast<int(*)[2][BM]>(smem + SM_::a + SM_::b);
+
+    const int tid = threadIdx.x;
+    const int wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
+    const int wm = wave / WN, wn = wave % WN;
+
+    int mt, nt, e, r0, r1;
+    xcd_split(bid, NT, mt, nt);
+    if (!find_tile(offsets, NE, mt, BM, e, r0, r1)) return;
+    const int rows = r1 - r0, n0 = nt * BN;
+    const float* __restrict__ We = W + (size_t)e * H * H;
+
+    // token ids: of this thread's A rows (registers) and of the tile's rows (LDS, epilogue)
+    int ta[AL];
+#pragma unroll
+    for (int i = 0; i < AL; ++i) {
+        const int row = tid / TPR + RPP * i;
+        ta[i] = (row < rows) ? perm[r0 + row] : -1;
+    }
+    const int tok_mine = (tid < BM && tid < rows) ? perm[r0 + tid] : -1;  // to LDS once the loads are out
+
+    f32x4 ra[PF][AL], rb[PF][BL];
+    auto load_b = [&](int c, int slot) {
+        const int k0 = c * KC;
+#pragma unroll
+        for (int i = 0; i < BL; ++i) {
+            if (!DX) {
+                const int r = tid / TPR + RPP * i, cc = 4 * (tid % TPR);
+                rb[slot][i] = ld4(We + (size_t)(n0 + r) * H + k0 + cc);
+            } else {
+                const int q = tid + kThreads * i, r = q / (BN / 4), cc = 4 * (q % (BN / 4));
+                rb[slot][i] = ld4(We + (size_t)(k0 + r) * H + n0 + cc);
+            }
+        }
+    };
+    const float* a_src[AL];
+    auto load_a = [&](int c, int slot) {
+#pragma unroll
+        for (int i = 0; i < AL; ++i) {
+            ra[slot][i] = ld4(a_src[i] + c * KC);
+            if (MEAN) ra[slot][i] *= inv_nh;
+        }
+    };
+    auto store_slice = [&](int slot, int buf) {
+#pragma unroll
+        for (int i = 0; i < AL; ++i) st4(&As[buf][tid / TPR + RPP * i][4 * (tid % TPR)], ra[slot][i]);
+#pragma unroll
+        for (int i = 0; i < BL; ++i) {
+            if (!DX) {
+                st4(&Bs[buf][tid / TPR + RPP * i][4 * (tid % TPR)], rb[slot][i]);
+            } else {
+                const int q = tid + kThreads * i;
+                st4(&Bs[buf][q / (BN / 4)][4 * (q % (BN / 4))], rb[slot][i]);
+            }
+        }
+    };
+
+    // W does not depend on perm: its loads go out while the token ids are in flight (loads
+    // return in issue order, so the ids arrive first).  The fences keep the compiler from
+    // sinking loads next to their first use.
+    float bv[SN];  // complete before the stores (the K loop waits for every load), see below
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < SN; ++j) bv[j] = DX ? 0.0f : bias[(size_t)e * H + n0 + wn * WTN + j * 32 + l32];
+#pragma unroll
+    for (int c = 0; c < PF; ++c) load_b(c, c);
+    __builtin_amdgcn_sched_barrier(0);
+    // a padded row reads token 0's row: output rows are independent and padded ones are
+    // never stored, so no branch is needed around the loads
+#pragma unroll
+    for (int i = 0; i < AL; ++i) {
+        const int t = ta[i] < 0 ? 0 : ta[i];
+        a_src[i] = A + (size_t)(MEAN ? t / nh : t) * H + 4 * (tid % TPR);
+    }
+#pragma unroll
+    for (int c = 0; c < PF; ++c) load_a(c, c);
+    __builtin_amdgcn_sched_barrier(0);
+    if (tid < BM) tok[0][tid] = tok_mine;  // read in the epilogue, after the barriers
+
+    f32x16 acc[SM][SN];
+#pragma unroll
+    for (int i = 0; i < SM; ++i)
+#pragma unroll
+        for (int j = 0; j < SN; ++j) acc[i][j] = f32x16{};
+    constexpr int NG = KC / 8;
+    f32x4 fa[2][SM], fb[2][SN];
+    auto load_frag = [&](int buf, int g, int fs) {
+        const int kk = 8 * g + 4 * h;
+#pragma unroll
+        for (int i = 0; i < SM; ++i) fa[fs][i] = ld4(&As[buf][wm * WTM + i * 32 + l32][kk]);
+#pragma unroll
+        for (int j = 0; j < SN; ++j) {
+            if (!DX) {
+                fb[fs][j] = ld4(&Bs[buf][wn * WTN + j * 32 + l32][kk]);
+            } else {
+                const int cc = wn * WTN + j * 32 + l32;
+                fb[fs][j] = f32x4{Bs[buf][kk + 0][cc], Bs[buf][kk + 1][cc], Bs[buf][kk + 2][cc], Bs[buf][kk + 3][cc]};
+            }
+        }
+    };
+    auto compute = [&](int buf) {
+        load_frag(buf, 0, 0);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            if (g + 1 < NG) load_frag(buf, g + 1, (g + 1) & 1);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int i = 0; i < SM; ++i)
+#pragma unroll
+                    for (int j = 0; j < SN; ++j) acc[i][j] = mfma32(fa[g & 1][i][s], fb[g & 1][j][s], acc[i][j]);
+        }
+    };
+
+    store_slice(0, 0);
+    if (PF < NKC) {
+        load_b(PF, 0);
+        load_a(PF, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) {
+        if (c + 1 < NKC) {
+            store_slice((c + 1) % PF, (c + 1) & 1);
+            if (c + 1 + PF < NKC) {
+                load_b(c + 1 + PF, (c + 1) % PF);
+                load_a(c + 1 + PF, (c + 1) % PF);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        compute(c & 1);
+        if (c + 1 < NKC) __syncthreads();
+    }
+
+#pragma unroll
+    for (int i = 0; i < SM; ++i) {
+        const int* tr = &tok[0][wm * WTM + i * 32 + 4 * h];
+#pragma unroll
+        for (int j = 0; j < SN; ++j)
+            store_block(Out, H, n0 + wn * WTN + j * 32 + l32, acc[i][j], bv[j], DX && accumulate,
+                        [&](int r) { return tr[8 * (r / 4) + (r % 4)]; });
+    }
+}
+
 // ----------------------------------------------------------------------------------
 // dW / db partials.  Workgroup (chunk c, tile (ot, it)): the chunk's tokens of one expert,
 // output block dW[o0:o0+BT, i0:i0+BT].  M = o, N = i, K = tokens.
 //   part_dw[c][o][i] = sum_{t in chunk} dY[t][o] X[t][i]
 //   part_db[c][o]    = sum_{t in chunk} dY[t][o]          (tiles with it == 0)
 // Token order inside a chunk is fixed (perm order), as is the MFMA accumulation order.
-// Same two-buffer pipeline as the row GEMM; token ids of slice c+2 are fetched while slice
-// c+1's rows are being loaded, so the gather never waits on an index load.
+// Slices go through two LDS buffers, fed from register rings of rows and token ids.
 // ----------------------------------------------------------------------------------
 template <int H, int KC>
 struct DwF32Smem {
@@ -313,6 +519,9 @@ struct DwF32Smem {
     static constexpr size_t bytes = 2 * a;
 };
 
+#ifndef MOE_DW_PF
+#define MOE_DW_PF 2  // K slices of rows in flight per dW workgroup (even)
+#endif
 template <int H, int KC, bool MEAN = false>
 __device__ __forceinline__ void dw_f32_body(char* smem, int bid, const float* __restrict__ dY,
                                                       const float* __restrict__ X,
@@ -326,6 +535,7 @@ __device__ __forceinline__ void dw_f32_body(char* smem, int bid, const float* __
     constexpr int WT = BT / 2, SUB = WT / 32;
     constexpr int Q = BT / 4;                  // float4 per row segment
     constexpr int LD = KC * Q / kThreads;      // float4 loads per thread per tensor per slice
+    constexpr int PF = MOE_DW_PF;
     float(&As)[2][KC][BT + kPadKN] = *reinterpret_cast<float(*)[2][KC][BT + kPadKN]>(smem);  // dY rows, o0..o0+BT
     float(&Bs)[2][KC][BT + kPadKN] =
         *reinterpret_cast<float(*)[2][KC][BT + kPadKN]>(smem + DwF32Smem<H, KC>::a);      // X rows, i0..i0+BT
@@ -348,75 +558,93 @@ __device__ __forceinline__ void dw_f32_body(char* smem, int bid, const float* __
         for (int j = 0; j < SUB; ++j) acc[i][j] = f32x16{};
     float dbacc = 0.0f;
 
-    int tk[LD];
-    f32x4 ra[LD], rb[LD];
-    auto load_ids = [&](int s) {
+    // Two register rings, slot k % PF for slice k: the rows of slices s+1 .. s+PF and the
+    // token ids of slices s+PF+1 .. s+2PF are in flight while slice s computes, so neither
+    // the gather nor its index loads wait on memory.  Loads past the chunk's end read its
+    // last token and are zeroed when stored to LDS, so no load sits in a branch and no
+    // result is touched before its slice is due (either would drain the ring).
+    int tk[PF][LD];
+    f32x4 ra[PF][LD], rb[PF][LD];
+    auto kpos = [&](int sl, int i) { return t0 + sl * KC + (tid + kThreads * i) / Q; };
+    auto load_ids = [&](int sl, int slot) {
 #pragma unroll
         for (int i = 0; i < LD; ++i) {
-            const int k = t0 + s * KC + (tid + kThreads * i) / Q;
-            tk[i] = (s < nslices && k < t1) ? perm[k] : -1;
+            const int k = kpos(sl, i);
+            tk[slot][i] = perm[k < t1 ? k : t1 - 1];
         }
     };
-    auto load_rows = [&]() {
+    auto load_rows = [&](int sl, int slot) {  // ids of slice sl are in tk[slot]; rows go to slot
 #pragma unroll
         for (int i = 0; i < LD; ++i) {
             const int cc = 4 * ((tid + kThreads * i) % Q);
-            ra[i] = f32x4{};
-            rb[i] = f32x4{};
-            if (tk[i] >= 0) {
-                const size_t t = (size_t)tk[i];
-                if (MEAN) {
-                    ra[i] = ld4(dY + (t / nh) * H + o0 + cc) * inv_nh;
-                } else {
-                    ra[i] = ld4(dY + t * H + o0 + cc);
-                }
-                rb[i] = ld4(X + t * H + i0 + cc);
-            }
+            const size_t t = (size_t)tk[slot][i];
+            ra[slot][i] = ld4(dY + (MEAN ? t / nh : t) * H + o0 + cc);
+            rb[slot][i] = ld4(X + t * H + i0 + cc);
         }
     };
-    auto store_rows = [&](int buf) {
+    auto store_rows = [&](int sl, int slot, int buf) {  // masking here, where the rows have arrived
 #pragma unroll
         for (int i = 0; i < LD; ++i) {
             const int q = tid + kThreads * i;
-            st4(&As[buf][q / Q][4 * (q % Q)], ra[i]);
-            st4(&Bs[buf][q / Q][4 * (q % Q)], rb[i]);
+            const bool v = kpos(sl, i) < t1;
+            f32x4 av = ra[slot][i];
+            if (MEAN) av *= inv_nh;
+            st4(&As[buf][q / Q][4 * (q % Q)], v ? av : f32x4{});
+            st4(&Bs[buf][q / Q][4 * (q % Q)], v ? rb[slot][i] : f32x4{});
         }
     };
 
-    load_ids(0);
-    load_rows();
-    load_ids(1);
-    store_rows(0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < PF; ++k) load_ids(k, k);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < PF; ++k) load_rows(k, k);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < PF; ++k) load_ids(PF + k, k);
+    __builtin_amdgcn_sched_barrier(0);
+    store_rows(0, 0, 0);
+    load_rows(PF, 0);
+    load_ids(2 * PF, 0);
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
+    static_assert(PF % 2 == 0, "the LDS buffer of slice s0 + u is u % 2");
 #pragma unroll 1
-    for (int s = 0; s < nslices; ++s) {
-        const int buf = s & 1;
-        if (s + 1 < nslices) {
-            load_rows();       // rows of slice s+1 (ids fetched one slice earlier)
-            load_ids(s + 2);
-        }
+    for (int s0 = 0; s0 < nslices; s0 += PF) {
 #pragma unroll
-        for (int kk = 0; kk < KC; kk += 8) {
+        for (int u = 0; u < PF; ++u) {
+            const int sl = s0 + u;
+            if (sl >= nslices) break;
+            // unconditional, also past the chunk's end (masked rows, clamped ids): a load under
+            // a branch makes the wait counts at the next slice conservative
+            store_rows(sl + 1, (u + 1) % PF, (u + 1) & 1);
+            load_rows(sl + 1 + PF, (u + 1) % PF);
+            load_ids(sl + 1 + 2 * PF, (u + 1) % PF);
+            __builtin_amdgcn_sched_barrier(0);
+            const int buf = u & 1;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int k = kk + 4 * h + q;
-                float a[SUB], b[SUB];
+            for (int kk = 0; kk < KC; kk += 8) {
 #pragma unroll
-                for (int i = 0; i < SUB; ++i) a[i] = As[buf][k][wm * WT + i * 32 + l32];
+                for (int q = 0; q < 4; ++q) {
+                    const int k = kk + 4 * h + q;
+                    float a[SUB], b[SUB];
 #pragma unroll
-                for (int j = 0; j < SUB; ++j) b[j] = Bs[buf][k][wn * WT + j * 32 + l32];
+                    for (int i = 0; i < SUB; ++i) a[i] = As[buf][k][wm * WT + i * 32 + l32];
 #pragma unroll
-                for (int i = 0; i < SUB; ++i)
+                    for (int j = 0; j < SUB; ++j) b[j] = Bs[buf][k][wn * WT + j * 32 + l32];
 #pragma unroll
-                    for (int j = 0; j < SUB; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+                    for (int i = 0; i < SUB; ++i)
+#pragma unroll
+                        for (int j = 0; j < SUB; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+                }
             }
+            if (do_db && tid < BT) {
+#pragma unroll
+                for (int k = 0; k < KC; ++k) dbacc += As[buf][k][tid];
+            }
+            __syncthreads();
         }
-        if (do_db && tid < BT) {
-#pragma unroll 8
-            for (int k = 0; k < KC; ++k) dbacc += As[buf][k][tid];
-        }
-        if (s + 1 < nslices) store_rows(buf ^ 1);
-        __syncthreads();
     }
 
     float* __restrict__ Pd = part_dw + (size_t)c * H * H;
@@ -443,17 +671,20 @@ __device__ __forceinline__ void dw_f32_body(char* smem, int bid, const float* __
 #else
 #define MOE_FWD_ATTR
 #endif
-template <int H, int BM, int BN, int KC>
+template <int H, int BM, int BN, int KC, bool ONE>
 __global__ __launch_bounds__(kThreads) MOE_FWD_ATTR void k_fwd_f32(const float* __restrict__ X, const float* __restrict__ W,
                                                        const float* __restrict__ bias, float* __restrict__ Y,
                                                        const int* __restrict__ offsets,
                                                        const int* __restrict__ perm, int NE, int ntile_ids) {
     __shared__ __attribute__((aligned(16))) char smem[RowsF32Smem<BM, BN, KC, false>::bytes];
-    rows_f32_body<H, BM, BN, KC, false>(smem, blockIdx.x, gridDim.x, ntile_ids, X, W, bias, Y, offsets, perm, NE,
-                                        0);
+    if (ONE)
+        rows_f32_onepass_body<H, BM, BN, KC, false>(smem, blockIdx.x, X, W, bias, Y, offsets, perm, NE, 0);
+    else
+        rows_f32_body<H, BM, BN, KC, false>(smem, blockIdx.x, gridDim.x, ntile_ids, X, W, bias, Y, offsets, perm,
+                                            NE, 0);
 }
 
-template <int H, int BM, int BN, int KCX, int KCW, bool MEAN>
+template <int H, int BM, int BN, int KCX, int KCW, bool MEAN, bool ONE>
 __global__ __launch_bounds__(kThreads) void k_bwd_f32(const float* __restrict__ dY, const float* __restrict__ X,
                                                        const float* __restrict__ W, float* __restrict__ dX,
                                                        int accumulate, float* __restrict__ part_dw,
@@ -463,9 +694,14 @@ __global__ __launch_bounds__(kThreads) void k_bwd_f32(const float* __restrict__ 
                                                        int n_dx, int dx_tile_ids, int nh, float inv_nh) {
     constexpr size_t r = RowsF32Smem<BM, BN, KCX, true>::bytes, d = DwF32Smem<H, KCW>::bytes;
     __shared__ __attribute__((aligned(16))) char smem[r > d ? r : d];  // one LDS region, either role
-    if ((int)blockIdx.x < n_dx)
-        rows_f32_body<H, BM, BN, KCX, true, MEAN>(smem, blockIdx.x, n_dx, dx_tile_ids, dY, W, nullptr, dX, offsets,
-                                                  perm, NE, accumulate, nh, inv_nh);
+    if ((int)blockIdx.x < n_dx) {
+        if (ONE)
+            rows_f32_onepass_body<H, BM, BN, KCX, true, MEAN>(smem, blockIdx.x, dY, W, nullptr, dX, offsets, perm, NE,
+                                                              accumulate, nh, inv_nh);
+        else
+            rows_f32_body<H, BM, BN, KCX, true, MEAN>(smem, blockIdx.x, n_dx, dx_tile_ids, dY, W, nullptr, dX,
+                                                      offsets, perm, NE, accumulate, nh, inv_nh);
+    }
     else
         dw_f32_body<H, KCW, MEAN>(smem, blockIdx.x - n_dx, dY, X, part_dw, part_db, offsets, perm, NE, P, T, nh,
                                   inv_nh);
@@ -510,6 +746,11 @@ static int dw_grid(int n_chunk_max) {
 #define MOE_DX_PERSIST_WGS 256
 #endif
 static int persist_wgs(int ids, int wgs, int from) { return (wgs <= 0 || ids < from) ? ids : wgs; }
+// Up to this many small-row tiles, a grid of one-tile workgroups with every K slice in
+// flight (the tiles fit in the resident slots, so latency, not throughput, bounds them).
+#ifndef MOE_ROWS_ONEPASS_MAX_IDS
+#define MOE_ROWS_ONEPASS_MAX_IDS 512
+#endif
 
 template <int H>
 static hipError_t fwd_f32(const float* X, const float* W, const float* bias, float* Y, const int32_t* offsets,
@@ -519,11 +760,14 @@ static hipError_t fwd_f32(const float* X, const float* W, const float* bias, flo
     const int ids = rows_grid<H>(T, NE, bm);
     const int grid = persist_wgs(ids, MOE_FWD_PERSIST_WGS, MOE_FWD_PERSIST_WGS);
     if (bm == 128)
-        hipLaunchKernelGGL((k_fwd_f32<H, 128, BN, MOE_F32_KC_FWD>), dim3(grid), dim3(kThreads), 0, s, X, W, bias, Y,
-                           offsets, perm, NE, ids);
+        hipLaunchKernelGGL((k_fwd_f32<H, 128, BN, MOE_F32_KC_FWD, false>), dim3(grid), dim3(kThreads), 0, s, X, W,
+                           bias, Y, offsets, perm, NE, ids);
+    else if (ids <= MOE_ROWS_ONEPASS_MAX_IDS)
+        hipLaunchKernelGGL((k_fwd_f32<H, MOE_ROWS_SMALL_BM, BN, MOE_F32_KC_FWD, true>), dim3(ids), dim3(kThreads), 0,
+                           s, X, W, bias, Y, offsets, perm, NE, ids);
     else
-        hipLaunchKernelGGL((k_fwd_f32<H, MOE_ROWS_SMALL_BM, BN, MOE_F32_KC_FWD>), dim3(grid), dim3(kThreads), 0, s, X,
-                           W, bias, Y, offsets, perm, NE, ids);
+        hipLaunchKernelGGL((k_fwd_f32<H, MOE_ROWS_SMALL_BM, BN, MOE_F32_KC_FWD, false>), dim3(grid), dim3(kThreads), 0,
+                           s, X, W, bias, Y, offsets, perm, NE, ids);
     return hipGetLastError();
 }
 
@@ -534,17 +778,22 @@ static hipError_t bwd_f32(const float* dY, const float* X, const float* W, float
     constexpr int BN = (H >= 128) ? 128 : H;
     const int bm = rows_bm<H>(T);
     const int dx_ids = rows_grid<H>(T, NE, bm);
-    const int n_dx = persist_wgs(dx_ids, MOE_DX_PERSIST_WGS, 2 * MOE_DX_PERSIST_WGS);  // a multiple of 8
+    const bool one = bm != 128 && dx_ids <= MOE_ROWS_ONEPASS_MAX_IDS;
+    const int n_dx = one ? dx_ids : persist_wgs(dx_ids, MOE_DX_PERSIST_WGS, 2 * MOE_DX_PERSIST_WGS);  // multiple of 8
     const int grid = n_dx + dw_grid<H>(n_chunk_max);
     const float inv_nh = 1.0f / (float)nh;
     if (bm == 128)
-        hipLaunchKernelGGL((k_bwd_f32<H, 128, BN, MOE_F32_KC_DX, MOE_F32_KC_DW, MEAN>), dim3(grid), dim3(kThreads), 0,
-                           s, dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, NE, P, (int)T, n_dx, dx_ids, nh,
-                           inv_nh);
-    else
-        hipLaunchKernelGGL((k_bwd_f32<H, MOE_ROWS_SMALL_BM, BN, MOE_F32_KC_DX, MOE_F32_KC_DW, MEAN>), dim3(grid),
+        hipLaunchKernelGGL((k_bwd_f32<H, 128, BN, MOE_F32_KC_DX, MOE_F32_KC_DW, MEAN, false>), dim3(grid),
                            dim3(kThreads), 0, s, dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, NE, P, (int)T,
                            n_dx, dx_ids, nh, inv_nh);
+    else if (one)
+        hipLaunchKernelGGL((k_bwd_f32<H, MOE_ROWS_SMALL_BM, BN, MOE_F32_KC_DX, MOE_F32_KC_DW, MEAN, true>), dim3(grid),
+                           dim3(kThreads), 0, s, dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, NE, P, (int)T,
+                           n_dx, dx_ids, nh, inv_nh);
+    else
+        hipLaunchKernelGGL((k_bwd_f32<H, MOE_ROWS_SMALL_BM, BN, MOE_F32_KC_DX, MOE_F32_KC_DW, MEAN, false>),
+                           dim3(grid), dim3(kThreads), 0, s, dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, NE, P,
+                           (int)T, n_dx, dx_ids, nh, inv_nh);
     return hipGetLastError();
 }
 
