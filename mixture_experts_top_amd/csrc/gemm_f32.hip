@@ -34,9 +34,6 @@ constexpr int kThreads = 256;   // 4 waves, arranged 2 x 2 over the output tile
 #ifndef MOE_F32_KC_DW
 #define MOE_F32_KC_DW 16
 #endif
-#ifndef MOE_ROWS_BIG_TILES_PER_CU
-#define MOE_ROWS_BIG_TILES_PER_CU 2
-#endif
 constexpr int kPad = 4;         // LDS row padding (floats) for K-contiguous tiles: 16-byte aligned rows
 #ifndef MOE_F32_PAD_KN
 #define MOE_F32_PAD_KN 8
@@ -126,8 +123,10 @@ __device__ __forceinline__ void rows_f32_body(char* smem, int wg, int nwg, int n
     constexpr int SM = WTM / 32, SN = WTN / 32;
     static_assert(SM >= 1 && SN >= 1, "wavefront tile must hold a 32x32 block");
     constexpr int TPR = KC / 4, RPP = kThreads / TPR;   // threads per row slice, rows per pass
-    constexpr int AL = BM / RPP, BL = BN * KC / (4 * kThreads);  // float4 loads per thread per slice
-    static_assert(KC % 8 == 0 && BM % RPP == 0 && (BN * KC) % (4 * kThreads) == 0, "tile shape");
+    // float4 loads per thread per slice; with BM < RPP only the first BM row-threads load A
+    constexpr int AL = (BM + RPP - 1) / RPP, BL = BN * KC / (4 * kThreads);
+    constexpr bool AFULL = BM % RPP == 0;
+    static_assert(KC % 8 == 0 && (AFULL || RPP % BM == 0) && (BN * KC) % (4 * kThreads) == 0, "tile shape");
     constexpr int BS_ROWS = DX ? KC : BN;
     constexpr int BS_COLS = DX ? BN + kPadKN : KC + kPad;
     using SM_ = RowsF32Smem<BM, BN, KC, DX>;
@@ -187,7 +186,10 @@ __device__ __forceinline__ void rows_f32_body(char* smem, int wg, int nwg, int n
     {
         int t0[AL];
 #pragma unroll
-        for (int i = 0; i < AL; ++i) t0[i] = tok[cur][tid / TPR + RPP * i];
+        for (int i = 0; i < AL; ++i) {
+            const int row = tid / TPR + RPP * i;
+            t0[i] = (AFULL || row < BM) ? tok[cur][row] : -1;
+        }
         set_a_src(t0);
     }
     f32x4 ra[AL], rb[BL];
@@ -210,7 +212,10 @@ __device__ __forceinline__ void rows_f32_body(char* smem, int wg, int nwg, int n
     };
     auto store_slice = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < AL; ++i) st4(&As[buf][tid / TPR + RPP * i][4 * (tid % TPR)], ra[i]);
+        for (int i = 0; i < AL; ++i) {
+            const int row = tid / TPR + RPP * i;
+            if (AFULL || row < BM) st4(&As[buf][row][4 * (tid % TPR)], ra[i]);
+        }
 #pragma unroll
         for (int i = 0; i < BL; ++i) {
             if (!DX) {
@@ -337,6 +342,9 @@ __device__ __forceinline__ void rows_f32_body(char* smem, int wg, int nwg, int n
 // tile waits on about three memory round trips (offsets, perm, first operands) rather than
 // one per slice.  Used when the grid has no more tiles than resident workgroups, where a
 // tile's latency is the kernel's time.
+#ifndef MOE_ONEPASS_RING_F4
+#define MOE_ONEPASS_RING_F4 12  // float4 registers per thread for the one-pass slice ring (keeps 4 waves/SIMD)
+#endif
 template <int H, int BM, int BN, int KC, bool DX, bool MEAN = false>
 __device__ __forceinline__ void rows_f32_onepass_body(char* smem, int bid, const float* __restrict__ A,
                                                       const float* __restrict__ W, const float* __restrict__ bias,
@@ -350,9 +358,10 @@ __device__ __forceinline__ void rows_f32_onepass_body(char* smem, int bid, const
     constexpr int SM = WTM / 32, SN = WTN / 32;
     static_assert(SM >= 1 && SN >= 1, "wavefront tile must hold a 32x32 block");
     constexpr int TPR = KC / 4, RPP = kThreads / TPR;
-    constexpr int AL = BM / RPP, BL = BN * KC / (4 * kThreads);
-    static_assert(KC % 8 == 0 && BM % RPP == 0 && (BN * KC) % (4 * kThreads) == 0, "tile shape");
-    constexpr int PF0 = 24 / (AL + BL);  // about 96 registers of slices in flight
+    constexpr int AL = (BM + RPP - 1) / RPP, BL = BN * KC / (4 * kThreads);
+    constexpr bool AFULL = BM % RPP == 0;  // else only the first BM row-threads load A
+    static_assert(KC % 8 == 0 && (AFULL || RPP % BM == 0) && (BN * KC) % (4 * kThreads) == 0, "tile shape");
+    constexpr int PF0 = MOE_ONEPASS_RING_F4 / (AL + BL);  // float4 registers of slices in flight
     constexpr int PF = PF0 < 1 ? 1 : (PF0 > NKC ? NKC : PF0);
     constexpr int BS_ROWS = DX ? KC : BN;
     constexpr int BS_COLS = DX ? BN + kPadKN : KC + kPad;
@@ -404,7 +413,10 @@ __device__ __forceinline__ void rows_f32_onepass_body(char* smem, int bid, const
     };
     auto store_slice = [&](int slot, int buf) {
 #pragma unroll
-        for (int i = 0; i < AL; ++i) st4(&As[buf][tid / TPR + RPP * i][4 * (tid % TPR)], ra[slot][i]);
+        for (int i = 0; i < AL; ++i) {
+            const int row = tid / TPR + RPP * i;
+            if (AFULL || row < BM) st4(&As[buf][row][4 * (tid % TPR)], ra[slot][i]);
+        }
 #pragma unroll
         for (int i = 0; i < BL; ++i) {
             if (!DX) {
@@ -512,9 +524,8 @@ __device__ __forceinline__ void rows_f32_onepass_body(char* smem, int bid, const
 // Token order inside a chunk is fixed (perm order), as is the MFMA accumulation order.
 // Slices go through two LDS buffers, fed from register rings of rows and token ids.
 // ----------------------------------------------------------------------------------
-template <int H, int KC>
+template <int BT, int KC>
 struct DwF32Smem {
-    static constexpr int BT = (H >= 128) ? 128 : 64;
     static constexpr size_t a = sizeof(float) * 2 * KC * (BT + kPadKN);
     static constexpr size_t bytes = 2 * a;
 };
@@ -522,7 +533,7 @@ struct DwF32Smem {
 #ifndef MOE_DW_PF
 #define MOE_DW_PF 2  // K slices of rows in flight per dW workgroup (even)
 #endif
-template <int H, int KC, bool MEAN = false>
+template <int H, int BT, int KC, bool MEAN = false>
 __device__ __forceinline__ void dw_f32_body(char* smem, int bid, const float* __restrict__ dY,
                                                       const float* __restrict__ X,
                                                       float* __restrict__ part_dw,
@@ -530,7 +541,6 @@ __device__ __forceinline__ void dw_f32_body(char* smem, int bid, const float* __
                                                       const int* __restrict__ offsets,
                                                       const int* __restrict__ perm, int NE,
                                                       int P, int T, int nh = 1, float inv_nh = 1.0f) {
-    constexpr int BT = (H >= 128) ? 128 : 64;
     constexpr int NTI = H / BT, TPC = NTI * NTI;
     constexpr int WT = BT / 2, SUB = WT / 32;
     constexpr int Q = BT / 4;                  // float4 per row segment
@@ -538,7 +548,7 @@ __device__ __forceinline__ void dw_f32_body(char* smem, int bid, const float* __
     constexpr int PF = MOE_DW_PF;
     float(&As)[2][KC][BT + kPadKN] = *reinterpret_cast<float(*)[2][KC][BT + kPadKN]>(smem);  // dY rows, o0..o0+BT
     float(&Bs)[2][KC][BT + kPadKN] =
-        *reinterpret_cast<float(*)[2][KC][BT + kPadKN]>(smem + DwF32Smem<H, KC>::a);      // X rows, i0..i0+BT
+        *reinterpret_cast<float(*)[2][KC][BT + kPadKN]>(smem + DwF32Smem<BT, KC>::a);      // X rows, i0..i0+BT
 
     int c, tile;
     xcd_split(bid, TPC, c, tile);
@@ -684,7 +694,7 @@ __global__ __launch_bounds__(kThreads) MOE_FWD_ATTR void k_fwd_f32(const float* 
                                             NE, 0);
 }
 
-template <int H, int BM, int BN, int KCX, int KCW, bool MEAN, bool ONE>
+template <int H, int BM, int BN, int BT, int KCX, int KCW, bool MEAN, bool ONE>
 __global__ __launch_bounds__(kThreads) void k_bwd_f32(const float* __restrict__ dY, const float* __restrict__ X,
                                                        const float* __restrict__ W, float* __restrict__ dX,
                                                        int accumulate, float* __restrict__ part_dw,
@@ -692,7 +702,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_f32(const float* __restrict__ 
                                                        const int* __restrict__ offsets,
                                                        const int* __restrict__ perm, int NE, int P, int T,
                                                        int n_dx, int dx_tile_ids, int nh, float inv_nh) {
-    constexpr size_t r = RowsF32Smem<BM, BN, KCX, true>::bytes, d = DwF32Smem<H, KCW>::bytes;
+    constexpr size_t r = RowsF32Smem<BM, BN, KCX, true>::bytes, d = DwF32Smem<BT, KCW>::bytes;
     __shared__ __attribute__((aligned(16))) char smem[r > d ? r : d];  // one LDS region, either role
     if ((int)blockIdx.x < n_dx) {
         if (ONE)
@@ -703,7 +713,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_f32(const float* __restrict__ 
                                                       offsets, perm, NE, accumulate, nh, inv_nh);
     }
     else
-        dw_f32_body<H, KCW, MEAN>(smem, blockIdx.x - n_dx, dY, X, part_dw, part_db, offsets, perm, NE, P, T, nh,
+        dw_f32_body<H, BT, KCW, MEAN>(smem, blockIdx.x - n_dx, dY, X, part_dw, part_db, offsets, perm, NE, P, T, nh,
                                   inv_nh);
 }
 
@@ -712,25 +722,30 @@ __global__ __launch_bounds__(kThreads) void k_bwd_f32(const float* __restrict__ 
 // ----------------------------------------------------------------------------------
 static inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
-// 128-row tiles once they give enough workgroups per compute unit, else 64-row tiles.
+// Tiles: 128 x (128 or H) rows x columns and 128 x 128 d_W tiles at large T; at small T
+// MOE_ROWS_SMALL_BM x MOE_ROWS_SMALL_BN and MOE_DW_SMALL_BT (f32_big_tiles decides).
 #ifndef MOE_ROWS_SMALL_BM
 #define MOE_ROWS_SMALL_BM 64
 #endif
+#ifndef MOE_ROWS_SMALL_BN
+#define MOE_ROWS_SMALL_BN 128
+#endif
 template <int H>
-static int rows_bm(int64_t T) {
-    constexpr int NT = H / ((H >= 128) ? 128 : H);
-    return ((T / 128) * NT >= MOE_ROWS_BIG_TILES_PER_CU * 256) ? 128 : MOE_ROWS_SMALL_BM;
-}
+struct F32Tiles {
+    static constexpr int BIG_BN = (H >= 128) ? 128 : H;
+    static constexpr int BIG_BT = (H >= 128) ? 128 : 64;
+    static constexpr int SMALL_BN = (MOE_ROWS_SMALL_BN < H) ? MOE_ROWS_SMALL_BN : H;
+    static constexpr int SMALL_BM = (SMALL_BN == 128 || MOE_ROWS_SMALL_BM >= 64) ? MOE_ROWS_SMALL_BM : 64;
+    static constexpr int SMALL_BT = (MOE_DW_SMALL_BT < H) ? MOE_DW_SMALL_BT : H;
+};
 
-template <int H>
+template <int H, int BN>
 static int rows_grid(int64_t T, int NE, int bm) {
-    constexpr int NT = H / ((H >= 128) ? 128 : H);
-    return round_up((int)((T + bm - 1) / bm) + NE, 8) * NT;
+    return round_up((int)((T + bm - 1) / bm) + NE, 8) * (H / BN);
 }
 
-template <int H>
+template <int H, int BT>
 static int dw_grid(int n_chunk_max) {
-    constexpr int BT = (H >= 128) ? 128 : 64;
     constexpr int TPC = (H / BT) * (H / BT);
     return round_up(n_chunk_max, 8) * TPC;
 }
@@ -749,25 +764,28 @@ static int persist_wgs(int ids, int wgs, int from) { return (wgs <= 0 || ids < f
 // Up to this many small-row tiles, a grid of one-tile workgroups with every K slice in
 // flight (the tiles fit in the resident slots, so latency, not throughput, bounds them).
 #ifndef MOE_ROWS_ONEPASS_MAX_IDS
-#define MOE_ROWS_ONEPASS_MAX_IDS 512
+#define MOE_ROWS_ONEPASS_MAX_IDS 1024
 #endif
 
 template <int H>
 static hipError_t fwd_f32(const float* X, const float* W, const float* bias, float* Y, const int32_t* offsets,
                           const int32_t* perm, int64_t T, int NE, hipStream_t s) {
-    constexpr int BN = (H >= 128) ? 128 : H;
-    const int bm = rows_bm<H>(T);
-    const int ids = rows_grid<H>(T, NE, bm);
-    const int grid = persist_wgs(ids, MOE_FWD_PERSIST_WGS, MOE_FWD_PERSIST_WGS);
-    if (bm == 128)
-        hipLaunchKernelGGL((k_fwd_f32<H, 128, BN, MOE_F32_KC_FWD, false>), dim3(grid), dim3(kThreads), 0, s, X, W,
-                           bias, Y, offsets, perm, NE, ids);
-    else if (ids <= MOE_ROWS_ONEPASS_MAX_IDS)
-        hipLaunchKernelGGL((k_fwd_f32<H, MOE_ROWS_SMALL_BM, BN, MOE_F32_KC_FWD, true>), dim3(ids), dim3(kThreads), 0,
-                           s, X, W, bias, Y, offsets, perm, NE, ids);
+    using TL = F32Tiles<H>;
+    if (f32_big_tiles(T, H)) {
+        const int ids = rows_grid<H, TL::BIG_BN>(T, NE, 128);
+        const int grid = persist_wgs(ids, MOE_FWD_PERSIST_WGS, MOE_FWD_PERSIST_WGS);
+        hipLaunchKernelGGL((k_fwd_f32<H, 128, TL::BIG_BN, MOE_F32_KC_FWD, false>), dim3(grid), dim3(kThreads), 0, s,
+                           X, W, bias, Y, offsets, perm, NE, ids);
+        return hipGetLastError();
+    }
+    const int ids = rows_grid<H, TL::SMALL_BN>(T, NE, TL::SMALL_BM);
+    if (ids <= MOE_ROWS_ONEPASS_MAX_IDS)
+        hipLaunchKernelGGL((k_fwd_f32<H, TL::SMALL_BM, TL::SMALL_BN, MOE_F32_KC_FWD, true>), dim3(ids),
+                           dim3(kThreads), 0, s, X, W, bias, Y, offsets, perm, NE, ids);
     else
-        hipLaunchKernelGGL((k_fwd_f32<H, MOE_ROWS_SMALL_BM, BN, MOE_F32_KC_FWD, false>), dim3(grid), dim3(kThreads), 0,
-                           s, X, W, bias, Y, offsets, perm, NE, ids);
+        hipLaunchKernelGGL((k_fwd_f32<H, TL::SMALL_BM, TL::SMALL_BN, MOE_F32_KC_FWD, false>),
+                           dim3(persist_wgs(ids, MOE_FWD_PERSIST_WGS, MOE_FWD_PERSIST_WGS)), dim3(kThreads), 0, s, X,
+                           W, bias, Y, offsets, perm, NE, ids);
     return hipGetLastError();
 }
 
@@ -775,25 +793,31 @@ template <int H, bool MEAN>
 static hipError_t bwd_f32(const float* dY, const float* X, const float* W, float* dX, int accumulate, float* pdw,
                           float* pdb, const int32_t* offsets, const int32_t* perm, int64_t T, int NE, int P,
                           int n_chunk_max, int nh, hipStream_t s) {
-    constexpr int BN = (H >= 128) ? 128 : H;
-    const int bm = rows_bm<H>(T);
-    const int dx_ids = rows_grid<H>(T, NE, bm);
-    const bool one = bm != 128 && dx_ids <= MOE_ROWS_ONEPASS_MAX_IDS;
-    const int n_dx = one ? dx_ids : persist_wgs(dx_ids, MOE_DX_PERSIST_WGS, 2 * MOE_DX_PERSIST_WGS);  // multiple of 8
-    const int grid = n_dx + dw_grid<H>(n_chunk_max);
+    using TL = F32Tiles<H>;
     const float inv_nh = 1.0f / (float)nh;
-    if (bm == 128)
-        hipLaunchKernelGGL((k_bwd_f32<H, 128, BN, MOE_F32_KC_DX, MOE_F32_KC_DW, MEAN, false>), dim3(grid),
-                           dim3(kThreads), 0, s, dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, NE, P, (int)T,
-                           n_dx, dx_ids, nh, inv_nh);
-    else if (one)
-        hipLaunchKernelGGL((k_bwd_f32<H, MOE_ROWS_SMALL_BM, BN, MOE_F32_KC_DX, MOE_F32_KC_DW, MEAN, true>), dim3(grid),
-                           dim3(kThreads), 0, s, dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, NE, P, (int)T,
-                           n_dx, dx_ids, nh, inv_nh);
-    else
-        hipLaunchKernelGGL((k_bwd_f32<H, MOE_ROWS_SMALL_BM, BN, MOE_F32_KC_DX, MOE_F32_KC_DW, MEAN, false>),
+    if (f32_big_tiles(T, H)) {
+        const int dx_ids = rows_grid<H, TL::BIG_BN>(T, NE, 128);
+        const int n_dx = persist_wgs(dx_ids, MOE_DX_PERSIST_WGS, 2 * MOE_DX_PERSIST_WGS);  // a multiple of 8
+        const int grid = n_dx + dw_grid<H, TL::BIG_BT>(n_chunk_max);
+        hipLaunchKernelGGL((k_bwd_f32<H, 128, TL::BIG_BN, TL::BIG_BT, MOE_F32_KC_DX, MOE_F32_KC_DW, MEAN, false>),
                            dim3(grid), dim3(kThreads), 0, s, dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, NE, P,
                            (int)T, n_dx, dx_ids, nh, inv_nh);
+        return hipGetLastError();
+    }
+    const int dx_ids = rows_grid<H, TL::SMALL_BN>(T, NE, TL::SMALL_BM);
+    const bool one = dx_ids <= MOE_ROWS_ONEPASS_MAX_IDS;
+    const int n_dx = one ? dx_ids : persist_wgs(dx_ids, MOE_DX_PERSIST_WGS, 2 * MOE_DX_PERSIST_WGS);
+    const int grid = n_dx + dw_grid<H, TL::SMALL_BT>(n_chunk_max);
+    if (one)
+        hipLaunchKernelGGL(
+            (k_bwd_f32<H, TL::SMALL_BM, TL::SMALL_BN, TL::SMALL_BT, MOE_F32_KC_DX, MOE_F32_KC_DW, MEAN, true>),
+            dim3(grid), dim3(kThreads), 0, s, dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, NE, P, (int)T, n_dx,
+            dx_ids, nh, inv_nh);
+    else
+        hipLaunchKernelGGL(
+            (k_bwd_f32<H, TL::SMALL_BM, TL::SMALL_BN, TL::SMALL_BT, MOE_F32_KC_DX, MOE_F32_KC_DW, MEAN, false>),
+            dim3(grid), dim3(kThreads), 0, s, dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, NE, P, (int)T, n_dx,
+            dx_ids, nh, inv_nh);
     return hipGetLastError();
 }
 

@@ -37,8 +37,8 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 #ifndef MOE_DW_MIN_CHUNK
 #define MOE_DW_MIN_CHUNK 128
 #endif
-static int plan_chunks(int64_t T, int H) {
-    const int bt = (H >= 128) ? 128 : 64;
+static int plan_chunks(int64_t T, int H, int act) {
+    const int bt = (act == MOE_DTYPE_F32) ? f32_dw_tile(T, H) : ((H >= 128) ? 128 : 64);
     const int tiles_per_chunk = (H / bt) * (H / bt);
     const int64_t pmax = (MOE_DW_WORKGROUPS + tiles_per_chunk - 1) / tiles_per_chunk;
     int64_t p = T / MOE_DW_MIN_CHUNK;
@@ -56,7 +56,7 @@ Plan make_plan(int64_t T, int H, int NE, int act) {
     p.n_rblk = (int)((T + kRouteTokens - 1) / kRouteTokens);
     p.n_ablk = (int)((T + kAuxTokens - 1) / kAuxTokens);
     if (H > 0) {
-        p.chunks = plan_chunks(T, H);
+        p.chunks = plan_chunks(T, H, act);
         p.n_chunk_max = p.chunks + NE;
     }
     size_t o = 0;

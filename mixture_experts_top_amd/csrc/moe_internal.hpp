@@ -30,6 +30,26 @@ enum KernelId {
     K_LAMBDA, K_REDUCE_AXIS0, K_COLLAPSE, K_SOFTMAX_CE, K_COUNT
 };
 
+// fp32 GEMM tiling, shared by the kernels' launchers and the workspace plan.  Large T:
+// 128-row tiles and 128 x 128 d_W tiles (64 for H = 64).  Small T (too few 128-row tiles
+// for MOE_ROWS_BIG_TILES_PER_CU per CU): smaller tiles, so that more workgroups hide the
+// memory latency that then bounds each one.
+#ifndef MOE_ROWS_BIG_TILES_PER_CU
+#define MOE_ROWS_BIG_TILES_PER_CU 2
+#endif
+#ifndef MOE_DW_SMALL_BT
+#define MOE_DW_SMALL_BT 64
+#endif
+inline bool f32_big_tiles(int64_t T, int H) {
+    const int64_t nt = H >= 128 ? H / 128 : 1;
+    return (T / 128) * nt >= MOE_ROWS_BIG_TILES_PER_CU * 256;
+}
+inline int f32_dw_tile(int64_t T, int H) {
+    const int big = H >= 128 ? 128 : 64;
+    const int small = MOE_DW_SMALL_BT < H ? MOE_DW_SMALL_BT : H;
+    return f32_big_tiles(T, H) ? big : small;
+}
+
 // Chunking of each expert's tokens for the d_W split-K.  With P chunks planned for T
 // tokens, expert e (c_e tokens) gets n_e = ceil(c_e P / T) chunks (none if c_e = 0), and
 // chunk j covers its tokens [floor(j c_e / n_e), floor((j+1) c_e / n_e)).  So chunks are
