@@ -241,6 +241,8 @@ def main():
     ap.add_argument("--skip-kernel-survey", action="store_true",
                     help="do not time every kernel first; time --kernel in the timed region")
     ap.add_argument("--kernel", default=None, help="kernel timed live in the timed region (default: the slowest)")
+    ap.add_argument("--timer-every", type=int, default=5,
+                    help="time the dominant kernel with HIP events in every n-th step of the timed region")
     ap.add_argument("--row", default="gate",
                     help="gate (default) | reduce_axis0 | collapse_fwd | collapse_bwd | softmax_ce")
     args = ap.parse_args()
@@ -334,10 +336,13 @@ def main():
             graph.replay()
         torch.cuda.synchronize()
 
-    # timed region: K steps, the dominant kernel bracketed by events in every step
+    # timed region: K steps; the dominant kernel is bracketed by a pair of events in every
+    # `--timer-every`-th step (each pair adds its own GPU commands to the step it sits in)
     K = args.steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    for a, b in evs:
+    every = max(1, args.timer_every)
+    timed = [i for i in range(K) if i % every == 0]
+    evs = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for i in timed}
+    for a, b in evs.values():
         a.record(); b.record()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -345,14 +350,17 @@ def main():
         if graph is not None:
             graph.replay()
         else:
-            moe.moe_set_launch_timer(dom, *evs[i])
+            if i in evs:
+                moe.moe_set_launch_timer(dom, *evs[i])
+            elif i - 1 in evs:
+                moe.moe_set_launch_timer(None)
             step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     moe.moe_set_launch_timer(None)
     ms = (t1 - t0) / K * 1e3
     if graph is None:
-        dom_us = float(np.mean([a.elapsed_time(b) for a, b in evs]) * 1e3)
+        dom_us = float(np.mean([a.elapsed_time(b) for a, b in evs.values()]) * 1e3)
     else:
         dom_us = kern_us.get(dom, float("nan"))
     amount, unit, bound = algorithmic(dom, wl)
@@ -401,6 +409,7 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": bound, "kernel": dom, "achieved": achieved, "peak": peak, "unit": runit,
                      "frac": achieved / peak, "traffic": measured_traffic(dom, wl), "avg_launch_us": dom_us,
+                     "timed_launches": len(evs) if graph is None else 0,
                      "per_launch": f"{amount:.4g} {unit}"},
         "step_roofline_frac": step_roof_frac,
         "pass_us": pass_us,

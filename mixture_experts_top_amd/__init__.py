@@ -112,10 +112,21 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr()
 
 
+_raw_stream = None
+
+
 def _stream(stream) -> Optional[int]:
+    """The given stream's handle, else the current stream of the current device.  The raw
+    lookup avoids building a Stream object on every call (a few microseconds each)."""
+    global _raw_stream
+    if stream is not None:
+        return stream.cuda_stream
     import torch
-    s = torch.cuda.current_stream() if stream is None else stream
-    return s.cuda_stream
+    if _raw_stream is None:
+        get = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        _raw_stream = (lambda: get(torch.cuda.current_device())) if get is not None else \
+            (lambda: torch.cuda.current_stream().cuda_stream)
+    return _raw_stream()
 
 
 def _act(t) -> int:
@@ -128,24 +139,27 @@ def _act(t) -> int:
 
 
 def _workspace(ws, B, NH, H, NE, act, device):
-    import torch
-    need = moe_workspace_bytes(B, NH, H, NE, act)
+    """A caller's workspace is passed with its size (the library rejects one too small);
+    without one, a workspace of the required size is allocated for this call."""
     if ws is None:
+        import torch
+        need = moe_workspace_bytes(B, NH, H, NE, act)
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
     return ws, ws.numel() * ws.element_size()
 
 
 def _shape3(t, name):
-    if t.dim() != 3:
-        raise ValueError(f"{name} must be [B, N_H, *], got {tuple(t.shape)}")
-    return tuple(int(x) for x in t.shape)
+    sh = t.shape
+    if len(sh) != 3:
+        raise ValueError(f"{name} must be [B, N_H, *], got {tuple(sh)}")
+    return sh[0], sh[1], sh[2]
 
 
 def _expect(t, name, shape, dtype):
     """Host-side check that a buffer has exactly the shape and dtype the kernels assume."""
     if t is None:
         return
-    if tuple(t.shape) != tuple(shape):
+    if t.shape != shape:
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")

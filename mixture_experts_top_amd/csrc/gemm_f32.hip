@@ -730,12 +730,22 @@ static inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
 #ifndef MOE_ROWS_SMALL_BN
 #define MOE_ROWS_SMALL_BN 128
 #endif
+// The forward's small-T tile may differ from dX's: the forward runs alone, while dX shares
+// the resident slots with the dW workgroups.
+#ifndef MOE_FWD_SMALL_BM
+#define MOE_FWD_SMALL_BM MOE_ROWS_SMALL_BM
+#endif
+#ifndef MOE_FWD_SMALL_BN
+#define MOE_FWD_SMALL_BN 64
+#endif
 template <int H>
 struct F32Tiles {
     static constexpr int BIG_BN = (H >= 128) ? 128 : H;
     static constexpr int BIG_BT = (H >= 128) ? 128 : 64;
     static constexpr int SMALL_BN = (MOE_ROWS_SMALL_BN < H) ? MOE_ROWS_SMALL_BN : H;
     static constexpr int SMALL_BM = (SMALL_BN == 128 || MOE_ROWS_SMALL_BM >= 64) ? MOE_ROWS_SMALL_BM : 64;
+    static constexpr int FWD_BN = (MOE_FWD_SMALL_BN < H) ? MOE_FWD_SMALL_BN : H;
+    static constexpr int FWD_BM = (FWD_BN == 128 || MOE_FWD_SMALL_BM >= 64) ? MOE_FWD_SMALL_BM : 64;
     static constexpr int SMALL_BT = (MOE_DW_SMALL_BT < H) ? MOE_DW_SMALL_BT : H;
 };
 
@@ -778,12 +788,12 @@ static hipError_t fwd_f32(const float* X, const float* W, const float* bias, flo
                            X, W, bias, Y, offsets, perm, NE, ids);
         return hipGetLastError();
     }
-    const int ids = rows_grid<H, TL::SMALL_BN>(T, NE, TL::SMALL_BM);
+    const int ids = rows_grid<H, TL::FWD_BN>(T, NE, TL::FWD_BM);
     if (ids <= MOE_ROWS_ONEPASS_MAX_IDS)
-        hipLaunchKernelGGL((k_fwd_f32<H, TL::SMALL_BM, TL::SMALL_BN, MOE_F32_KC_FWD, true>), dim3(ids),
+        hipLaunchKernelGGL((k_fwd_f32<H, TL::FWD_BM, TL::FWD_BN, MOE_F32_KC_FWD, true>), dim3(ids),
                            dim3(kThreads), 0, s, X, W, bias, Y, offsets, perm, NE, ids);
     else
-        hipLaunchKernelGGL((k_fwd_f32<H, TL::SMALL_BM, TL::SMALL_BN, MOE_F32_KC_FWD, false>),
+        hipLaunchKernelGGL((k_fwd_f32<H, TL::FWD_BM, TL::FWD_BN, MOE_F32_KC_FWD, false>),
                            dim3(persist_wgs(ids, MOE_FWD_PERSIST_WGS, MOE_FWD_PERSIST_WGS)), dim3(kThreads), 0, s, X,
                            W, bias, Y, offsets, perm, NE, ids);
     return hipGetLastError();
