@@ -25,34 +25,35 @@ __global__ __launch_bounds__(kAuxThreads) void k_aux_rows(const float* __restric
                                                           float* __restrict__ part) {
     __shared__ float red[kAuxThreads / 64][NEB];
     const int tid = threadIdx.x;
+    static_assert(kAuxTokens == kAuxThreads, "one token per thread");
+    const int64_t t = (int64_t)blockIdx.x * kAuxTokens + tid;
+    const bool vec = (NE % 4) == 0;
+    // this token's logits first, then the counts: every load is unconditional (entries past
+    // N_E read entry 0 and are never used), so they all go out before the first wait
+    float g[NEB];
+    const float* row = G + (t < T ? t : 0) * NE;
+    if (vec) {  // entries past N_E re-read the row's first ones; every use is guarded by e < N_E
+#pragma unroll
+        for (int q = 0; q < NEB / 4; ++q) {
+            const f32x4 v = reinterpret_cast<const f32x4*>(row)[4 * q < NE ? q : 0];
+            g[4 * q] = v.x; g[4 * q + 1] = v.y; g[4 * q + 2] = v.z; g[4 * q + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < NEB; ++e) g[e] = row[e < NE ? e : 0];
+    }
+    int cnt[NEB];
+#pragma unroll
+    for (int e = 0; e < NEB; ++e) cnt[e] = counts[e < NE ? e : 0];
     const float lam = lam_dev ? lam_dev[0] : lam_value;
     float frac[NEB], psum[NEB];
 #pragma unroll
-    for (int e = 0; e < NEB; ++e) {
-        frac[e] = (e < NE) ? (float)((double)counts[e] / (double)T) : 0.0f;
+    for (int e = 0; e < NEB; ++e) {  // unguarded so the loads stay unconditional: p[e] = 0 past N_E
+        frac[e] = (float)((double)cnt[e] / (double)T);
         psum[e] = 0.0f;
     }
     const float coef = (float)((double)lam * (double)NE / (double)T);
-    const bool vec = (NE % 4) == 0;
-    for (int j = 0; j < kAuxTokens / kAuxThreads; ++j) {
-        const int64_t t = (int64_t)blockIdx.x * kAuxTokens + j * kAuxThreads + tid;
-        if (t >= T) break;
-        const float* row = G + t * NE;
-        float g[NEB];
-        if (vec) {
-#pragma unroll
-            for (int q = 0; q < NEB / 4; ++q) {
-                if (4 * q < NE) {
-                    f32x4 v = reinterpret_cast<const f32x4*>(row)[q];
-                    g[4 * q] = v.x; g[4 * q + 1] = v.y; g[4 * q + 2] = v.z; g[4 * q + 3] = v.w;
-                } else {
-                    g[4 * q] = g[4 * q + 1] = g[4 * q + 2] = g[4 * q + 3] = 0.0f;
-                }
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < NEB; ++e) g[e] = (e < NE) ? row[e] : 0.0f;
-        }
+    if (t < T) {
         float m = g[0];
 #pragma unroll
         for (int e = 1; e < NEB; ++e)

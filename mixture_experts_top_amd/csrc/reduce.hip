@@ -57,9 +57,11 @@ __global__ __launch_bounds__(256) void k_reduce_dw(const float* __restrict__ pdw
     constexpr int RX = 256 / RY;
     __shared__ f32x4 red[256];
     const int e = blockIdx.y;
-    int cs = 0;
-    for (int i = 0; i < e; ++i) cs += expert_nchunks(offsets[i + 1] - offsets[i], P, T);
-    const int n = expert_nchunks(offsets[e + 1] - offsets[e], P, T);
+    // chunk range of expert e: one load per lane and a wavefront prefix sum over the experts
+    const int lane = threadIdx.x % 64;
+    const int nl = (lane < NE) ? expert_nchunks(offsets[lane + 1] - offsets[lane], P, T) : 0;
+    const int incl = wave_inclusive_sum(nl);
+    const int cs = __shfl(incl - nl, e), n = __shfl(nl, e);
     const size_t HH = (size_t)H * H;
     const int nbx = (int)(HH / (4 * RX));
     if ((int)blockIdx.x < nbx) {
@@ -69,9 +71,14 @@ __global__ __launch_bounds__(256) void k_reduce_dw(const float* __restrict__ pdw
     }
 }
 
+// Rows of threads per column tile: 16 (narrow tiles, more loads in flight per column) once
+// the plan has at least this many chunks, else 4.
+#ifndef MOE_REDUCE_RY16_MIN_P
+#define MOE_REDUCE_RY16_MIN_P 1024
+#endif
 hipError_t launch_reduce_dw(const float* part_dw, const float* part_db, const int32_t* offsets, int64_t T, int H,
                             int NE, int P, float* dW, float* db, hipStream_t s) {
-    if (P >= 1024) {
+    if (P >= MOE_REDUCE_RY16_MIN_P) {
         const int nbx = H * H / (4 * 16);
         hipLaunchKernelGGL(k_reduce_dw<16>, dim3(nbx + 1, NE), dim3(256), 0, s, part_dw, part_db, offsets, H, NE, P,
                            (int)T, dW, db);

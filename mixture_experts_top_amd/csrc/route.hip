@@ -203,18 +203,24 @@ __global__ __launch_bounds__(kRouteThreads) void k_scatter_scan(const int* __res
     __shared__ int bb[kMaxExperts];
     const int tid = threadIdx.x;
     const int b = blockIdx.x;
+    // this thread's token's expert: its load goes out first, with the histogram loads behind it
+    const int wave = tid / 64, lane = tid % 64;
+    const int64_t t = (int64_t)b * kRouteTokens + wave * 64 + lane;
+    const int e = (t < T) ? idx[t] : -1;
     int nep = 1;
     while (nep < NE) nep <<= 1;
     const int S = kRouteThreads / nep;
     {
-        const int e = tid % nep, sg = tid / nep;
+        const int ec = tid % nep, sg = tid / nep;
         int all = 0, before = 0;
-        if (e < NE)
+        if (ec < NE) {
+#pragma unroll 4
             for (int x = sg; x < nblk; x += S) {
-                const int v = hist[(int64_t)x * NE + e];
+                const int v = hist[(int64_t)x * NE + ec];
                 all += v;
                 before += (x < b) ? v : 0;
             }
+        }
         part[0][tid] = all;
         part[1][tid] = before;
     }
@@ -242,9 +248,6 @@ __global__ __launch_bounds__(kRouteThreads) void k_scatter_scan(const int* __res
         if (b == 0) offsets[NE] = acc;
     }
     __syncthreads();
-    const int wave = tid / 64, lane = tid % 64;
-    const int64_t t = (int64_t)b * kRouteTokens + wave * 64 + lane;
-    const int e = (t < T) ? idx[t] : -1;
     const int r = wave_rank(e, cnt[wave]);
     __syncthreads();
     if (tid < NE) {
