@@ -128,6 +128,12 @@ __device__ __forceinline__ void rows_bf16_body(char* smem, int bid, const uint16
     for (int i = 0; i < SM; ++i)
 #pragma unroll
         for (int j = 0; j < SN; ++j) acc[i][j] = f32x16{};
+    // the bias is loaded before the K loop: a load still pending in the epilogue's conditional
+    // stores would be waited for in each of them, and that wait also waits for every store
+    // issued before it
+    float bv[SN];
+#pragma unroll
+    for (int j = 0; j < SN; ++j) bv[j] = DX ? 0.0f : bias[(size_t)e * H + n0 + wn * WTN + j * 32 + l32];
 
     load_slice(0);
     store_slice(0);
@@ -155,18 +161,31 @@ __device__ __forceinline__ void rows_bf16_body(char* smem, int bid, const uint16
 #pragma unroll
     for (int j = 0; j < SN; ++j) {
         const int col = n0 + wn * WTN + j * 32 + l32;
-        const float bv = DX ? 0.0f : bias[(size_t)e * H + col];
 #pragma unroll
         for (int i = 0; i < SM; ++i) {
+            const int* tr = &tok[wm * WTM + i * 32 + 4 * h];
+            if (DX && accumulate) {
+                // four rows' current values are loaded before their stores (a padded row reads
+                // row 0 and drops it), so the block waits for memory four times, not sixteen
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = wm * WTM + i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
-                const int t = tok[row];
-                if (t >= 0) {
-                    uint16_t* o = Out + (size_t)t * H + col;
-                    float v = acc[i][j][r] + bv;
-                    if (DX && accumulate) v = bf16_to_f32(*o) + v;
-                    *o = f32_to_bf16(v);
+                for (int q = 0; q < 4; ++q) {
+                    int tk[4];
+                    uint16_t old[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        tk[u] = tr[8 * q + u];
+                        old[u] = Out[(size_t)(tk[u] < 0 ? 0 : tk[u]) * H + col];
+                    }
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (tk[u] >= 0)
+                            Out[(size_t)tk[u] * H + col] = f32_to_bf16(bf16_to_f32(old[u]) + acc[i][j][4 * q + u]);
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int t = tr[8 * (r / 4) + (r % 4)];
+                    if (t >= 0) Out[(size_t)t * H + col] = f32_to_bf16(acc[i][j][r] + bv[j]);
                 }
             }
         }

@@ -28,20 +28,25 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Number of d_W chunks P for T tokens (see expert_nchunks): about eight workgroups per compute
 // unit once the output tiles of a chunk are counted (several rounds, so the last partial
-// round is short), and chunks of at least 128 tokens.  The
-// chunk partials then stay within P x (H^2 + H) floats whatever the routing skew.  Depends
-// only on (T, H), so results are reproducible for a shape.
+// round is short), and chunks of at least MOE_DW_MIN_CHUNK tokens (MOE_DW_MIN_CHUNK_BIG in
+// the fp32 large-T tiling, where fewer, longer chunks shrink the partials more than they cost
+// the dW workgroups).  The chunk partials then stay within P x (H^2 + H) floats whatever the
+// routing skew.  Depends only on (T, H, act), so results are reproducible for a shape.
 #ifndef MOE_DW_WORKGROUPS
 #define MOE_DW_WORKGROUPS 2048
 #endif
 #ifndef MOE_DW_MIN_CHUNK
 #define MOE_DW_MIN_CHUNK 128
 #endif
+#ifndef MOE_DW_MIN_CHUNK_BIG
+#define MOE_DW_MIN_CHUNK_BIG 192
+#endif
 static int plan_chunks(int64_t T, int H, int act) {
-    const int bt = (act == MOE_DTYPE_F32) ? f32_dw_tile(T, H) : ((H >= 128) ? 128 : 64);
+    const bool f32 = act == MOE_DTYPE_F32;
+    const int bt = f32 ? f32_dw_tile(T, H) : ((H >= 128) ? 128 : 64);
     const int tiles_per_chunk = (H / bt) * (H / bt);
     const int64_t pmax = (MOE_DW_WORKGROUPS + tiles_per_chunk - 1) / tiles_per_chunk;
-    int64_t p = T / MOE_DW_MIN_CHUNK;
+    int64_t p = T / ((f32 && f32_big_tiles(T, H)) ? MOE_DW_MIN_CHUNK_BIG : MOE_DW_MIN_CHUNK);
     if (p > pmax) p = pmax;
     if (p < 1) p = 1;
     return (int)p;
