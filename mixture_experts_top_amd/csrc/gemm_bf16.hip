@@ -68,6 +68,12 @@ struct RowsBf16Smem {
     static constexpr size_t bytes = a + b + tok;
 };
 
+// K slices of both operands in flight per thread (a ring of registers), fed to two LDS
+// buffers: with a 64-wide slice worth ~0.2 us of MFMAs per wave, one slice of prefetch left
+// each tile waiting on one memory round trip per slice.
+#ifndef MOE_BF16_RING_U8
+#define MOE_BF16_RING_U8 16  // 16-byte registers per thread for the slice ring
+#endif
 template <int H, int BN, bool DX>
 __device__ __forceinline__ void rows_bf16_body(char* smem, int bid, const uint16_t* __restrict__ A,
                                                const uint16_t* __restrict__ Bw,
@@ -82,7 +88,8 @@ __device__ __forceinline__ void rows_bf16_body(char* smem, int bid, const uint16
     constexpr int TPR = KC / 8, RPP = kThreads / TPR;   // threads per 128-byte row slice, rows per pass
     constexpr int AL = BM / RPP, BL = BN / RPP;
     static_assert(H % KC == 0 && BM % RPP == 0 && BN % RPP == 0, "tile shape");
-    // two LDS buffers: the global loads of K-slice c+1 are issued before the MFMAs of slice c
+    constexpr int PF0 = MOE_BF16_RING_U8 / (AL + BL);
+    constexpr int PF = PF0 < 1 ? 1 : (PF0 > NKC ? NKC : PF0);
     using SM_ = RowsBf16Smem<H, BN>;
     uint16_t(&As)[2][BM][KP] = *reinterpret_cast<uint16_t(*)[2][BM][KP]>(smem);
     uint16_t(&Bs)[2][BN][KP] = *reinterpret_cast<uint16_t(*)[2][BN][KP]>(smem + SM_::a);
@@ -94,54 +101,82 @@ __device__ __forceinline__ void rows_bf16_body(char* smem, int bid, const uint16
     if (!find_tile(offsets, NE, mt, BM, e, r0, r1)) return;
     const int rows = r1 - r0;
     const int tid = threadIdx.x;
-    if (tid < BM) tok[tid] = (tid < rows) ? perm[r0 + tid] : -1;
-    __syncthreads();
-
     const int n0 = nt * BN;
     const uint16_t* __restrict__ Be = Bw + (size_t)e * H * H;
     const int wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
     const int wm = wave / 2, wn = wave % 2;
 
-    const uint16_t* a_src[AL];
+    // token ids: of this thread's A rows (registers) and of the tile's rows (LDS, epilogue)
+    int ta[AL];
 #pragma unroll
     for (int i = 0; i < AL; ++i) {
-        const int t = tok[tid / TPR + RPP * i];
-        a_src[i] = (t >= 0) ? A + (size_t)t * H + 8 * (tid % TPR) : nullptr;
+        const int row = tid / TPR + RPP * i;
+        ta[i] = (row < rows) ? perm[r0 + row] : -1;
     }
-    u16x8 ra[AL], rb[BL];
-    auto load_slice = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < AL; ++i) ra[i] = a_src[i] ? ld8(a_src[i] + k0) : u16x8{};
+    const int tok_mine = (tid < BM && tid < rows) ? perm[r0 + tid] : -1;
+    // the bias is loaded before the K loop: a load still pending in the epilogue's conditional
+    // stores would be waited for in each of them, and that wait also waits for every store
+    // issued before it
+    float bv[SN];
+
+    u16x8 ra[PF][AL], rb[PF][BL];
+    auto load_b = [&](int c, int slot) {
 #pragma unroll
         for (int i = 0; i < BL; ++i)
-            rb[i] = ld8(Be + (size_t)(n0 + tid / TPR + RPP * i) * H + k0 + 8 * (tid % TPR));
+            rb[slot][i] = ld8(Be + (size_t)(n0 + tid / TPR + RPP * i) * H + c * KC + 8 * (tid % TPR));
     };
-    auto store_slice = [&](int buf) {
+    const uint16_t* a_src[AL];
+    auto load_a = [&](int c, int slot) {
 #pragma unroll
-        for (int i = 0; i < AL; ++i) st8(&As[buf][tid / TPR + RPP * i][8 * (tid % TPR)], ra[i]);
-#pragma unroll
-        for (int i = 0; i < BL; ++i) st8(&Bs[buf][tid / TPR + RPP * i][8 * (tid % TPR)], rb[i]);
+        for (int i = 0; i < AL; ++i) ra[slot][i] = ld8(a_src[i] + c * KC);
     };
+    auto store_slice = [&](int slot, int buf) {
+#pragma unroll
+        for (int i = 0; i < AL; ++i) st8(&As[buf][tid / TPR + RPP * i][8 * (tid % TPR)], ra[slot][i]);
+#pragma unroll
+        for (int i = 0; i < BL; ++i) st8(&Bs[buf][tid / TPR + RPP * i][8 * (tid % TPR)], rb[slot][i]);
+    };
+
+    // W does not depend on perm: its loads go out while the token ids are in flight (loads
+    // return in issue order).  A padded row reads token 0's row: output rows are independent
+    // and padded ones are never stored.  The fences keep loads from sinking to their uses.
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < SN; ++j) bv[j] = DX ? 0.0f : bias[(size_t)e * H + n0 + wn * WTN + j * 32 + l32];
+#pragma unroll
+    for (int c = 0; c < PF; ++c) load_b(c, c);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < AL; ++i) a_src[i] = A + (size_t)(ta[i] < 0 ? 0 : ta[i]) * H + 8 * (tid % TPR);
+#pragma unroll
+    for (int c = 0; c < PF; ++c) load_a(c, c);
+    __builtin_amdgcn_sched_barrier(0);
+    if (tid < BM) tok[tid] = tok_mine;  // read in the epilogue, after the barriers
 
     f32x16 acc[SM][SN];
 #pragma unroll
     for (int i = 0; i < SM; ++i)
 #pragma unroll
         for (int j = 0; j < SN; ++j) acc[i][j] = f32x16{};
-    // the bias is loaded before the K loop: a load still pending in the epilogue's conditional
-    // stores would be waited for in each of them, and that wait also waits for every store
-    // issued before it
-    float bv[SN];
-#pragma unroll
-    for (int j = 0; j < SN; ++j) bv[j] = DX ? 0.0f : bias[(size_t)e * H + n0 + wn * WTN + j * 32 + l32];
 
-    load_slice(0);
-    store_slice(0);
+    store_slice(0, 0);
+    if (PF < NKC) {
+        load_b(PF, 0);
+        load_a(PF, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
     __syncthreads();
-#pragma unroll 1
+#pragma unroll
     for (int c = 0; c < NKC; ++c) {
         const int buf = c & 1;
-        if (c + 1 < NKC) load_slice((c + 1) * KC);
+        if (c + 1 < NKC) {
+            store_slice((c + 1) % PF, (c + 1) & 1);
+            if (c + 1 + PF < NKC) {
+                load_b(c + 1 + PF, (c + 1) % PF);
+                load_a(c + 1 + PF, (c + 1) % PF);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
 #pragma unroll
         for (int kk = 0; kk < KC; kk += 16) {
             u16x8 a[SM], b[SN];
@@ -154,8 +189,7 @@ __device__ __forceinline__ void rows_bf16_body(char* smem, int bid, const uint16
 #pragma unroll
                 for (int j = 0; j < SN; ++j) acc[i][j] = mfma_bf16(a[i], b[j], acc[i][j]);
         }
-        if (c + 1 < NKC) store_slice(buf ^ 1);
-        __syncthreads();
+        if (c + 1 < NKC) __syncthreads();
     }
 
 #pragma unroll
@@ -193,6 +227,13 @@ __device__ __forceinline__ void rows_bf16_body(char* smem, int bid, const uint16
 }
 
 // d_W / d_b partials for one chunk of one expert's tokens, output tile [o0:o0+BT, i0:i0+BT].
+//
+// The LDS tiles are [feature][token]; a thread's register transpose writes 4 tokens of 8
+// features (rows 8 apart), which with a plain layout puts a wave's 8-byte stores on a few
+// banks.  The 16-byte token chunks of row r are therefore XOR-swizzled by (r >> 4) & 7: the
+// stores of a wave then cover all 64 banks, and the MFMA fragment reads (16 consecutive rows
+// with one swizzle) stay conflict-free.
+__device__ __forceinline__ int swz(int row, int k) { return (((k >> 3) ^ ((row >> 4) & 7)) << 3) | (k & 7); }
 template <int H>
 struct DwBf16Smem {
     static constexpr int BT = (H >= 128) ? 128 : 64, KC = 64, KP = KC + 8;
@@ -279,8 +320,9 @@ __device__ __forceinline__ void dw_bf16_body(char* smem, int bid, const uint16_t
                     wa.y = (uint32_t)va[it][2][f] | ((uint32_t)va[it][3][f] << 16);
                     wb.x = (uint32_t)vb[it][0][f] | ((uint32_t)vb[it][1][f] << 16);
                     wb.y = (uint32_t)vb[it][2][f] | ((uint32_t)vb[it][3][f] << 16);
-                    *reinterpret_cast<uint2*>(&As[buf][8 * fq + f][4 * tq]) = wa;
-                    *reinterpret_cast<uint2*>(&Bs[buf][8 * fq + f][4 * tq]) = wb;
+                    const int row = 8 * fq + f, k = swz(row, 4 * tq);
+                    *reinterpret_cast<uint2*>(&As[buf][row][k]) = wa;
+                    *reinterpret_cast<uint2*>(&Bs[buf][row][k]) = wb;
                 }
             }
         }
@@ -302,9 +344,15 @@ __device__ __forceinline__ void dw_bf16_body(char* smem, int bid, const uint16_t
         for (int kk = 0; kk < KC; kk += 16) {
             u16x8 a[SUB], b[SUB];
 #pragma unroll
-            for (int i = 0; i < SUB; ++i) a[i] = ld8(&As[buf][wm * WT + i * 32 + l32][kk + 8 * h]);
+            for (int i = 0; i < SUB; ++i) {
+                const int row = wm * WT + i * 32 + l32;
+                a[i] = ld8(&As[buf][row][swz(row, kk + 8 * h)]);
+            }
 #pragma unroll
-            for (int j = 0; j < SUB; ++j) b[j] = ld8(&Bs[buf][wn * WT + j * 32 + l32][kk + 8 * h]);
+            for (int j = 0; j < SUB; ++j) {
+                const int row = wn * WT + j * 32 + l32;
+                b[j] = ld8(&Bs[buf][row][swz(row, kk + 8 * h)]);
+            }
 #pragma unroll
             for (int i = 0; i < SUB; ++i)
 #pragma unroll
@@ -313,7 +361,7 @@ __device__ __forceinline__ void dw_bf16_body(char* smem, int bid, const uint16_t
         if (do_db && tid < BT) {
 #pragma unroll
             for (int q = 0; q < KC / 8; ++q) {
-                const u16x8 v = ld8(&As[buf][tid][8 * q]);
+                const u16x8 v = ld8(&As[buf][tid][swz(tid, 8 * q)]);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) dbacc += bf16_to_f32(v[j]);
             }
