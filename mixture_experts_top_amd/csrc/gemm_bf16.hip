@@ -61,9 +61,12 @@ __global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restri
 }
 
 // Out[t, n0:n0+BN] = A[t, :] . Bw[e][n0:n0+BN, :]^T (+ bias[e] | + Out[t] when accumulating).
+#ifndef MOE_BF16_KC
+#define MOE_BF16_KC 64  // K slice of the bf16 row GEMM (a multiple of 16)
+#endif
 template <int H, int BN>
 struct RowsBf16Smem {
-    static constexpr int BM = 128, KC = 64, KP = KC + 8;
+    static constexpr int BM = 128, KC = (MOE_BF16_KC < H) ? MOE_BF16_KC : H, KP = KC + 8;
     static constexpr size_t a = sizeof(uint16_t) * 2 * BM * KP, b = sizeof(uint16_t) * 2 * BN * KP, tok = 4 * BM;
     static constexpr size_t bytes = a + b + tok;
 };
@@ -81,7 +84,7 @@ __device__ __forceinline__ void rows_bf16_body(char* smem, int bid, const uint16
                                                uint16_t* __restrict__ Out,
                                                const int* __restrict__ offsets,
                                                const int* __restrict__ perm, int NE, int accumulate) {
-    constexpr int BM = 128, KC = 64, KP = KC + 8, NKC = H / KC;
+    constexpr int BM = 128, KC = RowsBf16Smem<H, BN>::KC, KP = KC + 8, NKC = H / KC;
     constexpr int NT = H / BN;
     constexpr int WTM = BM / 2, WTN = BN / 2;
     constexpr int SM = WTM / 32, SN = WTN / 32;

@@ -694,7 +694,7 @@ __global__ __launch_bounds__(kThreads) MOE_FWD_ATTR void k_fwd_f32(const float* 
                                             NE, 0);
 }
 
-template <int H, int BM, int BN, int BT, int KCX, int KCW, bool MEAN, bool ONE>
+template <int H, int BM, int BN, int BT, int KCX, int KCW, bool MEAN, bool ONE, bool DWF = false>
 __global__ __launch_bounds__(kThreads) void k_bwd_f32(const float* __restrict__ dY, const float* __restrict__ X,
                                                        const float* __restrict__ W, float* __restrict__ dX,
                                                        int accumulate, float* __restrict__ part_dw,
@@ -704,6 +704,16 @@ __global__ __launch_bounds__(kThreads) void k_bwd_f32(const float* __restrict__ 
                                                        int n_dx, int dx_tile_ids, int nh, float inv_nh) {
     constexpr size_t r = RowsF32Smem<BM, BN, KCX, true>::bytes, d = DwF32Smem<BT, KCW>::bytes;
     __shared__ __attribute__((aligned(16))) char smem[r > d ? r : d];  // one LDS region, either role
+    if (DWF) {  // dW workgroups first (the long ones), then n_dx workgroups of a few dX tiles each
+        const int n_dw = (int)gridDim.x - n_dx;
+        if ((int)blockIdx.x < n_dw)
+            dw_f32_body<H, BT, KCW, MEAN>(smem, blockIdx.x, dY, X, part_dw, part_db, offsets, perm, NE, P, T, nh,
+                                          inv_nh);
+        else
+            rows_f32_body<H, BM, BN, KCX, true, MEAN>(smem, blockIdx.x - n_dw, n_dx, dx_tile_ids, dY, W, nullptr, dX,
+                                                      offsets, perm, NE, accumulate, nh, inv_nh);
+        return;
+    }
     if ((int)blockIdx.x < n_dx) {
         if (ONE)
             rows_f32_onepass_body<H, BM, BN, KCX, true, MEAN>(smem, blockIdx.x, dY, W, nullptr, dX, offsets, perm, NE,
@@ -762,13 +772,16 @@ static int dw_grid(int n_chunk_max) {
 
 // Row-GEMM workgroups once the tile ids reach `from` (0: one workgroup per tile).  Both
 // counts are multiples of 8, so every tile id a workgroup takes maps to the XCD of its
-// first one.  Forward: two per CU, its occupancy.  dX (fused backward): one per CU, the
-// dW workgroups fill the rest; below two tiles per workgroup it keeps one per tile.
+// first one.  Forward: two per CU, its occupancy.  dX in the small-T backward when its tiles
+// exceed the one-pass limit: one per CU, the dW workgroups fill the rest.
 #ifndef MOE_FWD_PERSIST_WGS
 #define MOE_FWD_PERSIST_WGS 512
 #endif
 #ifndef MOE_DX_PERSIST_WGS
 #define MOE_DX_PERSIST_WGS 256
+#endif
+#ifndef MOE_DX_TILES_PER_WG
+#define MOE_DX_TILES_PER_WG 1  // dX tiles per workgroup in the large-T backward
 #endif
 static int persist_wgs(int ids, int wgs, int from) { return (wgs <= 0 || ids < from) ? ids : wgs; }
 // Up to this many small-row tiles, a grid of one-tile workgroups with every K slice in
@@ -806,12 +819,16 @@ static hipError_t bwd_f32(const float* dY, const float* X, const float* W, float
     using TL = F32Tiles<H>;
     const float inv_nh = 1.0f / (float)nh;
     if (f32_big_tiles(T, H)) {
+        // Longest first: the dW workgroups (a whole chunk each) lead the grid and the dX tiles
+        // follow, MOE_DX_TILES_PER_WG per workgroup (persistent over those few, so each still
+        // prefetches its next tile), so the dispatcher evens out the end of the launch.
         const int dx_ids = rows_grid<H, TL::BIG_BN>(T, NE, 128);
-        const int n_dx = persist_wgs(dx_ids, MOE_DX_PERSIST_WGS, 2 * MOE_DX_PERSIST_WGS);  // a multiple of 8
+        const int n_dx = round_up((dx_ids + MOE_DX_TILES_PER_WG - 1) / MOE_DX_TILES_PER_WG, 8);
         const int grid = n_dx + dw_grid<H, TL::BIG_BT>(n_chunk_max);
-        hipLaunchKernelGGL((k_bwd_f32<H, 128, TL::BIG_BN, TL::BIG_BT, MOE_F32_KC_DX, MOE_F32_KC_DW, MEAN, false>),
-                           dim3(grid), dim3(kThreads), 0, s, dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, NE, P,
-                           (int)T, n_dx, dx_ids, nh, inv_nh);
+        hipLaunchKernelGGL(
+            (k_bwd_f32<H, 128, TL::BIG_BN, TL::BIG_BT, MOE_F32_KC_DX, MOE_F32_KC_DW, MEAN, false, true>), dim3(grid),
+            dim3(kThreads), 0, s, dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, NE, P, (int)T, n_dx, dx_ids, nh,
+            inv_nh);
         return hipGetLastError();
     }
     const int dx_ids = rows_grid<H, TL::SMALL_BN>(T, NE, TL::SMALL_BM);
