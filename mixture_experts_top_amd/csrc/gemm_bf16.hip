@@ -388,7 +388,7 @@ __device__ __forceinline__ void dw_bf16_body(char* smem, int bid, const uint16_t
     if (do_db && tid < BT) part_db[(size_t)c * H + o0 + tid] = dbacc;
 }
 
-// Kernels.  The backward is one launch: dX tiles first, then dW / db chunk tiles.
+// Kernels.  The backward is one launch: dW / db chunk tiles first, then dX tiles.
 template <int H, int BN>
 __global__ __launch_bounds__(kThreads) void k_fwd_bf16(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
                                                         const float* __restrict__ bias, uint16_t* __restrict__ Y,
@@ -408,10 +408,13 @@ __global__ __launch_bounds__(kThreads) void k_bwd_bf16(const uint16_t* __restric
                                                         const int* __restrict__ perm, int NE, int P, int T, int n_dx) {
     constexpr size_t r = RowsBf16Smem<H, BN>::bytes, d = DwBf16Smem<H>::bytes;
     __shared__ __attribute__((aligned(16))) char smem[r > d ? r : d];  // one LDS region, either role
-    if ((int)blockIdx.x < n_dx)
-        rows_bf16_body<H, BN, true>(smem, blockIdx.x, dY, Wt, nullptr, dX, offsets, perm, NE, accumulate);
+    // longest first: the dW workgroups (a whole chunk each) lead the grid, the dX tiles follow,
+    // so the dispatcher evens out the end of the launch
+    const int n_dw = (int)gridDim.x - n_dx;
+    if ((int)blockIdx.x < n_dw)
+        dw_bf16_body<H>(smem, blockIdx.x, dY, X, part_dw, part_db, offsets, perm, NE, P, T);
     else
-        dw_bf16_body<H>(smem, blockIdx.x - n_dx, dY, X, part_dw, part_db, offsets, perm, NE, P, T);
+        rows_bf16_body<H, BN, true>(smem, blockIdx.x - n_dw, dY, Wt, nullptr, dX, offsets, perm, NE, accumulate);
 }
 
 // ---------------------------------------------------------------- launchers
