@@ -89,6 +89,18 @@ __device__ __forceinline__ void store_block(float* __restrict__ Out, int H, int 
     }
 }
 
+// Like xcd_split with `per` N-tiles per row tile, but with R consecutive row tiles on one
+// XCD: row tile mt runs on XCD (mt / R) % 8.  The dX tiles of the small-T backward use it
+// with R = (tokens per dW chunk) / BM, so a dX tile and the dW chunk over the same rows of dY
+// (chunk c runs on XCD c % 8) read them through the same L2.  Covers every row tile below
+// the grid's count when that count is a multiple of 8 R.
+__device__ __forceinline__ void xcd_rows(int bid, int per, int R, int& major, int& minor) {
+    const int x = bid % 8, sl = bid / 8;
+    minor = sl % per;
+    const int r = (sl / per) % R, q = sl / (per * R);
+    major = R * (8 * q + x) + r;
+}
+
 }  // namespace
 
 // ----------------------------------------------------------------------------------
@@ -345,7 +357,7 @@ __device__ __forceinline__ void rows_f32_body(char* smem, int wg, int nwg, int n
 #ifndef MOE_ONEPASS_RING_F4
 #define MOE_ONEPASS_RING_F4 12  // float4 registers per thread for the one-pass slice ring (keeps 4 waves/SIMD)
 #endif
-template <int H, int BM, int BN, int KC, bool DX, bool MEAN = false>
+template <int H, int BM, int BN, int KC, bool DX, bool MEAN = false, int XR = 1>
 __device__ __forceinline__ void rows_f32_onepass_body(char* smem, int bid, const float* __restrict__ A,
                                                       const float* __restrict__ W, const float* __restrict__ bias,
                                                       float* __restrict__ Out, const int* __restrict__ offsets,
@@ -375,7 +387,10 @@ __device__ __forceinline__ void rows_f32_onepass_body(char* smem, int bid, const
     const int wm = wave / WN, wn = wave % WN;
 
     int mt, nt, e, r0, r1;
-    xcd_split(bid, NT, mt, nt);
+    if (XR == 1)
+        xcd_split(bid, NT, mt, nt);
+    else
+        xcd_rows(bid, NT, XR, mt, nt);
     if (!find_tile(offsets, NE, mt, BM, e, r0, r1)) return;
     const int rows = r1 - r0, n0 = nt * BN;
     const float* __restrict__ We = W + (size_t)e * H * H;
@@ -676,6 +691,14 @@ __device__ __forceinline__ void dw_f32_body(char* smem, int bid, const float* __
 // Kernels.  The backward is one launch: its first n_dx workgroups are dX tiles and the rest
 // are dW / db chunk tiles, so both halves fill the GPU together.
 // ----------------------------------------------------------------------------------
+// Row tiles per XCD group for the small-T backward's dX tiles (tokens per dW chunk / BM; 1
+// switches the alignment off).
+#ifndef MOE_DX_XCD_ALIGN
+#define MOE_DX_XCD_ALIGN 1
+#endif
+template <int BM>
+constexpr int DX_XR = MOE_DX_XCD_ALIGN ? ((MOE_DW_MIN_CHUNK / BM) > 0 ? MOE_DW_MIN_CHUNK / BM : 1) : 1;
+
 #ifdef MOE_FWD_WAVES_PER_EU
 #define MOE_FWD_ATTR __attribute__((amdgpu_waves_per_eu(MOE_FWD_WAVES_PER_EU)))
 #else
@@ -716,8 +739,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_f32(const float* __restrict__ 
     }
     if ((int)blockIdx.x < n_dx) {
         if (ONE)
-            rows_f32_onepass_body<H, BM, BN, KCX, true, MEAN>(smem, blockIdx.x, dY, W, nullptr, dX, offsets, perm, NE,
-                                                              accumulate, nh, inv_nh);
+            rows_f32_onepass_body<H, BM, BN, KCX, true, MEAN, DX_XR<BM>>(smem, blockIdx.x, dY, W, nullptr, dX, offsets,
+                                                                          perm, NE, accumulate, nh, inv_nh);
         else
             rows_f32_body<H, BM, BN, KCX, true, MEAN>(smem, blockIdx.x, n_dx, dx_tile_ids, dY, W, nullptr, dX,
                                                       offsets, perm, NE, accumulate, nh, inv_nh);
@@ -831,7 +854,8 @@ static hipError_t bwd_f32(const float* dY, const float* X, const float* W, float
             inv_nh);
         return hipGetLastError();
     }
-    const int dx_ids = rows_grid<H, TL::SMALL_BN>(T, NE, TL::SMALL_BM);
+    const int xr = DX_XR<TL::SMALL_BM>;
+    const int dx_ids = round_up((int)((T + TL::SMALL_BM - 1) / TL::SMALL_BM) + NE, 8 * xr) * (H / TL::SMALL_BN);
     const bool one = dx_ids <= MOE_ROWS_ONEPASS_MAX_IDS;
     const int n_dx = one ? dx_ids : persist_wgs(dx_ids, MOE_DX_PERSIST_WGS, 2 * MOE_DX_PERSIST_WGS);
     const int grid = n_dx + dw_grid<H, TL::SMALL_BT>(n_chunk_max);

@@ -35,12 +35,6 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 #ifndef MOE_DW_WORKGROUPS
 #define MOE_DW_WORKGROUPS 2048
 #endif
-#ifndef MOE_DW_MIN_CHUNK
-#define MOE_DW_MIN_CHUNK 128
-#endif
-#ifndef MOE_DW_MIN_CHUNK_BIG
-#define MOE_DW_MIN_CHUNK_BIG 192
-#endif
 static int plan_chunks(int64_t T, int H, int act) {
     const bool f32 = act == MOE_DTYPE_F32;
     const int bt = f32 ? f32_dw_tile(T, H) : ((H >= 128) ? 128 : 64);

@@ -40,6 +40,13 @@ enum KernelId {
 #ifndef MOE_DW_SMALL_BT
 #define MOE_DW_SMALL_BT 64
 #endif
+// Minimum tokens per d_W chunk (see plan_chunks): small-T tiling, fp32 large-T tiling.
+#ifndef MOE_DW_MIN_CHUNK
+#define MOE_DW_MIN_CHUNK 128
+#endif
+#ifndef MOE_DW_MIN_CHUNK_BIG
+#define MOE_DW_MIN_CHUNK_BIG 192
+#endif
 inline bool f32_big_tiles(int64_t T, int H) {
     const int64_t nt = H >= 128 ? H / 128 : 1;
     return (T / 128) * nt >= MOE_ROWS_BIG_TILES_PER_CU * 256;
