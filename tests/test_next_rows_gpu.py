@@ -75,7 +75,9 @@ def test_horizon_mean_collapse(gpu_lib, act, B, NH, H):
 
 
 @pytest.mark.parametrize("wl", [workloads.custom(173, 7, 128, 3), workloads.custom(61, 5, 256, 8),
-                                workloads.custom(3001, 5, 64, 4)], ids=["H128", "H256", "H64_multiblock"])
+                                workloads.custom(3001, 5, 64, 4),
+                                pytest.param(workloads.custom(14000, 5, 128, 4), marks=pytest.mark.slow)],
+                         ids=["H128", "H256", "H64_multiblock", "H128_large_T_tiling"])
 def test_bwd_from_mean_equals_collapse_then_bwd(gpu_lib, wl):
     import torch
     import mixture_experts_top_amd as moe

@@ -188,6 +188,17 @@ def test_persistent_tiles_full_parity(gpu_lib):
 
 
 @pytest.mark.slow
+def test_small_tile_persistent_paths_full_parity(gpu_lib):
+    """16,300 tokens, H=512, fp32: still the small-tile regime, but with more forward and dX
+    tiles than one-tile-per-workgroup grids take, so both run as persistent workgroups."""
+    from tests import gpu_run
+    wl = workloads.custom(3260, 5, 512, 6, gate_bias={2: 1.0})
+    print(f"[parity] small-tile persistent {wl}", flush=True)
+    inp = workloads.make_inputs(wl)
+    check_all(inp, gpu_run.run(inp))
+
+
+@pytest.mark.slow
 def test_large_stress_sampled_parity(gpu_lib):
     """1,048,576 tokens, H=256, N_E=16: routing and the aux pass in full; routed_ctx and
     d_fused_ctx on sampled tokens; d_b in full; d_W on sampled output rows of every expert."""
