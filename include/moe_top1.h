@@ -234,9 +234,11 @@ moe_status_t moe_softmax_ce_grad(const float* logits, const int32_t* labels, flo
 
 /*
  * Instrumentation.  While set, every launch of kernel `kernel_id` (MOE_KERNEL_*) made by
- * the calls above is bracketed by hipEventRecord(ev_start) and hipEventRecord(ev_stop) on
- * the call's stream.  The events are hipEvent_t handles created by the caller.  Pass
- * kernel_id < 0 to clear.  Process-wide setting; not thread-safe against concurrent calls.
+ * the calls above carries ev_start and ev_stop, which the command processor records at the
+ * kernel's own start and end (hipExtLaunchKernelGGL), so their difference is the kernel's
+ * duration.  A call that does not launch that kernel leaves the events untouched.  The
+ * events are hipEvent_t handles created by the caller.  Pass kernel_id < 0 to clear.
+ * Process-wide setting; not thread-safe against concurrent calls.
  */
 enum {
     MOE_KERNEL_ROUTE = 0,        /* argmax + per-block histogram */

@@ -161,7 +161,7 @@ __global__ void k_lambda_eff(const float* __restrict__ ent_ema, float floor_, fl
 
 hipError_t launch_lambda_eff(const float* ent_ema, float floor_, float max_extra, float target_frac, int K,
                              float* lambda_eff, hipStream_t s) {
-    hipLaunchKernelGGL(k_lambda_eff, dim3(1), dim3(64), 0, s, ent_ema, floor_, max_extra, target_frac, K, lambda_eff);
+    launch_kernel(k_lambda_eff, dim3(1), dim3(64), 0, s, ent_ema, floor_, max_extra, target_frac, K, lambda_eff);
     return hipGetLastError();
 }
 
@@ -169,22 +169,22 @@ hipError_t launch_aux_rows(const float* G, const int32_t* counts, int64_t T, int
                            float* dG, float* probs, float* part, int n_ablk, hipStream_t s) {
     dim3 grid(n_ablk), block(kAuxThreads);
     if (NE <= 4)
-        hipLaunchKernelGGL(k_aux_rows<4>, grid, block, 0, s, G, counts, (int)T, NE, lam, lam_dev, dG, probs, part);
+        launch_kernel(k_aux_rows<4>, grid, block, 0, s, G, counts, (int)T, NE, lam, lam_dev, dG, probs, part);
     else if (NE <= 8)
-        hipLaunchKernelGGL(k_aux_rows<8>, grid, block, 0, s, G, counts, (int)T, NE, lam, lam_dev, dG, probs, part);
+        launch_kernel(k_aux_rows<8>, grid, block, 0, s, G, counts, (int)T, NE, lam, lam_dev, dG, probs, part);
     else if (NE <= 16)
-        hipLaunchKernelGGL(k_aux_rows<16>, grid, block, 0, s, G, counts, (int)T, NE, lam, lam_dev, dG, probs, part);
+        launch_kernel(k_aux_rows<16>, grid, block, 0, s, G, counts, (int)T, NE, lam, lam_dev, dG, probs, part);
     else if (NE <= 32)
-        hipLaunchKernelGGL(k_aux_rows<32>, grid, block, 0, s, G, counts, (int)T, NE, lam, lam_dev, dG, probs, part);
+        launch_kernel(k_aux_rows<32>, grid, block, 0, s, G, counts, (int)T, NE, lam, lam_dev, dG, probs, part);
     else
-        hipLaunchKernelGGL(k_aux_rows<64>, grid, block, 0, s, G, counts, (int)T, NE, lam, lam_dev, dG, probs, part);
+        launch_kernel(k_aux_rows<64>, grid, block, 0, s, G, counts, (int)T, NE, lam, lam_dev, dG, probs, part);
     return hipGetLastError();
 }
 
 hipError_t launch_aux_final(const float* part, const int32_t* counts, int n_ablk, int64_t T, int NE,
                             float lam, const float* lam_dev, float* loss, float* frac, float* mean_prob,
                             hipStream_t s) {
-    hipLaunchKernelGGL(k_aux_final, dim3(1), dim3(256), 0, s, part, counts, n_ablk, (int)T, NE, lam, lam_dev, loss,
+    launch_kernel(k_aux_final, dim3(1), dim3(256), 0, s, part, counts, n_ablk, (int)T, NE, lam, lam_dev, loss,
                        frac, mean_prob);
     return hipGetLastError();
 }

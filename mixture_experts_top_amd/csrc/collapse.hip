@@ -82,15 +82,15 @@ hipError_t launch_collapse(bool bwd, int act, const void* in, void* out, int64_t
     const dim3 grid((unsigned)((n + 255) / 256));
     if (act == 0) {
         if (bwd)
-            hipLaunchKernelGGL(k_collapse_bwd_f32, grid, dim3(256), 0, s, (const float*)in, (float*)out, B, NH, H);
+            launch_kernel(k_collapse_bwd_f32, grid, dim3(256), 0, s, (const float*)in, (float*)out, B, NH, H);
         else
-            hipLaunchKernelGGL(k_collapse_fwd_f32, grid, dim3(256), 0, s, (const float*)in, (float*)out, B, NH, H);
+            launch_kernel(k_collapse_fwd_f32, grid, dim3(256), 0, s, (const float*)in, (float*)out, B, NH, H);
     } else {
         if (bwd)
-            hipLaunchKernelGGL(k_collapse_bwd_bf16, grid, dim3(256), 0, s, (const uint16_t*)in, (uint16_t*)out, B, NH,
+            launch_kernel(k_collapse_bwd_bf16, grid, dim3(256), 0, s, (const uint16_t*)in, (uint16_t*)out, B, NH,
                                H);
         else
-            hipLaunchKernelGGL(k_collapse_fwd_bf16, grid, dim3(256), 0, s, (const uint16_t*)in, (uint16_t*)out, B, NH,
+            launch_kernel(k_collapse_fwd_bf16, grid, dim3(256), 0, s, (const uint16_t*)in, (uint16_t*)out, B, NH,
                                H);
     }
     return hipGetLastError();

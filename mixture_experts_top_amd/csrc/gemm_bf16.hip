@@ -426,7 +426,7 @@ static hipError_t fwd_bf16(const uint16_t* X, const uint16_t* W, const float* bi
     constexpr int BN = (H >= 128) ? 128 : H;
     constexpr int NT = H / BN;
     const int grid = round_up((int)((T + 127) / 128) + NE, 8) * NT;
-    hipLaunchKernelGGL((k_fwd_bf16<H, BN>), dim3(grid), dim3(kThreads), 0, s, X, W, bias, Y, offsets, perm, NE);
+    launch_kernel((k_fwd_bf16<H, BN>), dim3(grid), dim3(kThreads), 0, s, X, W, bias, Y, offsets, perm, NE);
     return hipGetLastError();
 }
 
@@ -440,7 +440,7 @@ static hipError_t bwd_bf16(const uint16_t* dY, const uint16_t* X, const uint16_t
     constexpr int TPC = (H / BT) * (H / BT);
     const int n_dx = round_up((int)((T + 127) / 128) + NE, 8) * NT;
     const int grid = n_dx + round_up(n_chunk_max, 8) * TPC;
-    hipLaunchKernelGGL((k_bwd_bf16<H, BN>), dim3(grid), dim3(kThreads), 0, s, dY, X, Wt, dX, accumulate, pdw, pdb,
+    launch_kernel((k_bwd_bf16<H, BN>), dim3(grid), dim3(kThreads), 0, s, dY, X, Wt, dX, accumulate, pdw, pdb,
                        offsets, perm, NE, P, (int)T, n_dx);
     return hipGetLastError();
 }
@@ -458,7 +458,7 @@ hipError_t launch_fwd_gemm_bf16(const uint16_t* X, const uint16_t* W, const floa
 }
 
 hipError_t launch_transpose_w_bf16(const uint16_t* W, uint16_t* Wt, int H, int NE, hipStream_t s) {
-    hipLaunchKernelGGL(k_transpose_bf16, dim3(H / 64, H / 64, NE), dim3(256), 0, s, W, Wt, H);
+    launch_kernel(k_transpose_bf16, dim3(H / 64, H / 64, NE), dim3(256), 0, s, W, Wt, H);
     return hipGetLastError();
 }
 

@@ -820,16 +820,16 @@ static hipError_t fwd_f32(const float* X, const float* W, const float* bias, flo
     if (f32_big_tiles(T, H)) {
         const int ids = rows_grid<H, TL::BIG_BN>(T, NE, 128);
         const int grid = persist_wgs(ids, MOE_FWD_PERSIST_WGS, MOE_FWD_PERSIST_WGS);
-        hipLaunchKernelGGL((k_fwd_f32<H, 128, TL::BIG_BN, MOE_F32_KC_FWD, false>), dim3(grid), dim3(kThreads), 0, s,
+        launch_kernel((k_fwd_f32<H, 128, TL::BIG_BN, MOE_F32_KC_FWD, false>), dim3(grid), dim3(kThreads), 0, s,
                            X, W, bias, Y, offsets, perm, NE, ids);
         return hipGetLastError();
     }
     const int ids = rows_grid<H, TL::FWD_BN>(T, NE, TL::FWD_BM);
     if (ids <= MOE_ROWS_ONEPASS_MAX_IDS)
-        hipLaunchKernelGGL((k_fwd_f32<H, TL::FWD_BM, TL::FWD_BN, MOE_F32_KC_FWD, true>), dim3(ids),
+        launch_kernel((k_fwd_f32<H, TL::FWD_BM, TL::FWD_BN, MOE_F32_KC_FWD, true>), dim3(ids),
                            dim3(kThreads), 0, s, X, W, bias, Y, offsets, perm, NE, ids);
     else
-        hipLaunchKernelGGL((k_fwd_f32<H, TL::FWD_BM, TL::FWD_BN, MOE_F32_KC_FWD, false>),
+        launch_kernel((k_fwd_f32<H, TL::FWD_BM, TL::FWD_BN, MOE_F32_KC_FWD, false>),
                            dim3(persist_wgs(ids, MOE_FWD_PERSIST_WGS, MOE_FWD_PERSIST_WGS)), dim3(kThreads), 0, s, X,
                            W, bias, Y, offsets, perm, NE, ids);
     return hipGetLastError();
@@ -848,7 +848,7 @@ static hipError_t bwd_f32(const float* dY, const float* X, const float* W, float
         const int dx_ids = rows_grid<H, TL::BIG_BN>(T, NE, 128);
         const int n_dx = round_up((dx_ids + MOE_DX_TILES_PER_WG - 1) / MOE_DX_TILES_PER_WG, 8);
         const int grid = n_dx + dw_grid<H, TL::BIG_BT>(n_chunk_max);
-        hipLaunchKernelGGL(
+        launch_kernel(
             (k_bwd_f32<H, 128, TL::BIG_BN, TL::BIG_BT, MOE_F32_KC_DX, MOE_F32_KC_DW, MEAN, false, true>), dim3(grid),
             dim3(kThreads), 0, s, dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, NE, P, (int)T, n_dx, dx_ids, nh,
             inv_nh);
@@ -860,12 +860,12 @@ static hipError_t bwd_f32(const float* dY, const float* X, const float* W, float
     const int n_dx = one ? dx_ids : persist_wgs(dx_ids, MOE_DX_PERSIST_WGS, 2 * MOE_DX_PERSIST_WGS);
     const int grid = n_dx + dw_grid<H, TL::SMALL_BT>(n_chunk_max);
     if (one)
-        hipLaunchKernelGGL(
+        launch_kernel(
             (k_bwd_f32<H, TL::SMALL_BM, TL::SMALL_BN, TL::SMALL_BT, MOE_F32_KC_DX, MOE_F32_KC_DW, MEAN, true>),
             dim3(grid), dim3(kThreads), 0, s, dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, NE, P, (int)T, n_dx,
             dx_ids, nh, inv_nh);
     else
-        hipLaunchKernelGGL(
+        launch_kernel(
             (k_bwd_f32<H, TL::SMALL_BM, TL::SMALL_BN, TL::SMALL_BT, MOE_F32_KC_DX, MOE_F32_KC_DW, MEAN, false>),
             dim3(grid), dim3(kThreads), 0, s, dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, NE, P, (int)T, n_dx,
             dx_ids, nh, inv_nh);

@@ -76,11 +76,19 @@ Plan make_plan(int64_t T, int H, int NE, int act) {
 static int g_timer_kernel = -1;
 static hipEvent_t g_timer_start = nullptr, g_timer_stop = nullptr;
 
+static ArmedEvents g_armed;
+ArmedEvents& armed_events() { return g_armed; }
+
+// The timed kernel's launch carries the events (launch_kernel); if the launcher made no
+// launch, they are disarmed again and keep their earlier timestamps.
 TimerScope::TimerScope(KernelId k, hipStream_t st) : s(st), on(g_timer_kernel == (int)k) {
-    if (on) (void)hipEventRecord(g_timer_start, s);
+    if (on) {
+        g_armed.start = g_timer_start;
+        g_armed.stop = g_timer_stop;
+    }
 }
 TimerScope::~TimerScope() {
-    if (on) (void)hipEventRecord(g_timer_stop, s);
+    if (on) g_armed.start = g_armed.stop = nullptr;
 }
 
 // ---------------------------------------------------------------- validation

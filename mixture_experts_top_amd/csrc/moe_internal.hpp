@@ -5,6 +5,7 @@
 // kernel file provides.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -145,6 +146,30 @@ struct TimerScope {
     TimerScope(KernelId k, hipStream_t s);
     ~TimerScope();
 };
+
+// Events armed by a TimerScope for the next kernel launch (process-wide, like the timer).
+struct ArmedEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+ArmedEvents& armed_events();
+
+// Every kernel launch goes through here.  When a TimerScope has armed a pair of events, the
+// launch carries them and the command processor records them at the kernel's own start and
+// end (hipExtLaunchKernelGGL); otherwise it is a plain launch.  Arguments are converted to the
+// kernel's parameter types.
+template <typename... KArgs, typename... Args>
+inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t shm, hipStream_t s,
+                          Args... args) {
+    static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count");
+    ArmedEvents& ev = armed_events();
+    if (ev.start != nullptr) {
+        const hipEvent_t a = ev.start, b = ev.stop;
+        ev.start = ev.stop = nullptr;
+        hipExtLaunchKernelGGL(kernel, grid, block, shm, s, a, b, 0u, static_cast<KArgs>(args)...);
+    } else {
+        hipLaunchKernelGGL(kernel, grid, block, shm, s, static_cast<KArgs>(args)...);
+    }
+}
 
 // ---- launchers (each returns the hipError_t of its launch) ----
 hipError_t launch_route(const float* G, int64_t T, int NE, int32_t* idx, int32_t* hist,

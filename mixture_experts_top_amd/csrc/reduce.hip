@@ -80,11 +80,11 @@ hipError_t launch_reduce_dw(const float* part_dw, const float* part_db, const in
                             int NE, int P, float* dW, float* db, hipStream_t s) {
     if (P >= MOE_REDUCE_RY16_MIN_P) {
         const int nbx = H * H / (4 * 16);
-        hipLaunchKernelGGL(k_reduce_dw<16>, dim3(nbx + 1, NE), dim3(256), 0, s, part_dw, part_db, offsets, H, NE, P,
+        launch_kernel(k_reduce_dw<16>, dim3(nbx + 1, NE), dim3(256), 0, s, part_dw, part_db, offsets, H, NE, P,
                            (int)T, dW, db);
     } else {
         const int nbx = H * H / (4 * 64);
-        hipLaunchKernelGGL(k_reduce_dw<4>, dim3(nbx + 1, NE), dim3(256), 0, s, part_dw, part_db, offsets, H, NE, P,
+        launch_kernel(k_reduce_dw<4>, dim3(nbx + 1, NE), dim3(256), 0, s, part_dw, part_db, offsets, H, NE, P,
                            (int)T, dW, db);
     }
     return hipGetLastError();

@@ -74,16 +74,16 @@ hipError_t launch_reduce_axis0(const float* in, int64_t n_batch, int64_t n_tail,
     const int64_t tiles = (n_tail + (vec ? 256 : 64) - 1) / (vec ? 256 : 64);
     float* dst = (R == 1) ? out : part;
     if (vec) {
-        hipLaunchKernelGGL(k_reduce_axis0<true>, dim3((unsigned)tiles, (unsigned)R), dim3(256), 0, s, in, n_batch,
+        launch_kernel(k_reduce_axis0<true>, dim3((unsigned)tiles, (unsigned)R), dim3(256), 0, s, in, n_batch,
                            n_tail, rpc, dst);
         if (R > 1)
-            hipLaunchKernelGGL(k_reduce_axis0<true>, dim3((unsigned)tiles, 1), dim3(256), 0, s, part, R, n_tail, R,
+            launch_kernel(k_reduce_axis0<true>, dim3((unsigned)tiles, 1), dim3(256), 0, s, part, R, n_tail, R,
                                out);
     } else {
-        hipLaunchKernelGGL(k_reduce_axis0<false>, dim3((unsigned)tiles, (unsigned)R), dim3(256), 0, s, in, n_batch,
+        launch_kernel(k_reduce_axis0<false>, dim3((unsigned)tiles, (unsigned)R), dim3(256), 0, s, in, n_batch,
                            n_tail, rpc, dst);
         if (R > 1)
-            hipLaunchKernelGGL(k_reduce_axis0<false>, dim3((unsigned)tiles, 1), dim3(256), 0, s, part, R, n_tail, R,
+            launch_kernel(k_reduce_axis0<false>, dim3((unsigned)tiles, 1), dim3(256), 0, s, part, R, n_tail, R,
                                out);
     }
     return hipGetLastError();

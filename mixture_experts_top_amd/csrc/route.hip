@@ -266,27 +266,27 @@ bool scatter_scan_fits(int n_rblk, int NE) { return (int64_t)n_rblk * NE <= 4096
 
 hipError_t launch_scatter_scan(const int32_t* idx, int64_t T, int NE, const int32_t* hist, int n_rblk,
                                int32_t* counts, int32_t* offsets, int32_t* perm, hipStream_t s) {
-    hipLaunchKernelGGL(k_scatter_scan, dim3(n_rblk), dim3(kRouteThreads), 0, s, idx, (int)T, NE, hist, n_rblk, counts,
+    launch_kernel(k_scatter_scan, dim3(n_rblk), dim3(kRouteThreads), 0, s, idx, (int)T, NE, hist, n_rblk, counts,
                        offsets, perm);
     return hipGetLastError();
 }
 
 hipError_t launch_route(const float* G, int64_t T, int NE, int32_t* idx, int32_t* hist, int n_rblk,
                         hipStream_t s) {
-    hipLaunchKernelGGL(k_route, dim3(n_rblk), dim3(kRouteThreads), 0, s, G, (int)T, NE, idx, hist);
+    launch_kernel(k_route, dim3(n_rblk), dim3(kRouteThreads), 0, s, G, (int)T, NE, idx, hist);
     return hipGetLastError();
 }
 
 hipError_t launch_scan(const int32_t* hist, int n_rblk, int NE, int32_t* blkbase, int32_t* counts,
                        int32_t* offsets, hipStream_t s) {
-    hipLaunchKernelGGL(k_scan, dim3(1), dim3(kScanThreads), 0, s, hist, n_rblk, NE, blkbase, counts,
+    launch_kernel(k_scan, dim3(1), dim3(kScanThreads), 0, s, hist, n_rblk, NE, blkbase, counts,
                        offsets);
     return hipGetLastError();
 }
 
 hipError_t launch_scatter(const int32_t* idx, int64_t T, int NE, const int32_t* blkbase, int32_t* perm,
                           int n_rblk, hipStream_t s) {
-    hipLaunchKernelGGL(k_scatter, dim3(n_rblk), dim3(kRouteThreads), 0, s, idx, (int)T, NE, blkbase,
+    launch_kernel(k_scatter, dim3(n_rblk), dim3(kRouteThreads), 0, s, idx, (int)T, NE, blkbase,
                        perm);
     return hipGetLastError();
 }

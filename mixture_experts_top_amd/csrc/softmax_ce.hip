@@ -52,9 +52,9 @@ hipError_t launch_softmax_ce(const float* logits, const int32_t* labels, int64_t
     const dim3 grid((unsigned)((rows + 255) / 256));
     const float invB = 1.0f / (float)B;
     if (A <= 32)
-        hipLaunchKernelGGL(k_softmax_ce<32>, grid, dim3(256), 0, s, logits, labels, rows, A, invB, grad, ce);
+        launch_kernel(k_softmax_ce<32>, grid, dim3(256), 0, s, logits, labels, rows, A, invB, grad, ce);
     else
-        hipLaunchKernelGGL(k_softmax_ce<64>, grid, dim3(256), 0, s, logits, labels, rows, A, invB, grad, ce);
+        launch_kernel(k_softmax_ce<64>, grid, dim3(256), 0, s, logits, labels, rows, A, invB, grad, ce);
     return hipGetLastError();
 }
 
