@@ -354,15 +354,27 @@ __device__ __forceinline__ void rows_f32_body(char* smem, int wg, int nwg, int n
 // tile waits on about three memory round trips (offsets, perm, first operands) rather than
 // one per slice.  Used when the grid has no more tiles than resident workgroups, where a
 // tile's latency is the kernel's time.
+// Routing outputs, for a forward that forms its tiles' token ids itself (and writes perm,
+// counts and offsets) instead of reading the scatter's perm: the expert of every token and
+// the per-routing-block expert histogram (256 tokens per block).
+struct RouteView {
+    const int* idx;
+    const int* hist;
+    int nblk, T;
+    int* counts;
+    int* offsets;
+    int* perm;
+};
+
 #ifndef MOE_ONEPASS_RING_F4
 #define MOE_ONEPASS_RING_F4 12  // float4 registers per thread for the one-pass slice ring (keeps 4 waves/SIMD)
 #endif
-template <int H, int BM, int BN, int KC, bool DX, bool MEAN = false, int XR = 1>
+template <int H, int BM, int BN, int KC, bool DX, bool MEAN = false, int XR = 1, bool GATHER = false>
 __device__ __forceinline__ void rows_f32_onepass_body(char* smem, int bid, const float* __restrict__ A,
                                                       const float* __restrict__ W, const float* __restrict__ bias,
                                                       float* __restrict__ Out, const int* __restrict__ offsets,
                                                       const int* __restrict__ perm, int NE, int accumulate,
-                                                      int nh = 1, float inv_nh = 1.0f) {
+                                                      int nh = 1, float inv_nh = 1.0f, RouteView rv = {}) {
     constexpr int NKC = H / KC;
     constexpr int NT = H / BN;
     constexpr int WM = (BM >= 64) ? 2 : 1, WN = 4 / WM;
@@ -391,18 +403,64 @@ __device__ __forceinline__ void rows_f32_onepass_body(char* smem, int bid, const
         xcd_split(bid, NT, mt, nt);
     else
         xcd_rows(bid, NT, XR, mt, nt);
-    if (!find_tile(offsets, NE, mt, BM, e, r0, r1)) return;
+    int lo = 0;  // GATHER: the tile's first rank within its expert
+    if constexpr (!GATHER) {
+        if (!find_tile(offsets, NE, mt, BM, e, r0, r1)) return;
+    } else {
+        // The routing histogram (at most 4096 entries) goes to LDS, over the region the K
+        // slices use later; its column sums give every expert's count, hence the tile list.
+        static_assert(SM_::a + SM_::b >= sizeof(int) * (4096 + 256 + 8), "LDS for the histogram");
+        int* hs = reinterpret_cast<int*>(smem);
+        int* part = hs + 4096;
+        const int nhist = rv.nblk * NE;
+        for (int i = tid; i < nhist; i += kThreads) hs[i] = rv.hist[i];
+        if (tid < BM) tok[0][tid] = -1;
+        __syncthreads();
+        int nep = 1;
+        while (nep < NE) nep <<= 1;
+        const int S = kThreads / nep;
+        {
+            const int ec = tid % nep, sg = tid / nep;
+            int sum = 0;
+            if (ec < NE)
+                for (int x = sg; x < rv.nblk; x += S) sum += hs[x * NE + ec];
+            part[tid] = sum;
+        }
+        __syncthreads();
+        for (int half = S / 2; half >= 1; half >>= 1) {  // integer sums: exact in any order
+            if (tid / nep < half) part[tid] += part[tid + half * nep];
+            __syncthreads();
+        }
+        const int cnt_l = (lane < NE) ? part[lane] : 0;
+        const int off_l = wave_inclusive_sum(cnt_l) - cnt_l;
+        const int nt_l = (cnt_l + BM - 1) / BM;
+        const int tincl = wave_inclusive_sum(nt_l), texcl = tincl - nt_l;
+        if (bid == 0 && wave == 0 && lane < NE) {
+            rv.counts[lane] = cnt_l;
+            rv.offsets[lane] = off_l;
+            if (lane == NE - 1) rv.offsets[NE] = off_l + cnt_l;
+        }
+        const uint64_t hit = __ballot(lane < NE && mt >= texcl && mt < tincl);
+        if (hit == 0) return;  // the same for every wavefront of the workgroup
+        e = __ffsll((unsigned long long)hit) - 1;
+        lo = (mt - __builtin_amdgcn_readlane(texcl, e)) * BM;
+        r0 = __builtin_amdgcn_readlane(off_l, e) + lo;
+        r1 = r0 + min(BM, __builtin_amdgcn_readlane(cnt_l, e) - lo);
+    }
     const int rows = r1 - r0, n0 = nt * BN;
     const float* __restrict__ We = W + (size_t)e * H * H;
 
     // token ids: of this thread's A rows (registers) and of the tile's rows (LDS, epilogue)
     int ta[AL];
+    int tok_mine = -1;
+    if constexpr (!GATHER) {
 #pragma unroll
-    for (int i = 0; i < AL; ++i) {
-        const int row = tid / TPR + RPP * i;
-        ta[i] = (row < rows) ? perm[r0 + row] : -1;
+        for (int i = 0; i < AL; ++i) {
+            const int row = tid / TPR + RPP * i;
+            ta[i] = (row < rows) ? perm[r0 + row] : -1;
+        }
+        tok_mine = (tid < BM && tid < rows) ? perm[r0 + tid] : -1;  // to LDS once the loads are out
     }
-    const int tok_mine = (tid < BM && tid < rows) ? perm[r0 + tid] : -1;  // to LDS once the loads are out
 
     f32x4 ra[PF][AL], rb[PF][BL];
     auto load_b = [&](int c, int slot) {
@@ -453,6 +511,69 @@ __device__ __forceinline__ void rows_f32_onepass_body(char* smem, int bid, const
 #pragma unroll
     for (int c = 0; c < PF; ++c) load_b(c, c);
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (GATHER) {
+        // The tile's token ids, while W is in flight: ranks lo .. lo + rows - 1 of expert e, in
+        // token order.  Expert e's tokens before routing block x number sum_{x' < x} hist[x'][e];
+        // inside a block, ballots over the 4 wavefronts (64 tokens each) rank them in order --
+        // the same stable counting sort the scatter kernels perform, so perm is identical.
+        static_assert(kRouteTokens == kThreads, "one routing block per workgroup pass");
+        int* hs = reinterpret_cast<int*>(smem);
+        int* wsc = hs + 4096 + 256;  // per-wave scratch and the found block range
+        const int hi = lo + rows;    // ranks [lo, hi)
+        {
+            const int per = (rv.nblk + kThreads - 1) / kThreads;
+            const int x0 = min(tid * per, rv.nblk), x1 = min(x0 + per, rv.nblk);
+            int sl = 0;
+            for (int x = x0; x < x1; ++x) sl += hs[x * NE + e];
+            const int wincl = wave_inclusive_sum(sl);
+            if (lane == 63) wsc[wave] = wincl;
+            __syncthreads();
+            int p = wincl - sl;
+            for (int w = 0; w < wave; ++w) p += wsc[w];
+            for (int x = x0; x < x1; ++x) {
+                const int v = hs[x * NE + e];
+                if (p <= lo && lo < p + v) {
+                    wsc[4] = x;
+                    wsc[5] = p;
+                }
+                if (p <= hi - 1 && hi - 1 < p + v) wsc[6] = x;
+                p += v;
+            }
+            __syncthreads();
+        }
+        const int b0 = wsc[4], b1 = wsc[6];
+        int pre = wsc[5];
+        __syncthreads();  // wsc[0..3] are reused below
+        const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        for (int xb = b0; xb <= b1; xb += 4) {  // the experts of up to 4 blocks in one round trip
+            int ex[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int t = (xb + u) * kRouteTokens + tid;
+                ex[u] = (xb + u <= b1 && t < rv.T) ? rv.idx[t] : -1;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (xb + u > b1) break;  // uniform
+                const int t = (xb + u) * kRouteTokens + tid;
+                const uint64_t m = __ballot(ex[u] == e);
+                if (lane == 0) wsc[wave] = __popcll(m);
+                __syncthreads();
+                int g = pre;
+                for (int w = 0; w < wave; ++w) g += wsc[w];
+                g += __popcll(m & lt);
+                if (ex[u] == e && g >= lo && g < hi) tok[0][g - lo] = t;
+                pre += wsc[0] + wsc[1] + wsc[2] + wsc[3];
+                __syncthreads();
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < AL; ++i) {
+            const int row = tid / TPR + RPP * i;
+            ta[i] = ((AFULL || row < BM) && row < rows) ? tok[0][row] : -1;
+        }
+        if (nt == 0 && tid < rows) rv.perm[r0 + tid] = tok[0][tid];
+    }
     // a padded row reads token 0's row: output rows are independent and padded ones are
     // never stored, so no branch is needed around the loads
 #pragma unroll
@@ -463,7 +584,7 @@ __device__ __forceinline__ void rows_f32_onepass_body(char* smem, int bid, const
 #pragma unroll
     for (int c = 0; c < PF; ++c) load_a(c, c);
     __builtin_amdgcn_sched_barrier(0);
-    if (tid < BM) tok[0][tid] = tok_mine;  // read in the epilogue, after the barriers
+    if (!GATHER && tid < BM) tok[0][tid] = tok_mine;  // read in the epilogue, after the barriers
 
     f32x16 acc[SM][SN];
 #pragma unroll
@@ -717,6 +838,21 @@ __global__ __launch_bounds__(kThreads) MOE_FWD_ATTR void k_fwd_f32(const float* 
                                             NE, 0);
 }
 
+// Forward for small T that also forms perm, counts and offsets from the routing outputs, so
+// the forward pass is routing + this one launch (the scatter kernel is not needed).
+template <int H, int BM, int BN, int KC>
+__global__ __launch_bounds__(kThreads) void k_fwd_f32_gather(const float* __restrict__ X, const float* __restrict__ W,
+                                                             const float* __restrict__ bias, float* __restrict__ Y,
+                                                             const int* __restrict__ idx, const int* __restrict__ hist,
+                                                             int nblk, int T, int* __restrict__ counts,
+                                                             int* __restrict__ offsets, int* __restrict__ perm,
+                                                             int NE) {
+    __shared__ __attribute__((aligned(16))) char smem[RowsF32Smem<BM, BN, KC, false>::bytes];
+    const RouteView rv{idx, hist, nblk, T, counts, offsets, perm};
+    rows_f32_onepass_body<H, BM, BN, KC, false, false, 1, true>(smem, blockIdx.x, X, W, bias, Y, nullptr, nullptr,
+                                                                 NE, 0, 1, 1.0f, rv);
+}
+
 template <int H, int BM, int BN, int BT, int KCX, int KCW, bool MEAN, bool ONE, bool DWF = false>
 __global__ __launch_bounds__(kThreads) void k_bwd_f32(const float* __restrict__ dY, const float* __restrict__ X,
                                                        const float* __restrict__ W, float* __restrict__ dX,
@@ -809,6 +945,9 @@ static int dw_grid(int n_chunk_max) {
 static int persist_wgs(int ids, int wgs, int from) { return (wgs <= 0 || ids < from) ? ids : wgs; }
 // Up to this many small-row tiles, a grid of one-tile workgroups with every K slice in
 // flight (the tiles fit in the resident slots, so latency, not throughput, bounds them).
+#ifndef MOE_FWD_GATHER
+#define MOE_FWD_GATHER 1  // small-T forward forms perm itself (routing + one launch)
+#endif
 #ifndef MOE_ROWS_ONEPASS_MAX_IDS
 #define MOE_ROWS_ONEPASS_MAX_IDS 1024
 #endif
@@ -870,6 +1009,46 @@ static hipError_t bwd_f32(const float* dY, const float* X, const float* W, float
             dim3(grid), dim3(kThreads), 0, s, dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, NE, P, (int)T, n_dx,
             dx_ids, nh, inv_nh);
     return hipGetLastError();
+}
+
+template <int H>
+static hipError_t fwd_f32_gather(const float* X, const float* W, const float* bias, float* Y, const int32_t* idx,
+                                 const int32_t* hist, int n_rblk, int32_t* counts, int32_t* offsets, int32_t* perm,
+                                 int64_t T, int NE, hipStream_t s) {
+    using TL = F32Tiles<H>;
+    const int ids = rows_grid<H, TL::FWD_BN>(T, NE, TL::FWD_BM);
+    launch_kernel(k_fwd_f32_gather<H, TL::FWD_BM, TL::FWD_BN, MOE_F32_KC_FWD>, dim3(ids), dim3(kThreads), 0, s, X,
+                  W, bias, Y, idx, hist, n_rblk, (int)T, counts, offsets, perm, NE);
+    return hipGetLastError();
+}
+
+template <int H>
+static bool gather_fits_h(int64_t T, int NE) {
+    using TL = F32Tiles<H>;
+    return rows_grid<H, TL::FWD_BN>(T, NE, TL::FWD_BM) <= MOE_ROWS_ONEPASS_MAX_IDS;
+}
+
+bool fwd_gemm_f32_gather_fits(int64_t T, int H, int NE, int n_rblk) {
+    if (!MOE_FWD_GATHER || f32_big_tiles(T, H) || (int64_t)n_rblk * NE > 4096) return false;
+    switch (H) {
+        case 64: return gather_fits_h<64>(T, NE);
+        case 128: return gather_fits_h<128>(T, NE);
+        case 256: return gather_fits_h<256>(T, NE);
+        case 512: return gather_fits_h<512>(T, NE);
+    }
+    return false;
+}
+
+hipError_t launch_fwd_gemm_f32_gather(const float* X, const float* W, const float* bias, float* Y,
+                                      const int32_t* idx, const int32_t* hist, int n_rblk, int32_t* counts,
+                                      int32_t* offsets, int32_t* perm, int64_t T, int H, int NE, hipStream_t s) {
+    switch (H) {
+        case 64: return fwd_f32_gather<64>(X, W, bias, Y, idx, hist, n_rblk, counts, offsets, perm, T, NE, s);
+        case 128: return fwd_f32_gather<128>(X, W, bias, Y, idx, hist, n_rblk, counts, offsets, perm, T, NE, s);
+        case 256: return fwd_f32_gather<256>(X, W, bias, Y, idx, hist, n_rblk, counts, offsets, perm, T, NE, s);
+        case 512: return fwd_f32_gather<512>(X, W, bias, Y, idx, hist, n_rblk, counts, offsets, perm, T, NE, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_fwd_gemm_f32(const float* X, const float* W, const float* bias, float* Y, const int32_t* offsets,

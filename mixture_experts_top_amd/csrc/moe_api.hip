@@ -245,6 +245,16 @@ moe_status_t moe_top1_fwd(const void* fused_ctx, const float* gate_logits, const
     const Plan p = make_plan(B * NH, (int)H, (int)NE, act);
     if ((st = check_ws(fn, p, workspace, workspace_bytes)) != MOE_OK) return st;
     hipStream_t s = (hipStream_t)stream;
+    if (act == MOE_DTYPE_F32 && fwd_gemm_f32_gather_fits(p.T, p.H, p.NE, p.n_rblk)) {
+        // routing, then one forward launch that also forms perm, counts and offsets
+        int32_t* hist = at<int32_t>(workspace, p.off_hist);
+        LAUNCH(K_ROUTE, launch_route(gate_logits, p.T, p.NE, expert_idx, hist, p.n_rblk, s), "route");
+        LAUNCH(K_FWD_GEMM,
+               launch_fwd_gemm_f32_gather((const float*)fused_ctx, (const float*)W, b, (float*)routed_ctx, expert_idx,
+                                          hist, p.n_rblk, expert_counts, expert_offsets, perm, p.T, p.H, p.NE, s),
+               "fwd gemm");
+        return MOE_OK;
+    }
     if ((st = do_route(gate_logits, expert_idx, expert_counts, expert_offsets, perm, p, workspace, s)) != MOE_OK)
         return st;
     if (act == MOE_DTYPE_F32)

@@ -182,6 +182,10 @@ hipError_t launch_scan(const int32_t* hist, int n_rblk, int NE, int32_t* blkbase
 hipError_t launch_scatter(const int32_t* idx, int64_t T, int NE, const int32_t* blkbase,
                           int32_t* perm, int n_rblk, hipStream_t s);
 
+bool fwd_gemm_f32_gather_fits(int64_t T, int H, int NE, int n_rblk);
+hipError_t launch_fwd_gemm_f32_gather(const float* X, const float* W, const float* bias, float* Y,
+                                      const int32_t* idx, const int32_t* hist, int n_rblk, int32_t* counts,
+                                      int32_t* offsets, int32_t* perm, int64_t T, int H, int NE, hipStream_t s);
 hipError_t launch_fwd_gemm_f32(const float* X, const float* W, const float* bias, float* Y,
                                const int32_t* offsets, const int32_t* perm, int64_t T, int H, int NE,
                                hipStream_t s);
