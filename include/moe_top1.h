@@ -182,6 +182,27 @@ moe_status_t moe_aux_loss_lambda_dev(const float* gate_logits, const int32_t* ex
                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Forward pass and load-balancing aux loss in one call (summary block of the MoE-gate page:
+ * the aux loss needs only the gate logits and the routing counts, so it can be formed as
+ * soon as the routing is done).  Outputs are those of moe_top1_fwd followed by
+ * moe_aux_loss (lambda_dev == NULL) or by moe_aux_loss_lambda_dev (lambda_dev != NULL;
+ * `lambda` is then ignored) on the expert_counts just written -- bit for bit, whichever
+ * way the library schedules the work.  For fp32 activations, N_E <= 8 and small T the
+ * softmax column sums ride on the routing launch and dG / frac / mean_prob / loss on the
+ * forward GEMM launch (two launches in all); otherwise the calls run one after the other.
+ * Workspace as moe_top1_fwd.  Errors as moe_top1_fwd and moe_aux_loss; lambda_dev, when
+ * given, must be 4-byte aligned.
+ */
+moe_status_t moe_top1_fwd_aux(const void* fused_ctx, const float* gate_logits, const void* W,
+                              const float* b, void* routed_ctx,
+                              int32_t* expert_idx, int32_t* expert_counts, int32_t* expert_offsets,
+                              int32_t* perm, float lambda, const float* lambda_dev,
+                              float* loss, float* d_gate_logits, float* frac, float* mean_prob,
+                              float* probs,
+                              int64_t B, int64_t NH, int64_t H, int64_t NE, int act,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * reduce_axis0 (perf-pass page "b23f8f2efa", reduce_axis0 entry; MHA page "9170d24fe3",
  * trainer and BUG blocks): out[j] = sum_{r < n_batch} in[r * n_tail + j] for j < n_tail, fp32,
  * with a fixed summation order and no atomics (bitwise reproducible for a shape).  The rows

@@ -70,6 +70,8 @@ def load_library() -> ctypes.CDLL:
         "moe_horizon_mean_collapse_bwd": ([P, P, I64, I64, I64, I32, P], I32),
         "moe_top1_bwd_from_mean": ([P, P, P, P, P, P, P, P, I32, I64, I64, I64, I64, I32, P, SZ, P], I32),
         "moe_softmax_ce_grad": ([P, P, P, P, I64, I64, I64, P], I32),
+        "moe_top1_fwd_aux": ([P, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P, P, P,
+                              I64, I64, I64, I64, I32, P, SZ, P], I32),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -201,6 +203,38 @@ def moe_top1_fwd(fused_ctx, gate_logits, W, b, routed_ctx, expert_idx, expert_co
     _check(load_library().moe_top1_fwd(_ptr(fused_ctx), _ptr(gate_logits), _ptr(W), _ptr(b), _ptr(routed_ctx),
                                        _ptr(expert_idx), _ptr(expert_counts), _ptr(expert_offsets), _ptr(perm),
                                        B, NH, H, NE, act, _ptr(ws), wsb, _stream(stream)))
+
+
+def moe_top1_fwd_aux(fused_ctx, gate_logits, W, b, routed_ctx, expert_idx, expert_counts, expert_offsets, perm,
+                     lam, loss, d_gate_logits, frac=None, mean_prob=None, probs=None, lambda_dev=None,
+                     workspace=None, stream=None):
+    """moe_top1_fwd followed by the aux loss on the counts it wrote, in one call (lambda from
+    `lambda_dev` on the device when given, else `lam`)."""
+    import torch
+    B, NH, H = _shape3(fused_ctx, "fused_ctx")
+    NE = int(gate_logits.shape[-1])
+    T = B * NH
+    act = _act(fused_ctx)
+    _expect(gate_logits, "gate_logits", (B, NH, NE), torch.float32)
+    _expect(W, "W", (NE, H, H), fused_ctx.dtype)
+    _expect(b, "b", (NE, H), torch.float32)
+    _expect(routed_ctx, "routed_ctx", (B, NH, H), fused_ctx.dtype)
+    _expect(expert_idx, "expert_idx", (T,), torch.int32)
+    _expect(expert_counts, "expert_counts", (NE,), torch.int32)
+    _expect(expert_offsets, "expert_offsets", (NE + 1,), torch.int32)
+    _expect(perm, "perm", (T,), torch.int32)
+    _expect(loss, "loss", (1,), torch.float32)
+    _expect(d_gate_logits, "d_gate_logits", (B, NH, NE), torch.float32)
+    _expect(frac, "frac", (NE,), torch.float32)
+    _expect(mean_prob, "mean_prob", (NE,), torch.float32)
+    _expect(probs, "probs", (B, NH, NE), torch.float32)
+    _expect(lambda_dev, "lambda_dev", (1,), torch.float32)
+    ws, wsb = _workspace(workspace, B, NH, H, NE, act, fused_ctx.device)
+    _check(load_library().moe_top1_fwd_aux(_ptr(fused_ctx), _ptr(gate_logits), _ptr(W), _ptr(b), _ptr(routed_ctx),
+                                           _ptr(expert_idx), _ptr(expert_counts), _ptr(expert_offsets), _ptr(perm),
+                                           float(lam), _ptr(lambda_dev), _ptr(loss), _ptr(d_gate_logits),
+                                           _ptr(frac), _ptr(mean_prob), _ptr(probs), B, NH, H, NE, act, _ptr(ws),
+                                           wsb, _stream(stream)))
 
 
 def moe_top1_bwd(d_routed_ctx, fused_ctx, W, expert_offsets, perm, d_fused_ctx, d_W, d_b, accumulate_dx=False,

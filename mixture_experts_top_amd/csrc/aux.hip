@@ -3,15 +3,13 @@
 // MoE-gate commit page ("11b96dac6a"), summary block: softmax of gate_logits plus the
 // load-balancing loss frac . prob_mean x N_EXPERTS, scaled by lambda (lambda = 0.01 in
 // the static form that the adaptive-lambda page "2d0e6b6bdc" replaces).  ARCHITECTURE
-// block: this loss is the only differentiable signal into the gate.  The softmax is the
-// max-shifted form of the softmax/cross-entropy page ("6cfd7e6691").
+// block: this loss is the only differentiable signal into the gate.  The per-token
+// arithmetic is in aux_math.hpp.
 //
-// With frac held constant (it is a count),
-//   dL/dG[t, j] = (lambda N_E / T) p[t, j] (frac[j] - sum_e frac[e] p[t, e]).
 // dG needs no global quantity other than frac, so one pass over G writes dG and the
 // per-block column sums of p; a single-workgroup pass then forms mean_prob and the loss
 // in a fixed order (no atomics).
-#include "moe_internal.hpp"
+#include "aux_math.hpp"
 
 namespace moe {
 
@@ -24,94 +22,28 @@ __global__ __launch_bounds__(kAuxThreads) void k_aux_rows(const float* __restric
                                                           float* __restrict__ probs,
                                                           float* __restrict__ part) {
     __shared__ float red[kAuxThreads / 64][NEB];
-    const int tid = threadIdx.x;
     static_assert(kAuxTokens == kAuxThreads, "one token per thread");
-    const int64_t t = (int64_t)blockIdx.x * kAuxTokens + tid;
-    const bool vec = (NE % 4) == 0;
-    // this token's logits first, then the counts: every load is unconditional (entries past
-    // N_E read entry 0 and are never used), so they all go out before the first wait
+    const int64_t t = (int64_t)blockIdx.x * kAuxTokens + threadIdx.x;
     float g[NEB];
-    const float* row = G + (t < T ? t : 0) * NE;
-    if (vec) {  // entries past N_E re-read the row's first ones; every use is guarded by e < N_E
-#pragma unroll
-        for (int q = 0; q < NEB / 4; ++q) {
-            const f32x4 v = reinterpret_cast<const f32x4*>(row)[4 * q < NE ? q : 0];
-            g[4 * q] = v.x; g[4 * q + 1] = v.y; g[4 * q + 2] = v.z; g[4 * q + 3] = v.w;
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < NEB; ++e) g[e] = row[e < NE ? e : 0];
-    }
+    aux_load_logits<NEB>(G, t, T, NE, g);
     int cnt[NEB];
 #pragma unroll
     for (int e = 0; e < NEB; ++e) cnt[e] = counts[e < NE ? e : 0];
     const float lam = lam_dev ? lam_dev[0] : lam_value;
     float frac[NEB], psum[NEB];
+    aux_frac<NEB>(cnt, T, frac);
 #pragma unroll
-    for (int e = 0; e < NEB; ++e) {  // unguarded so the loads stay unconditional: p[e] = 0 past N_E
-        frac[e] = (float)((double)cnt[e] / (double)T);
-        psum[e] = 0.0f;
-    }
-    const float coef = (float)((double)lam * (double)NE / (double)T);
+    for (int e = 0; e < NEB; ++e) psum[e] = 0.0f;
     if (t < T) {
-        float m = g[0];
+        float p[NEB];
+        aux_softmax<NEB>(g, NE, p);
+        aux_grad_row<NEB>(p, frac, aux_coef(lam, NE, T), NE, t, dG, probs);
 #pragma unroll
-        for (int e = 1; e < NEB; ++e)
-            if (e < NE) m = fmaxf(m, g[e]);
-        float z[NEB], S = 0.0f;
-#pragma unroll
-        for (int e = 0; e < NEB; ++e) {
-            z[e] = (e < NE) ? expf(g[e] - m) : 0.0f;
-            S += z[e];
-        }
-        float p[NEB], sfp = 0.0f;
-#pragma unroll
-        for (int e = 0; e < NEB; ++e) {
-            p[e] = z[e] / S;
-            sfp += frac[e] * p[e];
-            psum[e] += p[e];
-        }
-        float* drow = dG + t * NE;
-        if (vec) {
-#pragma unroll
-            for (int q = 0; q < NEB / 4; ++q)
-                if (4 * q < NE) {
-                    f32x4 v;
-                    v.x = coef * p[4 * q] * (frac[4 * q] - sfp);
-                    v.y = coef * p[4 * q + 1] * (frac[4 * q + 1] - sfp);
-                    v.z = coef * p[4 * q + 2] * (frac[4 * q + 2] - sfp);
-                    v.w = coef * p[4 * q + 3] * (frac[4 * q + 3] - sfp);
-                    reinterpret_cast<f32x4*>(drow)[q] = v;
-                    if (probs)
-                        reinterpret_cast<f32x4*>(probs + t * NE)[q] =
-                            f32x4{p[4 * q], p[4 * q + 1], p[4 * q + 2], p[4 * q + 3]};
-                }
-        } else {
-#pragma unroll
-            for (int e = 0; e < NEB; ++e)
-                if (e < NE) {
-                    drow[e] = coef * p[e] * (frac[e] - sfp);
-                    if (probs) probs[t * NE + e] = p[e];
-                }
-        }
+        for (int e = 0; e < NEB; ++e) psum[e] = p[e];
     }
-    // column sums of p over the block: butterfly within each wave (every lane ends with
-    // the same bits), then the four wave sums in a fixed order.
-    const int wave = tid / 64, lane = tid % 64;
-#pragma unroll
-    for (int e = 0; e < NEB; ++e) {
-        float v = psum[e];
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-        if (lane == 0) red[wave][e] = v;
-    }
-    __syncthreads();
-    if (tid < NE)
-        part[(int64_t)blockIdx.x * NE + tid] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+    aux_block_colsum<NEB>(psum, red, NE, part + (int64_t)blockIdx.x * NE);
 }
 
-// One workgroup: thread (s, e) sums blocks s, s+S, ... of column e; the S partial sums
-// are then added in order; mean_prob, frac and the loss follow.
 __global__ __launch_bounds__(256) void k_aux_final(const float* __restrict__ part,
                                                    const int* __restrict__ counts, int nblk, int T,
                                                    int NE, float lam_value, const float* __restrict__ lam_dev,
@@ -120,33 +52,10 @@ __global__ __launch_bounds__(256) void k_aux_final(const float* __restrict__ par
                                                    float* __restrict__ mean_prob_out) {
     __shared__ float acc[256];
     __shared__ float mp[kMaxExperts], fr[kMaxExperts];
-    int nep = 1;
-    while (nep < NE) nep <<= 1;
-    const int S = 256 / nep;
-    const int tid = threadIdx.x, e = tid % nep, s = tid / nep;
-    float v = 0.0f;
-    if (e < NE)
-#pragma unroll 8
-        for (int b = s; b < nblk; b += S) v += part[(int64_t)b * NE + e];
-    acc[tid] = v;
-    __syncthreads();
-    if (tid < NE) {
-        float tot = 0.0f;
-        for (int q = 0; q < S; ++q) tot += acc[q * nep + tid];
-        const float m = (float)((double)tot / (double)T);
-        const float f = (float)((double)counts[tid] / (double)T);
-        mp[tid] = m;
-        fr[tid] = f;
-        if (mean_prob_out) mean_prob_out[tid] = m;
-        if (frac_out) frac_out[tid] = f;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        const float lam = lam_dev ? lam_dev[0] : lam_value;
-        double d = 0.0;
-        for (int x = 0; x < NE; ++x) d += (double)fr[x] * (double)mp[x];
-        loss[0] = (float)((double)lam * (double)NE * d);
-    }
+    const int tid = threadIdx.x;
+    const int cnt = tid < NE ? counts[tid] : 0;
+    const float lam = lam_dev ? lam_dev[0] : lam_value;
+    aux_final_block(part, cnt, nblk, T, NE, lam, loss, frac_out, mean_prob_out, acc, mp, fr);
 }
 
 // Adaptive load-balancing weight (adaptive-lambda page, formula block), one thread:

@@ -17,7 +17,7 @@
 // The K dimension of consecutive instructions may be assigned to lanes in any order as
 // long as A and B agree; here lane half h of step s in a group of 8 covers k = 4h + s, so
 // a lane fetches four consecutive k with one 16-byte LDS read when K is contiguous.
-#include "moe_internal.hpp"
+#include "aux_math.hpp"
 
 namespace moe {
 
@@ -366,6 +366,31 @@ struct RouteView {
     int* perm;
 };
 
+// Loads the routing histogram hist[nblk][N_E] (at most 4096 entries) into hs and sums its
+// columns into tot (256 ints): afterwards tot[e] holds expert e's token count, e < N_E.
+// Integer sums, exact in any order.  Contains barriers: every thread calls it.
+__device__ __forceinline__ void hist_counts_lds(int* hs, int* tot, const int* __restrict__ hist, int nblk, int NE) {
+    const int tid = threadIdx.x;
+    const int nhist = nblk * NE;
+    for (int i = tid; i < nhist; i += kThreads) hs[i] = hist[i];
+    __syncthreads();
+    int nep = 1;
+    while (nep < NE) nep <<= 1;
+    const int S = kThreads / nep;
+    {
+        const int ec = tid % nep, sg = tid / nep;
+        int sum = 0;
+        if (ec < NE)
+            for (int x = sg; x < nblk; x += S) sum += hs[x * NE + ec];
+        tot[tid] = sum;
+    }
+    __syncthreads();
+    for (int half = S / 2; half >= 1; half >>= 1) {
+        if (tid / nep < half) tot[tid] += tot[tid + half * nep];
+        __syncthreads();
+    }
+}
+
 #ifndef MOE_ONEPASS_RING_F4
 #define MOE_ONEPASS_RING_F4 12  // float4 registers per thread for the one-pass slice ring (keeps 4 waves/SIMD)
 #endif
@@ -412,25 +437,8 @@ __device__ __forceinline__ void rows_f32_onepass_body(char* smem, int bid, const
         static_assert(SM_::a + SM_::b >= sizeof(int) * (4096 + 256 + 8), "LDS for the histogram");
         int* hs = reinterpret_cast<int*>(smem);
         int* part = hs + 4096;
-        const int nhist = rv.nblk * NE;
-        for (int i = tid; i < nhist; i += kThreads) hs[i] = rv.hist[i];
         if (tid < BM) tok[0][tid] = -1;
-        __syncthreads();
-        int nep = 1;
-        while (nep < NE) nep <<= 1;
-        const int S = kThreads / nep;
-        {
-            const int ec = tid % nep, sg = tid / nep;
-            int sum = 0;
-            if (ec < NE)
-                for (int x = sg; x < rv.nblk; x += S) sum += hs[x * NE + ec];
-            part[tid] = sum;
-        }
-        __syncthreads();
-        for (int half = S / 2; half >= 1; half >>= 1) {  // integer sums: exact in any order
-            if (tid / nep < half) part[tid] += part[tid + half * nep];
-            __syncthreads();
-        }
+        hist_counts_lds(hs, part, rv.hist, rv.nblk, NE);
         const int cnt_l = (lane < NE) ? part[lane] : 0;
         const int off_l = wave_inclusive_sum(cnt_l) - cnt_l;
         const int nt_l = (cnt_l + BM - 1) / BM;
@@ -838,16 +846,75 @@ __global__ __launch_bounds__(kThreads) MOE_FWD_ATTR void k_fwd_f32(const float* 
                                             NE, 0);
 }
 
+// The load-balancing loss inside the forward launch (its inputs are all known once the
+// routing is done): n_ablk workgroups after the GEMM ones write dG (and probs) for 256
+// tokens each, and one more forms frac, mean_prob and the loss from the routing kernel's
+// softmax column sums.  Each takes the counts from the histogram itself, so none waits on
+// another workgroup; the arithmetic is the aux kernels' (aux_math.hpp), bit for bit.
+struct AuxFwd {
+    const float* G;     // gate logits [T][N_E]
+    const float* part;  // per-routing-block softmax column sums [n_ablk][N_E]
+    float lam;
+    const float* lam_dev;  // lambda on the device, or null
+    float* dG;
+    float* probs;  // optional
+    float* loss;
+    float* frac;       // optional
+    float* mean_prob;  // optional
+    int n_gemm;        // GEMM workgroups before the aux ones
+    int n_ablk;
+};
+
+template <int NEB>
+__device__ __forceinline__ void aux_in_forward(char* smem, int r, const int* __restrict__ hist, int nblk, int T,
+                                               int NE, const AuxFwd& ax) {
+    int* hs = reinterpret_cast<int*>(smem);
+    int* tot = hs + 4096;
+    float* acc = reinterpret_cast<float*>(tot + 256);
+    float* mp = acc + 256;
+    float* fr = mp + kMaxExperts;
+    const int64_t t = (int64_t)r * kAuxTokens + threadIdx.x;
+    float g[NEB];
+    aux_load_logits<NEB>(ax.G, t, T, NE, g);  // unconditional, before the histogram's barriers
+    hist_counts_lds(hs, tot, hist, nblk, NE);
+    const float lam = ax.lam_dev ? ax.lam_dev[0] : ax.lam;
+    if (r < ax.n_ablk) {
+        int cnt[NEB];
+#pragma unroll
+        for (int e = 0; e < NEB; ++e) cnt[e] = tot[e < NE ? e : 0];
+        float frac[NEB];
+        aux_frac<NEB>(cnt, T, frac);
+        if (t < T) {
+            float p[NEB];
+            aux_softmax<NEB>(g, NE, p);
+            aux_grad_row<NEB>(p, frac, aux_coef(lam, NE, T), NE, t, ax.dG, ax.probs);
+        }
+    } else {
+        const int tid = threadIdx.x;
+        aux_final_block(ax.part, tid < NE ? tot[tid] : 0, ax.n_ablk, T, NE, lam, ax.loss, ax.frac, ax.mean_prob, acc,
+                        mp, fr);
+    }
+}
+
 // Forward for small T that also forms perm, counts and offsets from the routing outputs, so
-// the forward pass is routing + this one launch (the scatter kernel is not needed).
-template <int H, int BM, int BN, int KC>
+// the forward pass is routing + this one launch (the scatter kernel is not needed).  With
+// NEB > 0 the grid also carries the load-balancing loss (AuxFwd).
+template <int H, int BM, int BN, int KC, int NEB>
 __global__ __launch_bounds__(kThreads) void k_fwd_f32_gather(const float* __restrict__ X, const float* __restrict__ W,
                                                              const float* __restrict__ bias, float* __restrict__ Y,
                                                              const int* __restrict__ idx, const int* __restrict__ hist,
                                                              int nblk, int T, int* __restrict__ counts,
                                                              int* __restrict__ offsets, int* __restrict__ perm,
-                                                             int NE) {
+                                                             int NE, AuxFwd ax) {
     __shared__ __attribute__((aligned(16))) char smem[RowsF32Smem<BM, BN, KC, false>::bytes];
+    if constexpr (NEB > 0) {
+        static_assert(RowsF32Smem<BM, BN, KC, false>::bytes >= sizeof(int) * (4096 + 2 * 256 + 2 * kMaxExperts),
+                      "LDS for the aux workgroups");
+        if ((int)blockIdx.x >= ax.n_gemm) {
+            aux_in_forward<NEB>(smem, (int)blockIdx.x - ax.n_gemm, hist, nblk, T, NE, ax);
+            return;
+        }
+    }
     const RouteView rv{idx, hist, nblk, T, counts, offsets, perm};
     rows_f32_onepass_body<H, BM, BN, KC, false, false, 1, true>(smem, blockIdx.x, X, W, bias, Y, nullptr, nullptr,
                                                                  NE, 0, 1, 1.0f, rv);
@@ -1014,11 +1081,36 @@ static hipError_t bwd_f32(const float* dY, const float* X, const float* W, float
 template <int H>
 static hipError_t fwd_f32_gather(const float* X, const float* W, const float* bias, float* Y, const int32_t* idx,
                                  const int32_t* hist, int n_rblk, int32_t* counts, int32_t* offsets, int32_t* perm,
-                                 int64_t T, int NE, hipStream_t s) {
+                                 int64_t T, int NE, const AuxFwdArgs* aux, hipStream_t s) {
     using TL = F32Tiles<H>;
-    const int ids = rows_grid<H, TL::FWD_BN>(T, NE, TL::FWD_BM);
-    launch_kernel(k_fwd_f32_gather<H, TL::FWD_BM, TL::FWD_BN, MOE_F32_KC_FWD>, dim3(ids), dim3(kThreads), 0, s, X,
-                  W, bias, Y, idx, hist, n_rblk, (int)T, counts, offsets, perm, NE);
+    constexpr int BM = TL::FWD_BM, BN = TL::FWD_BN, KC = MOE_F32_KC_FWD;
+    const int ids = rows_grid<H, BN>(T, NE, BM);
+    AuxFwd ax = {};
+    ax.n_gemm = ids;
+    if (!aux) {
+        launch_kernel(k_fwd_f32_gather<H, BM, BN, KC, 0>, dim3(ids), dim3(kThreads), 0, s, X, W, bias, Y, idx, hist,
+                      n_rblk, (int)T, counts, offsets, perm, NE, ax);
+        return hipGetLastError();
+    }
+    ax.G = aux->G;
+    ax.part = aux->part;
+    ax.lam = aux->lam;
+    ax.lam_dev = aux->lam_dev;
+    ax.dG = aux->dG;
+    ax.probs = aux->probs;
+    ax.loss = aux->loss;
+    ax.frac = aux->frac;
+    ax.mean_prob = aux->mean_prob;
+    ax.n_ablk = aux->n_ablk;
+    const dim3 grid(ids + ax.n_ablk + 1);
+    if (NE <= 4)
+        launch_kernel(k_fwd_f32_gather<H, BM, BN, KC, 4>, grid, dim3(kThreads), 0, s, X, W, bias, Y, idx, hist,
+                      n_rblk, (int)T, counts, offsets, perm, NE, ax);
+    else if (NE <= 8)
+        launch_kernel(k_fwd_f32_gather<H, BM, BN, KC, 8>, grid, dim3(kThreads), 0, s, X, W, bias, Y, idx, hist,
+                      n_rblk, (int)T, counts, offsets, perm, NE, ax);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
@@ -1041,12 +1133,14 @@ bool fwd_gemm_f32_gather_fits(int64_t T, int H, int NE, int n_rblk) {
 
 hipError_t launch_fwd_gemm_f32_gather(const float* X, const float* W, const float* bias, float* Y,
                                       const int32_t* idx, const int32_t* hist, int n_rblk, int32_t* counts,
-                                      int32_t* offsets, int32_t* perm, int64_t T, int H, int NE, hipStream_t s) {
+                                      int32_t* offsets, int32_t* perm, int64_t T, int H, int NE,
+                                      const AuxFwdArgs* aux, hipStream_t s) {
+    if (aux && (NE > kAuxFwdMaxExperts || aux->n_ablk != n_rblk)) return hipErrorInvalidValue;
     switch (H) {
-        case 64: return fwd_f32_gather<64>(X, W, bias, Y, idx, hist, n_rblk, counts, offsets, perm, T, NE, s);
-        case 128: return fwd_f32_gather<128>(X, W, bias, Y, idx, hist, n_rblk, counts, offsets, perm, T, NE, s);
-        case 256: return fwd_f32_gather<256>(X, W, bias, Y, idx, hist, n_rblk, counts, offsets, perm, T, NE, s);
-        case 512: return fwd_f32_gather<512>(X, W, bias, Y, idx, hist, n_rblk, counts, offsets, perm, T, NE, s);
+        case 64: return fwd_f32_gather<64>(X, W, bias, Y, idx, hist, n_rblk, counts, offsets, perm, T, NE, aux, s);
+        case 128: return fwd_f32_gather<128>(X, W, bias, Y, idx, hist, n_rblk, counts, offsets, perm, T, NE, aux, s);
+        case 256: return fwd_f32_gather<256>(X, W, bias, Y, idx, hist, n_rblk, counts, offsets, perm, T, NE, aux, s);
+        case 512: return fwd_f32_gather<512>(X, W, bias, Y, idx, hist, n_rblk, counts, offsets, perm, T, NE, aux, s);
     }
     return hipErrorInvalidValue;
 }

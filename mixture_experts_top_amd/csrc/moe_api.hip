@@ -251,7 +251,8 @@ moe_status_t moe_top1_fwd(const void* fused_ctx, const float* gate_logits, const
         LAUNCH(K_ROUTE, launch_route(gate_logits, p.T, p.NE, expert_idx, hist, p.n_rblk, s), "route");
         LAUNCH(K_FWD_GEMM,
                launch_fwd_gemm_f32_gather((const float*)fused_ctx, (const float*)W, b, (float*)routed_ctx, expert_idx,
-                                          hist, p.n_rblk, expert_counts, expert_offsets, perm, p.T, p.H, p.NE, s),
+                                          hist, p.n_rblk, expert_counts, expert_offsets, perm, p.T, p.H, p.NE,
+                                          nullptr, s),
                "fwd gemm");
         return MOE_OK;
     }
@@ -375,6 +376,46 @@ moe_status_t moe_aux_loss_lambda_dev(const float* gate_logits, const int32_t* ex
     if (!lambda_dev) return fail(MOE_ERR_INVALID_ARG, "%s: required pointer 'lambda_dev' is NULL", fn);
     return aux_impl(fn, gate_logits, expert_counts, 0.0f, lambda_dev, loss, d_gate_logits, frac, mean_prob, probs,
                     B, NH, NE, workspace, workspace_bytes, stream);
+}
+
+moe_status_t moe_top1_fwd_aux(const void* fused_ctx, const float* gate_logits, const void* W, const float* b,
+                              void* routed_ctx, int32_t* expert_idx, int32_t* expert_counts, int32_t* expert_offsets,
+                              int32_t* perm, float lambda, const float* lambda_dev, float* loss, float* d_gate_logits,
+                              float* frac, float* mean_prob, float* probs, int64_t B, int64_t NH, int64_t H,
+                              int64_t NE, int act, void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "moe_top1_fwd_aux";
+    moe_status_t st = check_shape(fn, B, NH, H, NE, act, true);
+    if (st != MOE_OK) return st;
+    REQ(fused_ctx); REQ(gate_logits); REQ(W); REQ(b); REQ(routed_ctx);
+    REQ(expert_idx); REQ(expert_counts); REQ(expert_offsets); REQ(perm);
+    REQ(loss); REQ(d_gate_logits); OPT(frac); OPT(mean_prob); OPT(probs);
+    if (lambda_dev && ((uintptr_t)lambda_dev & 3u))
+        return fail(MOE_ERR_INVALID_ARG, "%s: lambda_dev is not 4-byte aligned", fn);
+    if (!lambda_dev && !isfinite(lambda)) return fail(MOE_ERR_INVALID_ARG, "%s: lambda is not finite", fn);
+    const Plan p = make_plan(B * NH, (int)H, (int)NE, act);
+    if ((st = check_ws(fn, p, workspace, workspace_bytes)) != MOE_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (act == MOE_DTYPE_F32 && NE <= kAuxFwdMaxExperts && p.n_ablk == p.n_rblk &&
+        fwd_gemm_f32_gather_fits(p.T, p.H, p.NE, p.n_rblk)) {
+        // two launches: routing (+ the softmax column sums), then the forward GEMM whose grid
+        // also writes dG and the loss
+        int32_t* hist = at<int32_t>(workspace, p.off_hist);
+        float* part = at<float>(workspace, p.off_paux);
+        LAUNCH(K_ROUTE, launch_route_part(gate_logits, p.T, p.NE, expert_idx, hist, part, p.n_rblk, s), "route");
+        const AuxFwdArgs ax = {gate_logits, part, lambda, lambda_dev, d_gate_logits, probs, loss, frac, mean_prob,
+                               p.n_ablk};
+        LAUNCH(K_FWD_GEMM,
+               launch_fwd_gemm_f32_gather((const float*)fused_ctx, (const float*)W, b, (float*)routed_ctx, expert_idx,
+                                          hist, p.n_rblk, expert_counts, expert_offsets, perm, p.T, p.H, p.NE, &ax,
+                                          s),
+               "fwd gemm + aux");
+        return MOE_OK;
+    }
+    st = moe_top1_fwd(fused_ctx, gate_logits, W, b, routed_ctx, expert_idx, expert_counts, expert_offsets, perm, B, NH,
+                      H, NE, act, workspace, workspace_bytes, stream);
+    if (st != MOE_OK) return st;
+    return aux_impl(fn, gate_logits, expert_counts, lambda, lambda_dev, loss, d_gate_logits, frac, mean_prob, probs, B,
+                    NH, NE, workspace, workspace_bytes, stream);
 }
 
 moe_status_t moe_lambda_eff_update(const float* ent_ema, float lambda_floor, float lambda_max_extra,

@@ -172,6 +172,8 @@ inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint3
 }
 
 // ---- launchers (each returns the hipError_t of its launch) ----
+hipError_t launch_route_part(const float* G, int64_t T, int NE, int32_t* idx, int32_t* hist, float* part,
+                             int n_rblk, hipStream_t s);
 hipError_t launch_route(const float* G, int64_t T, int NE, int32_t* idx, int32_t* hist,
                         int n_rblk, hipStream_t s);
 bool scatter_scan_fits(int n_rblk, int NE);
@@ -182,10 +184,26 @@ hipError_t launch_scan(const int32_t* hist, int n_rblk, int NE, int32_t* blkbase
 hipError_t launch_scatter(const int32_t* idx, int64_t T, int NE, const int32_t* blkbase,
                           int32_t* perm, int n_rblk, hipStream_t s);
 
+// The load-balancing loss carried by the small-T forward launch (N_E <= kAuxFwdMaxExperts):
+// part holds the routing kernel's softmax column sums, one row per routing block.
+constexpr int kAuxFwdMaxExperts = 8;
+struct AuxFwdArgs {
+    const float* G;
+    const float* part;
+    float lam;
+    const float* lam_dev;
+    float* dG;
+    float* probs;
+    float* loss;
+    float* frac;
+    float* mean_prob;
+    int n_ablk;
+};
 bool fwd_gemm_f32_gather_fits(int64_t T, int H, int NE, int n_rblk);
 hipError_t launch_fwd_gemm_f32_gather(const float* X, const float* W, const float* bias, float* Y,
                                       const int32_t* idx, const int32_t* hist, int n_rblk, int32_t* counts,
-                                      int32_t* offsets, int32_t* perm, int64_t T, int H, int NE, hipStream_t s);
+                                      int32_t* offsets, int32_t* perm, int64_t T, int H, int NE,
+                                      const AuxFwdArgs* aux, hipStream_t s);
 hipError_t launch_fwd_gemm_f32(const float* X, const float* W, const float* bias, float* Y,
                                const int32_t* offsets, const int32_t* perm, int64_t T, int H, int NE,
                                hipStream_t s);

@@ -10,7 +10,7 @@
 // groups the tokens of each expert so that the expert linears become dense GEMMs.
 // Ranks inside a block come from wavefront ballots (lane order = token order), so the
 // permutation is stable and no atomics are used anywhere.
-#include "moe_internal.hpp"
+#include "aux_math.hpp"
 
 namespace moe {
 
@@ -89,6 +89,53 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(const float* __restrict
     if (tid < NE) {
         int s = 0;
         for (int g = 0; g < kRouteGroups; ++g) s += cnt[g][tid];
+        hist[(int64_t)blockIdx.x * NE + tid] = s;
+    }
+}
+
+// k_route with the first half of the load-balancing loss folded in: besides expert_idx
+// and hist[blk, :], the block's column sums of the gate softmax, part[blk, :] -- the same
+// bits k_aux_rows writes for these 256 tokens (aux_math.hpp), so the aux pass that
+// follows needs no column sums of its own.  The logits are loaded once for both.
+template <int NEB>
+__global__ __launch_bounds__(kRouteThreads) void k_route_part(const float* __restrict__ G, int T, int NE,
+                                                              int* __restrict__ idx_out, int* __restrict__ hist,
+                                                              float* __restrict__ part) {
+    static_assert(kRouteThreads == kRouteTokens && kRouteTokens == kAuxTokens && kRouteGroups == 4,
+                  "one token per thread, routing blocks = aux blocks");
+    __shared__ int cnt[kRouteGroups][kMaxExperts];
+    __shared__ float red[kRouteGroups][NEB];
+    const int tid = threadIdx.x;
+    for (int i = tid; i < kRouteGroups * kMaxExperts; i += kRouteThreads) (&cnt[0][0])[i] = 0;
+    const int64_t t = (int64_t)blockIdx.x * kRouteTokens + tid;
+    float g[NEB];
+    aux_load_logits<NEB>(G, t, T, NE, g);
+    __syncthreads();
+    int e = -1;
+    float psum[NEB];
+#pragma unroll
+    for (int x = 0; x < NEB; ++x) psum[x] = 0.0f;
+    if (t < T) {
+        // strict ">" upward from expert 0, as argmax_row: the lowest index among equal maxima
+        float best = g[0];
+        e = 0;
+#pragma unroll
+        for (int x = 1; x < NEB; ++x)
+            if (x < NE && g[x] > best) {
+                best = g[x];
+                e = x;
+            }
+        if (idx_out) idx_out[t] = e;
+        float p[NEB];
+        aux_softmax<NEB>(g, NE, p);
+#pragma unroll
+        for (int x = 0; x < NEB; ++x) psum[x] = p[x];
+    }
+    wave_rank(e, cnt[tid / 64]);
+    aux_block_colsum<NEB>(psum, red, NE, part + (int64_t)blockIdx.x * NE);  // its barrier orders cnt too
+    if (tid < NE) {
+        int s = 0;
+        for (int w = 0; w < kRouteGroups; ++w) s += cnt[w][tid];
         hist[(int64_t)blockIdx.x * NE + tid] = s;
     }
 }
@@ -274,6 +321,17 @@ hipError_t launch_scatter_scan(const int32_t* idx, int64_t T, int NE, const int3
 hipError_t launch_route(const float* G, int64_t T, int NE, int32_t* idx, int32_t* hist, int n_rblk,
                         hipStream_t s) {
     launch_kernel(k_route, dim3(n_rblk), dim3(kRouteThreads), 0, s, G, (int)T, NE, idx, hist);
+    return hipGetLastError();
+}
+
+hipError_t launch_route_part(const float* G, int64_t T, int NE, int32_t* idx, int32_t* hist, float* part,
+                             int n_rblk, hipStream_t s) {
+    if (NE <= 4)
+        launch_kernel(k_route_part<4>, dim3(n_rblk), dim3(kRouteThreads), 0, s, G, (int)T, NE, idx, hist, part);
+    else if (NE <= 8)
+        launch_kernel(k_route_part<8>, dim3(n_rblk), dim3(kRouteThreads), 0, s, G, (int)T, NE, idx, hist, part);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

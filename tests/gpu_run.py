@@ -81,6 +81,12 @@ def fwd(d: DevInputs, o: Buffers):
     moe.moe_top1_fwd(d.x, d.g, d.W, d.b, o.y, o.idx, o.counts, o.offsets, o.perm, workspace=o.ws)
 
 
+def fwd_aux(d: DevInputs, o: Buffers, lam=None, probs=True, lambda_dev=None):
+    moe.moe_top1_fwd_aux(d.x, d.g, d.W, d.b, o.y, o.idx, o.counts, o.offsets, o.perm,
+                         d.lam if lam is None else lam, o.loss, o.dg, frac=o.frac, mean_prob=o.mean_prob,
+                         probs=o.probs if probs else None, lambda_dev=lambda_dev, workspace=o.ws)
+
+
 def bwd(d: DevInputs, o: Buffers, accumulate=False):
     moe.moe_top1_bwd(d.dy, d.x, d.W, o.offsets, o.perm, o.dx, o.dW, o.db, accumulate_dx=accumulate, workspace=o.ws)
 
@@ -91,10 +97,16 @@ def aux(d: DevInputs, o: Buffers, counts=True, lam=None, probs=True, stream=None
                      stream=stream)
 
 
-def step(d: DevInputs, o: Buffers, probs=True, aux_stream=None):
-    """One pass of the hot path.  With `aux_stream`, the auxiliary loss (which needs only the
-    logits and the counts) runs on that stream, overlapping the backward; the calling stream
-    waits for it at the end.  The two use disjoint parts of the one workspace."""
+def step(d: DevInputs, o: Buffers, probs=True, aux_stream=None, fused=True):
+    """One pass of the hot path.  By default the forward and the auxiliary loss are one call
+    (moe_top1_fwd_aux), then the backward.  fused=False makes the three calls one by one;
+    with `aux_stream` as well, the auxiliary loss (which needs only the logits and the
+    counts) runs on that stream, overlapping the backward, and the calling stream waits for
+    it at the end.  The two use disjoint parts of the one workspace."""
+    if fused and aux_stream is None:
+        fwd_aux(d, o, probs=probs)
+        bwd(d, o)
+        return
     fwd(d, o)
     if aux_stream is None:
         bwd(d, o)
@@ -114,8 +126,8 @@ def snapshot(o: Buffers) -> dict:
             ("y", "idx", "counts", "offsets", "perm", "dx", "dW", "db", "loss", "dg", "frac", "mean_prob", "probs")}
 
 
-def run(inp, device="cuda") -> dict:
+def run(inp, device="cuda", fused=True) -> dict:
     d = upload(inp, device)
     o = Buffers(d)
-    step(d, o)
+    step(d, o, fused=fused)
     return snapshot(o)

@@ -102,6 +102,32 @@ def test_bwd_validation(lib):
     assert bwd(wsb=0) == WORKSPACE
 
 
+def test_fwd_aux_validation(lib):
+    def fa(**kw):
+        a = dict(x=FAKE, g=FAKE, w=FAKE, b=FAKE, y=FAKE, idx=FAKE, cnt=FAKE, off=FAKE, perm=FAKE, lam=0.01,
+                 lam_dev=None, loss=FAKE, dg=FAKE, probs=None, H=128, NE=4, act=0, ws=FAKE, wsb=1 << 40)
+        a.update(kw)
+        return lib.moe_top1_fwd_aux(a["x"], a["g"], a["w"], a["b"], a["y"], a["idx"], a["cnt"], a["off"],
+                                    a["perm"], a["lam"], a["lam_dev"], a["loss"], a["dg"], None, None, a["probs"],
+                                    8, 5, a["H"], a["NE"], a["act"], a["ws"], a["wsb"], None)
+    assert fa(x=None) == INVALID
+    assert b"fused_ctx" in lib.moe_last_error()
+    assert fa(perm=None) == INVALID
+    assert fa(loss=None) == INVALID
+    assert fa(dg=None) == INVALID
+    assert fa(probs=FAKE + 4) == INVALID
+    assert fa(lam=float("nan")) == INVALID
+    assert b"lambda" in lib.moe_last_error()
+    assert fa(lam=float("nan"), lam_dev=FAKE + 2, loss=None) == INVALID  # loss checked first
+    assert fa(lam=float("nan"), lam_dev=FAKE + 2) == INVALID
+    assert b"lambda_dev" in lib.moe_last_error()
+    assert fa(H=96) == UNSUPPORTED
+    assert fa(NE=65) == UNSUPPORTED
+    assert fa(act=5) == UNSUPPORTED
+    assert fa(ws=None) == WORKSPACE
+    assert fa(wsb=16) == WORKSPACE
+
+
 def test_aux_validation(lib):
     def aux(**kw):
         a = dict(g=FAKE, cnt=FAKE, lam=0.01, loss=FAKE, dg=FAKE, ws=FAKE, wsb=1 << 40, NE=4)

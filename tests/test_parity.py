@@ -86,6 +86,15 @@ def test_small_full_parity(gpu_lib, name):
     check_all(inp, gpu_run.run(inp))
 
 
+@pytest.mark.parametrize("name", ["tiny_ref_ties", "ragged_H128_NE3", "H256_NE8", "NE64_many_empty"])
+def test_small_parity_separate_calls(gpu_lib, name):
+    """The same, with moe_top1_fwd, moe_top1_bwd and moe_aux_loss called one by one."""
+    from tests import gpu_run
+    inp = workloads.make_inputs(SMALL[name])
+    print(f"[parity separate] {name} {SMALL[name]}", flush=True)
+    check_all(inp, gpu_run.run(inp, fused=False))
+
+
 def test_all_logits_equal_route_to_expert_zero(gpu_lib):
     from tests import gpu_run
     inp = workloads.make_inputs(workloads.custom(33, 5, 128, 6))
