@@ -57,12 +57,28 @@ __device__ __forceinline__ void xcd_split(int bid, int per, int& major, int& min
     minor = loc / 8;
 }
 
+// Token ids of the 16 rows a lane stores from a 32x32 accumulator block: row
+// 8 (r / 4) + 4 h + (r % 4) of the block, r = 0..15, read from the tile's id list in LDS
+// (tr points at the block's row 4 h) as four 16-byte reads with a single wait, so the
+// stores that follow do not each wait on an LDS read.
+__device__ __forceinline__ void block_row_ids(const int* tr, int (&tk)[16]) {
+    int4 v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = *reinterpret_cast<const int4*>(tr + 8 * q);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        tk[4 * q] = v[q].x; tk[4 * q + 1] = v[q].y; tk[4 * q + 2] = v[q].z; tk[4 * q + 3] = v[q].w;
+    }
+}
+
 // Stores one 32x32 accumulator block: its row 8 (r / 4) + 4 h + (r % 4) goes to token
 // tok_of(r) (negative: a padded row, not stored), column `col`.  No load may be pending
 // when the conditional stores run: a wait inside them would also wait for every store
 // issued before it.  With `prior` the output's current value is added (gradient
 // accumulation): four rows' loads go out before their stores (a padded row reads row 0
-// and drops it), so the block waits for memory four times, not sixteen.
+// and drops it), so the block waits for memory four times, not sixteen.  Reading the ids
+// one by one (tok_of from LDS) keeps registers free where they bound occupancy; where
+// they do not, store_block_ids takes the ids from registers.
 template <class TokOf>
 __device__ __forceinline__ void store_block(float* __restrict__ Out, int H, int col, const f32x16& a, float bv,
                                             bool prior, TokOf tok_of) {
@@ -89,6 +105,27 @@ __device__ __forceinline__ void store_block(float* __restrict__ Out, int H, int 
     }
 }
 
+// store_block with the 16 ids already in registers (block_row_ids): the stores do not
+// each wait on an LDS read.
+__device__ __forceinline__ void store_block_ids(float* __restrict__ Out, int H, int col, const f32x16& a, float bv,
+                                                bool prior, const int (&tk)[16]) {
+    if (prior) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            float old[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) old[u] = Out[(size_t)(tk[4 * q + u] < 0 ? 0 : tk[4 * q + u]) * H + col];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (tk[4 * q + u] >= 0) Out[(size_t)tk[4 * q + u] * H + col] = old[u] + (a[4 * q + u] + bv);
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            if (tk[r] >= 0) Out[(size_t)tk[r] * H + col] = a[r] + bv;
+    }
+}
+
 // Like xcd_split with `per` N-tiles per row tile, but with R consecutive row tiles on one
 // XCD: row tile mt runs on XCD (mt / R) % 8.  The dX tiles of the small-T backward use it
 // with R = (tokens per dW chunk) / BM, so a dX tile and the dW chunk over the same rows of dY
@@ -110,11 +147,17 @@ __device__ __forceinline__ void xcd_rows(int bid, int per, int R, int& major, in
 // issued into registers before the MFMAs of slice c, and stored to the other buffer after
 // them, so one barrier per slice suffices and load latency hides behind the MFMAs.
 // ----------------------------------------------------------------------------------
+#ifndef MOE_ONEPASS_STAGED_STORES
+#define MOE_ONEPASS_STAGED_STORES 1  // one-tile workgroups store their tile through LDS, whole rows
+#endif
 template <int BM, int BN, int KC, bool DX>
 struct RowsF32Smem {
     static constexpr int BS_ROWS = DX ? KC : BN, BS_COLS = DX ? BN + kPadKN : KC + kPad;
     static constexpr size_t a = sizeof(float) * 2 * BM * (KC + kPad), b = sizeof(float) * 2 * BS_ROWS * BS_COLS;
-    static constexpr size_t bytes = a + b + 2 * 4 * BM;  // + token ids of the current and the next tile
+    // the output tile staged row-major (the one-tile epilogue), over the K-slice buffers
+    static constexpr size_t stage = MOE_ONEPASS_STAGED_STORES ? sizeof(float) * BM * (BN + kPadKN) : 0;
+    static constexpr size_t tok_off = a + b > stage ? a + b : stage;
+    static constexpr size_t bytes = tok_off + 2 * 4 * BM;  // + token ids of the current and the next tile
 };
 
 // Persistent: workgroup `wg` of `nwg` computes tiles wg, wg + nwg, ... of the `ntile_ids` tile
@@ -144,7 +187,7 @@ __device__ __forceinline__ void rows_f32_body(char* smem, int wg, int nwg, int n
     using SM_ = RowsF32Smem<BM, BN, KC, DX>;
     float(&As)[2][BM][KC + kPad] = *reinterpret_cast<float(*)[2][BM][KC + kPad]>(smem);
     float(&Bs)[2][BS_ROWS][BS_COLS] = *reinterpret_cast<float(*)[2][BS_ROWS][BS_COLS]>(smem + SM_::a);
-    int(&tok)[2][BM] = *reinterpret_cast<int(*)[2][BM]>(smem + SM_::a + SM_::b);
+    int(&tok)[2][BM] = *reinterpret_cast<int(*)[2][BM]>(smem + SM_::tok_off);
 
     const int tid = threadIdx.x;
     const int wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
@@ -417,7 +460,7 @@ __device__ __forceinline__ void rows_f32_onepass_body(char* smem, int bid, const
     using SM_ = RowsF32Smem<BM, BN, KC, DX>;
     float(&As)[2][BM][KC + kPad] = *reinterpret_cast<float(*)[2][BM][KC + kPad]>(smem);
     float(&Bs)[2][BS_ROWS][BS_COLS] = *reinterpret_cast<float(*)[2][BS_ROWS][BS_COLS]>(smem + SM_::a);
-    int(&tok)[2][BM] = *reinterpret_cast<int(*)[2][BM]>(smem + SM_::a + SM_::b);
+    int(&tok)[2][BM] = *reinterpret_cast<int(*)[2][BM]>(smem + SM_::tok_off);
 
     const int tid = threadIdx.x;
     const int wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
@@ -650,13 +693,53 @@ __device__ __forceinline__ void rows_f32_onepass_body(char* smem, int bid, const
         if (c + 1 < NKC) __syncthreads();
     }
 
+    if constexpr (MOE_ONEPASS_STAGED_STORES) {
+        // Epilogue through LDS: the tile goes to a row-major staging area (over the K-slice
+        // buffers), then each output row is written as whole 16-byte segments -- a quarter of
+        // the store instructions of storing the accumulator blocks directly, and every row
+        // segment in one piece.  Same additions in the same order as store_block.
+        float(&St)[BM][BN + kPadKN] = *reinterpret_cast<float(*)[BM][BN + kPadKN]>(smem);
+        __syncthreads();  // every wavefront has read its last K slice
 #pragma unroll
-    for (int i = 0; i < SM; ++i) {
-        const int* tr = &tok[0][wm * WTM + i * 32 + 4 * h];
+        for (int i = 0; i < SM; ++i)
 #pragma unroll
-        for (int j = 0; j < SN; ++j)
-            store_block(Out, H, n0 + wn * WTN + j * 32 + l32, acc[i][j], bv[j], DX && accumulate,
-                        [&](int r) { return tr[8 * (r / 4) + (r % 4)]; });
+            for (int j = 0; j < SN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    St[wm * WTM + i * 32 + 8 * (r / 4) + 4 * h + (r % 4)][wn * WTN + j * 32 + l32] = acc[i][j][r] + bv[j];
+        __syncthreads();
+        constexpr int CPR = BN / 4, RPS = kThreads / CPR, NP = BM / RPS;  // float4 per row, rows per pass
+        static_assert(kThreads % CPR == 0 && BM % RPS == 0, "staged epilogue shape");
+        const int c4 = tid % CPR;
+        int tk[NP];
+        f32x4 v[NP];
+#pragma unroll
+        for (int q = 0; q < NP; ++q) {
+            const int row = q * RPS + tid / CPR;
+            tk[q] = tok[0][row];
+            v[q] = ld4(&St[row][4 * c4]);
+        }
+        if (DX && accumulate) {
+            f32x4 old[NP];  // all loads out before the first (conditional) store; padded rows read row 0
+#pragma unroll
+            for (int q = 0; q < NP; ++q) old[q] = ld4(Out + (size_t)(tk[q] < 0 ? 0 : tk[q]) * H + n0 + 4 * c4);
+#pragma unroll
+            for (int q = 0; q < NP; ++q)
+                if (tk[q] >= 0) st4(Out + (size_t)tk[q] * H + n0 + 4 * c4, old[q] + v[q]);
+        } else {
+#pragma unroll
+            for (int q = 0; q < NP; ++q)
+                if (tk[q] >= 0) st4(Out + (size_t)tk[q] * H + n0 + 4 * c4, v[q]);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < SM; ++i) {
+            int tk[16];
+            block_row_ids(&tok[0][wm * WTM + i * 32 + 4 * h], tk);
+#pragma unroll
+            for (int j = 0; j < SN; ++j)
+                store_block_ids(Out, H, n0 + wn * WTN + j * 32 + l32, acc[i][j], bv[j], DX && accumulate, tk);
+        }
     }
 }
 
