@@ -64,11 +64,17 @@ __global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restri
 #ifndef MOE_BF16_KC
 #define MOE_BF16_KC 64  // K slice of the bf16 row GEMM (a multiple of 16)
 #endif
+#ifndef MOE_BF16_STAGED_STORES
+#define MOE_BF16_STAGED_STORES 1  // output tiles go through LDS and out as whole 16-byte row segments
+#endif
+constexpr int kStPad = 8;  // fp32 staging rows: a stride of 8 (mod 64) floats keeps the two half-waves apart
 template <int H, int BN>
 struct RowsBf16Smem {
     static constexpr int BM = 128, KC = (MOE_BF16_KC < H) ? MOE_BF16_KC : H, KP = KC + 8;
     static constexpr size_t a = sizeof(uint16_t) * 2 * BM * KP, b = sizeof(uint16_t) * 2 * BN * KP, tok = 4 * BM;
-    static constexpr size_t bytes = a + b + tok;
+    static constexpr size_t stage = MOE_BF16_STAGED_STORES ? sizeof(float) * BM * (BN + kStPad) : 0;
+    static constexpr size_t tok_off = a + b > stage ? a + b : stage;
+    static constexpr size_t bytes = tok_off + tok;
 };
 
 // K slices of both operands in flight per thread (a ring of registers), fed to two LDS
@@ -96,7 +102,7 @@ __device__ __forceinline__ void rows_bf16_body(char* smem, int bid, const uint16
     using SM_ = RowsBf16Smem<H, BN>;
     uint16_t(&As)[2][BM][KP] = *reinterpret_cast<uint16_t(*)[2][BM][KP]>(smem);
     uint16_t(&Bs)[2][BN][KP] = *reinterpret_cast<uint16_t(*)[2][BN][KP]>(smem + SM_::a);
-    int* tok = reinterpret_cast<int*>(smem + SM_::a + SM_::b);
+    int* tok = reinterpret_cast<int*>(smem + SM_::tok_off);
 
     int mt, nt;
     xcd_split(bid, NT, mt, nt);
@@ -195,6 +201,46 @@ __device__ __forceinline__ void rows_bf16_body(char* smem, int bid, const uint16
         if (c + 1 < NKC) __syncthreads();
     }
 
+    if constexpr (MOE_BF16_STAGED_STORES) {
+        // Epilogue through LDS: the fp32 tile (+ bias) is staged row-major over the K-slice
+        // buffers, then each thread rounds 8 consecutive values to bf16 and writes them as one
+        // 16-byte piece of an output row -- an eighth of the store instructions of writing each
+        // lane's 2-byte values straight from the accumulators.  Same roundings as below.
+        float(&St)[BM][BN + kStPad] = *reinterpret_cast<float(*)[BM][BN + kStPad]>(smem);
+        const bool acc_dx = DX && accumulate;
+        __syncthreads();  // every wavefront has read its last K slice
+#pragma unroll
+        for (int i = 0; i < SM; ++i)
+#pragma unroll
+            for (int j = 0; j < SN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    St[wm * WTM + i * 32 + 8 * (r / 4) + 4 * h + (r % 4)][wn * WTN + j * 32 + l32] =
+                        acc_dx ? acc[i][j][r] : acc[i][j][r] + bv[j];
+        __syncthreads();
+        constexpr int CPR = BN / 8, RPS = kThreads / CPR, NP = BM / RPS;  // 8-wide pieces per row, rows per pass
+        static_assert(kThreads % CPR == 0 && BM % RPS == 0, "staged epilogue shape");
+        const int c8 = tid % CPR;
+        int tk[NP];
+#pragma unroll
+        for (int q = 0; q < NP; ++q) tk[q] = tok[q * RPS + tid / CPR];
+        u16x8 old[NP];
+        if (acc_dx) {  // every load out before the first (conditional) store; padded rows read row 0
+#pragma unroll
+            for (int q = 0; q < NP; ++q) old[q] = ld8(Out + (size_t)(tk[q] < 0 ? 0 : tk[q]) * H + n0 + 8 * c8);
+        }
+#pragma unroll
+        for (int q = 0; q < NP; ++q) {
+            const float* src = &St[q * RPS + tid / CPR][8 * c8];
+            const f32x4 v0 = *reinterpret_cast<const f32x4*>(src), v1 = *reinterpret_cast<const f32x4*>(src + 4);
+            const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+            u16x8 o;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) o[u] = f32_to_bf16(acc_dx ? bf16_to_f32(old[q][u]) + v[u] : v[u]);
+            if (tk[q] >= 0) st8(Out + (size_t)tk[q] * H + n0 + 8 * c8, o);
+        }
+        return;
+    }
 #pragma unroll
     for (int j = 0; j < SN; ++j) {
         const int col = n0 + wn * WTN + j * 32 + l32;
@@ -374,17 +420,39 @@ __device__ __forceinline__ void dw_bf16_body(char* smem, int bid, const uint16_t
     }
 
     float* __restrict__ Pd = part_dw + (size_t)c * H * H;
+    if constexpr (MOE_BF16_STAGED_STORES) {
+        // the partial tile through LDS (the loop's last barrier freed the buffers), then whole
+        // 16-byte row pieces
+        static_assert(DwBf16Smem<H>::bytes >= sizeof(float) * BT * (BT + kStPad), "LDS for the staged tile");
+        float(&St)[BT][BT + kStPad] = *reinterpret_cast<float(*)[BT][BT + kStPad]>(smem);
 #pragma unroll
-    for (int i = 0; i < SUB; ++i)
+        for (int i = 0; i < SUB; ++i)
 #pragma unroll
-        for (int j = 0; j < SUB; ++j) {
-            const int col = i0 + wn * WT + j * 32 + l32;
+            for (int j = 0; j < SUB; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = o0 + wm * WT + i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
-                Pd[(size_t)row * H + col] = acc[i][j][r];
-            }
+                for (int r = 0; r < 16; ++r)
+                    St[wm * WT + i * 32 + 8 * (r / 4) + 4 * h + (r % 4)][wn * WT + j * 32 + l32] = acc[i][j][r];
+        __syncthreads();
+        constexpr int CPR = BT / 4, RPS = kThreads / CPR;
+#pragma unroll
+        for (int q = 0; q < BT / RPS; ++q) {
+            const int row = q * RPS + tid / CPR, c4 = tid % CPR;
+            *reinterpret_cast<f32x4*>(Pd + (size_t)(o0 + row) * H + i0 + 4 * c4) =
+                *reinterpret_cast<const f32x4*>(&St[row][4 * c4]);
         }
+    } else {
+#pragma unroll
+        for (int i = 0; i < SUB; ++i)
+#pragma unroll
+            for (int j = 0; j < SUB; ++j) {
+                const int col = i0 + wn * WT + j * 32 + l32;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = o0 + wm * WT + i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
+                    Pd[(size_t)row * H + col] = acc[i][j][r];
+                }
+            }
+    }
     if (do_db && tid < BT) part_db[(size_t)c * H + o0 + tid] = dbacc;
 }
 
