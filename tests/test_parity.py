@@ -75,6 +75,8 @@ SMALL = {
     "bf16_H512_NE8": workloads.custom(64, 5, 512, 8, act="bf16"),
     "bf16_H64_NE3_ties": workloads.custom(97, 5, 64, 3, act="bf16", gate="int"),
     "bf16_H256_NE5": workloads.custom(150, 5, 256, 5, act="bf16"),
+    # a few thousand bf16 tiles (several per resident workgroup slot), ragged at every expert's end
+    "bf16_H512_many_tiles": workloads.custom(4096, 5, 512, 8, act="bf16", gate_bias={3: 1.0}),
 }
 
 
