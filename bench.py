@@ -238,6 +238,9 @@ def main():
     ap.add_argument("--separate-aux", action="store_true",
                     help="make the forward, backward and aux-loss calls one by one instead of "
                          "moe_top1_fwd_aux + moe_top1_bwd")
+    ap.add_argument("--cold-mib", type=int, default=512,
+                    help="after the timed region, also time steps that each follow a write of this many MiB "
+                         "(evicting L2 and the 256 MB Infinity Cache); 0 skips it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -397,6 +400,24 @@ def main():
     roof = pass_roofline_us(wl)
     step_roof_frac = sum(roof.values()) / (ms * 1e3)
 
+    # cold caches: the inputs are still in HBM, but a large write between steps evicts them from
+    # L2 and the Infinity Cache first; each step is timed alone with events around it
+    cold = None
+    if args.cold_mib > 0 and graph is None:
+        flush = torch.empty(args.cold_mib << 18, dtype=torch.float32, device="cuda")
+        reps = 20
+        evc = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for i, (a, b) in enumerate(evc):
+            flush.fill_(float(i))
+            a.record()
+            step()
+            b.record()
+        torch.cuda.synchronize()
+        cold_us = sorted(a.elapsed_time(b) * 1e3 for a, b in evc)
+        cold = {"median_us": cold_us[reps // 2], "min_us": cold_us[0], "flush_mib": args.cold_mib,
+                "routed_tokens_per_s": wl.T / (cold_us[reps // 2] * 1e-6), "steps": reps}
+        del flush
+
     cpu = None if args.no_cpu_baseline else cpu_baseline(inp, args.cpu_budget)
     T = wl.T
     out = {
@@ -424,6 +445,7 @@ def main():
                      "per_launch": f"{amount:.4g} {unit}"},
         "step_roofline_frac": step_roof_frac,
         "pass_us": pass_us,
+        "cold_cache_step": cold,
         "pass_roofline_us": roof,
         "kernel_avg_us": kern_us,
         "cpu_baseline": cpu,
