@@ -31,15 +31,16 @@ __global__ __launch_bounds__(256) void k_collapse_fwd_f32(const float* __restric
     *reinterpret_cast<f32x4*>(out + b * H + c) = s * inv;
 }
 
+// One thread per (b, 16-byte column group): d_out[b] is read once and written to the N_H rows.
 __global__ __launch_bounds__(256) void k_collapse_bwd_f32(const float* __restrict__ dout, float* __restrict__ dx,
                                                           int64_t B, int NH, int H) {
     const int q = H / 4;
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over B * NH * q
-    if (i >= B * NH * q) return;
-    const int64_t row = i / q, c = (i % q) * 4;
-    const int64_t b = row / NH;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over B * q
+    if (i >= B * q) return;
+    const int64_t b = i / q, c = (i % q) * 4;
     const float inv = 1.0f / (float)NH;
-    *reinterpret_cast<f32x4*>(dx + row * H + c) = *reinterpret_cast<const f32x4*>(dout + b * H + c) * inv;
+    const f32x4 v = *reinterpret_cast<const f32x4*>(dout + b * H + c) * inv;
+    for (int h = 0; h < NH; ++h) *reinterpret_cast<f32x4*>(dx + (b * NH + h) * H + c) = v;
 }
 
 __global__ __launch_bounds__(256) void k_collapse_fwd_bf16(const uint16_t* __restrict__ x, uint16_t* __restrict__ out,
@@ -64,21 +65,20 @@ __global__ __launch_bounds__(256) void k_collapse_fwd_bf16(const uint16_t* __res
 __global__ __launch_bounds__(256) void k_collapse_bwd_bf16(const uint16_t* __restrict__ dout, uint16_t* __restrict__ dx,
                                                            int64_t B, int NH, int H) {
     const int q = H / 8;
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= B * NH * q) return;
-    const int64_t row = i / q, c = (i % q) * 8;
-    const int64_t b = row / NH;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over B * q
+    if (i >= B * q) return;
+    const int64_t b = i / q, c = (i % q) * 8;
     const float inv = 1.0f / (float)NH;
     const u16x8 v = *reinterpret_cast<const u16x8*>(dout + b * H + c);
     u16x8 o;
 #pragma unroll
     for (int j = 0; j < 8; ++j) o[j] = to_bf(bf(v[j]) * inv);
-    *reinterpret_cast<u16x8*>(dx + row * H + c) = o;
+    for (int h = 0; h < NH; ++h) *reinterpret_cast<u16x8*>(dx + (b * NH + h) * H + c) = o;
 }
 
 hipError_t launch_collapse(bool bwd, int act, const void* in, void* out, int64_t B, int NH, int H, hipStream_t s) {
     const int per = (act == 0) ? 4 : 8;
-    const int64_t n = (bwd ? B * NH : B) * (H / per);
+    const int64_t n = B * (H / per);  // one thread per (b, column group), both directions
     const dim3 grid((unsigned)((n + 255) / 256));
     if (act == 0) {
         if (bwd)
