@@ -15,13 +15,34 @@ template <int AB>  // A <= AB
 __global__ __launch_bounds__(256) void k_softmax_ce(const float* __restrict__ logits, const int* __restrict__ labels,
                                                     int64_t rows, int A, float invB, float* __restrict__ grad,
                                                     float* __restrict__ ce) {
-    __shared__ float tile[256 * AB];
+    __shared__ __attribute__((aligned(16))) float tile[256 * AB];
+    constexpr int NV = AB / 4;  // 16-byte pieces per thread (256 rows x AB floats at most)
     const int tid = threadIdx.x;
     const int64_t r0 = (int64_t)blockIdx.x * 256;
     const int nrows = (int)min((int64_t)256, rows - r0);
-    const int64_t base = r0 * A;
+    const int64_t base = r0 * A;  // a multiple of 4 (256 rows per block)
     const int n = nrows * A;
-    for (int i = tid; i < n; i += 256) tile[i] = logits[base + i];
+    // 16-byte sweeps when both arrays allow them (4-byte aligned pointers are accepted too)
+    const bool vec = ((((uintptr_t)logits) | ((uintptr_t)grad)) & 15) == 0;
+    const int n4 = vec ? n / 4 : 0;
+    // The block's logits are one contiguous range: every 16-byte load of the sweep goes out
+    // before the first LDS store (unconditional loads, an index past the range re-reads piece
+    // 0 and is not stored), then the rest one float at a time.
+    if (vec) {
+        const f32x4* src = reinterpret_cast<const f32x4*>(logits + base);
+        f32x4 v[NV];
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int q = tid + 256 * k;
+            v[k] = src[q < n4 ? q : 0];
+        }
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int q = tid + 256 * k;
+            if (q < n4) reinterpret_cast<f32x4*>(tile)[q] = v[k];
+        }
+    }
+    for (int i = 4 * n4 + tid; i < n; i += 256) tile[i] = logits[base + i];
     __syncthreads();
     if (tid < nrows) {
         float* z = tile + tid * A;
@@ -44,7 +65,15 @@ __global__ __launch_bounds__(256) void k_softmax_ce(const float* __restrict__ lo
         ce[r0 + tid] = valid ? -logf(fmaxf(p_lab, 1e-30f)) : 0.0f;
     }
     __syncthreads();
-    for (int i = tid; i < n; i += 256) grad[base + i] = tile[i];
+    if (vec) {
+        f32x4* dst = reinterpret_cast<f32x4*>(grad + base);
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int q = tid + 256 * k;
+            if (q < n4) dst[q] = reinterpret_cast<const f32x4*>(tile)[q];
+        }
+    }
+    for (int i = 4 * n4 + tid; i < n; i += 256) grad[base + i] = tile[i];
 }
 
 hipError_t launch_softmax_ce(const float* logits, const int32_t* labels, int64_t rows, int A, int64_t B, float* grad,

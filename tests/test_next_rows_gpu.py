@@ -136,6 +136,30 @@ def test_softmax_ce_parity(gpu_lib, B, NH, A):
         assert np.abs(g[~sentinel].sum(axis=-1)).max() * B < 1e-5
 
 
+@pytest.mark.parametrize("shift", [1, 2, 3])
+def test_softmax_ce_parity_unaligned(gpu_lib, shift):
+    """logits and grad 4-byte but not 16-byte aligned: the element-wise sweeps."""
+    import torch
+    import mixture_experts_top_amd as moe
+    B, NH, A = 300, 3, 21
+    rng = np.random.default_rng(shift)
+    z = (rng.standard_normal((B, NH, A)) * 3).astype(np.float32)
+    lab = rng.integers(0, A, size=(B, NH)).astype(np.int32)
+    lab.reshape(-1)[::5] = -1
+    zbuf = torch.zeros(B * NH * A + 4, device="cuda")
+    zbuf[shift:shift + B * NH * A] = torch.from_numpy(z.reshape(-1)).cuda()
+    gbuf = torch.full((B * NH * A + 4,), float("nan"), device="cuda")
+    zv = zbuf[shift:shift + B * NH * A].view(B, NH, A)
+    gv = gbuf[shift:shift + B * NH * A].view(B, NH, A)
+    assert zv.data_ptr() % 16 != 0 and gv.data_ptr() % 16 != 0
+    ce = torch.full((B, NH), float("nan"), device="cuda")
+    moe.moe_softmax_ce_grad(zv, torch.from_numpy(lab).cuda(), gv, ce)
+    rce, rgrad = N.softmax_ce(z, lab)
+    C.elementwise("ce", ce.cpu().numpy(), rce)
+    C.elementwise("grad * B", gv.cpu().numpy() * B, rgrad * B)
+    assert torch.isnan(gbuf[:shift]).all() and torch.isnan(gbuf[shift + B * NH * A:]).all(), "wrote outside grad"
+
+
 def test_softmax_ce_uniform_logits_give_log_21(gpu_lib):
     import torch
     import mixture_experts_top_amd as moe
