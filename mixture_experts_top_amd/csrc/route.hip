@@ -14,35 +14,6 @@
 
 namespace moe {
 
-__device__ __forceinline__ int argmax_row(const float* __restrict__ g, int NE) {
-    float best = g[0];
-    int e_best = 0;
-    for (int e = 1; e < NE; ++e) {
-        float v = g[e];
-        if (v > best) { best = v; e_best = e; }
-    }
-    return e_best;
-}
-
-__device__ __forceinline__ int argmax_row4(const float* __restrict__ g, int NE) {
-    // NE % 4 == 0 and the row is 16-byte aligned.
-    const f32x4* g4 = reinterpret_cast<const f32x4*>(g);
-    f32x4 v = g4[0];
-    float best = v.x;
-    int e_best = 0;
-    if (v.y > best) { best = v.y; e_best = 1; }
-    if (v.z > best) { best = v.z; e_best = 2; }
-    if (v.w > best) { best = v.w; e_best = 3; }
-    for (int q = 1; q < NE / 4; ++q) {
-        v = g4[q];
-        if (v.x > best) { best = v.x; e_best = 4 * q; }
-        if (v.y > best) { best = v.y; e_best = 4 * q + 1; }
-        if (v.z > best) { best = v.z; e_best = 4 * q + 2; }
-        if (v.w > best) { best = v.w; e_best = 4 * q + 3; }
-    }
-    return e_best;
-}
-
 // Ranks each lane's expert among the lanes of its wave with the same expert.
 // Returns the rank (number of lower lanes with the same expert); for every expert that
 // occurs, the lowest such lane stores the wave's count into cnt[e].
@@ -63,28 +34,35 @@ __device__ __forceinline__ int wave_rank(int e, int* cnt /* nullable */) {
     return rank;
 }
 
-// One block: tokens [blk*1024, blk*1024+1024).  Writes expert_idx (if non-null) and the
-// block's histogram hist[blk, :].
+// One block: tokens [blk*256, blk*256+256), one per thread.  Writes expert_idx (if non-null)
+// and the block's histogram hist[blk, :].  The token's logits are loaded all at once
+// (aux_load_logits: no load waits on another), then scanned in registers.
+template <int NEB>
 __global__ __launch_bounds__(kRouteThreads) void k_route(const float* __restrict__ G, int T, int NE,
                                                          int* __restrict__ idx_out,
                                                          int* __restrict__ hist) {
+    static_assert(kRouteThreads == kRouteTokens && kRouteGroups == kRouteThreads / 64, "one token per thread");
     __shared__ int cnt[kRouteGroups][kMaxExperts];
     const int tid = threadIdx.x;
     for (int i = tid; i < kRouteGroups * kMaxExperts; i += kRouteThreads) (&cnt[0][0])[i] = 0;
+    const int64_t t = (int64_t)blockIdx.x * kRouteTokens + tid;
+    float g[NEB];
+    aux_load_logits<NEB>(G, t, T, NE, g);
     __syncthreads();
-    const int wave = tid / 64, lane = tid % 64;
-    const int64_t base = (int64_t)blockIdx.x * kRouteTokens;
-    const bool vec = (NE % 4) == 0;
-    for (int g = wave; g < kRouteGroups; g += kRouteThreads / 64) {
-        const int64_t t = base + g * 64 + lane;
-        int e = -1;
-        if (t < T) {
-            const float* row = G + t * NE;
-            e = vec ? argmax_row4(row, NE) : argmax_row(row, NE);
-            if (idx_out) idx_out[t] = e;
-        }
-        wave_rank(e, cnt[g]);
+    int e = -1;
+    if (t < T) {
+        // strict ">" upward from expert 0: the lowest index among equal maxima
+        float best = g[0];
+        e = 0;
+#pragma unroll
+        for (int x = 1; x < NEB; ++x)
+            if (x < NE && g[x] > best) {
+                best = g[x];
+                e = x;
+            }
+        if (idx_out) idx_out[t] = e;
     }
+    wave_rank(e, cnt[tid / 64]);
     __syncthreads();
     if (tid < NE) {
         int s = 0;
@@ -116,7 +94,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_part(const float* __res
 #pragma unroll
     for (int x = 0; x < NEB; ++x) psum[x] = 0.0f;
     if (t < T) {
-        // strict ">" upward from expert 0, as argmax_row: the lowest index among equal maxima
+        // strict ">" upward from expert 0: the lowest index among equal maxima
         float best = g[0];
         e = 0;
 #pragma unroll
@@ -320,7 +298,17 @@ hipError_t launch_scatter_scan(const int32_t* idx, int64_t T, int NE, const int3
 
 hipError_t launch_route(const float* G, int64_t T, int NE, int32_t* idx, int32_t* hist, int n_rblk,
                         hipStream_t s) {
-    launch_kernel(k_route, dim3(n_rblk), dim3(kRouteThreads), 0, s, G, (int)T, NE, idx, hist);
+    const dim3 grid(n_rblk), block(kRouteThreads);
+    if (NE <= 4)
+        launch_kernel(k_route<4>, grid, block, 0, s, G, (int)T, NE, idx, hist);
+    else if (NE <= 8)
+        launch_kernel(k_route<8>, grid, block, 0, s, G, (int)T, NE, idx, hist);
+    else if (NE <= 16)
+        launch_kernel(k_route<16>, grid, block, 0, s, G, (int)T, NE, idx, hist);
+    else if (NE <= 32)
+        launch_kernel(k_route<32>, grid, block, 0, s, G, (int)T, NE, idx, hist);
+    else
+        launch_kernel(k_route<64>, grid, block, 0, s, G, (int)T, NE, idx, hist);
     return hipGetLastError();
 }
 
