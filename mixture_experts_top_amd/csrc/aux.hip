@@ -22,16 +22,16 @@ __global__ __launch_bounds__(kAuxThreads) void k_aux_rows(const float* __restric
                                                           float* __restrict__ probs,
                                                           float* __restrict__ part) {
     __shared__ float red[kAuxThreads / 64][NEB];
+    __shared__ float sfrac[NEB];
     static_assert(kAuxTokens == kAuxThreads, "one token per thread");
-    const int64_t t = (int64_t)blockIdx.x * kAuxTokens + threadIdx.x;
+    const int tid = threadIdx.x;
+    const int64_t t = (int64_t)blockIdx.x * kAuxTokens + tid;
     float g[NEB];
     aux_load_logits<NEB>(G, t, T, NE, g);
-    int cnt[NEB];
-#pragma unroll
-    for (int e = 0; e < NEB; ++e) cnt[e] = counts[e < NE ? e : 0];
+    const int cnt_mine = counts[tid < NE ? tid : 0];  // entries past N_E are unused
     const float lam = lam_dev ? lam_dev[0] : lam_value;
     float frac[NEB], psum[NEB];
-    aux_frac<NEB>(cnt, T, frac);
+    aux_frac_table<NEB>(cnt_mine, T, sfrac, frac);
 #pragma unroll
     for (int e = 0; e < NEB; ++e) psum[e] = 0.0f;
     if (t < T) {

@@ -51,11 +51,18 @@ __device__ __forceinline__ void aux_softmax(const float (&g)[NEB], int NE, float
     for (int e = 0; e < NEB; ++e) p[e] = z[e] / S;
 }
 
-// frac[e] = counts[e] / T (in double, rounded once); entries past N_E are unused.
+// frac_e = count_e / T (in double, rounded once).
+__device__ __forceinline__ float aux_frac_of(int count, int64_t T) { return (float)((double)count / (double)T); }
+
+// Every thread's frac[0 .. NEB) from a per-workgroup table: threads e < NEB form entry e
+// from count_mine (their expert's count; entries past N_E are unused) once, instead of every
+// thread dividing in double N_E times.  Contains a barrier: every thread calls it.
 template <int NEB>
-__device__ __forceinline__ void aux_frac(const int (&cnt)[NEB], int64_t T, float (&frac)[NEB]) {
+__device__ __forceinline__ void aux_frac_table(int count_mine, int64_t T, float* sfrac, float (&frac)[NEB]) {
+    if ((int)threadIdx.x < NEB) sfrac[threadIdx.x] = aux_frac_of(count_mine, T);
+    __syncthreads();
 #pragma unroll
-    for (int e = 0; e < NEB; ++e) frac[e] = (float)((double)cnt[e] / (double)T);
+    for (int e = 0; e < NEB; ++e) frac[e] = sfrac[e];
 }
 
 __device__ __forceinline__ float aux_coef(float lam, int NE, int64_t T) {
@@ -135,7 +142,7 @@ __device__ __forceinline__ void aux_final_block(const float* __restrict__ part, 
         float tot = 0.0f;
         for (int q = 0; q < S; ++q) tot += acc[q * nep + tid];
         const float m = (float)((double)tot / (double)T);
-        const float f = (float)((double)count_mine / (double)T);
+        const float f = aux_frac_of(count_mine, T);
         mp[tid] = m;
         fr[tid] = f;
         if (mean_prob_out) mean_prob_out[tid] = m;

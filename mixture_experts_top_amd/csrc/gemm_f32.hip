@@ -962,11 +962,8 @@ __device__ __forceinline__ void aux_in_forward(char* smem, int r, const int* __r
     hist_counts_lds(hs, tot, hist, nblk, NE);
     const float lam = ax.lam_dev ? ax.lam_dev[0] : ax.lam;
     if (r < ax.n_ablk) {
-        int cnt[NEB];
-#pragma unroll
-        for (int e = 0; e < NEB; ++e) cnt[e] = tot[e < NE ? e : 0];
         float frac[NEB];
-        aux_frac<NEB>(cnt, T, frac);
+        aux_frac_table<NEB>(tot[(int)threadIdx.x < NE ? threadIdx.x : 0], T, fr, frac);
         if (t < T) {
             float p[NEB];
             aux_softmax<NEB>(g, NE, p);
