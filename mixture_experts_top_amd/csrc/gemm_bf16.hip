@@ -36,6 +36,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+// two values at once with v_cvt_pk_bf16_f32 (nearest even, the same bits as f32_to_bf16 for
+// every non-NaN input); lo goes to the lower half
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v){lo, hi}, bf16x2v));
+}
 
 __device__ __forceinline__ u16x8 ld8(const uint16_t* p) { return *reinterpret_cast<const u16x8*>(p); }
 __device__ __forceinline__ void st8(uint16_t* p, u16x8 v) { *reinterpret_cast<u16x8*>(p) = v; }
@@ -234,10 +242,14 @@ __device__ __forceinline__ void rows_bf16_body(char* smem, int bid, const uint16
             const float* src = &St[q * RPS + tid / CPR][8 * c8];
             const f32x4 v0 = *reinterpret_cast<const f32x4*>(src), v1 = *reinterpret_cast<const f32x4*>(src + 4);
             const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-            u16x8 o;
+            u32x4v pk;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) o[u] = f32_to_bf16(acc_dx ? bf16_to_f32(old[q][u]) + v[u] : v[u]);
-            if (tk[q] >= 0) st8(Out + (size_t)tk[q] * H + n0 + 8 * c8, o);
+            for (int u = 0; u < 4; ++u) {
+                const float a = acc_dx ? bf16_to_f32(old[q][2 * u]) + v[2 * u] : v[2 * u];
+                const float b = acc_dx ? bf16_to_f32(old[q][2 * u + 1]) + v[2 * u + 1] : v[2 * u + 1];
+                pk[u] = pack_bf16x2(a, b);
+            }
+            if (tk[q] >= 0) st8(Out + (size_t)tk[q] * H + n0 + 8 * c8, __builtin_bit_cast(u16x8, pk));
         }
         return;
     }
