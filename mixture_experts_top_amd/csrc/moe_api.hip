@@ -240,6 +240,23 @@ moe_status_t moe_top1_route(const float* gate_logits, int32_t* expert_idx, int32
                     (hipStream_t)stream);
 }
 
+// The forward GEMM once routing has formed offsets and perm.
+static moe_status_t fwd_gemm_only(const void* fused_ctx, const void* W, const float* b, void* routed_ctx,
+                                  const int32_t* expert_offsets, const int32_t* perm, const Plan& p, int act,
+                                  hipStream_t s) {
+    if (act == MOE_DTYPE_F32)
+        LAUNCH(K_FWD_GEMM,
+               launch_fwd_gemm_f32((const float*)fused_ctx, (const float*)W, b, (float*)routed_ctx,
+                                   expert_offsets, perm, p.T, p.H, p.NE, s),
+               "fwd gemm");
+    else
+        LAUNCH(K_FWD_GEMM,
+               launch_fwd_gemm_bf16((const uint16_t*)fused_ctx, (const uint16_t*)W, b, (uint16_t*)routed_ctx,
+                                    expert_offsets, perm, p.T, p.H, p.NE, s),
+               "fwd gemm");
+    return MOE_OK;
+}
+
 moe_status_t moe_top1_fwd(const void* fused_ctx, const float* gate_logits, const void* W, const float* b,
                           void* routed_ctx, int32_t* expert_idx, int32_t* expert_counts,
                           int32_t* expert_offsets, int32_t* perm, int64_t B, int64_t NH, int64_t H,
@@ -265,17 +282,7 @@ moe_status_t moe_top1_fwd(const void* fused_ctx, const float* gate_logits, const
     }
     if ((st = do_route(gate_logits, expert_idx, expert_counts, expert_offsets, perm, p, workspace, s)) != MOE_OK)
         return st;
-    if (act == MOE_DTYPE_F32)
-        LAUNCH(K_FWD_GEMM,
-               launch_fwd_gemm_f32((const float*)fused_ctx, (const float*)W, b, (float*)routed_ctx,
-                                   expert_offsets, perm, p.T, p.H, p.NE, s),
-               "fwd gemm");
-    else
-        LAUNCH(K_FWD_GEMM,
-               launch_fwd_gemm_bf16((const uint16_t*)fused_ctx, (const uint16_t*)W, b, (uint16_t*)routed_ctx,
-                                    expert_offsets, perm, p.T, p.H, p.NE, s),
-               "fwd gemm");
-    return MOE_OK;
+    return fwd_gemm_only(fused_ctx, W, b, routed_ctx, expert_offsets, perm, p, act, s);
 }
 
 static moe_status_t bwd_impl(const char* fn, const void* dy, int from_mean, const void* fused_ctx, const void* W,
@@ -417,6 +424,28 @@ moe_status_t moe_top1_fwd_aux(const void* fused_ctx, const float* gate_logits, c
                                           s),
                "fwd gemm + aux");
         return MOE_OK;
+    }
+    if (NE <= kAuxFwdMaxExperts) {
+        // routing with the softmax column sums, then the scatter (which knows the final counts)
+        // with dG and, in one extra block, the loss; then the forward GEMM alone
+        int32_t* hist = at<int32_t>(workspace, p.off_hist);
+        int32_t* blkbase = at<int32_t>(workspace, p.off_blkbase);
+        float* part = at<float>(workspace, p.off_paux);
+        LAUNCH(K_ROUTE, launch_route_part(gate_logits, p.T, p.NE, expert_idx, hist, part, p.n_rblk, s), "route");
+        const AuxFwdArgs ax = {gate_logits, part, lambda, lambda_dev, d_gate_logits, probs, loss, frac, mean_prob,
+                               p.n_ablk};
+        if (scatter_scan_fits(p.n_rblk, p.NE)) {
+            LAUNCH(K_SCATTER,
+                   launch_scatter_scan_aux(expert_idx, p.T, p.NE, hist, p.n_rblk, expert_counts, expert_offsets, perm,
+                                           ax, s),
+                   "scatter+scan + aux");
+        } else {
+            LAUNCH(K_SCAN, launch_scan(hist, p.n_rblk, p.NE, blkbase, expert_counts, expert_offsets, s), "scan");
+            LAUNCH(K_SCATTER,
+                   launch_scatter_aux(expert_idx, p.T, p.NE, blkbase, perm, expert_counts, p.n_rblk, ax, s),
+                   "scatter + aux");
+        }
+        return fwd_gemm_only(fused_ctx, W, b, routed_ctx, expert_offsets, perm, p, act, s);
     }
     st = moe_top1_fwd(fused_ctx, gate_logits, W, b, routed_ctx, expert_idx, expert_counts, expert_offsets, perm, B, NH,
                       H, NE, act, workspace, workspace_bytes, stream);

@@ -172,21 +172,8 @@ inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint3
 }
 
 // ---- launchers (each returns the hipError_t of its launch) ----
-hipError_t launch_route_part(const float* G, int64_t T, int NE, int32_t* idx, int32_t* hist, float* part,
-                             int n_rblk, hipStream_t s);
-hipError_t launch_route(const float* G, int64_t T, int NE, int32_t* idx, int32_t* hist,
-                        int n_rblk, hipStream_t s);
-bool scatter_scan_fits(int n_rblk, int NE);
-hipError_t launch_scatter_scan(const int32_t* idx, int64_t T, int NE, const int32_t* hist, int n_rblk,
-                               int32_t* counts, int32_t* offsets, int32_t* perm, hipStream_t s);
-hipError_t launch_scan(const int32_t* hist, int n_rblk, int NE, int32_t* blkbase,
-                       int32_t* counts, int32_t* offsets, hipStream_t s);
-hipError_t launch_scatter(const int32_t* idx, int64_t T, int NE, const int32_t* blkbase,
-                          int32_t* perm, int n_rblk, hipStream_t s);
-
-// The load-balancing loss carried by the small-T forward launch (N_E <= kAuxFwdMaxExperts):
-// part holds the routing kernel's softmax column sums, one row per routing block.
-constexpr int kAuxFwdMaxExperts = 8;
+// The aux loss riding on the routing and forward launches: inputs, lambda and outputs of
+// moe_aux_loss, plus the softmax column sums that k_route_part wrote (one row per 256-token block).
 struct AuxFwdArgs {
     const float* G;
     const float* part;
@@ -199,6 +186,27 @@ struct AuxFwdArgs {
     float* mean_prob;
     int n_ablk;
 };
+hipError_t launch_route_part(const float* G, int64_t T, int NE, int32_t* idx, int32_t* hist, float* part,
+                             int n_rblk, hipStream_t s);
+hipError_t launch_route(const float* G, int64_t T, int NE, int32_t* idx, int32_t* hist,
+                        int n_rblk, hipStream_t s);
+bool scatter_scan_fits(int n_rblk, int NE);
+hipError_t launch_scatter_scan(const int32_t* idx, int64_t T, int NE, const int32_t* hist, int n_rblk,
+                               int32_t* counts, int32_t* offsets, int32_t* perm, hipStream_t s);
+hipError_t launch_scatter_scan_aux(const int32_t* idx, int64_t T, int NE, const int32_t* hist, int n_rblk,
+                                   int32_t* counts, int32_t* offsets, int32_t* perm, const AuxFwdArgs& ax,
+                                   hipStream_t s);
+hipError_t launch_scatter_aux(const int32_t* idx, int64_t T, int NE, const int32_t* blkbase, int32_t* perm,
+                              const int32_t* counts, int n_rblk, const AuxFwdArgs& ax, hipStream_t s);
+hipError_t launch_scan(const int32_t* hist, int n_rblk, int NE, int32_t* blkbase,
+                       int32_t* counts, int32_t* offsets, hipStream_t s);
+hipError_t launch_scatter(const int32_t* idx, int64_t T, int NE, const int32_t* blkbase,
+                          int32_t* perm, int n_rblk, hipStream_t s);
+
+// The load-balancing loss carried by the small-T forward launch (N_E <= kAuxFwdMaxExperts):
+// part holds the routing kernel's softmax column sums, one row per routing block.
+constexpr int kAuxFwdMaxExperts = 8;
+
 bool fwd_gemm_f32_gather_fits(int64_t T, int H, int NE, int n_rblk);
 hipError_t launch_fwd_gemm_f32_gather(const float* X, const float* W, const float* bias, float* Y,
                                       const int32_t* idx, const int32_t* hist, int n_rblk, int32_t* counts,

@@ -169,20 +169,61 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(const int* __restrict__ h
     }
 }
 
+// The aux loss riding on a scatter launch (NEB > 0): the counts are final there, so each
+// scatter block also writes dG (and probs) for its 256 tokens -- the tokens of k_aux_rows'
+// block of the same index, with the same arithmetic (aux_math.hpp) -- and one extra block
+// (blockIdx.x == nblk) forms mean_prob, frac and the loss from the column sums that
+// k_route_part wrote in the launch before, as k_aux_final does.
+template <int NEB>
+__device__ __forceinline__ void scatter_aux_rows(const AuxFwdArgs& ax, const float (&g)[NEB], int count_mine,
+                                                 int64_t t, int T, int NE, float* sfrac) {
+    const float lam = ax.lam_dev ? ax.lam_dev[0] : ax.lam;
+    float frac[NEB];
+    aux_frac_table<NEB>(count_mine, T, sfrac, frac);  // contains a barrier
+    if (t < T) {
+        float p[NEB];
+        aux_softmax<NEB>(g, NE, p);
+        aux_grad_row<NEB>(p, frac, aux_coef(lam, NE, T), NE, t, ax.dG, ax.probs);
+    }
+}
+__device__ __forceinline__ void scatter_aux_final(const AuxFwdArgs& ax, int count_mine, int T, int NE) {
+    __shared__ float acc[256];
+    __shared__ float mp[kMaxExperts], fr[kMaxExperts];
+    static_assert(kRouteThreads == 256, "aux_final_block runs on 256 threads");
+    const float lam = ax.lam_dev ? ax.lam_dev[0] : ax.lam;
+    aux_final_block(ax.part, count_mine, ax.n_ablk, T, NE, lam, ax.loss, ax.frac, ax.mean_prob, acc, mp, fr);
+}
+
 // Same block decomposition as k_route.  Recomputes the in-block ranks from expert_idx
-// and writes perm[blkbase[blk, e] + rank] = t.
+// and writes perm[blkbase[blk, e] + rank] = t.  With NEB > 0 it also runs the aux rows
+// (counts from k_scan, final by then) and, in block nblk, the aux final.
+template <int NEB>
 __global__ __launch_bounds__(kRouteThreads) void k_scatter(const int* __restrict__ idx, int T, int NE,
                                                            const int* __restrict__ blkbase,
-                                                           int* __restrict__ perm) {
+                                                           int* __restrict__ perm, const int* __restrict__ counts,
+                                                           AuxFwdArgs ax) {
     __shared__ int cnt[kRouteGroups][kMaxExperts];
     __shared__ int bb[kMaxExperts];
     const int tid = threadIdx.x;
+    const int nblk = (int)gridDim.x - (NEB > 0 ? 1 : 0);
+    if constexpr (NEB > 0) {
+        if ((int)blockIdx.x == nblk) {
+            scatter_aux_final(ax, tid < NE ? counts[tid] : 0, T, NE);
+            return;
+        }
+    }
     for (int i = tid; i < kRouteGroups * kMaxExperts; i += kRouteThreads) (&cnt[0][0])[i] = 0;
     if (tid < NE) bb[tid] = blkbase[(int64_t)blockIdx.x * NE + tid];
     __syncthreads();
     const int wave = tid / 64, lane = tid % 64;
     const int64_t base = (int64_t)blockIdx.x * kRouteTokens;
     constexpr int GPW = kRouteGroups / (kRouteThreads / 64);  // groups per wave
+    float gl[NEB > 0 ? NEB : 1];
+    int cmine = 0;
+    if constexpr (NEB > 0) {  // this thread's token (one per thread, as in k_aux_rows) and counts
+        aux_load_logits<NEB>(ax.G, base + tid, T, NE, gl);
+        cmine = counts[tid < NE ? tid : 0];
+    }
     int my_e[GPW], my_rank[GPW];
 #pragma unroll
     for (int j = 0; j < GPW; ++j) {
@@ -212,6 +253,10 @@ __global__ __launch_bounds__(kRouteThreads) void k_scatter(const int* __restrict
             perm[bb[e] + cnt[g][e] + my_rank[j]] = (int)t;
         }
     }
+    if constexpr (NEB > 0) {
+        __shared__ float sfrac[NEB];
+        scatter_aux_rows<NEB>(ax, gl, cmine, base + tid, T, NE, sfrac);
+    }
 }
 
 // Scatter with the scan folded in, for small histograms (n_blk x N_E entries): every block
@@ -219,19 +264,25 @@ __global__ __launch_bounds__(kRouteThreads) void k_scatter(const int* __restrict
 // own base), so routing is two launches.  Block 0 writes counts and offsets.
 static_assert(kRouteGroups == kRouteThreads / 64, "one 64-token group per wavefront");
 
+// With NEB > 0 the aux rows ride on it too (see scatter_aux_rows), and block nblk sums the
+// histogram like the others, then runs the aux final.
+template <int NEB>
 __global__ __launch_bounds__(kRouteThreads) void k_scatter_scan(const int* __restrict__ idx, int T, int NE,
                                                                 const int* __restrict__ hist, int nblk,
                                                                 int* __restrict__ counts, int* __restrict__ offsets,
-                                                                int* __restrict__ perm) {
+                                                                int* __restrict__ perm, AuxFwdArgs ax) {
     __shared__ int cnt[kRouteGroups][kMaxExperts];
     __shared__ int part[2][kRouteThreads];
     __shared__ int bb[kMaxExperts];
     const int tid = threadIdx.x;
     const int b = blockIdx.x;
+    const bool final_blk = NEB > 0 && b == nblk;
     // this thread's token's expert: its load goes out first, with the histogram loads behind it
     const int wave = tid / 64, lane = tid % 64;
     const int64_t t = (int64_t)b * kRouteTokens + wave * 64 + lane;
-    const int e = (t < T) ? idx[t] : -1;
+    const int e = (t < T && !final_blk) ? idx[t] : -1;
+    float gl[NEB > 0 ? NEB : 1];
+    if constexpr (NEB > 0) aux_load_logits<NEB>(ax.G, (int64_t)b * kRouteTokens + tid, T, NE, gl);
     int nep = 1;
     while (nep < NE) nep <<= 1;
     const int S = kRouteThreads / nep;
@@ -273,6 +324,12 @@ __global__ __launch_bounds__(kRouteThreads) void k_scatter_scan(const int* __res
         if (b == 0) offsets[NE] = acc;
     }
     __syncthreads();
+    if constexpr (NEB > 0) {
+        if (final_blk) {  // the totals of every expert are in part[0][0 .. N_E)
+            scatter_aux_final(ax, tid < NE ? part[0][tid] : 0, T, NE);
+            return;
+        }
+    }
     const int r = wave_rank(e, cnt[wave]);
     __syncthreads();
     if (tid < NE) {
@@ -285,14 +342,31 @@ __global__ __launch_bounds__(kRouteThreads) void k_scatter_scan(const int* __res
     }
     __syncthreads();
     if (e >= 0) perm[bb[e] + cnt[wave][e] + r] = (int)t;
+    if constexpr (NEB > 0) {
+        __shared__ float sfrac[NEB];
+        scatter_aux_rows<NEB>(ax, gl, part[0][tid < NE ? tid : 0], (int64_t)b * kRouteTokens + tid, T, NE, sfrac);
+    }
 }
 
 bool scatter_scan_fits(int n_rblk, int NE) { return (int64_t)n_rblk * NE <= 4096; }
 
 hipError_t launch_scatter_scan(const int32_t* idx, int64_t T, int NE, const int32_t* hist, int n_rblk,
                                int32_t* counts, int32_t* offsets, int32_t* perm, hipStream_t s) {
-    launch_kernel(k_scatter_scan, dim3(n_rblk), dim3(kRouteThreads), 0, s, idx, (int)T, NE, hist, n_rblk, counts,
-                       offsets, perm);
+    launch_kernel(k_scatter_scan<0>, dim3(n_rblk), dim3(kRouteThreads), 0, s, idx, (int)T, NE, hist, n_rblk,
+                  counts, offsets, perm, AuxFwdArgs{});
+    return hipGetLastError();
+}
+
+hipError_t launch_scatter_scan_aux(const int32_t* idx, int64_t T, int NE, const int32_t* hist, int n_rblk,
+                                   int32_t* counts, int32_t* offsets, int32_t* perm, const AuxFwdArgs& ax,
+                                   hipStream_t s) {
+    const dim3 grid(n_rblk + 1), block(kRouteThreads);
+    if (NE <= 4)
+        launch_kernel(k_scatter_scan<4>, grid, block, 0, s, idx, (int)T, NE, hist, n_rblk, counts, offsets, perm, ax);
+    else if (NE <= 8)
+        launch_kernel(k_scatter_scan<8>, grid, block, 0, s, idx, (int)T, NE, hist, n_rblk, counts, offsets, perm, ax);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
@@ -332,8 +406,20 @@ hipError_t launch_scan(const int32_t* hist, int n_rblk, int NE, int32_t* blkbase
 
 hipError_t launch_scatter(const int32_t* idx, int64_t T, int NE, const int32_t* blkbase, int32_t* perm,
                           int n_rblk, hipStream_t s) {
-    launch_kernel(k_scatter, dim3(n_rblk), dim3(kRouteThreads), 0, s, idx, (int)T, NE, blkbase,
-                       perm);
+    launch_kernel(k_scatter<0>, dim3(n_rblk), dim3(kRouteThreads), 0, s, idx, (int)T, NE, blkbase, perm,
+                  (const int*)nullptr, AuxFwdArgs{});
+    return hipGetLastError();
+}
+
+hipError_t launch_scatter_aux(const int32_t* idx, int64_t T, int NE, const int32_t* blkbase, int32_t* perm,
+                              const int32_t* counts, int n_rblk, const AuxFwdArgs& ax, hipStream_t s) {
+    const dim3 grid(n_rblk + 1), block(kRouteThreads);
+    if (NE <= 4)
+        launch_kernel(k_scatter<4>, grid, block, 0, s, idx, (int)T, NE, blkbase, perm, counts, ax);
+    else if (NE <= 8)
+        launch_kernel(k_scatter<8>, grid, block, 0, s, idx, (int)T, NE, blkbase, perm, counts, ax);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

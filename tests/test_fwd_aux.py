@@ -1,7 +1,8 @@
 """moe_top1_fwd_aux against the calls it stands for: moe_top1_fwd followed by moe_aux_loss
 (or moe_aux_loss_lambda_dev) must give the same bits on every output, on the shapes where
-the loss rides on the routing and forward launches (fp32, N_E <= 8, small T) and on those
-where the library makes the calls one by one.  Parity of the one-call path with the oracle
+the loss rides on the routing and forward launches (fp32, N_E <= 8, small T), on the routing
+and scatter launches (N_E <= 8 otherwise), and on those where the library makes the calls
+one by one (N_E > 8).  Parity of the one-call path with the oracle
 is checked by test_parity (its step uses this call)."""
 import numpy as np
 import pytest
@@ -22,10 +23,15 @@ CASES = {
     "empty_expert": workloads.custom(64, 5, 128, 4, gate_bias={2: -1.0e4}),
     "multiblock_H64_NE8": workloads.custom(8191, 5, 64, 8),
     "NE7_int_ties": workloads.custom(80, 5, 256, 7, gate="int"),
-    # shapes where the calls run one by one
+    # shapes where the loss rides on the routing launches (N_E <= 8): scatter with the scan
+    # folded in, and separate scan + scatter (n_blk x N_E > 4096), fp32 and bf16
     "large_T": workloads.workload(3),
-    "NE16": workloads.custom(200, 5, 128, 16),
+    "scan_scatter_NE8": workloads.custom(28000, 5, 128, 8),
+    "scan_scatter_NE3_ragged": workloads.custom(70001, 5, 64, 3, gate_bias={1: -1.0e4}),
     "bf16": workloads.custom(200, 5, 128, 4, act="bf16"),
+    "bf16_H256_NE5": workloads.custom(3001, 5, 256, 5, act="bf16"),
+    # shapes where the calls run one by one
+    "NE16": workloads.custom(200, 5, 128, 16),
 }
 KEYS = ("y", "idx", "counts", "offsets", "perm", "loss", "dg", "frac", "mean_prob", "probs")
 
@@ -59,7 +65,7 @@ def test_fwd_aux_equals_separate_calls(gpu_lib, name):
     assert np.isfinite(b["loss"]).all() and np.isfinite(b["dg"]).all()
 
 
-@pytest.mark.parametrize("name", ["pages_shape", "ragged_H128_NE3", "large_T"])
+@pytest.mark.parametrize("name", ["pages_shape", "ragged_H128_NE3", "large_T", "scan_scatter_NE8", "bf16"])
 def test_fwd_aux_lambda_dev(gpu_lib, name):
     import torch
     import mixture_experts_top_amd as moe
