@@ -189,7 +189,9 @@ moe_status_t moe_aux_loss_lambda_dev(const float* gate_logits, const int32_t* ex
  * `lambda` is then ignored) on the expert_counts just written -- bit for bit, whichever
  * way the library schedules the work.  For fp32 activations, N_E <= 8 and small T the
  * softmax column sums ride on the routing launch and dG / frac / mean_prob / loss on the
- * forward GEMM launch (two launches in all); otherwise the calls run one after the other.
+ * forward GEMM launch (two launches in all); otherwise, for N_E <= 16, the column sums ride
+ * on the routing launch and dG / frac / mean_prob / loss on the scatter launch that forms
+ * perm; for N_E > 16 the calls run one after the other.
  * Workspace as moe_top1_fwd.  Errors as moe_top1_fwd and moe_aux_loss; lambda_dev, when
  * given, must be 4-byte aligned.
  */

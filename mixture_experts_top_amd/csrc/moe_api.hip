@@ -425,7 +425,7 @@ moe_status_t moe_top1_fwd_aux(const void* fused_ctx, const float* gate_logits, c
                "fwd gemm + aux");
         return MOE_OK;
     }
-    if (NE <= kAuxFwdMaxExperts) {
+    if (NE <= kAuxScatterMaxExperts) {
         // routing with the softmax column sums, then the scatter (which knows the final counts)
         // with dG and, in one extra block, the loss; then the forward GEMM alone
         int32_t* hist = at<int32_t>(workspace, p.off_hist);

@@ -205,7 +205,8 @@ hipError_t launch_scatter(const int32_t* idx, int64_t T, int NE, const int32_t* 
 
 // The load-balancing loss carried by the small-T forward launch (N_E <= kAuxFwdMaxExperts):
 // part holds the routing kernel's softmax column sums, one row per routing block.
-constexpr int kAuxFwdMaxExperts = 8;
+constexpr int kAuxFwdMaxExperts = 8;      // aux carried by the one-pass forward GEMM
+constexpr int kAuxScatterMaxExperts = 16;  // aux carried by the routing and scatter launches
 
 bool fwd_gemm_f32_gather_fits(int64_t T, int H, int NE, int n_rblk);
 hipError_t launch_fwd_gemm_f32_gather(const float* X, const float* W, const float* bias, float* Y,

@@ -365,6 +365,8 @@ hipError_t launch_scatter_scan_aux(const int32_t* idx, int64_t T, int NE, const 
         launch_kernel(k_scatter_scan<4>, grid, block, 0, s, idx, (int)T, NE, hist, n_rblk, counts, offsets, perm, ax);
     else if (NE <= 8)
         launch_kernel(k_scatter_scan<8>, grid, block, 0, s, idx, (int)T, NE, hist, n_rblk, counts, offsets, perm, ax);
+    else if (NE <= 16)
+        launch_kernel(k_scatter_scan<16>, grid, block, 0, s, idx, (int)T, NE, hist, n_rblk, counts, offsets, perm, ax);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
@@ -392,6 +394,8 @@ hipError_t launch_route_part(const float* G, int64_t T, int NE, int32_t* idx, in
         launch_kernel(k_route_part<4>, dim3(n_rblk), dim3(kRouteThreads), 0, s, G, (int)T, NE, idx, hist, part);
     else if (NE <= 8)
         launch_kernel(k_route_part<8>, dim3(n_rblk), dim3(kRouteThreads), 0, s, G, (int)T, NE, idx, hist, part);
+    else if (NE <= 16)
+        launch_kernel(k_route_part<16>, dim3(n_rblk), dim3(kRouteThreads), 0, s, G, (int)T, NE, idx, hist, part);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
@@ -418,6 +422,8 @@ hipError_t launch_scatter_aux(const int32_t* idx, int64_t T, int NE, const int32
         launch_kernel(k_scatter<4>, grid, block, 0, s, idx, (int)T, NE, blkbase, perm, counts, ax);
     else if (NE <= 8)
         launch_kernel(k_scatter<8>, grid, block, 0, s, idx, (int)T, NE, blkbase, perm, counts, ax);
+    else if (NE <= 16)
+        launch_kernel(k_scatter<16>, grid, block, 0, s, idx, (int)T, NE, blkbase, perm, counts, ax);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -1,8 +1,8 @@
 """moe_top1_fwd_aux against the calls it stands for: moe_top1_fwd followed by moe_aux_loss
 (or moe_aux_loss_lambda_dev) must give the same bits on every output, on the shapes where
 the loss rides on the routing and forward launches (fp32, N_E <= 8, small T), on the routing
-and scatter launches (N_E <= 8 otherwise), and on those where the library makes the calls
-one by one (N_E > 8).  Parity of the one-call path with the oracle
+and scatter launches (N_E <= 16 otherwise), and on those where the library makes the calls
+one by one (N_E > 16).  Parity of the one-call path with the oracle
 is checked by test_parity (its step uses this call)."""
 import numpy as np
 import pytest
@@ -30,8 +30,10 @@ CASES = {
     "scan_scatter_NE3_ragged": workloads.custom(70001, 5, 64, 3, gate_bias={1: -1.0e4}),
     "bf16": workloads.custom(200, 5, 128, 4, act="bf16"),
     "bf16_H256_NE5": workloads.custom(3001, 5, 256, 5, act="bf16"),
-    # shapes where the calls run one by one
     "NE16": workloads.custom(200, 5, 128, 16),
+    "NE13_scan_scatter": workloads.custom(20000, 5, 64, 13, gate="int"),
+    # shapes where the calls run one by one
+    "NE17": workloads.custom(200, 5, 128, 17),
 }
 KEYS = ("y", "idx", "counts", "offsets", "perm", "loss", "dg", "frac", "mean_prob", "probs")
 
