@@ -1,7 +1,7 @@
 // Per-token arithmetic of the load-balancing auxiliary loss, shared by every kernel that
 // computes a part of it (the aux kernels, the routing kernel that also sums the softmax
-// columns, and the forward GEMM that also writes the logit gradient), so that each part
-// gives the same bits wherever it runs.
+// columns, and the forward GEMM or the scatter kernels that also write the logit gradient
+// and the loss), so that each part gives the same bits wherever it runs.
 //
 // MoE-gate commit page ("11b96dac6a"), summary block: softmax of the gate logits and the
 // loss lambda N_E sum_e frac[e] mean_prob[e]; the softmax is the max-shifted form of the
