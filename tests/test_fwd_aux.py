@@ -30,6 +30,9 @@ CASES = {
     "scan_scatter_NE3_ragged": workloads.custom(70001, 5, 64, 3, gate_bias={1: -1.0e4}),
     "bf16": workloads.custom(200, 5, 128, 4, act="bf16"),
     "bf16_H256_NE5": workloads.custom(3001, 5, 256, 5, act="bf16"),
+    "bf16_single_token": workloads.custom(1, 1, 128, 4, act="bf16"),
+    "bf16_NE1": workloads.custom(300, 5, 128, 1, act="bf16"),
+    "bf16_empty_expert_ties": workloads.custom(64, 5, 64, 4, act="bf16", gate="int", gate_bias={2: -1.0e4}),
     "NE16": workloads.custom(200, 5, 128, 16),
     "NE13_scan_scatter": workloads.custom(20000, 5, 64, 13, gate="int"),
     # shapes where the calls run one by one
