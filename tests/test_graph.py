@@ -8,10 +8,21 @@ import workloads
 pytestmark = pytest.mark.gpu
 
 
-def test_graph_replay_matches_eager(gpu_lib):
+GRAPH_CASES = {
+    # the aux loss on the forward launch (fp32, small T), on the scatter with the scan folded in
+    # (bf16), and on a separate scan + scatter (n_blk x N_E > 4096)
+    "gather_f32": workloads.custom(300, 5, 128, 4),
+    "scatter_scan_bf16": workloads.custom(300, 5, 256, 4, act="bf16"),
+    "scan_scatter_f32": workloads.custom(28000, 5, 128, 8),
+}
+
+
+@pytest.mark.parametrize("name", sorted(GRAPH_CASES))
+def test_graph_replay_matches_eager(gpu_lib, name):
     import torch
     from tests import gpu_run
-    inp = workloads.make_inputs(workloads.custom(300, 5, 128, 4))
+    print(f"[graph] {name} {GRAPH_CASES[name]}", flush=True)
+    inp = workloads.make_inputs(GRAPH_CASES[name])
     d = gpu_run.upload(inp)
     eager = gpu_run.Buffers(d)
     gpu_run.step(d, eager)
