@@ -41,12 +41,15 @@ enum KernelId {
 #ifndef MOE_DW_SMALL_BT
 #define MOE_DW_SMALL_BT 64
 #endif
-// Minimum tokens per d_W chunk (see plan_chunks): small-T tiling, fp32 large-T tiling.
+// Minimum tokens per d_W chunk (see plan_chunks): small-T tiling, fp32 large-T tiling.  With
+// the large-T 128 x 128 dW tiles, 320-token chunks took the imbalanced shape's (81,920 tokens,
+// H = 128) backward from 81 to 71 µs against 192 (256: 73, 512: 74, 768: 82 µs); the large-stress
+// plan is capped by the workgroup budget first, so it does not change.
 #ifndef MOE_DW_MIN_CHUNK
 #define MOE_DW_MIN_CHUNK 128
 #endif
 #ifndef MOE_DW_MIN_CHUNK_BIG
-#define MOE_DW_MIN_CHUNK_BIG 192
+#define MOE_DW_MIN_CHUNK_BIG 320
 #endif
 inline bool f32_big_tiles(int64_t T, int H) {
     const int64_t nt = H >= 128 ? H / 128 : 1;
