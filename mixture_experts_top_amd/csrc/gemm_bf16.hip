@@ -41,6 +41,8 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_floa
 typedef float f32x2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+typedef int i32x2v __attribute__((ext_vector_type(2)));
+typedef int i32x4v __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v){lo, hi}, bf16x2v));
 }
@@ -287,6 +289,227 @@ __device__ __forceinline__ void rows_bf16_body(char* smem, int bid, const uint16
     }
 }
 
+// Forward with a column slice of W[e] resident in LDS (H = 256, 512).
+//
+// The tiled kernel above reads a 128 x 128 tile of each operand from L2 for every output tile:
+// at T = 163,840, H = 512 that is 1.3 GB of L2 -> CU traffic for 168 MB of X.  Here a
+// workgroup (one per CU, 4 wavefronts) keeps BN columns of W[e] in LDS (BN x H bf16 =
+// 128 KB) and each wavefront streams groups of 32 of the expert's tokens through that slice,
+// its X rows loaded straight into MFMA operand registers: no LDS traffic for X and no barrier
+// between groups.  The NS = H / BN workgroups that cover one range of token groups run on the
+// same XCD (blockIdx % 8), so X comes from HBM once and from L2 NS times.
+//
+// Operand layouts.  A dot product may take its k in any order if both operands take the same
+// one: at k-step s = 4 q + i (i < 4) lane half h supplies the 8 k of 16-byte chunk
+// c = 8 q + 4 h + i of its row, so over 4 consecutive k-steps a lane reads 64 contiguous bytes
+// of its X row.  LDS row p = l32 + 32 j of the slice holds W[e] row n0 + NB l32 + j: lane l32
+// of column block j then produces output feature n0 + NB l32 + j, so a lane's NB results for
+// a token are adjacent features and leave as one 2 NB-byte store.  Chunk c of LDS row p sits at
+// chunk c ^ (p & 15), so the 16 lanes that read together touch 16 different bank groups.
+// Stores go through a buffer descriptor: padded rows of a ragged group get an offset past its
+// end and the hardware drops them, so no store is conditional (needs T H 2 < 2^31 bytes).
+template <int H>
+struct WsBf16 {
+    static constexpr int BN = (2 * H * H <= 131072) ? H : 131072 / (2 * H);  // columns per slice
+    static constexpr int NB = BN / 32;                                       // 32-wide column blocks
+    static constexpr int NS = H / BN;                                        // slices (workgroups per range)
+    static constexpr int NSL = H / 128;                                      // 8-k-step slices of a group
+};
+#ifndef MOE_WS_SUB
+#define MOE_WS_SUB 1            // 32-row MFMA blocks per wavefront group
+#endif
+#ifndef MOE_WS_WAVES
+#define MOE_WS_WAVES 4          // wavefronts per workgroup (one per SIMD: 8 spill)
+#endif
+constexpr int kWsWaves = MOE_WS_WAVES, kWsThreads = 64 * kWsWaves;
+constexpr int kWsSub = MOE_WS_SUB;
+constexpr int kWsGroup = 32 * kWsSub;  // tokens per wavefront group
+#ifndef MOE_WS_BPF
+#define MOE_WS_BPF 2            // k-steps of W fragments read ahead
+#endif
+constexpr int kWsWgs = 256;     // resident-slice grid: a multiple of 8 x NS
+
+// Lane e < N_E: expert e's first sorted position, count, and the exclusive / inclusive prefix
+// of its 32-token groups.
+struct WsGroups {
+    int l0, c, excl, incl;
+};
+__device__ __forceinline__ WsGroups ws_groups(const int* __restrict__ offsets, int NE) {
+    const int lane = __lane_id();
+    WsGroups g{0, 0, 0, 0};
+    if (lane < NE) {
+        g.l0 = offsets[lane];
+        g.c = offsets[lane + 1] - g.l0;
+    }
+    const int n = (g.c + kWsGroup - 1) / kWsGroup;
+    g.incl = wave_inclusive_sum(n);
+    g.excl = g.incl - n;
+    return g;
+}
+// Token of row `row` of group g (g < 0: no group), -1 for padded rows.  Branch-free; the one
+// perm load is unconditional (position 0 when there is no group: callers run only when T > 0).
+__device__ __forceinline__ int ws_token(const WsGroups& gt, int NE, const int* __restrict__ perm, int g, int row) {
+    const uint64_t hit = __ballot(__lane_id() < NE && g >= gt.excl && g < gt.incl);
+    const int le = hit ? __ffsll((unsigned long long)hit) - 1 : 0;
+    const int j = g - __builtin_amdgcn_readlane(gt.excl, le);
+    const int r0 = hit ? __builtin_amdgcn_readlane(gt.l0, le) + kWsGroup * j : 0;
+    const int rows = hit ? min(kWsGroup, __builtin_amdgcn_readlane(gt.c, le) - kWsGroup * j) : 0;
+    const int t = perm[r0 + min(row, max(rows - 1, 0))];
+    return row < rows ? t : -1;
+}
+
+template <int H>
+__global__ __launch_bounds__(kWsThreads, 1) void k_fwd_bf16_ws(const uint16_t* __restrict__ X,
+                                                              const uint16_t* __restrict__ W,
+                                                              const float* __restrict__ bias,
+                                                              uint16_t* __restrict__ Y,
+                                                              const int* __restrict__ offsets,
+                                                              const int* __restrict__ perm, int NE, int T) {
+    using C = WsBf16<H>;
+    constexpr int BN = C::BN, NB = C::NB, NSL = C::NSL, CPR = H / 8;
+    static_assert(NB == 4 || NB == 8, "a lane stores 8 or 16 bytes per row");
+    static_assert((BN * CPR) % kWsThreads == 0 && (BN * CPR / kWsThreads) % 8 == 0, "slice load shape");
+    __shared__ __attribute__((aligned(16))) uint16_t Ws[BN * H];
+    __shared__ __attribute__((aligned(16))) int Tk[kWsWaves][kWsGroup];
+    constexpr int SUB = kWsSub;
+    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
+    const int xcd = blockIdx.x % 8, a = blockIdx.x / 8;
+    const int ns = a % C::NS, NR = (int)gridDim.x / C::NS, rr = (a / C::NS) * 8 + xcd;
+    const WsGroups gt = ws_groups(offsets, NE);
+    const int Gt = __builtin_amdgcn_readlane(gt.incl, 63);
+    const int g0 = (int)((int64_t)Gt * rr / NR), g1 = (int)((int64_t)Gt * (rr + 1) / NR);
+    if (g0 >= g1) return;
+    const int n0 = ns * BN;
+    const __amdgpu_buffer_rsrc_t yr =
+        __builtin_amdgcn_make_buffer_rsrc(Y, (short)0, (int)((int64_t)T * H * 2), 0x00020000);
+
+    // one group of X rows ahead: slice k of the next group replaces slice k.  Row block u of a
+    // group is rows 32 u + l32; tok[u] is this lane's token in block u.
+    u16x8 ring[NSL][SUB][8];
+    auto load_slice = [&](const int (&t)[SUB], int k) {
+#pragma unroll
+        for (int u = 0; u < SUB; ++u) {
+            const uint16_t* src = X + (size_t)(t[u] < 0 ? 0 : t[u]) * H + 32 * h;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) ring[k][u][s] = ld8(src + 128 * k + 64 * (s / 4) + 8 * (s % 4));
+        }
+    };
+    auto tokens = [&](int gg, int (&t)[SUB]) {
+#pragma unroll
+        for (int u = 0; u < SUB; ++u) t[u] = ws_token(gt, NE, perm, gg < g1 ? gg : -1, 32 * u + l32);
+    };
+    // this wavefront's groups: g0 + wave, g0 + wave + kWsWaves, ...
+    int g = g0 + wave;
+    int tok[SUB], tokn[SUB];
+    tokens(g, tok);
+    tokens(g + kWsWaves, tokn);
+#pragma unroll
+    for (int k = 0; k < NSL; ++k) load_slice(tok, k);
+
+    for (int e = 0; e < NE; ++e) {
+        const int s0 = max(g0, __builtin_amdgcn_readlane(gt.excl, e));
+        const int s1 = min(g1, __builtin_amdgcn_readlane(gt.incl, e));
+        if (s0 >= s1) continue;
+        __syncthreads();  // every wavefront is done with the previous slice
+        const uint16_t* __restrict__ We = W + (size_t)e * H * H;
+#pragma unroll
+        for (int u0 = 0; u0 < BN * CPR / kWsThreads; u0 += 8) {
+            u16x8 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int idx = tid + kWsThreads * (u0 + u), p = idx / CPR, c = idx % CPR;
+                v[u] = ld8(We + (size_t)(n0 + NB * (p % 32) + p / 32) * H + 8 * c);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int idx = tid + kWsThreads * (u0 + u), p = idx / CPR, c = idx % CPR;
+                st8(&Ws[p * H + 8 * (c ^ (p & 15))], v[u]);
+            }
+        }
+        __syncthreads();
+        float bv[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) bv[j] = bias[(size_t)e * H + n0 + NB * l32 + j];
+
+        // groups of this wavefront in [s0, s1): g >= s0 holds because the segments before
+        // this one took every earlier group
+        for (; g < s1; g += kWsWaves) {
+            int toknn[SUB];
+            tokens(g + 2 * kWsWaves, toknn);
+            // the tokens of the 16 rows per block whose results this lane holds (rows
+            // 32 u + 8 v + 4 h + q), through the wavefront's slot in LDS (a wavefront's LDS
+            // operations complete in order)
+#pragma unroll
+            for (int u = 0; u < SUB; ++u) Tk[wave][32 * u + l32] = tok[u];
+            i32x4v trow[SUB][4];
+#pragma unroll
+            for (int u = 0; u < SUB; ++u)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    trow[u][v] = *reinterpret_cast<const i32x4v*>(&Tk[wave][32 * u + 8 * v + 4 * h]);
+            f32x16 acc[SUB][NB];
+#pragma unroll
+            for (int u = 0; u < SUB; ++u)
+#pragma unroll
+                for (int j = 0; j < NB; ++j) acc[u][j] = f32x16{};
+            // W fragments MOE_WS_BPF k-steps ahead of the MFMAs that use them; the fence keeps
+            // the compiler from sinking the reads next to their uses
+            constexpr int BPF = MOE_WS_BPF, NKS = 8 * NSL;
+            u16x8 bq[BPF + 1][NB];
+            auto load_b = [&](int ks) {
+                const int c = 16 * (ks / 8) + 8 * ((ks % 8) / 4) + 4 * h + (ks % 4);
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+                    bq[ks % (BPF + 1)][j] = ld8(&Ws[(l32 + 32 * j) * H + 8 * (c ^ (l32 & 15))]);
+            };
+#pragma unroll
+            for (int ks = 0; ks < BPF; ++ks) load_b(ks);
+#pragma unroll
+            for (int k = 0; k < NSL; ++k) {
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const int ks = 8 * k + s;
+                    if (ks + BPF < NKS) load_b(ks + BPF);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int j = 0; j < NB; ++j)
+#pragma unroll
+                        for (int u = 0; u < SUB; ++u)
+                            acc[u][j] = mfma_bf16(ring[k][u][s], bq[ks % (BPF + 1)][j], acc[u][j]);
+                }
+                // slice k of the next group goes out once slice k of this one is consumed
+                __builtin_amdgcn_sched_barrier(0x010E);
+                load_slice(tokn, k);
+                __builtin_amdgcn_sched_barrier(0x010E);
+            }
+#pragma unroll
+            for (int u = 0; u < SUB; ++u)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int t = trow[u][r / 4][r % 4];
+                    const int off = t >= 0 ? (t * H + n0 + NB * l32) * 2 : (int)0x80000000;
+                    if constexpr (NB == 4) {
+                        i32x2v pk;
+                        pk[0] = (int)pack_bf16x2(acc[u][0][r] + bv[0], acc[u][1][r] + bv[1]);
+                        pk[1] = (int)pack_bf16x2(acc[u][2][r] + bv[2], acc[u][3][r] + bv[3]);
+                        __builtin_amdgcn_raw_buffer_store_b64(pk, yr, off, 0, 0);
+                    } else {
+                        i32x4v pk;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            pk[q] = (int)pack_bf16x2(acc[u][2 * q][r] + bv[2 * q], acc[u][2 * q + 1][r] + bv[2 * q + 1]);
+                        __builtin_amdgcn_raw_buffer_store_b128(pk, yr, off, 0, 0);
+                    }
+                }
+#pragma unroll
+            for (int u = 0; u < SUB; ++u) {
+                tok[u] = tokn[u];
+                tokn[u] = toknn[u];
+            }
+        }
+    }
+}
+
 // d_W / d_b partials for one chunk of one expert's tokens, output tile [o0:o0+BT, i0:i0+BT].
 //
 // The LDS tiles are [feature][token]; a thread's register transpose writes 4 tokens of 8
@@ -500,9 +723,19 @@ __global__ __launch_bounds__(kThreads) void k_bwd_bf16(const uint16_t* __restric
 // ---------------------------------------------------------------- launchers
 static inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
+#ifndef MOE_BF16_WS_FWD
+#define MOE_BF16_WS_FWD 1  // H = 256 / 512 forward with the W slice resident in LDS
+#endif
 template <int H>
 static hipError_t fwd_bf16(const uint16_t* X, const uint16_t* W, const float* bias, uint16_t* Y,
                            const int32_t* offsets, const int32_t* perm, int64_t T, int NE, hipStream_t s) {
+    if constexpr (H >= 256) {
+        if (MOE_BF16_WS_FWD && T * H * 2 < ((int64_t)1 << 31)) {
+            launch_kernel((k_fwd_bf16_ws<H>), dim3(kWsWgs), dim3(kWsThreads), 0, s, X, W, bias, Y, offsets, perm, NE,
+                          (int)T);
+            return hipGetLastError();
+        }
+    }
     constexpr int BN = (H >= 128) ? 128 : H;
     constexpr int NT = H / BN;
     const int grid = round_up((int)((T + 127) / 128) + NE, 8) * NT;
