@@ -77,6 +77,14 @@ SMALL = {
     "bf16_H256_NE5": workloads.custom(150, 5, 256, 5, act="bf16"),
     # a few thousand bf16 tiles (several per resident workgroup slot), ragged at every expert's end
     "bf16_H512_many_tiles": workloads.custom(4096, 5, 512, 8, act="bf16", gate_bias={3: 1.0}),
+    # the H = 256 / 512 forward keeps a W slice per workgroup and walks a range of 32-token
+    # groups: ranges that cross expert boundaries and an empty expert in mid-range, one expert
+    # only, a single token (most workgroups get no group), N_E = 16 with tied logits
+    "bf16_H512_ranges_cross_experts": workloads.custom(1500, 5, 512, 8, act="bf16",
+                                                       gate_bias={2: -1.0e4, 5: 1.5}),
+    "bf16_H512_NE1": workloads.custom(700, 3, 512, 1, act="bf16"),
+    "bf16_H512_single_token": workloads.custom(1, 1, 512, 4, act="bf16"),
+    "bf16_H256_NE16_int_ties": workloads.custom(333, 7, 256, 16, act="bf16", gate="int"),
 }
 
 
