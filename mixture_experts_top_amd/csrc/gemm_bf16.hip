@@ -297,7 +297,9 @@ __device__ __forceinline__ void rows_bf16_body(char* smem, int bid, const uint16
 // 128 KB) and each wavefront streams groups of 32 of the expert's tokens through that slice,
 // its X rows loaded straight into MFMA operand registers: no LDS traffic for X and no barrier
 // between groups.  The NS = H / BN workgroups that cover one range of token groups run on the
-// same XCD (blockIdx % 8), so X comes from HBM once and from L2 NS times.
+// same XCD (blockIdx % 8), so X comes from HBM once and from L2 NS times.  At that shape the
+// L2 -> CU requests halve and the forward goes from 134 to 128 us: the X loads, which one group
+// of register ring does not cover, still hold it (with X rows served from L1 it takes 81 us).
 //
 // Operand layouts.  A dot product may take its k in any order if both operands take the same
 // one: at k-step s = 4 q + i (i < 4) lane half h supplies the 8 k of 16-byte chunk
@@ -316,10 +318,10 @@ struct WsBf16 {
     static constexpr int NSL = H / 128;                                      // 8-k-step slices of a group
 };
 #ifndef MOE_WS_SUB
-#define MOE_WS_SUB 1            // 32-row MFMA blocks per wavefront group
+#define MOE_WS_SUB 1            // 32-row MFMA blocks per wavefront group (2 spills registers)
 #endif
 #ifndef MOE_WS_WAVES
-#define MOE_WS_WAVES 4          // wavefronts per workgroup (one per SIMD: 8 spill)
+#define MOE_WS_WAVES 4          // wavefronts per workgroup, one per SIMD (8 spills registers)
 #endif
 constexpr int kWsWaves = MOE_WS_WAVES, kWsThreads = 64 * kWsWaves;
 constexpr int kWsSub = MOE_WS_SUB;
