@@ -9,8 +9,8 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("wl", [workloads.workload(2), workloads.custom(173, 7, 256, 5),
                                 workloads.custom(1000, 5, 128, 8, gate_bias={4: 2.5}, lam=0.05),
-                                workloads.custom(300, 5, 512, 8, act="bf16")],
-                         ids=["pages_shape", "ragged_H256_NE5", "skewed", "bf16_H512"])
+                                workloads.custom(300, 5, 512, 8, act="bf16"), workloads.workload(4)],
+                         ids=["pages_shape", "ragged_H256_NE5", "skewed", "bf16_H512", "wider_bf16"])
 def test_repeats_are_bitwise_identical(gpu_lib, wl):
     from tests import gpu_run
     inp = workloads.make_inputs(wl)
