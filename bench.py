@@ -68,8 +68,7 @@ def pass_roofline_us(wl):
 
 
 KERNEL_SOURCES = {"fwd_gemm": "gemm", "bwd_gemm": "gemm", "route": "route.hip", "scan": "route.hip",
-                  "scatter": "route.hip", "reduce": "reduce.hip", "aux": "aux.hip", "aux_final": "aux.hip",
-                  "w_transpose": "gemm_bf16.hip"}
+                  "scatter": "route.hip", "reduce": "reduce.hip", "aux": "aux.hip", "aux_final": "aux.hip"}
 
 
 def kernel_source_digest(kernel, act):
@@ -301,8 +300,6 @@ def main():
     nk = 10
     kern_us = {}
     gate_kernels = ["route", "scan", "scatter", "fwd_gemm", "bwd_gemm", "reduce", "aux", "aux_final"]
-    if wl.act == "bf16":
-        gate_kernels.append("w_transpose")
     for k in ([] if args.skip_kernel_survey else gate_kernels):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nk)]
         marks = [torch.cuda.Event(enable_timing=True) for _ in range(nk)]

@@ -272,7 +272,7 @@ enum {
     MOE_KERNEL_REDUCE = 5,       /* deterministic chunk reduction -> d_W, d_b */
     MOE_KERNEL_AUX = 6,          /* softmax, dG, per-block column sums of p */
     MOE_KERNEL_AUX_FINAL = 7,    /* mean_prob, frac, loss */
-    MOE_KERNEL_W_TRANSPOSE = 8,  /* bf16 backward only: W^T staged for the dX GEMM */
+    MOE_KERNEL_W_TRANSPOSE = 8,  /* reserved: no kernel of this id is launched any more */
     MOE_KERNEL_LAMBDA = 9,       /* adaptive lambda update */
     MOE_KERNEL_REDUCE_AXIS0 = 10,/* standalone reduce_axis0 */
     MOE_KERNEL_COLLAPSE = 11,    /* horizon mean collapse, forward or backward */

@@ -7,10 +7,10 @@
 //
 // v_mfma_f32_32x32x16_bf16: lane l (half h = l / 32) supplies 8 consecutive k of row
 // m = l % 32 of A and of column n = l % 32 of B (k = 8h .. 8h+7); the fp32 result has the
-// same lane layout as the fp32 32x32 instruction.  Every operand is therefore one 16-byte
-// LDS read from a tile whose K dimension is contiguous:
-//   forward  A = X rows, B = W[e] rows (W is [out][in]: K = in is contiguous)
-//   dX       A = dY rows, B = W[e]^T rows, from a transposed copy of W made per call
+// same lane layout as the fp32 32x32 instruction.  Operands come from LDS tiles:
+//   forward  A = X rows, B = W[e] rows (W is [out][in]: K = in is contiguous): one 16-byte read
+//   dX       A = dY rows, B = W[e] as stored, a [k = out][n = in] tile whose fragments come from
+//            two transposing 8-byte reads (ds_read_b64_tr_b16, see tr_frag)
 //   dW       A = dY^T, B = X^T: token rows are transposed in registers while staging
 //            (4 tokens x 8 features per thread) so K = tokens is contiguous in LDS.
 #include "moe_internal.hpp"
@@ -58,19 +58,33 @@ __device__ __forceinline__ void xcd_split(int bid, int per, int& major, int& min
 
 }  // namespace
 
-// Wt[e][i][o] = W[e][o][i], 64 x 64 tiles through LDS.
-__global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restrict__ W, uint16_t* __restrict__ Wt,
-                                                        int H) {
-    __shared__ uint16_t tile[64][66];
-    const size_t base = (size_t)blockIdx.z * H * H;
-    const int bx = blockIdx.x * 64, by = blockIdx.y * 64;
-    const int tx = threadIdx.x % 64, ty = threadIdx.x / 64;
-    for (int r = ty; r < 64; r += 4) tile[r][tx] = W[base + (size_t)(by + r) * H + bx + tx];
-    __syncthreads();
-    for (int r = ty; r < 64; r += 4) Wt[base + (size_t)(bx + r) * H + by + tx] = tile[tx][r];
+// MFMA B fragment (8 consecutive k of one column n per lane) from a row-major [k][n] bf16 LDS
+// tile, through gfx950's transposing LDS read ds_read_b64_tr_b16.  Its lane layout, measured:
+// within each group of 16 lanes, output lane i's element q is element (i & 3) of the 8 bytes
+// that lane 4 q + (i >> 2) addressed -- so lane j of a group pointing at row j >> 2, columns
+// 4 (j & 3) .. + 3 of a 4-row x 16-column block hands lane i the 4 rows of column i; two such
+// reads give the 8 k of an operand.  blk: the fragment's first row (k) and column (n); RS: the
+// tile's row stride in elements (BN + 32: 64 bytes of padding, where these reads measured
+// conflict-free).
+typedef short i16x4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4v* lds_i16x4_ptr;
+template <int RS>
+__device__ __forceinline__ u16x8 tr_frag(const uint16_t* blk, int lane) {
+    const int h = lane / 32, grp = (lane % 32) / 16, j = lane % 16;
+    const uint16_t* p = blk + (8 * h + (j >> 2)) * RS + 16 * grp + 4 * (j & 3);
+    const i16x4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(p));
+    const i16x4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(p + 4 * RS));
+    u16x8 v;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        v[q] = (uint16_t)lo[q];
+        v[4 + q] = (uint16_t)hi[q];
+    }
+    return v;
 }
 
-// Out[t, n0:n0+BN] = A[t, :] . Bw[e][n0:n0+BN, :]^T (+ bias[e] | + Out[t] when accumulating).
+// Out[t, n0:n0+BN] = A[t, :] . Bw[e][n0:n0+BN, :]^T (+ bias[e] | + Out[t] when accumulating);
+// for dX, A = dY and Out[t, n] = sum_k A[t, k] W[e][k, n] (W read as stored, see tr_frag).
 #ifndef MOE_BF16_KC
 #define MOE_BF16_KC 64  // K slice of the bf16 row GEMM (a multiple of 16)
 #endif
@@ -81,7 +95,9 @@ constexpr int kStPad = 8;  // fp32 staging rows: a stride of 8 (mod 64) floats k
 template <int H, int BN>
 struct RowsBf16Smem {
     static constexpr int BM = 128, KC = (MOE_BF16_KC < H) ? MOE_BF16_KC : H, KP = KC + 8;
-    static constexpr size_t a = sizeof(uint16_t) * 2 * BM * KP, b = sizeof(uint16_t) * 2 * BN * KP, tok = 4 * BM;
+    static constexpr int RSB = BN + 32;  // dX: row stride of the [k][n] W tile (64 bytes of padding)
+    static constexpr size_t a = sizeof(uint16_t) * 2 * BM * KP, tok = 4 * BM;
+    static constexpr size_t b = sizeof(uint16_t) * 2 * (BN * KP > KC * RSB ? BN * KP : KC * RSB);
     static constexpr size_t stage = MOE_BF16_STAGED_STORES ? sizeof(float) * BM * (BN + kStPad) : 0;
     static constexpr size_t tok_off = a + b > stage ? a + b : stage;
     static constexpr size_t bytes = tok_off + tok;
@@ -112,6 +128,11 @@ __device__ __forceinline__ void rows_bf16_body(char* smem, int bid, const uint16
     using SM_ = RowsBf16Smem<H, BN>;
     uint16_t(&As)[2][BM][KP] = *reinterpret_cast<uint16_t(*)[2][BM][KP]>(smem);
     uint16_t(&Bs)[2][BN][KP] = *reinterpret_cast<uint16_t(*)[2][BN][KP]>(smem + SM_::a);
+    // dX reads W[e] as stored ([out][in]: K = out is the row index) into a [k][n] tile and takes
+    // its fragments with the transposing LDS read
+    constexpr int RSB = SM_::RSB, TPRB = BN / 8, RPPB = kThreads / TPRB;
+    static_assert(!DX || (KC % RPPB == 0 && KC / RPPB == BL), "dX W tile shape");
+    uint16_t(&Bt)[2][KC][RSB] = *reinterpret_cast<uint16_t(*)[2][KC][RSB]>(smem + SM_::a);
     int* tok = reinterpret_cast<int*>(smem + SM_::tok_off);
 
     int mt, nt;
@@ -142,7 +163,8 @@ __device__ __forceinline__ void rows_bf16_body(char* smem, int bid, const uint16
     auto load_b = [&](int c, int slot) {
 #pragma unroll
         for (int i = 0; i < BL; ++i)
-            rb[slot][i] = ld8(Be + (size_t)(n0 + tid / TPR + RPP * i) * H + c * KC + 8 * (tid % TPR));
+            rb[slot][i] = DX ? ld8(Be + (size_t)(c * KC + tid / TPRB + RPPB * i) * H + n0 + 8 * (tid % TPRB))
+                             : ld8(Be + (size_t)(n0 + tid / TPR + RPP * i) * H + c * KC + 8 * (tid % TPR));
     };
     const uint16_t* a_src[AL];
     auto load_a = [&](int c, int slot) {
@@ -153,7 +175,12 @@ __device__ __forceinline__ void rows_bf16_body(char* smem, int bid, const uint16
 #pragma unroll
         for (int i = 0; i < AL; ++i) st8(&As[buf][tid / TPR + RPP * i][8 * (tid % TPR)], ra[slot][i]);
 #pragma unroll
-        for (int i = 0; i < BL; ++i) st8(&Bs[buf][tid / TPR + RPP * i][8 * (tid % TPR)], rb[slot][i]);
+        for (int i = 0; i < BL; ++i) {
+            if constexpr (DX)
+                st8(&Bt[buf][tid / TPRB + RPPB * i][8 * (tid % TPRB)], rb[slot][i]);
+            else
+                st8(&Bs[buf][tid / TPR + RPP * i][8 * (tid % TPR)], rb[slot][i]);
+        }
     };
 
     // W does not depend on perm: its loads go out while the token ids are in flight (loads
@@ -202,7 +229,9 @@ __device__ __forceinline__ void rows_bf16_body(char* smem, int bid, const uint16
 #pragma unroll
             for (int i = 0; i < SM; ++i) a[i] = ld8(&As[buf][wm * WTM + i * 32 + l32][kk + 8 * h]);
 #pragma unroll
-            for (int j = 0; j < SN; ++j) b[j] = ld8(&Bs[buf][wn * WTN + j * 32 + l32][kk + 8 * h]);
+            for (int j = 0; j < SN; ++j)
+                b[j] = DX ? tr_frag<RSB>(&Bt[buf][kk][wn * WTN + j * 32], lane)
+                          : ld8(&Bs[buf][wn * WTN + j * 32 + l32][kk + 8 * h]);
 #pragma unroll
             for (int i = 0; i < SM; ++i)
 #pragma unroll
@@ -714,7 +743,7 @@ __global__ __launch_bounds__(kThreads) void k_fwd_bf16(const uint16_t* __restric
 template <int H, int BN>
 __global__ __launch_bounds__(kThreads) void k_bwd_bf16(const uint16_t* __restrict__ dY,
                                                         const uint16_t* __restrict__ X,
-                                                        const uint16_t* __restrict__ Wt, uint16_t* __restrict__ dX,
+                                                        const uint16_t* __restrict__ W, uint16_t* __restrict__ dX,
                                                         int accumulate, float* __restrict__ part_dw,
                                                         float* __restrict__ part_db,
                                                         const int* __restrict__ offsets,
@@ -727,7 +756,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_bf16(const uint16_t* __restric
     if ((int)blockIdx.x < n_dw)
         dw_bf16_body<H>(smem, blockIdx.x, dY, X, part_dw, part_db, offsets, perm, NE, P, T);
     else
-        rows_bf16_body<H, BN, true>(smem, blockIdx.x - n_dw, dY, Wt, nullptr, dX, offsets, perm, NE, accumulate);
+        rows_bf16_body<H, BN, true>(smem, blockIdx.x - n_dw, dY, W, nullptr, dX, offsets, perm, NE, accumulate);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -754,7 +783,7 @@ static hipError_t fwd_bf16(const uint16_t* X, const uint16_t* W, const float* bi
 }
 
 template <int H>
-static hipError_t bwd_bf16(const uint16_t* dY, const uint16_t* X, const uint16_t* Wt, uint16_t* dX, int accumulate,
+static hipError_t bwd_bf16(const uint16_t* dY, const uint16_t* X, const uint16_t* W, uint16_t* dX, int accumulate,
                            float* pdw, float* pdb, const int32_t* offsets, const int32_t* perm, int64_t T, int NE,
                            int P, int n_chunk_max, hipStream_t s) {
     constexpr int BN = (H >= 128) ? 128 : H;
@@ -763,7 +792,7 @@ static hipError_t bwd_bf16(const uint16_t* dY, const uint16_t* X, const uint16_t
     constexpr int TPC = (H / BT) * (H / BT);
     const int n_dx = round_up((int)((T + 127) / 128) + NE, 8) * NT;
     const int grid = n_dx + round_up(n_chunk_max, 8) * TPC;
-    launch_kernel((k_bwd_bf16<H, BN>), dim3(grid), dim3(kThreads), 0, s, dY, X, Wt, dX, accumulate, pdw, pdb,
+    launch_kernel((k_bwd_bf16<H, BN>), dim3(grid), dim3(kThreads), 0, s, dY, X, W, dX, accumulate, pdw, pdb,
                        offsets, perm, NE, P, (int)T, n_dx);
     return hipGetLastError();
 }
@@ -780,19 +809,14 @@ hipError_t launch_fwd_gemm_bf16(const uint16_t* X, const uint16_t* W, const floa
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_transpose_w_bf16(const uint16_t* W, uint16_t* Wt, int H, int NE, hipStream_t s) {
-    launch_kernel(k_transpose_bf16, dim3(H / 64, H / 64, NE), dim3(256), 0, s, W, Wt, H);
-    return hipGetLastError();
-}
-
-hipError_t launch_bwd_gemm_bf16(const uint16_t* dY, const uint16_t* X, const uint16_t* Wt, uint16_t* dX,
+hipError_t launch_bwd_gemm_bf16(const uint16_t* dY, const uint16_t* X, const uint16_t* W, uint16_t* dX,
                                 int accumulate, float* pdw, float* pdb, const int32_t* offsets, const int32_t* perm,
                                 int64_t T, int H, int NE, int P, int n_chunk_max, hipStream_t s) {
     switch (H) {
-        case 64: return bwd_bf16<64>(dY, X, Wt, dX, accumulate, pdw, pdb, offsets, perm, T, NE, P, n_chunk_max, s);
-        case 128: return bwd_bf16<128>(dY, X, Wt, dX, accumulate, pdw, pdb, offsets, perm, T, NE, P, n_chunk_max, s);
-        case 256: return bwd_bf16<256>(dY, X, Wt, dX, accumulate, pdw, pdb, offsets, perm, T, NE, P, n_chunk_max, s);
-        case 512: return bwd_bf16<512>(dY, X, Wt, dX, accumulate, pdw, pdb, offsets, perm, T, NE, P, n_chunk_max, s);
+        case 64: return bwd_bf16<64>(dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, T, NE, P, n_chunk_max, s);
+        case 128: return bwd_bf16<128>(dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, T, NE, P, n_chunk_max, s);
+        case 256: return bwd_bf16<256>(dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, T, NE, P, n_chunk_max, s);
+        case 512: return bwd_bf16<512>(dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, T, NE, P, n_chunk_max, s);
     }
     return hipErrorInvalidValue;
 }

@@ -74,7 +74,6 @@ Plan make_plan(int64_t T, int H, int NE, int act) {
     p.off_paux = o;    o += align256((size_t)p.n_ablk * NE * 4);
     p.off_pdw = o;     o += align256((size_t)p.n_chunk_max * H * H * 4);
     p.off_pdb = o;     o += align256((size_t)p.n_chunk_max * H * 4);
-    p.off_wt = o;      o += (act == MOE_DTYPE_BF16) ? align256((size_t)NE * H * H * 2) : 0;
     p.total = o;
     return p;
 }
@@ -313,10 +312,9 @@ static moe_status_t bwd_impl(const char* fn, const void* dy, int from_mean, cons
                                    p.n_chunk_max, s),
                "bwd gemm");
     } else {
-        uint16_t* wt = at<uint16_t>(workspace, p.off_wt);
-        LAUNCH(K_W_TRANSPOSE, launch_transpose_w_bf16((const uint16_t*)W, wt, p.H, p.NE, s), "w transpose");
         LAUNCH(K_BWD_GEMM,
-               launch_bwd_gemm_bf16((const uint16_t*)dy, (const uint16_t*)fused_ctx, wt, (uint16_t*)d_fused_ctx,
+               launch_bwd_gemm_bf16((const uint16_t*)dy, (const uint16_t*)fused_ctx, (const uint16_t*)W,
+                                    (uint16_t*)d_fused_ctx,
                                     accumulate_dx, pdw, pdb, expert_offsets, perm, p.T, p.H, p.NE, p.chunks,
                                     p.n_chunk_max, s),
                "bwd gemm");

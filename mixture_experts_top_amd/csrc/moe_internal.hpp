@@ -136,7 +136,7 @@ struct Plan {
     int n_chunk_max = 0;  // P + N_E, upper bound of the chunk count
     int n_ablk = 0;       // aux blocks
     size_t off_hist = 0, off_blkbase = 0, off_idx = 0, off_counts = 0, off_offsets = 0;
-    size_t off_pdw = 0, off_pdb = 0, off_paux = 0, off_wt = 0;
+    size_t off_pdw = 0, off_pdb = 0, off_paux = 0;
     size_t total = 0;
 };
 
@@ -232,8 +232,7 @@ hipError_t launch_bwd_gemm_f32_from_mean(const float* d_mean, const float* X, co
 hipError_t launch_fwd_gemm_bf16(const uint16_t* X, const uint16_t* W, const float* bias, uint16_t* Y,
                                 const int32_t* offsets, const int32_t* perm, int64_t T, int H, int NE,
                                 hipStream_t s);
-hipError_t launch_transpose_w_bf16(const uint16_t* W, uint16_t* Wt, int H, int NE, hipStream_t s);
-hipError_t launch_bwd_gemm_bf16(const uint16_t* dY, const uint16_t* X, const uint16_t* Wt, uint16_t* dX,
+hipError_t launch_bwd_gemm_bf16(const uint16_t* dY, const uint16_t* X, const uint16_t* W, uint16_t* dX,
                                 int accumulate, float* part_dw, float* part_db, const int32_t* offsets,
                                 const int32_t* perm, int64_t T, int H, int NE, int P, int n_chunk_max,
                                 hipStream_t s);
