@@ -47,7 +47,8 @@ __device__ __forceinline__ void column_sum(const float* __restrict__ in, size_t 
 
 // grid (H*H/(4 RX) + 1, N_E): x < H*H/(4 RX) -> a column tile of dW[e]; the last x -> db[e].
 // RY rows of threads share an expert's chunk rows: 4 when experts have few chunks (wide
-// column tiles, few workgroups), 8 or 16 when they have more (more loads in flight).
+// column tiles, few workgroups; 2 when they average fewer than 8), 8 or 16 when they have more
+// (more loads in flight).
 template <int RY>
 __global__ __launch_bounds__(256) void k_reduce_dw(const float* __restrict__ pdw,
                                                    const float* __restrict__ pdb,
@@ -78,12 +79,26 @@ __global__ __launch_bounds__(256) void k_reduce_dw(const float* __restrict__ pdw
 #endif
 // 8 rows of threads when the experts average at least this many chunks each (and the plan
 // stays under MOE_REDUCE_RY16_MIN_P): imbalanced shape (T = 81,920, N_E = 8) reduce 8.9 -> 7.0 us
+// MOE_REDUCE_RYLOW rows of threads (wider column tiles, half the workgroups) when the experts
+// average fewer than MOE_REDUCE_RYLOW_MAX_CPE chunks each: wider-bf16 shape (32 chunks over 8
+// experts) reduce 15.8 -> 13.3 us
+#ifndef MOE_REDUCE_RYLOW_MAX_CPE
+#define MOE_REDUCE_RYLOW_MAX_CPE 8
+#endif
+#ifndef MOE_REDUCE_RYLOW
+#define MOE_REDUCE_RYLOW 2
+#endif
 #ifndef MOE_REDUCE_RY8_MIN_CPE
 #define MOE_REDUCE_RY8_MIN_CPE 16
 #endif
 hipError_t launch_reduce_dw(const float* part_dw, const float* part_db, const int32_t* offsets, int64_t T, int H,
                             int NE, int P, float* dW, float* db, hipStream_t s) {
-    if (P < MOE_REDUCE_RY16_MIN_P && P / NE >= MOE_REDUCE_RY8_MIN_CPE) {
+    if (P / NE < MOE_REDUCE_RYLOW_MAX_CPE) {
+        constexpr int RY = MOE_REDUCE_RYLOW;
+        const int nbx = H * H / (4 * (256 / RY));
+        launch_kernel(k_reduce_dw<RY>, dim3(nbx + 1, NE), dim3(256), 0, s, part_dw, part_db, offsets, H, NE, P,
+                      (int)T, dW, db);
+    } else if (P < MOE_REDUCE_RY16_MIN_P && P / NE >= MOE_REDUCE_RY8_MIN_CPE) {
         const int nbx = H * H / (4 * 32);
         launch_kernel(k_reduce_dw<8>, dim3(nbx + 1, NE), dim3(256), 0, s, part_dw, part_db, offsets, H, NE, P,
                       (int)T, dW, db);
