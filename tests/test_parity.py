@@ -85,6 +85,10 @@ SMALL = {
     "bf16_H512_NE1": workloads.custom(700, 3, 512, 1, act="bf16"),
     "bf16_H512_single_token": workloads.custom(1, 1, 512, 4, act="bf16"),
     "bf16_H256_NE16_int_ties": workloads.custom(333, 7, 256, 16, act="bf16", gate="int"),
+    # the d_W reduce picks its column-tile shape from the chunks per expert (2, 4, 8 or 16 rows of
+    # threads); 48 chunks of 128 tokens over 4 experts takes the 4-row shape, which no workload
+    # above reaches
+    "reduce_mid_chunks_per_expert": workloads.custom(1229, 5, 128, 4),
 }
 
 
