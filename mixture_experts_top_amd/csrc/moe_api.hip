@@ -32,14 +32,17 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // the fp32 large-T tiling, where fewer, longer chunks shrink the partials more than they cost
 // the dW workgroups).  The chunk partials then stay within P x (H^2 + H) floats whatever the
 // routing skew.  Depends only on (T, H, act), so results are reproducible for a shape.  The
-// bf16 kernels get a quarter of the dW workgroups: at T = 163,840, H = 512 that is 32 chunks
-// instead of 128 (1 MB of fp32 partials each), which took the reduce from 35 to 16 µs and the
-// backward from 340 to 330 µs.
+// bf16 kernels get far fewer dW workgroups: at T = 163,840, H = 512, 320 plan 20 chunks (1 MB
+// of fp32 partials each; 128 took the reduce to 35 us).  With 8 balanced experts that is 2.5
+// chunks per expert on average, so every expert takes 3 chunks of equal length, and the 384 dW
+// workgroups leave slots free for the dX tiles of the same launch from its start: step 445 ->
+// 432 us against 512 (4 or 5 chunks per expert, a count at the rounding boundary; 384 and 256:
+// 444 and 464 us).
 #ifndef MOE_DW_WORKGROUPS
 #define MOE_DW_WORKGROUPS 2048
 #endif
 #ifndef MOE_DW_WORKGROUPS_BF16
-#define MOE_DW_WORKGROUPS_BF16 512
+#define MOE_DW_WORKGROUPS_BF16 320
 #endif
 static int plan_chunks(int64_t T, int H, int act) {
     const bool f32 = act == MOE_DTYPE_F32;
