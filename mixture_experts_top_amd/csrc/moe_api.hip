@@ -34,10 +34,10 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // routing skew.  Depends only on (T, H, act), so results are reproducible for a shape.  The
 // bf16 kernels get far fewer dW workgroups: at T = 163,840, H = 512, 320 plan 20 chunks (1 MB
 // of fp32 partials each; 128 took the reduce to 35 us).  With 8 balanced experts that is 2.5
-// chunks per expert on average, so every expert takes 3 chunks of equal length, and the 384 dW
-// workgroups leave slots free for the dX tiles of the same launch from its start: step 445 ->
-// 432 us against 512 (4 or 5 chunks per expert, a count at the rounding boundary; 384 and 256:
-// 444 and 464 us).
+// chunks per expert on average, so every expert takes 3 chunks of equal length: step 445 ->
+// 432 us against 512, where the average (4) sits on the rounding boundary and experts take 4 or
+// 5 chunks, so some chunks are a quarter longer than the rest (384 and 256, also on a boundary:
+// 444 and 464 us; 448, 4 equal chunks each: 432 us; 192, 2 each: 440 us).
 #ifndef MOE_DW_WORKGROUPS
 #define MOE_DW_WORKGROUPS 2048
 #endif
