@@ -32,12 +32,13 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // the fp32 large-T tiling, where fewer, longer chunks shrink the partials more than they cost
 // the dW workgroups).  The chunk partials then stay within P x (H^2 + H) floats whatever the
 // routing skew.  Depends only on (T, H, act), so results are reproducible for a shape.  The
-// bf16 kernels get far fewer dW workgroups: at T = 163,840, H = 512, 320 plan 20 chunks (1 MB
-// of fp32 partials each; 128 took the reduce to 35 us).  With 8 balanced experts that is 2.5
-// chunks per expert on average, so every expert takes 3 chunks of equal length: step 445 ->
-// 432 us against 512, where the average (4) sits on the rounding boundary and experts take 4 or
-// 5 chunks, so some chunks are a quarter longer than the rest (384 and 256, also on a boundary:
-// 444 and 464 us; 448, 4 equal chunks each: 432 us; 192, 2 each: 440 us).
+// bf16 kernels get far fewer dW workgroups.  At T = 163,840, H = 512 (16 tiles per chunk, 2
+// workgroups per CU, so 512 run at once), 320 plan 20 chunks (1 MB of fp32 partials each; 128
+// took the reduce to 35 us): each of 8 balanced experts takes 3 chunks, 384 dW workgroups run in
+// one round and the free slots start dX tiles.  512 planned 32, but experts on the rounding
+// boundary take 4 or 5 chunks: 36 chunks, 576 workgroups, 64 of them in a second round (step
+// 445 against 432 us; 448: 4 chunks each, 512 workgroups, 432 us; 384: 444 us; 256 and 192,
+// chunks of 10,240 tokens: 464 and 440 us).
 #ifndef MOE_DW_WORKGROUPS
 #define MOE_DW_WORKGROUPS 2048
 #endif
