@@ -85,6 +85,8 @@ SMALL = {
     "bf16_H512_NE1": workloads.custom(700, 3, 512, 1, act="bf16"),
     "bf16_H512_single_token": workloads.custom(1, 1, 512, 4, act="bf16"),
     "bf16_H256_NE16_int_ties": workloads.custom(333, 7, 256, 16, act="bf16", gate="int"),
+    "bf16_H256_NE64_many_empty": workloads.custom(50, 4, 256, 64, act="bf16"),
+    "bf16_H512_NE20": workloads.custom(300, 5, 512, 20, act="bf16"),
     # the d_W reduce picks its column-tile shape from the chunks per expert (2, 4, 8 or 16 rows of
     # threads); 48 chunks of 128 tokens over 4 experts takes the 4-row shape, which no workload
     # above reaches
