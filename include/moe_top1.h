@@ -127,6 +127,11 @@ moe_status_t moe_top1_fwd(const void* fused_ctx, const float* gate_logits, const
  *                                                              accumulate_dx != 0)
  *   d_W[e] = sum_{t : e*(t) = e} d_routed_ctx[t, :]^T (outer) fused_ctx[t, :]  (overwritten)
  *   d_b[e] = sum_{t : e*(t) = e} d_routed_ctx[t, :]                            (overwritten)
+ * expert_offsets and perm are read under guards (each offset clamped to [0, T] and the list
+ * made non-decreasing; each token id clamped to [0, T - 1]; see the MHA wiring page
+ * "9170d24fe3", BUG CAUGHT DURING WIRING block), so routing that does not belong to these
+ * tokens gives meaningless results but no access outside the caller's buffers; routing from
+ * moe_top1_fwd is unchanged by them.
  * Experts with no tokens get d_W[e] = d_b[e] = +0.0 exactly.  The token sums are taken
  * per fixed-size chunk of each expert's tokens and the chunk partials are then summed
  * in chunk order (no atomics), so the result depends only on the inputs and the shape.

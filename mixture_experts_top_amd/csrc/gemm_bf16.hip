@@ -115,7 +115,7 @@ __device__ __forceinline__ void rows_bf16_body(char* smem, int bid, const uint16
                                                const float* __restrict__ bias,
                                                uint16_t* __restrict__ Out,
                                                const int* __restrict__ offsets,
-                                               const int* __restrict__ perm, int NE, int accumulate) {
+                                               const int* __restrict__ perm, int NE, int T, int accumulate) {
     constexpr int BM = 128, KC = RowsBf16Smem<H, BN>::KC, KP = KC + 8, NKC = H / KC;
     constexpr int NT = H / BN;
     constexpr int WTM = BM / 2, WTN = BN / 2;
@@ -138,7 +138,7 @@ __device__ __forceinline__ void rows_bf16_body(char* smem, int bid, const uint16
     int mt, nt;
     xcd_split(bid, NT, mt, nt);
     int e, r0, r1;
-    if (!find_tile(offsets, NE, mt, BM, e, r0, r1)) return;
+    if (!find_tile(offsets, NE, T, mt, BM, e, r0, r1)) return;
     const int rows = r1 - r0;
     const int tid = threadIdx.x;
     const int n0 = nt * BN;
@@ -151,9 +151,9 @@ __device__ __forceinline__ void rows_bf16_body(char* smem, int bid, const uint16
 #pragma unroll
     for (int i = 0; i < AL; ++i) {
         const int row = tid / TPR + RPP * i;
-        ta[i] = (row < rows) ? perm[r0 + row] : -1;
+        ta[i] = (row < rows) ? load_token(perm, r0 + row, T) : -1;
     }
-    const int tok_mine = (tid < BM && tid < rows) ? perm[r0 + tid] : -1;
+    const int tok_mine = (tid < BM && tid < rows) ? load_token(perm, r0 + tid, T) : -1;
     // the bias is loaded before the K loop: a load still pending in the epilogue's conditional
     // stores would be waited for in each of them, and that wait also waits for every store
     // issued before it
@@ -373,13 +373,9 @@ __device__ __forceinline__ constexpr int ws_chunk(int s, int h) {
 struct WsGroups {
     int l0, c, excl, incl;
 };
-__device__ __forceinline__ WsGroups ws_groups(const int* __restrict__ offsets, int NE) {
-    const int lane = __lane_id();
+__device__ __forceinline__ WsGroups ws_groups(const int* __restrict__ offsets, int NE, int T) {
     WsGroups g{0, 0, 0, 0};
-    if (lane < NE) {
-        g.l0 = offsets[lane];
-        g.c = offsets[lane + 1] - g.l0;
-    }
+    expert_range(offsets, NE, T, g.l0, g.c);
     const int n = (g.c + kWsGroup - 1) / kWsGroup;
     g.incl = wave_inclusive_sum(n);
     g.excl = g.incl - n;
@@ -387,13 +383,14 @@ __device__ __forceinline__ WsGroups ws_groups(const int* __restrict__ offsets, i
 }
 // Token of row `row` of group g (g < 0: no group), -1 for padded rows.  Branch-free; the one
 // perm load is unconditional (position 0 when there is no group: callers run only when T > 0).
-__device__ __forceinline__ int ws_token(const WsGroups& gt, int NE, const int* __restrict__ perm, int g, int row) {
+__device__ __forceinline__ int ws_token(const WsGroups& gt, int NE, int T, const int* __restrict__ perm, int g,
+                                        int row) {
     const uint64_t hit = __ballot(__lane_id() < NE && g >= gt.excl && g < gt.incl);
     const int le = hit ? __ffsll((unsigned long long)hit) - 1 : 0;
     const int j = g - __builtin_amdgcn_readlane(gt.excl, le);
     const int r0 = hit ? __builtin_amdgcn_readlane(gt.l0, le) + kWsGroup * j : 0;
     const int rows = hit ? min(kWsGroup, __builtin_amdgcn_readlane(gt.c, le) - kWsGroup * j) : 0;
-    const int t = perm[r0 + min(row, max(rows - 1, 0))];
+    const int t = load_token(perm, r0 + min(row, max(rows - 1, 0)), T);
     return row < rows ? t : -1;
 }
 
@@ -414,7 +411,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void k_fwd_bf16_ws(const uint16_t* _
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
     const int xcd = blockIdx.x % 8, a = blockIdx.x / 8;
     const int ns = a % C::NS, NR = (int)gridDim.x / C::NS, rr = (a / C::NS) * 8 + xcd;
-    const WsGroups gt = ws_groups(offsets, NE);
+    const WsGroups gt = ws_groups(offsets, NE, T);
     const int Gt = __builtin_amdgcn_readlane(gt.incl, 63);
     const int g0 = (int)((int64_t)Gt * rr / NR), g1 = (int)((int64_t)Gt * (rr + 1) / NR);
     if (g0 >= g1) return;
@@ -435,7 +432,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void k_fwd_bf16_ws(const uint16_t* _
     };
     auto tokens = [&](int gg, int (&t)[SUB]) {
 #pragma unroll
-        for (int u = 0; u < SUB; ++u) t[u] = ws_token(gt, NE, perm, gg < g1 ? gg : -1, 32 * u + l32);
+        for (int u = 0; u < SUB; ++u) t[u] = ws_token(gt, NE, T, perm, gg < g1 ? gg : -1, 32 * u + l32);
     };
     // this wavefront's groups: g0 + wave, g0 + wave + kWsWaves, ...
     int g = g0 + wave;
@@ -610,7 +607,7 @@ __device__ __forceinline__ void dw_bf16_body(char* smem, int bid, const uint16_t
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int k = t0 + sl * KC + 4 * tq + j;
-                tk[it][j] = (q < ITEMS && sl < nslices && k < t1) ? perm[k] : -1;
+                tk[it][j] = (q < ITEMS && sl < nslices && k < t1) ? load_token(perm, k, T) : -1;
             }
         }
     };
@@ -735,9 +732,9 @@ template <int H, int BN>
 __global__ __launch_bounds__(kThreads) void k_fwd_bf16(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
                                                         const float* __restrict__ bias, uint16_t* __restrict__ Y,
                                                         const int* __restrict__ offsets,
-                                                        const int* __restrict__ perm, int NE) {
+                                                        const int* __restrict__ perm, int NE, int T) {
     __shared__ __attribute__((aligned(16))) char smem[RowsBf16Smem<H, BN>::bytes];
-    rows_bf16_body<H, BN, false>(smem, blockIdx.x, X, W, bias, Y, offsets, perm, NE, 0);
+    rows_bf16_body<H, BN, false>(smem, blockIdx.x, X, W, bias, Y, offsets, perm, NE, T, 0);
 }
 
 template <int H, int BN>
@@ -756,7 +753,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_bf16(const uint16_t* __restric
     if ((int)blockIdx.x < n_dw)
         dw_bf16_body<H>(smem, blockIdx.x, dY, X, part_dw, part_db, offsets, perm, NE, P, T);
     else
-        rows_bf16_body<H, BN, true>(smem, blockIdx.x - n_dw, dY, W, nullptr, dX, offsets, perm, NE, accumulate);
+        rows_bf16_body<H, BN, true>(smem, blockIdx.x - n_dw, dY, W, nullptr, dX, offsets, perm, NE, T, accumulate);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -778,7 +775,7 @@ static hipError_t fwd_bf16(const uint16_t* X, const uint16_t* W, const float* bi
     constexpr int BN = (H >= 128) ? 128 : H;
     constexpr int NT = H / BN;
     const int grid = round_up((int)((T + 127) / 128) + NE, 8) * NT;
-    launch_kernel((k_fwd_bf16<H, BN>), dim3(grid), dim3(kThreads), 0, s, X, W, bias, Y, offsets, perm, NE);
+    launch_kernel((k_fwd_bf16<H, BN>), dim3(grid), dim3(kThreads), 0, s, X, W, bias, Y, offsets, perm, NE, (int)T);
     return hipGetLastError();
 }
 

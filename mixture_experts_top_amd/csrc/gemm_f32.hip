@@ -169,7 +169,7 @@ __device__ __forceinline__ void rows_f32_body(char* smem, int wg, int nwg, int n
                                               const float* __restrict__ A, const float* __restrict__ W,
                                               const float* __restrict__ bias, float* __restrict__ Out,
                                               const int* __restrict__ offsets, const int* __restrict__ perm,
-                                              int NE, int accumulate, int nh = 1, float inv_nh = 1.0f) {
+                                              int NE, int T, int accumulate, int nh = 1, float inv_nh = 1.0f) {
     // MEAN: row t of A is A[t / nh] * inv_nh (the backward of a mean over nh horizons)
     constexpr int NKC = H / KC;
     constexpr int NT = H / BN;
@@ -194,12 +194,9 @@ __device__ __forceinline__ void rows_f32_body(char* smem, int wg, int nwg, int n
     const int wm = wave / WN, wn = wave % WN;
 
     // expert table: lane l < NE holds expert l's first row, row count and tile count
-    int x_lo = 0, x_cnt = 0, x_n = 0;
-    if (lane < NE) {
-        x_lo = offsets[lane];
-        x_cnt = offsets[lane + 1] - x_lo;
-        x_n = (x_cnt + BM - 1) / BM;
-    }
+    int x_lo, x_cnt;
+    expert_range(offsets, NE, T, x_lo, x_cnt);
+    const int x_n = (x_cnt + BM - 1) / BM;
     const int x_incl = wave_inclusive_sum(x_n), x_excl = x_incl - x_n;
     auto lookup = [&](int id, int& e, int& r0, int& rows, int& n0) -> bool {
         int mt, nt;
@@ -224,7 +221,7 @@ __device__ __forceinline__ void rows_f32_body(char* smem, int wg, int nwg, int n
     int id = next_valid(wg, e, r0, rows, n0);
     if (id < 0) return;
     int cur = 0;
-    if (tid < BM) tok[cur][tid] = (tid < rows) ? perm[r0 + tid] : -1;
+    if (tid < BM) tok[cur][tid] = (tid < rows) ? load_token(perm, r0 + tid, T) : -1;
     __syncthreads();
 
     const float* __restrict__ We = W + (size_t)e * H * H;
@@ -344,11 +341,11 @@ __device__ __forceinline__ void rows_f32_body(char* smem, int wg, int nwg, int n
 #pragma unroll
                 for (int j = 0; j < SN; ++j) bv_next[j] = bias[(size_t)e2 * H + n02 + wn * WTN + j * 32 + l32];
             }
-            if (tid < BM && tid < rows2) tok_next = perm[r02 + tid];
+            if (tid < BM && tid < rows2) tok_next = load_token(perm, r02 + tid, T);
 #pragma unroll
             for (int i = 0; i < AL; ++i) {
                 const int row = tid / TPR + RPP * i;
-                if (row < rows2) tn[i] = perm[r02 + row];
+                if (row < rows2) tn[i] = load_token(perm, r02 + row, T);
             }
         }
 #pragma unroll 1
@@ -441,7 +438,7 @@ template <int H, int BM, int BN, int KC, bool DX, bool MEAN = false, int XR = 1,
 __device__ __forceinline__ void rows_f32_onepass_body(char* smem, int bid, const float* __restrict__ A,
                                                       const float* __restrict__ W, const float* __restrict__ bias,
                                                       float* __restrict__ Out, const int* __restrict__ offsets,
-                                                      const int* __restrict__ perm, int NE, int accumulate,
+                                                      const int* __restrict__ perm, int NE, int T, int accumulate,
                                                       int nh = 1, float inv_nh = 1.0f, RouteView rv = {}) {
     constexpr int NKC = H / KC;
     constexpr int NT = H / BN;
@@ -473,7 +470,7 @@ __device__ __forceinline__ void rows_f32_onepass_body(char* smem, int bid, const
         xcd_rows(bid, NT, XR, mt, nt);
     int lo = 0;  // GATHER: the tile's first rank within its expert
     if constexpr (!GATHER) {
-        if (!find_tile(offsets, NE, mt, BM, e, r0, r1)) return;
+        if (!find_tile(offsets, NE, T, mt, BM, e, r0, r1)) return;
     } else {
         // The routing histogram (at most 4096 entries) goes to LDS, over the region the K
         // slices use later; its column sums give every expert's count, hence the tile list.
@@ -508,9 +505,9 @@ __device__ __forceinline__ void rows_f32_onepass_body(char* smem, int bid, const
 #pragma unroll
         for (int i = 0; i < AL; ++i) {
             const int row = tid / TPR + RPP * i;
-            ta[i] = (row < rows) ? perm[r0 + row] : -1;
+            ta[i] = (row < rows) ? load_token(perm, r0 + row, T) : -1;
         }
-        tok_mine = (tid < BM && tid < rows) ? perm[r0 + tid] : -1;  // to LDS once the loads are out
+        tok_mine = (tid < BM && tid < rows) ? load_token(perm, r0 + tid, T) : -1;  // to LDS once the loads are out
     }
 
     f32x4 ra[PF][AL], rb[PF][BL];
@@ -807,7 +804,7 @@ __device__ __forceinline__ void dw_f32_body(char* smem, int bid, const float* __
 #pragma unroll
         for (int i = 0; i < LD; ++i) {
             const int k = kpos(sl, i);
-            tk[slot][i] = perm[k < t1 ? k : t1 - 1];
+            tk[slot][i] = load_token(perm, k < t1 ? k : t1 - 1, T);
         }
     };
     auto load_rows = [&](int sl, int slot) {  // ids of slice sl are in tk[slot]; rows go to slot
@@ -920,13 +917,13 @@ template <int H, int BM, int BN, int KC, bool ONE>
 __global__ __launch_bounds__(kThreads) MOE_FWD_ATTR void k_fwd_f32(const float* __restrict__ X, const float* __restrict__ W,
                                                        const float* __restrict__ bias, float* __restrict__ Y,
                                                        const int* __restrict__ offsets,
-                                                       const int* __restrict__ perm, int NE, int ntile_ids) {
+                                                       const int* __restrict__ perm, int NE, int T, int ntile_ids) {
     __shared__ __attribute__((aligned(16))) char smem[RowsF32Smem<BM, BN, KC, false>::bytes];
     if (ONE)
-        rows_f32_onepass_body<H, BM, BN, KC, false>(smem, blockIdx.x, X, W, bias, Y, offsets, perm, NE, 0);
+        rows_f32_onepass_body<H, BM, BN, KC, false>(smem, blockIdx.x, X, W, bias, Y, offsets, perm, NE, T, 0);
     else
         rows_f32_body<H, BM, BN, KC, false>(smem, blockIdx.x, gridDim.x, ntile_ids, X, W, bias, Y, offsets, perm,
-                                            NE, 0);
+                                            NE, T, 0);
 }
 
 // The load-balancing loss inside the forward launch (its inputs are all known once the
@@ -997,7 +994,7 @@ __global__ __launch_bounds__(kThreads) void k_fwd_f32_gather(const float* __rest
     }
     const RouteView rv{idx, hist, nblk, T, counts, offsets, perm};
     rows_f32_onepass_body<H, BM, BN, KC, false, false, 1, true>(smem, blockIdx.x, X, W, bias, Y, nullptr, nullptr,
-                                                                 NE, 0, 1, 1.0f, rv);
+                                                                 NE, T, 0, 1, 1.0f, rv);
 }
 
 template <int H, int BM, int BN, int BT, int KCX, int KCW, bool MEAN, bool ONE, bool DWF = false>
@@ -1017,16 +1014,16 @@ __global__ __launch_bounds__(kThreads) void k_bwd_f32(const float* __restrict__ 
                                           inv_nh);
         else
             rows_f32_body<H, BM, BN, KCX, true, MEAN>(smem, blockIdx.x - n_dw, n_dx, dx_tile_ids, dY, W, nullptr, dX,
-                                                      offsets, perm, NE, accumulate, nh, inv_nh);
+                                                      offsets, perm, NE, T, accumulate, nh, inv_nh);
         return;
     }
     if ((int)blockIdx.x < n_dx) {
         if (ONE)
             rows_f32_onepass_body<H, BM, BN, KCX, true, MEAN, DX_XR<BM>>(smem, blockIdx.x, dY, W, nullptr, dX, offsets,
-                                                                          perm, NE, accumulate, nh, inv_nh);
+                                                                          perm, NE, T, accumulate, nh, inv_nh);
         else
             rows_f32_body<H, BM, BN, KCX, true, MEAN>(smem, blockIdx.x, n_dx, dx_tile_ids, dY, W, nullptr, dX,
-                                                      offsets, perm, NE, accumulate, nh, inv_nh);
+                                                      offsets, perm, NE, T, accumulate, nh, inv_nh);
     }
     else
         dw_f32_body<H, BT, KCW, MEAN>(smem, blockIdx.x - n_dx, dY, X, part_dw, part_db, offsets, perm, NE, P, T, nh,
@@ -1107,17 +1104,17 @@ static hipError_t fwd_f32(const float* X, const float* W, const float* bias, flo
         const int ids = rows_grid<H, TL::BIG_BN>(T, NE, 128);
         const int grid = persist_wgs(ids, MOE_FWD_PERSIST_WGS, MOE_FWD_PERSIST_WGS);
         launch_kernel((k_fwd_f32<H, 128, TL::BIG_BN, MOE_F32_KC_FWD, false>), dim3(grid), dim3(kThreads), 0, s,
-                           X, W, bias, Y, offsets, perm, NE, ids);
+                           X, W, bias, Y, offsets, perm, NE, (int)T, ids);
         return hipGetLastError();
     }
     const int ids = rows_grid<H, TL::FWD_BN>(T, NE, TL::FWD_BM);
     if (ids <= MOE_ROWS_ONEPASS_MAX_IDS)
         launch_kernel((k_fwd_f32<H, TL::FWD_BM, TL::FWD_BN, MOE_F32_KC_FWD, true>), dim3(ids),
-                           dim3(kThreads), 0, s, X, W, bias, Y, offsets, perm, NE, ids);
+                           dim3(kThreads), 0, s, X, W, bias, Y, offsets, perm, NE, (int)T, ids);
     else
         launch_kernel((k_fwd_f32<H, TL::FWD_BM, TL::FWD_BN, MOE_F32_KC_FWD, false>),
                            dim3(persist_wgs(ids, MOE_FWD_PERSIST_WGS, MOE_FWD_PERSIST_WGS)), dim3(kThreads), 0, s, X,
-                           W, bias, Y, offsets, perm, NE, ids);
+                           W, bias, Y, offsets, perm, NE, (int)T, ids);
     return hipGetLastError();
 }
 

@@ -10,6 +10,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "routing_guard.hpp"
+
 namespace moe {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -81,19 +83,41 @@ __device__ __forceinline__ int wave_inclusive_sum(int v) {
     return v;
 }
 
+// Inclusive running maximum over the 64 lanes of a wavefront.
+__device__ __forceinline__ int wave_inclusive_max(int v) {
+    const int lane = __lane_id();
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int u = __shfl_up(v, d);
+        if (lane >= d) v = max(v, u);
+    }
+    return v;
+}
+
+// Lane l < NE: expert l's first position lo in perm and its token count cnt, from offsets
+// under the guards of routing_guard.hpp (clamped to [0, T], made non-decreasing by a running
+// maximum over the lanes); lanes >= NE get cnt = 0.  One load per lane, no serial chain.
+__device__ __forceinline__ void expert_range(const int* __restrict__ offsets, int NE, int T, int& lo, int& cnt) {
+    const int lane = __lane_id();
+    int a = 0, b = 0;
+    if (lane < NE) {
+        a = guard_offset(offsets[lane], T);
+        b = offsets[lane + 1];
+    }
+    lo = wave_inclusive_max(a);
+    cnt = lane < NE ? guard_count(lo, b, T) : 0;
+}
+
 // Wavefront-wide lookup of the unit `u` in a list cut expert by expert: lane l < NE holds
-// expert l's offsets and its number of units n_l; a prefix sum over lanes finds the expert
-// whose units cover u.  One load per lane and no serial chain; all lanes get the same
-// (uniform) result.  Returns false if u is past the last unit.
-__device__ __forceinline__ bool wave_find(const int* __restrict__ offsets, int NE, int u, int bm, int P, int T,
+// expert l's range (expert_range) and its number of units n_l; a prefix sum over lanes finds
+// the expert whose units cover u.  All lanes get the same (uniform) result.  Returns false if
+// u is past the last unit.
+__device__ __forceinline__ bool wave_find(const int* __restrict__ offsets, int NE, int T, int u, int bm, int P,
                                           bool chunks, int& e, int& j, int& lo, int& cnt, int& n_e) {
     const int lane = __lane_id();
-    int l0 = 0, c = 0, n = 0;
-    if (lane < NE) {
-        l0 = offsets[lane];
-        c = offsets[lane + 1] - l0;
-        n = chunks ? expert_nchunks(c, P, T) : (c + bm - 1) / bm;
-    }
+    int l0, c;
+    expert_range(offsets, NE, T, l0, c);
+    const int n = lane < NE ? (chunks ? expert_nchunks(c, P, T) : (c + bm - 1) / bm) : 0;
     const int incl = wave_inclusive_sum(n);
     const int excl = incl - n;
     const uint64_t hit = __ballot(lane < NE && u >= excl && u < incl);
@@ -108,10 +132,10 @@ __device__ __forceinline__ bool wave_find(const int* __restrict__ offsets, int N
 }
 
 // M-tile `mt` of rows cut into tiles of bm per expert -> expert e, rows [r0, r1) of perm.
-__device__ __forceinline__ bool find_tile(const int* __restrict__ offsets, int NE, int mt, int bm, int& e, int& r0,
-                                          int& r1) {
+__device__ __forceinline__ bool find_tile(const int* __restrict__ offsets, int NE, int T, int mt, int bm, int& e,
+                                          int& r0, int& r1) {
     int j, lo, cnt, n;
-    if (!wave_find(offsets, NE, mt, bm, 0, 1, false, e, j, lo, cnt, n)) return false;
+    if (!wave_find(offsets, NE, T, mt, bm, 0, false, e, j, lo, cnt, n)) return false;
     r0 = lo + j * bm;
     r1 = min(lo + cnt, r0 + bm);
     return true;
@@ -121,10 +145,15 @@ __device__ __forceinline__ bool find_tile(const int* __restrict__ offsets, int N
 __device__ __forceinline__ bool find_chunk(const int* __restrict__ offsets, int NE, int P, int T, int c, int& e,
                                            int& t0, int& t1) {
     int j, lo, cnt, n;
-    if (!wave_find(offsets, NE, c, 1, P, T, true, e, j, lo, cnt, n)) return false;
+    if (!wave_find(offsets, NE, T, c, 1, P, true, e, j, lo, cnt, n)) return false;
     t0 = lo + (int)((int64_t)j * cnt / n);
     t1 = lo + (int)((int64_t)(j + 1) * cnt / n);
     return true;
+}
+
+// Token id at position k of perm, guarded (routing_guard.hpp).
+__device__ __forceinline__ int load_token(const int* __restrict__ perm, int k, int T) {
+    return guard_token(perm[k], T);
 }
 
 // Workspace layout for one (T, H, N_E, act).  Every section starts on a 256-byte boundary.

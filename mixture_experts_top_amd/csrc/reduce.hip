@@ -58,9 +58,12 @@ __global__ __launch_bounds__(256) void k_reduce_dw(const float* __restrict__ pdw
     constexpr int RX = 256 / RY;
     __shared__ f32x4 red[256];
     const int e = blockIdx.y;
-    // chunk range of expert e: one load per lane and a wavefront prefix sum over the experts
+    // chunk range of expert e: one load per lane (guarded, routing_guard.hpp) and a wavefront
+    // prefix sum over the experts
     const int lane = threadIdx.x % 64;
-    const int nl = (lane < NE) ? expert_nchunks(offsets[lane + 1] - offsets[lane], P, T) : 0;
+    int lo, cnt;
+    expert_range(offsets, NE, T, lo, cnt);
+    const int nl = expert_nchunks(cnt, P, T);
     const int incl = wave_inclusive_sum(nl);
     const int cs = __shfl(incl - nl, e), n = __shfl(nl, e);
     const size_t HH = (size_t)H * H;
