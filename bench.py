@@ -262,7 +262,7 @@ def main():
 
     import mixture_experts_top_amd as moe
     import workloads
-    from tests import gpu_run
+    from mixture_experts_top_amd import runner as gpu_run
 
     if not torch.cuda.is_available():
         log("no GPU visible")

@@ -140,13 +140,22 @@ def _act(t) -> int:
     raise ValueError(f"activation dtype must be float32 or bfloat16, got {t.dtype}")
 
 
-def _workspace(ws, B, NH, H, NE, act, device):
+def _scratch(nbytes, device, stream):
+    """A temporary device buffer for one call.  torch's caching allocator ties a block to the
+    stream it was allocated on; when the kernels run on another stream, record_stream keeps
+    the block from being handed out again before that stream has run them."""
+    import torch
+    buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    if stream is not None and stream != torch.cuda.current_stream(buf.device):
+        buf.record_stream(stream)
+    return buf
+
+
+def _workspace(ws, B, NH, H, NE, act, device, stream=None):
     """A caller's workspace is passed with its size (the library rejects one too small);
     without one, a workspace of the required size is allocated for this call."""
     if ws is None:
-        import torch
-        need = moe_workspace_bytes(B, NH, H, NE, act)
-        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+        ws = _scratch(moe_workspace_bytes(B, NH, H, NE, act), device, stream)
     return ws, ws.numel() * ws.element_size()
 
 
@@ -178,7 +187,7 @@ def moe_top1_route(gate_logits, expert_idx, expert_counts, expert_offsets, perm,
     _expect(expert_counts, "expert_counts", (NE,), torch.int32)
     _expect(expert_offsets, "expert_offsets", (NE + 1,), torch.int32)
     _expect(perm, "perm", (T,), torch.int32)
-    ws, wsb = _workspace(workspace, B, NH, 64, NE, DTYPE_F32, gate_logits.device)
+    ws, wsb = _workspace(workspace, B, NH, 64, NE, DTYPE_F32, gate_logits.device, stream)
     _check(load_library().moe_top1_route(_ptr(gate_logits), _ptr(expert_idx), _ptr(expert_counts),
                                          _ptr(expert_offsets), _ptr(perm), B, NH, NE, _ptr(ws), wsb,
                                          _stream(stream)))
@@ -199,7 +208,7 @@ def moe_top1_fwd(fused_ctx, gate_logits, W, b, routed_ctx, expert_idx, expert_co
     _expect(expert_counts, "expert_counts", (NE,), torch.int32)
     _expect(expert_offsets, "expert_offsets", (NE + 1,), torch.int32)
     _expect(perm, "perm", (T,), torch.int32)
-    ws, wsb = _workspace(workspace, B, NH, H, NE, act, fused_ctx.device)
+    ws, wsb = _workspace(workspace, B, NH, H, NE, act, fused_ctx.device, stream)
     _check(load_library().moe_top1_fwd(_ptr(fused_ctx), _ptr(gate_logits), _ptr(W), _ptr(b), _ptr(routed_ctx),
                                        _ptr(expert_idx), _ptr(expert_counts), _ptr(expert_offsets), _ptr(perm),
                                        B, NH, H, NE, act, _ptr(ws), wsb, _stream(stream)))
@@ -229,7 +238,7 @@ def moe_top1_fwd_aux(fused_ctx, gate_logits, W, b, routed_ctx, expert_idx, exper
     _expect(mean_prob, "mean_prob", (NE,), torch.float32)
     _expect(probs, "probs", (B, NH, NE), torch.float32)
     _expect(lambda_dev, "lambda_dev", (1,), torch.float32)
-    ws, wsb = _workspace(workspace, B, NH, H, NE, act, fused_ctx.device)
+    ws, wsb = _workspace(workspace, B, NH, H, NE, act, fused_ctx.device, stream)
     _check(load_library().moe_top1_fwd_aux(_ptr(fused_ctx), _ptr(gate_logits), _ptr(W), _ptr(b), _ptr(routed_ctx),
                                            _ptr(expert_idx), _ptr(expert_counts), _ptr(expert_offsets), _ptr(perm),
                                            float(lam), _ptr(lambda_dev), _ptr(loss), _ptr(d_gate_logits),
@@ -251,7 +260,7 @@ def moe_top1_bwd(d_routed_ctx, fused_ctx, W, expert_offsets, perm, d_fused_ctx, 
     _expect(d_fused_ctx, "d_fused_ctx", (B, NH, H), fused_ctx.dtype)
     _expect(d_W, "d_W", (NE, H, H), torch.float32)
     _expect(d_b, "d_b", (NE, H), torch.float32)
-    ws, wsb = _workspace(workspace, B, NH, H, NE, act, fused_ctx.device)
+    ws, wsb = _workspace(workspace, B, NH, H, NE, act, fused_ctx.device, stream)
     _check(load_library().moe_top1_bwd(_ptr(d_routed_ctx), _ptr(fused_ctx), _ptr(W), _ptr(expert_offsets),
                                        _ptr(perm), _ptr(d_fused_ctx), _ptr(d_W), _ptr(d_b), int(bool(accumulate_dx)),
                                        B, NH, H, NE, act, _ptr(ws), wsb, _stream(stream)))
@@ -268,7 +277,7 @@ def moe_aux_loss(gate_logits, expert_counts, lam, loss, d_gate_logits, frac=None
     _expect(frac, "frac", (NE,), torch.float32)
     _expect(mean_prob, "mean_prob", (NE,), torch.float32)
     _expect(probs, "probs", (B, NH, NE), torch.float32)
-    ws, wsb = _workspace(workspace, B, NH, 64, NE, DTYPE_F32, gate_logits.device)
+    ws, wsb = _workspace(workspace, B, NH, 64, NE, DTYPE_F32, gate_logits.device, stream)
     _check(load_library().moe_aux_loss(_ptr(gate_logits), _ptr(expert_counts), float(lam), _ptr(loss),
                                        _ptr(d_gate_logits), _ptr(frac), _ptr(mean_prob), _ptr(probs),
                                        B, NH, NE, _ptr(ws), wsb, _stream(stream)))
@@ -296,7 +305,7 @@ def moe_aux_loss_lambda_dev(gate_logits, expert_counts, lambda_dev, loss, d_gate
     _expect(frac, "frac", (NE,), torch.float32)
     _expect(mean_prob, "mean_prob", (NE,), torch.float32)
     _expect(probs, "probs", (B, NH, NE), torch.float32)
-    ws, wsb = _workspace(workspace, B, NH, 64, NE, DTYPE_F32, gate_logits.device)
+    ws, wsb = _workspace(workspace, B, NH, 64, NE, DTYPE_F32, gate_logits.device, stream)
     _check(load_library().moe_aux_loss_lambda_dev(_ptr(gate_logits), _ptr(expert_counts), _ptr(lambda_dev),
                                                   _ptr(loss), _ptr(d_gate_logits), _ptr(frac), _ptr(mean_prob),
                                                   _ptr(probs), B, NH, NE, _ptr(ws), wsb, _stream(stream)))
@@ -318,7 +327,7 @@ def moe_reduce_axis0(inp, out, workspace=None, stream=None):
     _expect(out, "out", (n_tail,), torch.float32)
     need = moe_reduce_axis0_workspace_bytes(n_batch, n_tail)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=inp.device)
+        workspace = _scratch(need, inp.device, stream)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load_library().moe_reduce_axis0(_ptr(inp), n_batch, n_tail, _ptr(out), _ptr(workspace), wsb,
                                            _stream(stream)))
@@ -351,7 +360,7 @@ def moe_top1_bwd_from_mean(d_ctx_mean, fused_ctx, W, expert_offsets, perm, d_fus
     _expect(d_fused_ctx, "d_fused_ctx", (B, NH, H), fused_ctx.dtype)
     _expect(d_W, "d_W", (NE, H, H), torch.float32)
     _expect(d_b, "d_b", (NE, H), torch.float32)
-    ws, wsb = _workspace(workspace, B, NH, H, NE, act, fused_ctx.device)
+    ws, wsb = _workspace(workspace, B, NH, H, NE, act, fused_ctx.device, stream)
     _check(load_library().moe_top1_bwd_from_mean(_ptr(d_ctx_mean), _ptr(fused_ctx), _ptr(W), _ptr(expert_offsets),
                                                  _ptr(perm), _ptr(d_fused_ctx), _ptr(d_W), _ptr(d_b),
                                                  int(bool(accumulate_dx)), B, NH, H, NE, act, _ptr(ws), wsb,
