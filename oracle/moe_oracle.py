@@ -24,6 +24,8 @@ What is computed, and where the pages define it (the commit page
                 inactive experts get exactly zero; d_fused_ctx = W[e*]^T @ d_out
                 (optionally added to a previous d_fused_ctx: the page calls it an
                 accumulator).  The gate logits get no gradient from this path.
+* backward_entries -- the same sums as backward's d_W[e] and d_b[e], restricted to chosen
+                output and input features (for sampled checks of very large inputs).
 * aux        -- summary block: softmax of gate_logits and the load-balancing loss
                 lambda * N_E * sum_e frac_e * mean_prob_e.  The softmax follows the
                 stable form of the softmax/cross-entropy page ("6cfd7e6691"): shift
@@ -116,6 +118,22 @@ def backward(d_out, fused_ctx, W, expert_idx, d_fused_ctx_prev=None) -> BwdResul
         dW[e] = dY[rows].T @ X[rows]
         db[e] = dY[rows].sum(axis=0)
     return BwdResult(dX, dW, db)
+
+
+def backward_entries(d_out_cols, fused_ctx_cols, expert_idx, e: int):
+    """Selected entries of d_W[e] and d_b[e], from the same definition as `backward` (summary
+    block: expert e's gradient sums over its own tokens only), for inputs too large to
+    differentiate whole.  d_out_cols [T, k_o] holds the wanted columns o of d_out for every
+    token, fused_ctx_cols [T, k_i] the wanted columns i of fused_ctx; returns
+        d_W[e][o, i] = sum over tokens t routed to e of d_out[t, o] * fused_ctx[t, i]   [k_o, k_i]
+        d_b[e][o]    = sum over tokens t routed to e of d_out[t, o]                     [k_o]
+    both exactly zero when expert e has no tokens."""
+    dY = np.asarray(d_out_cols, dtype=np.float64)
+    X = np.asarray(fused_ctx_cols, dtype=np.float64)
+    rows = np.asarray(expert_idx).reshape(-1) == e
+    if not rows.any():
+        return np.zeros((dY.shape[1], X.shape[1])), np.zeros(dY.shape[1])
+    return dY[rows].T @ X[rows], dY[rows].sum(axis=0)
 
 
 @dataclass

@@ -1,7 +1,7 @@
 """Pins that tie the CPU oracle to the mathematics, written over an implementation.
 
 Each ``pin_*`` takes an object with the oracle's functions (route, group, forward,
-backward, aux, softmax) and raises AssertionError when it disagrees with a value
+backward, backward_entries, aux, softmax) and raises AssertionError when it disagrees with a value
 that the pages or the mathematics fix.  tests/test_oracle.py runs them against the
 oracle; tests/test_oracle_mutants.py runs them against copies of the oracle with a
 planted mistake and checks that some pin fails.
@@ -209,6 +209,20 @@ def pin_bwd_brute(impl):
     _close(bw.d_fused_ctx, dX, what="brute dX")
     _close(bw.d_W, dW, what="brute dW")
     _close(bw.d_b, db, what="brute db")
+
+
+def pin_bwd_entries_brute(impl):
+    """Selected d_W / d_b entries equal the loop-only oracle's, empty expert included."""
+    X, G, W, b, dY = _tiny(13, B=3, NH=4, H=5, NE=4, ints=True)
+    G[..., 3] = -10.0  # expert 3 gets no tokens
+    idx = impl.route(G, 4)
+    _, dW, db = brute.backward(dY.reshape(-1, 5).tolist(), X.reshape(-1, 5).tolist(), W.tolist(), list(idx))
+    dW, db = np.array(dW), np.array(db)
+    rows, cols = [4, 0, 2], [1, 3]
+    for e in range(4):
+        w, bb = impl.backward_entries(dY.reshape(-1, 5)[:, rows], X.reshape(-1, 5)[:, cols], idx, e)
+        _close(w, dW[e][np.ix_(rows, cols)], what=f"entries dW[{e}]")
+        _close(bb, db[e][rows], what=f"entries db[{e}]")
 
 
 def pin_ste_gate_gets_no_expert_gradient(impl):

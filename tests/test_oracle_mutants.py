@@ -14,7 +14,8 @@ from tests import oracle_pins
 
 def _copy(**repl):
     ns = types.SimpleNamespace(route=O.route, group=O.group, forward=O.forward,
-                               backward=O.backward, aux=O.aux, softmax=O.softmax)
+                               backward=O.backward, backward_entries=O.backward_entries, aux=O.aux,
+                               softmax=O.softmax)
     for k, v in repl.items():
         setattr(ns, k, v)
     return ns
@@ -82,6 +83,19 @@ def _bwd_variant(kind):
     return bwd
 
 
+def _entries_variant(kind):
+    def entries(dYc, Xc, idx, e):
+        dYc = np.asarray(dYc, dtype=np.float64)
+        Xc = np.asarray(Xc, dtype=np.float64)
+        m = np.asarray(idx).reshape(-1) == e
+        if kind == "all_tokens":
+            return dYc.T @ Xc, dYc.sum(axis=0)
+        if kind == "next_expert":
+            m = np.asarray(idx).reshape(-1) == (e + 1) % 4
+        return dYc[m].T @ Xc[m], dYc[m].sum(axis=0)
+    return entries
+
+
 def _aux_variant(kind):
     def aux(G, counts, lam):
         a = O.aux(G, counts, lam)
@@ -126,6 +140,8 @@ MUTANTS = {
     "bwd_dw_mean_not_sum": _copy(backward=_bwd_variant("dw_mean")),
     "bwd_inactive_negative_zero": _copy(backward=_bwd_variant("inactive_negzero")),
     "bwd_ignores_accumulate": _copy(backward=_bwd_variant("no_accumulate")),
+    "bwd_entries_over_all_tokens": _copy(backward_entries=_entries_variant("all_tokens")),
+    "bwd_entries_of_next_expert": _copy(backward_entries=_entries_variant("next_expert")),
     "aux_missing_ne_factor": _copy(aux=_aux_variant("no_ne_factor")),
     "aux_grad_sign": _copy(aux=_aux_variant("grad_sign")),
     "aux_grad_uses_mean_prob": _copy(aux=_aux_variant("grad_uses_mean_prob")),
