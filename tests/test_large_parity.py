@@ -1,0 +1,165 @@
+"""Parity at the largest sizes, in the launch configuration the benchmark times.
+
+* Large stress (1,048,576 tokens, H = 256, N_E = 16, fp32): every element of every output
+  against the fp64 oracle -- routing bit-exact; routed_ctx, d_fused_ctx, d_W and d_b expert
+  by expert (the oracle's forward and backward applied to each expert's own tokens, which
+  is all that expert's outputs depend on); the aux pass whole.  The MoE page's NUMGRAD
+  VERIFICATION block checks the gate at its own size; this is the same check at the largest
+  shape, and with the perf page's Discipline block (results that do not depend on the run).
+* Maximum sizes: bf16 with 2,100,000 tokens at H = 512 (routed_ctx over 2 GiB, so the forward
+  takes the tiled kernel with 64-bit row offsets instead of the resident-slice one) and fp32
+  with 16,776,192 tokens at H = 128 (T * H just under 2^31, the library's limit).  Inputs are
+  drawn on the device (workloads.make_inputs_device); routing and the aux pass are compared
+  whole, routed_ctx and d_fused_ctx on sampled tokens, d_W and d_b on sampled entries of
+  every expert (oracle.backward_entries over all of the expert's tokens).
+"""
+import numpy as np
+import pytest
+
+import workloads
+from oracle import moe_oracle as O
+from tests import compare as C
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+def check_aux_full(got_loss, got_mp, got_frac, got_dg, G, counts, lam):
+    NE = counts.shape[0]
+    T = int(counts.sum())
+    a = O.aux(G, counts, lam)
+    C.elementwise("loss", got_loss, a.loss)
+    C.elementwise("mean_prob", got_mp, a.mean_prob)
+    C.frac_ulp("frac", got_frac, counts, T)
+    scale = T / (lam * NE)
+    C.elementwise("d_gate_logits * T/(lambda N_E)", got_dg.reshape(T, NE) * scale, a.d_gate_logits * scale)
+
+
+# ------------------------------------------------------------------ large stress, in full
+
+@pytest.fixture(scope="module")
+def w5(gpu_lib):
+    from tests import gpu_run
+    wl = workloads.workload(5)
+    print(f"[parity] workload 5 {wl}", flush=True)
+    inp = workloads.make_inputs(wl)
+    got = gpu_run.run(inp)
+    e = O.route(inp.gate_logits, wl.NE)
+    counts, offsets, perm = O.group(e, wl.NE)
+    return inp, got, e, counts, offsets, perm
+
+
+def test_large_stress_routing_and_aux(w5):
+    inp, got, e, counts, offsets, perm = w5
+    C.exact("expert_idx", got["idx"], e)
+    C.exact("counts", got["counts"], counts)
+    C.exact("offsets", got["offsets"], offsets)
+    C.exact("perm", got["perm"], perm)
+    T, NE = inp.wl.T, inp.wl.NE
+    a = O.aux(inp.gate_logits, counts, inp.wl.lam)
+    C.elementwise("probs", got["probs"].reshape(T, NE), a.probs)
+    check_aux_full(got["loss"][0], got["mean_prob"], got["frac"], got["dg"], inp.gate_logits, counts, inp.wl.lam)
+
+
+@pytest.mark.parametrize("half", [0, 1])
+def test_large_stress_every_output_element(w5, half):
+    """routed_ctx, d_fused_ctx, d_W and d_b in full, eight experts per test."""
+    inp, got, e, counts, offsets, perm = w5
+    wl = inp.wl
+    T, H, NE = wl.T, wl.H, wl.NE
+    X = inp.fused_ctx.reshape(T, H)
+    G = inp.gate_logits.reshape(T, NE)
+    dY = inp.d_out.reshape(T, H)
+    Y, dX = got["y"].reshape(T, H), got["dx"].reshape(T, H)
+    literal_fail = 0
+    for x in range(half * NE // 2, (half + 1) * NE // 2):
+        S = perm[offsets[x]:offsets[x + 1]]
+        f = O.forward(X[S], G[S], inp.W, inp.b)
+        assert (f.expert_idx == x).all()
+        C.elementwise(f"routed_ctx[expert {x}]", Y[S], f.routed_ctx)
+        bw = O.backward(dY[S], X[S], inp.W, f.expert_idx)
+        C.elementwise(f"d_fused_ctx[expert {x}]", dX[S], bw.d_fused_ctx)
+        C.per_expert_scaled(f"d_W[expert {x}]", got["dW"][x:x + 1], bw.d_W[x:x + 1])
+        C.per_expert_scaled(f"d_b[expert {x}]", got["db"][x:x + 1], bw.d_b[x:x + 1])
+        # the literal elementwise rule, as a diagnostic (the long sums are held to the
+        # RMS-scaled rule above)
+        o = bw.d_W[x]
+        literal_fail += int((np.abs(got["dW"][x] - o) > 1e-5 + 1e-4 * np.abs(o)).sum())
+    print(f"[parity] d_W entries outside the literal 1e-4 / 1e-5 rule: {literal_fail} of {NE // 2 * H * H}",
+          flush=True)
+
+
+# ------------------------------------------------------------------ maximum sizes
+
+def _sample_rows(T, perm, offsets, n=4096, seed=123):
+    rng = np.random.default_rng(seed)
+    rows = rng.choice(T, n, replace=False)
+    inner = offsets[1:-1]
+    edges = np.concatenate([perm[inner[(inner > 0) & (inner < T)] - 1], perm[inner[(inner > 0) & (inner < T)]]])
+    return np.unique(np.concatenate([rows, [0, T - 1], edges]))
+
+
+def _max_size_check(wl, tol_kind):
+    import torch
+    from tests import gpu_run
+    print(f"[parity] maximum size {wl}", flush=True)
+    di = workloads.make_inputs_device(wl)
+    d = gpu_run.wrap(di)
+    o = gpu_run.Buffers(d, poison=False)
+    gpu_run.step(d, o)
+    torch.cuda.synchronize()
+    T, H, NE = wl.T, wl.H, wl.NE
+    host = gpu_run.to_host
+    G = host(d.g).reshape(T, NE)
+    e = O.route(G, NE)
+    counts, offsets, perm = O.group(e, NE)
+    C.exact("expert_idx", host(o.idx), e)
+    C.exact("counts", host(o.counts), counts)
+    C.exact("offsets", host(o.offsets), offsets)
+    C.exact("perm", host(o.perm), perm)
+    check_aux_full(host(o.loss)[0], host(o.mean_prob), host(o.frac), host(o.dg), G, counts, wl.lam)
+
+    W, b = host(d.W), host(d.b)
+    rows = _sample_rows(T, perm, offsets)
+    ri = torch.from_numpy(rows).to(d.x.device)
+    x2, dy2 = d.x.view(T, H), d.dy.view(T, H)
+    Xs, dYs = host(x2.index_select(0, ri)), host(dy2.index_select(0, ri))
+    f = O.forward(Xs, G[rows], W, b)
+    bw = O.backward(dYs, Xs, W, f.expert_idx)
+    ys, dxs = host(o.y.view(T, H).index_select(0, ri)), host(o.dx.view(T, H).index_select(0, ri))
+    if tol_kind == "bf16":
+        C.bf16_scaled("routed_ctx[sample]", ys, f.routed_ctx)
+        C.bf16_scaled("d_fused_ctx[sample]", dxs, bw.d_fused_ctx)
+    else:
+        C.elementwise("routed_ctx[sample]", ys, f.routed_ctx)
+        C.elementwise("d_fused_ctx[sample]", dxs, bw.d_fused_ctx)
+
+    rng = np.random.default_rng(7)
+    orow = np.sort(rng.choice(H, 8, replace=False))
+    icol = np.sort(rng.choice(H, 16, replace=False))
+    dYc = host(dy2.index_select(1, torch.from_numpy(orow).to(d.x.device)))
+    Xc = host(x2.index_select(1, torch.from_numpy(icol).to(d.x.device)))
+    gdW, gdb = host(o.dW), host(o.db)
+    for x in range(NE):
+        w_ref, b_ref = O.backward_entries(dYc, Xc, e, x)
+        w_got, b_got = gdW[x][np.ix_(orow, icol)], gdb[x][orow]
+        if tol_kind == "bf16":
+            C.bf16_scaled(f"d_W[{x}][sampled entries]", w_got, w_ref)
+            C.bf16_scaled(f"d_b[{x}][sampled entries]", b_got, b_ref)
+        else:
+            C.per_expert_scaled(f"d_W[{x}][sampled entries]", w_got[None], w_ref[None])
+            C.per_expert_scaled(f"d_b[{x}][sampled entries]", b_got[None], b_ref[None])
+
+
+def test_max_size_bf16_over_2gib(gpu_lib):
+    """2,100,000 tokens x 512 bf16: routed_ctx is 2.15 GB, past the resident-slice forward's
+    32-bit byte offsets, so the tiled forward runs."""
+    wl = workloads.custom(420000, 5, 512, 8, act="bf16", seed=2101)
+    assert wl.T * wl.H * 2 >= 2 ** 31 and wl.T * wl.H < 2 ** 31
+    _max_size_check(wl, "bf16")
+
+
+def test_max_size_fp32_at_the_limit(gpu_lib):
+    """16,776,192 tokens x 128 fp32: T * H = 2^31 - 131,072, the largest shape the library takes."""
+    wl = workloads.custom(2796032, 6, 128, 4, seed=2102)
+    assert 2 ** 31 - 2 ** 18 < wl.T * wl.H < 2 ** 31
+    _max_size_check(wl, "f32")

@@ -2,8 +2,8 @@
 
 Small shapes are compared element by element on every output; they span several
 128-row tiles, several d_W chunks per expert and ragged tails.  The full-size workloads
-are compared in the launch configuration the benchmark times: completely where the
-oracle is quick, and on sampled rows otherwise.
+are compared whole in the launch configuration the benchmark times (the large-stress one
+and the maximum sizes in tests/test_large_parity.py).
 """
 import numpy as np
 import pytest
@@ -221,44 +221,3 @@ def test_small_tile_persistent_paths_full_parity(gpu_lib):
     print(f"[parity] small-tile persistent {wl}", flush=True)
     inp = workloads.make_inputs(wl)
     check_all(inp, gpu_run.run(inp))
-
-
-@pytest.mark.slow
-def test_large_stress_sampled_parity(gpu_lib):
-    """1,048,576 tokens, H=256, N_E=16: routing and the aux pass in full; routed_ctx and
-    d_fused_ctx on sampled tokens; d_b in full; d_W on sampled output rows of every expert."""
-    from tests import gpu_run
-    wl = workloads.workload(5)
-    print(f"[parity] workload 5 {wl}", flush=True)
-    inp = workloads.make_inputs(wl)
-    got = gpu_run.run(inp)
-    T, H, NE = wl.T, wl.H, wl.NE
-    e = O.route(inp.gate_logits, NE)
-    counts, offsets, perm = O.group(e, NE)
-    C.exact("expert_idx", got["idx"], e)
-    C.exact("counts", got["counts"], counts)
-    C.exact("offsets", got["offsets"], offsets)
-    C.exact("perm", got["perm"], perm)
-    rng = np.random.default_rng(123)
-    rows = np.sort(rng.choice(T, 4096, replace=False))
-    rows = np.concatenate([rows, [0, T - 1], perm[offsets[1:-1] - 1], perm[offsets[1:-1]]])
-    X = inp.fused_ctx.reshape(T, H)
-    dY = inp.d_out.reshape(T, H)
-    fs = O.forward(X[rows], inp.gate_logits.reshape(T, NE)[rows], inp.W, inp.b)
-    C.elementwise("routed_ctx[sample]", got["y"].reshape(T, H)[rows], fs.routed_ctx)
-    bs = O.backward(dY[rows], X[rows], inp.W, e[rows])
-    C.elementwise("d_fused_ctx[sample]", got["dx"].reshape(T, H)[rows], bs.d_fused_ctx)
-    # d_b in full and d_W on 8 sampled output rows per expert, tolerance scaled by the
-    # RMS of the sampled slice
-    gdW, gdb = got["dW"], got["db"]
-    db = np.zeros((NE, H))
-    for x in range(NE):
-        S = perm[offsets[x]:offsets[x + 1]]
-        dYe = dY[S].astype(np.float64)
-        db[x] = dYe.sum(axis=0)
-        orows = rng.choice(H, 8, replace=False)
-        ref = dYe[:, orows].T @ X[S].astype(np.float64)
-        C.per_expert_scaled(f"d_W[{x}][sampled rows]", gdW[x][orows][None], ref[None])
-    C.per_expert_scaled("d_b", gdb, db)
-    a = O.aux(inp.gate_logits, counts, wl.lam)
-    check_aux(inp, got, a, counts)

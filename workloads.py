@@ -148,3 +148,48 @@ def custom(B: int, NH: int, H: int, NE: int, *, act: str = "f32", gate: str = "n
     """A small workload with the same distributions, for edge cases and tests."""
     return Workload(f"custom_{B}x{NH}x{H}x{NE}_{act}", B=B, NH=NH, H=H, NE=NE, act=act,
                     gate=gate, lam=lam, seed=seed, **kw)
+
+
+@dataclass
+class DeviceInputs:
+    """Inputs drawn on the GPU (torch tensors), for sizes too large to draw on the host in the
+    time a test has: same shapes, distributions and draw order as make_inputs, from torch's
+    counter-based device generator instead of numpy's; bf16 tensors are rounded from fp32
+    with round to nearest even (torch's conversion)."""
+    wl: Workload
+    fused_ctx: "object"
+    gate_logits: "object"
+    W: "object"
+    b: "object"
+    d_out: "object"
+
+
+def make_inputs_device(wl: Workload, device="cuda", seed: Optional[int] = None) -> DeviceInputs:
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(wl.seed if seed is None else seed)
+    B, NH, H, NE = wl.B, wl.NH, wl.H, wl.NE
+    bound = 1.0 / float(np.sqrt(H))
+    act = torch.bfloat16 if wl.act == "bf16" else torch.float32
+
+    def normal(shape, std=1.0):
+        t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        return t.mul_(std) if std != 1.0 else t
+
+    def uniform(shape):
+        return torch.rand(shape, generator=g, device=device, dtype=torch.float32).mul_(2 * bound).sub_(bound)
+
+    x = normal((B, NH, H)).to(act)
+    if wl.gate == "int":
+        gl = torch.randint(-2, 3, (B, NH, NE), generator=g, device=device).to(torch.float32)
+    else:
+        gl = normal((B, NH, NE), wl.gate_std)
+    if wl.gate_offset_range > 0.0:
+        r = wl.gate_offset_range
+        gl += torch.rand(NE, generator=g, device=device, dtype=torch.float32) * (2 * r) - r
+    for e, v in wl.gate_bias.items():
+        gl[..., e] += v
+    w = uniform((NE, H, H)).to(act)
+    bias = uniform((NE, H))
+    dy = normal((B, NH, H)).to(act)
+    return DeviceInputs(wl, x.contiguous(), gl.contiguous(), w.contiguous(), bias.contiguous(), dy.contiguous())
