@@ -120,6 +120,26 @@ moe_status_t moe_top1_fwd(const void* fused_ctx, const float* gate_logits, const
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * moe_top1_fwd without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same operation, outputs and kernels as moe_top1_fwd, bit for bit.  Its scratch (the routing
+ * histograms and block bases, 2 * ceil(T / 256) * N_E int32, each part rounded up to 256
+ * bytes) lives in an 8 MiB device array inside the library, one per device, held from the
+ * first call on that device until the process ends; that first call looks up the array's
+ * address (hipGetSymbolAddress: no allocation) and should be made before any graph capture.
+ * The call allocates and frees nothing.  Every call on one device uses that device's one
+ * array, so calls that may overlap on a device (different streams, different host threads)
+ * race: serialise them.  Shapes whose scratch exceeds the array (ceil(T / 256) * N_E above
+ * about one million entries) return MOE_ERR_WORKSPACE before anything is launched; other
+ * errors as moe_top1_fwd.
+ */
+moe_status_t moe_top1_fwd_noalloc(const void* fused_ctx, const float* gate_logits, const void* W,
+                                  const float* b, void* routed_ctx,
+                                  int32_t* expert_idx, int32_t* expert_counts, int32_t* expert_offsets,
+                                  int32_t* perm,
+                                  int64_t B, int64_t NH, int64_t H, int64_t NE, int act, void* stream);
+
+/*
  * Backward pass (summary and ARCHITECTURE blocks of the MoE-gate page), given the
  * expert_offsets and perm written by moe_top1_fwd for the same tokens:
  *   d_fused_ctx[t, :] = W[e*(t)]^T @ d_routed_ctx[t, :]      (overwritten, or added to

@@ -14,7 +14,7 @@ from typing import Optional
 
 __all__ = [
     "load_library", "library_path", "moe_abi_version", "moe_workspace_bytes", "moe_top1_route",
-    "moe_top1_fwd", "moe_top1_bwd", "moe_aux_loss", "moe_set_launch_timer", "moe_kernel_name",
+    "moe_top1_fwd", "moe_top1_fwd_noalloc", "moe_top1_bwd", "moe_aux_loss", "moe_set_launch_timer", "moe_kernel_name",
     "moe_lambda_eff_update", "moe_aux_loss_lambda_dev", "moe_reduce_axis0", "moe_reduce_axis0_workspace_bytes",
     "moe_horizon_mean_collapse_fwd", "moe_horizon_mean_collapse_bwd", "moe_top1_bwd_from_mean",
     "moe_softmax_ce_grad", "MoeError", "KERNELS", "DTYPE_F32", "DTYPE_BF16",
@@ -59,6 +59,7 @@ def load_library() -> ctypes.CDLL:
         "moe_workspace_bytes": ([I64, I64, I64, I64, I32, ctypes.POINTER(SZ)], I32),
         "moe_top1_route": ([P, P, P, P, P, I64, I64, I64, P, SZ, P], I32),
         "moe_top1_fwd": ([P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I32, P, SZ, P], I32),
+        "moe_top1_fwd_noalloc": ([P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I32, P], I32),
         "moe_top1_bwd": ([P, P, P, P, P, P, P, P, I32, I64, I64, I64, I64, I32, P, SZ, P], I32),
         "moe_aux_loss": ([P, P, ctypes.c_float, P, P, P, P, P, I64, I64, I64, P, SZ, P], I32),
         "moe_set_launch_timer": ([I32, P, P], I32),
@@ -212,6 +213,29 @@ def moe_top1_fwd(fused_ctx, gate_logits, W, b, routed_ctx, expert_idx, expert_co
     _check(load_library().moe_top1_fwd(_ptr(fused_ctx), _ptr(gate_logits), _ptr(W), _ptr(b), _ptr(routed_ctx),
                                        _ptr(expert_idx), _ptr(expert_counts), _ptr(expert_offsets), _ptr(perm),
                                        B, NH, H, NE, act, _ptr(ws), wsb, _stream(stream)))
+
+
+def moe_top1_fwd_noalloc(fused_ctx, gate_logits, W, b, routed_ctx, expert_idx, expert_counts, expert_offsets, perm,
+                         stream=None):
+    """moe_top1_fwd with its scratch in the library's per-device array: no workspace argument,
+    nothing allocated (calls that overlap on one device race)."""
+    import torch
+    B, NH, H = _shape3(fused_ctx, "fused_ctx")
+    NE = int(gate_logits.shape[-1])
+    T = B * NH
+    act = _act(fused_ctx)
+    _expect(gate_logits, "gate_logits", (B, NH, NE), torch.float32)
+    _expect(W, "W", (NE, H, H), fused_ctx.dtype)
+    _expect(b, "b", (NE, H), torch.float32)
+    _expect(routed_ctx, "routed_ctx", (B, NH, H), fused_ctx.dtype)
+    _expect(expert_idx, "expert_idx", (T,), torch.int32)
+    _expect(expert_counts, "expert_counts", (NE,), torch.int32)
+    _expect(expert_offsets, "expert_offsets", (NE + 1,), torch.int32)
+    _expect(perm, "perm", (T,), torch.int32)
+    _check(load_library().moe_top1_fwd_noalloc(_ptr(fused_ctx), _ptr(gate_logits), _ptr(W), _ptr(b),
+                                               _ptr(routed_ctx), _ptr(expert_idx), _ptr(expert_counts),
+                                               _ptr(expert_offsets), _ptr(perm), B, NH, H, NE, act,
+                                               _stream(stream)))
 
 
 def moe_top1_fwd_aux(fused_ctx, gate_logits, W, b, routed_ctx, expert_idx, expert_counts, expert_offsets, perm,

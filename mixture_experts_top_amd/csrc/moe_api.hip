@@ -6,6 +6,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "moe_internal.hpp"
 
 namespace moe {
@@ -174,6 +176,38 @@ static moe_status_t do_route(const float* G, int32_t* idx, int32_t* counts, int3
     return MOE_OK;
 }
 
+// ---------------------------------------------------------------- allocation-free forward
+// The forward pass's scratch (routing histograms and block bases) in a file-scope device
+// array instead of a caller's workspace.  Each device the library runs on holds its own copy
+// of the array for the life of the process; its address on the current device is looked up
+// once (hipGetSymbolAddress) at the first call there.  Every call on a device shares that
+// device's array: calls that overlap on one device race.  The kernels write every scratch
+// word they later read (one histogram row per routing block, then the block bases), so
+// nothing needs clearing between calls.
+constexpr size_t kNoAllocScratchBytes = (size_t)8 << 20;  // 8 MiB per device
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+static constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices] = {};
+
+static moe_status_t scratch_on_current_device(const char* fn, void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "%s: device %d out of range", fn, dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!ptr) return fail(MOE_ERR_HIP, "%s: scratch address is NULL", fn);
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -260,18 +294,23 @@ static moe_status_t fwd_gemm_only(const void* fused_ctx, const void* W, const fl
     return MOE_OK;
 }
 
-moe_status_t moe_top1_fwd(const void* fused_ctx, const float* gate_logits, const void* W, const float* b,
-                          void* routed_ctx, int32_t* expert_idx, int32_t* expert_counts,
-                          int32_t* expert_offsets, int32_t* perm, int64_t B, int64_t NH, int64_t H,
-                          int64_t NE, int act, void* workspace, size_t workspace_bytes, void* stream) {
-    const char* fn = "moe_top1_fwd";
+// Arguments of the forward pass checked (shape, pointers); nothing is launched.
+static moe_status_t check_fwd_args(const char* fn, const void* fused_ctx, const float* gate_logits, const void* W,
+                                   const float* b, const void* routed_ctx, const int32_t* expert_idx,
+                                   const int32_t* expert_counts, const int32_t* expert_offsets, const int32_t* perm,
+                                   int64_t B, int64_t NH, int64_t H, int64_t NE, int act) {
     moe_status_t st = check_shape(fn, B, NH, H, NE, act, true);
     if (st != MOE_OK) return st;
     REQ(fused_ctx); REQ(gate_logits); REQ(W); REQ(b); REQ(routed_ctx);
     REQ(expert_idx); REQ(expert_counts); REQ(expert_offsets); REQ(perm);
-    const Plan p = make_plan(B * NH, (int)H, (int)NE, act);
-    if ((st = check_ws(fn, p, workspace, workspace_bytes)) != MOE_OK) return st;
-    hipStream_t s = (hipStream_t)stream;
+    return MOE_OK;
+}
+
+// The forward pass once its arguments are checked; it uses the routing sections of the
+// workspace only (histograms and block bases: the plan's bytes below off_idx).
+static moe_status_t fwd_launch(const void* fused_ctx, const float* gate_logits, const void* W, const float* b,
+                               void* routed_ctx, int32_t* expert_idx, int32_t* expert_counts, int32_t* expert_offsets,
+                               int32_t* perm, const Plan& p, int act, void* workspace, hipStream_t s) {
     if (act == MOE_DTYPE_F32 && fwd_gemm_f32_gather_fits(p.T, p.H, p.NE, p.n_rblk)) {
         // routing, then one forward launch that also forms perm, counts and offsets
         int32_t* hist = at<int32_t>(workspace, p.off_hist);
@@ -283,9 +322,44 @@ moe_status_t moe_top1_fwd(const void* fused_ctx, const float* gate_logits, const
                "fwd gemm");
         return MOE_OK;
     }
-    if ((st = do_route(gate_logits, expert_idx, expert_counts, expert_offsets, perm, p, workspace, s)) != MOE_OK)
-        return st;
+    moe_status_t st = do_route(gate_logits, expert_idx, expert_counts, expert_offsets, perm, p, workspace, s);
+    if (st != MOE_OK) return st;
     return fwd_gemm_only(fused_ctx, W, b, routed_ctx, expert_offsets, perm, p, act, s);
+}
+
+moe_status_t moe_top1_fwd(const void* fused_ctx, const float* gate_logits, const void* W, const float* b,
+                          void* routed_ctx, int32_t* expert_idx, int32_t* expert_counts,
+                          int32_t* expert_offsets, int32_t* perm, int64_t B, int64_t NH, int64_t H,
+                          int64_t NE, int act, void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "moe_top1_fwd";
+    moe_status_t st = check_fwd_args(fn, fused_ctx, gate_logits, W, b, routed_ctx, expert_idx, expert_counts,
+                                     expert_offsets, perm, B, NH, H, NE, act);
+    if (st != MOE_OK) return st;
+    const Plan p = make_plan(B * NH, (int)H, (int)NE, act);
+    if ((st = check_ws(fn, p, workspace, workspace_bytes)) != MOE_OK) return st;
+    return fwd_launch(fused_ctx, gate_logits, W, b, routed_ctx, expert_idx, expert_counts, expert_offsets, perm, p,
+                      act, workspace, (hipStream_t)stream);
+}
+
+
+moe_status_t moe_top1_fwd_noalloc(const void* fused_ctx, const float* gate_logits, const void* W, const float* b,
+                                  void* routed_ctx, int32_t* expert_idx, int32_t* expert_counts,
+                                  int32_t* expert_offsets, int32_t* perm, int64_t B, int64_t NH, int64_t H,
+                                  int64_t NE, int act, void* stream) {
+    const char* fn = "moe_top1_fwd_noalloc";
+    moe_status_t st = check_fwd_args(fn, fused_ctx, gate_logits, W, b, routed_ctx, expert_idx, expert_counts,
+                                     expert_offsets, perm, B, NH, H, NE, act);
+    if (st != MOE_OK) return st;
+    const Plan p = make_plan(B * NH, (int)H, (int)NE, act);
+    if (p.off_idx > kNoAllocScratchBytes)
+        return fail(MOE_ERR_WORKSPACE,
+                    "%s: the routing scratch for ceil(T/256) * N_E = %lld histogram entries needs %zu bytes, more than "
+                    "the %zu-byte device array; use moe_top1_fwd with a workspace",
+                    fn, (long long)p.n_rblk * NE, p.off_idx, kNoAllocScratchBytes);
+    void* ws = nullptr;
+    if ((st = scratch_on_current_device(fn, &ws)) != MOE_OK) return st;
+    return fwd_launch(fused_ctx, gate_logits, W, b, routed_ctx, expert_idx, expert_counts, expert_offsets, perm, p,
+                      act, ws, (hipStream_t)stream);
 }
 
 static moe_status_t bwd_impl(const char* fn, const void* dy, int from_mean, const void* fused_ctx, const void* W,
