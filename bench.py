@@ -95,14 +95,27 @@ def measured_traffic(kernel, wl):
     return rec.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(inp, budget_s=12.0):
-    """The oracle as it stands, on this host's cores, over a bounded sample of the workload."""
-    import numpy as np
+def cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(inp, budget_s=12.0, single_budget_s=4.0):
+    """The oracle as it stands, on this host's cores, over a bounded sample of the workload;
+    then the same sample with the BLAS library held to one thread."""
     from oracle import moe_oracle as O
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:  # pragma: no cover
+        threadpool_limits = None
         cores = 1
     wl = inp.wl
     T = wl.T
@@ -114,17 +127,29 @@ def cpu_baseline(inp, budget_s=12.0):
     one = time.perf_counter() - t0
     if one > budget_s:
         n = max(1024, int(T * budget_s / one / 2))
-    reps, tok, el = 0, 0, 0.0
-    while el < budget_s and reps < 1000:
-        t0 = time.perf_counter()
-        f = O.forward(x[:n], g[:n], inp.W, inp.b)
-        O.backward(dy[:n], x[:n], inp.W, f.expert_idx)
-        O.aux(g[:n], f.counts, wl.lam)
-        el += time.perf_counter() - t0
-        reps += 1
-        tok += n
-    return {"value": tok / el, "unit": "routed tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{reps} x fwd+bwd+aux over the first {n} of {T} tokens ({el:.1f} s, fp64 NumPy)"}
+
+    def run(budget):
+        reps, tok, el = 0, 0, 0.0
+        while el < budget and reps < 1000:
+            t0 = time.perf_counter()
+            f = O.forward(x[:n], g[:n], inp.W, inp.b)
+            O.backward(dy[:n], x[:n], inp.W, f.expert_idx)
+            O.aux(g[:n], f.counts, wl.lam)
+            el += time.perf_counter() - t0
+            reps += 1
+            tok += n
+        return tok / el, reps, el
+
+    rate, reps, el = run(budget_s)
+    out = {"value": rate, "unit": "routed tokens/s", "cores": int(cores), "kind": "oracle",
+           "sample": f"{reps} x fwd+bwd+aux over the first {n} of {T} tokens ({el:.1f} s, fp64 NumPy)",
+           "cpu_model": cpu_model(), "host_threads": len(os.sched_getaffinity(0))}
+    if threadpool_limits is not None and single_budget_s > 0:
+        with threadpool_limits(limits=1, user_api="blas"):
+            r1, reps1, el1 = run(single_budget_s)
+        out["single_thread"] = {"value": r1, "unit": "routed tokens/s", "cores": 1,
+                                "sample": f"{reps1} x the same sample ({el1:.1f} s)"}
+    return out
 
 
 def bench_row(args):
@@ -223,86 +248,37 @@ def bench_row(args):
     print(json.dumps(out), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=2)
-    ap.add_argument("--graph", action="store_true", help="replay the step as one captured HIP graph")
-    ap.add_argument("--aux-stream", action="store_true",
-                    help="run the auxiliary loss on a second stream, overlapping the backward (default: "
-                         "after it, on one stream; the cross-stream join costs more than it hides at the "
-                         "pages' shape)")
-    ap.add_argument("--separate-aux", action="store_true",
-                    help="make the forward, backward and aux-loss calls one by one instead of "
-                         "moe_top1_fwd_aux + moe_top1_bwd")
-    ap.add_argument("--cold-mib", type=int, default=512,
-                    help="after the timed region, also time steps that each follow a write of this many MiB "
-                         "(evicting L2 and the 256 MB Infinity Cache); 0 skips it")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--calib-copy-mib", type=int, default=0,
-                    help="run a plain device copy of this size first (counter calibration under rocprofv3 --pmc)")
-    ap.add_argument("--skip-kernel-survey", action="store_true",
-                    help="do not time every kernel first; time --kernel in the timed region")
-    ap.add_argument("--kernel", default=None, help="kernel timed live in the timed region (default: the slowest)")
-    ap.add_argument("--timer-every", type=int, default=5,
-                    help="time the dominant kernel with HIP events in every n-th step of the timed region")
-    ap.add_argument("--row", default="gate",
-                    help="gate (default) | reduce_axis0 | collapse_fwd | collapse_bwd | softmax_ce")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the library has no multi-GPU path (run with --gpus 1)",
-              file=sys.stderr)
-        sys.exit(2)
-
+def measure_gate(wl, d, o, args, K, warmup, cold_reps, survey=True, kernel=None):
+    """Times K steps of the gate's hot path on the resident inputs d (outputs and workspace o):
+    warm-up, a per-kernel survey that finds the dominant kernel (outside the timed region), the
+    timed region with that kernel's own start/end events in every `--timer-every`-th step, and
+    (cold_reps > 0) steps that each follow a large write evicting L2 and the Infinity Cache,
+    with the step and the dominant kernel timed."""
     import numpy as np
     import torch
 
     import mixture_experts_top_amd as moe
-    import workloads
     from mixture_experts_top_amd import runner as gpu_run
-
-    if not torch.cuda.is_available():
-        log("no GPU visible")
-        sys.exit(1)
-    if args.row != "gate":
-        bench_row(args)
-        return
-    moe.load_library()
-    wl = workloads.workload(args.workload)
-    log(f"[bench] workload {args.workload}: {wl}")
-    inp = workloads.make_inputs(wl)
-    d = gpu_run.upload(inp)
-    o = gpu_run.Buffers(d, poison=False)
     stream = torch.cuda.current_stream()
     aux_stream = torch.cuda.Stream() if args.aux_stream else None  # default priority
 
     def step():  # the optional probs output is not requested: the aux pass writes dG only
         gpu_run.step(d, o, probs=False, aux_stream=aux_stream, fused=not args.separate_aux)
 
-    if args.calib_copy_mib:
-        n = args.calib_copy_mib << 20
-        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"[bench] calibration copy: {args.calib_copy_mib} MiB read + {args.calib_copy_mib} MiB written, 3 launches")
-        del src, dst
-
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
 
     # per-kernel averages (outside the timed region) to find the dominant kernel
     nk = 10
     kern_us = {}
     gate_kernels = ["route", "scan", "scatter", "fwd_gemm", "bwd_gemm", "reduce", "aux", "aux_final"]
-    for k in ([] if args.skip_kernel_survey else gate_kernels):
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nk)]
-        marks = [torch.cuda.Event(enable_timing=True) for _ in range(nk)]
+    for k in (gate_kernels if survey else []):
+        evs = [(ev(), ev()) for _ in range(nk)]
+        marks = [ev() for _ in range(nk)]
         for a, b in evs:
             a.record(); b.record()
         torch.cuda.synchronize()
@@ -318,14 +294,12 @@ def main():
         vals = [a.elapsed_time(b) for (a, b), m in zip(evs, marks) if m.elapsed_time(a) >= 0]
         if vals:
             kern_us[k] = float(np.mean(vals) * 1e3)
-    if args.kernel:
-        dom = args.kernel
+    if kernel:
+        dom = kernel
     elif kern_us:
-        dom = max((k for k in kern_us if k in ("fwd_gemm", "bwd_gemm", "aux", "reduce")),
-                  key=lambda k: kern_us[k])
+        dom = max((k for k in kern_us if k in ("fwd_gemm", "bwd_gemm", "aux", "reduce")), key=lambda k: kern_us[k])
     else:
         dom = "fwd_gemm"
-    log("[bench] kernel avg us: " + ", ".join(f"{k}={v:.2f}" for k, v in kern_us.items()) + f"; dominant={dom}")
 
     graph = None
     if args.graph:
@@ -338,16 +312,15 @@ def main():
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             step()
-        for _ in range(args.warmup):
+        for _ in range(warmup):
             graph.replay()
         torch.cuda.synchronize()
 
-    # timed region: K steps; the dominant kernel is bracketed by a pair of events in every
+    # timed region: K steps; the dominant kernel carries a pair of events in every
     # `--timer-every`-th step (each pair adds its own GPU commands to the step it sits in)
-    K = args.steps
     every = max(1, args.timer_every)
     timed = [i for i in range(K) if i % every == 0]
-    evs = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for i in timed}
+    evs = {i: (ev(), ev()) for i in timed}
     for a, b in evs.values():
         a.record(); b.record()
     torch.cuda.synchronize()
@@ -369,15 +342,154 @@ def main():
         dom_us = float(np.mean([a.elapsed_time(b) for a, b in evs.values()]) * 1e3)
     else:
         dom_us = kern_us.get(dom, float("nan"))
+
+    # cold caches: the inputs are still in HBM, but a large write before each step evicts them
+    # from L2 and the 256 MB Infinity Cache first; the step and its dominant kernel are timed
+    cold = None
+    if cold_reps > 0 and args.cold_mib > 0 and graph is None:
+        flush = torch.empty(args.cold_mib << 18, dtype=torch.float32, device="cuda")
+        # the steps alone first (a kernel timer adds work to the step it sits in), then as many
+        # again with the dominant kernel's own start / end events
+        evc = [(ev(), ev()) for _ in range(cold_reps)]
+        evk = [(ev(), ev()) for _ in range(cold_reps)]
+        for c, e in evk:
+            c.record(); e.record()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(evc):
+            flush.fill_(float(i))
+            a.record()
+            step()
+            b.record()
+        for i, (c, e) in enumerate(evk):
+            flush.fill_(float(i))
+            moe.moe_set_launch_timer(dom, c, e)
+            step()
+            moe.moe_set_launch_timer(None)
+        torch.cuda.synchronize()
+        cold_us = sorted(a.elapsed_time(b) * 1e3 for a, b in evc)
+        cold_k = sorted(c.elapsed_time(e) * 1e3 for c, e in evk)
+        cold = {"median_us": cold_us[cold_reps // 2], "min_us": cold_us[0], "flush_mib": args.cold_mib,
+                "routed_tokens_per_s": wl.T / (cold_us[cold_reps // 2] * 1e-6), "steps": cold_reps,
+                "kernel": dom, "kernel_median_us": cold_k[cold_reps // 2]}
+        del flush
+    return {"ms": ms, "dom": dom, "dom_us": dom_us, "kern_us": kern_us, "timed_launches": len(evs) if graph is None
+            else 0, "graph": graph is not None, "aux_stream": aux_stream is not None, "cold": cold, "step": step}
+
+
+def kernel_roofline(dom, dom_us, wl):
     amount, unit, bound = algorithmic(dom, wl)
     if bound == "mfma":
         achieved = amount / (dom_us * 1e-6) / 1e12
-        peak = PEAK_TFLOPS[wl.act]
-        runit = "TFLOP/s"
-    else:
-        achieved = amount / (dom_us * 1e-6) / 1e9
-        peak = PEAK_HBM_GBS
-        runit = "GB/s"
+        return bound, achieved, PEAK_TFLOPS[wl.act], "TFLOP/s", amount, unit
+    achieved = amount / (dom_us * 1e-6) / 1e9
+    return bound, achieved, PEAK_HBM_GBS, "GB/s", amount, unit
+
+
+def largest_config(args):
+    """The large-stress workload (1,048,576 tokens, H = 256, N_E = 16, fp32), the largest
+    configuration the headline target is quoted on: its step, dominant kernel and roofline
+    fractions, measured the same way as the headline (a sub-record of the one JSON line)."""
+    import torch
+
+    import workloads
+    from mixture_experts_top_amd import runner as gpu_run
+    wl = workloads.workload(5)
+    log(f"[bench] largest config: {wl}")
+    d = gpu_run.upload(workloads.make_inputs(wl))
+    o = gpu_run.Buffers(d, poison=False)
+    m = measure_gate(wl, d, o, args, K=args.largest_steps, warmup=3, cold_reps=5)
+    roof = pass_roofline_us(wl)
+    bound, achieved, peak, runit, amount, unit = kernel_roofline(m["dom"], m["dom_us"], wl)
+    out = {"workload": wl.name, "B": wl.B, "N_H": wl.NH, "H": wl.H, "N_E": wl.NE, "T": wl.T, "act": wl.act,
+           "steps": args.largest_steps, "ms_per_step": m["ms"], "routed_tokens_per_s": wl.T / (m["ms"] * 1e-3),
+           "step_roofline_us": sum(roof.values()), "step_roofline_frac": sum(roof.values()) / (m["ms"] * 1e3),
+           "kernel": m["dom"], "kernel_avg_us": m["dom_us"], "kernel_achieved": achieved, "kernel_peak": peak,
+           "kernel_unit": runit, "kernel_frac": achieved / peak, "kernel_timed_launches": m["timed_launches"],
+           "kernel_traffic": measured_traffic(m["dom"], wl), "kernels_avg_us": m["kern_us"],
+           "cold_cache_step": m["cold"]}
+    if m["cold"]:
+        kb = kernel_roofline(m["dom"], m["cold"]["kernel_median_us"], wl)
+        out["cold_cache_step"]["kernel_frac"] = kb[1] / kb[2]
+        out["cold_cache_step"]["step_roofline_frac"] = sum(roof.values()) / m["cold"]["median_us"]
+    del d, o
+    torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--graph", action="store_true", help="replay the step as one captured HIP graph")
+    ap.add_argument("--aux-stream", action="store_true",
+                    help="run the auxiliary loss on a second stream, overlapping the backward (default: "
+                         "after it, on one stream; the cross-stream join costs more than it hides at the "
+                         "pages' shape)")
+    ap.add_argument("--separate-aux", action="store_true",
+                    help="make the forward, backward and aux-loss calls one by one instead of "
+                         "moe_top1_fwd_aux + moe_top1_bwd")
+    ap.add_argument("--cold-mib", type=int, default=512,
+                    help="also time steps that each follow a write of this many MiB (evicting L2 and the "
+                         "256 MB Infinity Cache); 0 skips them")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--cpu-single-budget", type=float, default=4.0,
+                    help="seconds of the single-thread oracle timing (0 skips it)")
+    ap.add_argument("--largest", choices=["auto", "none"], default="auto",
+                    help="auto: also measure the large-stress workload (sub-record largest_config) when the "
+                         "headline workload is another one")
+    ap.add_argument("--largest-steps", type=int, default=20)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run a plain device copy of this size first (counter calibration under rocprofv3 --pmc)")
+    ap.add_argument("--skip-kernel-survey", action="store_true",
+                    help="do not time every kernel first; time --kernel in the timed region")
+    ap.add_argument("--kernel", default=None, help="kernel timed live in the timed region (default: the slowest)")
+    ap.add_argument("--timer-every", type=int, default=5,
+                    help="time the dominant kernel with HIP events in every n-th step of the timed region")
+    ap.add_argument("--row", default="gate",
+                    help="gate (default) | reduce_axis0 | collapse_fwd | collapse_bwd | softmax_ce")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the library has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mixture_experts_top_amd as moe
+    import workloads
+    from mixture_experts_top_amd import runner as gpu_run
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        sys.exit(1)
+    if args.row != "gate":
+        bench_row(args)
+        return
+    moe.load_library()
+    wl = workloads.workload(args.workload)
+    log(f"[bench] workload {args.workload}: {wl}")
+    inp = workloads.make_inputs(wl)
+    d = gpu_run.upload(inp)
+    o = gpu_run.Buffers(d, poison=False)
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy: {args.calib_copy_mib} MiB read + {args.calib_copy_mib} MiB written, 3 launches")
+        del src, dst
+
+    m = measure_gate(wl, d, o, args, K=args.steps, warmup=args.warmup, cold_reps=20,
+                     survey=not args.skip_kernel_survey, kernel=args.kernel)
+    ms, dom, dom_us, kern_us = m["ms"], m["dom"], m["dom_us"], m["kern_us"]
+    log("[bench] kernel avg us: " + ", ".join(f"{k}={v:.2f}" for k, v in kern_us.items()) + f"; dominant={dom}")
+    bound, achieved, peak, runit, amount, unit = kernel_roofline(dom, dom_us, wl)
 
     # per-pass times (eager, after the timed region)
     def time_pass(fn, n=20):
@@ -396,33 +508,28 @@ def main():
                "fwd+aux (one call)": time_pass(lambda: gpu_run.fwd_aux(d, o, probs=False))}
     roof = pass_roofline_us(wl)
     step_roof_frac = sum(roof.values()) / (ms * 1e3)
+    cold = m["cold"]
+    if cold:
+        kb = kernel_roofline(dom, cold["kernel_median_us"], wl)
+        cold["kernel_frac"] = kb[1] / kb[2]
+        cold["step_roofline_frac"] = sum(roof.values()) / cold["median_us"]
+    del d, o
+    torch.cuda.empty_cache()
 
-    # cold caches: the inputs are still in HBM, but a large write between steps evicts them from
-    # L2 and the Infinity Cache first; each step is timed alone with events around it
-    cold = None
-    if args.cold_mib > 0 and graph is None:
-        flush = torch.empty(args.cold_mib << 18, dtype=torch.float32, device="cuda")
-        reps = 20
-        evc = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-        for i, (a, b) in enumerate(evc):
-            flush.fill_(float(i))
-            a.record()
-            step()
-            b.record()
-        torch.cuda.synchronize()
-        cold_us = sorted(a.elapsed_time(b) * 1e3 for a, b in evc)
-        cold = {"median_us": cold_us[reps // 2], "min_us": cold_us[0], "flush_mib": args.cold_mib,
-                "routed_tokens_per_s": wl.T / (cold_us[reps // 2] * 1e-6), "steps": reps}
-        del flush
+    largest = None
+    if args.largest == "auto" and args.workload != 5 and not args.graph:
+        largest = largest_config(args)
+        log(f"[bench] largest config: {largest['ms_per_step'] * 1e3:.1f} us/step, step frac "
+            f"{largest['step_roofline_frac']:.3f}, {largest['kernel']} frac {largest['kernel_frac']:.3f}")
 
-    cpu = None if args.no_cpu_baseline else cpu_baseline(inp, args.cpu_budget)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(inp, args.cpu_budget, args.cpu_single_budget)
     T = wl.T
     out = {
         "metric": METRIC,
         "value": T / (ms * 1e-3),
         "unit": "routed tokens/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
         "higher_is_better": True,
@@ -431,20 +538,19 @@ def main():
         "dtype": wl.act,
         "data": "synthetic (seeded; see workloads.py)",
         "config": {"workload": wl.name, "B": wl.B, "N_H": wl.NH, "H": wl.H, "N_E": wl.NE, "T": T,
-                   "lambda": wl.lam, "act": wl.act, "launch": "hip-graph" if graph is not None else "eager",
-                   "streams": 1 if aux_stream is None else 2,
-                   "calls": ("fwd, bwd, aux" if args.separate_aux or aux_stream is not None
-                             else "fwd_aux, bwd"),
+                   "lambda": wl.lam, "act": wl.act, "launch": "hip-graph" if m["graph"] else "eager",
+                   "streams": 2 if m["aux_stream"] else 1,
+                   "calls": ("fwd, bwd, aux" if args.separate_aux or m["aux_stream"] else "fwd_aux, bwd"),
                    "parallelism": "single GPU"},
         "roofline": {"bound": bound, "kernel": dom, "achieved": achieved, "peak": peak, "unit": runit,
                      "frac": achieved / peak, "traffic": measured_traffic(dom, wl), "avg_launch_us": dom_us,
-                     "timed_launches": len(evs) if graph is None else 0,
-                     "per_launch": f"{amount:.4g} {unit}"},
+                     "timed_launches": m["timed_launches"], "per_launch": f"{amount:.4g} {unit}"},
         "step_roofline_frac": step_roof_frac,
         "pass_us": pass_us,
         "cold_cache_step": cold,
         "pass_roofline_us": roof,
         "kernel_avg_us": kern_us,
+        "largest_config": largest,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
