@@ -255,14 +255,15 @@ moe_status_t moe_horizon_mean_collapse_bwd(const void* d_ctx_mean, void* d_x, in
                                            int64_t H, int act, void* stream);
 
 /*
- * moe_top1_bwd with the horizon mean collapse folded into its input: instead of
- * d_routed_ctx [B, N_H, H] it takes d_ctx_mean [B, H] and uses
- *   d_routed_ctx[b, h, :] = d_ctx_mean[b, :] * (1/N_H)
+ * moe_top1_bwd with the horizon mean collapse folded into its input (MHA page "9170d24fe3",
+ * new-kernel block): instead of d_routed_ctx [B, N_H, H] it takes d_ctx_mean [B, H] (act
+ * dtype: fp32, or bf16 for bf16 activations) and uses
+ *   d_routed_ctx[b, h, :] = d_ctx_mean[b, :] * (1/N_H)      (bf16: rounded to bf16, nearest even)
  * while staging the GEMM operands, so d_routed_ctx is never written or read.  Outputs,
  * workspace and errors as moe_top1_bwd; bitwise equal to moe_horizon_mean_collapse_bwd
- * followed by moe_top1_bwd.  fp32 activations only (bf16 -> MOE_ERR_UNSUPPORTED).
+ * followed by moe_top1_bwd, in either dtype.
  */
-moe_status_t moe_top1_bwd_from_mean(const float* d_ctx_mean, const void* fused_ctx, const void* W,
+moe_status_t moe_top1_bwd_from_mean(const void* d_ctx_mean, const void* fused_ctx, const void* W,
                                     const int32_t* expert_offsets, const int32_t* perm,
                                     void* d_fused_ctx, float* d_W, float* d_b, int accumulate_dx,
                                     int64_t B, int64_t NH, int64_t H, int64_t NE, int act,

@@ -377,7 +377,7 @@ def moe_top1_bwd_from_mean(d_ctx_mean, fused_ctx, W, expert_offsets, perm, d_fus
     NE = int(W.shape[0])
     T = B * NH
     act = _act(fused_ctx)
-    _expect(d_ctx_mean, "d_ctx_mean", (B, H), torch.float32)
+    _expect(d_ctx_mean, "d_ctx_mean", (B, H), fused_ctx.dtype)
     _expect(W, "W", (NE, H, H), fused_ctx.dtype)
     _expect(expert_offsets, "expert_offsets", (NE + 1,), torch.int32)
     _expect(perm, "perm", (T,), torch.int32)

@@ -48,6 +48,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 __device__ __forceinline__ u16x8 ld8(const uint16_t* p) { return *reinterpret_cast<const u16x8*>(p); }
+// Eight bf16 values times an fp32 factor, rounded back to bf16 (nearest even): a row of d_routed_ctx
+// formed from the horizon mean's gradient, d_mean[b] * (1/N_H), exactly as the collapse backward
+// stores it.
+__device__ __forceinline__ u16x8 scale8(u16x8 v, float f) {
+    u16x8 o;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = f32_to_bf16(bf16_to_f32(v[j]) * f);
+    return o;
+}
 __device__ __forceinline__ void st8(uint16_t* p, u16x8 v) { *reinterpret_cast<u16x8*>(p) = v; }
 
 __device__ __forceinline__ void xcd_split(int bid, int per, int& major, int& minor) {
@@ -109,13 +118,15 @@ struct RowsBf16Smem {
 #ifndef MOE_BF16_RING_U8
 #define MOE_BF16_RING_U8 16  // 16-byte registers per thread for the slice ring
 #endif
-template <int H, int BN, bool DX>
+template <int H, int BN, bool DX, bool MEAN = false>
 __device__ __forceinline__ void rows_bf16_body(char* smem, int bid, const uint16_t* __restrict__ A,
                                                const uint16_t* __restrict__ Bw,
                                                const float* __restrict__ bias,
                                                uint16_t* __restrict__ Out,
                                                const int* __restrict__ offsets,
-                                               const int* __restrict__ perm, int NE, int T, int accumulate) {
+                                               const int* __restrict__ perm, int NE, int T, int accumulate,
+                                               int nh = 1, float inv_nh = 1.0f) {
+    // MEAN (dX only): row t of A is bf16(A[t / nh] * inv_nh)
     constexpr int BM = 128, KC = RowsBf16Smem<H, BN>::KC, KP = KC + 8, NKC = H / KC;
     constexpr int NT = H / BN;
     constexpr int WTM = BM / 2, WTN = BN / 2;
@@ -173,7 +184,8 @@ __device__ __forceinline__ void rows_bf16_body(char* smem, int bid, const uint16
     };
     auto store_slice = [&](int slot, int buf) {
 #pragma unroll
-        for (int i = 0; i < AL; ++i) st8(&As[buf][tid / TPR + RPP * i][8 * (tid % TPR)], ra[slot][i]);
+        for (int i = 0; i < AL; ++i)
+            st8(&As[buf][tid / TPR + RPP * i][8 * (tid % TPR)], MEAN ? scale8(ra[slot][i], inv_nh) : ra[slot][i]);
 #pragma unroll
         for (int i = 0; i < BL; ++i) {
             if constexpr (DX)
@@ -193,7 +205,10 @@ __device__ __forceinline__ void rows_bf16_body(char* smem, int bid, const uint16
     for (int c = 0; c < PF; ++c) load_b(c, c);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < AL; ++i) a_src[i] = A + (size_t)(ta[i] < 0 ? 0 : ta[i]) * H + 8 * (tid % TPR);
+    for (int i = 0; i < AL; ++i) {
+        const int t = ta[i] < 0 ? 0 : ta[i];
+        a_src[i] = A + (size_t)(MEAN ? t / nh : t) * H + 8 * (tid % TPR);
+    }
 #pragma unroll
     for (int c = 0; c < PF; ++c) load_a(c, c);
     __builtin_amdgcn_sched_barrier(0);
@@ -553,27 +568,36 @@ __global__ __launch_bounds__(kWsThreads, 1) void k_fwd_bf16_ws(const uint16_t* _
 // banks.  The 16-byte token chunks of row r are therefore XOR-swizzled by (r >> 4) & 7: the
 // stores of a wave then cover all 64 banks, and the MFMA fragment reads (16 consecutive rows
 // with one swizzle) stay conflict-free.
+//
+// BT = 128: four wavefronts of 64 x 64 (this body shares a launch with the dX tiles).
+// BT = 256 (H = 256, 512): four wavefronts of 128 x 128 (16 accumulator blocks each, one
+// workgroup per compute unit, a launch of its own).  A 128 x 128 tile per chunk re-reads the
+// chunk's dY and X columns once per partner tile (four at H = 512) and needs twice the L2 -> CU
+// bytes per MFMA; the 256 x 256 tile halves both and halves the LDS fragment reads per MFMA.
 __device__ __forceinline__ int swz(int row, int k) { return (((k >> 3) ^ ((row >> 4) & 7)) << 3) | (k & 7); }
-template <int H>
+template <int BT>
 struct DwBf16Smem {
-    static constexpr int BT = (H >= 128) ? 128 : 64, KC = 64, KP = KC + 8;
+    static constexpr int KC = 64, KP = KC + 8;
     static constexpr size_t a = sizeof(uint16_t) * 2 * BT * KP;
     static constexpr size_t bytes = 2 * a;
 };
 
-template <int H>
+// PFR: slices of rows in flight (1: one slice ahead, loaded while the current one computes).
+// NTH: threads per workgroup (256: wavefronts 2 x 2 over the tile; 512: 2 x 4).
+template <int H, int BT, bool MEAN = false, int PFR = 1, int NTH = kThreads>
 __device__ __forceinline__ void dw_bf16_body(char* smem, int bid, const uint16_t* __restrict__ dY,
-                                                       const uint16_t* __restrict__ X,
-                                                       float* __restrict__ part_dw, float* __restrict__ part_db,
-                                                       const int* __restrict__ offsets,
-                                                       const int* __restrict__ perm, int NE, int P, int T) {
-    constexpr int BT = (H >= 128) ? 128 : 64;
+                                             const uint16_t* __restrict__ X, float* __restrict__ part_dw,
+                                             float* __restrict__ part_db, const int* __restrict__ offsets,
+                                             const int* __restrict__ perm, int NE, int P, int T, int nh = 1,
+                                             float inv_nh = 1.0f) {
+    // MEAN: row t of dY is bf16(dY[t / nh] * inv_nh)
     constexpr int NTI = H / BT, TPC = NTI * NTI;
-    constexpr int KC = 64, KP = KC + 8;
-    constexpr int WT = BT / 2, SUB = WT / 32;
+    constexpr int KC = DwBf16Smem<BT>::KC, KP = DwBf16Smem<BT>::KP;
+    constexpr int WN_W = NTH / 128;                      // wavefronts along the tile's columns
+    constexpr int WTM = BT / 2, WTN = BT / WN_W, SUBM = WTM / 32, SUBN = WTN / 32;
     constexpr int ITEMS = (KC / 4) * (BT / 8);  // (4 tokens x 8 features) blocks per stage
-    uint16_t(&As)[2][BT][KP] = *reinterpret_cast<uint16_t(*)[2][BT][KP]>(smem);                     // dY^T [o][t]
-    uint16_t(&Bs)[2][BT][KP] = *reinterpret_cast<uint16_t(*)[2][BT][KP]>(smem + DwBf16Smem<H>::a);  // X^T  [i][t]
+    uint16_t(&As)[2][BT][KP] = *reinterpret_cast<uint16_t(*)[2][BT][KP]>(smem);                        // dY^T [o][t]
+    uint16_t(&Bs)[2][BT][KP] = *reinterpret_cast<uint16_t(*)[2][BT][KP]>(smem + DwBf16Smem<BT>::a);  // X^T  [i][t]
 
     int c, tile;
     xcd_split(bid, TPC, c, tile);
@@ -583,26 +607,26 @@ __device__ __forceinline__ void dw_bf16_body(char* smem, int bid, const uint16_t
     const bool do_db = (tile % NTI) == 0;
     const int tid = threadIdx.x;
     const int wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
-    const int wm = wave / 2, wn = wave % 2;
+    const int wm = wave / WN_W, wn = wave % WN_W;
 
-    f32x16 acc[SUB][SUB];
+    f32x16 acc[SUBM][SUBN];
 #pragma unroll
-    for (int i = 0; i < SUB; ++i)
+    for (int i = 0; i < SUBM; ++i)
 #pragma unroll
-        for (int j = 0; j < SUB; ++j) acc[i][j] = f32x16{};
+        for (int j = 0; j < SUBN; ++j) acc[i][j] = f32x16{};
     float dbacc = 0.0f;
 
     // Two LDS buffers; per thread IPT items of (4 tokens x 8 features) per tensor, loaded one
     // slice ahead of the MFMAs, transposed in registers when stored.  Token ids are fetched
     // one slice further ahead.
-    constexpr int IPT = (ITEMS + kThreads - 1) / kThreads;
+    constexpr int IPT = (ITEMS + NTH - 1) / NTH;
     const int nslices = (t1 - t0 + KC - 1) / KC;
     int tk[IPT][4];
     u16x8 va[IPT][4], vb[IPT][4];
     auto load_ids = [&](int sl) {
 #pragma unroll
         for (int it = 0; it < IPT; ++it) {
-            const int q = tid + kThreads * it;
+            const int q = tid + NTH * it;
             const int tq = q / (BT / 8);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -614,14 +638,14 @@ __device__ __forceinline__ void dw_bf16_body(char* smem, int bid, const uint16_t
     auto load_rows = [&]() {
 #pragma unroll
         for (int it = 0; it < IPT; ++it) {
-            const int fq = (tid + kThreads * it) % (BT / 8);
+            const int fq = (tid + NTH * it) % (BT / 8);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 va[it][j] = u16x8{};
                 vb[it][j] = u16x8{};
                 if (tk[it][j] >= 0) {
                     const size_t t = (size_t)tk[it][j];
-                    va[it][j] = ld8(dY + t * H + o0 + 8 * fq);
+                    va[it][j] = ld8(dY + (MEAN ? t / nh : t) * H + o0 + 8 * fq);
                     vb[it][j] = ld8(X + t * H + i0 + 8 * fq);
                 }
             }
@@ -630,9 +654,13 @@ __device__ __forceinline__ void dw_bf16_body(char* smem, int bid, const uint16_t
     auto store_rows = [&](int buf) {
 #pragma unroll
         for (int it = 0; it < IPT; ++it) {
-            const int q = tid + kThreads * it;
+            const int q = tid + NTH * it;
             if (q < ITEMS) {
                 const int tq = q / (BT / 8), fq = q % (BT / 8);
+                if (MEAN) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) va[it][j] = scale8(va[it][j], inv_nh);
+                }
 #pragma unroll
                 for (int f = 0; f < 8; ++f) {
                     uint2 wa, wb;
@@ -648,35 +676,24 @@ __device__ __forceinline__ void dw_bf16_body(char* smem, int bid, const uint16_t
         }
     };
 
-    load_ids(0);
-    load_rows();
-    load_ids(1);
-    store_rows(0);
-    __syncthreads();
-#pragma unroll 1
-    for (int sl = 0; sl < nslices; ++sl) {
-        const int buf = sl & 1;
-        if (sl + 1 < nslices) {
-            load_rows();
-            load_ids(sl + 2);
-        }
+    auto compute = [&](int buf) {
 #pragma unroll
         for (int kk = 0; kk < KC; kk += 16) {
-            u16x8 a[SUB], b[SUB];
+            u16x8 a[SUBM], b[SUBN];
 #pragma unroll
-            for (int i = 0; i < SUB; ++i) {
-                const int row = wm * WT + i * 32 + l32;
+            for (int i = 0; i < SUBM; ++i) {
+                const int row = wm * WTM + i * 32 + l32;
                 a[i] = ld8(&As[buf][row][swz(row, kk + 8 * h)]);
             }
 #pragma unroll
-            for (int j = 0; j < SUB; ++j) {
-                const int row = wn * WT + j * 32 + l32;
+            for (int j = 0; j < SUBN; ++j) {
+                const int row = wn * WTN + j * 32 + l32;
                 b[j] = ld8(&Bs[buf][row][swz(row, kk + 8 * h)]);
             }
 #pragma unroll
-            for (int i = 0; i < SUB; ++i)
+            for (int i = 0; i < SUBM; ++i)
 #pragma unroll
-                for (int j = 0; j < SUB; ++j) acc[i][j] = mfma_bf16(a[i], b[j], acc[i][j]);
+                for (int j = 0; j < SUBN; ++j) acc[i][j] = mfma_bf16(a[i], b[j], acc[i][j]);
         }
         if (do_db && tid < BT) {
 #pragma unroll
@@ -686,40 +703,152 @@ __device__ __forceinline__ void dw_bf16_body(char* smem, int bid, const uint16_t
                 for (int j = 0; j < 8; ++j) dbacc += bf16_to_f32(v[j]);
             }
         }
-        if (sl + 1 < nslices) store_rows(buf ^ 1);
+    };
+
+    if constexpr (PFR == 1) {
+        load_ids(0);
+        load_rows();
+        load_ids(1);
+        store_rows(0);
         __syncthreads();
+#pragma unroll 1
+        for (int sl = 0; sl < nslices; ++sl) {
+            const int buf = sl & 1;
+            if (sl + 1 < nslices) {
+                load_rows();
+                load_ids(sl + 2);
+            }
+            compute(buf);
+            if (sl + 1 < nslices) store_rows(buf ^ 1);
+            __syncthreads();
+        }
+    } else {
+        // A ring of PFR slices in registers (one wavefront per SIMD leaves the registers for it):
+        // the rows of slices s+1 .. s+PFR and the token ids of the PFR slices after those are in
+        // flight while slice s computes.  Loads past the chunk's end read its last token and are
+        // zeroed when stored, so no load sits under a branch.
+        static_assert(PFR % 2 == 0, "the LDS buffer of slice s0 + u is u % 2");
+        int tkr[PFR][IPT][4];
+        u16x8 var[PFR][IPT][4], vbr[PFR][IPT][4];
+        auto kpos = [&](int sl, int it, int j) { return t0 + sl * KC + 4 * ((tid + NTH * it) / (BT / 8)) + j; };
+        auto rids = [&](int sl, int slot) {
+#pragma unroll
+            for (int it = 0; it < IPT; ++it)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int k = kpos(sl, it, j);
+                    tkr[slot][it][j] = load_token(perm, k < t1 ? k : t1 - 1, T);
+                }
+        };
+        auto rrows = [&](int slot) {
+#pragma unroll
+            for (int it = 0; it < IPT; ++it) {
+                const int fq = (tid + NTH * it) % (BT / 8);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const size_t t = (size_t)tkr[slot][it][j];
+                    var[slot][it][j] = ld8(dY + (MEAN ? t / nh : t) * H + o0 + 8 * fq);
+                    vbr[slot][it][j] = ld8(X + t * H + i0 + 8 * fq);
+                }
+            }
+        };
+        auto rstore = [&](int sl, int slot, int buf) {
+#pragma unroll
+            for (int it = 0; it < IPT; ++it) {
+                const int q = tid + NTH * it;
+                if (q < ITEMS) {
+                    const int tq = q / (BT / 8), fq = q % (BT / 8);
+                    u16x8 wa4[4], wb4[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const bool v = kpos(sl, it, j) < t1;
+                        wa4[j] = v ? (MEAN ? scale8(var[slot][it][j], inv_nh) : var[slot][it][j]) : u16x8{};
+                        wb4[j] = v ? vbr[slot][it][j] : u16x8{};
+                    }
+#pragma unroll
+                    for (int f = 0; f < 8; ++f) {
+                        uint2 wa, wb;
+                        wa.x = (uint32_t)wa4[0][f] | ((uint32_t)wa4[1][f] << 16);
+                        wa.y = (uint32_t)wa4[2][f] | ((uint32_t)wa4[3][f] << 16);
+                        wb.x = (uint32_t)wb4[0][f] | ((uint32_t)wb4[1][f] << 16);
+                        wb.y = (uint32_t)wb4[2][f] | ((uint32_t)wb4[3][f] << 16);
+                        const int row = 8 * fq + f, k = swz(row, 4 * tq);
+                        *reinterpret_cast<uint2*>(&As[buf][row][k]) = wa;
+                        *reinterpret_cast<uint2*>(&Bs[buf][row][k]) = wb;
+                    }
+                }
+            }
+        };
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < PFR; ++k) rids(k, k);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < PFR; ++k) rrows(k);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < PFR; ++k) rids(PFR + k, k);
+        __builtin_amdgcn_sched_barrier(0);
+        rstore(0, 0, 0);
+        rrows(0);
+        rids(2 * PFR, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+#pragma unroll 1
+        for (int s0 = 0; s0 < nslices; s0 += PFR) {
+#pragma unroll
+            for (int u = 0; u < PFR; ++u) {
+                const int sl = s0 + u;
+                if (sl >= nslices) break;
+                rstore(sl + 1, (u + 1) % PFR, (u + 1) & 1);
+                rrows((u + 1) % PFR);
+                rids(sl + 1 + 2 * PFR, (u + 1) % PFR);
+                __builtin_amdgcn_sched_barrier(0);
+                compute(u & 1);
+                __syncthreads();
+            }
+        }
     }
 
     float* __restrict__ Pd = part_dw + (size_t)c * H * H;
     if constexpr (MOE_BF16_STAGED_STORES) {
-        // the partial tile through LDS (the loop's last barrier freed the buffers), then whole
-        // 16-byte row pieces
-        static_assert(DwBf16Smem<H>::bytes >= sizeof(float) * BT * (BT + kStPad), "LDS for the staged tile");
-        float(&St)[BT][BT + kStPad] = *reinterpret_cast<float(*)[BT][BT + kStPad]>(smem);
+        // The partial tile through LDS (the loop's last barrier freed the buffers), then whole
+        // 16-byte row pieces; a 256 x 256 tile goes in two halves of 128 rows (the wavefronts
+        // with wm = 0, then those with wm = 1).
+        constexpr int HR = (DwBf16Smem<BT>::bytes >= sizeof(float) * BT * (BT + kStPad)) ? BT : BT / 2;
+        static_assert(DwBf16Smem<BT>::bytes >= sizeof(float) * HR * (BT + kStPad), "LDS for the staged tile");
+        float(&St)[HR][BT + kStPad] = *reinterpret_cast<float(*)[HR][BT + kStPad]>(smem);
+        constexpr int CPR = BT / 4, RPS = NTH / CPR;
 #pragma unroll
-        for (int i = 0; i < SUB; ++i)
+        for (int half = 0; half < BT / HR; ++half) {
+            if (half > 0) __syncthreads();  // the previous half has been read
+            if (HR == BT || wm == half) {
 #pragma unroll
-            for (int j = 0; j < SUB; ++j)
+                for (int i = 0; i < SUBM; ++i)
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    St[wm * WT + i * 32 + 8 * (r / 4) + 4 * h + (r % 4)][wn * WT + j * 32 + l32] = acc[i][j][r];
-        __syncthreads();
-        constexpr int CPR = BT / 4, RPS = kThreads / CPR;
+                    for (int j = 0; j < SUBN; ++j)
 #pragma unroll
-        for (int q = 0; q < BT / RPS; ++q) {
-            const int row = q * RPS + tid / CPR, c4 = tid % CPR;
-            *reinterpret_cast<f32x4*>(Pd + (size_t)(o0 + row) * H + i0 + 4 * c4) =
-                *reinterpret_cast<const f32x4*>(&St[row][4 * c4]);
+                        for (int r = 0; r < 16; ++r)
+                            St[(HR == BT ? wm * WTM : 0) + i * 32 + 8 * (r / 4) + 4 * h + (r % 4)]
+                              [wn * WTN + j * 32 + l32] = acc[i][j][r];
+            }
+            __syncthreads();
+#pragma unroll
+            for (int q = 0; q < HR / RPS; ++q) {
+                const int row = q * RPS + tid / CPR, c4 = tid % CPR;
+                *reinterpret_cast<f32x4*>(Pd + (size_t)(o0 + half * HR + row) * H + i0 + 4 * c4) =
+                    *reinterpret_cast<const f32x4*>(&St[row][4 * c4]);
+            }
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < SUB; ++i)
+        for (int i = 0; i < SUBM; ++i)
 #pragma unroll
-            for (int j = 0; j < SUB; ++j) {
-                const int col = i0 + wn * WT + j * 32 + l32;
+            for (int j = 0; j < SUBN; ++j) {
+                const int col = i0 + wn * WTN + j * 32 + l32;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int row = o0 + wm * WT + i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
+                    const int row = o0 + wm * WTM + i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
                     Pd[(size_t)row * H + col] = acc[i][j][r];
                 }
             }
@@ -727,7 +856,225 @@ __device__ __forceinline__ void dw_bf16_body(char* smem, int bid, const uint16_t
     if (do_db && tid < BT) part_db[(size_t)c * H + o0 + tid] = dbacc;
 }
 
-// Kernels.  The backward is one launch: dW / db chunk tiles first, then dX tiles.
+// d_W / d_b partials with 256 x 256 output tiles (H = 256, 512), staged token-major.
+//
+// The chunk's rows go to LDS as loaded (16-byte stores, no register transpose): tile [t][f],
+// 64 tokens x 256 features of dY (o0 ..) and of X (i0 ..), rows of 512 bytes.  The MFMA
+// fragments want 8 consecutive tokens of one feature per lane, which gfx950's transposing LDS
+// read ds_read_b64_tr_b16 gives (see tr_frag).  The 16-byte chunk c of row t sits at chunk
+// c ^ 4 (t & 3): a wavefront's stores (two whole rows) stay conflict-free, and the 8 rows x 64
+// bytes of one transposing read spread over all 64 banks twice -- the minimum.
+// Eight wavefronts, 2 (o) x 4 (i), each 128 x 64 of the tile (8 accumulator blocks); d_b comes
+// from the dY fragments of the wavefronts with wn = 0 (each lane sums its 8 tokens, the two lane
+// halves are added at the end).
+constexpr int kDwtThreads = 512;
+#ifndef MOE_BF16_DWT_RING
+#define MOE_BF16_DWT_RING 1  // slices of rows in flight (1, or an even ring; 2 spills registers)
+#endif
+struct DwtSmem {
+    static constexpr int KC = 64, ROWB = 512;                 // tokens per slice, bytes per row
+    static constexpr size_t tile = (size_t)KC * ROWB;          // one tensor, one slice: 32 KB
+    static constexpr size_t bufs = 4 * tile;                   // 2 buffers x {dY, X}
+    static constexpr size_t stage = sizeof(float) * 128 * (256 + kStPad);  // half the output tile
+    static constexpr size_t bytes = bufs > stage ? bufs : stage;
+};
+__device__ __forceinline__ u16x8 tr_frag_swz(const char* tile, int r0, int c0, int lane) {
+    // rows r0 .. r0 + 15 (8 per lane half), columns c0 .. c0 + 31 (elements); r0 % 16 == 0, c0 % 32 == 0
+    const int h = lane / 32, grp = (lane % 32) / 16, j = lane % 16;
+    const int R = r0 + 8 * h + (j >> 2);
+    const int C = c0 + 16 * grp + 4 * (j & 3);
+    const int off = R * DwtSmem::ROWB + ((((C >> 3) ^ (4 * (j >> 2))) << 4) | ((C & 7) * 2));
+    const i16x4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(tile + off));
+    const i16x4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(tile + off + 4 * DwtSmem::ROWB));
+    u16x8 v;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        v[q] = (uint16_t)lo[q];
+        v[4 + q] = (uint16_t)hi[q];
+    }
+    return v;
+}
+
+template <int H, bool MEAN>
+__device__ __forceinline__ void dw_bf16_tr_body(char* smem, int bid, const uint16_t* __restrict__ dY,
+                                                const uint16_t* __restrict__ X, float* __restrict__ part_dw,
+                                                float* __restrict__ part_db, const int* __restrict__ offsets,
+                                                const int* __restrict__ perm, int NE, int P, int T, int nh,
+                                                float inv_nh) {
+    constexpr int BT = 256, NTI = H / BT, TPC = NTI * NTI;
+    constexpr int KC = DwtSmem::KC, ROWB = DwtSmem::ROWB;
+    constexpr int SUBM = 4, SUBN = 2;  // 128 x 64 per wavefront
+    char* tiles = smem;  // [buf][tensor][KC][ROWB]
+    auto tile = [&](int buf, int tensor) { return tiles + (2 * buf + tensor) * DwtSmem::tile; };
+
+    int c, tl;
+    xcd_split(bid, TPC, c, tl);
+    int e = -1, t0 = 0, t1 = 0;
+    if (!find_chunk(offsets, NE, P, T, c, e, t0, t1)) return;
+    const int o0 = (tl / NTI) * BT, i0 = (tl % NTI) * BT;
+    const bool do_db = (tl % NTI) == 0;
+    const int tid = threadIdx.x;
+    const int wave = tid / 64, lane = tid % 64, l32 = lane % 32;
+    const int wm = wave / 4, wn = wave % 4;
+    const bool db_wave = do_db && wn == 0;
+
+    f32x16 acc[SUBM][SUBN];
+#pragma unroll
+    for (int i = 0; i < SUBM; ++i)
+#pragma unroll
+        for (int j = 0; j < SUBN; ++j) acc[i][j] = f32x16{};
+    float dbacc[SUBM] = {0.0f, 0.0f, 0.0f, 0.0f};
+
+    // thread -> (token quad tq, feature chunk fq): 4 tokens x 16 bytes of each tensor per slice;
+    // fq runs fastest, so a wavefront's loads of one token cover 512 contiguous bytes
+    const int fq = tid % 32, tq = tid / 32;
+    const int nslices = (t1 - t0 + KC - 1) / KC;
+    // A ring of PF slices in registers: the rows of slices s+1 .. s+PF and the token ids of the
+    // PF slices after those are in flight while slice s computes.  Loads past the chunk's end
+    // read its last token and are zeroed when stored, so no load sits under a branch.
+    constexpr int PF = MOE_BF16_DWT_RING;
+    static_assert(PF == 1 || PF % 2 == 0, "the LDS buffer of slice s0 + u is u % 2");
+    int tk[PF][4];
+    u16x8 va[PF][4], vb[PF][4];
+    auto kpos = [&](int sl, int j) { return t0 + sl * KC + 4 * tq + j; };
+    auto load_ids = [&](int sl, int slot) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int k = kpos(sl, j);
+            tk[slot][j] = load_token(perm, k < t1 ? k : t1 - 1, T);
+        }
+    };
+    auto load_rows = [&](int slot) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const size_t t = (size_t)tk[slot][j];
+            va[slot][j] = ld8(dY + (MEAN ? t / nh : t) * H + o0 + 8 * fq);
+            vb[slot][j] = ld8(X + t * H + i0 + 8 * fq);
+        }
+    };
+    auto store_rows = [&](int sl, int slot, int buf) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bool v = kpos(sl, j) < t1;
+            const int row = 4 * tq + j;
+            const int off = row * ROWB + ((fq ^ (4 * j)) << 4);  // row & 3 == j
+            st8(reinterpret_cast<uint16_t*>(tile(buf, 0) + off), v ? va[slot][j] : u16x8{});
+            st8(reinterpret_cast<uint16_t*>(tile(buf, 1) + off), v ? vb[slot][j] : u16x8{});
+        }
+    };
+    auto compute = [&](int buf) {
+        const char* ta = tile(buf, 0);
+        const char* tb = tile(buf, 1);
+#pragma unroll
+        for (int kk = 0; kk < KC; kk += 16) {
+            u16x8 a[SUBM], b[SUBN];
+#pragma unroll
+            for (int i = 0; i < SUBM; ++i) {
+                a[i] = tr_frag_swz(ta, kk, wm * 128 + 32 * i, lane);
+                if (MEAN) a[i] = scale8(a[i], inv_nh);
+            }
+#pragma unroll
+            for (int j = 0; j < SUBN; ++j) b[j] = tr_frag_swz(tb, kk, wn * 64 + 32 * j, lane);
+#pragma unroll
+            for (int i = 0; i < SUBM; ++i)
+#pragma unroll
+                for (int j = 0; j < SUBN; ++j) acc[i][j] = mfma_bf16(a[i], b[j], acc[i][j]);
+            if (db_wave) {
+#pragma unroll
+                for (int i = 0; i < SUBM; ++i)
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) dbacc[i] += bf16_to_f32(a[i][q]);
+            }
+        }
+    };
+
+    if constexpr (PF == 1) {
+        load_ids(0, 0);
+        load_rows(0);
+        load_ids(1, 0);
+        store_rows(0, 0, 0);
+        __syncthreads();
+#pragma unroll 1
+        for (int sl = 0; sl < nslices; ++sl) {
+            const int buf = sl & 1;
+            if (sl + 1 < nslices) {
+                load_rows(0);
+                load_ids(sl + 2, 0);
+            }
+            compute(buf);
+            if (sl + 1 < nslices) store_rows(sl + 1, 0, buf ^ 1);
+            __syncthreads();
+        }
+    } else {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < PF; ++k) load_ids(k, k);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < PF; ++k) load_rows(k);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < PF; ++k) load_ids(PF + k, k);
+        __builtin_amdgcn_sched_barrier(0);
+        store_rows(0, 0, 0);
+        load_rows(0);
+        load_ids(2 * PF, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+#pragma unroll 1
+        for (int s0 = 0; s0 < nslices; s0 += PF) {
+#pragma unroll
+            for (int u = 0; u < PF; ++u) {
+                const int sl = s0 + u;
+                if (sl >= nslices) break;
+                store_rows(sl + 1, (u + 1) % PF, (u + 1) & 1);
+                load_rows((u + 1) % PF);
+                load_ids(sl + 1 + 2 * PF, (u + 1) % PF);
+                __builtin_amdgcn_sched_barrier(0);
+                compute(u & 1);
+                __syncthreads();
+            }
+        }
+    }
+
+    // the partial tile in two halves of 128 rows through LDS (the loop's last barrier freed the
+    // buffers), then whole 16-byte row pieces
+    float* __restrict__ Pd = part_dw + (size_t)c * H * H;
+    float(&St)[128][BT + kStPad] = *reinterpret_cast<float(*)[128][BT + kStPad]>(smem);
+    const int h = lane / 32;
+    constexpr int CPR = BT / 4, RPS = kDwtThreads / CPR;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        if (half > 0) __syncthreads();
+        if (wm == half) {
+#pragma unroll
+            for (int i = 0; i < SUBM; ++i)
+#pragma unroll
+                for (int j = 0; j < SUBN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        St[i * 32 + 8 * (r / 4) + 4 * h + (r % 4)][wn * 64 + j * 32 + l32] = acc[i][j][r];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < 128 / RPS; ++q) {
+            const int row = q * RPS + tid / CPR, c4 = tid % CPR;
+            *reinterpret_cast<f32x4*>(Pd + (size_t)(o0 + half * 128 + row) * H + i0 + 4 * c4) =
+                *reinterpret_cast<const f32x4*>(&St[row][4 * c4]);
+        }
+    }
+    if (db_wave) {
+#pragma unroll
+        for (int i = 0; i < SUBM; ++i) {
+            const float tot = dbacc[i] + __shfl_xor(dbacc[i], 32);
+            if (lane < 32) part_db[(size_t)c * H + o0 + wm * 128 + 32 * i + l32] = tot;
+        }
+    }
+}
+
+// Kernels.  For H <= 128 the backward is one launch: dW / db chunk tiles first, then dX tiles.
+// For H = 256 / 512 the 256 x 256 dW tiles take a whole compute unit each (their registers), so
+// they run as a launch of their own ahead of the dX launch.
 template <int H, int BN>
 __global__ __launch_bounds__(kThreads) void k_fwd_bf16(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
                                                         const float* __restrict__ bias, uint16_t* __restrict__ Y,
@@ -737,23 +1084,64 @@ __global__ __launch_bounds__(kThreads) void k_fwd_bf16(const uint16_t* __restric
     rows_bf16_body<H, BN, false>(smem, blockIdx.x, X, W, bias, Y, offsets, perm, NE, T, 0);
 }
 
-template <int H, int BN>
+// ACC: dX is added to the existing contents (a compile-time choice, as in the fp32 kernels).
+template <int H, int BN, bool MEAN, bool ACC>
 __global__ __launch_bounds__(kThreads) void k_bwd_bf16(const uint16_t* __restrict__ dY,
                                                         const uint16_t* __restrict__ X,
                                                         const uint16_t* __restrict__ W, uint16_t* __restrict__ dX,
                                                         int accumulate, float* __restrict__ part_dw,
                                                         float* __restrict__ part_db,
                                                         const int* __restrict__ offsets,
-                                                        const int* __restrict__ perm, int NE, int P, int T, int n_dx) {
-    constexpr size_t r = RowsBf16Smem<H, BN>::bytes, d = DwBf16Smem<H>::bytes;
+                                                        const int* __restrict__ perm, int NE, int P, int T, int n_dx,
+                                                        int nh, float inv_nh) {
+    constexpr int BT = bf16_dw_tile(H);
+    constexpr size_t r = RowsBf16Smem<H, BN>::bytes, d = DwBf16Smem<BT>::bytes;
     __shared__ __attribute__((aligned(16))) char smem[r > d ? r : d];  // one LDS region, either role
     // longest first: the dW workgroups (a whole chunk each) lead the grid, the dX tiles follow,
     // so the dispatcher evens out the end of the launch
     const int n_dw = (int)gridDim.x - n_dx;
     if ((int)blockIdx.x < n_dw)
-        dw_bf16_body<H>(smem, blockIdx.x, dY, X, part_dw, part_db, offsets, perm, NE, P, T);
+        dw_bf16_body<H, BT, MEAN>(smem, blockIdx.x, dY, X, part_dw, part_db, offsets, perm, NE, P, T, nh, inv_nh);
     else
-        rows_bf16_body<H, BN, true>(smem, blockIdx.x - n_dw, dY, W, nullptr, dX, offsets, perm, NE, T, accumulate);
+        rows_bf16_body<H, BN, true, MEAN>(smem, blockIdx.x - n_dw, dY, W, nullptr, dX, offsets, perm, NE, T,
+                                          (int)ACC, nh, inv_nh);
+}
+
+#ifndef MOE_BF16_DW_RING
+#define MOE_BF16_DW_RING 1  // slices in flight in the 256 x 256 d_W kernel (1, or an even ring)
+#endif
+constexpr int kDwBigThreads = 512;  // 256 x 256 d_W tile: 8 wavefronts of 128 x 64, two per SIMD
+#ifndef MOE_BF16_DW_TR
+#define MOE_BF16_DW_TR 1  // 256 x 256 d_W tiles staged token-major and read with transposing LDS reads
+#endif
+template <int H, bool MEAN>
+__global__ __launch_bounds__(kDwBigThreads) void k_dw_bf16(const uint16_t* __restrict__ dY,
+                                                          const uint16_t* __restrict__ X, float* __restrict__ part_dw,
+                                                          float* __restrict__ part_db,
+                                                          const int* __restrict__ offsets,
+                                                          const int* __restrict__ perm, int NE, int P, int T, int nh,
+                                                          float inv_nh) {
+    constexpr int BT = bf16_dw_tile(H);
+    if constexpr (MOE_BF16_DW_TR) {
+        static_assert(kDwtThreads == kDwBigThreads && BT == 256, "token-major d_W tile shape");
+        __shared__ __attribute__((aligned(16))) char smem[DwtSmem::bytes];
+        dw_bf16_tr_body<H, MEAN>(smem, blockIdx.x, dY, X, part_dw, part_db, offsets, perm, NE, P, T, nh, inv_nh);
+    } else {
+        __shared__ __attribute__((aligned(16))) char smem[DwBf16Smem<BT>::bytes];
+        dw_bf16_body<H, BT, MEAN, MOE_BF16_DW_RING, kDwBigThreads>(smem, blockIdx.x, dY, X, part_dw, part_db,
+                                                                   offsets, perm, NE, P, T, nh, inv_nh);
+    }
+}
+
+template <int H, int BN, bool MEAN, bool ACC>
+__global__ __launch_bounds__(kThreads) void k_dx_bf16(const uint16_t* __restrict__ dY, const uint16_t* __restrict__ W,
+                                                       uint16_t* __restrict__ dX, int accumulate,
+                                                       const int* __restrict__ offsets,
+                                                       const int* __restrict__ perm, int NE, int T, int nh,
+                                                       float inv_nh) {
+    __shared__ __attribute__((aligned(16))) char smem[RowsBf16Smem<H, BN>::bytes];
+    rows_bf16_body<H, BN, true, MEAN>(smem, blockIdx.x, dY, W, nullptr, dX, offsets, perm, NE, T, (int)ACC, nh,
+                                      inv_nh);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -779,18 +1167,28 @@ static hipError_t fwd_bf16(const uint16_t* X, const uint16_t* W, const float* bi
     return hipGetLastError();
 }
 
-template <int H>
+template <int H, bool MEAN, bool ACC>
 static hipError_t bwd_bf16(const uint16_t* dY, const uint16_t* X, const uint16_t* W, uint16_t* dX, int accumulate,
                            float* pdw, float* pdb, const int32_t* offsets, const int32_t* perm, int64_t T, int NE,
-                           int P, int n_chunk_max, hipStream_t s) {
+                           int P, int n_chunk_max, int nh, hipStream_t s) {
     constexpr int BN = (H >= 128) ? 128 : H;
     constexpr int NT = H / BN;
-    constexpr int BT = (H >= 128) ? 128 : 64;
+    constexpr int BT = bf16_dw_tile(H);
     constexpr int TPC = (H / BT) * (H / BT);
+    const float inv_nh = 1.0f / (float)nh;
     const int n_dx = round_up((int)((T + 127) / 128) + NE, 8) * NT;
-    const int grid = n_dx + round_up(n_chunk_max, 8) * TPC;
-    launch_kernel((k_bwd_bf16<H, BN>), dim3(grid), dim3(kThreads), 0, s, dY, X, W, dX, accumulate, pdw, pdb,
-                       offsets, perm, NE, P, (int)T, n_dx);
+    const int n_dw = round_up(n_chunk_max, 8) * TPC;
+    if constexpr (BT == 256) {
+        // the kernel timer (if armed) brackets both launches
+        const ArmedEvents ev = take_armed_events();
+        launch_kernel_ev((k_dw_bf16<H, MEAN>), dim3(n_dw), dim3(kDwBigThreads), 0, s, ev.start, nullptr, dY, X, pdw, pdb,
+                         offsets, perm, NE, P, (int)T, nh, inv_nh);
+        launch_kernel_ev((k_dx_bf16<H, BN, MEAN, ACC>), dim3(n_dx), dim3(kThreads), 0, s, nullptr, ev.stop, dY, W, dX,
+                         accumulate, offsets, perm, NE, (int)T, nh, inv_nh);
+    } else {
+        launch_kernel((k_bwd_bf16<H, BN, MEAN, ACC>), dim3(n_dx + n_dw), dim3(kThreads), 0, s, dY, X, W, dX, accumulate,
+                      pdw, pdb, offsets, perm, NE, P, (int)T, n_dx, nh, inv_nh);
+    }
     return hipGetLastError();
 }
 
@@ -806,16 +1204,43 @@ hipError_t launch_fwd_gemm_bf16(const uint16_t* X, const uint16_t* W, const floa
     return hipErrorInvalidValue;
 }
 
+template <bool MEAN, bool ACC>
+static hipError_t bwd_bf16_h2(const uint16_t* dY, const uint16_t* X, const uint16_t* W, uint16_t* dX, float* pdw,
+                              float* pdb, const int32_t* offsets, const int32_t* perm, int64_t T, int H, int NE, int P,
+                              int n_chunk_max, int nh, hipStream_t s) {
+    const int acc = ACC ? 1 : 0;
+    switch (H) {
+        case 64: return bwd_bf16<64, MEAN, ACC>(dY, X, W, dX, acc, pdw, pdb, offsets, perm, T, NE, P, n_chunk_max, nh, s);
+        case 128:
+            return bwd_bf16<128, MEAN, ACC>(dY, X, W, dX, acc, pdw, pdb, offsets, perm, T, NE, P, n_chunk_max, nh, s);
+        case 256:
+            return bwd_bf16<256, MEAN, ACC>(dY, X, W, dX, acc, pdw, pdb, offsets, perm, T, NE, P, n_chunk_max, nh, s);
+        case 512:
+            return bwd_bf16<512, MEAN, ACC>(dY, X, W, dX, acc, pdw, pdb, offsets, perm, T, NE, P, n_chunk_max, nh, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <bool MEAN>
+static hipError_t bwd_bf16_h(const uint16_t* dY, const uint16_t* X, const uint16_t* W, uint16_t* dX, int accumulate,
+                             float* pdw, float* pdb, const int32_t* offsets, const int32_t* perm, int64_t T, int H,
+                             int NE, int P, int n_chunk_max, int nh, hipStream_t s) {
+    if (accumulate)
+        return bwd_bf16_h2<MEAN, true>(dY, X, W, dX, pdw, pdb, offsets, perm, T, H, NE, P, n_chunk_max, nh, s);
+    return bwd_bf16_h2<MEAN, false>(dY, X, W, dX, pdw, pdb, offsets, perm, T, H, NE, P, n_chunk_max, nh, s);
+}
+
 hipError_t launch_bwd_gemm_bf16(const uint16_t* dY, const uint16_t* X, const uint16_t* W, uint16_t* dX,
                                 int accumulate, float* pdw, float* pdb, const int32_t* offsets, const int32_t* perm,
                                 int64_t T, int H, int NE, int P, int n_chunk_max, hipStream_t s) {
-    switch (H) {
-        case 64: return bwd_bf16<64>(dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, T, NE, P, n_chunk_max, s);
-        case 128: return bwd_bf16<128>(dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, T, NE, P, n_chunk_max, s);
-        case 256: return bwd_bf16<256>(dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, T, NE, P, n_chunk_max, s);
-        case 512: return bwd_bf16<512>(dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, T, NE, P, n_chunk_max, s);
-    }
-    return hipErrorInvalidValue;
+    return bwd_bf16_h<false>(dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, T, H, NE, P, n_chunk_max, 1, s);
+}
+
+hipError_t launch_bwd_gemm_bf16_from_mean(const uint16_t* d_mean, const uint16_t* X, const uint16_t* W, uint16_t* dX,
+                                          int accumulate, float* pdw, float* pdb, const int32_t* offsets,
+                                          const int32_t* perm, int64_t T, int H, int NE, int NH, int P,
+                                          int n_chunk_max, hipStream_t s) {
+    return bwd_bf16_h<true>(d_mean, X, W, dX, accumulate, pdw, pdb, offsets, perm, T, H, NE, P, n_chunk_max, NH, s);
 }
 
 }  // namespace moe

@@ -164,7 +164,9 @@ struct RowsF32Smem {
 // ids (ids past the real tile count are skipped).  The experts' offsets are read once per
 // wavefront; during the last K-slice of a tile the next tile's token ids and first K-slice are
 // loaded, so that latency overlaps the MFMAs and the epilogue stores.
-template <int H, int BM, int BN, int KC, bool DX, bool MEAN = false>
+// WNK: the B tile is read [n][k] (k contiguous), as the forward reads W[e][out][in]; dX passes
+// W as stored ([k][n], WNK = false) or its transpose (WNK = true, then read like the forward).
+template <int H, int BM, int BN, int KC, bool DX, bool MEAN = false, bool WNK = !DX>
 __device__ __forceinline__ void rows_f32_body(char* smem, int wg, int nwg, int ntile_ids,
                                               const float* __restrict__ A, const float* __restrict__ W,
                                               const float* __restrict__ bias, float* __restrict__ Out,
@@ -182,9 +184,9 @@ __device__ __forceinline__ void rows_f32_body(char* smem, int wg, int nwg, int n
     constexpr int AL = (BM + RPP - 1) / RPP, BL = BN * KC / (4 * kThreads);
     constexpr bool AFULL = BM % RPP == 0;
     static_assert(KC % 8 == 0 && (AFULL || RPP % BM == 0) && (BN * KC) % (4 * kThreads) == 0, "tile shape");
-    constexpr int BS_ROWS = DX ? KC : BN;
-    constexpr int BS_COLS = DX ? BN + kPadKN : KC + kPad;
-    using SM_ = RowsF32Smem<BM, BN, KC, DX>;
+    constexpr int BS_ROWS = !WNK ? KC : BN;
+    constexpr int BS_COLS = !WNK ? BN + kPadKN : KC + kPad;
+    using SM_ = RowsF32Smem<BM, BN, KC, !WNK>;
     float(&As)[2][BM][KC + kPad] = *reinterpret_cast<float(*)[2][BM][KC + kPad]>(smem);
     float(&Bs)[2][BS_ROWS][BS_COLS] = *reinterpret_cast<float(*)[2][BS_ROWS][BS_COLS]>(smem + SM_::a);
     int(&tok)[2][BM] = *reinterpret_cast<int(*)[2][BM]>(smem + SM_::tok_off);
@@ -253,7 +255,7 @@ __device__ __forceinline__ void rows_f32_body(char* smem, int wg, int nwg, int n
         }
 #pragma unroll
         for (int i = 0; i < BL; ++i) {
-            if (!DX) {
+            if (WNK) {
                 const int r = tid / TPR + RPP * i, c = 4 * (tid % TPR);
                 rb[i] = ld4(We + (size_t)(wn0 + r) * H + k0 + c);
             } else {
@@ -270,7 +272,7 @@ __device__ __forceinline__ void rows_f32_body(char* smem, int wg, int nwg, int n
         }
 #pragma unroll
         for (int i = 0; i < BL; ++i) {
-            if (!DX) {
+            if (WNK) {
                 st4(&Bs[buf][tid / TPR + RPP * i][4 * (tid % TPR)], rb[i]);
             } else {
                 const int q = tid + kThreads * i;
@@ -295,7 +297,7 @@ __device__ __forceinline__ void rows_f32_body(char* smem, int wg, int nwg, int n
         for (int i = 0; i < SM; ++i) fa[slot][i] = ld4(&As[buf][wm * WTM + i * 32 + l32][kk]);
 #pragma unroll
         for (int j = 0; j < SN; ++j) {
-            if (!DX) {
+            if (WNK) {
                 fb[slot][j] = ld4(&Bs[buf][wn * WTN + j * 32 + l32][kk]);
             } else {
                 const int cc = wn * WTN + j * 32 + l32;
@@ -757,7 +759,8 @@ struct DwF32Smem {
 #ifndef MOE_DW_PF
 #define MOE_DW_PF 2  // K slices of rows in flight per dW workgroup (even)
 #endif
-template <int H, int BT, int KC, bool MEAN = false>
+// NTH threads: 256 (wavefronts 2 x 2 over the tile) or 512 (2 x 4, for 256 x 256 tiles).
+template <int H, int BT, int KC, bool MEAN = false, int NTH = kThreads>
 __device__ __forceinline__ void dw_f32_body(char* smem, int bid, const float* __restrict__ dY,
                                                       const float* __restrict__ X,
                                                       float* __restrict__ part_dw,
@@ -766,9 +769,10 @@ __device__ __forceinline__ void dw_f32_body(char* smem, int bid, const float* __
                                                       const int* __restrict__ perm, int NE,
                                                       int P, int T, int nh = 1, float inv_nh = 1.0f) {
     constexpr int NTI = H / BT, TPC = NTI * NTI;
-    constexpr int WT = BT / 2, SUB = WT / 32;
+    constexpr int WN_W = NTH / 128;  // wavefronts along the tile's columns
+    constexpr int WTM = BT / 2, WTN = BT / WN_W, SUBM = WTM / 32, SUBN = WTN / 32;
     constexpr int Q = BT / 4;                  // float4 per row segment
-    constexpr int LD = KC * Q / kThreads;      // float4 loads per thread per tensor per slice
+    constexpr int LD = KC * Q / NTH;      // float4 loads per thread per tensor per slice
     constexpr int PF = MOE_DW_PF;
     float(&As)[2][KC][BT + kPadKN] = *reinterpret_cast<float(*)[2][KC][BT + kPadKN]>(smem);  // dY rows, o0..o0+BT
     float(&Bs)[2][KC][BT + kPadKN] =
@@ -782,14 +786,14 @@ __device__ __forceinline__ void dw_f32_body(char* smem, int bid, const float* __
     const bool do_db = (tile % NTI) == 0;
     const int tid = threadIdx.x;
     const int wave = tid / 64, lane = tid % 64, h = lane / 32, l32 = lane % 32;
-    const int wm = wave / 2, wn = wave % 2;
+    const int wm = wave / WN_W, wn = wave % WN_W;
     const int nslices = (t1 - t0 + KC - 1) / KC;
 
-    f32x16 acc[SUB][SUB];
+    f32x16 acc[SUBM][SUBN];
 #pragma unroll
-    for (int i = 0; i < SUB; ++i)
+    for (int i = 0; i < SUBM; ++i)
 #pragma unroll
-        for (int j = 0; j < SUB; ++j) acc[i][j] = f32x16{};
+        for (int j = 0; j < SUBN; ++j) acc[i][j] = f32x16{};
     float dbacc = 0.0f;
 
     // Two register rings, slot k % PF for slice k: the rows of slices s+1 .. s+PF and the
@@ -799,7 +803,7 @@ __device__ __forceinline__ void dw_f32_body(char* smem, int bid, const float* __
     // result is touched before its slice is due (either would drain the ring).
     int tk[PF][LD];
     f32x4 ra[PF][LD], rb[PF][LD];
-    auto kpos = [&](int sl, int i) { return t0 + sl * KC + (tid + kThreads * i) / Q; };
+    auto kpos = [&](int sl, int i) { return t0 + sl * KC + (tid + NTH * i) / Q; };
     auto load_ids = [&](int sl, int slot) {
 #pragma unroll
         for (int i = 0; i < LD; ++i) {
@@ -810,7 +814,7 @@ __device__ __forceinline__ void dw_f32_body(char* smem, int bid, const float* __
     auto load_rows = [&](int sl, int slot) {  // ids of slice sl are in tk[slot]; rows go to slot
 #pragma unroll
         for (int i = 0; i < LD; ++i) {
-            const int cc = 4 * ((tid + kThreads * i) % Q);
+            const int cc = 4 * ((tid + NTH * i) % Q);
             const size_t t = (size_t)tk[slot][i];
             ra[slot][i] = ld4(dY + (MEAN ? t / nh : t) * H + o0 + cc);
             rb[slot][i] = ld4(X + t * H + i0 + cc);
@@ -819,7 +823,7 @@ __device__ __forceinline__ void dw_f32_body(char* smem, int bid, const float* __
     auto store_rows = [&](int sl, int slot, int buf) {  // masking here, where the rows have arrived
 #pragma unroll
         for (int i = 0; i < LD; ++i) {
-            const int q = tid + kThreads * i;
+            const int q = tid + NTH * i;
             const bool v = kpos(sl, i) < t1;
             f32x4 av = ra[slot][i];
             if (MEAN) av *= inv_nh;
@@ -862,15 +866,15 @@ __device__ __forceinline__ void dw_f32_body(char* smem, int bid, const float* __
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int k = kk + 4 * h + q;
-                    float a[SUB], b[SUB];
+                    float a[SUBM], b[SUBN];
 #pragma unroll
-                    for (int i = 0; i < SUB; ++i) a[i] = As[buf][k][wm * WT + i * 32 + l32];
+                    for (int i = 0; i < SUBM; ++i) a[i] = As[buf][k][wm * WTM + i * 32 + l32];
 #pragma unroll
-                    for (int j = 0; j < SUB; ++j) b[j] = Bs[buf][k][wn * WT + j * 32 + l32];
+                    for (int j = 0; j < SUBN; ++j) b[j] = Bs[buf][k][wn * WTN + j * 32 + l32];
 #pragma unroll
-                    for (int i = 0; i < SUB; ++i)
+                    for (int i = 0; i < SUBM; ++i)
 #pragma unroll
-                        for (int j = 0; j < SUB; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+                        for (int j = 0; j < SUBN; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
                 }
             }
             if (do_db && tid < BT) {
@@ -883,13 +887,13 @@ __device__ __forceinline__ void dw_f32_body(char* smem, int bid, const float* __
 
     float* __restrict__ Pd = part_dw + (size_t)c * H * H;
 #pragma unroll
-    for (int i = 0; i < SUB; ++i)
+    for (int i = 0; i < SUBM; ++i)
 #pragma unroll
-        for (int j = 0; j < SUB; ++j) {
-            const int col = i0 + wn * WT + j * 32 + l32;
+        for (int j = 0; j < SUBN; ++j) {
+            const int col = i0 + wn * WTN + j * 32 + l32;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int row = o0 + wm * WT + i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
+                const int row = o0 + wm * WTM + i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
                 Pd[(size_t)row * H + col] = acc[i][j][r];
             }
         }
@@ -997,7 +1001,9 @@ __global__ __launch_bounds__(kThreads) void k_fwd_f32_gather(const float* __rest
                                                                  NE, T, 0, 1, 1.0f, rv);
 }
 
-template <int H, int BM, int BN, int BT, int KCX, int KCW, bool MEAN, bool ONE, bool DWF = false>
+// ACC: dX is added to the existing contents (a compile-time choice: with a run-time flag the
+// epilogue carries the load-then-store path and the waits it needs even when it is not taken).
+template <int H, int BM, int BN, int BT, int KCX, int KCW, bool MEAN, bool ONE, bool DWF = false, bool ACC = false>
 __global__ __launch_bounds__(kThreads) void k_bwd_f32(const float* __restrict__ dY, const float* __restrict__ X,
                                                        const float* __restrict__ W, float* __restrict__ dX,
                                                        int accumulate, float* __restrict__ part_dw,
@@ -1014,20 +1020,90 @@ __global__ __launch_bounds__(kThreads) void k_bwd_f32(const float* __restrict__ 
                                           inv_nh);
         else
             rows_f32_body<H, BM, BN, KCX, true, MEAN>(smem, blockIdx.x - n_dw, n_dx, dx_tile_ids, dY, W, nullptr, dX,
-                                                      offsets, perm, NE, T, accumulate, nh, inv_nh);
+                                                      offsets, perm, NE, T, (int)ACC, nh, inv_nh);
         return;
     }
     if ((int)blockIdx.x < n_dx) {
         if (ONE)
             rows_f32_onepass_body<H, BM, BN, KCX, true, MEAN, DX_XR<BM>>(smem, blockIdx.x, dY, W, nullptr, dX, offsets,
-                                                                          perm, NE, T, accumulate, nh, inv_nh);
+                                                                          perm, NE, T, (int)ACC, nh, inv_nh);
         else
             rows_f32_body<H, BM, BN, KCX, true, MEAN>(smem, blockIdx.x, n_dx, dx_tile_ids, dY, W, nullptr, dX,
-                                                      offsets, perm, NE, T, accumulate, nh, inv_nh);
+                                                      offsets, perm, NE, T, (int)ACC, nh, inv_nh);
     }
     else
         dw_f32_body<H, BT, KCW, MEAN>(smem, blockIdx.x - n_dx, dY, X, part_dw, part_db, offsets, perm, NE, P, T, nh,
                                   inv_nh);
+}
+
+// Large T, H = 256 / 512: the 256 x 256 d_W tiles (eight wavefronts of 128 x 64, one workgroup
+// per compute unit) in a launch of their own, then the dX tiles as a persistent launch.  A
+// 128 x 128 d_W tile re-reads its chunk's dY and X columns once per partner tile; with the
+// whole 256 x 256 block per workgroup each chunk row is read once.
+constexpr int kDwBigThreads = 512;
+// The first N_E workgroups of the launch write Wt[e] = W[e]^T for the dX launch that follows
+// (64 x 64 blocks through LDS, rows padded by one float), the rest compute d_W tiles.
+template <int H>
+__device__ __forceinline__ void transpose_w_body(char* smem, int e, const float* __restrict__ W, float* __restrict__ Wt) {
+    float(&tb)[64][65] = *reinterpret_cast<float(*)[64][65]>(smem);
+    const float* __restrict__ src = W + (size_t)e * H * H;
+    float* __restrict__ dst = Wt + (size_t)e * H * H;
+    const int tid = threadIdx.x;
+#pragma unroll 1
+    for (int b = 0; b < (H / 64) * (H / 64); ++b) {
+        const int r0 = (b / (H / 64)) * 64, c0 = (b % (H / 64)) * 64;
+        f32x4 v[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {  // 64 rows x 16 float4, two per thread
+            const int q = tid + kDwBigThreads * u;
+            v[u] = ld4(src + (size_t)(r0 + q / 16) * H + c0 + 4 * (q % 16));
+        }
+        if (b > 0) __syncthreads();  // the previous block has been read out
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int q = tid + kDwBigThreads * u;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) tb[4 * (q % 16) + x][q / 16] = v[u][x];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int q = tid + kDwBigThreads * u;
+            const int r = q / 16, c = 4 * (q % 16);
+            st4(dst + (size_t)(c0 + r) * H + r0 + c, f32x4{tb[r][c], tb[r][c + 1], tb[r][c + 2], tb[r][c + 3]});
+        }
+    }
+}
+
+template <int H, int KCW, bool MEAN>
+__global__ __launch_bounds__(kDwBigThreads) void k_dw_f32_big(const float* __restrict__ dY,
+                                                               const float* __restrict__ X,
+                                                               const float* __restrict__ W, float* __restrict__ Wt,
+                                                               float* __restrict__ part_dw,
+                                                               float* __restrict__ part_db,
+                                                               const int* __restrict__ offsets,
+                                                               const int* __restrict__ perm, int NE, int P, int T,
+                                                               int nh, float inv_nh) {
+    __shared__ __attribute__((aligned(16))) char smem[DwF32Smem<256, KCW>::bytes];
+    static_assert(DwF32Smem<256, KCW>::bytes >= sizeof(float) * 64 * 65, "LDS for the transpose");
+    if ((int)blockIdx.x < NE) {
+        transpose_w_body<H>(smem, blockIdx.x, W, Wt);
+        return;
+    }
+    dw_f32_body<H, 256, KCW, MEAN, kDwBigThreads>(smem, (int)blockIdx.x - NE, dY, X, part_dw, part_db, offsets, perm,
+                                                  NE, P, T, nh, inv_nh);
+}
+
+// dX from the transposed weights Wt[e] = W[e]^T (written by the d_W launch), read like the
+// forward reads W: 16-byte fragment reads and the forward's 32-wide K slices.
+template <int H, int BN, int KCX, bool MEAN, bool ACC>
+__global__ __launch_bounds__(kThreads) void k_dx_f32(const float* __restrict__ dY, const float* __restrict__ Wt,
+                                                      float* __restrict__ dX, int accumulate,
+                                                      const int* __restrict__ offsets, const int* __restrict__ perm,
+                                                      int NE, int T, int dx_tile_ids, int nh, float inv_nh) {
+    __shared__ __attribute__((aligned(16))) char smem[RowsF32Smem<128, BN, KCX, false>::bytes];
+    rows_f32_body<H, 128, BN, KCX, true, MEAN, true>(smem, blockIdx.x, gridDim.x, dx_tile_ids, dY, Wt, nullptr, dX,
+                                                     offsets, perm, NE, T, (int)ACC, nh, inv_nh);
 }
 
 // ----------------------------------------------------------------------------------
@@ -1083,6 +1159,9 @@ static int dw_grid(int n_chunk_max) {
 #ifndef MOE_DX_PERSIST_WGS
 #define MOE_DX_PERSIST_WGS 256
 #endif
+#ifndef MOE_DX_BIG_PERSIST_WGS
+#define MOE_DX_BIG_PERSIST_WGS 512  // dX launch of its own (after the 256 x 256 d_W launch): two per CU
+#endif
 #ifndef MOE_DX_TILES_PER_WG
 #define MOE_DX_TILES_PER_WG 1  // dX tiles per workgroup in the large-T backward
 #endif
@@ -1118,12 +1197,28 @@ static hipError_t fwd_f32(const float* X, const float* W, const float* bias, flo
     return hipGetLastError();
 }
 
-template <int H, bool MEAN>
+template <int H, bool MEAN, bool ACC>
 static hipError_t bwd_f32(const float* dY, const float* X, const float* W, float* dX, int accumulate, float* pdw,
-                          float* pdb, const int32_t* offsets, const int32_t* perm, int64_t T, int NE, int P,
+                          float* pdb, float* wt, const int32_t* offsets, const int32_t* perm, int64_t T, int NE, int P,
                           int n_chunk_max, int nh, hipStream_t s) {
     using TL = F32Tiles<H>;
     const float inv_nh = 1.0f / (float)nh;
+    if constexpr (H >= 256) {
+        if (f32_dw_tile(T, H) == 256) {
+            // the kernel timer (if armed) brackets both launches
+            constexpr int TPC = (H / 256) * (H / 256);
+            const int dx_ids = rows_grid<H, TL::BIG_BN>(T, NE, 128);
+            const ArmedEvents ev = take_armed_events();
+            launch_kernel_ev((k_dw_f32_big<H, MOE_F32_KC_DW, MEAN>), dim3(NE + round_up(n_chunk_max, 8) * TPC),
+                             dim3(kDwBigThreads), 0, s, ev.start, nullptr, dY, X, W, wt, pdw, pdb, offsets, perm, NE,
+                             P, (int)T, nh, inv_nh);
+            launch_kernel_ev((k_dx_f32<H, TL::BIG_BN, MOE_F32_KC_FWD, MEAN, ACC>),
+                             dim3(persist_wgs(dx_ids, MOE_DX_BIG_PERSIST_WGS, MOE_DX_BIG_PERSIST_WGS)), dim3(kThreads),
+                             0, s, nullptr, ev.stop, dY, wt, dX, accumulate, offsets, perm, NE, (int)T, dx_ids, nh,
+                             inv_nh);
+            return hipGetLastError();
+        }
+    }
     if (f32_big_tiles(T, H)) {
         // Longest first: the dW workgroups (a whole chunk each) lead the grid and the dX tiles
         // follow, MOE_DX_TILES_PER_WG per workgroup (persistent over those few, so each still
@@ -1132,7 +1227,7 @@ static hipError_t bwd_f32(const float* dY, const float* X, const float* W, float
         const int n_dx = round_up((dx_ids + MOE_DX_TILES_PER_WG - 1) / MOE_DX_TILES_PER_WG, 8);
         const int grid = n_dx + dw_grid<H, TL::BIG_BT>(n_chunk_max);
         launch_kernel(
-            (k_bwd_f32<H, 128, TL::BIG_BN, TL::BIG_BT, MOE_F32_KC_DX, MOE_F32_KC_DW, MEAN, false, true>), dim3(grid),
+            (k_bwd_f32<H, 128, TL::BIG_BN, TL::BIG_BT, MOE_F32_KC_DX, MOE_F32_KC_DW, MEAN, false, true, ACC>), dim3(grid),
             dim3(kThreads), 0, s, dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, NE, P, (int)T, n_dx, dx_ids, nh,
             inv_nh);
         return hipGetLastError();
@@ -1144,12 +1239,12 @@ static hipError_t bwd_f32(const float* dY, const float* X, const float* W, float
     const int grid = n_dx + dw_grid<H, TL::SMALL_BT>(n_chunk_max);
     if (one)
         launch_kernel(
-            (k_bwd_f32<H, TL::SMALL_BM, TL::SMALL_BN, TL::SMALL_BT, MOE_F32_KC_DX, MOE_F32_KC_DW, MEAN, true>),
+            (k_bwd_f32<H, TL::SMALL_BM, TL::SMALL_BN, TL::SMALL_BT, MOE_F32_KC_DX, MOE_F32_KC_DW, MEAN, true, false, ACC>),
             dim3(grid), dim3(kThreads), 0, s, dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, NE, P, (int)T, n_dx,
             dx_ids, nh, inv_nh);
     else
         launch_kernel(
-            (k_bwd_f32<H, TL::SMALL_BM, TL::SMALL_BN, TL::SMALL_BT, MOE_F32_KC_DX, MOE_F32_KC_DW, MEAN, false>),
+            (k_bwd_f32<H, TL::SMALL_BM, TL::SMALL_BN, TL::SMALL_BT, MOE_F32_KC_DX, MOE_F32_KC_DW, MEAN, false, false, ACC>),
             dim3(grid), dim3(kThreads), 0, s, dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, NE, P, (int)T, n_dx,
             dx_ids, nh, inv_nh);
     return hipGetLastError();
@@ -1233,34 +1328,45 @@ hipError_t launch_fwd_gemm_f32(const float* X, const float* W, const float* bias
     return hipErrorInvalidValue;
 }
 
-template <bool MEAN>
-static hipError_t bwd_f32_h(const float* dY, const float* X, const float* W, float* dX, int accumulate, float* pdw,
-                            float* pdb, const int32_t* offsets, const int32_t* perm, int64_t T, int H, int NE, int P,
-                            int n_chunk_max, int nh, hipStream_t s) {
+template <bool MEAN, bool ACC>
+static hipError_t bwd_f32_h2(const float* dY, const float* X, const float* W, float* dX, float* pdw, float* pdb,
+                             float* wt, const int32_t* offsets, const int32_t* perm, int64_t T, int H, int NE, int P,
+                             int n_chunk_max, int nh, hipStream_t s) {
+    const int acc = ACC ? 1 : 0;
     switch (H) {
         case 64:
-            return bwd_f32<64, MEAN>(dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, T, NE, P, n_chunk_max, nh, s);
+            return bwd_f32<64, MEAN, ACC>(dY, X, W, dX, acc, pdw, pdb, wt, offsets, perm, T, NE, P, n_chunk_max, nh, s);
         case 128:
-            return bwd_f32<128, MEAN>(dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, T, NE, P, n_chunk_max, nh, s);
+            return bwd_f32<128, MEAN, ACC>(dY, X, W, dX, acc, pdw, pdb, wt, offsets, perm, T, NE, P, n_chunk_max, nh, s);
         case 256:
-            return bwd_f32<256, MEAN>(dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, T, NE, P, n_chunk_max, nh, s);
+            return bwd_f32<256, MEAN, ACC>(dY, X, W, dX, acc, pdw, pdb, wt, offsets, perm, T, NE, P, n_chunk_max, nh, s);
         case 512:
-            return bwd_f32<512, MEAN>(dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, T, NE, P, n_chunk_max, nh, s);
+            return bwd_f32<512, MEAN, ACC>(dY, X, W, dX, acc, pdw, pdb, wt, offsets, perm, T, NE, P, n_chunk_max, nh, s);
     }
     return hipErrorInvalidValue;
 }
 
+template <bool MEAN>
+static hipError_t bwd_f32_h(const float* dY, const float* X, const float* W, float* dX, int accumulate, float* pdw,
+                            float* pdb, float* wt, const int32_t* offsets, const int32_t* perm, int64_t T, int H,
+                            int NE, int P, int n_chunk_max, int nh, hipStream_t s) {
+    if (accumulate)
+        return bwd_f32_h2<MEAN, true>(dY, X, W, dX, pdw, pdb, wt, offsets, perm, T, H, NE, P, n_chunk_max, nh, s);
+    return bwd_f32_h2<MEAN, false>(dY, X, W, dX, pdw, pdb, wt, offsets, perm, T, H, NE, P, n_chunk_max, nh, s);
+}
+
 hipError_t launch_bwd_gemm_f32(const float* dY, const float* X, const float* W, float* dX, int accumulate,
-                               float* pdw, float* pdb, const int32_t* offsets, const int32_t* perm, int64_t T, int H,
-                               int NE, int P, int n_chunk_max, hipStream_t s) {
-    return bwd_f32_h<false>(dY, X, W, dX, accumulate, pdw, pdb, offsets, perm, T, H, NE, P, n_chunk_max, 1, s);
+                               float* pdw, float* pdb, float* wt, const int32_t* offsets, const int32_t* perm,
+                               int64_t T, int H, int NE, int P, int n_chunk_max, hipStream_t s) {
+    return bwd_f32_h<false>(dY, X, W, dX, accumulate, pdw, pdb, wt, offsets, perm, T, H, NE, P, n_chunk_max, 1, s);
 }
 
 hipError_t launch_bwd_gemm_f32_from_mean(const float* d_mean, const float* X, const float* W, float* dX,
-                                         int accumulate, float* pdw, float* pdb, const int32_t* offsets,
+                                         int accumulate, float* pdw, float* pdb, float* wt, const int32_t* offsets,
                                          const int32_t* perm, int64_t T, int H, int NE, int NH, int P,
                                          int n_chunk_max, hipStream_t s) {
-    return bwd_f32_h<true>(d_mean, X, W, dX, accumulate, pdw, pdb, offsets, perm, T, H, NE, P, n_chunk_max, NH, s);
+    return bwd_f32_h<true>(d_mean, X, W, dX, accumulate, pdw, pdb, wt, offsets, perm, T, H, NE, P, n_chunk_max, NH,
+                           s);
 }
 
 }  // namespace moe

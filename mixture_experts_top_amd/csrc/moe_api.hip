@@ -47,12 +47,20 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 #ifndef MOE_DW_WORKGROUPS_BF16
 #define MOE_DW_WORKGROUPS_BF16 320
 #endif
-static int plan_chunks(int64_t T, int H, int act) {
+// 256 x 256 d_W tiles (bf16 and large-T fp32 at H = 256, 512): one workgroup per compute unit,
+// in a launch of their own, so the budget is one round of 256 workgroups.
+#ifndef MOE_DW_WORKGROUPS_BIG
+#define MOE_DW_WORKGROUPS_BIG 256
+#endif
+static int plan_chunks(int64_t T, int H, int NE, int act) {
     const bool f32 = act == MOE_DTYPE_F32;
-    const int bt = f32 ? f32_dw_tile(T, H) : ((H >= 128) ? 128 : 64);
+    const int bt = f32 ? f32_dw_tile(T, H) : bf16_dw_tile(H);
     const int tiles_per_chunk = (H / bt) * (H / bt);
-    const int64_t wg = f32 ? MOE_DW_WORKGROUPS : MOE_DW_WORKGROUPS_BF16;
-    const int64_t pmax = (wg + tiles_per_chunk - 1) / tiles_per_chunk;
+    const int64_t wg = bt == 256 ? MOE_DW_WORKGROUPS_BIG : (f32 ? MOE_DW_WORKGROUPS : MOE_DW_WORKGROUPS_BF16);
+    int64_t pmax = (wg + tiles_per_chunk - 1) / tiles_per_chunk;
+    // the 256 x 256 tiles run one round of one workgroup per compute unit: plan P so that even
+    // the worst case of P + N_E chunks stays within the budget
+    if (bt == 256) pmax = pmax - NE > 1 ? pmax - NE : 1;
     int64_t p = T / ((f32 && f32_big_tiles(T, H)) ? MOE_DW_MIN_CHUNK_BIG : MOE_DW_MIN_CHUNK);
     if (p > pmax) p = pmax;
     if (p < 1) p = 1;
@@ -68,7 +76,7 @@ Plan make_plan(int64_t T, int H, int NE, int act) {
     p.n_rblk = (int)((T + kRouteTokens - 1) / kRouteTokens);
     p.n_ablk = (int)((T + kAuxTokens - 1) / kAuxTokens);
     if (H > 0) {
-        p.chunks = plan_chunks(T, H, act);
+        p.chunks = plan_chunks(T, H, NE, act);
         p.n_chunk_max = p.chunks + NE;
     }
     size_t o = 0;
@@ -80,6 +88,8 @@ Plan make_plan(int64_t T, int H, int NE, int act) {
     p.off_paux = o;    o += align256((size_t)p.n_ablk * NE * 4);
     p.off_pdw = o;     o += align256((size_t)p.n_chunk_max * H * H * 4);
     p.off_pdb = o;     o += align256((size_t)p.n_chunk_max * H * 4);
+    p.wt_bytes = (act == MOE_DTYPE_F32 && H > 0 && f32_dw_tile(T, H) == 256) ? (size_t)NE * H * H * 4 : 0;
+    p.off_wt = o;      o += align256(p.wt_bytes);
     p.total = o;
     return p;
 }
@@ -368,8 +378,6 @@ static moe_status_t bwd_impl(const char* fn, const void* dy, int from_mean, cons
                              void* workspace, size_t workspace_bytes, void* stream) {
     moe_status_t st = check_shape(fn, B, NH, H, NE, act, true);
     if (st != MOE_OK) return st;
-    if (from_mean && act != MOE_DTYPE_F32)
-        return fail(MOE_ERR_UNSUPPORTED, "%s: only fp32 activations are supported", fn);
     REQ(dy); REQ(fused_ctx); REQ(W); REQ(expert_offsets); REQ(perm);
     REQ(d_fused_ctx); REQ(d_W); REQ(d_b);
     const Plan p = make_plan(B * NH, (int)H, (int)NE, act);
@@ -377,16 +385,23 @@ static moe_status_t bwd_impl(const char* fn, const void* dy, int from_mean, cons
     hipStream_t s = (hipStream_t)stream;
     float* pdw = at<float>(workspace, p.off_pdw);
     float* pdb = at<float>(workspace, p.off_pdb);
-    if (from_mean) {
+    float* wt = at<float>(workspace, p.off_wt);
+    if (from_mean && act == MOE_DTYPE_F32) {
         LAUNCH(K_BWD_GEMM,
                launch_bwd_gemm_f32_from_mean((const float*)dy, (const float*)fused_ctx, (const float*)W,
-                                             (float*)d_fused_ctx, accumulate_dx, pdw, pdb, expert_offsets, perm, p.T,
-                                             p.H, p.NE, (int)NH, p.chunks, p.n_chunk_max, s),
+                                             (float*)d_fused_ctx, accumulate_dx, pdw, pdb, wt, expert_offsets, perm,
+                                             p.T, p.H, p.NE, (int)NH, p.chunks, p.n_chunk_max, s),
+               "bwd gemm (from mean)");
+    } else if (from_mean) {
+        LAUNCH(K_BWD_GEMM,
+               launch_bwd_gemm_bf16_from_mean((const uint16_t*)dy, (const uint16_t*)fused_ctx, (const uint16_t*)W,
+                                              (uint16_t*)d_fused_ctx, accumulate_dx, pdw, pdb, expert_offsets, perm,
+                                              p.T, p.H, p.NE, (int)NH, p.chunks, p.n_chunk_max, s),
                "bwd gemm (from mean)");
     } else if (act == MOE_DTYPE_F32) {
         LAUNCH(K_BWD_GEMM,
                launch_bwd_gemm_f32((const float*)dy, (const float*)fused_ctx, (const float*)W, (float*)d_fused_ctx,
-                                   accumulate_dx, pdw, pdb, expert_offsets, perm, p.T, p.H, p.NE, p.chunks,
+                                   accumulate_dx, pdw, pdb, wt, expert_offsets, perm, p.T, p.H, p.NE, p.chunks,
                                    p.n_chunk_max, s),
                "bwd gemm");
     } else {
@@ -409,7 +424,7 @@ moe_status_t moe_top1_bwd(const void* d_routed_ctx, const void* fused_ctx, const
                     accumulate_dx, B, NH, H, NE, act, workspace, workspace_bytes, stream);
 }
 
-moe_status_t moe_top1_bwd_from_mean(const float* d_ctx_mean, const void* fused_ctx, const void* W,
+moe_status_t moe_top1_bwd_from_mean(const void* d_ctx_mean, const void* fused_ctx, const void* W,
                                     const int32_t* expert_offsets, const int32_t* perm, void* d_fused_ctx, float* d_W,
                                     float* d_b, int accumulate_dx, int64_t B, int64_t NH, int64_t H, int64_t NE,
                                     int act, void* workspace, size_t workspace_bytes, void* stream) {

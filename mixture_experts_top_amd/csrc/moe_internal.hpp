@@ -57,11 +57,24 @@ inline bool f32_big_tiles(int64_t T, int H) {
     const int64_t nt = H >= 128 ? H / 128 : 1;
     return (T / 128) * nt >= MOE_ROWS_BIG_TILES_PER_CU * 256;
 }
+// fp32 d_W tiles of 256 x 256 at large T for H = 256, 512: eight wavefronts per workgroup,
+// one workgroup per compute unit, in a launch of their own ahead of the dX launch.
+#ifndef MOE_F32_DW_BIG
+#define MOE_F32_DW_BIG 1
+#endif
 inline int f32_dw_tile(int64_t T, int H) {
     const int big = H >= 128 ? 128 : 64;
     const int small = MOE_DW_SMALL_BT < H ? MOE_DW_SMALL_BT : H;
-    return f32_big_tiles(T, H) ? big : small;
+    if (!f32_big_tiles(T, H)) return small;
+    return (MOE_F32_DW_BIG && H >= 256) ? 256 : big;
 }
+
+// bf16 d_W output tile (BT x BT per workgroup): 256 x 256 for H = 256 / 512 (one workgroup of
+// four wavefronts per compute unit, each wavefront a 128 x 128 quarter), else H or 128.
+#ifndef MOE_BF16_DW_BIG
+#define MOE_BF16_DW_BIG 1
+#endif
+constexpr int bf16_dw_tile(int H) { return (MOE_BF16_DW_BIG && H >= 256) ? 256 : (H >= 128 ? 128 : 64); }
 
 // Chunking of each expert's tokens for the d_W split-K.  With P chunks planned for T
 // tokens, expert e (c_e tokens) gets n_e = ceil(c_e P / T) chunks (none if c_e = 0), and
@@ -166,6 +179,7 @@ struct Plan {
     int n_ablk = 0;       // aux blocks
     size_t off_hist = 0, off_blkbase = 0, off_idx = 0, off_counts = 0, off_offsets = 0;
     size_t off_pdw = 0, off_pdb = 0, off_paux = 0;
+    size_t off_wt = 0, wt_bytes = 0;  // W^T per expert (fp32 with 256 x 256 d_W tiles), else empty
     size_t total = 0;
 };
 
@@ -201,6 +215,25 @@ inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint3
     } else {
         hipLaunchKernelGGL(kernel, grid, block, shm, s, static_cast<KArgs>(args)...);
     }
+}
+
+// A launch with explicit start / stop events (either may be null), for a launcher that makes
+// several launches under one kernel id: it takes the armed events (take_armed_events) and
+// gives the start event to its first launch and the stop event to its last, so the pair
+// brackets all of them.
+template <typename... KArgs, typename... Args>
+inline void launch_kernel_ev(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t shm, hipStream_t s,
+                             hipEvent_t start, hipEvent_t stop, Args... args) {
+    static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count");
+    if (start != nullptr || stop != nullptr)
+        hipExtLaunchKernelGGL(kernel, grid, block, shm, s, start, stop, 0u, static_cast<KArgs>(args)...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, shm, s, static_cast<KArgs>(args)...);
+}
+inline ArmedEvents take_armed_events() {
+    ArmedEvents e = armed_events();
+    armed_events() = ArmedEvents{};
+    return e;
 }
 
 // ---- launchers (each returns the hipError_t of its launch) ----
@@ -248,15 +281,16 @@ hipError_t launch_fwd_gemm_f32_gather(const float* X, const float* W, const floa
 hipError_t launch_fwd_gemm_f32(const float* X, const float* W, const float* bias, float* Y,
                                const int32_t* offsets, const int32_t* perm, int64_t T, int H, int NE,
                                hipStream_t s);
-// dX (overwrite or accumulate) and the d_W / d_b chunk partials, one launch
+// dX (overwrite or accumulate) and the d_W / d_b chunk partials (wt: the plan's W^T section,
+// used with the 256 x 256 d_W tiles)
 hipError_t launch_bwd_gemm_f32(const float* dY, const float* X, const float* W, float* dX, int accumulate,
-                               float* part_dw, float* part_db, const int32_t* offsets, const int32_t* perm,
+                               float* part_dw, float* part_db, float* wt, const int32_t* offsets, const int32_t* perm,
                                int64_t T, int H, int NE, int P, int n_chunk_max, hipStream_t s);
 // same, with row t of dY = d_mean[t / NH] * (1/NH) (backward through a mean over NH horizons)
 hipError_t launch_bwd_gemm_f32_from_mean(const float* d_mean, const float* X, const float* W, float* dX,
-                                         int accumulate, float* part_dw, float* part_db, const int32_t* offsets,
-                                         const int32_t* perm, int64_t T, int H, int NE, int NH, int P,
-                                         int n_chunk_max, hipStream_t s);
+                                         int accumulate, float* part_dw, float* part_db, float* wt,
+                                         const int32_t* offsets, const int32_t* perm, int64_t T, int H, int NE, int NH,
+                                         int P, int n_chunk_max, hipStream_t s);
 // bf16 storage (raw uint16 patterns), fp32 accumulation
 hipError_t launch_fwd_gemm_bf16(const uint16_t* X, const uint16_t* W, const float* bias, uint16_t* Y,
                                 const int32_t* offsets, const int32_t* perm, int64_t T, int H, int NE,
@@ -265,6 +299,11 @@ hipError_t launch_bwd_gemm_bf16(const uint16_t* dY, const uint16_t* X, const uin
                                 int accumulate, float* part_dw, float* part_db, const int32_t* offsets,
                                 const int32_t* perm, int64_t T, int H, int NE, int P, int n_chunk_max,
                                 hipStream_t s);
+// same, with row t of dY = bf16(d_mean[t / NH] * (1/NH)) (backward through a mean over NH horizons)
+hipError_t launch_bwd_gemm_bf16_from_mean(const uint16_t* d_mean, const uint16_t* X, const uint16_t* W, uint16_t* dX,
+                                          int accumulate, float* part_dw, float* part_db, const int32_t* offsets,
+                                          const int32_t* perm, int64_t T, int H, int NE, int NH, int P,
+                                          int n_chunk_max, hipStream_t s);
 hipError_t launch_reduce_dw(const float* part_dw, const float* part_db, const int32_t* offsets,
                             int64_t T, int H, int NE, int P, float* dW, float* db, hipStream_t s);
 

@@ -191,7 +191,9 @@ def test_next_rows_validation(lib):
     assert lib.moe_horizon_mean_collapse_bwd(FAKE, FAKE, 4, 5, 12, 1, None) == UNSUPPORTED  # H % 8 for bf16
     assert lib.moe_horizon_mean_collapse_fwd(None, FAKE, 4, 5, 64, 0, None) == INVALID
     assert lib.moe_top1_bwd_from_mean(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 5, 128, 4, 1, FAKE,
-                                      1 << 40, None) == UNSUPPORTED                      # bf16
+                                      0, None) == WORKSPACE                              # bf16, no room
+    assert lib.moe_top1_bwd_from_mean(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 5, 128, 4, 2, FAKE,
+                                      1 << 40, None) == UNSUPPORTED                      # unknown dtype
     assert lib.moe_softmax_ce_grad(FAKE, FAKE, FAKE, FAKE, 4, 5, 65, None) == UNSUPPORTED
     assert lib.moe_softmax_ce_grad(FAKE, None, FAKE, FAKE, 4, 5, 21, None) == INVALID
     assert lib.moe_softmax_ce_grad(FAKE, FAKE, FAKE, FAKE, 0, 5, 21, None) == INVALID

@@ -76,8 +76,13 @@ def test_horizon_mean_collapse(gpu_lib, act, B, NH, H):
 
 @pytest.mark.parametrize("wl", [workloads.custom(173, 7, 128, 3), workloads.custom(61, 5, 256, 8),
                                 workloads.custom(3001, 5, 64, 4),
-                                pytest.param(workloads.custom(14000, 5, 128, 4), marks=pytest.mark.slow)],
-                         ids=["H128", "H256", "H64_multiblock", "H128_large_T_tiling"])
+                                pytest.param(workloads.custom(14000, 5, 128, 4), marks=pytest.mark.slow),
+                                pytest.param(workloads.custom(9000, 5, 256, 6), marks=pytest.mark.slow),
+                                workloads.custom(97, 5, 128, 3, act="bf16"),
+                                workloads.custom(150, 7, 256, 5, act="bf16"),
+                                workloads.custom(600, 5, 512, 8, act="bf16", gate_bias={2: 1.0})],
+                         ids=["H128", "H256", "H64_multiblock", "H128_large_T_tiling", "H256_big_dw_tiles",
+                              "bf16_H128", "bf16_H256", "bf16_H512"])
 def test_bwd_from_mean_equals_collapse_then_bwd(gpu_lib, wl):
     import torch
     import mixture_experts_top_amd as moe
@@ -85,12 +90,16 @@ def test_bwd_from_mean_equals_collapse_then_bwd(gpu_lib, wl):
     inp = workloads.make_inputs(wl)
     B, NH, H = inp.fused_ctx.shape
     d_mean = np.random.default_rng(9).standard_normal((B, H)).astype(np.float32)
+    d_bits = None
+    if wl.act == "bf16":
+        d_bits = workloads.f32_to_bf16_bits(d_mean)
+        d_mean = workloads.bf16_bits_to_f32(d_bits)
     dv = gpu_run.upload(inp)
     o = gpu_run.Buffers(dv)
     gpu_run.fwd(dv, o)
-    dm = torch.from_numpy(d_mean).cuda()
+    dm = gpu_run.dev_act(d_mean, d_bits)
     # unfused: collapse backward, then the gate backward
-    dY = torch.empty(B, NH, H, device="cuda")
+    dY = torch.empty(B, NH, H, dtype=dv.x.dtype, device="cuda")
     moe.moe_horizon_mean_collapse_bwd(dm, dY)
     dv2 = gpu_run.DevInputs(dv.x, dv.g, dv.W, dv.b, dY, dv.lam)
     gpu_run.bwd(dv2, o)
@@ -106,9 +115,14 @@ def test_bwd_from_mean_equals_collapse_then_bwd(gpu_lib, wl):
     # and against the oracle
     f = O.forward(inp.fused_ctx, inp.gate_logits, inp.W, inp.b)
     bw = O.backward(N.horizon_mean_bwd(d_mean, NH), inp.fused_ctx, inp.W, f.expert_idx)
-    C.elementwise("d_fused_ctx", got["dx"].reshape(B * NH, H), bw.d_fused_ctx)
-    C.per_expert_scaled("d_W", got["dW"], bw.d_W)
-    C.per_expert_scaled("d_b", got["db"], bw.d_b)
+    if wl.act == "bf16":
+        C.bf16_scaled("d_fused_ctx", got["dx"].reshape(B * NH, H), bw.d_fused_ctx)
+        C.bf16_scaled("d_W", got["dW"], bw.d_W, per_expert=True)
+        C.bf16_scaled("d_b", got["db"], bw.d_b, per_expert=True)
+    else:
+        C.elementwise("d_fused_ctx", got["dx"].reshape(B * NH, H), bw.d_fused_ctx)
+        C.per_expert_scaled("d_W", got["dW"], bw.d_W)
+        C.per_expert_scaled("d_b", got["db"], bw.d_b)
 
 
 # ---------------------------------------------------------------- softmax-CE head

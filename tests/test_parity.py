@@ -141,10 +141,13 @@ def test_route_entry_point_matches_fwd_routing(gpu_lib):
     C.exact("perm", perm.cpu().numpy(), p)
 
 
-def test_accumulate_dx(gpu_lib):
+@pytest.mark.parametrize("wl", [workloads.custom(70, 5, 128, 4), workloads.custom(9000, 5, 256, 6),
+                                workloads.custom(14000, 5, 128, 8)],
+                         ids=["small_T", "big_dw_tiles_H256", "large_T_H128"])
+def test_accumulate_dx(gpu_lib, wl):
     import torch
     from tests import gpu_run
-    inp = workloads.make_inputs(workloads.custom(70, 5, 128, 4))
+    inp = workloads.make_inputs(wl)
     d = gpu_run.upload(inp)
     o = gpu_run.Buffers(d)
     gpu_run.fwd(d, o)
@@ -157,10 +160,14 @@ def test_accumulate_dx(gpu_lib):
     C.elementwise("d_fused_ctx (accumulate)", got["dx"].reshape(bw.d_fused_ctx.shape), bw.d_fused_ctx)
 
 
-def test_accumulate_dx_bf16(gpu_lib):
+@pytest.mark.parametrize("wl", [workloads.custom(70, 5, 256, 4, act="bf16"),
+                                workloads.custom(900, 5, 512, 6, act="bf16"),
+                                workloads.custom(300, 5, 128, 4, act="bf16")],
+                         ids=["H256", "H512", "H128_one_launch"])
+def test_accumulate_dx_bf16(gpu_lib, wl):
     import torch
     from tests import gpu_run
-    inp = workloads.make_inputs(workloads.custom(70, 5, 256, 4, act="bf16"))
+    inp = workloads.make_inputs(wl)
     d = gpu_run.upload(inp)
     o = gpu_run.Buffers(d)
     gpu_run.fwd(d, o)
@@ -208,6 +215,19 @@ def test_persistent_tiles_full_parity(gpu_lib):
     from tests import gpu_run
     wl = workloads.custom(20000, 5, 256, 8, gate_bias={4: 1.5}, lam=0.05)
     print(f"[parity] persistent tiles {wl}", flush=True)
+    inp = workloads.make_inputs(wl)
+    check_all(inp, gpu_run.run(inp))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("wl", [workloads.custom(4000, 5, 512, 6, gate_bias={1: 0.7}),
+                                workloads.custom(7000, 5, 256, 20, gate="int")],
+                         ids=["H512_NE6", "H256_NE20_ties"])
+def test_big_dw_tiles_full_parity(gpu_lib, wl):
+    """Large-T fp32 at H = 256 / 512: 256 x 256 d_W tiles (a launch of their own, four per chunk
+    at H = 512) and the persistent dX launch, with ragged chunks, tied logits and N_E = 20."""
+    from tests import gpu_run
+    print(f"[parity] big d_W tiles {wl}", flush=True)
     inp = workloads.make_inputs(wl)
     check_all(inp, gpu_run.run(inp))
 
