@@ -1072,6 +1072,186 @@ __device__ __forceinline__ void dw_bf16_tr_body(char* smem, int bid, const uint1
     }
 }
 
+// The same d_W tile fed by direct global -> LDS loads.  Same tile, wavefront grid and LDS row
+// layout as dw_bf16_tr_body (token-major rows of 512 bytes, chunk c of row t at c ^ 4 (t & 3)),
+// but the rows go from global memory straight into LDS with gfx950's global_load_lds_dwordx4
+// (lane i's 16 bytes land at the instruction's LDS base + 16 i), through a ring of R stages of
+// 32 tokens: the rows of the next R - 1 slices are in flight while a slice computes, and they
+// cost no registers.  Each stage is an LDS object of its own, so the compiler can tell the
+// stages apart and a read of one stage does not wait for the loads into another.  A slice is
+// complete in LDS once this wavefront's vector-memory counter has fallen to the number of loads
+// issued after it -- every ring step issues the same six (four row loads, two token ids) in a
+// fixed order, with no exit inside a ring cycle -- and visible to every wavefront after the
+// barrier that follows.
+// Rows past the chunk's end (and the slices that pad the last ring cycle) read a zero row.
+#ifndef MOE_BF16_DW_DMA
+#define MOE_BF16_DW_DMA 1
+#endif
+#ifndef MOE_BF16_DMA_STAGES
+#define MOE_BF16_DMA_STAGES 4
+#endif
+struct DwdSmem {
+    static constexpr int KC = 32, ROWB = 512;            // tokens per slice, bytes per row
+    static constexpr size_t tensor = (size_t)KC * ROWB;  // one tensor of one slice: 16 KB
+    static constexpr size_t stage = 2 * tensor;          // dY then X
+};
+static __device__ __attribute__((aligned(16))) uint16_t kZeroRow[256];
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// s_waitcnt with the vector-memory count at N and the LDS count at 0 (export count untouched)
+template <int N>
+__device__ __forceinline__ void wait_vm_lds() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+template <int H, bool MEAN, int R>
+__device__ __forceinline__ void dw_bf16_dma_body(char* const (&st)[R], int bid, const uint16_t* __restrict__ dY,
+                                                 const uint16_t* __restrict__ X, float* __restrict__ part_dw,
+                                                 float* __restrict__ part_db, const int* __restrict__ offsets,
+                                                 const int* __restrict__ perm, int NE, int P, int T, int nh,
+                                                 float inv_nh) {
+    static_assert(R >= 3, "ring depth");
+    constexpr int BT = 256, NTI = H / BT, TPC = NTI * NTI;
+    constexpr int KC = DwdSmem::KC, ROWB = DwdSmem::ROWB;
+    constexpr int SUBM = 4, SUBN = 2;  // 128 x 64 per wavefront
+
+    int c, tl;
+    xcd_split(bid, TPC, c, tl);
+    int e = -1, t0 = 0, t1 = 0;
+    if (!find_chunk(offsets, NE, P, T, c, e, t0, t1)) return;
+    const int o0 = (tl / NTI) * BT, i0 = (tl % NTI) * BT;
+    const bool do_db = (tl % NTI) == 0;
+    const int tid = threadIdx.x;
+    const int wave = tid / 64, lane = tid % 64, l32 = lane % 32;
+    const int wm = wave / 4, wn = wave % 4;
+    const bool db_wave = do_db && wn == 0;
+
+    f32x16 acc[SUBM][SUBN];
+#pragma unroll
+    for (int i = 0; i < SUBM; ++i)
+#pragma unroll
+        for (int j = 0; j < SUBN; ++j) acc[i][j] = f32x16{};
+    float dbacc[SUBM] = {0.0f, 0.0f, 0.0f, 0.0f};
+
+    // wavefront w fills rows 4w .. 4w + 3 of each tensor of a stage, two rows per load: in load q,
+    // lane i takes row 4w + 2q + (i >> 5) and physical chunk i & 31, i.e. logical chunk
+    // (i & 31) ^ 4 (row & 3) with row & 3 = 2q + (i >> 5)
+    const int lh = lane >> 5, pch = lane & 31;
+    const int lc0 = pch ^ (4 * lh), lc1 = pch ^ (4 * (2 + lh));
+    const int nslices = (t1 - t0 + KC - 1) / KC;
+    auto row_k = [&](int sl, int q) { return t0 + sl * KC + 4 * wave + 2 * q + lh; };
+    // perm entries of the slice whose index is congruent to the slot mod R, as loaded: the
+    // guard is applied where the rows are addressed, so no wait for them sits at the ring's back edge
+    int tk[R][2];
+    auto load_ids = [&](int sl, int slot) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int k = row_k(sl, q);
+            tk[slot][q] = perm[k < t1 ? k : (t1 > 0 ? t1 - 1 : 0)];
+        }
+    };
+    auto dma = [&](int sl, int slot, char* stg) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const bool v = row_k(sl, q) < t1;
+            const int lc = q ? lc1 : lc0;
+            const size_t t = (size_t)guard_token(tk[slot][q], T);
+            const uint16_t* gy = v ? dY + (MEAN ? t / nh : t) * H + o0 + 8 * lc : kZeroRow + 8 * lc;
+            const uint16_t* gx = v ? X + t * H + i0 + 8 * lc : kZeroRow + 8 * lc;
+            char* ly = stg + (4 * wave + 2 * q) * ROWB;
+            __builtin_amdgcn_global_load_lds((const void*)gy, (lds_void_ptr)ly, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)gx, (lds_void_ptr)(ly + DwdSmem::tensor), 16, 0, 0);
+        }
+    };
+    auto compute = [&](const char* stg) {
+        const char* ta = stg;
+        const char* tb = stg + DwdSmem::tensor;
+#pragma unroll
+        for (int kk = 0; kk < KC; kk += 16) {
+            u16x8 a[SUBM], b[SUBN];
+#pragma unroll
+            for (int i = 0; i < SUBM; ++i) {
+                a[i] = tr_frag_swz(ta, kk, wm * 128 + 32 * i, lane);
+                if (MEAN) a[i] = scale8(a[i], inv_nh);
+            }
+#pragma unroll
+            for (int j = 0; j < SUBN; ++j) b[j] = tr_frag_swz(tb, kk, wn * 64 + 32 * j, lane);
+#pragma unroll
+            for (int i = 0; i < SUBM; ++i)
+#pragma unroll
+                for (int j = 0; j < SUBN; ++j) acc[i][j] = mfma_bf16(a[i], b[j], acc[i][j]);
+            if (db_wave) {
+#pragma unroll
+                for (int i = 0; i < SUBM; ++i)
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) dbacc[i] += bf16_to_f32(a[i][q]);
+            }
+        }
+    };
+
+    // prologue: token ids of slices 0 .. R - 1, then the rows of slices 0 .. R - 2, each followed
+    // by the ids of the slice R later (the same six loads per slice as a ring step).  The
+    // scheduling barriers keep the loads in this order, which the counts below rely on.
+    auto pin = [] {  // no load moves across this point, in the optimiser or the scheduler
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+#pragma unroll
+    for (int k = 0; k < R; ++k) load_ids(k, k);
+#pragma unroll
+    for (int k = 0; k + 1 < R; ++k) {
+        pin();
+        dma(k, k, st[k]);
+        pin();
+        load_ids(k + R, k);
+    }
+    pin();
+    // ring step s: wait for slice s (at least the R - 2 later steps' six loads each were issued
+    // after its rows), barrier (slice s visible; every wavefront is done with the stage of slice
+    // s - 1), rows of slice s + R - 1 into that stage, ids of slice s + 2R - 1, slice s's MFMAs
+    // at least one cycle, so the loop has no conditional entry for the prologue's loads to sink
+    // into (an empty chunk computes nothing and writes zeros)
+    const int ncycles = max(1, (nslices + R - 1) / R);
+    int cyc = 0;
+#pragma unroll 1
+    do {
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            const int s = cyc * R + u;
+            wait_vm_lds<6 * (R - 2)>();
+            __builtin_amdgcn_s_barrier();
+            pin();
+            dma(s + R - 1, (u + R - 1) % R, st[(u + R - 1) % R]);
+            pin();
+            load_ids(s + 2 * R - 1, (u + R - 1) % R);
+            pin();
+            if (s < nslices) compute(st[u]);
+        }
+    } while (++cyc < ncycles);
+    // every load into LDS must land before the workgroup ends (the LDS is the next one's)
+    wait_vm_lds<0>();
+
+    // the partial tile straight from the accumulators: each store writes two 128-byte row pieces
+    float* __restrict__ Pd = part_dw + (size_t)c * H * H;
+    const int h = lane / 32;
+#pragma unroll
+    for (int i = 0; i < SUBM; ++i)
+#pragma unroll
+        for (int j = 0; j < SUBN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                Pd[(size_t)(o0 + wm * 128 + i * 32 + 8 * (r / 4) + 4 * h + (r % 4)) * H + i0 + wn * 64 + j * 32 + l32] =
+                    acc[i][j][r];
+    if (db_wave) {
+#pragma unroll
+        for (int i = 0; i < SUBM; ++i) {
+            const float tot = dbacc[i] + __shfl_xor(dbacc[i], 32);
+            if (lane < 32) part_db[(size_t)c * H + o0 + wm * 128 + 32 * i + l32] = tot;
+        }
+    }
+}
+
 // Kernels.  For H <= 128 the backward is one launch: dW / db chunk tiles first, then dX tiles.
 // For H = 256 / 512 the 256 x 256 dW tiles take a whole compute unit each (their registers), so
 // they run as a launch of their own ahead of the dX launch.
@@ -1122,7 +1302,21 @@ __global__ __launch_bounds__(kDwBigThreads) void k_dw_bf16(const uint16_t* __res
                                                           const int* __restrict__ perm, int NE, int P, int T, int nh,
                                                           float inv_nh) {
     constexpr int BT = bf16_dw_tile(H);
-    if constexpr (MOE_BF16_DW_TR) {
+    if constexpr (MOE_BF16_DW_DMA) {
+        static_assert(kDwBigThreads == 512 && BT == 256, "direct-to-LDS d_W tile shape");
+        constexpr int R = MOE_BF16_DMA_STAGES;
+        static_assert(R >= 3 && R <= 5, "stages of 32 KB within the LDS");
+        __shared__ __attribute__((aligned(16))) char s0[DwdSmem::stage];
+        __shared__ __attribute__((aligned(16))) char s1[DwdSmem::stage];
+        __shared__ __attribute__((aligned(16))) char s2[R > 2 ? DwdSmem::stage : 16];
+        __shared__ __attribute__((aligned(16))) char s3[R > 3 ? DwdSmem::stage : 16];
+        __shared__ __attribute__((aligned(16))) char s4[R > 4 ? DwdSmem::stage : 16];
+        char* const all[5] = {s0, s1, s2, s3, s4};
+        char* st[R];
+#pragma unroll
+        for (int k = 0; k < R; ++k) st[k] = all[k];
+        dw_bf16_dma_body<H, MEAN, R>(st, blockIdx.x, dY, X, part_dw, part_db, offsets, perm, NE, P, T, nh, inv_nh);
+    } else if constexpr (MOE_BF16_DW_TR) {
         static_assert(kDwtThreads == kDwBigThreads && BT == 256, "token-major d_W tile shape");
         __shared__ __attribute__((aligned(16))) char smem[DwtSmem::bytes];
         dw_bf16_tr_body<H, MEAN>(smem, blockIdx.x, dY, X, part_dw, part_db, offsets, perm, NE, P, T, nh, inv_nh);
