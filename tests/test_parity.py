@@ -162,8 +162,9 @@ def test_accumulate_dx(gpu_lib, wl):
 
 @pytest.mark.parametrize("wl", [workloads.custom(70, 5, 256, 4, act="bf16"),
                                 workloads.custom(900, 5, 512, 6, act="bf16"),
-                                workloads.custom(300, 5, 128, 4, act="bf16")],
-                         ids=["H256", "H512", "H128_one_launch"])
+                                workloads.custom(300, 5, 128, 4, act="bf16"),
+                                pytest.param(workloads.custom(14000, 5, 512, 6, act="bf16"), marks=pytest.mark.slow)],
+                         ids=["H256", "H512", "H128_one_launch", "H512_large_T"])
 def test_accumulate_dx_bf16(gpu_lib, wl):
     import torch
     from tests import gpu_run
@@ -228,6 +229,20 @@ def test_big_dw_tiles_full_parity(gpu_lib, wl):
     at H = 512) and the persistent dX launch, with ragged chunks, tied logits and N_E = 20."""
     from tests import gpu_run
     print(f"[parity] big d_W tiles {wl}", flush=True)
+    inp = workloads.make_inputs(wl)
+    check_all(inp, gpu_run.run(inp))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("wl", [workloads.custom(14000, 5, 512, 8, act="bf16", gate_bias={3: 1.0}),
+                                workloads.custom(27000, 5, 256, 6, act="bf16", gate="int")],
+                         ids=["H512_skewed", "H256_ties"])
+def test_bf16_large_T_full_parity(gpu_lib, wl):
+    """bf16 at H = 256 / 512 and 70,000 - 135,000 tokens: the resident-slice forward, the dX
+    tiles and the d_W tiles fed by direct global-to-LDS loads (about 90 slices per chunk), with
+    a ragged tile at every expert's end, a skewed expert and tied logits."""
+    from tests import gpu_run
+    print(f"[parity] bf16 large T {wl}", flush=True)
     inp = workloads.make_inputs(wl)
     check_all(inp, gpu_run.run(inp))
 
