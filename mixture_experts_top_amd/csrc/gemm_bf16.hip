@@ -1095,7 +1095,7 @@ struct DwdSmem {
     static constexpr size_t tensor = (size_t)KC * ROWB;  // one tensor of one slice: 16 KB
     static constexpr size_t stage = 2 * tensor;          // dY then X
 };
-static __device__ __attribute__((aligned(16))) uint16_t kZeroRow[256];
+static __device__ __attribute__((aligned(16))) uint16_t kZeroRow[512];  // one zero row of up to H = 512
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
 // s_waitcnt with the vector-memory count at N and the LDS count at 0 (export count untouched)
@@ -1252,6 +1252,241 @@ __device__ __forceinline__ void dw_bf16_dma_body(char* const (&st)[R], int bid, 
     }
 }
 
+// W-stationary row GEMM (H = 256 / 512, large T): Out[t, n0 : n0 + 256] = A[t, :] . Wm[n, :]^T
+// (+ bias) for the tokens of one expert.  Each of the 256 workgroups (one per compute unit,
+// eight wavefronts, two per SIMD) owns a 256-feature slice of W[e] -- each wavefront 32
+// features, held in its registers as MFMA operands for the whole K (128 VGPRs at H = 512) --
+// and streams a fixed share of the expert-sorted token order through it in groups of 32
+// tokens: their rows go to LDS whole (one row per load instruction at H = 512, 16-byte chunk c
+// of row r at c ^ (r & 15)), each wavefront reads its MFMA fragments from there, and the fp32
+// results are staged in LDS and written a group later by all threads as whole 512-byte pieces
+// of output rows.  Against the resident-slice forward (W in LDS, rows loaded straight into
+// operand registers, 64 rows per load instruction) a row is fetched by half as many compute
+// units and each load touches 8 cache lines instead of 64.  The forward passes W ([n][k]),
+// dX passes W^T.
+// The token share: slice s of workgroup wg covers positions [v T / V, (v + 1) T / V) of the
+// expert-sorted order (V workgroups per slice, the slices of one share on one XCD), cut at
+// expert boundaries into segments; each segment loads its expert's W slice once (dX: its W^T
+// fragments, through LDS and the transposing read).
+#ifndef MOE_BF16_WST
+#define MOE_BF16_WST 1
+#endif
+constexpr int kWstThreads = 512, kWstWgs = 256, kWstGT = 32;
+template <int H>
+struct WstSmem {
+    static constexpr int ROWB = 2 * H;                          // bytes per token row
+    static constexpr size_t xbuf = (size_t)kWstGT * ROWB;       // one group's rows
+    static constexpr size_t obuf = (size_t)kWstGT * 256 * 4;    // one group's fp32 results [32][256]
+    static constexpr size_t ost_off = 2 * xbuf;
+    static constexpr size_t bias_off = ost_off + 2 * obuf;
+    static constexpr size_t ids_off = bias_off + 256 * 4;       // token ids: [5][32]
+    static constexpr size_t bytes = ids_off + 5 * kWstGT * 4;
+};
+// 256 workgroups when every slice share holds at least 8 groups of 32 tokens
+static inline bool bf16_wst(int64_t T, int H) {
+    return MOE_BF16_WST && H >= 256 && T >= (int64_t)(kWstWgs / (H / 256)) * 8 * kWstGT;
+}
+
+template <int H, bool DX, bool MEAN, bool ACC>
+__device__ __forceinline__ void rows_bf16_wst_body(char* smem, const uint16_t* __restrict__ A,
+                                                   const uint16_t* __restrict__ Wm, const float* __restrict__ bias,
+                                                   uint16_t* __restrict__ Out, const int* __restrict__ offsets,
+                                                   const int* __restrict__ perm, int NE, int T, int nh,
+                                                   float inv_nh) {
+    using S = WstSmem<H>;
+    constexpr int NS = H / 256, NKS = H / 16, V = kWstWgs / NS;
+    constexpr int CPR = S::ROWB / 16;       // 16-byte chunks per row
+    constexpr int RPI = kWstThreads / CPR;  // rows per load round
+    constexpr int NL = kWstGT / RPI;        // row loads per thread per group
+    static_assert(kWstWgs % (8 * NS) == 0 && kWstGT % RPI == 0, "shape");
+    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, l32 = lane % 32, h = lane / 32;
+    const int bid = blockIdx.x;
+    const int s = (bid / 8) % NS, v = (bid % 8) + 8 * (bid / (8 * NS));
+    const int n0 = 256 * s, fw = 32 * wave;  // this wavefront's features n0 + fw + 0..31
+    const int P0 = (int)((int64_t)v * T / V), P1 = (int)((int64_t)(v + 1) * T / V);
+    char* const xb0 = smem;
+    char* const xb1 = smem + S::xbuf;
+    float* const ob0 = reinterpret_cast<float*>(smem + S::ost_off);
+    float* const ob1 = reinterpret_cast<float*>(smem + S::ost_off + S::obuf);
+    float* const bias_s = reinterpret_cast<float*>(smem + S::bias_off);
+    // token ids of group g in ids[g % 5]: written at g - 2, read at g - 1 (its rows' loads) and at
+    // g + 1 (its output), so with five buffers no wavefront overwrites ids another still reads
+    int(&ids)[5][kWstGT] = *reinterpret_cast<int(*)[5][kWstGT]>(smem + S::ids_off);
+    int x_lo, x_cnt;
+    expert_range(offsets, NE, T, x_lo, x_cnt);
+    const int lrow = tid / CPR, lch = tid % CPR;
+    // output pieces: thread -> feature chunk pc (8 features) of rows tid / 32 + 16 i
+    const int pc = tid % 32, prow = tid / 32;
+
+    u16x8 wr[NKS];  // features n0 + fw + l32, k 16 ks + 8 h ..
+    u16x8 xr[NL];   // the next group's rows, in flight
+
+    auto load_x = [&](const int* gid) {  // a padded row reads the zero row
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            const int t = gid[lrow + RPI * j];
+            const uint16_t* src =
+                t >= 0 ? A + (size_t)(MEAN ? t / nh : t) * H + 8 * lch : kZeroRow + 8 * lch;
+            xr[j] = ld8(src);
+        }
+    };
+    auto store_x = [&](char* xb) {
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            const int r = lrow + RPI * j;
+            st8(reinterpret_cast<uint16_t*>(xb + r * S::ROWB + 16 * (lch ^ (r & 15))), xr[j]);
+        }
+    };
+    // fp32 result row r (token), 64 chunks of 4 features: chunk c at c ^ (r & 15)
+    auto ost_at = [](float* ob, int r, int c) { return ob + r * 256 + 4 * (c ^ (r & 15)); };
+    auto compute = [&](const char* xb, float* ob) {
+        const char* row = xb + l32 * S::ROWB;
+        f32x16 acc = f32x16{};
+        // fragments in batches of 4 k-steps, each batch read before its MFMAs, so the LDS reads
+        // overlap the MFMA chain instead of each MFMA waiting for its own read
+        constexpr int KB = 4;
+#pragma unroll
+        for (int k0 = 0; k0 < NKS; k0 += KB) {
+            u16x8 xf[KB];
+#pragma unroll
+            for (int u = 0; u < KB; ++u)
+                xf[u] = *reinterpret_cast<const u16x8*>(row + 16 * ((2 * (k0 + u) + h) ^ (l32 & 15)));
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < KB; ++u) {
+                if (MEAN) xf[u] = scale8(xf[u], inv_nh);
+                acc = mfma_bf16(wr[k0 + u], xf[u], acc);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // lane: token l32, features fw + 8 q + 4 h .. + 3
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f32x4 val = {acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+            *reinterpret_cast<f32x4*>(ost_at(ob, l32, (fw >> 2) + 2 * q + h)) = val;
+        }
+    };
+    auto store_out = [&](const float* ob, const int* gid) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int r = prow + 16 * i;
+            const int t = gid[r];
+            u16x8 old;
+            if (ACC) old = ld8(Out + (size_t)(t < 0 ? 0 : t) * H + n0 + 8 * pc);
+            const f32x4 a0 = *reinterpret_cast<const f32x4*>(ost_at(const_cast<float*>(ob), r, 2 * pc));
+            const f32x4 a1 = *reinterpret_cast<const f32x4*>(ost_at(const_cast<float*>(ob), r, 2 * pc + 1));
+            float vv[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+            if (!DX) {
+                const f32x4 b0 = *reinterpret_cast<const f32x4*>(bias_s + 8 * pc);
+                const f32x4 b1 = *reinterpret_cast<const f32x4*>(bias_s + 8 * pc + 4);
+                const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+                for (int u = 0; u < 8; ++u) vv[u] += bv[u];
+            }
+            if (ACC) {
+#pragma unroll
+                for (int u = 0; u < 8; ++u) vv[u] = bf16_to_f32(old[u]) + vv[u];
+            }
+            u32x4v pk;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) pk[u] = pack_bf16x2(vv[2 * u], vv[2 * u + 1]);
+            if (t >= 0) st8(Out + (size_t)t * H + n0 + 8 * pc, __builtin_bit_cast(u16x8, pk));
+        }
+    };
+
+    int p = P0;
+    while (p < P1) {
+        // segment: positions [p, se) of expert e
+        const uint64_t hit = __ballot(lane < NE && p >= x_lo && p < x_lo + x_cnt);
+        if (hit == 0) break;  // (only with routing that does not cover [0, T))
+        const int e = __ffsll((unsigned long long)hit) - 1;
+        const int se = min(P1, __builtin_amdgcn_readlane(x_lo, e) + __builtin_amdgcn_readlane(x_cnt, e));
+        const int G = (se - p + kWstGT - 1) / kWstGT;
+        // this thread's entry of perm in group g, as loaded (an unconditional load of a clamped
+        // position, so no wait sits under a branch; the guard and the validity are applied where
+        // the id is written to LDS, a group later, so nothing waits for the load here)
+        auto group_raw = [&](int g) {
+            const int k = p + kWstGT * g + (tid % kWstGT);
+            return perm[k < se ? k : se - 1];
+        };
+        auto group_valid = [&](int g) { return g < G && p + kWstGT * g + (tid % kWstGT) < se; };
+        __syncthreads();  // the previous segment is done with the bias, ids and staged results
+        if constexpr (!DX) {  // W[e] rows n0 + fw + l32, k contiguous
+            const uint16_t* __restrict__ We = Wm + (size_t)e * H * H + (size_t)(n0 + fw + l32) * H + 8 * h;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) wr[ks] = ld8(We + 16 * ks);
+        } else {
+            // W^T fragments: W[e] rows k (256 at a time) x columns n0 .. n0 + 255 staged in the
+            // group buffers (512-byte rows, chunk c of row r at c ^ 4 (r & 3)), read back with the
+            // transposing LDS read (8 consecutive k of one column per lane)
+            constexpr int WROWS = (2 * S::xbuf + 2 * S::obuf >= 256 * 512) ? 256 : 128;  // rows per stage
+            static_assert(2 * S::xbuf + 2 * S::obuf >= (size_t)WROWS * 512 && H % WROWS == 0, "LDS for a W stage");
+            char* const wst = smem;
+#pragma unroll  // compile-time k0, so the register array wr keeps constant indices
+            for (int k0 = 0; k0 < H; k0 += WROWS) {
+                if (k0 > 0) __syncthreads();  // the previous stage is read
+#pragma unroll 1
+                for (int rb = 0; rb < WROWS; rb += 32) {  // 32 rows per batch: 2 loads per thread
+                    u16x8 wv[2];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const int r = rb + 16 * u + tid / 32;
+                        wv[u] = ld8(Wm + (size_t)e * H * H + (size_t)(k0 + r) * H + n0 + 8 * (tid % 32));
+                    }
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const int r = rb + 16 * u + tid / 32;
+                        st8(reinterpret_cast<uint16_t*>(wst + r * 512 + 16 * ((tid % 32) ^ (4 * (r & 3)))), wv[u]);
+                    }
+                }
+                __syncthreads();
+#pragma unroll
+                for (int ks = 0; ks < WROWS / 16; ++ks) wr[k0 / 16 + ks] = tr_frag_swz(wst, 16 * ks, fw, lane);
+            }
+        }
+        if (!DX && tid < 256) bias_s[tid] = bias[(size_t)e * H + n0 + tid];
+        {
+            const int i0 = group_raw(0), i1 = group_raw(1);
+            if (tid < kWstGT) {
+                ids[0][tid] = group_valid(0) ? guard_token(i0, T) : -1;
+                ids[1][tid] = group_valid(1) ? guard_token(i1, T) : -1;
+            }
+        }
+        int idr = group_raw(2);  // ids in flight: of group g + 2 during group g
+        __syncthreads();
+        load_x(ids[0]);
+        // group g: its rows to LDS (and the ids of g + 2); the output of g - 1 to memory; the rows
+        // of g + 1 and the ids of g + 3 into flight (after the stores: ahead of them, the stores
+        // queue behind the loads and the next wait takes longer); the MFMAs of g
+#pragma unroll 1
+        for (int g = 0; g < G; ++g) {
+            char* const xb = (g & 1) ? xb1 : xb0;
+            store_x(xb);
+            if (tid < kWstGT) ids[(g + 2) % 5][tid] = group_valid(g + 2) ? guard_token(idr, T) : -1;
+            __syncthreads();
+            if (g > 0) store_out((g & 1) ? ob0 : ob1, ids[(g - 1) % 5]);
+            if (g + 1 < G) load_x(ids[(g + 1) % 5]);
+            idr = group_raw(g + 3);
+            compute(xb, (g & 1) ? ob1 : ob0);
+        }
+        __syncthreads();
+        store_out(((G - 1) & 1) ? ob1 : ob0, ids[(G - 1) % 5]);
+        p = se;
+    }
+}
+
+template <int H, bool DX, bool MEAN, bool ACC>
+__global__ __launch_bounds__(kWstThreads) void k_rows_bf16_wst(const uint16_t* __restrict__ A,
+                                                                const uint16_t* __restrict__ Wm,
+                                                                const float* __restrict__ bias,
+                                                                uint16_t* __restrict__ Out,
+                                                                const int* __restrict__ offsets,
+                                                                const int* __restrict__ perm, int NE, int T, int nh,
+                                                                float inv_nh) {
+    __shared__ __attribute__((aligned(16))) char smem[WstSmem<H>::bytes];
+    rows_bf16_wst_body<H, DX, MEAN, ACC>(smem, A, Wm, bias, Out, offsets, perm, NE, T, nh, inv_nh);
+}
+
 // Kernels.  For H <= 128 the backward is one launch: dW / db chunk tiles first, then dX tiles.
 // For H = 256 / 512 the 256 x 256 dW tiles take a whole compute unit each (their registers), so
 // they run as a launch of their own ahead of the dX launch.
@@ -1348,6 +1583,11 @@ template <int H>
 static hipError_t fwd_bf16(const uint16_t* X, const uint16_t* W, const float* bias, uint16_t* Y,
                            const int32_t* offsets, const int32_t* perm, int64_t T, int NE, hipStream_t s) {
     if constexpr (H >= 256) {
+        if (bf16_wst(T, H)) {
+            launch_kernel((k_rows_bf16_wst<H, false, false, false>), dim3(kWstWgs), dim3(kWstThreads), 0, s, X, W,
+                          bias, Y, offsets, perm, NE, (int)T, 1, 1.0f);
+            return hipGetLastError();
+        }
         if (MOE_BF16_WS_FWD && T * H * 2 < ((int64_t)1 << 31)) {
             launch_kernel((k_fwd_bf16_ws<H>), dim3(kWsWgs), dim3(kWsThreads), 0, s, X, W, bias, Y, offsets, perm, NE,
                           (int)T);
@@ -1377,8 +1617,13 @@ static hipError_t bwd_bf16(const uint16_t* dY, const uint16_t* X, const uint16_t
         const ArmedEvents ev = take_armed_events();
         launch_kernel_ev((k_dw_bf16<H, MEAN>), dim3(n_dw), dim3(kDwBigThreads), 0, s, ev.start, nullptr, dY, X, pdw, pdb,
                          offsets, perm, NE, P, (int)T, nh, inv_nh);
-        launch_kernel_ev((k_dx_bf16<H, BN, MEAN, ACC>), dim3(n_dx), dim3(kThreads), 0, s, nullptr, ev.stop, dY, W, dX,
-                         accumulate, offsets, perm, NE, (int)T, nh, inv_nh);
+        if (bf16_wst(T, H)) {
+            launch_kernel_ev((k_rows_bf16_wst<H, true, MEAN, ACC>), dim3(kWstWgs), dim3(kWstThreads), 0, s, nullptr,
+                             ev.stop, dY, W, nullptr, dX, offsets, perm, NE, (int)T, nh, inv_nh);
+        } else {
+            launch_kernel_ev((k_dx_bf16<H, BN, MEAN, ACC>), dim3(n_dx), dim3(kThreads), 0, s, nullptr, ev.stop, dY, W,
+                             dX, accumulate, offsets, perm, NE, (int)T, nh, inv_nh);
+        }
     } else {
         launch_kernel((k_bwd_bf16<H, BN, MEAN, ACC>), dim3(n_dx + n_dw), dim3(kThreads), 0, s, dY, X, W, dX, accumulate,
                       pdw, pdb, offsets, perm, NE, P, (int)T, n_dx, nh, inv_nh);
