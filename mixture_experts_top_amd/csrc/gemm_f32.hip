@@ -1036,6 +1036,187 @@ __global__ __launch_bounds__(kThreads) void k_bwd_f32(const float* __restrict__ 
                                   inv_nh);
 }
 
+// W-stationary row GEMM (H = 256, large T): Out[t, :] = A[t, :] . Wm[n, :]^T (+ bias) for the
+// tokens of one expert.  Each of the 256 workgroups (one per compute unit, eight wavefronts, two
+// per SIMD) holds all of W[e] -- each wavefront 32 features for the whole K in its registers as
+// MFMA operands (128 VGPRs) -- and streams a fixed share of the expert-sorted token order
+// through it in groups of 32 tokens: their rows go to LDS whole (one 1 KB row per load
+// instruction, 16-byte chunk c of row r at c ^ (r & 15)), each wavefront reads its fragments
+// from there, and the results are staged in LDS and written a group later as whole rows.
+// Per group a wavefront issues 128 MFMAs back to back: one barrier per 32 tokens, and no tile
+// epilogue between K slices.  The k order (lane half h of MFMA step j in block m takes
+// k = 8 m + 4 h + j) and the epilogue's additions are those of the tiled kernels, so the results
+// are the same bits.  The forward passes W ([n][k]); dX passes W^T (written by the d_W launch).
+// The token share of workgroup v: positions [v T / 256, (v + 1) T / 256) of the expert-sorted
+// order, cut at expert boundaries into segments; each segment loads its expert's W once.
+#ifndef MOE_F32_WST
+#define MOE_F32_WST 1
+#endif
+constexpr int kF32WstThreads = 512, kF32WstWgs = 256, kF32WstGT = 32;
+struct F32WstSmem {
+    static constexpr int H = 256, ROWB = 4 * H;                   // bytes per token row
+    static constexpr size_t xbuf = (size_t)kF32WstGT * ROWB;      // one group's rows: 32 KB
+    static constexpr size_t obuf = (size_t)kF32WstGT * H * 4;     // one group's results: 32 KB
+    static constexpr size_t ost_off = 2 * xbuf, bias_off = ost_off + 2 * obuf;
+    static constexpr size_t ids_off = bias_off + H * 4;           // token ids: [5][32]
+    static constexpr size_t bytes = ids_off + 5 * kF32WstGT * 4;
+};
+static __device__ __attribute__((aligned(16))) float kZeroRowF[256];  // padded rows read these
+// 256 workgroups when every share holds at least 8 groups of 32 tokens
+static inline bool f32_wst(int64_t T, int H) {
+    return MOE_F32_WST && H == 256 && T >= (int64_t)kF32WstWgs * 8 * kF32WstGT;
+}
+
+template <bool DX, bool MEAN, bool ACC>
+__device__ __forceinline__ void rows_f32_wst_body(char* smem, const float* __restrict__ A,
+                                                  const float* __restrict__ Wm, const float* __restrict__ bias,
+                                                  float* __restrict__ Out, const int* __restrict__ offsets,
+                                                  const int* __restrict__ perm, int NE, int T, int nh,
+                                                  float inv_nh) {
+    using S = F32WstSmem;
+    constexpr int H = S::H, NM = H / 8, GT = kF32WstGT;
+    constexpr int CPR = S::ROWB / 16;        // 16-byte chunks per row: 64
+    constexpr int RPI = kF32WstThreads / CPR;  // rows per load round: 8
+    constexpr int NL = GT / RPI;             // row loads per thread per group: 4
+    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, l32 = lane % 32, h = lane / 32;
+    const int v = blockIdx.x, fw = 32 * wave;
+    const int P0 = (int)((int64_t)v * T / kF32WstWgs), P1 = (int)((int64_t)(v + 1) * T / kF32WstWgs);
+    char* const xb0 = smem;
+    char* const xb1 = smem + S::xbuf;
+    float* const ob0 = reinterpret_cast<float*>(smem + S::ost_off);
+    float* const ob1 = reinterpret_cast<float*>(smem + S::ost_off + S::obuf);
+    float* const bias_s = reinterpret_cast<float*>(smem + S::bias_off);
+    // token ids of group g in ids[g % 5]: written at g - 2, read at g - 1 (its rows' loads) and at
+    // g + 1 (its output), so with five buffers no wavefront overwrites ids another still reads
+    int(&ids)[5][GT] = *reinterpret_cast<int(*)[5][GT]>(smem + S::ids_off);
+    int x_lo, x_cnt;
+    expert_range(offsets, NE, T, x_lo, x_cnt);
+    const int lrow = tid / CPR, lch = tid % CPR;
+
+    f32x4 wr[NM];  // feature fw + l32, k 8 m + 4 h .. + 3
+    f32x4 xr[NL];  // the next group's rows, in flight
+
+    auto load_x = [&](const int* gid) {  // a padded row reads the zero row
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            const int t = gid[lrow + RPI * j];
+            xr[j] = ld4(t >= 0 ? A + (size_t)(MEAN ? t / nh : t) * H + 4 * lch : kZeroRowF + 4 * lch);
+        }
+    };
+    auto store_x = [&](char* xb) {
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            const int r = lrow + RPI * j;
+            st4(reinterpret_cast<float*>(xb + r * S::ROWB + 16 * (lch ^ (r & 15))), xr[j]);
+        }
+    };
+    // fp32 result row r (token), 64 chunks of 4 features: chunk c at c ^ (r & 15)
+    auto ost_at = [](float* ob, int r, int c) { return ob + r * H + 4 * (c ^ (r & 15)); };
+    auto compute = [&](const char* xb, float* ob) {
+        const char* row = xb + l32 * S::ROWB;
+        f32x16 acc = f32x16{};
+        constexpr int MB = 4;  // fragments read 4 blocks of 8 k ahead of their MFMAs
+#pragma unroll
+        for (int m0 = 0; m0 < NM; m0 += MB) {
+            f32x4 xf[MB];
+#pragma unroll
+            for (int u = 0; u < MB; ++u) {
+                xf[u] = *reinterpret_cast<const f32x4*>(row + 16 * ((2 * (m0 + u) + h) ^ (l32 & 15)));
+                if (MEAN) xf[u] *= inv_nh;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < MB; ++u)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc = mfma32(wr[m0 + u][j], xf[u][j], acc);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // lane: token l32, features fw + 8 q + 4 h .. + 3
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f32x4 val = {acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+            *reinterpret_cast<f32x4*>(ost_at(ob, l32, (fw >> 2) + 2 * q + h)) = val;
+        }
+    };
+    // staged results of a group -> rows: thread covers features 4 c .. + 3 of rows tid / 64 + 8 i
+    auto store_out = [&](float* ob, const int* gid) {
+        const int c = tid % 64;
+        f32x4 bq = f32x4{};
+        if (!DX) bq = *reinterpret_cast<const f32x4*>(bias_s + 4 * c);
+#pragma unroll
+        for (int i = 0; i < GT / 8; ++i) {
+            const int r = tid / 64 + 8 * i;
+            const int t = gid[r];
+            f32x4 v = *reinterpret_cast<const f32x4*>(ost_at(ob, r, c));
+            if (!DX) v = v + bq;
+            if (ACC) v = ld4(Out + (size_t)(t < 0 ? 0 : t) * H + 4 * c) + v;
+            if (t >= 0) st4(Out + (size_t)t * H + 4 * c, v);
+        }
+    };
+
+    int p = P0;
+    while (p < P1) {
+        // segment: positions [p, se) of expert e
+        const uint64_t hit = __ballot(lane < NE && p >= x_lo && p < x_lo + x_cnt);
+        if (hit == 0) break;  // (only with routing that does not cover [0, T))
+        const int e = __ffsll((unsigned long long)hit) - 1;
+        const int se = min(P1, __builtin_amdgcn_readlane(x_lo, e) + __builtin_amdgcn_readlane(x_cnt, e));
+        const int G = (se - p + GT - 1) / GT;
+        // this thread's entry of perm in group g, as loaded (unconditional, of a clamped position;
+        // the guard and the validity are applied where the id is written to LDS, a group later)
+        auto group_raw = [&](int g) {
+            const int k = p + GT * g + (tid % GT);
+            return perm[k < se ? k : se - 1];
+        };
+        auto group_valid = [&](int g) { return g < G && p + GT * g + (tid % GT) < se; };
+        __syncthreads();  // the previous segment is done with the bias, ids and staged results
+        {
+            const float* __restrict__ We = Wm + (size_t)e * H * H + (size_t)(fw + l32) * H + 4 * h;
+#pragma unroll
+            for (int m = 0; m < NM; ++m) wr[m] = ld4(We + 8 * m);
+        }
+        if (!DX && tid < H) bias_s[tid] = bias[(size_t)e * H + tid];
+        {
+            const int i0 = group_raw(0), i1 = group_raw(1);
+            if (tid < GT) {
+                ids[0][tid] = group_valid(0) ? guard_token(i0, T) : -1;
+                ids[1][tid] = group_valid(1) ? guard_token(i1, T) : -1;
+            }
+        }
+        int idr = group_raw(2);  // ids in flight: of group g + 2 during group g
+        __syncthreads();
+        load_x(ids[0]);
+        // group g: its rows to LDS (and the ids of g + 2); the output of g - 1 to memory; the rows
+        // of g + 1 and the ids of g + 3 into flight; the MFMAs of g
+#pragma unroll 1
+        for (int g = 0; g < G; ++g) {
+            char* const xb = (g & 1) ? xb1 : xb0;
+            store_x(xb);
+            if (tid < GT) ids[(g + 2) % 5][tid] = group_valid(g + 2) ? guard_token(idr, T) : -1;
+            __syncthreads();
+            if (g > 0) store_out((g & 1) ? ob0 : ob1, ids[(g - 1) % 5]);
+            if (g + 1 < G) load_x(ids[(g + 1) % 5]);
+            idr = group_raw(g + 3);
+            compute(xb, (g & 1) ? ob1 : ob0);
+        }
+        __syncthreads();
+        store_out(((G - 1) & 1) ? ob1 : ob0, ids[(G - 1) % 5]);
+        p = se;
+    }
+}
+
+template <bool DX, bool MEAN, bool ACC>
+__global__ __launch_bounds__(kF32WstThreads) void k_rows_f32_wst(const float* __restrict__ A,
+                                                                  const float* __restrict__ Wm,
+                                                                  const float* __restrict__ bias,
+                                                                  float* __restrict__ Out,
+                                                                  const int* __restrict__ offsets,
+                                                                  const int* __restrict__ perm, int NE, int T,
+                                                                  int nh, float inv_nh) {
+    __shared__ __attribute__((aligned(16))) char smem[F32WstSmem::bytes];
+    rows_f32_wst_body<DX, MEAN, ACC>(smem, A, Wm, bias, Out, offsets, perm, NE, T, nh, inv_nh);
+}
+
 // Large T, H = 256 / 512: the 256 x 256 d_W tiles (eight wavefronts of 128 x 64, one workgroup
 // per compute unit) in a launch of their own, then the dX tiles as a persistent launch.  A
 // 128 x 128 d_W tile re-reads its chunk's dY and X columns once per partner tile; with the
@@ -1179,6 +1360,11 @@ template <int H>
 static hipError_t fwd_f32(const float* X, const float* W, const float* bias, float* Y, const int32_t* offsets,
                           const int32_t* perm, int64_t T, int NE, hipStream_t s) {
     using TL = F32Tiles<H>;
+    if (f32_wst(T, H)) {
+        launch_kernel((k_rows_f32_wst<false, false, false>), dim3(kF32WstWgs), dim3(kF32WstThreads), 0, s, X, W, bias,
+                      Y, offsets, perm, NE, (int)T, 1, 1.0f);
+        return hipGetLastError();
+    }
     if (f32_big_tiles(T, H)) {
         const int ids = rows_grid<H, TL::BIG_BN>(T, NE, 128);
         const int grid = persist_wgs(ids, MOE_FWD_PERSIST_WGS, MOE_FWD_PERSIST_WGS);
@@ -1212,10 +1398,14 @@ static hipError_t bwd_f32(const float* dY, const float* X, const float* W, float
             launch_kernel_ev((k_dw_f32_big<H, MOE_F32_KC_DW, MEAN>), dim3(NE + round_up(n_chunk_max, 8) * TPC),
                              dim3(kDwBigThreads), 0, s, ev.start, nullptr, dY, X, W, wt, pdw, pdb, offsets, perm, NE,
                              P, (int)T, nh, inv_nh);
-            launch_kernel_ev((k_dx_f32<H, TL::BIG_BN, MOE_F32_KC_FWD, MEAN, ACC>),
-                             dim3(persist_wgs(dx_ids, MOE_DX_BIG_PERSIST_WGS, MOE_DX_BIG_PERSIST_WGS)), dim3(kThreads),
-                             0, s, nullptr, ev.stop, dY, wt, dX, accumulate, offsets, perm, NE, (int)T, dx_ids, nh,
-                             inv_nh);
+            if (f32_wst(T, H))
+                launch_kernel_ev((k_rows_f32_wst<true, MEAN, ACC>), dim3(kF32WstWgs), dim3(kF32WstThreads), 0, s,
+                                 nullptr, ev.stop, dY, wt, nullptr, dX, offsets, perm, NE, (int)T, nh, inv_nh);
+            else
+                launch_kernel_ev((k_dx_f32<H, TL::BIG_BN, MOE_F32_KC_FWD, MEAN, ACC>),
+                                 dim3(persist_wgs(dx_ids, MOE_DX_BIG_PERSIST_WGS, MOE_DX_BIG_PERSIST_WGS)),
+                                 dim3(kThreads), 0, s, nullptr, ev.stop, dY, wt, dX, accumulate, offsets, perm, NE,
+                                 (int)T, dx_ids, nh, inv_nh);
             return hipGetLastError();
         }
     }

@@ -142,8 +142,9 @@ def test_route_entry_point_matches_fwd_routing(gpu_lib):
 
 
 @pytest.mark.parametrize("wl", [workloads.custom(70, 5, 128, 4), workloads.custom(9000, 5, 256, 6),
-                                workloads.custom(14000, 5, 128, 8)],
-                         ids=["small_T", "big_dw_tiles_H256", "large_T_H128"])
+                                workloads.custom(14000, 5, 128, 8),
+                                pytest.param(workloads.custom(14000, 5, 256, 6), marks=pytest.mark.slow)],
+                         ids=["small_T", "big_dw_tiles_H256", "large_T_H128", "w_stationary_H256"])
 def test_accumulate_dx(gpu_lib, wl):
     import torch
     from tests import gpu_run
