@@ -48,6 +48,9 @@ __device__ __forceinline__ f32x16 mfma32(float a, float b, f32x16 c) {
 
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 __device__ __forceinline__ void st4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+// Non-temporal store (the write does not allocate in the cache hierarchy as reusable data):
+// for outputs no workgroup of the same launch reads back.
+__device__ __forceinline__ void st4_nt(float* p, f32x4 v) { __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p)); }
 
 // Workgroup ids are dealt to the 8 XCDs round-robin.  The `per` tiles that share one
 // operand block get ids id, id+8, id+16, ... so they land on the same XCD (same L2).
@@ -696,7 +699,10 @@ __device__ __forceinline__ void rows_f32_onepass_body(char* smem, int bid, const
         // Epilogue through LDS: the tile goes to a row-major staging area (over the K-slice
         // buffers), then each output row is written as whole 16-byte segments -- a quarter of
         // the store instructions of storing the accumulator blocks directly, and every row
-        // segment in one piece.  Same additions in the same order as store_block.
+        // segment in one piece.  Same additions in the same order as store_block.  The rows go
+        // out as non-temporal stores (pages-shape step 42.7 -> 41.4 us: the forward and the
+        // backward each ~0.6 us shorter; storing the d_W partials that way as well made the
+        // imbalanced-shape backward 1.7 us slower, their reduce reads them back).
         float(&St)[BM][BN + kPadKN] = *reinterpret_cast<float(*)[BM][BN + kPadKN]>(smem);
         __syncthreads();  // every wavefront has read its last K slice
 #pragma unroll
@@ -724,11 +730,11 @@ __device__ __forceinline__ void rows_f32_onepass_body(char* smem, int bid, const
             for (int q = 0; q < NP; ++q) old[q] = ld4(Out + (size_t)(tk[q] < 0 ? 0 : tk[q]) * H + n0 + 4 * c4);
 #pragma unroll
             for (int q = 0; q < NP; ++q)
-                if (tk[q] >= 0) st4(Out + (size_t)tk[q] * H + n0 + 4 * c4, old[q] + v[q]);
+                if (tk[q] >= 0) st4_nt(Out + (size_t)tk[q] * H + n0 + 4 * c4, old[q] + v[q]);
         } else {
 #pragma unroll
             for (int q = 0; q < NP; ++q)
-                if (tk[q] >= 0) st4(Out + (size_t)tk[q] * H + n0 + 4 * c4, v[q]);
+                if (tk[q] >= 0) st4_nt(Out + (size_t)tk[q] * H + n0 + 4 * c4, v[q]);
         }
     } else {
 #pragma unroll
@@ -757,10 +763,14 @@ struct DwF32Smem {
 };
 
 #ifndef MOE_DW_PF
-#define MOE_DW_PF 2  // K slices of rows in flight per dW workgroup (even)
+#define MOE_DW_PF 2  // K slices of rows in flight per workgroup of the 256 x 256 dW tiles (even)
+#endif
+#ifndef MOE_DW_RING_F4
+#define MOE_DW_RING_F4 4  // float4 registers of rows in flight per thread in the smaller dW tiles
 #endif
 // NTH threads: 256 (wavefronts 2 x 2 over the tile) or 512 (2 x 4, for 256 x 256 tiles).
-template <int H, int BT, int KC, bool MEAN = false, int NTH = kThreads>
+// PFX: K slices in flight (0: as many as MOE_DW_RING_F4 registers hold, even, at least 2).
+template <int H, int BT, int KC, bool MEAN = false, int NTH = kThreads, int PFX = 0>
 __device__ __forceinline__ void dw_f32_body(char* smem, int bid, const float* __restrict__ dY,
                                                       const float* __restrict__ X,
                                                       float* __restrict__ part_dw,
@@ -773,7 +783,8 @@ __device__ __forceinline__ void dw_f32_body(char* smem, int bid, const float* __
     constexpr int WTM = BT / 2, WTN = BT / WN_W, SUBM = WTM / 32, SUBN = WTN / 32;
     constexpr int Q = BT / 4;                  // float4 per row segment
     constexpr int LD = KC * Q / NTH;      // float4 loads per thread per tensor per slice
-    constexpr int PF = MOE_DW_PF;
+    constexpr int PF0 = PFX > 0 ? PFX : MOE_DW_RING_F4 / (2 * LD);
+    constexpr int PF = PF0 < 2 ? 2 : PF0 - PF0 % 2;
     float(&As)[2][KC][BT + kPadKN] = *reinterpret_cast<float(*)[2][KC][BT + kPadKN]>(smem);  // dY rows, o0..o0+BT
     float(&Bs)[2][KC][BT + kPadKN] =
         *reinterpret_cast<float(*)[2][KC][BT + kPadKN]>(smem + DwF32Smem<BT, KC>::a);      // X rows, i0..i0+BT
@@ -796,26 +807,31 @@ __device__ __forceinline__ void dw_f32_body(char* smem, int bid, const float* __
         for (int j = 0; j < SUBN; ++j) acc[i][j] = f32x16{};
     float dbacc = 0.0f;
 
-    // Two register rings, slot k % PF for slice k: the rows of slices s+1 .. s+PF and the
-    // token ids of slices s+PF+1 .. s+2PF are in flight while slice s computes, so neither
-    // the gather nor its index loads wait on memory.  Loads past the chunk's end read its
-    // last token and are zeroed when stored to LDS, so no load sits in a branch and no
-    // result is touched before its slice is due (either would drain the ring).
-    int tk[PF][LD];
+    // Two register rings: the rows of slices s+1 .. s+PF (slot k % PF for slice k) and the
+    // token ids of slices s+1 .. s+2PF (slot k % 2PF) are in flight while slice s computes,
+    // so neither the gather nor its index loads wait on memory; every id of the first 2PF
+    // slices goes out before the first rows, so the start costs two round trips, not three.
+    // Loads past the chunk's end read its last token and are zeroed when stored to LDS, so no
+    // load sits in a branch; token ids stay raw in the ring and are guarded where the rows
+    // are addressed; the ring loop has no exit inside a cycle.  Each of these, otherwise,
+    // makes the compiler wait for every load in flight at the loop's back edge.  (Rings of 4
+    // and 8 slices measured no faster at the pages' shape: there every workgroup's first
+    // loads arrive as one burst bound by memory bandwidth, and the MFMAs bound the rest.)
+    int tk[2 * PF][LD];
     f32x4 ra[PF][LD], rb[PF][LD];
     auto kpos = [&](int sl, int i) { return t0 + sl * KC + (tid + NTH * i) / Q; };
     auto load_ids = [&](int sl, int slot) {
 #pragma unroll
         for (int i = 0; i < LD; ++i) {
             const int k = kpos(sl, i);
-            tk[slot][i] = load_token(perm, k < t1 ? k : t1 - 1, T);
+            tk[slot][i] = perm[k < t1 ? k : t1 - 1];
         }
     };
-    auto load_rows = [&](int sl, int slot) {  // ids of slice sl are in tk[slot]; rows go to slot
+    auto load_rows = [&](int slot, int islot) {  // ids in tk[islot]; rows go to slot
 #pragma unroll
         for (int i = 0; i < LD; ++i) {
             const int cc = 4 * ((tid + NTH * i) % Q);
-            const size_t t = (size_t)tk[slot][i];
+            const size_t t = (size_t)guard_token(tk[islot][i], T);
             ra[slot][i] = ld4(dY + (MEAN ? t / nh : t) * H + o0 + cc);
             rb[slot][i] = ld4(X + t * H + i0 + cc);
         }
@@ -834,56 +850,53 @@ __device__ __forceinline__ void dw_f32_body(char* smem, int bid, const float* __
 
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int k = 0; k < PF; ++k) load_ids(k, k);
+    for (int k = 0; k < 2 * PF; ++k) load_ids(k, k);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < PF; ++k) load_rows(k, k);
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int k = 0; k < PF; ++k) load_ids(PF + k, k);
-    __builtin_amdgcn_sched_barrier(0);
     store_rows(0, 0, 0);
-    load_rows(PF, 0);
-    load_ids(2 * PF, 0);
+    load_rows(0, PF);        // slice PF
+    load_ids(2 * PF, 0);     // slice 2PF, over slice 0's ids
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     static_assert(PF % 2 == 0, "the LDS buffer of slice s0 + u is u % 2");
-#pragma unroll 1
-    for (int s0 = 0; s0 < nslices; s0 += PF) {
+    int s0 = 0;
+    do {  // whole cycles of 2PF slices; slices past the chunk's end load (clamped), do not compute
 #pragma unroll
-        for (int u = 0; u < PF; ++u) {
+        for (int u = 0; u < 2 * PF; ++u) {
             const int sl = s0 + u;
-            if (sl >= nslices) break;
-            // unconditional, also past the chunk's end (masked rows, clamped ids): a load under
-            // a branch makes the wait counts at the next slice conservative
             store_rows(sl + 1, (u + 1) % PF, (u + 1) & 1);
-            load_rows(sl + 1 + PF, (u + 1) % PF);
-            load_ids(sl + 1 + 2 * PF, (u + 1) % PF);
+            load_rows((u + 1) % PF, (u + 1 + PF) % (2 * PF));  // slice sl + 1 + PF
+            load_ids(sl + 1 + 2 * PF, (u + 1) % (2 * PF));
             __builtin_amdgcn_sched_barrier(0);
-            const int buf = u & 1;
+            if (sl < nslices) {  // uniform; LDS reads and MFMAs only
+                const int buf = u & 1;
 #pragma unroll
-            for (int kk = 0; kk < KC; kk += 8) {
+                for (int kk = 0; kk < KC; kk += 8) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int k = kk + 4 * h + q;
-                    float a[SUBM], b[SUBN];
+                    for (int q = 0; q < 4; ++q) {
+                        const int k = kk + 4 * h + q;
+                        float a[SUBM], b[SUBN];
 #pragma unroll
-                    for (int i = 0; i < SUBM; ++i) a[i] = As[buf][k][wm * WTM + i * 32 + l32];
+                        for (int i = 0; i < SUBM; ++i) a[i] = As[buf][k][wm * WTM + i * 32 + l32];
 #pragma unroll
-                    for (int j = 0; j < SUBN; ++j) b[j] = Bs[buf][k][wn * WTN + j * 32 + l32];
+                        for (int j = 0; j < SUBN; ++j) b[j] = Bs[buf][k][wn * WTN + j * 32 + l32];
 #pragma unroll
-                    for (int i = 0; i < SUBM; ++i)
+                        for (int i = 0; i < SUBM; ++i)
 #pragma unroll
-                        for (int j = 0; j < SUBN; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+                            for (int j = 0; j < SUBN; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+                    }
                 }
-            }
-            if (do_db && tid < BT) {
+                if (do_db && tid < BT) {
 #pragma unroll
-                for (int k = 0; k < KC; ++k) dbacc += As[buf][k][tid];
+                    for (int k = 0; k < KC; ++k) dbacc += As[buf][k][tid];
+                }
             }
             __syncthreads();
         }
-    }
+        s0 += 2 * PF;
+    } while (s0 < nslices);
 
     float* __restrict__ Pd = part_dw + (size_t)c * H * H;
 #pragma unroll
@@ -1003,8 +1016,11 @@ __global__ __launch_bounds__(kThreads) void k_fwd_f32_gather(const float* __rest
 
 // ACC: dX is added to the existing contents (a compile-time choice: with a run-time flag the
 // epilogue carries the load-then-store path and the waits it needs even when it is not taken).
+// The one-pass grids (small T) are sized so that every workgroup is resident at once with four
+// wavefronts per SIMD; the attribute keeps the register count there (at H = 512 it would spill).
 template <int H, int BM, int BN, int BT, int KCX, int KCW, bool MEAN, bool ONE, bool DWF = false, bool ACC = false>
-__global__ __launch_bounds__(kThreads) void k_bwd_f32(const float* __restrict__ dY, const float* __restrict__ X,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ONE && H <= 256 ? 4 : 1)))
+void k_bwd_f32(const float* __restrict__ dY, const float* __restrict__ X,
                                                        const float* __restrict__ W, float* __restrict__ dX,
                                                        int accumulate, float* __restrict__ part_dw,
                                                        float* __restrict__ part_db,
@@ -1271,7 +1287,7 @@ __global__ __launch_bounds__(kDwBigThreads) void k_dw_f32_big(const float* __res
         transpose_w_body<H>(smem, blockIdx.x, W, Wt);
         return;
     }
-    dw_f32_body<H, 256, KCW, MEAN, kDwBigThreads>(smem, (int)blockIdx.x - NE, dY, X, part_dw, part_db, offsets, perm,
+    dw_f32_body<H, 256, KCW, MEAN, kDwBigThreads, MOE_DW_PF>(smem, (int)blockIdx.x - NE, dY, X, part_dw, part_db, offsets, perm,
                                                   NE, P, T, nh, inv_nh);
 }
 
