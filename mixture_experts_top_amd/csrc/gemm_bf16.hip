@@ -58,6 +58,9 @@ __device__ __forceinline__ u16x8 scale8(u16x8 v, float f) {
     return o;
 }
 __device__ __forceinline__ void st8(uint16_t* p, u16x8 v) { *reinterpret_cast<u16x8*>(p) = v; }
+// Non-temporal store, for the GEMM outputs, which no workgroup of the same launch reads back
+// (wider-bf16 step 373.5 -> 364 us against plain stores).
+__device__ __forceinline__ void st8_nt(uint16_t* p, u16x8 v) { __builtin_nontemporal_store(v, reinterpret_cast<u16x8*>(p)); }
 
 __device__ __forceinline__ void xcd_split(int bid, int per, int& major, int& minor) {
     const int grp = bid / (8 * per), loc = bid % (8 * per);
@@ -295,7 +298,7 @@ __device__ __forceinline__ void rows_bf16_body(char* smem, int bid, const uint16
                 const float b = acc_dx ? bf16_to_f32(old[q][2 * u + 1]) + v[2 * u + 1] : v[2 * u + 1];
                 pk[u] = pack_bf16x2(a, b);
             }
-            if (tk[q] >= 0) st8(Out + (size_t)tk[q] * H + n0 + 8 * c8, __builtin_bit_cast(u16x8, pk));
+            if (tk[q] >= 0) st8_nt(Out + (size_t)tk[q] * H + n0 + 8 * c8, __builtin_bit_cast(u16x8, pk));
         }
         return;
     }
@@ -1390,7 +1393,7 @@ __device__ __forceinline__ void rows_bf16_wst_body(char* smem, const uint16_t* _
             u32x4v pk;
 #pragma unroll
             for (int u = 0; u < 4; ++u) pk[u] = pack_bf16x2(vv[2 * u], vv[2 * u + 1]);
-            if (t >= 0) st8(Out + (size_t)t * H + n0 + 8 * pc, __builtin_bit_cast(u16x8, pk));
+            if (t >= 0) st8_nt(Out + (size_t)t * H + n0 + 8 * pc, __builtin_bit_cast(u16x8, pk));
         }
     };
 

@@ -48,9 +48,13 @@ __device__ __forceinline__ f32x16 mfma32(float a, float b, f32x16 c) {
 
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 __device__ __forceinline__ void st4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
-// Non-temporal store (the write does not allocate in the cache hierarchy as reusable data):
-// for outputs no workgroup of the same launch reads back.
+// Non-temporal stores (the write does not allocate in the cache hierarchy as reusable data),
+// for the GEMM outputs, which no workgroup of the same launch reads back.  Measured against
+// plain stores: pages-shape step 42.7 -> 41.4 us, imbalanced 117.8 -> 115.4 us, large stress
+// 3418 -> 3409 us.  Not for the d_W partials, which the reduce reads back next (the
+// imbalanced-shape backward was 1.7 us slower).
 __device__ __forceinline__ void st4_nt(float* p, f32x4 v) { __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p)); }
+__device__ __forceinline__ void st1_nt(float* p, float v) { __builtin_nontemporal_store(v, p); }
 
 // Workgroup ids are dealt to the 8 XCDs round-robin.  The `per` tiles that share one
 // operand block get ids id, id+8, id+16, ... so they land on the same XCD (same L2).
@@ -97,13 +101,13 @@ __device__ __forceinline__ void store_block(float* __restrict__ Out, int H, int 
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u)
-                if (tk[u] >= 0) Out[(size_t)tk[u] * H + col] = old[u] + (a[4 * q + u] + bv);
+                if (tk[u] >= 0) st1_nt(&Out[(size_t)tk[u] * H + col], old[u] + (a[4 * q + u] + bv));
         }
     } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int t = tok_of(r);
-            if (t >= 0) Out[(size_t)t * H + col] = a[r] + bv;
+            if (t >= 0) st1_nt(&Out[(size_t)t * H + col], a[r] + bv);
         }
     }
 }
@@ -120,12 +124,12 @@ __device__ __forceinline__ void store_block_ids(float* __restrict__ Out, int H, 
             for (int u = 0; u < 4; ++u) old[u] = Out[(size_t)(tk[4 * q + u] < 0 ? 0 : tk[4 * q + u]) * H + col];
 #pragma unroll
             for (int u = 0; u < 4; ++u)
-                if (tk[4 * q + u] >= 0) Out[(size_t)tk[4 * q + u] * H + col] = old[u] + (a[4 * q + u] + bv);
+                if (tk[4 * q + u] >= 0) st1_nt(&Out[(size_t)tk[4 * q + u] * H + col], old[u] + (a[4 * q + u] + bv));
         }
     } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-            if (tk[r] >= 0) Out[(size_t)tk[r] * H + col] = a[r] + bv;
+            if (tk[r] >= 0) st1_nt(&Out[(size_t)tk[r] * H + col], a[r] + bv);
     }
 }
 
@@ -699,10 +703,7 @@ __device__ __forceinline__ void rows_f32_onepass_body(char* smem, int bid, const
         // Epilogue through LDS: the tile goes to a row-major staging area (over the K-slice
         // buffers), then each output row is written as whole 16-byte segments -- a quarter of
         // the store instructions of storing the accumulator blocks directly, and every row
-        // segment in one piece.  Same additions in the same order as store_block.  The rows go
-        // out as non-temporal stores (pages-shape step 42.7 -> 41.4 us: the forward and the
-        // backward each ~0.6 us shorter; storing the d_W partials that way as well made the
-        // imbalanced-shape backward 1.7 us slower, their reduce reads them back).
+        // segment in one piece.  Same additions in the same order as store_block.
         float(&St)[BM][BN + kPadKN] = *reinterpret_cast<float(*)[BM][BN + kPadKN]>(smem);
         __syncthreads();  // every wavefront has read its last K slice
 #pragma unroll
@@ -1166,7 +1167,7 @@ __device__ __forceinline__ void rows_f32_wst_body(char* smem, const float* __res
             f32x4 v = *reinterpret_cast<const f32x4*>(ost_at(ob, r, c));
             if (!DX) v = v + bq;
             if (ACC) v = ld4(Out + (size_t)(t < 0 ? 0 : t) * H + 4 * c) + v;
-            if (t >= 0) st4(Out + (size_t)t * H + 4 * c, v);
+            if (t >= 0) st4_nt(Out + (size_t)t * H + 4 * c, v);
         }
     };
 
