@@ -4,6 +4,10 @@
 //
 // One thread per (b, 16-byte column group): the forward sums the N_H rows of its column in
 // horizon order, so accesses are coalesced along H and the result is deterministic.
+// Streams touched once go through non-temporal accesses (no reusable cache lines): measured at
+// B = 131,072, N_H = 8, H = 256 fp32, the forward with non-temporal loads and stores 5.40 ->
+// 6.19 TB/s, the backward with non-temporal stores 5.25 -> 6.18 TB/s (its reads of d_out as
+// non-temporal loads: 4.92 TB/s, slower).
 #include "moe_internal.hpp"
 
 namespace moe {
@@ -27,8 +31,8 @@ __global__ __launch_bounds__(256) void k_collapse_fwd_f32(const float* __restric
     const int64_t b = i / q, c = (i % q) * 4;
     const float inv = 1.0f / (float)NH;
     f32x4 s = f32x4{};
-    for (int h = 0; h < NH; ++h) s += *reinterpret_cast<const f32x4*>(x + (b * NH + h) * H + c);
-    *reinterpret_cast<f32x4*>(out + b * H + c) = s * inv;
+    for (int h = 0; h < NH; ++h) s += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(x + (b * NH + h) * H + c));
+    __builtin_nontemporal_store(s * inv, reinterpret_cast<f32x4*>(out + b * H + c));
 }
 
 // One thread per (b, 16-byte column group): d_out[b] is read once and written to the N_H rows.
@@ -40,7 +44,7 @@ __global__ __launch_bounds__(256) void k_collapse_bwd_f32(const float* __restric
     const int64_t b = i / q, c = (i % q) * 4;
     const float inv = 1.0f / (float)NH;
     const f32x4 v = *reinterpret_cast<const f32x4*>(dout + b * H + c) * inv;
-    for (int h = 0; h < NH; ++h) *reinterpret_cast<f32x4*>(dx + (b * NH + h) * H + c) = v;
+    for (int h = 0; h < NH; ++h) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dx + (b * NH + h) * H + c));
 }
 
 __global__ __launch_bounds__(256) void k_collapse_fwd_bf16(const uint16_t* __restrict__ x, uint16_t* __restrict__ out,
@@ -52,14 +56,14 @@ __global__ __launch_bounds__(256) void k_collapse_fwd_bf16(const uint16_t* __res
     const float inv = 1.0f / (float)NH;
     float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int h = 0; h < NH; ++h) {
-        const u16x8 v = *reinterpret_cast<const u16x8*>(x + (b * NH + h) * H + c);
+        const u16x8 v = __builtin_nontemporal_load(reinterpret_cast<const u16x8*>(x + (b * NH + h) * H + c));
 #pragma unroll
         for (int j = 0; j < 8; ++j) s[j] += bf(v[j]);
     }
     u16x8 o;
 #pragma unroll
     for (int j = 0; j < 8; ++j) o[j] = to_bf(s[j] * inv);
-    *reinterpret_cast<u16x8*>(out + b * H + c) = o;
+    __builtin_nontemporal_store(o, reinterpret_cast<u16x8*>(out + b * H + c));
 }
 
 __global__ __launch_bounds__(256) void k_collapse_bwd_bf16(const uint16_t* __restrict__ dout, uint16_t* __restrict__ dx,
@@ -73,7 +77,7 @@ __global__ __launch_bounds__(256) void k_collapse_bwd_bf16(const uint16_t* __res
     u16x8 o;
 #pragma unroll
     for (int j = 0; j < 8; ++j) o[j] = to_bf(bf(v[j]) * inv);
-    for (int h = 0; h < NH; ++h) *reinterpret_cast<u16x8*>(dx + (b * NH + h) * H + c) = o;
+    for (int h = 0; h < NH; ++h) __builtin_nontemporal_store(o, reinterpret_cast<u16x8*>(dx + (b * NH + h) * H + c));
 }
 
 hipError_t launch_collapse(bool bwd, int act, const void* in, void* out, int64_t B, int NH, int H, hipStream_t s) {

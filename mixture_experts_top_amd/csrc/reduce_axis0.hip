@@ -35,7 +35,8 @@ __global__ __launch_bounds__(256) void k_reduce_axis0(const float* __restrict__ 
         f32x4 s = f32x4{};
         if (ok) {
 #pragma unroll 8
-            for (int64_t r = r0 + ty; r < r1; r += 4) s += ld4(in + r * n_tail + col);
+            for (int64_t r = r0 + ty; r < r1; r += 4)  // read once: non-temporal (6.25 -> 6.93 TB/s)
+                s += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(in + r * n_tail + col));
         }
         st4(&red[ty][4 * tx], s);
         __syncthreads();
