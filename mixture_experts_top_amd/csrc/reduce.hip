@@ -75,6 +75,60 @@ __global__ __launch_bounds__(256) void k_reduce_dw(const float* __restrict__ pdw
     }
 }
 
+// Few chunks per expert: one thread per column owns four float4 columns (tid + 256 j, so each
+// load instruction reads 1 KB of one row) and sums every chunk of them in chunk order, NB
+// chunks per batch with all of a batch's loads unconditional (clamped chunk index), so 4 NB
+// loads per thread are in flight at once.  grid (H*H/(16*256) + 1, N_E); the last x does db.
+template <int NB>
+__global__ __launch_bounds__(256) void k_reduce_dw_wide(const float* __restrict__ pdw,
+                                                        const float* __restrict__ pdb,
+                                                        const int* __restrict__ offsets, int H, int NE,
+                                                        int P, int T, float* __restrict__ dW,
+                                                        float* __restrict__ db) {
+    constexpr int CPT = 4;
+    const int e = blockIdx.y;
+    int lo, cnt;
+    expert_range(offsets, NE, T, lo, cnt);
+    const int nl = expert_nchunks(cnt, P, T);
+    const int incl = wave_inclusive_sum(nl);
+    const int cs = __shfl(incl - nl, e), n = __shfl(nl, e);
+    const size_t HH = (size_t)H * H;
+    const int nbx = (int)(HH / (4 * 256 * CPT));
+    const bool isdb = (int)blockIdx.x >= nbx;
+    const float* __restrict__ in = isdb ? pdb : pdw;
+    const size_t len = isdb ? (size_t)H : HH;
+    float* __restrict__ out = isdb ? db + (size_t)e * H : dW + (size_t)e * HH;
+    const size_t c0 = isdb ? 0 : (size_t)blockIdx.x * 4 * 256 * CPT;
+    size_t col[CPT];
+    bool ok[CPT];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+        col[j] = c0 + 4 * ((size_t)threadIdx.x + 256 * j);
+        ok[j] = col[j] < len;
+        if (!ok[j]) col[j] = 0;
+    }
+    f32x4 s[CPT];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) s[j] = f32x4{};
+    for (int b0 = 0; b0 < n; b0 += NB) {
+        f32x4 v[NB][CPT];
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            const float* row = in + (size_t)(cs + (b0 + u < n ? b0 + u : n - 1)) * len;
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) v[u][j] = ld4(row + col[j]);
+        }
+#pragma unroll
+        for (int u = 0; u < NB; ++u)
+            if (b0 + u < n)
+#pragma unroll
+                for (int j = 0; j < CPT; ++j) s[j] += v[u][j];
+    }
+#pragma unroll
+    for (int j = 0; j < CPT; ++j)
+        if (ok[j]) st4(out + col[j], s[j]);
+}
+
 // Rows of threads per column tile: 16 (narrow tiles, more loads in flight per column) once
 // the plan has at least this many chunks, else 4.
 #ifndef MOE_REDUCE_RY16_MIN_P
@@ -91,12 +145,22 @@ __global__ __launch_bounds__(256) void k_reduce_dw(const float* __restrict__ pdw
 #ifndef MOE_REDUCE_RYLOW
 #define MOE_REDUCE_RYLOW 2
 #endif
+#ifndef MOE_REDUCE_WIDE
+#define MOE_REDUCE_WIDE 1
+#endif
+#ifndef MOE_REDUCE_WIDE_MAX_CPE
+#define MOE_REDUCE_WIDE_MAX_CPE 8
+#endif
 #ifndef MOE_REDUCE_RY8_MIN_CPE
 #define MOE_REDUCE_RY8_MIN_CPE 16
 #endif
 hipError_t launch_reduce_dw(const float* part_dw, const float* part_db, const int32_t* offsets, int64_t T, int H,
                             int NE, int P, float* dW, float* db, hipStream_t s) {
-    if (P / NE < MOE_REDUCE_RYLOW_MAX_CPE) {
+    if (MOE_REDUCE_WIDE && P / NE < MOE_REDUCE_WIDE_MAX_CPE && (H * H) % (16 * 256) == 0) {
+        const int nbx = H * H / (16 * 256);
+        launch_kernel(k_reduce_dw_wide<4>, dim3(nbx + 1, NE), dim3(256), 0, s, part_dw, part_db, offsets, H, NE, P,
+                      (int)T, dW, db);
+    } else if (P / NE < MOE_REDUCE_RYLOW_MAX_CPE) {
         constexpr int RY = MOE_REDUCE_RYLOW;
         const int nbx = H * H / (4 * (256 / RY));
         launch_kernel(k_reduce_dw<RY>, dim3(nbx + 1, NE), dim3(256), 0, s, part_dw, part_db, offsets, H, NE, P,
