@@ -1129,7 +1129,9 @@ __device__ __forceinline__ void rows_f32_wst_body(char* smem, const float* __res
     };
     // fp32 result row r (token), 64 chunks of 4 features: chunk c at c ^ (r & 15)
     auto ost_at = [](float* ob, int r, int c) { return ob + r * H + 4 * (c ^ (r & 15)); };
-    auto compute = [&](const char* xb, float* ob) {
+    // mid(b) runs after the b-th batch of MFMAs has been issued (the previous group's output
+    // rows, one per batch, so their stores overlap the MFMA chain)
+    auto compute = [&](const char* xb, float* ob, auto&& mid) {
         const char* row = xb + l32 * S::ROWB;
         f32x16 acc = f32x16{};
         constexpr int MB = 4;  // fragments read 4 blocks of 8 k ahead of their MFMAs
@@ -1147,6 +1149,8 @@ __device__ __forceinline__ void rows_f32_wst_body(char* smem, const float* __res
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc = mfma32(wr[m0 + u][j], xf[u][j], acc);
             __builtin_amdgcn_sched_barrier(0);
+            mid(m0 / MB);
+            __builtin_amdgcn_sched_barrier(0);
         }
         // lane: token l32, features fw + 8 q + 4 h .. + 3
 #pragma unroll
@@ -1156,19 +1160,20 @@ __device__ __forceinline__ void rows_f32_wst_body(char* smem, const float* __res
         }
     };
     // staged results of a group -> rows: thread covers features 4 c .. + 3 of rows tid / 64 + 8 i
-    auto store_out = [&](float* ob, const int* gid) {
+    auto store_row = [&](float* ob, const int* gid, int i) {
         const int c = tid % 64;
         f32x4 bq = f32x4{};
         if (!DX) bq = *reinterpret_cast<const f32x4*>(bias_s + 4 * c);
+        const int r = tid / 64 + 8 * i;
+        const int t = gid[r];
+        f32x4 v = *reinterpret_cast<const f32x4*>(ost_at(ob, r, c));
+        if (!DX) v = v + bq;
+        if (ACC) v = ld4(Out + (size_t)(t < 0 ? 0 : t) * H + 4 * c) + v;
+        if (t >= 0) st4_nt(Out + (size_t)t * H + 4 * c, v);
+    };
+    auto store_out = [&](float* ob, const int* gid) {
 #pragma unroll
-        for (int i = 0; i < GT / 8; ++i) {
-            const int r = tid / 64 + 8 * i;
-            const int t = gid[r];
-            f32x4 v = *reinterpret_cast<const f32x4*>(ost_at(ob, r, c));
-            if (!DX) v = v + bq;
-            if (ACC) v = ld4(Out + (size_t)(t < 0 ? 0 : t) * H + 4 * c) + v;
-            if (t >= 0) st4_nt(Out + (size_t)t * H + 4 * c, v);
-        }
+        for (int i = 0; i < GT / 8; ++i) store_row(ob, gid, i);
     };
 
     int p = P0;
@@ -1203,18 +1208,23 @@ __device__ __forceinline__ void rows_f32_wst_body(char* smem, const float* __res
         int idr = group_raw(2);  // ids in flight: of group g + 2 during group g
         __syncthreads();
         load_x(ids[0]);
-        // group g: its rows to LDS (and the ids of g + 2); the output of g - 1 to memory; the rows
-        // of g + 1 and the ids of g + 3 into flight; the MFMAs of g
+        // group g: its rows to LDS (and the ids of g + 2); the rows of g + 1 and the ids of g + 3
+        // into flight; the MFMAs of g, with the output of g - 1 to memory between them
 #pragma unroll 1
         for (int g = 0; g < G; ++g) {
             char* const xb = (g & 1) ? xb1 : xb0;
             store_x(xb);
             if (tid < GT) ids[(g + 2) % 5][tid] = group_valid(g + 2) ? guard_token(idr, T) : -1;
             __syncthreads();
-            if (g > 0) store_out((g & 1) ? ob0 : ob1, ids[(g - 1) % 5]);
             if (g + 1 < G) load_x(ids[(g + 1) % 5]);
             idr = group_raw(g + 3);
-            compute(xb, (g & 1) ? ob1 : ob0);
+            // the output of group g - 1 (none before group 0), one row per thread after each of
+            // the first MFMA batches of group g, so its stores overlap the MFMA chain
+            float* const obp = (g & 1) ? ob0 : ob1;
+            const int* const gidp = ids[(g + 4) % 5];
+            compute(xb, (g & 1) ? ob1 : ob0, [&](int b) {
+                if (b < GT / 8 && g > 0) store_row(obp, gidp, b);
+            });
         }
         __syncthreads();
         store_out(((G - 1) & 1) ? ob1 : ob0, ids[(G - 1) % 5]);
