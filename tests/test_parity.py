@@ -87,9 +87,10 @@ SMALL = {
     "bf16_H256_NE16_int_ties": workloads.custom(333, 7, 256, 16, act="bf16", gate="int"),
     "bf16_H256_NE64_many_empty": workloads.custom(50, 4, 256, 64, act="bf16"),
     "bf16_H512_NE20": workloads.custom(300, 5, 512, 20, act="bf16"),
-    # the d_W reduce picks its column-tile shape from the chunks per expert (2, 4, 8 or 16 rows of
-    # threads); 48 chunks of 128 tokens over 4 experts takes the 4-row shape, which no workload
-    # above reaches
+    # the d_W reduce picks its kernel from the chunks per expert (the wide kernel below 8, else
+    # 4, 8 or 16 rows of threads); 48 chunks of 128 tokens over 4 experts takes the 4-row shape,
+    # which no workload above reaches (the wide kernel's batch loop and its empty experts:
+    # skewed_lam005, empty_expert, NE64_many_empty)
     "reduce_mid_chunks_per_expert": workloads.custom(1229, 5, 128, 4),
 }
 
