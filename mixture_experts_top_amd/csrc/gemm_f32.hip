@@ -764,13 +764,17 @@ struct DwF32Smem {
 };
 
 #ifndef MOE_DW_PF
-#define MOE_DW_PF 2  // K slices of rows in flight per workgroup of the 256 x 256 dW tiles (even)
+#define MOE_DW_PF 2  // K slices of rows in flight per workgroup of the 256 x 256 dW tiles
+#endif
+#ifndef MOE_F32_KC_DW_BIG
+#define MOE_F32_KC_DW_BIG 16  // tokens per K slice in the 256 x 256 dW tiles
 #endif
 #ifndef MOE_DW_RING_F4
 #define MOE_DW_RING_F4 4  // float4 registers of rows in flight per thread in the smaller dW tiles
 #endif
 // NTH threads: 256 (wavefronts 2 x 2 over the tile) or 512 (2 x 4, for 256 x 256 tiles).
-// PFX: K slices in flight (0: as many as MOE_DW_RING_F4 registers hold, even, at least 2).
+// PFX: K slices of rows in flight (0: as many as MOE_DW_RING_F4 registers hold, even, at
+// least 2).
 template <int H, int BT, int KC, bool MEAN = false, int NTH = kThreads, int PFX = 0>
 __device__ __forceinline__ void dw_f32_body(char* smem, int bid, const float* __restrict__ dY,
                                                       const float* __restrict__ X,
@@ -784,8 +788,8 @@ __device__ __forceinline__ void dw_f32_body(char* smem, int bid, const float* __
     constexpr int WTM = BT / 2, WTN = BT / WN_W, SUBM = WTM / 32, SUBN = WTN / 32;
     constexpr int Q = BT / 4;                  // float4 per row segment
     constexpr int LD = KC * Q / NTH;      // float4 loads per thread per tensor per slice
-    constexpr int PF0 = PFX > 0 ? PFX : MOE_DW_RING_F4 / (2 * LD);
-    constexpr int PF = PF0 < 2 ? 2 : PF0 - PF0 % 2;
+    constexpr int PF0 = MOE_DW_RING_F4 / (2 * LD);
+    constexpr int PF = PFX > 0 ? PFX : (PF0 < 2 ? 2 : PF0 - PF0 % 2);
     float(&As)[2][KC][BT + kPadKN] = *reinterpret_cast<float(*)[2][KC][BT + kPadKN]>(smem);  // dY rows, o0..o0+BT
     float(&Bs)[2][KC][BT + kPadKN] =
         *reinterpret_cast<float(*)[2][KC][BT + kPadKN]>(smem + DwF32Smem<BT, KC>::a);      // X rows, i0..i0+BT
@@ -861,7 +865,7 @@ __device__ __forceinline__ void dw_f32_body(char* smem, int bid, const float* __
     load_ids(2 * PF, 0);     // slice 2PF, over slice 0's ids
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
-    static_assert(PF % 2 == 0, "the LDS buffer of slice s0 + u is u % 2");
+    // cycles of 2PF slices start at even slices: the LDS buffer of slice s0 + u is u % 2
     int s0 = 0;
     do {  // whole cycles of 2PF slices; slices past the chunk's end load (clamped), do not compute
 #pragma unroll
@@ -1422,7 +1426,7 @@ static hipError_t bwd_f32(const float* dY, const float* X, const float* W, float
             constexpr int TPC = (H / 256) * (H / 256);
             const int dx_ids = rows_grid<H, TL::BIG_BN>(T, NE, 128);
             const ArmedEvents ev = take_armed_events();
-            launch_kernel_ev((k_dw_f32_big<H, MOE_F32_KC_DW, MEAN>), dim3(NE + round_up(n_chunk_max, 8) * TPC),
+            launch_kernel_ev((k_dw_f32_big<H, MOE_F32_KC_DW_BIG, MEAN>), dim3(NE + round_up(n_chunk_max, 8) * TPC),
                              dim3(kDwBigThreads), 0, s, ev.start, nullptr, dY, X, W, wt, pdw, pdb, offsets, perm, NE,
                              P, (int)T, nh, inv_nh);
             if (f32_wst(T, H))
