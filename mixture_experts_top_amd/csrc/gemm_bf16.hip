@@ -1290,6 +1290,33 @@ static inline bool bf16_wst(int64_t T, int H) {
     return MOE_BF16_WST && H >= 256 && T >= (int64_t)(kWstWgs / (H / 256)) * 8 * kWstGT;
 }
 
+// Rows k0 .. k0 + NR - 1, columns n0 .. n0 + 255 of one expert's W (bf16, rows of H) into an
+// LDS stage of 512-byte rows, 16-byte chunk c of row r at c ^ 4 (r & 3) (where the transposing
+// reads of tr_frag_swz find them conflict-free), with direct-to-LDS loads, two rows per
+// wavefront load and all of them in flight at once; the caller waits and synchronises.
+template <int H, int NR>
+__device__ __forceinline__ void stage_w_rows(char* wst, const uint16_t* __restrict__ We, int k0, int n0, int wave,
+                                             int lane) {
+    constexpr int PER = NR / 2 / (kWstThreads / 64);  // loads per wavefront, two rows each
+    static_assert(NR % 32 == 0 && PER % 2 == 0, "rows per stage");
+    // wavefront w fills rows 2 PER w .. + 2 PER - 1, four rows (two loads) per step; within a
+    // step, lane i takes row 2 q + (i >> 5) of load q and physical chunk i & 31 (r & 3 = 2 q + (i >> 5))
+    const int sub = lane >> 5, pc = lane & 31;
+    const int off0 = sub * H + 8 * (pc ^ (4 * sub));
+    const int off1 = (2 + sub) * H + 8 * (pc ^ (4 * (2 + sub)));
+    const uint16_t* src = We + (size_t)(k0 + 2 * PER * wave) * H + n0;
+    char* dst = wst + 2 * PER * wave * 512;
+    // a loop, not unrolled: unrolled, the compiler keeps every load's address live across the
+    // caller's loops (and spills them)
+#pragma unroll 1
+    for (int j = 0; j < PER; j += 2) {
+        __builtin_amdgcn_global_load_lds((const void*)(src + off0), (lds_void_ptr)dst, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(src + off1), (lds_void_ptr)(dst + 1024), 16, 0, 0);
+        src += 4 * H;
+        dst += 2048;
+    }
+}
+
 template <int H, bool DX, bool MEAN, bool ACC>
 __device__ __forceinline__ void rows_bf16_wst_body(char* smem, const uint16_t* __restrict__ A,
                                                    const uint16_t* __restrict__ Wm, const float* __restrict__ bias,
@@ -1428,20 +1455,9 @@ __device__ __forceinline__ void rows_bf16_wst_body(char* smem, const uint16_t* _
 #pragma unroll  // compile-time k0, so the register array wr keeps constant indices
             for (int k0 = 0; k0 < H; k0 += WROWS) {
                 if (k0 > 0) __syncthreads();  // the previous stage is read
-#pragma unroll 1
-                for (int rb = 0; rb < WROWS; rb += 32) {  // 32 rows per batch: 2 loads per thread
-                    u16x8 wv[2];
-#pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        const int r = rb + 16 * u + tid / 32;
-                        wv[u] = ld8(Wm + (size_t)e * H * H + (size_t)(k0 + r) * H + n0 + 8 * (tid % 32));
-                    }
-#pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        const int r = rb + 16 * u + tid / 32;
-                        st8(reinterpret_cast<uint16_t*>(wst + r * 512 + 16 * ((tid % 32) ^ (4 * (r & 3)))), wv[u]);
-                    }
-                }
+                stage_w_rows<H, WROWS>(wst, Wm + (size_t)e * H * H, k0, n0,
+                                       __builtin_amdgcn_readfirstlane(wave), lane);
+                wait_vm_lds<0>();
                 __syncthreads();
 #pragma unroll
                 for (int ks = 0; ks < WROWS / 16; ++ks) wr[k0 / 16 + ks] = tr_frag_swz(wst, 16 * ks, fw, lane);
@@ -1478,6 +1494,253 @@ __device__ __forceinline__ void rows_bf16_wst_body(char* smem, const uint16_t* _
     }
 }
 
+// Role-split variant (outputs overwritten, not accumulated).  The single-role body above keeps one
+// group of rows in flight: its loads go through registers, and because every wavefront also has
+// output stores pending, the wait for those rows is a wait for everything.  Here wavefronts 0-3
+// ("loaders") move rows from global memory straight into a ring of three LDS stages
+// (global_load_lds_dwordx4), two groups ahead of the MFMAs, and issue no stores; wavefronts 4-7
+// ("storers") write the finished rows and issue no loads into that ring.  Each role's loop thus
+// has one kind of memory operation pending and waits for exactly the group it needs.  All eight
+// wavefronts run the MFMAs on their 32 features as before; bias add and bf16 rounding happen in
+// the accumulator registers (the same fp32 add and the same rounding as the single-role body, so
+// the results are bit-identical), and the bf16 rows are staged in LDS for the storers.
+#ifndef MOE_BF16_WST_ROLES
+#define MOE_BF16_WST_ROLES 1
+#endif
+template <int H>
+struct WsrSmem {
+    static constexpr int ROWB = 2 * H;                          // bytes per token row
+    static constexpr int NX = 3;                                // row stages
+    static constexpr size_t xbuf = (size_t)kWstGT * ROWB;       // one group's rows
+    static constexpr size_t obuf = (size_t)kWstGT * 256 * 2;    // one group's bf16 results [32][256]
+    static constexpr size_t ost_off = NX * xbuf;
+    static constexpr size_t bias_off = ost_off + 2 * obuf;
+    static constexpr size_t ids_off = bias_off + 256 * 4;       // token ids: [4][32]
+    static constexpr size_t raw_off = ids_off + 4 * kWstGT * 4; // perm entries as loaded: [4][4 waves][64]
+    static constexpr size_t bytes = raw_off + 4 * 4 * 64 * 4;
+};
+
+template <int H, bool DX, bool MEAN>
+__device__ __forceinline__ void rows_bf16_wsr_body(char* smem, const uint16_t* __restrict__ A,
+                                                   const uint16_t* __restrict__ Wm, const float* __restrict__ bias,
+                                                   uint16_t* __restrict__ Out, const int* __restrict__ offsets,
+                                                   const int* __restrict__ perm, int NE, int T, int nh,
+                                                   float inv_nh) {
+    using S = WsrSmem<H>;
+    constexpr int NS = H / 256, NKS = H / 16, V = kWstWgs / NS;
+    constexpr int CPR = S::ROWB / 16;   // 16-byte chunks per row
+    constexpr int RPD = 64 / CPR;       // rows per direct-to-LDS load of one wavefront (64 x 16 bytes)
+    constexpr int NLW = 4;              // loader wavefronts
+    constexpr int RPW = kWstGT / NLW;   // rows per loader wavefront per group
+    constexpr int DPG = RPW / RPD;      // direct-to-LDS loads per loader wavefront per group
+    static_assert(kWstThreads == 512 && RPW % RPD == 0 && CPR >= 16, "shape");
+    const int tid = threadIdx.x, lane = tid % 64, l32 = lane % 32, h = lane / 32;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+    const bool loader = wave < NLW;
+    const int bid = blockIdx.x;
+    const int s = (bid / 8) % NS, v = (bid % 8) + 8 * (bid / (8 * NS));
+    const int n0 = 256 * s, fw = 32 * wave;  // this wavefront's features n0 + fw + 0..31
+    const int P0 = (int)((int64_t)v * T / V), P1 = (int)((int64_t)(v + 1) * T / V);
+    float* const bias_s = reinterpret_cast<float*>(smem + S::bias_off);
+    // token ids of group g in ids[g % 4]: written by the loaders when they issue the group's rows
+    // (two groups ahead), read by the storers a group after its MFMAs
+    int(&ids)[4][kWstGT] = *reinterpret_cast<int(*)[4][kWstGT]>(smem + S::ids_off);
+    auto xstage = [&](int g) { return smem + (g % S::NX) * S::xbuf; };
+    auto ostage = [&](int g) { return smem + S::ost_off + (g & 1) * S::obuf; };
+    int x_lo, x_cnt;
+    expert_range(offsets, NE, T, x_lo, x_cnt);
+
+    u16x8 wr[NKS];  // features n0 + fw + l32, k 16 ks + 8 h ..
+
+    // MFMAs of one group; the results, plus bias and rounded to bf16, into the group's output
+    // stage: row = token l32, 16-byte chunk c (features 8c .. 8c + 7) at c ^ (row & 31)
+    auto compute = [&](int g) {
+        const char* row = xstage(g) + l32 * S::ROWB;
+        auto frag = [&](int ks) {
+            return *reinterpret_cast<const u16x8*>(row + 16 * ((2 * ks + h) ^ (l32 & 15)));
+        };
+        // software-pipelined in batches of KB k-steps: the reads of the next batch are issued
+        // before the MFMAs of this one, so the LDS serves one batch while the matrix cores work
+        // on the other (with all wavefronts reading, then all multiplying, in step, the two
+        // would take turns)
+        constexpr int KB = 2;
+        f32x16 acc = f32x16{};
+        u16x8 cur[KB], nxt[KB];
+#pragma unroll
+        for (int u = 0; u < KB; ++u) cur[u] = frag(u);
+#pragma unroll
+        for (int k0 = 0; k0 < NKS; k0 += KB) {
+            if (k0 + KB < NKS) {
+#pragma unroll
+                for (int u = 0; u < KB; ++u) nxt[u] = frag(k0 + KB + u);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < KB; ++u) {
+                if (MEAN) cur[u] = scale8(cur[u], inv_nh);
+                acc = mfma_bf16(wr[k0 + u], cur[u], acc);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < KB; ++u) cur[u] = nxt[u];
+        }
+        // lane: token l32, features fw + 8 q + 4 h .. + 3
+        char* const orow = ostage(g) + l32 * 512;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            float vv[4] = {acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+            if (!DX) {
+                const f32x4 b = *reinterpret_cast<const f32x4*>(bias_s + fw + 8 * q + 4 * h);
+                vv[0] += b.x;
+                vv[1] += b.y;
+                vv[2] += b.z;
+                vv[3] += b.w;
+            }
+            const i32x2v pk = {(int)pack_bf16x2(vv[0], vv[1]), (int)pack_bf16x2(vv[2], vv[3])};
+            *reinterpret_cast<i32x2v*>(orow + 16 * (((fw >> 3) + q) ^ (l32 & 31)) + 8 * h) = pk;
+        }
+    };
+
+    int p = P0;
+    while (p < P1) {
+        // segment: positions [p, se) of expert e
+        const uint64_t hit = __ballot(lane < NE && p >= x_lo && p < x_lo + x_cnt);
+        if (hit == 0) break;  // (only with routing that does not cover [0, T))
+        const int e = __ffsll((unsigned long long)hit) - 1;
+        const int se = min(P1, __builtin_amdgcn_readlane(x_lo, e) + __builtin_amdgcn_readlane(x_cnt, e));
+        const int G = (se - p + kWstGT - 1) / kWstGT;
+        __syncthreads();  // the previous segment is done with every stage, the bias and the ids
+        if constexpr (!DX) {  // W[e] rows n0 + fw + l32, k contiguous
+            const uint16_t* __restrict__ We = Wm + (size_t)e * H * H + (size_t)(n0 + fw + l32) * H + 8 * h;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) wr[ks] = ld8(We + 16 * ks);
+        } else {
+            // W^T fragments: W[e] rows k (WROWS at a time) x columns n0 .. n0 + 255 staged in the
+            // row and output stages (512-byte rows, chunk c of row r at c ^ 4 (r & 3)), read back
+            // with the transposing LDS read (8 consecutive k of one column per lane)
+            constexpr int WROWS = (S::bias_off >= 256 * 512) ? 256 : 128;
+            static_assert(S::bias_off >= (size_t)WROWS * 512 && H % WROWS == 0, "LDS for a W stage");
+            char* const wst = smem;
+#pragma unroll
+            for (int k0 = 0; k0 < H; k0 += WROWS) {
+                if (k0 > 0) __syncthreads();
+                stage_w_rows<H, WROWS>(wst, Wm + (size_t)e * H * H, k0, n0, wave, lane);
+                wait_vm_lds<0>();
+                __syncthreads();
+#pragma unroll
+                for (int ks = 0; ks < WROWS / 16; ++ks) wr[k0 / 16 + ks] = tr_frag_swz(wst, 16 * ks, fw, lane);
+            }
+            __syncthreads();  // every wavefront has its fragments before the rows overwrite the stage
+        }
+        if (!DX && tid < 256) bias_s[tid] = bias[(size_t)e * H + n0 + tid];
+        if (loader) {
+            // perm entries of this wavefront's rows RPW wave + (i % RPW) of group g (lane i; clamped
+            // positions, validity applied when the group is issued), loaded straight into LDS
+            // like the rows.  Nothing in this loop is loaded into registers: the compiler models
+            // a direct-to-LDS load as a flat access, and while one is in flight every wait it
+            // would insert for a register load is a wait for everything.  The only waits on the
+            // vector-memory counter are the explicit ones below, which count these loads too.
+            int* const raw_s = reinterpret_cast<int*>(smem + S::raw_off) + 64 * wave;
+            auto load_ids = [&](int g) {
+                const int* src = perm + min(p + kWstGT * g + RPW * wave + lane % RPW, se - 1);
+                __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_ptr)(raw_s + 256 * (g & 3)), 4, 0, 0);
+            };
+            // group g's rows into its stage: load q covers rows RPW wave + RPD q .. + RPD - 1, lane
+            // i taking row RPW wave + RPD q + i / CPR and physical chunk i % CPR, which holds
+            // logical chunk (i % CPR) ^ (row & 15); padded rows read the zero row
+            auto issue = [&](int g) {
+                const int kb = p + kWstGT * g + RPW * wave;
+                const int raw = raw_s[256 * (g & 3) + lane];  // the entry of row lane % RPW
+                // every lane writes the id of row lane % RPW (lanes with the same row write the
+                // same value), so no branch
+                ids[g & 3][RPW * wave + lane % RPW] = kb + lane % RPW < se ? guard_token(raw, T) : -1;
+                char* const xs = xstage(g);
+#pragma unroll
+                for (int q = 0; q < DPG; ++q) {
+                    const int sub = lane / CPR, pcl = lane % CPR;
+                    const int j = RPD * q + sub, rw = RPW * wave + j;
+                    const int rj = RPD == 1 ? __builtin_amdgcn_readlane(raw, RPD * q)
+                                            : (sub ? __builtin_amdgcn_readlane(raw, RPD * q + 1)
+                                                   : __builtin_amdgcn_readlane(raw, RPD * q));
+                    const int tt = kb + j < se ? guard_token(rj, T) : -1;
+                    const int lc = pcl ^ (rw & 15);
+                    const uint16_t* src =
+                        tt >= 0 ? A + (size_t)(MEAN ? tt / nh : tt) * H + 8 * lc : kZeroRow + 8 * lc;
+                    __builtin_amdgcn_global_load_lds((const void*)src,
+                                                     (lds_void_ptr)(xs + (RPW * wave + RPD * q) * S::ROWB), 16, 0, 0);
+                }
+            };
+            auto pin = [] {  // no memory access moves across this point
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            load_ids(0);
+            load_ids(1);
+            load_ids(2);
+            pin();
+            wait_vm_lds<0>();
+            pin();
+            // groups at or past G are issued too, as zero rows into a stage no one reads any more,
+            // so that every iteration has the same loads in flight and every wait one count
+            issue(0);
+            issue(1);
+            // the barriers here wait explicitly: a workgroup fence would also wait for the rows
+            // still in flight into LDS.  lgkmcnt(0) covers this wavefront's LDS writes (ids,
+            // bias, results); the empty asm and the scheduling barriers keep every memory access
+            // on its side of the barrier
+            auto ring_barrier = [&] {
+                pin();
+                wait_vm_lds<DPG>();
+                __builtin_amdgcn_s_barrier();
+                pin();
+            };
+            ring_barrier();
+            // group g: the ids of g + 3, then the rows of g + 2 into the stage g - 1 used (every
+            // wavefront finished it before the barrier), the MFMAs of g, then the wait for the
+            // rows of g + 1 (only those of g + 2 may stay in flight; the ids are older)
+#pragma unroll 1
+            for (int g = 0; g < G; ++g) {
+                load_ids(g + 3);
+                pin();
+                issue(g + 2);
+                pin();
+                compute(g);
+                ring_barrier();
+            }
+            wait_vm_lds<0>();  // the last zero rows land before the stages are used again
+        } else {
+            // storer wavefront sw: rows 2 sw + i / 32 + 8 j, 16-byte chunk i % 32, of a group
+            const int sw = wave - NLW;
+            auto store = [&](int g) {
+                const char* os = ostage(g);
+                int t[4];
+                u16x8 val[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 2 * sw + h + 8 * j;
+                    t[j] = ids[g & 3][r];
+                    val[j] = *reinterpret_cast<const u16x8*>(os + r * 512 + 16 * (l32 ^ (r & 31)));
+                }
+                // all eight LDS reads issued before the first store (not one pair per store)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) asm volatile("" ::"v"(val[j]), "v"(t[j]));
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (t[j] >= 0) st8_nt(Out + (size_t)t[j] * H + n0 + 8 * l32, val[j]);
+            };
+            __syncthreads();
+#pragma unroll 1
+            for (int g = 0; g < G; ++g) {
+                if (g > 0) store(g - 1);
+                compute(g);
+                __syncthreads();
+            }
+            store(G - 1);
+        }
+        p = se;
+    }
+}
+
 template <int H, bool DX, bool MEAN, bool ACC>
 __global__ __launch_bounds__(kWstThreads) void k_rows_bf16_wst(const uint16_t* __restrict__ A,
                                                                 const uint16_t* __restrict__ Wm,
@@ -1486,8 +1749,12 @@ __global__ __launch_bounds__(kWstThreads) void k_rows_bf16_wst(const uint16_t* _
                                                                 const int* __restrict__ offsets,
                                                                 const int* __restrict__ perm, int NE, int T, int nh,
                                                                 float inv_nh) {
-    __shared__ __attribute__((aligned(16))) char smem[WstSmem<H>::bytes];
-    rows_bf16_wst_body<H, DX, MEAN, ACC>(smem, A, Wm, bias, Out, offsets, perm, NE, T, nh, inv_nh);
+    constexpr bool ROLES = MOE_BF16_WST_ROLES && !ACC;
+    __shared__ __attribute__((aligned(16))) char smem[ROLES ? WsrSmem<H>::bytes : WstSmem<H>::bytes];
+    if constexpr (ROLES)
+        rows_bf16_wsr_body<H, DX, MEAN>(smem, A, Wm, bias, Out, offsets, perm, NE, T, nh, inv_nh);
+    else
+        rows_bf16_wst_body<H, DX, MEAN, ACC>(smem, A, Wm, bias, Out, offsets, perm, NE, T, nh, inv_nh);
 }
 
 // Kernels.  For H <= 128 the backward is one launch: dW / db chunk tiles first, then dX tiles.
