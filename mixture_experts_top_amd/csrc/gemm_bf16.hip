@@ -1100,6 +1100,12 @@ struct DwdSmem {
 };
 static __device__ __attribute__((aligned(16))) uint16_t kZeroRow[512];  // one zero row of up to H = 512
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
+// LDS-qualified element types, for volatile reads (through a generic pointer a volatile read
+// stays a flat access, which also waits on the vector-memory counter)
+typedef __attribute__((address_space(3))) int lds_int;
+// buffer descriptor word 3 for raw (untyped) buffer accesses on CDNA: 32-bit data format
+constexpr int kBufWord3 = 0x00020000;
+typedef __attribute__((address_space(3))) u16x8 lds_u16x8;
 
 // s_waitcnt with the vector-memory count at N and the LDS count at 0 (export count untouched)
 template <int N>
@@ -1294,10 +1300,10 @@ static inline bool bf16_wst(int64_t T, int H) {
 // LDS stage of 512-byte rows, 16-byte chunk c of row r at c ^ 4 (r & 3) (where the transposing
 // reads of tr_frag_swz find them conflict-free), with direct-to-LDS loads, two rows per
 // wavefront load and all of them in flight at once; the caller waits and synchronises.
-template <int H, int NR>
+template <int H, int NR, int NWV>
 __device__ __forceinline__ void stage_w_rows(char* wst, const uint16_t* __restrict__ We, int k0, int n0, int wave,
                                              int lane) {
-    constexpr int PER = NR / 2 / (kWstThreads / 64);  // loads per wavefront, two rows each
+    constexpr int PER = NR / 2 / NWV;  // loads per wavefront (NWV of them), two rows each
     static_assert(NR % 32 == 0 && PER % 2 == 0, "rows per stage");
     // wavefront w fills rows 2 PER w .. + 2 PER - 1, four rows (two loads) per step; within a
     // step, lane i takes row 2 q + (i >> 5) of load q and physical chunk i & 31 (r & 3 = 2 q + (i >> 5))
@@ -1455,8 +1461,8 @@ __device__ __forceinline__ void rows_bf16_wst_body(char* smem, const uint16_t* _
 #pragma unroll  // compile-time k0, so the register array wr keeps constant indices
             for (int k0 = 0; k0 < H; k0 += WROWS) {
                 if (k0 > 0) __syncthreads();  // the previous stage is read
-                stage_w_rows<H, WROWS>(wst, Wm + (size_t)e * H * H, k0, n0,
-                                       __builtin_amdgcn_readfirstlane(wave), lane);
+                stage_w_rows<H, WROWS, kWstThreads / 64>(wst, Wm + (size_t)e * H * H, k0, n0,
+                                                         __builtin_amdgcn_readfirstlane(wave), lane);
                 wait_vm_lds<0>();
                 __syncthreads();
 #pragma unroll
@@ -1496,17 +1502,32 @@ __device__ __forceinline__ void rows_bf16_wst_body(char* smem, const uint16_t* _
 
 // Role-split variant (outputs overwritten, not accumulated).  The single-role body above keeps one
 // group of rows in flight: its loads go through registers, and because every wavefront also has
-// output stores pending, the wait for those rows is a wait for everything.  Here wavefronts 0-3
-// ("loaders") move rows from global memory straight into a ring of three LDS stages
-// (global_load_lds_dwordx4), two groups ahead of the MFMAs, and issue no stores; wavefronts 4-7
-// ("storers") write the finished rows and issue no loads into that ring.  Each role's loop thus
-// has one kind of memory operation pending and waits for exactly the group it needs.  All eight
-// wavefronts run the MFMAs on their 32 features as before; bias add and bf16 rounding happen in
+// output stores pending, the wait for those rows is a wait for everything.  Here the first half
+// of the NW wavefronts ("loaders") move rows from global memory straight into a ring of three
+// LDS stages (global_load_lds_dwordx4), two groups ahead of the MFMAs, and issue no stores; the
+// other half ("storers") write the finished rows and issue no loads into that ring.  Each role's
+// loop thus has one kind of memory operation pending and waits for exactly the group it needs.
+// All wavefronts run the MFMAs, each on 256 / NW features; bias add and bf16 rounding happen in
 // the accumulator registers (the same fp32 add and the same rounding as the single-role body, so
 // the results are bit-identical), and the bf16 rows are staged in LDS for the storers.
+// NW = 4 (one wavefront per SIMD, 64 features each: W in 256 of its 512 registers at H = 512)
+// reads every row fragment from LDS once per two MFMAs; NW = 8 (two per SIMD, 32 features each)
+// once per MFMA, and the LDS reads of eight wavefronts then bound the loop.
 #ifndef MOE_BF16_WST_ROLES
 #define MOE_BF16_WST_ROLES 1
 #endif
+#ifndef MOE_BF16_WSR_WAVES
+#define MOE_BF16_WSR_WAVES 8
+#endif
+#ifndef MOE_BF16_WSR_KB
+#define MOE_BF16_WSR_KB 1
+#endif
+#ifndef MOE_BF16_WSR_PD
+#define MOE_BF16_WSR_PD 3
+#endif
+static_assert(MOE_BF16_WSR_WAVES == 4 || MOE_BF16_WSR_WAVES == 8, "role-split wavefronts");
+template <bool ACC>
+constexpr int wst_threads() { return (MOE_BF16_WST_ROLES && !ACC) ? 64 * MOE_BF16_WSR_WAVES : kWstThreads; }
 template <int H>
 struct WsrSmem {
     static constexpr int ROWB = 2 * H;                          // bytes per token row
@@ -1520,7 +1541,7 @@ struct WsrSmem {
     static constexpr size_t bytes = raw_off + 4 * 4 * 64 * 4;
 };
 
-template <int H, bool DX, bool MEAN>
+template <int H, bool DX, bool MEAN, int NW>
 __device__ __forceinline__ void rows_bf16_wsr_body(char* smem, const uint16_t* __restrict__ A,
                                                    const uint16_t* __restrict__ Wm, const float* __restrict__ bias,
                                                    uint16_t* __restrict__ Out, const int* __restrict__ offsets,
@@ -1530,16 +1551,19 @@ __device__ __forceinline__ void rows_bf16_wsr_body(char* smem, const uint16_t* _
     constexpr int NS = H / 256, NKS = H / 16, V = kWstWgs / NS;
     constexpr int CPR = S::ROWB / 16;   // 16-byte chunks per row
     constexpr int RPD = 64 / CPR;       // rows per direct-to-LDS load of one wavefront (64 x 16 bytes)
-    constexpr int NLW = 4;              // loader wavefronts
+    constexpr int NB = 8 / NW;          // 32-feature blocks per wavefront
+    constexpr int NLW = NW / 2;         // loader wavefronts
     constexpr int RPW = kWstGT / NLW;   // rows per loader wavefront per group
     constexpr int DPG = RPW / RPD;      // direct-to-LDS loads per loader wavefront per group
-    static_assert(kWstThreads == 512 && RPW % RPD == 0 && CPR >= 16, "shape");
+    constexpr int SW = NW - NLW;        // storer wavefronts
+    constexpr int RPL = kWstGT / (2 * SW);  // rows per storer lane per group
+    static_assert((NW == 4 || NW == 8) && RPW % RPD == 0 && RPW <= 64 && CPR >= 16, "shape");
     const int tid = threadIdx.x, lane = tid % 64, l32 = lane % 32, h = lane / 32;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
     const bool loader = wave < NLW;
     const int bid = blockIdx.x;
     const int s = (bid / 8) % NS, v = (bid % 8) + 8 * (bid / (8 * NS));
-    const int n0 = 256 * s, fw = 32 * wave;  // this wavefront's features n0 + fw + 0..31
+    const int n0 = 256 * s, fw = 32 * NB * wave;  // this wavefront's features n0 + fw + 0 .. 32 NB - 1
     const int P0 = (int)((int64_t)v * T / V), P1 = (int)((int64_t)(v + 1) * T / V);
     float* const bias_s = reinterpret_cast<float*>(smem + S::bias_off);
     // token ids of group g in ids[g % 4]: written by the loaders when they issue the group's rows
@@ -1550,55 +1574,80 @@ __device__ __forceinline__ void rows_bf16_wsr_body(char* smem, const uint16_t* _
     int x_lo, x_cnt;
     expert_range(offsets, NE, T, x_lo, x_cnt);
 
-    u16x8 wr[NKS];  // features n0 + fw + l32, k 16 ks + 8 h ..
+    u16x8 wr[NB][NKS];  // block b: features n0 + fw + 32 b + l32, k 16 ks + 8 h ..
 
     // MFMAs of one group; the results, plus bias and rounded to bf16, into the group's output
-    // stage: row = token l32, 16-byte chunk c (features 8c .. 8c + 7) at c ^ (row & 31)
-    auto compute = [&](int g) {
+    // stage: row = token l32, 16-byte chunk c (features 8c .. 8c + 7) at c ^ (row & 31).
+    // mid(bt) runs after the MFMAs of batch bt are issued: the role's memory work placed there
+    // issues while the matrix cores are busy, instead of in a phase of its own.
+    constexpr int NBT = NKS / MOE_BF16_WSR_KB;  // batches of the MFMA loop
+    auto compute = [&](int g, auto&& mid) {
         const char* row = xstage(g) + l32 * S::ROWB;
+        // chunk (2 ks + h) ^ (l32 & 15) of the row, written as 16 (ks / 8) + ((2 (ks % 8) + h) ^
+        // (l32 & 15)): the same chunk (the xor touches only the low four bits), but with eight
+        // per-lane offsets and the rest an immediate, not one address register per k-step
         auto frag = [&](int ks) {
-            return *reinterpret_cast<const u16x8*>(row + 16 * ((2 * ks + h) ^ (l32 & 15)));
+            return *reinterpret_cast<const u16x8*>(row + 256 * (ks >> 3) + 16 * ((2 * (ks & 7) + h) ^ (l32 & 15)));
         };
-        // software-pipelined in batches of KB k-steps: the reads of the next batch are issued
-        // before the MFMAs of this one, so the LDS serves one batch while the matrix cores work
-        // on the other (with all wavefronts reading, then all multiplying, in step, the two
-        // would take turns)
-        constexpr int KB = 2;
-        f32x16 acc = f32x16{};
-        u16x8 cur[KB], nxt[KB];
+        // software-pipelined in batches of KB k-steps, the reads PD batches ahead of the MFMAs
+        // that use them, so the LDS serves later batches while the matrix cores work on this one
+        // (with all wavefronts reading, then all multiplying, in step, the two would take turns;
+        // one batch ahead leaves the LDS latency uncovered)
+        constexpr int KB = MOE_BF16_WSR_KB;
+        constexpr int PD = MOE_BF16_WSR_PD;
+        static_assert(NKS % KB == 0 && PD >= 1 && PD < NBT, "pipeline");
+        f32x16 acc[NB];
 #pragma unroll
-        for (int u = 0; u < KB; ++u) cur[u] = frag(u);
+        for (int b = 0; b < NB; ++b) acc[b] = f32x16{};
+        u16x8 buf[PD + 1][KB];
 #pragma unroll
-        for (int k0 = 0; k0 < NKS; k0 += KB) {
-            if (k0 + KB < NKS) {
+        for (int bt = 0; bt < PD; ++bt)
 #pragma unroll
-                for (int u = 0; u < KB; ++u) nxt[u] = frag(k0 + KB + u);
+            for (int u = 0; u < KB; ++u) buf[bt][u] = frag(KB * bt + u);
+#pragma unroll
+        for (int bt = 0; bt < NBT; ++bt) {
+            if (bt + PD < NBT) {
+#pragma unroll
+                for (int u = 0; u < KB; ++u) buf[(bt + PD) % (PD + 1)][u] = frag(KB * (bt + PD) + u);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int u = 0; u < KB; ++u) {
-                if (MEAN) cur[u] = scale8(cur[u], inv_nh);
-                acc = mfma_bf16(wr[k0 + u], cur[u], acc);
+                u16x8 x = buf[bt % (PD + 1)][u];
+                if (MEAN) x = scale8(x, inv_nh);
+#pragma unroll
+                for (int b = 0; b < NB; ++b) acc[b] = mfma_bf16(wr[b][KB * bt + u], x, acc[b]);
             }
+            mid(bt);
             __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int u = 0; u < KB; ++u) cur[u] = nxt[u];
         }
-        // lane: token l32, features fw + 8 q + 4 h .. + 3
+        // lane: token l32, features fw + 32 b + 8 q + 4 h .. + 3
         char* const orow = ostage(g) + l32 * 512;
+        // the bias reads all issued before the first staging write (which the compiler cannot
+        // tell apart from them, so interleaved they would each wait on their own)
+        f32x4 bv[NB][4];
+        if (!DX) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            float vv[4] = {acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
-            if (!DX) {
-                const f32x4 b = *reinterpret_cast<const f32x4*>(bias_s + fw + 8 * q + 4 * h);
-                vv[0] += b.x;
-                vv[1] += b.y;
-                vv[2] += b.z;
-                vv[3] += b.w;
-            }
-            const i32x2v pk = {(int)pack_bf16x2(vv[0], vv[1]), (int)pack_bf16x2(vv[2], vv[3])};
-            *reinterpret_cast<i32x2v*>(orow + 16 * (((fw >> 3) + q) ^ (l32 & 31)) + 8 * h) = pk;
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    bv[b][q] = *reinterpret_cast<const f32x4*>(bias_s + fw + 32 * b + 8 * q + 4 * h);
         }
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int f = fw + 32 * b + 8 * q;
+                float vv[4] = {acc[b][4 * q], acc[b][4 * q + 1], acc[b][4 * q + 2], acc[b][4 * q + 3]};
+                if (!DX) {
+                    vv[0] += bv[b][q].x;
+                    vv[1] += bv[b][q].y;
+                    vv[2] += bv[b][q].z;
+                    vv[3] += bv[b][q].w;
+                }
+                const i32x2v pk = {(int)pack_bf16x2(vv[0], vv[1]), (int)pack_bf16x2(vv[2], vv[3])};
+                *reinterpret_cast<i32x2v*>(orow + 16 * ((f >> 3) ^ (l32 & 31)) + 8 * h) = pk;
+            }
     };
 
     int p = P0;
@@ -1610,10 +1659,14 @@ __device__ __forceinline__ void rows_bf16_wsr_body(char* smem, const uint16_t* _
         const int se = min(P1, __builtin_amdgcn_readlane(x_lo, e) + __builtin_amdgcn_readlane(x_cnt, e));
         const int G = (se - p + kWstGT - 1) / kWstGT;
         __syncthreads();  // the previous segment is done with every stage, the bias and the ids
-        if constexpr (!DX) {  // W[e] rows n0 + fw + l32, k contiguous
-            const uint16_t* __restrict__ We = Wm + (size_t)e * H * H + (size_t)(n0 + fw + l32) * H + 8 * h;
+        if constexpr (!DX) {  // W[e] rows n0 + fw + 32 b + l32, k contiguous
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) wr[ks] = ld8(We + 16 * ks);
+            for (int b = 0; b < NB; ++b) {
+                const uint16_t* __restrict__ We =
+                    Wm + (size_t)e * H * H + (size_t)(n0 + fw + 32 * b + l32) * H + 8 * h;
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) wr[b][ks] = ld8(We + 16 * ks);
+            }
         } else {
             // W^T fragments: W[e] rows k (WROWS at a time) x columns n0 .. n0 + 255 staged in the
             // row and output stages (512-byte rows, chunk c of row r at c ^ 4 (r & 3)), read back
@@ -1624,11 +1677,14 @@ __device__ __forceinline__ void rows_bf16_wsr_body(char* smem, const uint16_t* _
 #pragma unroll
             for (int k0 = 0; k0 < H; k0 += WROWS) {
                 if (k0 > 0) __syncthreads();
-                stage_w_rows<H, WROWS>(wst, Wm + (size_t)e * H * H, k0, n0, wave, lane);
+                stage_w_rows<H, WROWS, NW>(wst, Wm + (size_t)e * H * H, k0, n0, wave, lane);
                 wait_vm_lds<0>();
                 __syncthreads();
 #pragma unroll
-                for (int ks = 0; ks < WROWS / 16; ++ks) wr[k0 / 16 + ks] = tr_frag_swz(wst, 16 * ks, fw, lane);
+                for (int b = 0; b < NB; ++b)
+#pragma unroll
+                    for (int ks = 0; ks < WROWS / 16; ++ks)
+                        wr[b][k0 / 16 + ks] = tr_frag_swz(wst, 16 * ks, fw + 32 * b, lane);
             }
             __syncthreads();  // every wavefront has its fragments before the rows overwrite the stage
         }
@@ -1641,9 +1697,28 @@ __device__ __forceinline__ void rows_bf16_wsr_body(char* smem, const uint16_t* _
             // would insert for a register load is a wait for everything.  The only waits on the
             // vector-memory counter are the explicit ones below, which count these loads too.
             int* const raw_s = reinterpret_cast<int*>(smem + S::raw_off) + 64 * wave;
+            // The loads into LDS go through buffer descriptors where they can: the compiler
+            // models global_load_lds as a flat access, and while one is in flight every LDS
+            // wait it inserts (those of the MFMA loop's fragment reads) becomes a wait for all
+            // of them; a buffer load is a plain vector-memory access.
+            const __amdgpu_buffer_rsrc_t perm_rs =
+                __builtin_amdgcn_make_buffer_rsrc((void*)(perm + p), 0, 4 * (se - p), kBufWord3);
             auto load_ids = [&](int g) {
-                const int* src = perm + min(p + kWstGT * g + RPW * wave + lane % RPW, se - 1);
-                __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_ptr)(raw_s + 256 * (g & 3)), 4, 0, 0);
+                const int k = min(p + kWstGT * g + RPW * wave + lane % RPW, se - 1) - p;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(perm_rs, (lds_void_ptr)(raw_s + 256 * (g & 3)), 4, 4 * k, 0, 0,
+                                                         0);
+            };
+            // one wavefront load of rows into LDS: with one row per load (H = 512) a buffer load
+            // through a descriptor of that row (tt uniform); with two (H = 256) the global form
+            auto row_dma = [&](int tt, int lc, char* dst) {
+                const uint16_t* rowp = tt >= 0 ? A + (size_t)(MEAN ? tt / nh : tt) * H : kZeroRow;
+                if constexpr (RPD == 1) {
+                    const __amdgpu_buffer_rsrc_t rs =
+                        __builtin_amdgcn_make_buffer_rsrc((void*)rowp, 0, S::ROWB, kBufWord3);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)dst, 16, 16 * lc, 0, 0, 0);
+                } else {
+                    __builtin_amdgcn_global_load_lds((const void*)(rowp + 8 * lc), (lds_void_ptr)dst, 16, 0, 0);
+                }
             };
             // group g's rows into its stage: load q covers rows RPW wave + RPD q .. + RPD - 1, lane
             // i taking row RPW wave + RPD q + i / CPR and physical chunk i % CPR, which holds
@@ -1663,11 +1738,7 @@ __device__ __forceinline__ void rows_bf16_wsr_body(char* smem, const uint16_t* _
                                             : (sub ? __builtin_amdgcn_readlane(raw, RPD * q + 1)
                                                    : __builtin_amdgcn_readlane(raw, RPD * q));
                     const int tt = kb + j < se ? guard_token(rj, T) : -1;
-                    const int lc = pcl ^ (rw & 15);
-                    const uint16_t* src =
-                        tt >= 0 ? A + (size_t)(MEAN ? tt / nh : tt) * H + 8 * lc : kZeroRow + 8 * lc;
-                    __builtin_amdgcn_global_load_lds((const void*)src,
-                                                     (lds_void_ptr)(xs + (RPW * wave + RPD * q) * S::ROWB), 16, 0, 0);
+                    row_dma(tt, pcl ^ (rw & 15), xs + (RPW * wave + RPD * q) * S::ROWB);
                 }
             };
             auto pin = [] {  // no memory access moves across this point
@@ -1695,44 +1766,89 @@ __device__ __forceinline__ void rows_bf16_wsr_body(char* smem, const uint16_t* _
                 pin();
             };
             ring_barrier();
-            // group g: the ids of g + 3, then the rows of g + 2 into the stage g - 1 used (every
-            // wavefront finished it before the barrier), the MFMAs of g, then the wait for the
-            // rows of g + 1 (only those of g + 2 may stay in flight; the ids are older)
+            // group g: the ids of g + 3, then, interleaved with the MFMAs of g (one load every
+            // STEP batches), the rows of g + 2 into the stage g - 1 used (every wavefront finished
+            // it before the barrier); then the wait for the rows of g + 1 (only those of g + 2
+            // may stay in flight; the ids are older)
+            constexpr int STEP = NBT / DPG;
+            static_assert(NBT % DPG == 0 && STEP >= 1, "loads per batch");
 #pragma unroll 1
             for (int g = 0; g < G; ++g) {
                 load_ids(g + 3);
                 pin();
-                issue(g + 2);
-                pin();
-                compute(g);
+                const int gi = g + 2, kb = p + kWstGT * gi + RPW * wave;
+                const int raw = *(volatile const lds_int*)(raw_s + 256 * (gi & 3) + lane);
+                char* const xs = xstage(gi);
+                int tq[DPG];  // per load: this lane's row's token (-1: padded)
+                compute(g, [&](int bt) {
+                    if (bt == 0) {
+                        ids[gi & 3][RPW * wave + lane % RPW] = kb + lane % RPW < se ? guard_token(raw, T) : -1;
+#pragma unroll
+                        for (int q = 0; q < DPG; ++q) {
+                            const int sub = lane / CPR, j = RPD * q + sub;
+                            const int rj = RPD == 1 ? __builtin_amdgcn_readlane(raw, RPD * q)
+                                                    : (sub ? __builtin_amdgcn_readlane(raw, RPD * q + 1)
+                                                           : __builtin_amdgcn_readlane(raw, RPD * q));
+                            tq[q] = kb + j < se ? guard_token(rj, T) : -1;
+                        }
+                    }
+                    if (bt % STEP == STEP - 1) {
+                        const int q = bt / STEP;
+                        const int sub = lane / CPR, pcl = lane % CPR, rw = RPW * wave + RPD * q + sub;
+                        row_dma(tq[q], pcl ^ (rw & 15), xs + (RPW * wave + RPD * q) * S::ROWB);
+                    }
+                });
                 ring_barrier();
             }
             wait_vm_lds<0>();  // the last zero rows land before the stages are used again
         } else {
-            // storer wavefront sw: rows 2 sw + i / 32 + 8 j, 16-byte chunk i % 32, of a group
+            // storer wavefront sw: rows 2 sw + i / 32 + 2 SW j, 16-byte chunk i % 32, of a group
             const int sw = wave - NLW;
             auto store = [&](int g) {
                 const char* os = ostage(g);
-                int t[4];
-                u16x8 val[4];
+                int t[RPL];
+                u16x8 val[RPL];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r = 2 * sw + h + 8 * j;
+                for (int j = 0; j < RPL; ++j) {
+                    const int r = 2 * sw + h + 2 * SW * j;
                     t[j] = ids[g & 3][r];
                     val[j] = *reinterpret_cast<const u16x8*>(os + r * 512 + 16 * (l32 ^ (r & 31)));
                 }
-                // all eight LDS reads issued before the first store (not one pair per store)
+                // every LDS read issued before the first store (not one pair per store)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) asm volatile("" ::"v"(val[j]), "v"(t[j]));
+                for (int j = 0; j < RPL; ++j) asm volatile("" ::"v"(val[j]), "v"(t[j]));
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < RPL; ++j)
                     if (t[j] >= 0) st8_nt(Out + (size_t)t[j] * H + n0 + 8 * l32, val[j]);
             };
             __syncthreads();
+            compute(0, [](int) {});
+            __syncthreads();
+            // group g: the rows of g - 1 written two at a time between the MFMAs of g (read from
+            // LDS SS batches before they are stored; volatile, so the reads stay where they are
+            // and the waits for them go where the stores use them)
+            constexpr int SS = NBT / RPL;
+            static_assert(NBT % RPL == 0 && RPL % 2 == 0 && SS >= 1, "stores per batch");
 #pragma unroll 1
-            for (int g = 0; g < G; ++g) {
-                if (g > 0) store(g - 1);
-                compute(g);
+            for (int g = 1; g < G; ++g) {
+                const char* os = ostage(g - 1);
+                int t[2];
+                u16x8 val[2];
+                compute(g, [&](int bt) {
+                    if (bt % (2 * SS) == 0) {
+#pragma unroll
+                        for (int u = 0; u < 2; ++u) {
+                            const int r = 2 * sw + h + 2 * SW * (2 * (bt / (2 * SS)) + u);
+                            t[u] = *(volatile const lds_int*)(&ids[(g - 1) & 3][r]);
+                            val[u] = *(volatile const lds_u16x8*)(os + r * 512 + 16 * (l32 ^ (r & 31)));
+                        }
+                    }
+                    if (bt % (2 * SS) == SS) {
+#pragma unroll
+                        for (int u = 0; u < 2; ++u)
+                            if (t[u] >= 0) st8_nt(Out + (size_t)t[u] * H + n0 + 8 * l32, val[u]);
+                    }
+                });
                 __syncthreads();
             }
             store(G - 1);
@@ -1742,7 +1858,8 @@ __device__ __forceinline__ void rows_bf16_wsr_body(char* smem, const uint16_t* _
 }
 
 template <int H, bool DX, bool MEAN, bool ACC>
-__global__ __launch_bounds__(kWstThreads) void k_rows_bf16_wst(const uint16_t* __restrict__ A,
+__global__ __launch_bounds__(wst_threads<ACC>()) __attribute__((amdgpu_waves_per_eu(
+    wst_threads<ACC>() == 256 ? 1 : 2))) void k_rows_bf16_wst(const uint16_t* __restrict__ A,
                                                                 const uint16_t* __restrict__ Wm,
                                                                 const float* __restrict__ bias,
                                                                 uint16_t* __restrict__ Out,
@@ -1752,7 +1869,8 @@ __global__ __launch_bounds__(kWstThreads) void k_rows_bf16_wst(const uint16_t* _
     constexpr bool ROLES = MOE_BF16_WST_ROLES && !ACC;
     __shared__ __attribute__((aligned(16))) char smem[ROLES ? WsrSmem<H>::bytes : WstSmem<H>::bytes];
     if constexpr (ROLES)
-        rows_bf16_wsr_body<H, DX, MEAN>(smem, A, Wm, bias, Out, offsets, perm, NE, T, nh, inv_nh);
+        rows_bf16_wsr_body<H, DX, MEAN, MOE_BF16_WSR_WAVES>(smem, A, Wm, bias, Out, offsets, perm, NE, T, nh,
+                                                            inv_nh);
     else
         rows_bf16_wst_body<H, DX, MEAN, ACC>(smem, A, Wm, bias, Out, offsets, perm, NE, T, nh, inv_nh);
 }
@@ -1854,7 +1972,8 @@ static hipError_t fwd_bf16(const uint16_t* X, const uint16_t* W, const float* bi
                            const int32_t* offsets, const int32_t* perm, int64_t T, int NE, hipStream_t s) {
     if constexpr (H >= 256) {
         if (bf16_wst(T, H)) {
-            launch_kernel((k_rows_bf16_wst<H, false, false, false>), dim3(kWstWgs), dim3(kWstThreads), 0, s, X, W,
+            launch_kernel((k_rows_bf16_wst<H, false, false, false>), dim3(kWstWgs), dim3(wst_threads<false>()), 0, s,
+                          X, W,
                           bias, Y, offsets, perm, NE, (int)T, 1, 1.0f);
             return hipGetLastError();
         }
@@ -1888,7 +2007,8 @@ static hipError_t bwd_bf16(const uint16_t* dY, const uint16_t* X, const uint16_t
         launch_kernel_ev((k_dw_bf16<H, MEAN>), dim3(n_dw), dim3(kDwBigThreads), 0, s, ev.start, nullptr, dY, X, pdw, pdb,
                          offsets, perm, NE, P, (int)T, nh, inv_nh);
         if (bf16_wst(T, H)) {
-            launch_kernel_ev((k_rows_bf16_wst<H, true, MEAN, ACC>), dim3(kWstWgs), dim3(kWstThreads), 0, s, nullptr,
+            launch_kernel_ev((k_rows_bf16_wst<H, true, MEAN, ACC>), dim3(kWstWgs), dim3(wst_threads<ACC>()), 0, s,
+                             nullptr,
                              ev.stop, dY, W, nullptr, dX, offsets, perm, NE, (int)T, nh, inv_nh);
         } else {
             launch_kernel_ev((k_dx_bf16<H, BN, MEAN, ACC>), dim3(n_dx), dim3(kThreads), 0, s, nullptr, ev.stop, dY, W,
