@@ -1105,6 +1105,9 @@ typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef __attribute__((address_space(3))) int lds_int;
 // buffer descriptor word 3 for raw (untyped) buffer accesses on CDNA: 32-bit data format
 constexpr int kBufWord3 = 0x00020000;
+// a byte offset past the end of any tensor the library takes (fewer than 2^31 bf16 elements):
+// a buffer load from it returns zeros
+constexpr uint32_t kPastEnd = 0xFFFF0000u;
 typedef __attribute__((address_space(3))) u16x8 lds_u16x8;
 
 // s_waitcnt with the vector-memory count at N and the LDS count at 0 (export count untouched)
@@ -1160,17 +1163,25 @@ __device__ __forceinline__ void dw_bf16_dma_body(char* const (&st)[R], int bid, 
             tk[slot][q] = perm[k < t1 ? k : (t1 > 0 ? t1 - 1 : 0)];
         }
     };
+    // buffer loads through descriptors of the whole of dY and X (bf16 tensors of fewer than 2^31
+    // elements, so every byte offset fits 32 bits); a padded row takes an offset past the end,
+    // which the range check turns into zeros.  (The buffer form, not global_load_lds: the
+    // compiler treats the global form as a flat access and then makes every LDS wait total.)
+    const __amdgpu_buffer_rsrc_t y_rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)dY, 0, (int)((uint32_t)(MEAN ? T / nh : T) * (uint32_t)H * 2u), kBufWord3);
+    const __amdgpu_buffer_rsrc_t x_rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)X, 0, (int)((uint32_t)T * (uint32_t)H * 2u), kBufWord3);
     auto dma = [&](int sl, int slot, char* stg) {
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const bool v = row_k(sl, q) < t1;
             const int lc = q ? lc1 : lc0;
-            const size_t t = (size_t)guard_token(tk[slot][q], T);
-            const uint16_t* gy = v ? dY + (MEAN ? t / nh : t) * H + o0 + 8 * lc : kZeroRow + 8 * lc;
-            const uint16_t* gx = v ? X + t * H + i0 + 8 * lc : kZeroRow + 8 * lc;
+            const uint32_t t = (uint32_t)guard_token(tk[slot][q], T);
+            const uint32_t oy = v ? (((MEAN ? t / nh : t) * H + o0 + 8 * lc) * 2u) : kPastEnd;
+            const uint32_t ox = v ? ((t * H + i0 + 8 * lc) * 2u) : kPastEnd;
             char* ly = stg + (4 * wave + 2 * q) * ROWB;
-            __builtin_amdgcn_global_load_lds((const void*)gy, (lds_void_ptr)ly, 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void*)gx, (lds_void_ptr)(ly + DwdSmem::tensor), 16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(y_rs, (lds_void_ptr)ly, 16, (int)oy, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rs, (lds_void_ptr)(ly + DwdSmem::tensor), 16, (int)ox, 0, 0, 0);
         }
     };
     auto compute = [&](const char* stg) {
@@ -1708,16 +1719,23 @@ __device__ __forceinline__ void rows_bf16_wsr_body(char* smem, const uint16_t* _
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(perm_rs, (lds_void_ptr)(raw_s + 256 * (g & 3)), 4, 4 * k, 0, 0,
                                                          0);
             };
-            // one wavefront load of rows into LDS: with one row per load (H = 512) a buffer load
-            // through a descriptor of that row (tt uniform); with two (H = 256) the global form
+            // one wavefront load of rows into LDS.  One row per load (H = 512): a descriptor of
+            // that row (tt uniform; a padded row reads the zero row), so the lane offsets are
+            // constants.  Two rows per load (H = 256): a descriptor of the whole of A (fewer than
+            // 2^31 bf16 elements: byte offsets fit 32 bits), a padded row taking an offset past
+            // the end, which the range check turns into zeros.
+            const __amdgpu_buffer_rsrc_t a_rs = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)A, 0, (int)((uint32_t)(MEAN ? T / nh : T) * (uint32_t)H * 2u), kBufWord3);
             auto row_dma = [&](int tt, int lc, char* dst) {
-                const uint16_t* rowp = tt >= 0 ? A + (size_t)(MEAN ? tt / nh : tt) * H : kZeroRow;
                 if constexpr (RPD == 1) {
+                    const uint16_t* rowp = tt >= 0 ? A + (size_t)(MEAN ? tt / nh : tt) * H : kZeroRow;
                     const __amdgpu_buffer_rsrc_t rs =
                         __builtin_amdgcn_make_buffer_rsrc((void*)rowp, 0, S::ROWB, kBufWord3);
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)dst, 16, 16 * lc, 0, 0, 0);
                 } else {
-                    __builtin_amdgcn_global_load_lds((const void*)(rowp + 8 * lc), (lds_void_ptr)dst, 16, 0, 0);
+                    const uint32_t off =
+                        tt >= 0 ? (((uint32_t)(MEAN ? tt / nh : tt) * H + 8 * lc) * 2u) : kPastEnd;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, (lds_void_ptr)dst, 16, (int)off, 0, 0, 0);
                 }
             };
             // group g's rows into its stage: load q covers rows RPW wave + RPD q .. + RPD - 1, lane
