@@ -1077,7 +1077,7 @@ __device__ __forceinline__ void dw_bf16_tr_body(char* smem, int bid, const uint1
 
 // The same d_W tile fed by direct global -> LDS loads.  Same tile, wavefront grid and LDS row
 // layout as dw_bf16_tr_body (token-major rows of 512 bytes, chunk c of row t at c ^ 4 (t & 3)),
-// but the rows go from global memory straight into LDS with gfx950's global_load_lds_dwordx4
+// but the rows go from global memory straight into LDS with buffer_load_dwordx4 ... lds
 // (lane i's 16 bytes land at the instruction's LDS base + 16 i), through a ring of R stages of
 // 32 tokens: the rows of the next R - 1 slices are in flight while a slice computes, and they
 // cost no registers.  Each stage is an LDS object of its own, so the compiler can tell the
@@ -1086,7 +1086,8 @@ __device__ __forceinline__ void dw_bf16_tr_body(char* smem, int bid, const uint1
 // issued after it -- every ring step issues the same six (four row loads, two token ids) in a
 // fixed order, with no exit inside a ring cycle -- and visible to every wavefront after the
 // barrier that follows.
-// Rows past the chunk's end (and the slices that pad the last ring cycle) read a zero row.
+// Rows past the chunk's end (and the slices that pad the last ring cycle) read zeros: their byte
+// offset lies past the end of the buffer.
 #ifndef MOE_BF16_DW_DMA
 #define MOE_BF16_DW_DMA 1
 #endif
@@ -1515,15 +1516,16 @@ __device__ __forceinline__ void rows_bf16_wst_body(char* smem, const uint16_t* _
 // group of rows in flight: its loads go through registers, and because every wavefront also has
 // output stores pending, the wait for those rows is a wait for everything.  Here the first half
 // of the NW wavefronts ("loaders") move rows from global memory straight into a ring of three
-// LDS stages (global_load_lds_dwordx4), two groups ahead of the MFMAs, and issue no stores; the
+// LDS stages (buffer_load_dwordx4 ... lds), two groups ahead of the MFMAs, and issue no stores; the
 // other half ("storers") write the finished rows and issue no loads into that ring.  Each role's
 // loop thus has one kind of memory operation pending and waits for exactly the group it needs.
 // All wavefronts run the MFMAs, each on 256 / NW features; bias add and bf16 rounding happen in
 // the accumulator registers (the same fp32 add and the same rounding as the single-role body, so
 // the results are bit-identical), and the bf16 rows are staged in LDS for the storers.
 // NW = 4 (one wavefront per SIMD, 64 features each: W in 256 of its 512 registers at H = 512)
-// reads every row fragment from LDS once per two MFMAs; NW = 8 (two per SIMD, 32 features each)
-// once per MFMA, and the LDS reads of eight wavefronts then bound the loop.
+// reads every row fragment from LDS once per two MFMAs, NW = 8 (two per SIMD, 32 features each)
+// once per MFMA; NW = 8 measured faster at H = 512 (a single wavefront per SIMD leaves the
+// latencies of its LDS reads and loads uncovered).
 #ifndef MOE_BF16_WST_ROLES
 #define MOE_BF16_WST_ROLES 1
 #endif
