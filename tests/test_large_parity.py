@@ -6,8 +6,9 @@
   is all that expert's outputs depend on); the aux pass whole.  The MoE page's NUMGRAD
   VERIFICATION block checks the gate at its own size; this is the same check at the largest
   shape, and with the perf page's Discipline block (results that do not depend on the run).
-* Maximum sizes: bf16 with 2,100,000 tokens at H = 512 (routed_ctx over 2 GiB, so the forward
-  takes the tiled kernel with 64-bit row offsets instead of the resident-slice one) and fp32
+* Maximum sizes: bf16 with 2,100,000 tokens at H = 512 (routed_ctx over 2 GiB: the
+  W-stationary forward and dX address each row through a buffer descriptor of that row, and
+  the d_W tiles through whole-tensor descriptors with 32-bit byte offsets) and fp32
   with 16,776,192 tokens at H = 128 (T * H just under 2^31, the library's limit).  Inputs are
   drawn on the device (workloads.make_inputs_device); routing and the aux pass are compared
   whole, routed_ctx and d_fused_ctx on sampled tokens, d_W and d_b on sampled entries of
@@ -151,8 +152,9 @@ def _max_size_check(wl, tol_kind):
 
 
 def test_max_size_bf16_over_2gib(gpu_lib):
-    """2,100,000 tokens x 512 bf16: routed_ctx is 2.15 GB, past the resident-slice forward's
-    32-bit byte offsets, so the tiled forward runs."""
+    """2,100,000 tokens x 512 bf16: routed_ctx is 2.15 GB, past 2^31 bytes; the W-stationary
+    forward and dX (row descriptors) and the d_W tiles (whole-tensor descriptors, byte offsets
+    below 2^32) run at this size."""
     wl = workloads.custom(420000, 5, 512, 8, act="bf16", seed=2101)
     assert wl.T * wl.H * 2 >= 2 ** 31 and wl.T * wl.H < 2 ** 31
     _max_size_check(wl, "bf16")
