@@ -82,10 +82,12 @@ def test_horizon_mean_collapse(gpu_lib, act, B, NH, H):
                                 workloads.custom(97, 5, 128, 3, act="bf16"),
                                 workloads.custom(150, 7, 256, 5, act="bf16"),
                                 workloads.custom(600, 5, 512, 8, act="bf16", gate_bias={2: 1.0}),
-                                pytest.param(workloads.custom(16500, 8, 256, 5, act="bf16"), marks=pytest.mark.slow)],
+                                pytest.param(workloads.custom(16500, 8, 256, 5, act="bf16"), marks=pytest.mark.slow),
+                                pytest.param(workloads.custom(7000, 5, 512, 8, act="bf16", seed=33),
+                                             marks=pytest.mark.slow)],
                          ids=["H128", "H256", "H64_multiblock", "H128_large_T_tiling", "H256_big_dw_tiles",
                               "H256_w_stationary",
-                              "bf16_H128", "bf16_H256", "bf16_H512", "bf16_H256_large_T"])
+                              "bf16_H128", "bf16_H256", "bf16_H512", "bf16_H256_large_T", "bf16_H512_w_stationary"])
 def test_bwd_from_mean_equals_collapse_then_bwd(gpu_lib, wl):
     import torch
     import mixture_experts_top_amd as moe

@@ -12,6 +12,8 @@ import workloads
 from oracle import moe_oracle as O
 from tests import compare as C
 
+W_STATIONARY_GROUP = 32  # tokens per group of the W-stationary bf16 kernels
+
 pytestmark = pytest.mark.gpu
 
 
@@ -246,6 +248,24 @@ def test_bf16_large_T_full_parity(gpu_lib, wl):
     from tests import gpu_run
     print(f"[parity] bf16 large T {wl}", flush=True)
     inp = workloads.make_inputs(wl)
+    check_all(inp, gpu_run.run(inp))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("wl", [workloads.custom(7000, 5, 512, 8, act="bf16", gate_bias={2: 5.5}, seed=31),
+                                workloads.custom(14000, 5, 256, 6, act="bf16", gate_bias={0: 5.5}, seed=32)],
+                         ids=["H512", "H256"])
+def test_bf16_w_stationary_one_big_expert_and_tiny_ones(gpu_lib, wl):
+    """35,000 / 70,000 bf16 tokens at H = 512 / 256 (the W-stationary forward and dX, with their
+    loader and storer wavefronts), one expert taking nearly every token and the others a few or
+    none: segments of a single 32-token group that is mostly padding (zero rows: the zero row at
+    H = 512, out-of-range buffer offsets at H = 256), and d_W chunks of a handful of tokens."""
+    from tests import gpu_run
+    print(f"[parity] bf16 W-stationary skew {wl}", flush=True)
+    inp = workloads.make_inputs(wl)
+    counts = np.bincount(inp.gate_logits.reshape(-1, wl.NE).argmax(axis=1), minlength=wl.NE)
+    small = counts[counts < W_STATIONARY_GROUP]
+    assert counts.max() > 0.9 * wl.T and small.size >= 1, counts  # the shape this case is for
     check_all(inp, gpu_run.run(inp))
 
 
