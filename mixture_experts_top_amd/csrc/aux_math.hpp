@@ -102,18 +102,16 @@ __device__ __forceinline__ void aux_grad_row(const float (&p)[NEB], const float 
 }
 
 // Column sums of p over a workgroup of 256 threads (one token each; psum = 0 for tokens
-// past T): a butterfly within each wavefront (every lane ends with the same bits), then
-// the four wavefront sums in a fixed order, written to part_row[0 .. N_E).  Contains a
-// barrier: every thread of the workgroup calls it.
+// past T): each wavefront's sum in the fixed order of wave_sum, then the four wavefront sums
+// in a fixed order, written to part_row[0 .. N_E).  Contains a barrier: every thread of the
+// workgroup calls it.
 template <int NEB>
 __device__ __forceinline__ void aux_block_colsum(const float (&psum)[NEB], float (*red)[NEB], int NE,
                                                  float* __restrict__ part_row) {
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
 #pragma unroll
     for (int e = 0; e < NEB; ++e) {
-        float v = psum[e];
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+        const float v = wave_sum(psum[e]);
         if (lane == 0) red[wave][e] = v;
     }
     __syncthreads();

@@ -85,26 +85,66 @@ __device__ __forceinline__ int expert_nchunks(int c, int P, int T) {
     return c == 0 ? 0 : (int)(((int64_t)c * P + T - 1) / T);
 }
 
-// Inclusive prefix sum over the 64 lanes of a wavefront (every lane holds one term).
-__device__ __forceinline__ int wave_inclusive_sum(int v) {
-    const int lane = __lane_id();
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int u = __shfl_up(v, d);
-        if (lane >= d) v += u;
-    }
-    return v;
+// Cross-lane steps through DPP (data-parallel primitives: a VALU operand read from another
+// lane of the same 16-lane row) rather than LDS permutes: each step is one VALU instruction,
+// where a permute is an LDS round trip that the next step waits for.  dpp_move returns, in
+// every lane, src of the lane that CTRL names, or `id` where that lane lies outside the row.
+// CTRL: quad_perm p (0x00 - 0xFF, two bits per lane of a quad), row_shr n (0x110 + n),
+// row_ror n (0x120 + n).
+template <int CTRL>
+__device__ __forceinline__ int dpp_move(int src, int id) {
+    return __builtin_amdgcn_update_dpp(id, src, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float src) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, src), CTRL, 0xF, 0xF,
+                                                                 false));
 }
 
-// Inclusive running maximum over the 64 lanes of a wavefront.
-__device__ __forceinline__ int wave_inclusive_max(int v) {
+// Inclusive prefix sum over the 64 lanes of a wavefront (every lane holds one term): a
+// doubling scan inside each 16-lane row (shifts of 1, 2, 4, 8), then the totals of the rows
+// below are added.  Integer sums, so the order does not matter.
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
     const int lane = __lane_id();
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int u = __shfl_up(v, d);
-        if (lane >= d) v = max(v, u);
-    }
-    return v;
+    v += dpp_move<0x111>(v, 0);
+    v += dpp_move<0x112>(v, 0);
+    v += dpp_move<0x114>(v, 0);
+    v += dpp_move<0x118>(v, 0);
+    const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
+              r2 = __builtin_amdgcn_readlane(v, 47);
+    const int row = lane >> 4;
+    return v + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+}
+
+// Inclusive running maximum over the 64 lanes of a wavefront, for non-negative terms (0 is
+// the identity the shifts bring in, so a result is always one of the terms or 0).
+__device__ __forceinline__ int wave_inclusive_max_nonneg(int v) {
+    const int lane = __lane_id();
+    v = max(v, dpp_move<0x111>(v, 0));
+    v = max(v, dpp_move<0x112>(v, 0));
+    v = max(v, dpp_move<0x114>(v, 0));
+    v = max(v, dpp_move<0x118>(v, 0));
+    const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
+              r2 = __builtin_amdgcn_readlane(v, 47);
+    const int row = lane >> 4;
+    const int below = row > 2 ? max(max(r0, r1), r2) : (row > 1 ? max(r0, r1) : (row > 0 ? r0 : 0));
+    return max(v, below);
+}
+
+// Sum of v over the 64 lanes of a wavefront, the same bits in every lane: within each quad
+// (exchanges with lane ^ 1, then ^ 2: every lane of a quad holds the same sum), across the
+// quads of a row (rotations by 4 and 8), then the four row sums of lanes 0, 16, 32, 48 in
+// that order.  A fixed order, so the result does not depend on the run.
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp_move<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+    v += dpp_move<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+    v += dpp_move<0x124>(v);  // row_ror 4
+    v += dpp_move<0x128>(v);  // row_ror 8
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    return ((r0 + r1) + r2) + r3;
 }
 
 // Lane l < NE: expert l's first position lo in perm and its token count cnt, from offsets
@@ -117,7 +157,7 @@ __device__ __forceinline__ void expert_range(const int* __restrict__ offsets, in
         a = guard_offset(offsets[lane], T);
         b = offsets[lane + 1];
     }
-    lo = wave_inclusive_max(a);
+    lo = wave_inclusive_max_nonneg(a);
     cnt = lane < NE ? guard_count(lo, b, T) : 0;
 }
 

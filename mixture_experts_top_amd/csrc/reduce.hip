@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void k_reduce_dw(const float* __restrict__ pdw
     expert_range(offsets, NE, T, lo, cnt);
     const int nl = expert_nchunks(cnt, P, T);
     const int incl = wave_inclusive_sum(nl);
-    const int cs = __shfl(incl - nl, e), n = __shfl(nl, e);
+    const int cs = __builtin_amdgcn_readlane(incl - nl, e), n = __builtin_amdgcn_readlane(nl, e);
     const size_t HH = (size_t)H * H;
     const int nbx = (int)(HH / (4 * RX));
     if ((int)blockIdx.x < nbx) {
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(256) void k_reduce_dw_wide(const float* __restrict_
     expert_range(offsets, NE, T, lo, cnt);
     const int nl = expert_nchunks(cnt, P, T);
     const int incl = wave_inclusive_sum(nl);
-    const int cs = __shfl(incl - nl, e), n = __shfl(nl, e);
+    const int cs = __builtin_amdgcn_readlane(incl - nl, e), n = __builtin_amdgcn_readlane(nl, e);
     const size_t HH = (size_t)H * H;
     const int nbx = (int)(HH / (4 * 256 * CPT));
     const bool isdb = (int)blockIdx.x >= nbx;
