@@ -118,6 +118,23 @@ __device__ __forceinline__ void aux_block_colsum(const float (&psum)[NEB], float
     if (tid < NE) part_row[tid] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
 }
 
+// v += part[b][e] for b = s, s + S, ... < nblk in ascending order, NB loads in flight.
+template <int NB>
+__device__ __forceinline__ void aux_colsum_batched(const float* __restrict__ part, int nblk, int NE, int S, int s,
+                                                   int e, float& v) {
+    for (int b0 = s; b0 < nblk; b0 += NB * S) {
+        float pv[NB];
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            const int b = b0 + u * S;
+            pv[u] = part[(int64_t)(b < nblk ? b : s) * NE + e];
+        }
+#pragma unroll
+        for (int u = 0; u < NB; ++u)
+            if (b0 + u * S < nblk) v += pv[u];
+    }
+}
+
 // One workgroup of 256 threads: mean_prob from the per-block column sums (thread (s, e)
 // sums blocks s, s + S, ... of column e, then the S partial sums are added in order),
 // frac from the counts (thread e < N_E passes count_e), and the loss.  acc: 256 floats of
@@ -131,9 +148,15 @@ __device__ __forceinline__ void aux_final_block(const float* __restrict__ part, 
     const int S = 256 / nep;
     const int tid = threadIdx.x, e = tid % nep, s = tid / nep;
     float v = 0.0f;
-    if (e < NE)
-#pragma unroll 8
-        for (int b = s; b < nblk; b += S) v += part[(int64_t)b * NE + e];
+    if (e < NE && s < nblk) {
+        // blocks s, s + S, ... in ascending order, loaded NB at a time (a block past nblk
+        // re-reads block s and is not added), so a thread waits once per batch, not once per
+        // block: 8 per batch when a thread has at most 8 blocks, else 32
+        if (nblk <= 8 * S)
+            aux_colsum_batched<8>(part, nblk, NE, S, s, e, v);
+        else
+            aux_colsum_batched<32>(part, nblk, NE, S, s, e, v);
+    }
     acc[tid] = v;
     __syncthreads();
     if (tid < NE) {

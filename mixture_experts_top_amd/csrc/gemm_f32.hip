@@ -421,7 +421,21 @@ struct RouteView {
 __device__ __forceinline__ void hist_counts_lds(int* hs, int* tot, const int* __restrict__ hist, int nblk, int NE) {
     const int tid = threadIdx.x;
     const int nhist = nblk * NE;
-    for (int i = tid; i < nhist; i += kThreads) hs[i] = hist[i];
+    // every load of a thread out before the first wait (one round trip, not one per entry)
+    constexpr int MAXU = 4096 / kThreads;
+    const int per = (nhist + kThreads - 1) / kThreads;
+    int hv[MAXU];
+#pragma unroll
+    for (int u = 0; u < MAXU; ++u)
+        if (u < per) {
+            const int i = tid + kThreads * u;
+            hv[u] = hist[i < nhist ? i : nhist - 1];
+        }
+#pragma unroll
+    for (int u = 0; u < MAXU; ++u) {
+        const int i = tid + kThreads * u;
+        if (u < per && i < nhist) hs[i] = hv[u];
+    }
     __syncthreads();
     int nep = 1;
     while (nep < NE) nep <<= 1;

@@ -21,18 +21,29 @@ __device__ __forceinline__ void st4(float* p, f32x4 v) { *reinterpret_cast<f32x4
 
 // Sums rows [cs, cs + n) of a [rows][len] fp32 array into out[col0 : col0 + 4 RX] (float4
 // lanes); +0.0 when n == 0.  Thread row ty takes rows ty, ty + RY, ... in order, then the RY
-// row sums are added in order.
+// row sums are added in order.  The rows are loaded NB at a time, every load of a batch
+// unconditional (a row index past n re-reads row n - 1, which is not added), so a thread
+// waits on one memory round trip per batch rather than one per row.
 template <int RY>
 __device__ __forceinline__ void column_sum(const float* __restrict__ in, size_t len, int cs, int n, size_t col0,
                                            float* __restrict__ out, f32x4* red) {
-    constexpr int RX = 256 / RY;
+    constexpr int RX = 256 / RY, NB = 8;
     const int tx = threadIdx.x % RX, ty = threadIdx.x / RX;
     const size_t col = col0 + 4 * (size_t)tx;
     const bool ok = col < len;
     f32x4 s = f32x4{};
-    if (ok) {
-#pragma unroll 8
-        for (int c = ty; c < n; c += RY) s += ld4(in + (size_t)(cs + c) * len + col);
+    if (ok && n > 0) {
+        for (int c0 = ty; c0 < n; c0 += NB * RY) {
+            f32x4 v[NB];
+#pragma unroll
+            for (int u = 0; u < NB; ++u) {
+                const int c = c0 + u * RY;
+                v[u] = ld4(in + (size_t)(cs + (c < n ? c : n - 1)) * len + col);
+            }
+#pragma unroll
+            for (int u = 0; u < NB; ++u)
+                if (c0 + u * RY < n) s += v[u];
+        }
     }
     red[ty * RX + tx] = s;
     __syncthreads();

@@ -289,12 +289,24 @@ __global__ __launch_bounds__(kRouteThreads) void k_scatter_scan(const int* __res
     {
         const int ec = tid % nep, sg = tid / nep;
         int all = 0, before = 0;
-        if (ec < NE) {
-#pragma unroll 4
-            for (int x = sg; x < nblk; x += S) {
-                const int v = hist[(int64_t)x * NE + ec];
-                all += v;
-                before += (x < b) ? v : 0;
+        if (ec < NE && sg < nblk) {
+            // 8 loads at a time, all unconditional (a block past nblk re-reads block sg and is
+            // not counted): one memory round trip per batch
+            for (int x0 = sg; x0 < nblk; x0 += 8 * S) {
+                int hv[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int x = x0 + u * S;
+                    hv[u] = hist[(int64_t)(x < nblk ? x : sg) * NE + ec];
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int x = x0 + u * S;
+                    if (x < nblk) {
+                        all += hv[u];
+                        before += (x < b) ? hv[u] : 0;
+                    }
+                }
             }
         }
         part[0][tid] = all;
