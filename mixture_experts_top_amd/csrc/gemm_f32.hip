@@ -418,6 +418,10 @@ struct RouteView {
 // Loads the routing histogram hist[nblk][N_E] (at most 4096 entries) into hs and sums its
 // columns into tot (256 ints): afterwards tot[e] holds expert e's token count, e < N_E.
 // Integer sums, exact in any order.  Contains barriers: every thread calls it.
+// Thread (ec, sg) = (tid % nep, tid / nep) sums blocks sg, sg + S, ... of column ec (nep = N_E
+// rounded up to a power of two, S = 256 / nep); the S segment sums of a column are then added
+// inside each 16-lane row through DPP rotations (nep <= 8) and across rows through LDS, so the
+// whole reduction costs two barriers.
 __device__ __forceinline__ void hist_counts_lds(int* hs, int* tot, const int* __restrict__ hist, int nblk, int NE) {
     const int tid = threadIdx.x;
     const int nhist = nblk * NE;
@@ -436,22 +440,41 @@ __device__ __forceinline__ void hist_counts_lds(int* hs, int* tot, const int* __
         const int i = tid + kThreads * u;
         if (u < per && i < nhist) hs[i] = hv[u];
     }
-    __syncthreads();
     int nep = 1;
     while (nep < NE) nep <<= 1;
     const int S = kThreads / nep;
-    {
-        const int ec = tid % nep, sg = tid / nep;
-        int sum = 0;
+    const int ec = tid % nep, sg = tid / nep;
+    int sum = 0;
+    if (nep == NE) {
+        // entry tid + 256 u is block sg + S u of column ec: this thread's own loads
+#pragma unroll
+        for (int u = 0; u < MAXU; ++u)
+            if (u < per && tid + kThreads * u < nhist) sum += hv[u];
+    } else {
+        __syncthreads();
         if (ec < NE)
             for (int x = sg; x < nblk; x += S) sum += hs[x * NE + ec];
-        tot[tid] = sum;
     }
+    // partial sums of column ec: with nep <= 8 the lanes of a row that share ec are summed in
+    // registers (rotations keep lane % nep), one value per (row, ec) goes to LDS
+    if (nep <= 8) {
+        if (nep == 1) sum += dpp_move<0xB1>(sum, 0);
+        if (nep <= 2) sum += dpp_move<0x4E>(sum, 0);
+        if (nep <= 4) sum += dpp_move<0x124>(sum, 0);
+        sum += dpp_move<0x128>(sum, 0);
+    }
+    // nep <= 8: 16 rows x nep entries at tot[128 ..]; else S entries per column over tot[0 .. 255]
+    const bool small = nep <= 8;
+    int* red = small ? tot + 128 : tot;
+    if (!small || (tid % 16) < nep) red[small ? (tid / 16) * nep + ec : tid] = sum;
     __syncthreads();
-    for (int half = S / 2; half >= 1; half >>= 1) {
-        if (tid / nep < half) tot[tid] += tot[tid + half * nep];
-        __syncthreads();
-    }
+    const int nparts = small ? 16 : S;
+    int cnt = 0;
+    if (tid < NE)
+        for (int q = 0; q < nparts; ++q) cnt += red[q * nep + tid];
+    if (!small) __syncthreads();  // red overlaps tot[0 .. N_E)
+    if (tid < NE) tot[tid] = cnt;
+    __syncthreads();
 }
 
 #ifndef MOE_ONEPASS_RING_F4
