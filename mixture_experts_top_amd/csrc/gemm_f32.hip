@@ -28,6 +28,11 @@ constexpr int kThreads = 256;   // 4 waves, arranged 2 x 2 over the output tile
 #ifndef MOE_F32_KC_FWD
 #define MOE_F32_KC_FWD 32
 #endif
+// the small-T forward's one-tile workgroups (one K slice in flight while the previous
+// computes): 16-wide slices measured 0.2 us faster than 32 at the pages' shape
+#ifndef MOE_F32_KC_FWD_SMALL
+#define MOE_F32_KC_FWD_SMALL 16
+#endif
 #ifndef MOE_F32_KC_DX
 #define MOE_F32_KC_DX 16
 #endif
@@ -399,10 +404,10 @@ __device__ __forceinline__ void rows_f32_body(char* smem, int wg, int nwg, int n
 }
 
 // One tile per workgroup, with a ring of PF K-slices in registers: while slice c computes,
-// the global loads of the next PF slices are outstanding (all of K when it fits), so a
-// tile waits on about three memory round trips (offsets, perm, first operands) rather than
-// one per slice.  Used when the grid has no more tiles than resident workgroups, where a
-// tile's latency is the kernel's time.
+// the global loads of the next PF slices are outstanding (PF from MOE_ONEPASS_RING_F4: one
+// slice by default), so a tile waits on about three memory round trips (offsets, perm,
+// first operands) before its K loop.  Used when the grid has no more tiles than resident
+// workgroups, where a tile's latency is the kernel's time.
 // Routing outputs, for a forward that forms its tiles' token ids itself (and writes perm,
 // counts and offsets) instead of reading the scatter's perm: the expert of every token and
 // the per-routing-block expert histogram (256 tokens per block).
@@ -477,8 +482,12 @@ __device__ __forceinline__ void hist_counts_lds(int* hs, int* tot, const int* __
     __syncthreads();
 }
 
+// float4 registers per thread for the one-pass slice ring.  4 (one K slice in flight while
+// the previous one computes) against 12 (three or four, all of K at H = 128): pages-shape step
+// 39.3 -> 38.6 us, and 6 / 8 / 10 in between; every workgroup of these grids starts at once,
+// so deeper rings only lengthen the first burst of loads that all of them wait behind.
 #ifndef MOE_ONEPASS_RING_F4
-#define MOE_ONEPASS_RING_F4 12  // float4 registers per thread for the one-pass slice ring (keeps 4 waves/SIMD)
+#define MOE_ONEPASS_RING_F4 4
 #endif
 template <int H, int BM, int BN, int KC, bool DX, bool MEAN = false, int XR = 1, bool GATHER = false>
 __device__ __forceinline__ void rows_f32_onepass_body(char* smem, int bid, const float* __restrict__ A,
@@ -1442,7 +1451,7 @@ static hipError_t fwd_f32(const float* X, const float* W, const float* bias, flo
     }
     const int ids = rows_grid<H, TL::FWD_BN>(T, NE, TL::FWD_BM);
     if (ids <= MOE_ROWS_ONEPASS_MAX_IDS)
-        launch_kernel((k_fwd_f32<H, TL::FWD_BM, TL::FWD_BN, MOE_F32_KC_FWD, true>), dim3(ids),
+        launch_kernel((k_fwd_f32<H, TL::FWD_BM, TL::FWD_BN, MOE_F32_KC_FWD_SMALL, true>), dim3(ids),
                            dim3(kThreads), 0, s, X, W, bias, Y, offsets, perm, NE, (int)T, ids);
     else
         launch_kernel((k_fwd_f32<H, TL::FWD_BM, TL::FWD_BN, MOE_F32_KC_FWD, false>),
@@ -1513,7 +1522,7 @@ static hipError_t fwd_f32_gather(const float* X, const float* W, const float* bi
                                  const int32_t* hist, int n_rblk, int32_t* counts, int32_t* offsets, int32_t* perm,
                                  int64_t T, int NE, const AuxFwdArgs* aux, hipStream_t s) {
     using TL = F32Tiles<H>;
-    constexpr int BM = TL::FWD_BM, BN = TL::FWD_BN, KC = MOE_F32_KC_FWD;
+    constexpr int BM = TL::FWD_BM, BN = TL::FWD_BN, KC = MOE_F32_KC_FWD_SMALL;
     const int ids = rows_grid<H, BN>(T, NE, BM);
     AuxFwd ax = {};
     ax.n_gemm = ids;
