@@ -72,14 +72,18 @@ KERNEL_SOURCES = {"fwd_gemm": "gemm", "bwd_gemm": "gemm", "route": "route.hip", 
 
 
 def kernel_source_digest(kernel, act):
-    """sha256 of the HIP source that holds a kernel (for matching stored counter readings)."""
+    """sha256 of the HIP source that holds a kernel and of the library's headers, which every
+    source includes (for matching stored counter readings)."""
     import hashlib
     src = KERNEL_SOURCES[kernel]
     if src == "gemm":
         src = "gemm_bf16.hip" if act == "bf16" else "gemm_f32.hip"
-    path = os.path.join(ROOT, "mixture_experts_top_amd", "csrc", src)
-    with open(path, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()
+    csrc = os.path.join(ROOT, "mixture_experts_top_amd", "csrc")
+    h = hashlib.sha256()
+    for name in [src] + sorted(f for f in os.listdir(csrc) if f.endswith(".hpp")):
+        with open(os.path.join(csrc, name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def measured_traffic(kernel, wl):
