@@ -90,7 +90,9 @@ __device__ __forceinline__ int expert_nchunks(int c, int P, int T) {
 // where a permute is an LDS round trip that the next step waits for.  dpp_move returns, in
 // every lane, src of the lane that CTRL names, or `id` where that lane lies outside the row.
 // CTRL: quad_perm p (0x00 - 0xFF, two bits per lane of a quad), row_shr n (0x110 + n),
-// row_ror n (0x120 + n).
+// row_ror n (0x120 + n).  The scans and sums below read other lanes' registers (DPP sources,
+// readlane), so all 64 lanes of the wavefront must be active where they are called: every
+// caller runs them in code that the whole workgroup executes.
 template <int CTRL>
 __device__ __forceinline__ int dpp_move(int src, int id) {
     return __builtin_amdgcn_update_dpp(id, src, CTRL, 0xF, 0xF, false);
