@@ -71,9 +71,34 @@ KERNEL_SOURCES = {"fwd_gemm": "gemm", "bwd_gemm": "gemm", "route": "route.hip", 
                   "scatter": "route.hip", "reduce": "reduce.hip", "aux": "aux.hip", "aux_final": "aux.hip"}
 
 
+def _code_only(text):
+    """C++ source with comments removed and whitespace runs collapsed (string literals kept)."""
+    import re
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c == '"':  # string literal, copied as is
+            j = i + 1
+            while j < n and text[j] != '"':
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return re.sub(r"\s+", " ", "".join(out)).strip()
+
+
 def kernel_source_digest(kernel, act):
-    """sha256 of the HIP source that holds a kernel and of the library's headers, which every
-    source includes (for matching stored counter readings)."""
+    """sha256 of the code (comments and whitespace left out) of the HIP source that holds a
+    kernel and of the library's headers, which every source includes: matches stored counter
+    readings to the code they were taken on."""
     import hashlib
     src = KERNEL_SOURCES[kernel]
     if src == "gemm":
@@ -81,8 +106,8 @@ def kernel_source_digest(kernel, act):
     csrc = os.path.join(ROOT, "mixture_experts_top_amd", "csrc")
     h = hashlib.sha256()
     for name in [src] + sorted(f for f in os.listdir(csrc) if f.endswith(".hpp")):
-        with open(os.path.join(csrc, name), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()
 
 
