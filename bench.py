@@ -445,6 +445,54 @@ def largest_config(args):
     return out
 
 
+def measure_peaks(wgs=1024, iters=20000, copy_mib=1024, reps=5):
+    """What the chip delivers on this machine, beside the spec-sheet peaks the roofline fractions
+    divide by: the library's MFMA loop (four independent chains per wavefront, 4 wavefronts
+    per workgroup, 4 workgroups per CU) in fp32 and bf16, the shader clock during it, and the
+    STREAM copy.  Best of `reps` timed launches each."""
+    import torch
+
+    import mixture_experts_top_amd as moe
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            t = a.elapsed_time(b) * 1e-3
+            best = t if best is None else min(best, t)
+        return best
+
+    out = {}
+    sink = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    ticks = torch.empty(wgs, 2, dtype=torch.int64, device="cuda")
+    for act, name, per in ((moe.DTYPE_F32, "f32", 4096), (moe.DTYPE_BF16, "bf16", 32768)):
+        it = iters if act == moe.DTYPE_F32 else iters * 4
+        t = timed(lambda: moe.moe_probe_mfma(act, wgs, it, sink, ticks))
+        flops = wgs * 4 * it * 4 * per
+        tk = ticks.cpu().double()
+        ratio = float((tk[:, 0] / tk[:, 1]).median())
+        out[f"mfma_{name}_tflops"] = flops / t / 1e12
+        out[f"mfma_{name}_frac_of_spec"] = flops / t / 1e12 / PEAK_TFLOPS[name]
+        # clock64 / wall_clock64 ticks; the constant clock (s_memrealtime) runs at 100 MHz
+        out[f"shader_clock_ghz_during_{name}"] = ratio * 0.1
+    n = (copy_mib << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    t = timed(lambda: moe.moe_probe_copy(src, dst))
+    out["copy_gbs"] = 2 * n * 4 / t / 1e9
+    out["copy_frac_of_spec"] = out["copy_gbs"] / PEAK_HBM_GBS
+    out["copy_bytes"] = 2 * n * 4
+    del src, dst, sink, ticks
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -477,6 +525,8 @@ def main():
     ap.add_argument("--kernel", default=None, help="kernel timed live in the timed region (default: the slowest)")
     ap.add_argument("--timer-every", type=int, default=5,
                     help="time the dominant kernel with HIP events in every n-th step of the timed region")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the MFMA-loop / copy calibration (sub-record peaks)")
     ap.add_argument("--row", default="gate",
                     help="gate (default) | reduce_axis0 | collapse_fwd | collapse_bwd | softmax_ce")
     args = ap.parse_args()
@@ -551,6 +601,9 @@ def main():
         log(f"[bench] largest config: {largest['ms_per_step'] * 1e3:.1f} us/step, step frac "
             f"{largest['step_roofline_frac']:.3f}, {largest['kernel']} frac {largest['kernel_frac']:.3f}")
 
+    peaks = None if args.no_peaks else measure_peaks()
+    if peaks:
+        log("[bench] peaks: " + ", ".join(f"{k}={v:.4g}" for k, v in peaks.items()))
     cpu = None if args.no_cpu_baseline else cpu_baseline(inp, args.cpu_budget, args.cpu_single_budget)
     T = wl.T
     out = {
@@ -580,6 +633,7 @@ def main():
         "pass_roofline_us": roof,
         "kernel_avg_us": kern_us,
         "largest_config": largest,
+        "peaks": peaks,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -310,6 +310,26 @@ moe_status_t moe_set_launch_timer(int kernel_id, void* ev_start, void* ev_stop);
 /* Name of a MOE_KERNEL_* id (static text), NULL if out of range. */
 const char* moe_kernel_name(int kernel_id);
 
+/*
+ * Calibration probes (not part of the gate): what this chip delivers, against the
+ * spec-sheet peaks that roofline fractions divide by.  Both only enqueue on `stream`.
+ *
+ * moe_probe_mfma: `workgroups` workgroups of 256 threads (4 wavefronts); each wavefront
+ *   issues `iters` rounds of four independent MFMA chains -- act MOE_DTYPE_F32:
+ *   v_mfma_f32_32x32x2_f32 (4,096 flops each), MOE_DTYPE_BF16: v_mfma_f32_32x32x16_bf16
+ *   (32,768 flops each) -- so a call performs workgroups * 4 * iters * 4 * (flops per
+ *   instruction) flops.  Writes one checksum per thread, sink [workgroups * 256] fp32, and
+ *   for each workgroup the shader-clock and constant-clock ticks its first wavefront spent
+ *   in the loop, ticks [workgroups][2] int64 (clock64, wall_clock64: their ratio times the
+ *   constant clock's rate, hipDeviceAttributeWallClockRate, is the shader clock).
+ *   workgroups in [1, 2^20], iters > 0; sink 4-byte and ticks 8-byte aligned.
+ * moe_probe_copy: dst[0 .. bytes) = src[0 .. bytes) (the STREAM copy: 16-byte loads and
+ *   stores); both 16-byte aligned, bytes a positive multiple of 16, no overlap.
+ * Errors: MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED as above, MOE_ERR_HIP on a failed launch.
+ */
+moe_status_t moe_probe_mfma(int act, int64_t workgroups, int64_t iters, float* sink, int64_t* ticks, void* stream);
+moe_status_t moe_probe_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -17,7 +17,7 @@ __all__ = [
     "moe_top1_fwd", "moe_top1_fwd_noalloc", "moe_top1_bwd", "moe_aux_loss", "moe_set_launch_timer", "moe_kernel_name",
     "moe_lambda_eff_update", "moe_aux_loss_lambda_dev", "moe_reduce_axis0", "moe_reduce_axis0_workspace_bytes",
     "moe_horizon_mean_collapse_fwd", "moe_horizon_mean_collapse_bwd", "moe_top1_bwd_from_mean",
-    "moe_softmax_ce_grad", "MoeError", "KERNELS", "DTYPE_F32", "DTYPE_BF16",
+    "moe_softmax_ce_grad", "moe_probe_mfma", "moe_probe_copy", "MoeError", "KERNELS", "DTYPE_F32", "DTYPE_BF16",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -71,6 +71,8 @@ def load_library() -> ctypes.CDLL:
         "moe_horizon_mean_collapse_bwd": ([P, P, I64, I64, I64, I32, P], I32),
         "moe_top1_bwd_from_mean": ([P, P, P, P, P, P, P, P, I32, I64, I64, I64, I64, I32, P, SZ, P], I32),
         "moe_softmax_ce_grad": ([P, P, P, P, I64, I64, I64, P], I32),
+        "moe_probe_mfma": ([I32, I64, I64, P, P, P], I32),
+        "moe_probe_copy": ([P, P, I64, P], I32),
         "moe_top1_fwd_aux": ([P, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P, P, P,
                               I64, I64, I64, I64, I32, P, SZ, P], I32),
     }
@@ -400,6 +402,23 @@ def moe_softmax_ce_grad(logits, labels, grad, ce, stream=None):
     _expect(ce, "ce", (B, NH), torch.float32)
     _check(load_library().moe_softmax_ce_grad(_ptr(logits), _ptr(labels), _ptr(grad), _ptr(ce), B, NH, A,
                                               _stream(stream)))
+
+
+def moe_probe_mfma(act, workgroups, iters, sink, ticks, stream=None):
+    """Calibration MFMA loop (see moe_top1.h): sink [workgroups * 256] fp32, ticks
+    [workgroups, 2] int64 on the GPU."""
+    import torch
+    _expect(sink, "sink", (workgroups * 256,), torch.float32)
+    _expect(ticks, "ticks", (workgroups, 2), torch.int64)
+    _check(load_library().moe_probe_mfma(act, workgroups, iters, _ptr(sink), _ptr(ticks), _stream(stream)))
+
+
+def moe_probe_copy(src, dst, stream=None):
+    """Calibration copy dst = src (same number of bytes, a multiple of 16)."""
+    nb = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nb:
+        raise ValueError("src and dst must hold the same number of bytes")
+    _check(load_library().moe_probe_copy(_ptr(src), _ptr(dst), nb, _stream(stream)))
 
 
 def moe_set_launch_timer(kernel, ev_start=None, ev_stop=None):

@@ -649,4 +649,36 @@ moe_status_t moe_softmax_ce_grad(const float* logits, const int32_t* labels, flo
     return MOE_OK;
 }
 
+// ---------------------------------------------------------------- calibration probes
+}  // extern "C"
+namespace moe {  // peak_probe.hip
+hipError_t launch_probe_mfma(int act, int64_t workgroups, int64_t iters, float* sink, int64_t* ticks,
+                             hipStream_t s);
+hipError_t launch_probe_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
+}  // namespace moe
+extern "C" {
+
+moe_status_t moe_probe_mfma(int act, int64_t workgroups, int64_t iters, float* sink, int64_t* ticks, void* stream) {
+    const char* fn = "moe_probe_mfma";
+    if (act != MOE_DTYPE_F32 && act != MOE_DTYPE_BF16) return fail(MOE_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, act);
+    if (workgroups <= 0 || workgroups > (1 << 20) || iters <= 0)
+        return fail(MOE_ERR_INVALID_ARG, "%s: workgroups must be in [1, 2^20] and iters positive", fn);
+    if (!sink || !ticks) return fail(MOE_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (((uintptr_t)sink & 3u) || ((uintptr_t)ticks & 7u))
+        return fail(MOE_ERR_INVALID_ARG, "%s: sink must be 4-byte and ticks 8-byte aligned", fn);
+    const hipError_t e = launch_probe_mfma(act, workgroups, iters, sink, ticks, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "MFMA probe");
+    return MOE_OK;
+}
+
+moe_status_t moe_probe_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+    const char* fn = "moe_probe_copy";
+    if (!src || !dst) return fail(MOE_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (!aligned16(src) || !aligned16(dst)) return fail(MOE_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", fn);
+    if (bytes <= 0 || (bytes & 15) != 0) return fail(MOE_ERR_INVALID_ARG, "%s: bytes must be a positive multiple of 16", fn);
+    const hipError_t e = launch_probe_copy(src, dst, bytes, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "copy probe");
+    return MOE_OK;
+}
+
 }  // extern "C"

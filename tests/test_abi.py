@@ -197,3 +197,15 @@ def test_next_rows_validation(lib):
     assert lib.moe_softmax_ce_grad(FAKE, FAKE, FAKE, FAKE, 4, 5, 65, None) == UNSUPPORTED
     assert lib.moe_softmax_ce_grad(FAKE, None, FAKE, FAKE, 4, 5, 21, None) == INVALID
     assert lib.moe_softmax_ce_grad(FAKE, FAKE, FAKE, FAKE, 0, 5, 21, None) == INVALID
+
+
+def test_probe_validation(lib):
+    assert lib.moe_probe_mfma(2, 8, 10, FAKE, FAKE, None) == UNSUPPORTED               # unknown dtype
+    assert lib.moe_probe_mfma(0, 0, 10, FAKE, FAKE, None) == INVALID                   # no workgroups
+    assert lib.moe_probe_mfma(0, (1 << 20) + 1, 10, FAKE, FAKE, None) == INVALID
+    assert lib.moe_probe_mfma(1, 8, 0, FAKE, FAKE, None) == INVALID                    # no iterations
+    assert lib.moe_probe_mfma(0, 8, 10, None, FAKE, None) == INVALID
+    assert lib.moe_probe_mfma(0, 8, 10, FAKE, FAKE + 4, None) == INVALID               # ticks need 8 B
+    assert lib.moe_probe_copy(FAKE, FAKE + 8, 1024, None) == INVALID                   # 16-byte alignment
+    assert lib.moe_probe_copy(FAKE, FAKE, 1000, None) == INVALID                       # multiple of 16
+    assert lib.moe_probe_copy(None, FAKE, 1024, None) == INVALID
