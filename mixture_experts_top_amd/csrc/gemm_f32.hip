@@ -1129,6 +1129,9 @@ struct F32WstSmem {
     static constexpr size_t bytes = ids_off + 5 * kF32WstGT * 4;
 };
 static __device__ __attribute__((aligned(16))) float kZeroRowF[256];  // padded rows read these
+// padded output rows of the W-stationary kernel are written here (never read), so that no store
+// is conditional and every group issues the same memory operations
+static __device__ __attribute__((aligned(16))) float kSinkRowF[256];
 // 256 workgroups when every share holds at least 8 groups of 32 tokens
 static inline bool f32_wst(int64_t T, int H) {
     return MOE_F32_WST && H == 256 && T >= (int64_t)kF32WstWgs * 8 * kF32WstGT;
@@ -1159,16 +1162,20 @@ __device__ __forceinline__ void rows_f32_wst_body(char* smem, const float* __res
     int x_lo, x_cnt;
     expert_range(offsets, NE, T, x_lo, x_cnt);
     const int lrow = tid / CPR, lch = tid % CPR;
+    // perm [T] int32 through a buffer descriptor (word 3: raw 32-bit accesses on CDNA)
+    const __amdgpu_buffer_rsrc_t perm_rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)perm, 0, (int)((uint32_t)T * 4u), 0x00020000);
 
     f32x4 wr[NM];  // feature fw + l32, k 8 m + 4 h .. + 3
     f32x4 xr[NL];  // the next group's rows, in flight
 
-    auto load_x = [&](const int* gid) {  // a padded row reads the zero row
+    auto load_x_one = [&](const int* gid, int j) {  // a padded row reads the zero row
+        const int t = gid[lrow + RPI * j];
+        xr[j] = ld4(t >= 0 ? A + (size_t)(MEAN ? t / nh : t) * H + 4 * lch : kZeroRowF + 4 * lch);
+    };
+    auto load_x = [&](const int* gid) {
 #pragma unroll
-        for (int j = 0; j < NL; ++j) {
-            const int t = gid[lrow + RPI * j];
-            xr[j] = ld4(t >= 0 ? A + (size_t)(MEAN ? t / nh : t) * H + 4 * lch : kZeroRowF + 4 * lch);
-        }
+        for (int j = 0; j < NL; ++j) load_x_one(gid, j);
     };
     auto store_x = [&](char* xb) {
 #pragma unroll
@@ -1219,7 +1226,7 @@ __device__ __forceinline__ void rows_f32_wst_body(char* smem, const float* __res
         f32x4 v = *reinterpret_cast<const f32x4*>(ost_at(ob, r, c));
         if (!DX) v = v + bq;
         if (ACC) v = ld4(Out + (size_t)(t < 0 ? 0 : t) * H + 4 * c) + v;
-        if (t >= 0) st4_nt(Out + (size_t)t * H + 4 * c, v);
+        st4_nt(t >= 0 ? Out + (size_t)t * H + 4 * c : kSinkRowF + 4 * c, v);
     };
     auto store_out = [&](float* ob, const int* gid) {
 #pragma unroll
@@ -1235,10 +1242,12 @@ __device__ __forceinline__ void rows_f32_wst_body(char* smem, const float* __res
         const int se = min(P1, __builtin_amdgcn_readlane(x_lo, e) + __builtin_amdgcn_readlane(x_cnt, e));
         const int G = (se - p + GT - 1) / GT;
         // this thread's entry of perm in group g, as loaded (unconditional, of a clamped position;
-        // the guard and the validity are applied where the id is written to LDS, a group later)
+        // the guard and the validity are applied where the id is written to LDS, at the end of
+        // the group).  A buffer load: unlike a load through the read-only pointer, the compiler
+        // keeps it where it is issued instead of sinking it to its use.
         auto group_raw = [&](int g) {
             const int k = p + GT * g + (tid % GT);
-            return perm[k < se ? k : se - 1];
+            return __builtin_amdgcn_raw_buffer_load_b32(perm_rs, (k < se ? k : se - 1) * 4, 0, 0);
         };
         auto group_valid = [&](int g) { return g < G && p + GT * g + (tid % GT) < se; };
         __syncthreads();  // the previous segment is done with the bias, ids and staged results
@@ -1253,28 +1262,46 @@ __device__ __forceinline__ void rows_f32_wst_body(char* smem, const float* __res
             if (tid < GT) {
                 ids[0][tid] = group_valid(0) ? guard_token(i0, T) : -1;
                 ids[1][tid] = group_valid(1) ? guard_token(i1, T) : -1;
+                ids[4][tid] = -1;  // "group -1": the output stores issued during group 0 go to the sink
             }
         }
-        int idr = group_raw(2);  // ids in flight: of group g + 2 during group g
         __syncthreads();
         load_x(ids[0]);
-        // group g: its rows to LDS (and the ids of g + 2); the rows of g + 1 and the ids of g + 3
-        // into flight; the MFMAs of g, with the output of g - 1 to memory between them
+        store_x(xb0);  // the rows of group 0, visible after the loop's first barrier
+        // group g: barrier (its rows and the ids of g + 1 visible, every wavefront done with group
+        // g - 1 and so with the row stage of g + 1); the perm entries of g + 2 into flight; the
+        // MFMAs of g with, between its batches, the row loads of g + 1 (first half) and the output
+        // rows of g - 1 (second half; none before group 0), one per batch, so the vector-memory work
+        // of the eight wavefronts overlaps the MFMA chain instead of queueing behind the barrier
+        // (issued all at once there, the row loads alone took about 1,100 of the 20,000 cycles of
+        // a group); then the ids of g + 2 and the rows of g + 1 to LDS.  Every wait for a load is
+        // in the iteration that issued it, so it counts exactly the memory operations issued after.
+        static_assert(NM / 4 >= NL + GT / 8, "a batch for every row load and output row");
 #pragma unroll 1
         for (int g = 0; g < G; ++g) {
-            char* const xb = (g & 1) ? xb1 : xb0;
-            store_x(xb);
-            if (tid < GT) ids[(g + 2) % 5][tid] = group_valid(g + 2) ? guard_token(idr, T) : -1;
             __syncthreads();
-            if (g + 1 < G) load_x(ids[(g + 1) % 5]);
-            idr = group_raw(g + 3);
-            // the output of group g - 1 (none before group 0), one row per thread after each of
-            // the first MFMA batches of group g, so its stores overlap the MFMA chain
+            const int idr = group_raw(g + 2);
+            // keep this load here, ahead of the group's other memory operations (the compiler
+            // would otherwise sink it to its use, where waiting for it waits for all of them)
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
             float* const obp = (g & 1) ? ob0 : ob1;
             const int* const gidp = ids[(g + 4) % 5];
-            compute(xb, (g & 1) ? ob1 : ob0, [&](int b) {
-                if (b < GT / 8 && g > 0) store_row(obp, gidp, b);
+            const int* const gidn = ids[(g + 1) % 5];
+            // no condition on g: past the last group the ids are -1 (zero rows loaded, staged and
+            // never read), and group -1's ids are -1 (its "outputs" go to the sink row)
+            compute((g & 1) ? xb1 : xb0, (g & 1) ? ob1 : ob0, [&](int b) {
+                if (b < NL)
+                    load_x_one(gidn, b);
+                else if (b - NL < GT / 8)
+                    store_row(obp, gidp, b - NL);
             });
+            // the perm entries of g + 2 are used by every thread from here (an empty asm that takes
+            // the value), so the compiler cannot move their load into the branch below
+            int idv = idr;
+            asm volatile("" : "+v"(idv));
+            if (tid < GT) ids[(g + 2) % 5][tid] = group_valid(g + 2) ? guard_token(idv, T) : -1;
+            store_x((g & 1) ? xb0 : xb1);
         }
         __syncthreads();
         store_out(((G - 1) & 1) ? ob1 : ob0, ids[(G - 1) % 5]);
