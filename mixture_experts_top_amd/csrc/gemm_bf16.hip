@@ -1722,17 +1722,18 @@ __device__ __forceinline__ void rows_bf16_wsr_body(char* smem, const uint16_t* _
                                                          0);
             };
             // one wavefront load of rows into LDS.  One row per load (H = 512): a descriptor of
-            // that row (tt uniform; a padded row reads the zero row), so the lane offsets are
-            // constants.  Two rows per load (H = 256): a descriptor of the whole of A (fewer than
+            // that row (tt uniform), so the lane offsets are constants; a padded row gets a
+            // descriptor of no bytes, which the range check turns into zeros without a memory
+            // access (every workgroup reading one zero row would queue on one L2 channel).  Two rows per load (H = 256): a descriptor of the whole of A (fewer than
             // 2^31 bf16 elements: byte offsets fit 32 bits), a padded row taking an offset past
             // the end, which the range check turns into zeros.
             const __amdgpu_buffer_rsrc_t a_rs = __builtin_amdgcn_make_buffer_rsrc(
                 (void*)A, 0, (int)((uint32_t)(MEAN ? T / nh : T) * (uint32_t)H * 2u), kBufWord3);
             auto row_dma = [&](int tt, int lc, char* dst) {
                 if constexpr (RPD == 1) {
-                    const uint16_t* rowp = tt >= 0 ? A + (size_t)(MEAN ? tt / nh : tt) * H : kZeroRow;
+                    const uint16_t* rowp = tt >= 0 ? A + (size_t)(MEAN ? tt / nh : tt) * H : A;
                     const __amdgpu_buffer_rsrc_t rs =
-                        __builtin_amdgcn_make_buffer_rsrc((void*)rowp, 0, S::ROWB, kBufWord3);
+                        __builtin_amdgcn_make_buffer_rsrc((void*)rowp, 0, tt >= 0 ? S::ROWB : 0, kBufWord3);
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_ptr)dst, 16, 16 * lc, 0, 0, 0);
                 } else {
                     const uint32_t off =
@@ -1742,7 +1743,7 @@ __device__ __forceinline__ void rows_bf16_wsr_body(char* smem, const uint16_t* _
             };
             // group g's rows into its stage: load q covers rows RPW wave + RPD q .. + RPD - 1, lane
             // i taking row RPW wave + RPD q + i / CPR and physical chunk i % CPR, which holds
-            // logical chunk (i % CPR) ^ (row & 15); padded rows read the zero row
+            // logical chunk (i % CPR) ^ (row & 15); padded rows are zeros
             auto issue = [&](int g) {
                 const int kb = p + kWstGT * g + RPW * wave;
                 const int raw = raw_s[256 * (g & 3) + lane];  // the entry of row lane % RPW

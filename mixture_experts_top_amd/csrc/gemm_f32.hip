@@ -1128,10 +1128,13 @@ struct F32WstSmem {
     static constexpr size_t ids_off = bias_off + H * 4;           // token ids: [5][32]
     static constexpr size_t bytes = ids_off + 5 * kF32WstGT * 4;
 };
-static __device__ __attribute__((aligned(16))) float kZeroRowF[256];  // padded rows read these
-// padded output rows of the W-stationary kernel are written here (never read), so that no store
-// is conditional and every group issues the same memory operations
-static __device__ __attribute__((aligned(16))) float kSinkRowF[256];
+// padded rows of the W-stationary kernel read zeros from these rows and write their results to
+// the sink rows (never read), so that no load or store is conditional and every group issues the
+// same memory operations.  One row per workgroup of an XCD's 32 (blocks go to the XCDs in turn):
+// every workgroup on one row would queue its padded groups on one L2 channel.
+constexpr int kF32PadRows = 32;
+static __device__ __attribute__((aligned(16))) float kZeroRowF[kF32PadRows * 256];
+static __device__ __attribute__((aligned(16))) float kSinkRowF[kF32PadRows * 256];
 // 256 workgroups when every share holds at least 8 groups of 32 tokens
 static inline bool f32_wst(int64_t T, int H) {
     return MOE_F32_WST && H == 256 && T >= (int64_t)kF32WstWgs * 8 * kF32WstGT;
@@ -1169,9 +1172,10 @@ __device__ __forceinline__ void rows_f32_wst_body(char* smem, const float* __res
     f32x4 wr[NM];  // feature fw + l32, k 8 m + 4 h .. + 3
     f32x4 xr[NL];  // the next group's rows, in flight
 
-    auto load_x_one = [&](const int* gid, int j) {  // a padded row reads the zero row
+    const int pad_row = 256 * ((blockIdx.x / 8) % kF32PadRows);
+    auto load_x_one = [&](const int* gid, int j) {  // a padded row reads a zero row
         const int t = gid[lrow + RPI * j];
-        xr[j] = ld4(t >= 0 ? A + (size_t)(MEAN ? t / nh : t) * H + 4 * lch : kZeroRowF + 4 * lch);
+        xr[j] = ld4(t >= 0 ? A + (size_t)(MEAN ? t / nh : t) * H + 4 * lch : kZeroRowF + pad_row + 4 * lch);
     };
     auto load_x = [&](const int* gid) {
 #pragma unroll
@@ -1225,8 +1229,9 @@ __device__ __forceinline__ void rows_f32_wst_body(char* smem, const float* __res
         const int t = gid[r];
         f32x4 v = *reinterpret_cast<const f32x4*>(ost_at(ob, r, c));
         if (!DX) v = v + bq;
-        if (ACC) v = ld4(Out + (size_t)(t < 0 ? 0 : t) * H + 4 * c) + v;
-        st4_nt(t >= 0 ? Out + (size_t)t * H + 4 * c : kSinkRowF + 4 * c, v);
+        float* const dst = t >= 0 ? Out + (size_t)t * H + 4 * c : kSinkRowF + pad_row + 4 * c;
+        if (ACC) v = ld4(dst) + v;
+        st4_nt(dst, v);
     };
     auto store_out = [&](float* ob, const int* gid) {
 #pragma unroll
