@@ -20,6 +20,12 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe_top1.so")
+# A second library with the bf16 W-stationary and resident-slice kernels switched off, so that
+# every bf16 GEMM runs the tiled kernels: at H = 256 / 512 the default dispatch sends every size
+# to one of the other two, and the parity tests compare the tiled ones through this build.
+LIB_TILED = os.path.join(PKG, "libmoe_top1_tiled.so")
+BUILD_TILED = os.path.join(ROOT, "_build_tiled")
+TILED_DEFINES = ("MOE_BF16_WST=0", "MOE_BF16_WS_FWD=0")
 ARCH = "gfx950"
 
 
@@ -68,6 +74,11 @@ def build(jobs: int = 8, verbose: bool = False, defines=(), out: str = LIB, buil
     if verbose:
         print(f"built {LIB_OUT}")
     return LIB_OUT
+
+
+def build_tiled(jobs: int = 8, verbose: bool = False) -> str:
+    """The bf16-tiled test library (see LIB_TILED)."""
+    return build(jobs, verbose, defines=TILED_DEFINES, out=LIB_TILED, build_dir=BUILD_TILED)
 
 
 if __name__ == "__main__":

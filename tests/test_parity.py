@@ -237,6 +237,32 @@ def test_big_dw_tiles_full_parity(gpu_lib, wl):
     check_all(inp, gpu_run.run(inp))
 
 
+@pytest.mark.parametrize("wl", [workloads.custom(70, 5, 256, 4, act="bf16"),
+                                workloads.custom(900, 5, 512, 6, act="bf16", gate_bias={2: 1.0}),
+                                workloads.custom(5000, 5, 256, 5, act="bf16", gate="int")],
+                         ids=["H256", "H512_skewed", "H256_ties_many_tiles"])
+def test_bf16_tiled_kernels_parity(gpu_lib, wl):
+    """The tiled bf16 forward, dX and d_W kernels at H = 256 / 512, which the default dispatch
+    never reaches (the W-stationary kernels take every T from 32,768 / 65,536 tokens and the
+    resident-slice forward everything below that): the same cases through a build with those two
+    switched off, compared with the oracle in full; ragged 128-row tiles, a skewed expert, ties."""
+    import os
+    from mixture_experts_top_amd import build as b
+    from tests import gpu_run
+    if not os.path.exists(b.LIB_TILED):
+        pytest.fail(f"{b.LIB_TILED} is not built; run __graft_entry__.build()")
+    print(f"[parity] bf16 tiled build {wl}", flush=True)
+    saved_lib, saved_path = gpu_lib._lib, gpu_lib.library_path
+    try:
+        gpu_lib.library_path = lambda: b.LIB_TILED
+        gpu_lib._lib = None
+        gpu_lib.load_library()
+        inp = workloads.make_inputs(wl)
+        check_all(inp, gpu_run.run(inp))
+    finally:
+        gpu_lib._lib, gpu_lib.library_path = saved_lib, saved_path
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("wl", [workloads.custom(14000, 5, 512, 8, act="bf16", gate_bias={3: 1.0}),
                                 workloads.custom(27000, 5, 256, 6, act="bf16", gate="int")],
